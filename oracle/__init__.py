@@ -1,0 +1,234 @@
+"""CPU oracle for the KDA layer path -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, the smoke check in ``__graft_entry__`` and the CPU-baseline
+leg of ``bench.py`` may import this package.  The HIP library never calls it
+and there is no CPU fallback through it.
+
+Two pieces:
+
+* ``kda_oracle.c`` (built here with gcc): the token-by-token recurrence, the
+  short causal convolution and the checkpoint enumeration, in fp64 (default)
+  or fp32 (``real="f32"``).
+* ``bruteforce.py``: numpy fp64 evaluations of the same definitions written
+  as explicit matrix products, for tiny sizes only.
+
+Every function takes torch tensors or numpy arrays; values are upcast to
+float32 exactly (bf16 -> fp32 is exact) before the C code sees them.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import sys
+from pathlib import Path
+
+import numpy as np
+
+HERE = Path(__file__).resolve().parent
+SRC = HERE / "kda_oracle.c"
+
+_LIB_NAMES = {"f64": "liboracle_f64.so", "f32": "liboracle_f32.so"}
+
+
+def build(real: str = "f64", mutant: int = 0, out: Path | None = None, quiet=True) -> Path:
+    """Compile ``kda_oracle.c`` with gcc -O2 -fopenmp.  Returns the .so path."""
+    if out is None:
+        out = HERE / (_LIB_NAMES[real] if mutant == 0 else f"liboracle_{real}_m{mutant}.so")
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-Wall", "-Wextra",
+           "-Wno-unused-parameter", f"-DORACLE_MUTANT={int(mutant)}"]
+    if real == "f32":
+        cmd.append("-DORACLE_REAL_FLOAT")
+    cmd += [str(SRC), "-o", str(out), "-lm"]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("oracle build failed:\n" + res.stderr)
+    if not quiet and res.stderr:
+        print(res.stderr, file=sys.stderr)
+    return out
+
+
+def _as_f32(x):
+    if x is None:
+        return None
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            return np.ascontiguousarray(x.detach().to("cpu", torch.float32).numpy())
+    except ImportError:  # pragma: no cover
+        pass
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+
+
+def _as_i32(x):
+    if x is None:
+        return None
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            return np.ascontiguousarray(x.detach().to("cpu", torch.int32).numpy())
+    except ImportError:  # pragma: no cover
+        pass
+    return np.ascontiguousarray(np.asarray(x, dtype=np.int32))
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+class Oracle:
+    """ctypes front of one build of ``kda_oracle.c``."""
+
+    def __init__(self, path: Path):
+        self.path = Path(path)
+        self.lib = ctypes.CDLL(str(self.path))
+        L = self.lib
+        vp, i32, i64, dbl = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_double
+        L.oracle_real_bytes.restype = ctypes.c_int
+        L.oracle_mutant.restype = ctypes.c_int
+        L.oracle_get_threads.restype = ctypes.c_int
+        L.oracle_set_threads.argtypes = [ctypes.c_int]
+        L.oracle_ckpt_enumerate.restype = i64
+        L.oracle_ckpt_enumerate.argtypes = [vp, vp, i32, i32, vp, vp, i64]
+        L.oracle_kda_varlen.restype = ctypes.c_int
+        L.oracle_kda_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, dbl,
+                                        vp, vp, vp, vp, i32, vp, i64, vp, i64, i32]
+        L.oracle_kda_verify.restype = ctypes.c_int
+        L.oracle_kda_verify.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, dbl,
+                                        vp, vp, vp, vp, vp]
+        L.oracle_conv_short.restype = ctypes.c_int
+        L.oracle_conv_short.argtypes = [vp, i64, vp, vp, i32, vp, i32, i32, i32, vp, vp, vp,
+                                        vp, vp]
+        self.real = np.float64 if L.oracle_real_bytes() == 8 else np.float32
+        self.mutant = L.oracle_mutant()
+
+    # -- threads -----------------------------------------------------------
+    def set_threads(self, n: int):
+        self.lib.oracle_set_threads(int(n))
+
+    def threads(self) -> int:
+        return self.lib.oracle_get_threads()
+
+    # -- checkpoint positions ---------------------------------------------
+    def ckpt_enumerate(self, cu_seqlens, interval, start_pos=None):
+        cu = _as_i32(cu_seqlens)
+        sp = _as_i32(start_pos)
+        n = cu.size - 1
+        ck_cu = np.zeros(n + 1, np.int32)
+        total = self.lib.oracle_ckpt_enumerate(_p(cu), _p(sp), n, int(interval), _p(ck_cu), None, 0)
+        pos = np.zeros(max(total, 1), np.int32)
+        self.lib.oracle_ckpt_enumerate(_p(cu), _p(sp), n, int(interval), _p(ck_cu), _p(pos), total)
+        return ck_cu, pos[:total]
+
+    # -- recurrence ---------------------------------------------------------
+    def kda_varlen(self, q, k, v, g, beta, cu_seqlens, *, init=None, has_init=None,
+                   start_pos=None, scale=1.0, ckpt_interval=0, pairs=None, want_o=True,
+                   want_final=True):
+        """Token-by-token recurrence over a packed batch.
+
+        q, k, g [T, H, dk]; v [T, H, dv]; beta [T, H]; cu_seqlens [N+1];
+        init [N, H, dk, dv] or None; has_init [N] (0/1) or None.
+        Returns dict with o [T, H, dv] (zeros for pairs not computed), final
+        [N, H, dk, dv], ckpt [n_ckpt, H, dk, dv], ckpt_cu, ckpt_pos.
+        """
+        q, k, v, g, beta = (_as_f32(t) for t in (q, k, v, g, beta))
+        cu = _as_i32(cu_seqlens)
+        sp = _as_i32(start_pos)
+        T, H, dk = q.shape
+        dv = v.shape[-1]
+        N = cu.size - 1
+        init_a = None if init is None else np.ascontiguousarray(np.asarray(
+            init.detach().cpu().numpy() if hasattr(init, "detach") else init, dtype=self.real))
+        hi = _as_i32(has_init)
+        pr = None if pairs is None else np.ascontiguousarray(np.asarray(pairs, np.int32).reshape(-1, 2))
+        o = np.zeros((T, H, dv), self.real) if want_o else None
+        final = np.zeros((N, H, dk, dv), self.real) if want_final else None
+        ck_cu, ck_pos = self.ckpt_enumerate(cu, ckpt_interval, sp)
+        n_ck = int(ck_cu[-1])
+        ck = np.zeros((n_ck, H, dk, dv), self.real) if n_ck else None
+        rc = self.lib.oracle_kda_varlen(
+            _p(q), _p(k), _p(v), _p(g), _p(beta), _p(cu), _p(sp), N, H, dk, dv, float(scale),
+            _p(init_a), _p(hi), _p(o if want_o else np.zeros(1, self.real)), _p(final),
+            int(ckpt_interval), _p(ck), n_ck, _p(pr), 0 if pr is None else pr.shape[0],
+            0 if want_o else 1)
+        if rc != 0:
+            raise RuntimeError(f"oracle_kda_varlen failed ({rc})")
+        return {"o": o, "final": final, "ckpt": ck, "ckpt_cu": ck_cu, "ckpt_pos": ck_pos}
+
+    def kda_verify(self, q, k, v, g, beta, init, accepted_len=None, *, scale=1.0):
+        """Speculative verify.  q, k, g [N, Ts, H, dk]; v [N, Ts, H, dv];
+        beta [N, Ts, H]; init [N, H, dk, dv]; accepted_len [N] or None (= Ts).
+        Returns dict o [N, Ts, H, dv], committed [N, H, dk, dv] (NaN where
+        rejected), committed_len [N]."""
+        q, k, v, g, beta = (_as_f32(t) for t in (q, k, v, g, beta))
+        N, Ts, H, dk = q.shape
+        dv = v.shape[-1]
+        init_a = np.ascontiguousarray(np.asarray(
+            init.detach().cpu().numpy() if hasattr(init, "detach") else init, dtype=self.real))
+        acc = _as_i32(accepted_len)
+        o = np.zeros((N, Ts, H, dv), self.real)
+        com = np.full((N, H, dk, dv), np.nan, self.real)
+        clen = np.zeros(N, np.int32)
+        rc = self.lib.oracle_kda_verify(_p(q), _p(k), _p(v), _p(g), _p(beta), N, Ts, H, dk, dv,
+                                        float(scale), _p(init_a), _p(acc), _p(o), _p(com),
+                                        _p(clen))
+        if rc != 0:
+            raise RuntimeError(f"oracle_kda_verify failed ({rc})")
+        return {"o": o, "committed": com, "committed_len": clen}
+
+    # -- convolution --------------------------------------------------------
+    def conv_short(self, x, w, cu_seqlens, *, bias=None, act=0, state=None, has_state=None,
+                   advance_len=None):
+        """Short causal depthwise convolution.  x [T, C]; w [C, W];
+        state [N, C, W-1] or None.  Returns (y [T, C], new_state [N, C, W-1])."""
+        x = _as_f32(x)
+        w = _as_f32(w)
+        b = _as_f32(bias)
+        st = _as_f32(state)
+        hs = _as_i32(has_state)
+        adv = _as_i32(advance_len)
+        cu = _as_i32(cu_seqlens)
+        T, C = x.shape
+        W = w.shape[1]
+        N = cu.size - 1
+        y = np.zeros((T, C), self.real)
+        ns = np.zeros((N, C, W - 1), self.real)
+        rc = self.lib.oracle_conv_short(_p(x), C, _p(w), _p(b), int(act), _p(cu), N, C, W,
+                                        _p(st), _p(hs), _p(adv), _p(y), _p(ns))
+        if rc != 0:
+            raise RuntimeError(f"oracle_conv_short failed ({rc})")
+        return y, ns
+
+
+_cache: dict = {}
+
+
+def load(real: str = "f64", rebuild: bool = False) -> Oracle:
+    """Load (building first if needed) the oracle of precision ``real``."""
+    key = real
+    if key in _cache and not rebuild:
+        return _cache[key]
+    path = HERE / _LIB_NAMES[real]
+    if rebuild or not path.exists() or path.stat().st_mtime < SRC.stat().st_mtime:
+        build(real)
+    o = Oracle(path)
+    _cache[key] = o
+    return o
+
+
+def load_mutant(mutant: int, outdir: Path, real: str = "f64") -> Oracle:
+    """Build and load a planted-mistake variant (for pin tests)."""
+    path = Path(outdir) / f"liboracle_{real}_m{mutant}.so"
+    build(real, mutant=mutant, out=path)
+    return Oracle(path)
+
+
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    """Round float64 values to bfloat16 (round to nearest even), returned as
+    float64 -- used to express comparisons in the kernel's output precision."""
+    import torch
+    return torch.from_numpy(np.asarray(x, np.float64)).to(torch.bfloat16).to(torch.float64).numpy()
+
+
+__all__ = ["Oracle", "load", "load_mutant", "build", "bf16_round"]
