@@ -1,0 +1,349 @@
+// extern "C" entry points of libkda: argument validation, optional
+// KDA_CHECK=1 validation of device index arrays, and dispatch to the kernel
+// launchers.  No allocation, no synchronisation (outside KDA_CHECK=1).
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <vector>
+
+#include "kda_internal.h"
+
+namespace kda {
+
+static thread_local char g_last_error[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+static bool check_enabled() {
+  static int cached = -1;
+  if (cached < 0) {
+    const char* e = getenv("KDA_CHECK");
+    cached = (e && e[0] && e[0] != '0') ? 1 : 0;
+  }
+  return cached == 1;
+}
+
+static size_t dtype_bytes(int dt) { return dt == KDA_BF16 ? 2 : 4; }
+
+static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+static bool supported_d(int dk, int dv) {
+  return dk == dv && (dk == 16 || dk == 32 || dk == 64 || dk == 128);
+}
+
+// token stride: 0 -> packed; must cover one token's [H, d] row and keep
+// 16-byte alignment.
+static int fix_stride(int64_t& stride, int64_t packed, int dt, const char* name) {
+  if (stride == 0) stride = packed;
+  if (stride < packed) return fail(KDA_ERR_SHAPE, "%s stride %lld < %lld", name, (long long)stride, (long long)packed);
+  if ((stride * (int64_t)dtype_bytes(dt)) % 16 != 0)
+    return fail(KDA_ERR_ALIGN, "%s stride %lld not 16-byte aligned", name, (long long)stride);
+  return KDA_OK;
+}
+
+// beta's stride only needs to cover H scalars
+static int fix_beta_stride(int64_t& stride, int64_t H) {
+  if (stride == 0) stride = H;
+  if (stride < H) return fail(KDA_ERR_SHAPE, "beta stride %lld < H", (long long)stride);
+  return KDA_OK;
+}
+
+template <typename T>
+static bool copy_to_host(std::vector<T>& out, const T* dev, size_t n, hipStream_t stream) {
+  out.assign(n, T());
+  if (n == 0) return true;
+  if (hipMemcpyAsync(out.data(), dev, n * sizeof(T), hipMemcpyDeviceToHost, stream) != hipSuccess) return false;
+  return hipStreamSynchronize(stream) == hipSuccess;
+}
+
+// KDA_CHECK=1: slots in range, no source slot of one sequence used as a
+// destination of another.
+static int check_slots(const int32_t* src, const int32_t* dst, int n_seq, int64_t n_slots,
+                       const std::vector<int32_t>* extra_dst, hipStream_t stream) {
+  std::vector<int32_t> hs, hd;
+  if (!copy_to_host(hs, src, n_seq, stream) || !copy_to_host(hd, dst, n_seq, stream))
+    return fail(KDA_ERR_HIP, "KDA_CHECK: copying slot arrays failed");
+  for (int i = 0; i < n_seq; ++i) {
+    if (hs[i] < -1 || hs[i] >= n_slots) return fail(KDA_ERR_ARG, "src_slot[%d] = %d out of range", i, hs[i]);
+    if (hd[i] < -1 || hd[i] >= n_slots) return fail(KDA_ERR_ARG, "dst_slot[%d] = %d out of range", i, hd[i]);
+  }
+  for (int i = 0; i < n_seq; ++i) {
+    if (hs[i] < 0) continue;
+    for (int j = 0; j < n_seq; ++j)
+      if (j != i && hd[j] == hs[i])
+        return fail(KDA_ERR_ARG, "src_slot[%d] = %d is dst_slot[%d] (same-call reuse)", i, hs[i], j);
+    if (extra_dst)
+      for (int32_t c : *extra_dst)
+        if (c == hs[i]) return fail(KDA_ERR_ARG, "src_slot[%d] = %d is also a checkpoint slot", i, hs[i]);
+  }
+  return KDA_OK;
+}
+
+static int check_cu(const int32_t* cu, int n_seq, int64_t T_tot, hipStream_t stream,
+                    std::vector<int32_t>* out = nullptr) {
+  std::vector<int32_t> h;
+  if (!copy_to_host(h, cu, (size_t)n_seq + 1, stream)) return fail(KDA_ERR_HIP, "KDA_CHECK: copying cu_seqlens failed");
+  if (h[0] < 0) return fail(KDA_ERR_ARG, "cu_seqlens[0] = %d < 0", h[0]);
+  for (int i = 0; i < n_seq; ++i)
+    if (h[i + 1] < h[i]) return fail(KDA_ERR_ARG, "cu_seqlens decreases at %d", i);
+  if (h[n_seq] > T_tot) return fail(KDA_ERR_ARG, "cu_seqlens[n_seq] = %d > T_tot", h[n_seq]);
+  if (out) *out = h;
+  return KDA_OK;
+}
+
+}  // namespace kda
+
+using namespace kda;
+
+extern "C" {
+
+const char* kda_status_str(int status) {
+  switch (status) {
+    case KDA_OK: return "KDA_OK";
+    case KDA_ERR_NULL: return "KDA_ERR_NULL";
+    case KDA_ERR_SHAPE: return "KDA_ERR_SHAPE";
+    case KDA_ERR_DTYPE: return "KDA_ERR_DTYPE";
+    case KDA_ERR_ALIGN: return "KDA_ERR_ALIGN";
+    case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE";
+    case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED";
+    case KDA_ERR_HIP: return "KDA_ERR_HIP";
+    case KDA_ERR_ARG: return "KDA_ERR_ARG";
+    case KDA_ERR_CAPACITY: return "KDA_ERR_CAPACITY";
+    default: return "KDA_ERR_UNKNOWN";
+  }
+}
+
+int kda_abi_version(void) { return KDA_ABI_VERSION; }
+
+const char* kda_last_error(void) { return g_last_error; }
+
+size_t kda_args_sizeof(int which) {
+  switch (which) {
+    case 0: return sizeof(kda_conv_args);
+    case 1: return sizeof(kda_prefill_args);
+    case 2: return sizeof(kda_decode_args);
+    case 3: return sizeof(kda_verify_args);
+    default: return 0;
+  }
+}
+
+// ------------------------------------------------------------------ conv
+int kda_conv_short(const kda_conv_args* a, kda_stream_t stream_) {
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  if (!a) return fail(KDA_ERR_NULL, "args is NULL");
+  if (a->struct_size != sizeof(kda_conv_args)) return fail(KDA_ERR_ARG, "struct_size mismatch");
+  if (a->dtype != KDA_BF16 && a->dtype != KDA_F32) return fail(KDA_ERR_DTYPE, "dtype %d", a->dtype);
+  if (a->n_seq < 0 || a->T_tot < 0 || a->n_slots < 0) return fail(KDA_ERR_SHAPE, "negative size");
+  if (a->n_seq == 0) return KDA_OK;
+  if (a->W < 2 || a->W > 8) return fail(KDA_ERR_UNSUPPORTED, "conv width W = %d (2..8)", a->W);
+  const int V = 16 / (int)dtype_bytes(a->dtype);
+  if (a->C <= 0 || a->C % V != 0) return fail(KDA_ERR_SHAPE, "C = %d not a positive multiple of %d", a->C, V);
+  if (!a->cu_seqlens || !a->weight || !a->src_slot || !a->dst_slot || !a->conv_pool)
+    return fail(KDA_ERR_NULL, "conv: required pointer is NULL");
+  if (a->T_tot > 0 && (!a->x || !a->y)) return fail(KDA_ERR_NULL, "conv: x or y is NULL");
+  kda_conv_args b = *a;
+  if (b.x_stride == 0) b.x_stride = b.C;
+  if (b.y_stride == 0) b.y_stride = b.C;
+  if (b.x_stride < b.C || b.y_stride < b.C) return fail(KDA_ERR_SHAPE, "conv stride < C");
+  const int64_t eb = dtype_bytes(b.dtype);
+  if ((b.x_stride * eb) % 16 || (b.y_stride * eb) % 16 || !aligned16(b.x) || !aligned16(b.y) ||
+      !aligned16(b.conv_pool))
+    return fail(KDA_ERR_ALIGN, "conv: x, y or conv_pool not 16-byte aligned");
+  if (b.T_tot / 64 + b.n_seq > 0x7fffffffLL) return fail(KDA_ERR_SHAPE, "conv: too many tokens");
+  if (check_enabled()) {
+    int st = check_cu(b.cu_seqlens, b.n_seq, b.T_tot, stream);
+    if (st) return st;
+    st = check_slots(b.src_slot, b.dst_slot, b.n_seq, b.n_slots, nullptr, stream);
+    if (st) return st;
+  }
+  ConvParams p{};
+  p.x = b.x; p.y = b.y; p.w = b.weight; p.bias = b.bias; p.cu = b.cu_seqlens; p.pool = b.conv_pool;
+  p.src_slot = b.src_slot; p.dst_slot = b.dst_slot; p.adv = b.advance_len;
+  p.x_stride = b.x_stride; p.y_stride = b.y_stride; p.T_tot = b.T_tot; p.n_slots = b.n_slots;
+  p.n_seq = b.n_seq; p.C = b.C; p.W = b.W; p.act = b.act;
+  return launch_conv(p, b.dtype, stream);
+}
+
+// ------------------------------------------------------------------ ckpt plan
+int kda_ckpt_plan(const int32_t* cu, const int32_t* start_pos, int32_t n_seq, int32_t interval,
+                  int32_t chunk, int32_t* ckpt_cu, int32_t* ckpt_pos, int32_t cap,
+                  int32_t* n_total) {
+  if (!cu || !ckpt_cu || !n_total) return fail(KDA_ERR_NULL, "ckpt_plan: required pointer is NULL");
+  if (n_seq < 0 || cap < 0) return fail(KDA_ERR_SHAPE, "ckpt_plan: negative size");
+  if (chunk != 16 && chunk != 32 && chunk != 64) return fail(KDA_ERR_UNSUPPORTED, "chunk %d", chunk);
+  if (interval <= 0 || interval % chunk != 0)
+    return fail(KDA_ERR_ALIGN, "interval %d not a positive multiple of chunk %d", interval, chunk);
+  int64_t total = 0;
+  ckpt_cu[0] = 0;
+  for (int s = 0; s < n_seq; ++s) {
+    const int64_t len = (int64_t)cu[s + 1] - cu[s];
+    const int64_t st = start_pos ? start_pos[s] : 0;
+    if (len < 0 || st < 0) return fail(KDA_ERR_SHAPE, "ckpt_plan: sequence %d has negative length or start", s);
+    const int64_t n = len > 0 ? (st + len - 1) / interval - st / interval : 0;
+    for (int64_t m = 0; m < n; ++m) {
+      const int64_t pos = (st / interval + 1 + m) * interval;
+      if (total + m < cap && ckpt_pos) ckpt_pos[total + m] = (int32_t)pos;
+    }
+    total += n;
+    if (total > 0x7fffffffLL) return fail(KDA_ERR_SHAPE, "ckpt_plan: too many checkpoints");
+    ckpt_cu[s + 1] = (int32_t)total;
+  }
+  *n_total = (int32_t)total;
+  if (total > cap) return fail(KDA_ERR_CAPACITY, "ckpt_plan: %lld checkpoints > cap %d", (long long)total, cap);
+  return KDA_OK;
+}
+
+// ------------------------------------------------------------------ decode / verify
+static int step_common(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                       void* o, int64_t& qs, int64_t& ks, int64_t& vs, int64_t& gs, int64_t& bs,
+                       int64_t& os, int H, int dk, int dv, int in_dt, int out_dt, float* pool,
+                       const int32_t* src, const int32_t* dst) {
+  if (in_dt != KDA_BF16 && in_dt != KDA_F32) return fail(KDA_ERR_DTYPE, "in_dtype %d", in_dt);
+  if (out_dt != KDA_BF16 && out_dt != KDA_F32) return fail(KDA_ERR_DTYPE, "out_dtype %d", out_dt);
+  if (H <= 0) return fail(KDA_ERR_SHAPE, "H = %d", H);
+  if (!supported_d(dk, dv)) return fail(KDA_ERR_UNSUPPORTED, "d_k = %d, d_v = %d (need equal, 16/32/64/128)", dk, dv);
+  if (!q || !k || !v || !g || !beta || !pool || !src || !dst) return fail(KDA_ERR_NULL, "required pointer is NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) || !aligned16(pool) || (o && !aligned16(o)))
+    return fail(KDA_ERR_ALIGN, "q, k, v, g, o or state_pool not 16-byte aligned");
+  int st;
+  if ((st = fix_stride(qs, (int64_t)H * dk, in_dt, "q"))) return st;
+  if ((st = fix_stride(ks, (int64_t)H * dk, in_dt, "k"))) return st;
+  if ((st = fix_stride(vs, (int64_t)H * dv, in_dt, "v"))) return st;
+  if ((st = fix_stride(gs, (int64_t)H * dk, in_dt, "g"))) return st;
+  if ((st = fix_stride(os, (int64_t)H * dv, out_dt, "o"))) return st;
+  if ((st = fix_beta_stride(bs, H))) return st;
+  return KDA_OK;
+}
+
+int kda_decode(const kda_decode_args* a, kda_stream_t stream_) {
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  if (!a) return fail(KDA_ERR_NULL, "args is NULL");
+  if (a->struct_size != sizeof(kda_decode_args)) return fail(KDA_ERR_ARG, "struct_size mismatch");
+  if (a->n_seq < 0 || a->n_slots < 0) return fail(KDA_ERR_SHAPE, "negative size");
+  if (a->n_seq == 0) return KDA_OK;
+  kda_decode_args b = *a;
+  if (!b.o) return fail(KDA_ERR_NULL, "decode: o is NULL");
+  int st = step_common(b.q, b.k, b.v, b.g, b.beta, b.o, b.q_stride, b.k_stride, b.v_stride, b.g_stride,
+                       b.beta_stride, b.o_stride, b.H, b.d_k, b.d_v, b.in_dtype, b.out_dtype, b.state_pool,
+                       b.src_slot, b.dst_slot);
+  if (st) return st;
+  if ((int64_t)b.n_seq * b.H > 0x7fffffffLL) return fail(KDA_ERR_SHAPE, "n_seq * H too large");
+  if (check_enabled()) {
+    st = check_slots(b.src_slot, b.dst_slot, b.n_seq, b.n_slots, nullptr, stream);
+    if (st) return st;
+  }
+  StepParams p{};
+  p.q = b.q; p.k = b.k; p.v = b.v; p.g = b.g; p.beta = b.beta; p.o = b.o; p.pool = b.state_pool;
+  p.src_slot = b.src_slot; p.dst_slot = b.dst_slot; p.accepted_len = nullptr; p.committed_len_out = nullptr;
+  p.q_stride = b.q_stride; p.k_stride = b.k_stride; p.v_stride = b.v_stride; p.g_stride = b.g_stride;
+  p.beta_stride = b.beta_stride; p.o_stride = b.o_stride; p.n_slots = b.n_slots;
+  p.n_seq = b.n_seq; p.T_spec = 1; p.H = b.H; p.commit_all = 1; p.scale = b.scale;
+  return launch_step(p, b.d_k, b.in_dtype, b.out_dtype, stream);
+}
+
+int kda_verify(const kda_verify_args* a, kda_stream_t stream_) {
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  if (!a) return fail(KDA_ERR_NULL, "args is NULL");
+  if (a->struct_size != sizeof(kda_verify_args)) return fail(KDA_ERR_ARG, "struct_size mismatch");
+  if (a->n_seq < 0 || a->n_slots < 0) return fail(KDA_ERR_SHAPE, "negative size");
+  if (a->T_spec < 1 || a->T_spec > 16) return fail(KDA_ERR_SHAPE, "T_spec = %d (1..16)", a->T_spec);
+  if (a->n_seq == 0) return KDA_OK;
+  kda_verify_args b = *a;
+  if (!b.o && !b.accepted_len) return fail(KDA_ERR_NULL, "verify: neither o nor accepted_len given");
+  int st = step_common(b.q, b.k, b.v, b.g, b.beta, b.o, b.q_stride, b.k_stride, b.v_stride, b.g_stride,
+                       b.beta_stride, b.o_stride, b.H, b.d_k, b.d_v, b.in_dtype, b.out_dtype, b.state_pool,
+                       b.src_slot, b.dst_slot);
+  if (st) return st;
+  if ((int64_t)b.n_seq * b.H > 0x7fffffffLL) return fail(KDA_ERR_SHAPE, "n_seq * H too large");
+  if (check_enabled()) {
+    st = check_slots(b.src_slot, b.dst_slot, b.n_seq, b.n_slots, nullptr, stream);
+    if (st) return st;
+  }
+  StepParams p{};
+  p.q = b.q; p.k = b.k; p.v = b.v; p.g = b.g; p.beta = b.beta; p.o = b.o; p.pool = b.state_pool;
+  p.src_slot = b.src_slot; p.dst_slot = b.dst_slot; p.accepted_len = b.accepted_len;
+  p.committed_len_out = b.committed_len_out;
+  p.q_stride = b.q_stride; p.k_stride = b.k_stride; p.v_stride = b.v_stride; p.g_stride = b.g_stride;
+  p.beta_stride = b.beta_stride; p.o_stride = b.o_stride; p.n_slots = b.n_slots;
+  p.n_seq = b.n_seq; p.T_spec = b.T_spec; p.H = b.H; p.commit_all = 0; p.scale = b.scale;
+  return launch_step(p, b.d_k, b.in_dtype, b.out_dtype, stream);
+}
+
+// ------------------------------------------------------------------ prefill
+static int prefill_validate(const kda_prefill_args* a, kda_prefill_args& b) {
+  if (!a) return fail(KDA_ERR_NULL, "args is NULL");
+  if (a->struct_size != sizeof(kda_prefill_args)) return fail(KDA_ERR_ARG, "struct_size mismatch");
+  if (a->n_seq < 0 || a->T_tot < 0 || a->n_slots < 0 || a->n_ckpt < 0 || a->workspace_bytes < 0)
+    return fail(KDA_ERR_SHAPE, "negative size");
+  b = *a;
+  if (b.chunk != 16 && b.chunk != 32 && b.chunk != 64) return fail(KDA_ERR_UNSUPPORTED, "chunk %d (16, 32, 64)", b.chunk);
+  if (b.ckpt_interval < 0) return fail(KDA_ERR_SHAPE, "ckpt_interval < 0");
+  if (b.ckpt_interval > 0 && b.ckpt_interval % b.chunk != 0)
+    return fail(KDA_ERR_ALIGN, "ckpt_interval %d not a multiple of chunk %d", b.ckpt_interval, b.chunk);
+  if (b.ckpt_interval > 0 && (!b.ckpt_cu || (b.n_ckpt > 0 && !b.ckpt_slot)))
+    return fail(KDA_ERR_NULL, "checkpoints requested without ckpt_cu / ckpt_slot");
+  if (!b.cu_seqlens) return fail(KDA_ERR_NULL, "cu_seqlens is NULL");
+  int st = step_common(b.q, b.k, b.v, b.g, b.beta, b.o, b.q_stride, b.k_stride, b.v_stride, b.g_stride,
+                       b.beta_stride, b.o_stride, b.H, b.d_k, b.d_v, b.in_dtype, b.out_dtype, b.state_pool,
+                       b.src_slot, b.dst_slot);
+  if (st) return st;
+  if (!b.o) return fail(KDA_ERR_NULL, "prefill: o is NULL");
+  return KDA_OK;
+}
+
+static PrefillParams prefill_params(const kda_prefill_args& b) {
+  PrefillParams p{};
+  p.q = b.q; p.k = b.k; p.v = b.v; p.g = b.g; p.beta = b.beta; p.o = b.o; p.cu = b.cu_seqlens;
+  p.pool = b.state_pool; p.src_slot = b.src_slot; p.dst_slot = b.dst_slot; p.start_pos = b.start_pos;
+  p.ckpt_cu = b.ckpt_interval > 0 ? b.ckpt_cu : nullptr; p.ckpt_slot = b.ckpt_slot;
+  p.ckpt_pos_out = b.ckpt_pos_out; p.workspace = b.workspace;
+  p.q_stride = b.q_stride; p.k_stride = b.k_stride; p.v_stride = b.v_stride; p.g_stride = b.g_stride;
+  p.beta_stride = b.beta_stride; p.o_stride = b.o_stride;
+  p.T_tot = b.T_tot; p.n_slots = b.n_slots; p.n_ckpt = b.n_ckpt; p.workspace_bytes = b.workspace_bytes;
+  p.n_seq = b.n_seq; p.H = b.H; p.chunk = b.chunk; p.ckpt_interval = b.ckpt_interval; p.scale = b.scale;
+  return p;
+}
+
+int64_t kda_prefill_workspace_bytes(const kda_prefill_args* a) {
+  kda_prefill_args b;
+  if (prefill_validate(a, b) != KDA_OK) return -1;
+  return prefill_workspace_bytes(prefill_params(b), b.d_k);
+}
+
+int kda_prefill_varlen(const kda_prefill_args* a, kda_stream_t stream_) {
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  kda_prefill_args b;
+  int st = prefill_validate(a, b);
+  if (st) return st;
+  if (b.n_seq == 0) return KDA_OK;
+  PrefillParams p = prefill_params(b);
+  const int64_t need = prefill_workspace_bytes(p, b.d_k);
+  if (need > 0 && (!b.workspace || b.workspace_bytes < need))
+    return fail(KDA_ERR_WORKSPACE, "workspace %lld bytes < %lld needed", (long long)b.workspace_bytes, (long long)need);
+  if (need > 0 && !aligned16(b.workspace)) return fail(KDA_ERR_ALIGN, "workspace not 16-byte aligned");
+  if (check_enabled()) {
+    std::vector<int32_t> hcu;
+    st = check_cu(b.cu_seqlens, b.n_seq, b.T_tot, stream, &hcu);
+    if (st) return st;
+    std::vector<int32_t> ck;
+    if (b.ckpt_interval > 0 && b.n_ckpt > 0) {
+      if (!copy_to_host(ck, b.ckpt_slot, (size_t)b.n_ckpt, stream)) return fail(KDA_ERR_HIP, "KDA_CHECK: copy failed");
+      for (int32_t c : ck)
+        if (c < -1 || c >= b.n_slots) return fail(KDA_ERR_ARG, "ckpt_slot %d out of range", c);
+    }
+    st = check_slots(b.src_slot, b.dst_slot, b.n_seq, b.n_slots, &ck, stream);
+    if (st) return st;
+  }
+  return launch_prefill(p, b.d_k, b.in_dtype, b.out_dtype, stream);
+}
+
+}  // extern "C"

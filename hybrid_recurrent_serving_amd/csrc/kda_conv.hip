@@ -1,0 +1,249 @@
+// Short causal depthwise convolution with carried state (the KDA layer's
+// q/k/v convolution; "Kimi K3 + vLLM: Inside the Day-0 Production
+// Integration", sections "Kimi Delta Attention: When Prefix Caching Meets
+// Recurrent State" and "Separate Prefill/Decode Code Paths").
+//
+//   y[t, c] = bias[c] + sum_{j<W} w[c, j] * xbar[t - (W-1) + j, c]   (+ SiLU)
+//
+// xbar = carried state (last W-1 raw inputs, oldest first) ++ tokens.
+//
+// Pure streaming: 2 x sizeof(T) bytes per element plus the state.  Each
+// thread owns VEC = 16 / sizeof(T) adjacent channels (one 16-byte vector per
+// token row), so a 256-thread workgroup reads 4 KiB (bf16) of one token row
+// per load instruction.
+//
+// Work items (blockIdx.x):
+//  * "head" item s < n_seq: the first min(len, W-1) tokens of sequence s
+//    (those that need the carried history) AND the new state.  Only this
+//    item reads the source slot and only it writes the destination slot, so
+//    updating a slot in place (src == dst) is race free.
+//  * "body" item n_seq + b: packed tokens [b*TT, (b+1)*TT), skipping each
+//    sequence's first W-1 tokens.  These only read x, with a sliding window
+//    of the previous W-1 rows in registers.
+
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+
+constexpr int CONV_TT = 64;      // tokens per body item
+constexpr int CONV_THREADS = 256;
+
+template <typename T> struct Vec16;
+template <> struct Vec16<bf16_t> {
+  static constexpr int N = 8;
+  __device__ static __forceinline__ void ld(const bf16_t* p, float (&x)[8]) {
+    uint4 t = *reinterpret_cast<const uint4*>(p);
+    uint32_t w[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = __uint_as_float(w[i] << 16);
+      x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+  __device__ static __forceinline__ void st(bf16_t* p, const float (&x)[8]) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = static_cast<uint32_t>(f32_to_bf16(x[2 * i])) |
+             (static_cast<uint32_t>(f32_to_bf16(x[2 * i + 1])) << 16);
+    *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+};
+template <> struct Vec16<float> {
+  static constexpr int N = 4;
+  __device__ static __forceinline__ void ld(const float* p, float (&x)[4]) { io<float>::ld4(p, x); }
+  __device__ static __forceinline__ void st(float* p, const float (&x)[4]) { io<float>::st4(p, x); }
+};
+
+__device__ __forceinline__ float conv_finish(float acc, int act) {
+  if (act == 1) acc = acc / (1.f + expf(-acc));
+  return acc;
+}
+
+template <typename T, int W>
+__global__ void __launch_bounds__(CONV_THREADS) conv_kernel(const ConvParams p) {
+  constexpr int V = Vec16<T>::N;
+  constexpr int HIST = W - 1;
+  const int item = blockIdx.x;
+  const int64_t c0 = (static_cast<int64_t>(blockIdx.y) * CONV_THREADS + threadIdx.x) * V;
+  if (c0 >= p.C) return;
+  const T* xb = static_cast<const T*>(p.x);
+  T* yb = static_cast<T*>(p.y);
+
+  // taps of my channels: wt[j][i] = w[c0 + i, j]
+  float wt[W][V];
+  {
+    const T* wp = static_cast<const T*>(p.w) + c0 * W;
+#pragma unroll
+    for (int i = 0; i < V; ++i)
+#pragma unroll
+      for (int j = 0; j < W; ++j) wt[j][i] = io<T>::ld(wp + i * W + j);
+  }
+  float bias[V];
+#pragma unroll
+  for (int i = 0; i < V; ++i) bias[i] = p.bias ? io<T>::ld(static_cast<const T*>(p.bias) + c0 + i) : 0.f;
+
+  if (item < p.n_seq) {
+    // ---------------- head item: tokens that need the history + new state
+    const int s = item;
+    int64_t bos = p.cu[s], eos = p.cu[s + 1];
+    bos = bos < 0 ? 0 : (bos > p.T_tot ? p.T_tot : bos);
+    eos = eos < bos ? bos : (eos > p.T_tot ? p.T_tot : eos);
+    const int64_t len = eos - bos;
+    const int src = p.src_slot[s];
+    const int dst = p.dst_slot[s];
+    const bool has_src = src >= 0 && src < p.n_slots;
+    const bool has_dst = dst >= 0 && dst < p.n_slots;
+    // xh[j] = xbar[j] for j < 2*HIST: history then the first HIST tokens
+    float xh[2 * HIST][V];
+    if (has_src) {
+      const T* sp = static_cast<const T*>(p.pool) + (static_cast<int64_t>(src) * p.C + c0) * HIST;
+#pragma unroll
+      for (int j = 0; j < HIST; ++j)
+#pragma unroll
+        for (int i = 0; i < V; ++i) xh[j][i] = io<T>::ld(sp + i * HIST + j);
+    } else {
+#pragma unroll
+      for (int j = 0; j < HIST; ++j)
+#pragma unroll
+        for (int i = 0; i < V; ++i) xh[j][i] = 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < HIST; ++j) {
+      if (j < len) {
+        Vec16<T>::ld(xb + (bos + j) * p.x_stride + c0, xh[HIST + j]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < V; ++i) xh[HIST + j][i] = 0.f;
+      }
+    }
+    // new state = xbar[a .. a + HIST), a = advance length clamped to [0, len]
+    int64_t a = p.adv ? static_cast<int64_t>(p.adv[s]) : len;
+    a = a < 0 ? 0 : (a > len ? len : a);
+    float ns[HIST][V];
+#pragma unroll
+    for (int j = 0; j < HIST; ++j) {
+      const int64_t idx = a + j;
+      if (idx < 2 * HIST) {
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+          float val = 0.f;
+#pragma unroll
+          for (int q = 0; q < 2 * HIST; ++q) val = (q == idx) ? xh[q][i] : val;
+          ns[j][i] = val;
+        }
+      } else {
+        Vec16<T>::ld(xb + (bos + idx - HIST) * p.x_stride + c0, ns[j]);
+      }
+    }
+    // outputs of the first min(len, HIST) tokens
+#pragma unroll
+    for (int t = 0; t < HIST; ++t) {
+      if (t < len) {
+        float out[V];
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+          float acc = bias[i];
+#pragma unroll
+          for (int j = 0; j < W; ++j) acc = fmaf(wt[j][i], xh[t + j][i], acc);
+          out[i] = conv_finish(acc, p.act);
+        }
+        Vec16<T>::st(yb + (bos + t) * p.y_stride + c0, out);
+      }
+    }
+    if (has_dst) {
+      T* dp = static_cast<T*>(p.pool) + (static_cast<int64_t>(dst) * p.C + c0) * HIST;
+#pragma unroll
+      for (int j = 0; j < HIST; ++j)
+#pragma unroll
+        for (int i = 0; i < V; ++i) io<T>::st(dp + i * HIST + j, ns[j][i]);
+    }
+    return;
+  }
+
+  // ---------------- body item: packed tokens [t0, t1)
+  const int64_t t0 = static_cast<int64_t>(item - p.n_seq) * CONV_TT;
+  if (t0 >= p.T_tot) return;
+  const int64_t t1 = t0 + CONV_TT < p.T_tot ? t0 + CONV_TT : p.T_tot;
+  // sequence containing t0: the last s with cu[s] <= t0
+  int lo = 0, hi = p.n_seq;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (p.cu[mid] <= t0) lo = mid; else hi = mid;
+  }
+  int s = lo;
+  int64_t bos = p.cu[s], eos = p.cu[s + 1];
+  float win[HIST][V];  // rows t-HIST .. t-1
+  bool have_win = false;
+  for (int64_t t = t0; t < t1; ++t) {
+    while (t >= eos && s < p.n_seq - 1) {
+      ++s;
+      bos = p.cu[s];
+      eos = p.cu[s + 1];
+      have_win = false;
+    }
+    if (t < bos || t >= eos || t - bos < HIST) {
+      have_win = false;
+      continue;
+    }
+    if (!have_win) {
+#pragma unroll
+      for (int j = 0; j < HIST; ++j) Vec16<T>::ld(xb + (t - HIST + j) * p.x_stride + c0, win[j]);
+      have_win = true;
+    }
+    float cur[V];
+    Vec16<T>::ld(xb + t * p.x_stride + c0, cur);
+    float out[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      float acc = bias[i];
+#pragma unroll
+      for (int j = 0; j < HIST; ++j) acc = fmaf(wt[j][i], win[j][i], acc);
+      acc = fmaf(wt[HIST][i], cur[i], acc);
+      out[i] = conv_finish(acc, p.act);
+    }
+    Vec16<T>::st(yb + t * p.y_stride + c0, out);
+#pragma unroll
+    for (int j = 0; j + 1 < HIST; ++j)
+#pragma unroll
+      for (int i = 0; i < V; ++i) win[j][i] = win[j + 1][i];
+#pragma unroll
+    for (int i = 0; i < V; ++i) win[HIST - 1][i] = cur[i];
+  }
+}
+
+template <typename T, int W>
+static int launch_conv_t(const ConvParams& p, hipStream_t stream) {
+  constexpr int V = 16 / sizeof(T);
+  const int64_t groups = (p.C + V - 1) / V;
+  dim3 grid(static_cast<uint32_t>(p.n_seq + p.n_tiles),
+            static_cast<uint32_t>((groups + CONV_THREADS - 1) / CONV_THREADS));
+  hipLaunchKernelGGL((conv_kernel<T, W>), grid, dim3(CONV_THREADS), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, "conv kernel launch: %s", hipGetErrorString(e));
+  return KDA_OK;
+}
+
+template <typename T>
+static int launch_conv_w(const ConvParams& p, hipStream_t stream) {
+  switch (p.W) {
+    case 2: return launch_conv_t<T, 2>(p, stream);
+    case 3: return launch_conv_t<T, 3>(p, stream);
+    case 4: return launch_conv_t<T, 4>(p, stream);
+    case 5: return launch_conv_t<T, 5>(p, stream);
+    case 6: return launch_conv_t<T, 6>(p, stream);
+    case 7: return launch_conv_t<T, 7>(p, stream);
+    case 8: return launch_conv_t<T, 8>(p, stream);
+    default: return fail(KDA_ERR_UNSUPPORTED, "conv width W = %d not built (2..8)", p.W);
+  }
+}
+
+int launch_conv(const ConvParams& p0, int dtype, hipStream_t stream) {
+  ConvParams p = p0;
+  p.n_tiles = static_cast<int32_t>((p.T_tot + CONV_TT - 1) / CONV_TT);
+  if (dtype == KDA_BF16) return launch_conv_w<bf16_t>(p, stream);
+  return launch_conv_w<float>(p, stream);
+}
+
+}  // namespace kda

@@ -1,0 +1,76 @@
+// Device-side helpers shared by the libkda kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+typedef uint16_t bf16_t;  // raw bfloat16 bits
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// fp32 -> bf16, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<bf16_t>(u >> 16);
+}
+
+template <typename T> struct io;
+
+template <> struct io<float> {
+  __device__ static __forceinline__ float ld(const float* p) { return *p; }
+  __device__ static __forceinline__ void st(float* p, float x) { *p = x; }
+  // load 4 consecutive elements (16-byte aligned for float)
+  __device__ static __forceinline__ void ld4(const float* p, float (&x)[4]) {
+    float4 t = *reinterpret_cast<const float4*>(p);
+    x[0] = t.x; x[1] = t.y; x[2] = t.z; x[3] = t.w;
+  }
+  __device__ static __forceinline__ void st4(float* p, const float (&x)[4]) {
+    *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
+  }
+};
+
+template <> struct io<bf16_t> {
+  __device__ static __forceinline__ float ld(const bf16_t* p) { return bf16_to_f32(*p); }
+  __device__ static __forceinline__ void st(bf16_t* p, float x) { *p = f32_to_bf16(x); }
+  // 4 consecutive elements = 8 bytes (8-byte aligned)
+  __device__ static __forceinline__ void ld4(const bf16_t* p, float (&x)[4]) {
+    uint2 t = *reinterpret_cast<const uint2*>(p);
+    x[0] = __uint_as_float(t.x << 16);
+    x[1] = __uint_as_float(t.x & 0xffff0000u);
+    x[2] = __uint_as_float(t.y << 16);
+    x[3] = __uint_as_float(t.y & 0xffff0000u);
+  }
+  __device__ static __forceinline__ void st4(bf16_t* p, const float (&x)[4]) {
+    uint2 t;
+    t.x = static_cast<uint32_t>(f32_to_bf16(x[0])) | (static_cast<uint32_t>(f32_to_bf16(x[1])) << 16);
+    t.y = static_cast<uint32_t>(f32_to_bf16(x[2])) | (static_cast<uint32_t>(f32_to_bf16(x[3])) << 16);
+    *reinterpret_cast<uint2*>(p) = t;
+  }
+};
+
+// Load n consecutive elements (n a multiple of 4) as floats.
+template <typename T, int N>
+__device__ __forceinline__ void ld_vec(const T* p, float (&x)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; i += 4) {
+    float t[4];
+    io<T>::ld4(p + i, t);
+    x[i] = t[0]; x[i + 1] = t[1]; x[i + 2] = t[2]; x[i + 3] = t[3];
+  }
+}
+
+// Sum over the lanes that differ only in bits >= log2(FIRST) of the lane id.
+template <int FIRST>
+__device__ __forceinline__ float wave_sum_from(float x) {
+#pragma unroll
+  for (int m = FIRST; m < 64; m <<= 1) x += __shfl_xor(x, m, 64);
+  return x;
+}
+
+}  // namespace kda

@@ -1,0 +1,67 @@
+// Host-side internals of libkda: kernel parameter blocks and launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/kda.h"
+
+namespace kda {
+
+// Record a one-line reason for the calling thread's last failure.
+int fail(int status, const char* fmt, ...);
+
+// ---------------------------------------------------------------- recurrent
+// One pass of the token recurrence on register-resident state tiles; serves
+// kda_decode (T_spec = 1) and kda_verify.
+struct StepParams {
+  const void *q, *k, *v, *g, *beta;
+  void* o;                        // NULL: no outputs
+  float* pool;
+  const int32_t *src_slot, *dst_slot;
+  const int32_t* accepted_len;    // NULL: no commit (outputs only) unless commit_all
+  int32_t* committed_len_out;
+  int64_t q_stride, k_stride, v_stride, g_stride, beta_stride, o_stride;  // per token
+  int64_t n_slots;
+  int32_t n_seq, T_spec, H;
+  int32_t commit_all;             // decode: store after T_spec tokens
+  float scale;
+};
+
+int launch_step(const StepParams& p, int D, int in_dtype, int out_dtype, hipStream_t stream);
+
+// ---------------------------------------------------------------- conv
+struct ConvParams {
+  const void* x;
+  void* y;
+  const void* w;
+  const void* bias;
+  const int32_t* cu;
+  void* pool;
+  const int32_t *src_slot, *dst_slot, *adv;
+  int64_t x_stride, y_stride, T_tot, n_slots;
+  int32_t n_seq, C, W, act;
+  int32_t n_tiles;                // body tiles of TT tokens
+};
+
+int launch_conv(const ConvParams& p, int dtype, hipStream_t stream);
+
+// ---------------------------------------------------------------- prefill
+struct PrefillParams {
+  const void *q, *k, *v, *g, *beta;
+  void* o;
+  const int32_t* cu;
+  float* pool;
+  const int32_t *src_slot, *dst_slot, *start_pos, *ckpt_cu, *ckpt_slot;
+  int32_t* ckpt_pos_out;
+  void* workspace;
+  int64_t q_stride, k_stride, v_stride, g_stride, beta_stride, o_stride;
+  int64_t T_tot, n_slots, n_ckpt, workspace_bytes;
+  int32_t n_seq, H, chunk, ckpt_interval;
+  float scale;
+};
+
+int64_t prefill_workspace_bytes(const PrefillParams& p, int D);
+int launch_prefill(const PrefillParams& p, int D, int in_dtype, int out_dtype, hipStream_t stream);
+
+}  // namespace kda

@@ -1,0 +1,182 @@
+// Token-by-token KDA recurrence on register-resident fp32 state tiles:
+// the decode step (one token per sequence, state updated in place) and
+// speculative verification (T_spec tokens, commit at the accepted length).
+//
+// Decode and verify are bound by HBM: per (sequence, head) the whole
+// d_k x d_v fp32 state is read once and written at most once, and there are
+// only ~1-7 flops per state byte.  Each wavefront owns a COLS-wide column
+// slice of one head's state (all d_k rows): lane (rg, cg) holds rows
+// [rg*RPL, rg*RPL + RPL) x columns [4cg, 4cg + 4) of the slice, loaded and
+// stored as 16-byte vectors, so one load instruction covers RG rows x
+// (COLS * 4) contiguous bytes.  The reductions over key channels
+// (S^T k and S^T q) only cross lanes of the same wave (shuffles), so the
+// waves of a head never synchronise.
+//
+// Recurrence (per token, decay first, correction against the decayed state,
+// output from the updated state):
+//     S <- Diag(exp g) S;  w = S^T k;  S <- S + beta k (v - w)^T;  o = scale S^T q
+// which is (I - beta k k^T) Diag(alpha) S + beta k v^T followed by
+// o = S^T q ("Kimi K3 + vLLM: Inside the Day-0 Production Integration",
+// section "Kimi Delta Attention: When Prefix Caching Meets Recurrent State",
+// describes the fixed-size matrix state; the update rule is the gated delta
+// rule with per-key-channel decay).
+
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+
+template <int D>
+struct StepLayout {
+  static constexpr int COLS = D < 32 ? D : 32;  // columns per wave
+  static constexpr int LPR = COLS / 4;          // lanes per row (4 columns each)
+  static constexpr int RG = 64 / LPR;           // row groups per wave
+  static constexpr int RPL = D / RG;            // rows per lane
+  static constexpr int WPH = D / COLS;          // waves per head
+  static_assert(RPL >= 1 && RPL * RG == D, "layout");
+};
+
+template <int D, typename Tin, typename Tout>
+__global__ void __launch_bounds__(64 * StepLayout<D>::WPH)
+step_kernel(const StepParams p) {
+  using L = StepLayout<D>;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t sh = blockIdx.x;
+  const int s = static_cast<int>(sh / p.H);
+  const int h = static_cast<int>(sh % p.H);
+  const int cg = lane % L::LPR;
+  const int rg = lane / L::LPR;
+  const int col = wave * L::COLS + 4 * cg;
+  const int row0 = rg * L::RPL;
+
+  const int src = p.src_slot[s];
+  const int dst = p.dst_slot[s];
+  const bool has_src = src >= 0 && src < p.n_slots;
+  const bool has_dst = dst >= 0 && dst < p.n_slots;
+
+  // commit bookkeeping: Lc = number of tokens after which the state is stored
+  int Lc = -1;
+  bool valid = false;
+  if (p.commit_all) {
+    Lc = p.T_spec;
+    valid = true;
+  } else if (p.accepted_len) {
+    Lc = p.accepted_len[s];
+    valid = Lc >= 0 && Lc <= p.T_spec;
+    if (h == 0 && threadIdx.x == 0 && p.committed_len_out) p.committed_len_out[s] = valid ? Lc : -1;
+  }
+  const bool do_store = valid && has_dst;
+  const int n_tok = p.o ? p.T_spec : (valid ? Lc : 0);
+
+  float S[L::RPL][4];
+  if (has_src) {
+    const float* sp = p.pool + ((static_cast<int64_t>(src) * p.H + h) * D + row0) * D + col;
+#pragma unroll
+    for (int i = 0; i < L::RPL; ++i) io<float>::ld4(sp + static_cast<int64_t>(i) * D, S[i]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < L::RPL; ++i) S[i][0] = S[i][1] = S[i][2] = S[i][3] = 0.f;
+  }
+  float* dp = has_dst ? p.pool + ((static_cast<int64_t>(dst) * p.H + h) * D + row0) * D + col : nullptr;
+  if (do_store && Lc == 0) {
+#pragma unroll
+    for (int i = 0; i < L::RPL; ++i) io<float>::st4(dp + static_cast<int64_t>(i) * D, S[i]);
+  }
+
+  const Tin* qb = static_cast<const Tin*>(p.q);
+  const Tin* kb = static_cast<const Tin*>(p.k);
+  const Tin* vb = static_cast<const Tin*>(p.v);
+  const Tin* gb = static_cast<const Tin*>(p.g);
+  const Tin* bb = static_cast<const Tin*>(p.beta);
+
+  for (int j = 0; j < n_tok; ++j) {
+    const int64_t tok = static_cast<int64_t>(s) * p.T_spec + j;
+    float kr[L::RPL], qr[L::RPL], gr[L::RPL], vc[4];
+    if constexpr (L::RPL >= 4) {
+      ld_vec<Tin, L::RPL>(kb + tok * p.k_stride + static_cast<int64_t>(h) * D + row0, kr);
+      ld_vec<Tin, L::RPL>(qb + tok * p.q_stride + static_cast<int64_t>(h) * D + row0, qr);
+      ld_vec<Tin, L::RPL>(gb + tok * p.g_stride + static_cast<int64_t>(h) * D + row0, gr);
+    } else {
+#pragma unroll
+      for (int i = 0; i < L::RPL; ++i) {
+        kr[i] = io<Tin>::ld(kb + tok * p.k_stride + static_cast<int64_t>(h) * D + row0 + i);
+        qr[i] = io<Tin>::ld(qb + tok * p.q_stride + static_cast<int64_t>(h) * D + row0 + i);
+        gr[i] = io<Tin>::ld(gb + tok * p.g_stride + static_cast<int64_t>(h) * D + row0 + i);
+      }
+    }
+    io<Tin>::ld4(vb + tok * p.v_stride + static_cast<int64_t>(h) * D + col, vc);
+    const float beta = io<Tin>::ld(bb + tok * p.beta_stride + h);
+
+    // Diag(alpha) S and the partial prediction S^T k over this lane's rows
+    float w[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < L::RPL; ++i) {
+      const float a = expf(gr[i]);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        S[i][c] *= a;
+        w[c] = fmaf(S[i][c], kr[i], w[c]);
+      }
+    }
+    float u[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      w[c] = wave_sum_from<L::LPR>(w[c]);
+      u[c] = beta * (vc[c] - w[c]);
+    }
+    // rank-1 correction and the output read-out from the updated state
+    float o[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < L::RPL; ++i) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        S[i][c] = fmaf(kr[i], u[c], S[i][c]);
+        o[c] = fmaf(S[i][c], qr[i], o[c]);
+      }
+    }
+    if (p.o) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) o[c] = wave_sum_from<L::LPR>(o[c]) * p.scale;
+      if (rg == 0) {
+        Tout* ob = static_cast<Tout*>(p.o) + tok * p.o_stride + static_cast<int64_t>(h) * D + col;
+        io<Tout>::st4(ob, o);
+      }
+    }
+    if (do_store && j + 1 == Lc) {
+#pragma unroll
+      for (int i = 0; i < L::RPL; ++i) io<float>::st4(dp + static_cast<int64_t>(i) * D, S[i]);
+    }
+  }
+}
+
+template <int D, typename Tin, typename Tout>
+static int launch_step_t(const StepParams& p, hipStream_t stream) {
+  using L = StepLayout<D>;
+  dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(p.n_seq) * p.H));
+  dim3 block(64 * L::WPH);
+  hipLaunchKernelGGL((step_kernel<D, Tin, Tout>), grid, block, 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, "step kernel launch: %s", hipGetErrorString(e));
+  return KDA_OK;
+}
+
+template <int D>
+static int launch_step_d(const StepParams& p, int in_dtype, int out_dtype, hipStream_t stream) {
+  if (in_dtype == KDA_BF16 && out_dtype == KDA_BF16) return launch_step_t<D, bf16_t, bf16_t>(p, stream);
+  if (in_dtype == KDA_BF16 && out_dtype == KDA_F32) return launch_step_t<D, bf16_t, float>(p, stream);
+  if (in_dtype == KDA_F32 && out_dtype == KDA_BF16) return launch_step_t<D, float, bf16_t>(p, stream);
+  return launch_step_t<D, float, float>(p, stream);
+}
+
+int launch_step(const StepParams& p, int D, int in_dtype, int out_dtype, hipStream_t stream) {
+  switch (D) {
+    case 16: return launch_step_d<16>(p, in_dtype, out_dtype, stream);
+    case 32: return launch_step_d<32>(p, in_dtype, out_dtype, stream);
+    case 64: return launch_step_d<64>(p, in_dtype, out_dtype, stream);
+    case 128: return launch_step_d<128>(p, in_dtype, out_dtype, stream);
+    default: return fail(KDA_ERR_UNSUPPORTED, "d = %d not built (16, 32, 64, 128)", D);
+  }
+}
+
+}  // namespace kda

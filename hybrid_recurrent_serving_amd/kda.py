@@ -1,0 +1,304 @@
+"""Thin ctypes binding of libkda (``include/kda.h``).
+
+Argument marshalling only: each function fills the C argument struct from
+torch tensors (device memory owned by torch) and calls the library on the
+current HIP stream.  Every step of the computation runs in libkda's HIP
+kernels; there is no fallback.  A non-OK status raises :class:`KDAError`.
+"""
+
+from __future__ import annotations
+
+import ctypes
+from pathlib import Path
+from typing import Optional
+
+PKG = Path(__file__).resolve().parent
+LIB_PATH = PKG / "libkda.so"
+
+KDA_BF16, KDA_F32 = 0, 1
+KDA_OK = 0
+
+c_vp = ctypes.c_void_p
+c_i32 = ctypes.c_int32
+c_i64 = ctypes.c_int64
+c_f32 = ctypes.c_float
+c_size = ctypes.c_size_t
+
+
+class KDAError(RuntimeError):
+    def __init__(self, status: int, name: str, detail: str):
+        super().__init__(f"{name}: {detail}")
+        self.status = status
+        self.name = name
+
+
+class ConvArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", c_size),
+        ("x", c_vp), ("y", c_vp), ("weight", c_vp), ("bias", c_vp), ("cu_seqlens", c_vp),
+        ("conv_pool", c_vp), ("src_slot", c_vp), ("dst_slot", c_vp), ("advance_len", c_vp),
+        ("x_stride", c_i64), ("y_stride", c_i64), ("T_tot", c_i64), ("n_slots", c_i64),
+        ("n_seq", c_i32), ("C", c_i32), ("W", c_i32), ("dtype", c_i32), ("act", c_i32),
+        ("reserved", c_i32),
+    ]
+
+
+class PrefillArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", c_size),
+        ("q", c_vp), ("k", c_vp), ("v", c_vp), ("g", c_vp), ("beta", c_vp), ("o", c_vp),
+        ("cu_seqlens", c_vp), ("state_pool", c_vp), ("src_slot", c_vp), ("dst_slot", c_vp),
+        ("start_pos", c_vp), ("ckpt_cu", c_vp), ("ckpt_slot", c_vp), ("ckpt_pos_out", c_vp),
+        ("workspace", c_vp),
+        ("q_stride", c_i64), ("k_stride", c_i64), ("v_stride", c_i64), ("g_stride", c_i64),
+        ("beta_stride", c_i64), ("o_stride", c_i64),
+        ("T_tot", c_i64), ("n_slots", c_i64), ("workspace_bytes", c_i64), ("n_ckpt", c_i64),
+        ("n_seq", c_i32), ("H", c_i32), ("d_k", c_i32), ("d_v", c_i32), ("chunk", c_i32),
+        ("in_dtype", c_i32), ("out_dtype", c_i32), ("ckpt_interval", c_i32), ("scale", c_f32),
+        ("reserved", c_i32),
+    ]
+
+
+class DecodeArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", c_size),
+        ("q", c_vp), ("k", c_vp), ("v", c_vp), ("g", c_vp), ("beta", c_vp), ("o", c_vp),
+        ("state_pool", c_vp), ("src_slot", c_vp), ("dst_slot", c_vp),
+        ("q_stride", c_i64), ("k_stride", c_i64), ("v_stride", c_i64), ("g_stride", c_i64),
+        ("beta_stride", c_i64), ("o_stride", c_i64), ("n_slots", c_i64),
+        ("n_seq", c_i32), ("H", c_i32), ("d_k", c_i32), ("d_v", c_i32),
+        ("in_dtype", c_i32), ("out_dtype", c_i32), ("scale", c_f32), ("reserved", c_i32),
+    ]
+
+
+class VerifyArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", c_size),
+        ("q", c_vp), ("k", c_vp), ("v", c_vp), ("g", c_vp), ("beta", c_vp), ("o", c_vp),
+        ("state_pool", c_vp), ("src_slot", c_vp), ("dst_slot", c_vp), ("accepted_len", c_vp),
+        ("committed_len_out", c_vp),
+        ("q_stride", c_i64), ("k_stride", c_i64), ("v_stride", c_i64), ("g_stride", c_i64),
+        ("beta_stride", c_i64), ("o_stride", c_i64), ("n_slots", c_i64),
+        ("n_seq", c_i32), ("T_spec", c_i32), ("H", c_i32), ("d_k", c_i32), ("d_v", c_i32),
+        ("in_dtype", c_i32), ("out_dtype", c_i32), ("scale", c_f32),
+    ]
+
+
+EXPORTS = ["kda_status_str", "kda_abi_version", "kda_last_error", "kda_args_sizeof",
+           "kda_conv_short", "kda_ckpt_plan", "kda_prefill_workspace_bytes",
+           "kda_prefill_varlen", "kda_decode", "kda_verify"]
+
+_lib = None
+
+
+def load_library(path: Optional[Path] = None):
+    """Load libkda.so (built by ``hybrid_recurrent_serving_amd.build``).
+
+    Raises FileNotFoundError when it is missing: the library is the only
+    implementation, there is nothing to fall back to.
+    """
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = Path(path) if path else LIB_PATH
+    if not p.exists():
+        raise FileNotFoundError(f"{p} is missing; build it with "
+                                "`python -m hybrid_recurrent_serving_amd.build`")
+    lib = ctypes.CDLL(str(p))
+    lib.kda_status_str.restype = ctypes.c_char_p
+    lib.kda_status_str.argtypes = [ctypes.c_int]
+    lib.kda_abi_version.restype = ctypes.c_int
+    lib.kda_last_error.restype = ctypes.c_char_p
+    lib.kda_args_sizeof.restype = c_size
+    lib.kda_args_sizeof.argtypes = [ctypes.c_int]
+    lib.kda_conv_short.argtypes = [ctypes.POINTER(ConvArgs), c_vp]
+    lib.kda_ckpt_plan.argtypes = [c_vp, c_vp, c_i32, c_i32, c_i32, c_vp, c_vp, c_i32, c_vp]
+    lib.kda_prefill_workspace_bytes.restype = c_i64
+    lib.kda_prefill_workspace_bytes.argtypes = [ctypes.POINTER(PrefillArgs)]
+    lib.kda_prefill_varlen.argtypes = [ctypes.POINTER(PrefillArgs), c_vp]
+    lib.kda_decode.argtypes = [ctypes.POINTER(DecodeArgs), c_vp]
+    lib.kda_verify.argtypes = [ctypes.POINTER(VerifyArgs), c_vp]
+    for name in ("kda_conv_short", "kda_ckpt_plan", "kda_prefill_varlen", "kda_decode", "kda_verify"):
+        getattr(lib, name).restype = ctypes.c_int
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _check(status: int, lib=None):
+    if status != KDA_OK:
+        lib = lib or load_library()
+        raise KDAError(status, lib.kda_status_str(status).decode(), lib.kda_last_error().decode())
+
+
+# --------------------------------------------------------------------- helpers
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return KDA_BF16
+    if t.dtype == torch.float32:
+        return KDA_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _tok_stride(t, inner_dims: int) -> int:
+    """Element distance between consecutive tokens; the inner dims must be
+    packed."""
+    if t is None:
+        return 0
+    st = t.stride()
+    exp = 1
+    for d in range(t.dim() - 1, t.dim() - 1 - inner_dims, -1):
+        if st[d] != exp:
+            raise ValueError("inner [H, d] block must be contiguous")
+        exp *= t.shape[d]
+    return st[t.dim() - 1 - inner_dims]
+
+
+def _stream(stream) -> int:
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+# --------------------------------------------------------------------- API
+def kda_status_str(status: int) -> str:
+    return load_library().kda_status_str(status).decode()
+
+
+def kda_abi_version() -> int:
+    return load_library().kda_abi_version()
+
+
+def kda_last_error() -> str:
+    return load_library().kda_last_error().decode()
+
+
+def kda_args_sizeof(which: int) -> int:
+    return load_library().kda_args_sizeof(which)
+
+
+def kda_conv_short(x, weight, cu_seqlens, conv_pool, src_slot, dst_slot, *, y=None, bias=None,
+                   act: int = 0, advance_len=None, stream=None):
+    """Short causal conv.  x [T, C]; weight [C, W]; conv_pool [S, C, W-1].
+    Returns y (allocated by torch when not given)."""
+    import torch
+    if y is None:
+        y = torch.empty_like(x)
+    a = ConvArgs()
+    a.struct_size = ctypes.sizeof(ConvArgs)
+    a.x, a.y, a.weight, a.bias = _ptr(x), _ptr(y), _ptr(weight), _ptr(bias)
+    a.cu_seqlens, a.conv_pool = _ptr(cu_seqlens), _ptr(conv_pool)
+    a.src_slot, a.dst_slot, a.advance_len = _ptr(src_slot), _ptr(dst_slot), _ptr(advance_len)
+    a.x_stride, a.y_stride = x.stride(0), y.stride(0)
+    a.T_tot, a.n_slots = x.shape[0], conv_pool.shape[0]
+    a.n_seq, a.C, a.W = cu_seqlens.numel() - 1, x.shape[1], weight.shape[1]
+    a.dtype, a.act = _dtype_code(x), act
+    _check(load_library().kda_conv_short(ctypes.byref(a), _stream(stream)))
+    return y
+
+
+def kda_ckpt_plan(cu_seqlens, interval: int, chunk: int, start_pos=None):
+    """Host checkpoint plan.  cu_seqlens / start_pos: host int sequences.
+    Returns (ckpt_cu list, ckpt_pos list)."""
+    import numpy as np
+    cu = np.ascontiguousarray(np.asarray(cu_seqlens, np.int32))
+    sp = None if start_pos is None else np.ascontiguousarray(np.asarray(start_pos, np.int32))
+    n = cu.size - 1
+    ck_cu = np.zeros(n + 1, np.int32)
+    total = ctypes.c_int32(0)
+    lib = load_library()
+    vp = lambda a: None if a is None else a.ctypes.data_as(c_vp)  # noqa: E731
+    st = lib.kda_ckpt_plan(vp(cu), vp(sp), n, int(interval), int(chunk), vp(ck_cu), None, 0,
+                           ctypes.byref(total))
+    if st not in (KDA_OK, 9):
+        _check(st, lib)
+    pos = np.zeros(max(total.value, 1), np.int32)
+    _check(lib.kda_ckpt_plan(vp(cu), vp(sp), n, int(interval), int(chunk), vp(ck_cu), vp(pos),
+                             total.value, ctypes.byref(total)), lib)
+    return ck_cu.tolist(), pos[:total.value].tolist()
+
+
+def _prefill_args(q, k, v, g, beta, o, cu_seqlens, state_pool, src_slot, dst_slot, chunk,
+                  start_pos, ckpt_interval, ckpt_cu, ckpt_slot, ckpt_pos_out, workspace, scale):
+    a = PrefillArgs()
+    a.struct_size = ctypes.sizeof(PrefillArgs)
+    a.q, a.k, a.v, a.g, a.beta, a.o = map(_ptr, (q, k, v, g, beta, o))
+    a.cu_seqlens, a.state_pool = _ptr(cu_seqlens), _ptr(state_pool)
+    a.src_slot, a.dst_slot, a.start_pos = _ptr(src_slot), _ptr(dst_slot), _ptr(start_pos)
+    a.ckpt_cu, a.ckpt_slot, a.ckpt_pos_out = _ptr(ckpt_cu), _ptr(ckpt_slot), _ptr(ckpt_pos_out)
+    a.workspace = _ptr(workspace)
+    a.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    a.q_stride, a.k_stride, a.v_stride = _tok_stride(q, 2), _tok_stride(k, 2), _tok_stride(v, 2)
+    a.g_stride, a.beta_stride, a.o_stride = _tok_stride(g, 2), _tok_stride(beta, 1), _tok_stride(o, 2)
+    a.T_tot, a.n_slots = q.shape[0], state_pool.shape[0]
+    a.n_ckpt = 0 if ckpt_slot is None else ckpt_slot.numel()
+    a.n_seq, a.H, a.d_k, a.d_v = cu_seqlens.numel() - 1, q.shape[1], q.shape[2], v.shape[2]
+    a.chunk = chunk
+    a.in_dtype, a.out_dtype = _dtype_code(q), _dtype_code(o)
+    a.ckpt_interval, a.scale = ckpt_interval, scale
+    return a
+
+
+def kda_prefill_workspace_bytes(q, k, v, g, beta, o, cu_seqlens, state_pool, src_slot, dst_slot,
+                                *, chunk=64, start_pos=None, ckpt_interval=0, ckpt_cu=None,
+                                ckpt_slot=None, scale=1.0) -> int:
+    a = _prefill_args(q, k, v, g, beta, o, cu_seqlens, state_pool, src_slot, dst_slot, chunk,
+                      start_pos, ckpt_interval, ckpt_cu, ckpt_slot, None, None, scale)
+    n = load_library().kda_prefill_workspace_bytes(ctypes.byref(a))
+    if n < 0:
+        raise KDAError(8, "KDA_ERR_ARG", kda_last_error())
+    return n
+
+
+def kda_prefill_varlen(q, k, v, g, beta, o, cu_seqlens, state_pool, src_slot, dst_slot, *,
+                       chunk=64, start_pos=None, ckpt_interval=0, ckpt_cu=None, ckpt_slot=None,
+                       ckpt_pos_out=None, workspace=None, scale=1.0, stream=None):
+    """Chunked varlen prefill; see include/kda.h for the argument contract."""
+    a = _prefill_args(q, k, v, g, beta, o, cu_seqlens, state_pool, src_slot, dst_slot, chunk,
+                      start_pos, ckpt_interval, ckpt_cu, ckpt_slot, ckpt_pos_out, workspace, scale)
+    _check(load_library().kda_prefill_varlen(ctypes.byref(a), _stream(stream)))
+    return o
+
+
+def kda_decode(q, k, v, g, beta, o, state_pool, src_slot, dst_slot, *, scale=1.0, stream=None):
+    """One token per sequence.  q, k, v, g [N, H, d]; beta [N, H]; o [N, H, d]."""
+    a = DecodeArgs()
+    a.struct_size = ctypes.sizeof(DecodeArgs)
+    a.q, a.k, a.v, a.g, a.beta, a.o = map(_ptr, (q, k, v, g, beta, o))
+    a.state_pool, a.src_slot, a.dst_slot = _ptr(state_pool), _ptr(src_slot), _ptr(dst_slot)
+    a.q_stride, a.k_stride, a.v_stride = _tok_stride(q, 2), _tok_stride(k, 2), _tok_stride(v, 2)
+    a.g_stride, a.beta_stride, a.o_stride = _tok_stride(g, 2), _tok_stride(beta, 1), _tok_stride(o, 2)
+    a.n_slots = state_pool.shape[0]
+    a.n_seq, a.H, a.d_k, a.d_v = q.shape[0], q.shape[1], q.shape[2], v.shape[2]
+    a.in_dtype, a.out_dtype, a.scale = _dtype_code(q), _dtype_code(o), scale
+    _check(load_library().kda_decode(ctypes.byref(a), _stream(stream)))
+    return o
+
+
+def kda_verify(q, k, v, g, beta, state_pool, src_slot, dst_slot, *, o=None, accepted_len=None,
+               committed_len_out=None, scale=1.0, stream=None):
+    """Speculative verify.  q, k, v, g [N, T_spec, H, d]; beta [N, T_spec, H]."""
+    a = VerifyArgs()
+    a.struct_size = ctypes.sizeof(VerifyArgs)
+    a.q, a.k, a.v, a.g, a.beta, a.o = map(_ptr, (q, k, v, g, beta, o))
+    a.state_pool, a.src_slot, a.dst_slot = _ptr(state_pool), _ptr(src_slot), _ptr(dst_slot)
+    a.accepted_len, a.committed_len_out = _ptr(accepted_len), _ptr(committed_len_out)
+    for name, t, inner in (("q", q, 2), ("k", k, 2), ("v", v, 2), ("g", g, 2), ("beta", beta, 1),
+                           ("o", o, 2)):
+        if t is not None and t.stride(0) != t.shape[1] * t.stride(1):
+            raise ValueError(f"{name}: sequences must be T_spec tokens apart")
+        setattr(a, f"{name}_stride", 0 if t is None else _tok_stride(t, inner))
+    a.n_slots = state_pool.shape[0]
+    a.n_seq, a.T_spec, a.H = q.shape[0], q.shape[1], q.shape[2]
+    a.d_k, a.d_v = q.shape[3], v.shape[3]
+    a.in_dtype = _dtype_code(q)
+    a.out_dtype = _dtype_code(o) if o is not None else KDA_F32
+    a.scale = scale
+    _check(load_library().kda_verify(ctypes.byref(a), _stream(stream)))
+    return o

@@ -1,0 +1,291 @@
+/*
+ * kda.h -- C ABI of libkda, the MI355X (gfx950) library for the Kimi Delta
+ * Attention (KDA) layer path.
+ *
+ * The method (pages: "Kimi K3 on vLLM: Up to 370 Tokens/sec", section "Kimi
+ * Delta Attention: a hybrid recurrent + full-attention stack"; "Kimi K3 +
+ * vLLM: Inside the Day-0 Production Integration", section "Kimi Delta
+ * Attention: When Prefix Caching Meets Recurrent State"): each KDA head keeps
+ * a fixed-size d_k x d_v matrix state S and a short causal-convolution state.
+ * The pages print no equation; this library computes the gated delta rule
+ * with per-key-channel decay,
+ *
+ *     S_t = (I - beta_t k_t k_t^T) Diag(exp g_t) S_{t-1} + beta_t k_t v_t^T,
+ *     o_t = scale * S_t^T q_t,
+ *
+ * decay first, correction against the decayed state, output from the
+ * updated state.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Every pointer inside an args struct is a DEVICE pointer unless its
+ *   comment says "host".  The caller owns every buffer; the library keeps no
+ *   handle, allocates nothing and never synchronises the stream (except
+ *   under the debug environment variable KDA_CHECK=1, which copies index
+ *   arrays to the host to validate them).
+ * - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream).
+ * - Inputs dtype: KDA_BF16 or KDA_F32 (`in_dtype`), outputs `out_dtype`.
+ *   Recurrent states are always fp32.  Arithmetic is fp32 (prefill products
+ *   on bf16 matrix cores with split operands, fp32 accumulation).
+ * - Per-token tensors are [tokens, H, d] with [H, d] contiguous; `*_stride`
+ *   is the distance in ELEMENTS between consecutive tokens (0 = packed,
+ *   i.e. H*d, or H for beta).  Base pointers and token strides of q, k, v,
+ *   g, o must be 16-byte aligned.
+ * - State pool: float [n_slots, H, d_k, d_v], d_v contiguous (row r = key
+ *   channel r).  A slot index of -1 means "zero initial state" for a source
+ *   and "do not write" for a destination.  Indices outside [-1, n_slots) are
+ *   treated like -1 (never dereferenced).
+ * - Supported sizes: d_k == d_v in {16, 32, 64, 128}; H >= 1.
+ * - Status: every call returns a kda_status; KDA_OK means the work was
+ *   enqueued.  kda_last_error() gives a one-line reason for the calling
+ *   thread's last failure.  n_seq == 0 is a no-op returning KDA_OK.
+ * - Preconditions on device data that cannot be checked without a sync
+ *   (checked only under KDA_CHECK=1): cu_seqlens non-decreasing and within
+ *   [0, T_tot]; no source slot of one sequence equals a destination or
+ *   checkpoint slot of another sequence in the same call (two sequences that
+ *   share a cached prefix must take their copies in separate calls).
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_ABI_VERSION 1
+
+typedef enum kda_status {
+    KDA_OK = 0,
+    KDA_ERR_NULL = 1,        /* a required pointer is NULL */
+    KDA_ERR_SHAPE = 2,       /* a size is out of range or inconsistent */
+    KDA_ERR_DTYPE = 3,       /* unknown dtype code */
+    KDA_ERR_ALIGN = 4,       /* pointer/stride not 16-byte aligned, or a
+                                checkpoint interval not a multiple of chunk */
+    KDA_ERR_WORKSPACE = 5,   /* workspace missing or too small */
+    KDA_ERR_UNSUPPORTED = 6, /* valid request outside what is built */
+    KDA_ERR_HIP = 7,         /* the HIP runtime reported an error */
+    KDA_ERR_ARG = 8,         /* malformed argument struct or invalid data
+                                (KDA_CHECK=1 validation) */
+    KDA_ERR_CAPACITY = 9     /* a host output array is too small */
+} kda_status;
+
+typedef enum kda_dtype { KDA_BF16 = 0, KDA_F32 = 1 } kda_dtype;
+
+typedef void *kda_stream_t; /* hipStream_t */
+
+/* Short human-readable name of a status code (static string). */
+const char *kda_status_str(int status);
+/* KDA_ABI_VERSION of the built library. */
+int kda_abi_version(void);
+/* One-line reason for the calling thread's most recent non-OK status. */
+const char *kda_last_error(void);
+/* sizeof() of each args struct as compiled into the library: which = 0 conv,
+ * 1 prefill, 2 decode, 3 verify.  Returns 0 for other values. */
+size_t kda_args_sizeof(int which);
+
+/* ------------------------------------------------------------------------
+ * kda_conv_short -- short causal depthwise convolution with carried state.
+ *
+ * The KDA layer runs a short causal convolution on its q/k/v channels and
+ * carries its state across calls (Day-0 Integration page, section "Kimi
+ * Delta Attention: When Prefix Caching Meets Recurrent State"; the fused
+ * decode kernel folds it in, section "Separate Prefill/Decode Code Paths").
+ *
+ *   y[t, c] = bias[c] + sum_{j=0}^{W-1} weight[c, j] * xbar[t - (W-1) + j, c]
+ *   (then SiLU when act == 1)
+ *
+ * where xbar is the sequence's carried state (last W-1 raw inputs, oldest
+ * first; zeros when src_slot < 0) followed by its tokens.  Tap W-1 multiplies
+ * the current token.  The new state (the last W-1 raw inputs after
+ * advance_len[s] tokens, or after all tokens when advance_len is NULL) is
+ * written to dst_slot[s] when >= 0; src == dst (in place) is allowed.
+ * Outputs are produced for every token.  Sequences may be empty.
+ * ---------------------------------------------------------------------- */
+typedef struct kda_conv_args {
+    size_t struct_size;          /* sizeof(kda_conv_args) */
+    const void *x;               /* [T_tot, C], row stride x_stride */
+    void *y;                     /* [T_tot, C], row stride y_stride */
+    const void *weight;          /* [C, W] contiguous */
+    const void *bias;            /* [C] or NULL */
+    const int32_t *cu_seqlens;   /* [n_seq + 1] token offsets into x / y */
+    void *conv_pool;             /* [n_slots, C, W-1] contiguous (channel-major) */
+    const int32_t *src_slot;     /* [n_seq]; -1 = zero history */
+    const int32_t *dst_slot;     /* [n_seq]; -1 = do not write */
+    const int32_t *advance_len;  /* [n_seq] or NULL; clamped to [0, len] */
+    int64_t x_stride;            /* elements between tokens (0 = C) */
+    int64_t y_stride;            /* elements between tokens (0 = C) */
+    int64_t T_tot;               /* rows of x and y */
+    int64_t n_slots;
+    int32_t n_seq;
+    int32_t C;                   /* channels; multiple of 16 / sizeof(dtype) */
+    int32_t W;                   /* 2..8 */
+    int32_t dtype;               /* x, y, weight, bias and conv_pool */
+    int32_t act;                 /* 0 none, 1 SiLU */
+    int32_t reserved;
+} kda_conv_args;
+
+int kda_conv_short(const kda_conv_args *args, kda_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * kda_ckpt_plan -- where interval checkpoints fall (host-only integer work).
+ *
+ * Interval retention (Day-0 Integration page, section "Interval-Based and
+ * Marconi-Style Retention"): a state snapshot is kept every `interval`
+ * tokens.  A sequence occupying absolute positions [start, start + len) gets
+ * one checkpoint for every multiple p of `interval` with start < p <
+ * start + len: the state after its first p - start tokens.  The final state
+ * is not a checkpoint (kda_prefill_varlen returns it through dst_slot).
+ * Count per sequence: floor((start + len - 1) / interval) - floor(start /
+ * interval) (0 when len == 0).
+ *
+ *   cu_seqlens   host [n_seq + 1]
+ *   start_pos    host [n_seq] absolute start of each sequence, or NULL (0)
+ *   interval     > 0 and a multiple of `chunk` (else KDA_ERR_ALIGN)
+ *   chunk        16, 32 or 64 (the prefill chunk the plan is for)
+ *   ckpt_cu      host [n_seq + 1] out: prefix counts
+ *   ckpt_pos     host [cap] out: positions, sequence by sequence (may be
+ *                NULL when cap == 0, to query the total)
+ *   n_total      host out: total number of checkpoints
+ * Returns KDA_ERR_CAPACITY (after filling ckpt_cu and n_total) when the
+ * total exceeds cap.
+ * ---------------------------------------------------------------------- */
+int kda_ckpt_plan(const int32_t *cu_seqlens, const int32_t *start_pos, int32_t n_seq,
+                  int32_t interval, int32_t chunk, int32_t *ckpt_cu, int32_t *ckpt_pos,
+                  int32_t cap, int32_t *n_total);
+
+/* ------------------------------------------------------------------------
+ * kda_prefill_varlen -- chunked prefill of packed sequences.
+ *
+ * Runs the recurrence over each sequence of a packed batch (cu_seqlens),
+ * starting from src_slot's state (or zero), writing every token's output,
+ * the final state to dst_slot, and interval checkpoints to ckpt_slot (the
+ * positions of kda_ckpt_plan, echoed in ckpt_pos_out).  This is how a
+ * long shared prompt's state snapshots are registered for prefix reuse and
+ * copied into a private destination before extension (Day-0 Integration
+ * page, section "Separating Physical Blocks, Scheduler Alignment, and
+ * Prefix Matching"): src is only read, never written.
+ *
+ * Chunk boundaries are aligned to absolute positions (multiples of chunk),
+ * so a sequence may start mid-chunk; checkpoints therefore always fall on
+ * chunk boundaries.  Long sequences are split into segments processed in
+ * parallel and joined by a transition-matrix combine; the split needs the
+ * workspace (size from kda_prefill_workspace_bytes for the same args; 0 is
+ * possible for short batches).
+ * ---------------------------------------------------------------------- */
+typedef struct kda_prefill_args {
+    size_t struct_size;          /* sizeof(kda_prefill_args) */
+    const void *q;               /* [T_tot, H, d_k] */
+    const void *k;               /* [T_tot, H, d_k] */
+    const void *v;               /* [T_tot, H, d_v] */
+    const void *g;               /* [T_tot, H, d_k] log decay (alpha = exp g) */
+    const void *beta;            /* [T_tot, H] */
+    void *o;                     /* [T_tot, H, d_v] out_dtype */
+    const int32_t *cu_seqlens;   /* [n_seq + 1] */
+    float *state_pool;           /* [n_slots, H, d_k, d_v] */
+    const int32_t *src_slot;     /* [n_seq]; -1 = zero initial state */
+    const int32_t *dst_slot;     /* [n_seq]; -1 = final state not written */
+    const int32_t *start_pos;    /* [n_seq] absolute start, or NULL (all 0) */
+    const int32_t *ckpt_cu;      /* [n_seq + 1] from kda_ckpt_plan, or NULL */
+    const int32_t *ckpt_slot;    /* [n_ckpt] pool slot of each checkpoint */
+    int32_t *ckpt_pos_out;       /* [n_ckpt] or NULL: position written */
+    void *workspace;             /* scratch of workspace_bytes, or NULL */
+    int64_t q_stride, k_stride, v_stride, g_stride, beta_stride, o_stride; /* 0 = packed */
+    int64_t T_tot;
+    int64_t n_slots;
+    int64_t workspace_bytes;
+    int64_t n_ckpt;              /* length of ckpt_slot / ckpt_pos_out */
+    int32_t n_seq;
+    int32_t H, d_k, d_v;
+    int32_t chunk;               /* 16, 32 or 64 */
+    int32_t in_dtype, out_dtype;
+    int32_t ckpt_interval;       /* 0 = no checkpoints; multiple of chunk */
+    float scale;
+    int32_t reserved;
+} kda_prefill_args;
+
+/* Workspace bytes kda_prefill_varlen needs for these args (host-only). */
+int64_t kda_prefill_workspace_bytes(const kda_prefill_args *args);
+int kda_prefill_varlen(const kda_prefill_args *args, kda_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * kda_decode -- one token per sequence, state updated in place.
+ *
+ * The decode step of the KDA layer (Day-0 Integration page, section
+ * "Separate Prefill/Decode Code Paths"; "Kimi K3 on vLLM", section "Kimi
+ * Delta Attention: a hybrid recurrent + full-attention stack", where decode
+ * runs a fused kernel): for sequence s the state is read from src_slot[s],
+ * advanced by one token and written to dst_slot[s] (usually the same slot).
+ * ---------------------------------------------------------------------- */
+typedef struct kda_decode_args {
+    size_t struct_size;          /* sizeof(kda_decode_args) */
+    const void *q, *k, *v, *g;   /* [n_seq, H, d] */
+    const void *beta;            /* [n_seq, H] */
+    void *o;                     /* [n_seq, H, d_v] out_dtype */
+    float *state_pool;           /* [n_slots, H, d_k, d_v] */
+    const int32_t *src_slot;     /* [n_seq] */
+    const int32_t *dst_slot;     /* [n_seq] */
+    int64_t q_stride, k_stride, v_stride, g_stride, beta_stride, o_stride; /* 0 = packed */
+    int64_t n_slots;
+    int32_t n_seq;
+    int32_t H, d_k, d_v;
+    int32_t in_dtype, out_dtype;
+    float scale;
+    int32_t reserved;
+} kda_decode_args;
+
+int kda_decode(const kda_decode_args *args, kda_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * kda_verify -- speculative verification with a commit at the accepted
+ * length.
+ *
+ * Speculative decoding proposes several draft tokens that the target model
+ * verifies in one parallel pass ("Kimi K3 on vLLM", section "Ultra-low
+ * latency: speculative decoding with DSpark"; the KDA backend runs a separate
+ * path for it, section "Kimi Delta Attention: a hybrid recurrent +
+ * full-attention stack").  Each sequence holds T_spec tokens (position 0 =
+ * the last accepted token, then the drafts), laid out [n_seq, T_spec, H, d]
+ * with token stride *_stride (sequence stride = T_spec * token stride).
+ *
+ * Modes:
+ *   o != NULL, accepted_len == NULL : outputs for all T_spec positions; the
+ *                                     pool is not written.
+ *   o == NULL, accepted_len != NULL : commit only: the state after exactly
+ *                                     accepted_len[s] tokens goes to
+ *                                     dst_slot[s].
+ *   both                            : fused (outputs + commit in one pass).
+ * accepted_len[s] = L counts tokens including position 0; L = 0 commits the
+ * source state unchanged; L outside [0, T_spec] rejects the sequence:
+ * committed_len_out[s] = -1 and dst is not written.  Otherwise
+ * committed_len_out[s] = L.  Outputs at positions >= L are still produced
+ * from the running state.
+ * ---------------------------------------------------------------------- */
+typedef struct kda_verify_args {
+    size_t struct_size;          /* sizeof(kda_verify_args) */
+    const void *q, *k, *v, *g;   /* [n_seq, T_spec, H, d] */
+    const void *beta;            /* [n_seq, T_spec, H] */
+    void *o;                     /* [n_seq, T_spec, H, d_v] or NULL */
+    float *state_pool;           /* [n_slots, H, d_k, d_v] */
+    const int32_t *src_slot;     /* [n_seq] */
+    const int32_t *dst_slot;     /* [n_seq] */
+    const int32_t *accepted_len; /* [n_seq] or NULL */
+    int32_t *committed_len_out;  /* [n_seq] or NULL */
+    int64_t q_stride, k_stride, v_stride, g_stride, beta_stride, o_stride; /* per token; 0 = packed */
+    int64_t n_slots;
+    int32_t n_seq;
+    int32_t T_spec;              /* 1..16 */
+    int32_t H, d_k, d_v;
+    int32_t in_dtype, out_dtype;
+    float scale;
+} kda_verify_args;
+
+int kda_verify(const kda_verify_args *args, kda_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

@@ -1,0 +1,173 @@
+"""The C ABI on the CPU: the library loads, exports every declared entry
+point, its structs match the binding, and host-side validation returns the
+documented status codes without touching a GPU."""
+
+import ctypes
+import re
+from pathlib import Path
+
+import numpy as np
+import pytest
+
+from hybrid_recurrent_serving_amd import kda as K
+
+ROOT = Path(__file__).resolve().parents[1]
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return K.load_library()
+
+
+def declared_functions():
+    text = (ROOT / "include" / "kda.h").read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(K.EXPORTS)
+
+
+def test_abi_version_and_struct_sizes(lib):
+    assert lib.kda_abi_version() == 1
+    for which, cls in enumerate([K.ConvArgs, K.PrefillArgs, K.DecodeArgs, K.VerifyArgs]):
+        assert lib.kda_args_sizeof(which) == ctypes.sizeof(cls), cls.__name__
+    assert lib.kda_args_sizeof(7) == 0
+
+
+def test_status_strings(lib):
+    assert lib.kda_status_str(0) == b"KDA_OK"
+    assert lib.kda_status_str(4) == b"KDA_ERR_ALIGN"
+    assert lib.kda_status_str(99) == b"KDA_ERR_UNKNOWN"
+
+
+def _call(lib, fn, args):
+    return getattr(lib, fn)(ctypes.byref(args), None)
+
+
+def _decode_args(**kw):
+    a = K.DecodeArgs()
+    a.struct_size = ctypes.sizeof(K.DecodeArgs)
+    fake = 1 << 20  # a 16-byte aligned fake device address: never dereferenced on these paths
+    for f in ("q", "k", "v", "g", "beta", "o", "state_pool", "src_slot", "dst_slot"):
+        setattr(a, f, fake)
+    a.n_seq, a.H, a.d_k, a.d_v, a.n_slots = 4, 2, 128, 128, 4
+    a.in_dtype, a.out_dtype, a.scale = 0, 0, 1.0
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_decode_validation(lib):
+    assert lib.kda_decode(None, None) == 1
+    assert _call(lib, "kda_decode", _decode_args(struct_size=8)) == 8
+    assert _call(lib, "kda_decode", _decode_args(n_seq=0)) == 0         # no-op
+    assert _call(lib, "kda_decode", _decode_args(q=None)) == 1
+    assert _call(lib, "kda_decode", _decode_args(d_k=96, d_v=96)) == 6
+    assert _call(lib, "kda_decode", _decode_args(d_k=64, d_v=128)) == 6
+    assert _call(lib, "kda_decode", _decode_args(in_dtype=5)) == 3
+    assert _call(lib, "kda_decode", _decode_args(H=0)) == 2
+    assert _call(lib, "kda_decode", _decode_args(q=(1 << 20) + 2)) == 4
+    assert _call(lib, "kda_decode", _decode_args(q_stride=100)) == 2     # < H*d
+    assert _call(lib, "kda_decode", _decode_args(q_stride=257)) == 4     # not 16-byte aligned
+    assert b"aligned" in lib.kda_last_error()
+
+
+def _verify_args(**kw):
+    a = K.VerifyArgs()
+    a.struct_size = ctypes.sizeof(K.VerifyArgs)
+    fake = 1 << 20
+    for f in ("q", "k", "v", "g", "beta", "o", "state_pool", "src_slot", "dst_slot",
+              "accepted_len"):
+        setattr(a, f, fake)
+    a.n_seq, a.T_spec, a.H, a.d_k, a.d_v, a.n_slots = 4, 8, 2, 64, 64, 4
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_verify_validation(lib):
+    assert _call(lib, "kda_verify", _verify_args(T_spec=0)) == 2
+    assert _call(lib, "kda_verify", _verify_args(T_spec=17)) == 2
+    assert _call(lib, "kda_verify", _verify_args(o=None, accepted_len=None)) == 1
+    assert _call(lib, "kda_verify", _verify_args(n_seq=0)) == 0
+
+
+def _conv_args(**kw):
+    a = K.ConvArgs()
+    a.struct_size = ctypes.sizeof(K.ConvArgs)
+    fake = 1 << 20
+    for f in ("x", "y", "weight", "cu_seqlens", "conv_pool", "src_slot", "dst_slot"):
+        setattr(a, f, fake)
+    a.n_seq, a.C, a.W, a.T_tot, a.n_slots, a.dtype = 2, 64, 4, 10, 2, 0
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_conv_validation(lib):
+    assert _call(lib, "kda_conv_short", _conv_args(W=1)) == 6
+    assert _call(lib, "kda_conv_short", _conv_args(W=9)) == 6
+    assert _call(lib, "kda_conv_short", _conv_args(C=12)) == 2     # not a multiple of 8 (bf16)
+    assert _call(lib, "kda_conv_short", _conv_args(dtype=3)) == 3
+    assert _call(lib, "kda_conv_short", _conv_args(x_stride=65)) == 4
+    assert _call(lib, "kda_conv_short", _conv_args(n_seq=0)) == 0
+
+
+def _prefill_args(**kw):
+    a = K.PrefillArgs()
+    a.struct_size = ctypes.sizeof(K.PrefillArgs)
+    fake = 1 << 20
+    for f in ("q", "k", "v", "g", "beta", "o", "cu_seqlens", "state_pool", "src_slot", "dst_slot"):
+        setattr(a, f, fake)
+    a.n_seq, a.H, a.d_k, a.d_v, a.chunk, a.T_tot, a.n_slots = 2, 2, 64, 64, 64, 100, 4
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_prefill_validation(lib):
+    assert _call(lib, "kda_prefill_varlen", _prefill_args(chunk=48)) == 6
+    assert _call(lib, "kda_prefill_varlen", _prefill_args(ckpt_interval=100)) == 4
+    assert _call(lib, "kda_prefill_varlen", _prefill_args(ckpt_interval=128)) == 1  # no ckpt arrays
+    assert _call(lib, "kda_prefill_varlen", _prefill_args(cu_seqlens=None)) == 1
+    assert _call(lib, "kda_prefill_varlen", _prefill_args(n_seq=0)) == 0
+    assert lib.kda_prefill_workspace_bytes(ctypes.byref(_prefill_args(chunk=48))) == -1
+
+
+def test_ckpt_plan_matches_oracle_enumeration(oracle64):
+    rng = np.random.default_rng(3)
+    for trial in range(30):
+        n = int(rng.integers(1, 7))
+        lens = rng.integers(0, 5000, n)
+        starts = rng.integers(0, 3000, n)
+        cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+        chunk = int(rng.choice([16, 32, 64]))
+        interval = chunk * int(rng.integers(1, 40))
+        ck_cu, pos = K.kda_ckpt_plan(cu, interval, chunk, start_pos=starts)
+        o_cu, o_pos = oracle64.ckpt_enumerate(cu, interval, starts.astype(np.int32))
+        assert ck_cu == list(o_cu)
+        assert pos == list(o_pos)
+    # the long workload: 31 interior checkpoints
+    ck_cu, pos = K.kda_ckpt_plan([0, 1 << 20], 32768, 64)
+    assert ck_cu == [0, 31] and pos == [32768 * m for m in range(1, 32)]
+
+
+def test_ckpt_plan_errors(lib):
+    with pytest.raises(K.KDAError) as e:
+        K.kda_ckpt_plan([0, 100], 100, 64)
+    assert e.value.name == "KDA_ERR_ALIGN"
+    with pytest.raises(K.KDAError):
+        K.kda_ckpt_plan([0, 100], 64, 48)
+    cu = np.array([0, 1000], np.int32)
+    ck_cu = np.zeros(2, np.int32)
+    pos = np.zeros(2, np.int32)
+    total = ctypes.c_int32(0)
+    vp = lambda a: a.ctypes.data_as(ctypes.c_void_p)  # noqa: E731
+    st = lib.kda_ckpt_plan(vp(cu), None, 1, 64, 64, vp(ck_cu), vp(pos), 2, ctypes.byref(total))
+    assert st == 9 and total.value == 15 and ck_cu[1] == 15
