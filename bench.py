@@ -1,0 +1,277 @@
+#!/usr/bin/env python3
+"""Throughput of the KDA layer path on one MI355X.
+
+Default workload: batched decode (128 sequences x 1 token, H=16,
+d_k=d_v=128, bf16 inputs, fp32 recurrent state, short conv W=4 over the
+3*H*d q/k/v channels).  One step = kda_conv_short on the step's 128 token
+rows (carried conv state updated in place) + kda_decode (recurrent state
+updated in place).  The recurrent state rotates over 4 pools of 128 MiB so
+it cannot be served from the 256 MB Infinity Cache.
+
+Prints ONE JSON line.  ``value`` = recurrent-state bytes read + written per
+step / step time (GB/s).  ``roofline`` = the decode kernel's algorithmic
+bytes per launch / its average launch time (HIP events around each launch in
+the timed region) against 8 TB/s.  ``cpu_baseline`` = the CPU oracle on the
+same workload (a bounded number of whole steps), timed on the host cores.
+
+Other workloads (``--workload verify|prefill|long``) print the same format.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+from pathlib import Path
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+METRIC = "KDA prefill tokens/s (H=16,d=128) + decode/verify state GB/s vs HBM peak"
+TRAFFIC_FILE = ROOT / "profiles" / "traffic.json"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default="decode", choices=["decode", "verify"])
+    ap.add_argument("--pools", type=int, default=4, help="rotating state pools (MALL defeat)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle time budget")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--no-secondary", action="store_true")
+    return ap.parse_args()
+
+
+def kernel_source_hash(name: str) -> str:
+    src = ROOT / "hybrid_recurrent_serving_amd" / "csrc" / name
+    return hashlib.sha256(src.read_bytes()).hexdigest()[:16]
+
+
+def traffic_for(kernel_key: str, src_name: str, per_launch_units: float):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when it is missing or the kernel source has changed since."""
+    if not TRAFFIC_FILE.exists():
+        return None
+    try:
+        data = json.loads(TRAFFIC_FILE.read_text())
+        ent = data[kernel_key]
+    except (KeyError, ValueError):
+        return None
+    if ent.get("source_sha256_16") != kernel_source_hash(src_name):
+        return None
+    if ent.get("units_per_launch") != per_launch_units:
+        return None
+    return float(ent["hbm_bytes_per_launch"])
+
+
+def cpu_info():
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return model
+
+
+# ---------------------------------------------------------------- decode
+def bench_decode(args, torch, K, make_workload):
+    dev = torch.device("cuda:0")
+    N, H, D, W = 128, 16, 128, 4
+    C = 3 * H * D
+    wl = make_workload(1, with_conv=True)
+    q, k, v, g, b = (t.to(dev) for t in (wl.q, wl.k, wl.v, wl.g, wl.beta))
+    P = args.pools
+    pool = torch.empty(P * N, H, D, D, device=dev)
+    for i in range(P):
+        pool[i * N:(i + 1) * N] = wl.init_states.to(dev)
+    slot_sets = [torch.arange(i * N, (i + 1) * N, dtype=torch.int32, device=dev) for i in range(P)]
+    o = torch.empty(N, H, D, dtype=torch.bfloat16, device=dev)
+    x = wl.conv_x.to(dev)
+    cw = wl.conv_w.to(dev)
+    cpool = wl.conv_state.to(dev).clone()
+    cslots = torch.arange(N, dtype=torch.int32, device=dev)
+    cu = wl.cu_seqlens.to(dev)
+    y = torch.empty_like(x)
+
+    def step(i, ev=None):
+        K.kda_conv_short(x, cw, cu, cpool, cslots, cslots, y=y)
+        s = slot_sets[i % P]
+        if ev is not None:
+            ev[0].record()
+        K.kda_decode(q, k, v, g, b, o, pool, s, s)
+        if ev is not None:
+            ev[1].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record()
+    for i in range(args.steps):
+        step(i, evs[i])
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t0.elapsed_time(t1) / args.steps
+    k_ms = sum(a.elapsed_time(b_) for a, b_ in evs) / args.steps
+
+    state_bytes = N * H * D * D * 4 * 2                   # read + write
+    io_bytes = N * H * (4 * D * 2 + 2 + D * 2)            # q,k,v,g + beta + o (bf16)
+    alg_bytes = state_bytes + io_bytes                    # per launch of the decode kernel
+    value = state_bytes / (ms_step * 1e-3) / 1e9
+    achieved = alg_bytes / (k_ms * 1e-3) / 1e9
+    traffic = traffic_for("decode_step_kernel_d128_bf16", "kda_step.hip", N * H)
+    roof = {"kernel": "step_kernel<128,bf16,bf16> (kda_decode)", "bound": "hbm",
+            "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "alg_bytes_per_launch": alg_bytes, "avg_launch_us": round(k_ms * 1e3, 3)}
+
+    secondary = {}
+    if not args.no_secondary:
+        # hot: one pool only (state may sit in the Infinity Cache) -- labelled, not the value
+        s0 = slot_sets[0]
+        for _ in range(20):
+            K.kda_decode(q, k, v, g, b, o, pool, s0, s0)
+        a_, b2 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a_.record()
+        for _ in range(200):
+            K.kda_decode(q, k, v, g, b, o, pool, s0, s0)
+        b2.record()
+        torch.cuda.synchronize()
+        hot_us = a_.elapsed_time(b2) / 200 * 1e3
+        secondary["decode_hot_single_pool"] = {"us": round(hot_us, 2),
+                                               "GB_s": round(alg_bytes / hot_us / 1e3, 1)}
+        # plain device copy of the same bytes (torch copy kernel) as a practical ceiling
+        src_t = torch.empty(state_bytes // 8, dtype=torch.float32, device=dev)
+        dst_t = torch.empty_like(src_t)
+        srcs = [torch.empty_like(src_t) for _ in range(3)] + [src_t]
+        dsts = [torch.empty_like(dst_t) for _ in range(3)] + [dst_t]
+        for i in range(8):
+            dsts[i % 4].copy_(srcs[i % 4])
+        torch.cuda.synchronize()
+        a_.record()
+        for i in range(100):
+            dsts[i % 4].copy_(srcs[i % 4])
+        b2.record()
+        torch.cuda.synchronize()
+        cp_us = a_.elapsed_time(b2) / 100 * 1e3
+        secondary["copy_same_bytes"] = {"us": round(cp_us, 2),
+                                        "GB_s": round(state_bytes / cp_us / 1e3, 1)}
+        del srcs, dsts, src_t, dst_t
+        secondary["verify"] = bench_verify_secondary(torch, K, make_workload, dev)
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_decode(args, wl, state_bytes)
+    cfg = {"workload": "batched decode: 128 seqs x 1 token, H=16, d_k=d_v=128, conv W=4 "
+                       "over 6144 q/k/v channels, bf16 inputs, fp32 state",
+           "n_seq": N, "H": H, "d": D, "conv_W": W, "state_pools_rotated": P,
+           "step": "kda_conv_short + kda_decode", "value_counts": "recurrent state read+write"}
+    return {"metric": METRIC, "value": round(value, 1), "unit": "GB/s", "ms_per_step": ms_step,
+            "dtype": "f32", "config": cfg, "roofline": roof, "cpu_baseline": cpu,
+            "secondary": secondary, "wall_s": round(wall, 3)}
+
+
+def bench_verify_secondary(torch, K, make_workload, dev):
+    """Speculative verify (128 x 8 tokens, fused commit) -- reported beside the
+    decode line."""
+    wl = make_workload(4)
+    N, Ts, H, D = 128, 8, 16, 128
+    q, k, v, g, b = (t.to(dev) for t in (wl.q, wl.k, wl.v, wl.g, wl.beta))
+    P = 4
+    pool = torch.empty(P * N, H, D, D, device=dev)
+    for i in range(P):
+        pool[i * N:(i + 1) * N] = wl.init_states.to(dev)
+    slot_sets = [torch.arange(i * N, (i + 1) * N, dtype=torch.int32, device=dev) for i in range(P)]
+    L = wl.accepted_len.to(dev)
+    o = torch.empty(N, Ts, H, D, dtype=torch.bfloat16, device=dev)
+    for i in range(10):
+        s = slot_sets[i % P]
+        K.kda_verify(q, k, v, g, b, pool, s, s, o=o, accepted_len=L)
+    a_, b2 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a_.record()
+    n = 200
+    for i in range(n):
+        s = slot_sets[i % P]
+        K.kda_verify(q, k, v, g, b, pool, s, s, o=o, accepted_len=L)
+    b2.record()
+    torch.cuda.synchronize()
+    us = a_.elapsed_time(b2) / n * 1e3
+    state_bytes = N * H * D * D * 4 * 2
+    io = N * Ts * H * (4 * D * 2 + 2 + D * 2)
+    return {"workload": "verify 128 x 8 tokens, fused commit at L~U{1..8}", "us": round(us, 2),
+            "state_GB_s": round(state_bytes / us / 1e3, 1),
+            "alg_GB_s": round((state_bytes + io) / us / 1e3, 1),
+            "hbm_frac": round((state_bytes + io) / us / 1e3 / HBM_PEAK_GBS, 4)}
+
+
+def cpu_decode(args, wl, state_bytes):
+    import numpy as np
+    import oracle
+    orc = oracle.load("f64")
+    threads = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    orc.set_threads(threads)
+    init = wl.init_states.double().numpy()
+    has = np.ones(wl.n_seq, np.int32)
+    q, k, v, g, b = (t.float().numpy() for t in (wl.q, wl.k, wl.v, wl.g, wl.beta))
+    cx, cw, cs = wl.conv_x.float().numpy(), wl.conv_w.float().numpy(), wl.conv_state.float().numpy()
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        orc.conv_short(cx, cw, wl.cu_seqlens, state=cs)
+        orc.kda_varlen(q, k, v, g, b, wl.cu_seqlens, init=init, has_init=has)
+        reps += 1
+        if time.perf_counter() - t0 > args.cpu_seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(state_bytes * reps / dt / 1e9, 3), "unit": "GB/s", "cores": orc.threads(),
+            "kind": "oracle", "cpu": cpu_info(),
+            "sample": f"{reps} whole decode steps (conv + 128 seqs x 16 heads x 1 token, fp64 oracle), "
+                      f"{dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    from hybrid_recurrent_serving_amd import kda as K
+    from hybrid_recurrent_serving_amd.inputs import make_workload
+    K.load_library()
+    if args.workload == "decode":
+        res = bench_decode(args, torch, K, make_workload)
+    else:
+        raise SystemExit("verify workload is reported in the decode line's 'secondary' block")
+    line = {"metric": res["metric"], "value": res["value"], "unit": res["unit"], "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(res["ms_per_step"], 6),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": res["dtype"], "data": "synthetic (seeded; no datasets or weights)",
+            "config": res["config"], "roofline": res["roofline"],
+            "cpu_baseline": res["cpu_baseline"], "secondary": res["secondary"]}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -183,7 +183,7 @@ __global__ void __launch_bounds__(CONV_THREADS) conv_kernel(const ConvParams p) 
       eos = p.cu[s + 1];
       have_win = false;
     }
-    if (t < bos || t >= eos || t - bos < HIST) {
+    if (t < bos || t >= eos || t - bos < HIST || t < HIST) {
       have_win = false;
       continue;
     }

@@ -159,6 +159,36 @@ def _tok_stride(t, inner_dims: int) -> int:
     return st[t.dim() - 1 - inner_dims]
 
 
+def _expect(cond: bool, msg: str):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _same_lead(named, lead, what):
+    for name, t in named:
+        if t is not None:
+            _expect(tuple(t.shape[:len(lead)]) == tuple(lead),
+                    f"{name}: leading shape {tuple(t.shape[:len(lead)])} != {tuple(lead)} ({what})")
+
+
+def _device_tensors(**named):
+    """Every pointer handed to the library must be device memory of the right
+    integer type: a host pointer would be dereferenced by the GPU."""
+    import torch
+    for name, t in named.items():
+        if t is None:
+            continue
+        _expect(isinstance(t, torch.Tensor) and t.is_cuda, f"{name} must be a GPU tensor")
+        if name in ("cu_seqlens", "src_slot", "dst_slot", "advance_len", "start_pos", "ckpt_cu",
+                    "ckpt_slot", "ckpt_pos_out", "accepted_len", "committed_len_out"):
+            _expect(t.dtype == torch.int32 and t.is_contiguous(), f"{name} must be contiguous int32")
+
+
+def _same_dtype(ref, **named):
+    for name, t in named.items():
+        _expect(t is None or t.dtype == ref.dtype, f"{name}: dtype {t.dtype} != {ref.dtype}")
+
+
 def _stream(stream) -> int:
     import torch
     if stream is None:
@@ -190,6 +220,20 @@ def kda_conv_short(x, weight, cu_seqlens, conv_pool, src_slot, dst_slot, *, y=No
     import torch
     if y is None:
         y = torch.empty_like(x)
+    _expect(x.dim() == 2 and y.shape == x.shape, "x and y must be [T, C]")
+    T, C = x.shape
+    _expect(weight.dim() == 2 and weight.shape[0] == C, "weight must be [C, W]")
+    W = weight.shape[1]
+    _expect(conv_pool.dim() == 3 and conv_pool.shape[1] == C and conv_pool.shape[2] == W - 1,
+            "conv_pool must be [n_slots, C, W-1]")
+    n = cu_seqlens.numel() - 1
+    _expect(src_slot.numel() >= n and dst_slot.numel() >= n, "slot arrays shorter than n_seq")
+    _expect(bias is None or bias.numel() == C, "bias must be [C]")
+    _expect(advance_len is None or advance_len.numel() >= n, "advance_len shorter than n_seq")
+    _device_tensors(x=x, y=y, weight=weight, bias=bias, cu_seqlens=cu_seqlens, conv_pool=conv_pool,
+                    src_slot=src_slot, dst_slot=dst_slot, advance_len=advance_len)
+    _expect(weight.is_contiguous() and conv_pool.is_contiguous(), "weight / conv_pool must be contiguous")
+    _same_dtype(x, y=y, weight=weight, bias=bias, conv_pool=conv_pool)
     a = ConvArgs()
     a.struct_size = ctypes.sizeof(ConvArgs)
     a.x, a.y, a.weight, a.bias = _ptr(x), _ptr(y), _ptr(weight), _ptr(bias)
@@ -226,6 +270,26 @@ def kda_ckpt_plan(cu_seqlens, interval: int, chunk: int, start_pos=None):
 
 def _prefill_args(q, k, v, g, beta, o, cu_seqlens, state_pool, src_slot, dst_slot, chunk,
                   start_pos, ckpt_interval, ckpt_cu, ckpt_slot, ckpt_pos_out, workspace, scale):
+    import torch
+    _expect(q.dim() == 3 and v.dim() == 3 and beta.dim() == 2, "q/k/v/g [T, H, d], beta [T, H]")
+    T, H, dk = q.shape
+    _same_lead([("k", k), ("g", g)], (T, H, dk), "q")
+    _same_lead([("v", v), ("o", o)], (T, H, v.shape[2]), "v")
+    _same_lead([("beta", beta)], (T, H), "q")
+    _expect(state_pool.dim() == 4 and tuple(state_pool.shape[1:]) == (H, dk, v.shape[2]),
+            "state_pool must be [n_slots, H, d_k, d_v]")
+    n = cu_seqlens.numel() - 1
+    _expect(src_slot.numel() >= n and dst_slot.numel() >= n, "slot arrays shorter than n_seq")
+    _expect(start_pos is None or start_pos.numel() >= n, "start_pos shorter than n_seq")
+    _expect(ckpt_cu is None or ckpt_cu.numel() >= n + 1, "ckpt_cu shorter than n_seq + 1")
+    _expect(ckpt_pos_out is None or ckpt_slot is None or ckpt_pos_out.numel() >= ckpt_slot.numel(),
+            "ckpt_pos_out shorter than ckpt_slot")
+    _device_tensors(q=q, k=k, v=v, g=g, beta=beta, o=o, cu_seqlens=cu_seqlens, state_pool=state_pool,
+                    src_slot=src_slot, dst_slot=dst_slot, start_pos=start_pos, ckpt_cu=ckpt_cu,
+                    ckpt_slot=ckpt_slot, ckpt_pos_out=ckpt_pos_out, workspace=workspace)
+    _same_dtype(q, k=k, v=v, g=g, beta=beta)
+    _expect(state_pool.dtype == torch.float32 and state_pool.is_contiguous(),
+            "state_pool must be contiguous float32")
     a = PrefillArgs()
     a.struct_size = ctypes.sizeof(PrefillArgs)
     a.q, a.k, a.v, a.g, a.beta, a.o = map(_ptr, (q, k, v, g, beta, o))
@@ -268,6 +332,20 @@ def kda_prefill_varlen(q, k, v, g, beta, o, cu_seqlens, state_pool, src_slot, ds
 
 def kda_decode(q, k, v, g, beta, o, state_pool, src_slot, dst_slot, *, scale=1.0, stream=None):
     """One token per sequence.  q, k, v, g [N, H, d]; beta [N, H]; o [N, H, d]."""
+    import torch
+    _expect(q.dim() == 3 and v.dim() == 3 and beta.dim() == 2, "q/k/v/g [N, H, d], beta [N, H]")
+    N, H, dk = q.shape
+    _same_lead([("k", k), ("g", g)], (N, H, dk), "q")
+    _same_lead([("v", v), ("o", o)], (N, H, v.shape[2]), "v")
+    _same_lead([("beta", beta)], (N, H), "q")
+    _expect(state_pool.dim() == 4 and tuple(state_pool.shape[1:]) == (H, dk, v.shape[2]),
+            "state_pool must be [n_slots, H, d_k, d_v]")
+    _expect(src_slot.numel() >= N and dst_slot.numel() >= N, "slot arrays shorter than n_seq")
+    _device_tensors(q=q, k=k, v=v, g=g, beta=beta, o=o, state_pool=state_pool, src_slot=src_slot,
+                    dst_slot=dst_slot)
+    _same_dtype(q, k=k, v=v, g=g, beta=beta)
+    _expect(state_pool.dtype == torch.float32 and state_pool.is_contiguous(),
+            "state_pool must be contiguous float32")
     a = DecodeArgs()
     a.struct_size = ctypes.sizeof(DecodeArgs)
     a.q, a.k, a.v, a.g, a.beta, a.o = map(_ptr, (q, k, v, g, beta, o))
@@ -284,6 +362,24 @@ def kda_decode(q, k, v, g, beta, o, state_pool, src_slot, dst_slot, *, scale=1.0
 def kda_verify(q, k, v, g, beta, state_pool, src_slot, dst_slot, *, o=None, accepted_len=None,
                committed_len_out=None, scale=1.0, stream=None):
     """Speculative verify.  q, k, v, g [N, T_spec, H, d]; beta [N, T_spec, H]."""
+    import torch
+    _expect(q.dim() == 4 and v.dim() == 4 and beta.dim() == 3,
+            "q/k/v/g [N, T_spec, H, d], beta [N, T_spec, H]")
+    N, Ts, H, dk = q.shape
+    _same_lead([("k", k), ("g", g)], (N, Ts, H, dk), "q")
+    _same_lead([("v", v), ("o", o)], (N, Ts, H, v.shape[3]), "v")
+    _same_lead([("beta", beta)], (N, Ts, H), "q")
+    _expect(state_pool.dim() == 4 and tuple(state_pool.shape[1:]) == (H, dk, v.shape[3]),
+            "state_pool must be [n_slots, H, d_k, d_v]")
+    _expect(src_slot.numel() >= N and dst_slot.numel() >= N, "slot arrays shorter than n_seq")
+    _expect(accepted_len is None or accepted_len.numel() >= N, "accepted_len shorter than n_seq")
+    _expect(committed_len_out is None or committed_len_out.numel() >= N,
+            "committed_len_out shorter than n_seq")
+    _device_tensors(q=q, k=k, v=v, g=g, beta=beta, o=o, state_pool=state_pool, src_slot=src_slot,
+                    dst_slot=dst_slot, accepted_len=accepted_len, committed_len_out=committed_len_out)
+    _same_dtype(q, k=k, v=v, g=g, beta=beta)
+    _expect(state_pool.dtype == torch.float32 and state_pool.is_contiguous(),
+            "state_pool must be contiguous float32")
     a = VerifyArgs()
     a.struct_size = ctypes.sizeof(VerifyArgs)
     a.q, a.k, a.v, a.g, a.beta, a.o = map(_ptr, (q, k, v, g, beta, o))

@@ -1,0 +1,259 @@
+"""GPU parity of kda_decode and kda_verify against the CPU oracle, through
+the C ABI, on the seeded workloads and their edge cases."""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import gpu_util as U
+from hybrid_recurrent_serving_amd import kda as K
+from hybrid_recurrent_serving_amd.inputs import make_workload
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    d = U.device()
+    K.load_library()
+    return d
+
+
+def _oracle_states(wl):
+    init = np.zeros((wl.n_seq, wl.H, wl.dk, wl.dv))
+    has = np.zeros(wl.n_seq, np.int32)
+    for s, i in enumerate(wl.init_index):
+        if i >= 0:
+            init[s] = wl.init_states[i].double().numpy()
+            has[s] = 1
+    return init, has
+
+
+def test_decode_tiny_stepped_64(dev, oracle64):
+    """Tiny workload (T=64, H=2, d=16, fp32): 64 decode steps in place equal
+    the oracle's token loop at every position and in the final state."""
+    U.say("decode tiny stepped 64x")
+    wl = make_workload(0)
+    ref = oracle64.kda_varlen(wl.q, wl.k, wl.v, wl.g, wl.beta, wl.cu_seqlens)
+    q, k, v, g, b = (t.to(dev) for t in (wl.q, wl.k, wl.v, wl.g, wl.beta))
+    pool = torch.zeros(1, wl.H, wl.dk, wl.dv, device=dev)
+    slot = torch.zeros(1, dtype=torch.int32, device=dev)
+    o = torch.empty(64, wl.H, wl.dv, device=dev)
+    for t in range(64):
+        K.kda_decode(q[t:t + 1], k[t:t + 1], v[t:t + 1], g[t:t + 1], b[t:t + 1], o[t:t + 1],
+                     pool, slot, slot)
+    torch.cuda.synchronize()
+    U.assert_close("o", U.to_np(o), ref["o"], rel=1e-5, mx=1e-5)
+    U.assert_close("state", U.to_np(pool[0]), ref["final"][0], rel=1e-5, mx=1e-5)
+
+
+def test_decode_batched_128(dev, oracle64):
+    """Batched decode: 128 sequences x 1 token, H=16, d=128, bf16 inputs,
+    random fp32 states updated in place."""
+    U.say("decode batched 128 x H16 x d128")
+    wl = make_workload(1)
+    init, has = _oracle_states(wl)
+    ref = oracle64.kda_varlen(wl.q, wl.k, wl.v, wl.g, wl.beta, wl.cu_seqlens, init=init,
+                              has_init=has)
+    q, k, v, g, b = (t.to(dev) for t in (wl.q, wl.k, wl.v, wl.g, wl.beta))
+    pool = wl.init_states.to(dev).clone()
+    slots = torch.arange(128, dtype=torch.int32, device=dev)
+    o = torch.empty(128, 16, 128, dtype=torch.bfloat16, device=dev)
+    K.kda_decode(q, k, v, g, b, o, pool, slots, slots)
+    o32 = torch.empty(128, 16, 128, dtype=torch.float32, device=dev)
+    pool2 = wl.init_states.to(dev).clone()
+    K.kda_decode(q, k, v, g, b, o32, pool2, slots, slots)
+    torch.cuda.synchronize()
+    U.assert_close("o(bf16)", U.to_np(o), ref["o"])
+    U.assert_close("o(fp32)", U.to_np(o32), ref["o"], rel=1e-5, mx=1e-4)
+    U.assert_close("state", U.to_np(pool), ref["final"], rel=1e-5, mx=1e-4)
+    # bf16 output = the fp32 output rounded once
+    assert torch.equal(o, o32.to(torch.bfloat16))
+    assert torch.equal(pool, pool2)
+
+
+def test_decode_slots_cow_and_edges(dev):
+    """src != dst leaves src untouched (copy-on-write); src = -1 starts from
+    zero; dst = -1 writes nothing; out-of-range slots are never touched."""
+    U.say("decode slots / CoW / edges")
+    wl = make_workload(1, n_seq=6)
+    q, k, v, g, b = (t.to(dev) for t in (wl.q, wl.k, wl.v, wl.g, wl.beta))
+    pool = torch.randn(12, 16, 128, 128, device=dev) * 0.1
+    before = pool.clone()
+    src = torch.tensor([0, 1, -1, 3, 4, 99], dtype=torch.int32, device=dev)
+    dst = torch.tensor([6, 7, 8, -1, 4, 9], dtype=torch.int32, device=dev)
+    o = torch.empty(6, 16, 128, device=dev)
+    K.kda_decode(q, k, v, g, b, o, pool, src, dst)
+    torch.cuda.synchronize()
+    for s in (0, 1, 3):
+        assert torch.equal(pool[s], before[s]), "source slot modified"
+    assert torch.equal(pool[5], before[5]) and torch.equal(pool[10], before[10])
+    assert torch.equal(pool[11], before[11])
+    # a zero source equals an explicit zero state
+    zp = torch.zeros(1, 16, 128, 128, device=dev)
+    z = torch.zeros(1, dtype=torch.int32, device=dev)
+    o2 = torch.empty(1, 16, 128, device=dev)
+    K.kda_decode(q[2:3], k[2:3], v[2:3], g[2:3], b[2:3], o2, zp, z, z)
+    torch.cuda.synchronize()
+    assert torch.equal(pool[8], zp[0]) and torch.equal(o[2], o2[0])
+    # out-of-range source (99) behaves as zero state
+    K.kda_decode(q[5:6], k[5:6], v[5:6], g[5:6], b[5:6], o2, zp.zero_(), z, z)
+    torch.cuda.synchronize()
+    assert torch.equal(pool[9], zp[0])
+    # copy-on-write result equals the in-place result
+    pool_ip = before.clone()
+    slots = torch.tensor([0, 1], dtype=torch.int32, device=dev)
+    o3 = torch.empty(2, 16, 128, device=dev)
+    K.kda_decode(q[:2], k[:2], v[:2], g[:2], b[:2], o3, pool_ip, slots, slots)
+    torch.cuda.synchronize()
+    assert torch.equal(pool_ip[0], pool[6]) and torch.equal(pool_ip[1], pool[7])
+    assert torch.equal(o3, o[:2])
+
+
+@pytest.mark.parametrize("d", [16, 32, 64])
+def test_decode_small_heads(dev, oracle64, d):
+    U.say(f"decode d={d}")
+    wl = make_workload(1, n_seq=5, H=3, d=d)
+    init, has = _oracle_states(wl)
+    ref = oracle64.kda_varlen(wl.q, wl.k, wl.v, wl.g, wl.beta, wl.cu_seqlens, init=init,
+                              has_init=has, scale=0.5)
+    q, k, v, g, b = (t.to(dev) for t in (wl.q, wl.k, wl.v, wl.g, wl.beta))
+    pool = wl.init_states.to(dev).clone()
+    slots = torch.arange(5, dtype=torch.int32, device=dev)
+    o = torch.empty(5, 3, d, device=dev)
+    K.kda_decode(q, k, v, g, b, o, pool, slots, slots, scale=0.5)
+    torch.cuda.synchronize()
+    U.assert_close("o", U.to_np(o), ref["o"], rel=1e-5, mx=1e-4)
+    U.assert_close("state", U.to_np(pool), ref["final"], rel=1e-5, mx=1e-4)
+
+
+def test_decode_strided_inputs(dev, oracle64):
+    """q, k, v as views into one fused projection buffer (token stride 3*H*d)."""
+    U.say("decode strided")
+    wl = make_workload(1, n_seq=7, H=4, d=64)
+    init, has = _oracle_states(wl)
+    ref = oracle64.kda_varlen(wl.q, wl.k, wl.v, wl.g, wl.beta, wl.cu_seqlens, init=init,
+                              has_init=has)
+    fused = torch.cat([wl.q, wl.k, wl.v], dim=1).to(dev)  # [N, 3H, d]
+    q, k, v = fused[:, 0:4], fused[:, 4:8], fused[:, 8:12]
+    g, b = wl.g.to(dev), wl.beta.to(dev)
+    pool = wl.init_states.to(dev).clone()
+    slots = torch.arange(7, dtype=torch.int32, device=dev)
+    o = torch.empty(7, 4, 64, dtype=torch.bfloat16, device=dev)
+    K.kda_decode(q, k, v, g, b, o, pool, slots, slots)
+    torch.cuda.synchronize()
+    U.assert_close("o", U.to_np(o), ref["o"])
+    U.assert_close("state", U.to_np(pool), ref["final"], rel=1e-5, mx=1e-4)
+
+
+# ------------------------------------------------------------------ verify
+def test_verify_fused_128x8(dev, oracle64):
+    """Speculative verify: 128 sequences x 8 tokens, outputs at all positions,
+    state committed after exactly L ~ U{1..8} tokens; commit index exact."""
+    U.say("verify fused 128 x 8")
+    wl = make_workload(4)
+    L = wl.accepted_len
+    ref = oracle64.kda_verify(wl.q, wl.k, wl.v, wl.g, wl.beta, wl.init_states, L)
+    q, k, v, g, b = (t.to(dev) for t in (wl.q, wl.k, wl.v, wl.g, wl.beta))
+    pool = torch.cat([wl.init_states, torch.zeros_like(wl.init_states)]).to(dev)
+    src = torch.arange(128, dtype=torch.int32, device=dev)
+    dst = src + 128
+    o = torch.empty(128, 8, 16, 128, dtype=torch.bfloat16, device=dev)
+    clen = torch.full((128,), -7, dtype=torch.int32, device=dev)
+    K.kda_verify(q, k, v, g, b, pool, src, dst, o=o, accepted_len=L.to(dev), committed_len_out=clen)
+    torch.cuda.synchronize()
+    assert torch.equal(clen.cpu(), L), "committed length differs"
+    assert np.array_equal(ref["committed_len"], L.numpy())
+    U.assert_close("o", U.to_np(o), ref["o"])
+    U.assert_close("committed", U.to_np(pool[128:]), ref["committed"], rel=1e-5, mx=1e-4)
+    assert torch.equal(pool[:128].cpu(), wl.init_states), "source states modified"
+
+
+def test_verify_two_phase_equals_fused(dev):
+    """Outputs-only then commit-only gives bit-identical outputs and states to
+    the fused pass (same arithmetic in the same order)."""
+    U.say("verify two-phase == fused")
+    wl = make_workload(4, n_seq=32)
+    q, k, v, g, b = (t.to(dev) for t in (wl.q, wl.k, wl.v, wl.g, wl.beta))
+    L = wl.accepted_len.to(dev)
+    pool_f = wl.init_states.to(dev).clone()
+    pool_t = wl.init_states.to(dev).clone()
+    slots = torch.arange(32, dtype=torch.int32, device=dev)
+    o_f = torch.empty(32, 8, 16, 128, device=dev)
+    o_t = torch.empty(32, 8, 16, 128, device=dev)
+    K.kda_verify(q, k, v, g, b, pool_f, slots, slots, o=o_f, accepted_len=L)
+    K.kda_verify(q, k, v, g, b, pool_t, slots, slots, o=o_t)       # outputs only
+    torch.cuda.synchronize()
+    assert torch.equal(pool_t, wl.init_states.to(dev)), "outputs-only pass wrote the pool"
+    K.kda_verify(q, k, v, g, b, pool_t, slots, slots, accepted_len=L)  # commit only
+    torch.cuda.synchronize()
+    assert torch.equal(o_f, o_t)
+    assert torch.equal(pool_f, pool_t)
+
+
+def test_verify_edge_lengths(dev, oracle64):
+    """L = 0 commits the source state; L outside [0, T_spec] is rejected
+    (committed length -1, destination untouched); L = T_spec equals T_spec
+    decode steps."""
+    U.say("verify edge lengths")
+    wl = make_workload(4, n_seq=6, H=2, d=32)
+    L = torch.tensor([0, 8, -1, 9, 3, 1], dtype=torch.int32)
+    ref = oracle64.kda_verify(wl.q, wl.k, wl.v, wl.g, wl.beta, wl.init_states, L)
+    q, k, v, g, b = (t.to(dev) for t in (wl.q, wl.k, wl.v, wl.g, wl.beta))
+    pool = torch.cat([wl.init_states, torch.full_like(wl.init_states, 7.0)]).to(dev)
+    src = torch.arange(6, dtype=torch.int32, device=dev)
+    dst = src + 6
+    clen = torch.zeros(6, dtype=torch.int32, device=dev)
+    o = torch.empty(6, 8, 2, 32, device=dev)
+    K.kda_verify(q, k, v, g, b, pool, src, dst, o=o, accepted_len=L.to(dev), committed_len_out=clen)
+    torch.cuda.synchronize()
+    assert clen.cpu().tolist() == [0, 8, -1, -1, 3, 1]
+    assert torch.equal(pool[6].cpu(), wl.init_states[0])
+    assert torch.all(pool[8] == 7.0) and torch.all(pool[9] == 7.0)
+    for s in (1, 4, 5):
+        U.assert_close(f"committed[{s}]", U.to_np(pool[6 + s]), ref["committed"][s], rel=1e-5, mx=1e-4)
+    U.assert_close("o", U.to_np(o), ref["o"], rel=1e-5, mx=1e-4)
+    # L = T_spec commit equals 8 in-place decode steps
+    pool_d = wl.init_states[1:2].to(dev).clone()
+    z = torch.zeros(1, dtype=torch.int32, device=dev)
+    od = torch.empty(1, 2, 32, device=dev)
+    for t in range(8):
+        K.kda_decode(q[1:2, t], k[1:2, t], v[1:2, t], g[1:2, t], b[1:2, t], od, pool_d, z, z)
+        torch.cuda.synchronize()
+        assert torch.equal(od[0], o[1, t])
+    assert torch.equal(pool_d[0], pool[7])
+
+
+def test_verify_commit_index_probe(dev):
+    """alpha = 1, beta = 1, exactly orthonormal keys, queries = keys: the
+    committed state reads back v_j for j < L and the source state's value for
+    j >= L, so the commit index is recovered exactly from the state."""
+    U.say("verify commit-index probe")
+    import oracle_pins as P
+    r = np.random.default_rng(5)
+    N, Ts, H, d = 16, 8, 1, 16
+    keys = P.exact_orthonormal_rows(r, d)[:Ts]
+    k = torch.tensor(np.broadcast_to(keys[None, :, None, :], (N, Ts, H, d)).copy(), dtype=torch.float32)
+    v = torch.tensor(r.standard_normal((N, Ts, H, d)), dtype=torch.float32)
+    g = torch.zeros(N, Ts, H, d)
+    b = torch.ones(N, Ts, H)
+    S0 = torch.tensor(r.standard_normal((N, H, d, d)), dtype=torch.float32)
+    L = torch.tensor(r.integers(0, Ts + 1, N), dtype=torch.int32)
+    pool = torch.cat([S0, torch.zeros_like(S0)]).to(dev)
+    src = torch.arange(N, dtype=torch.int32, device=dev)
+    K.kda_verify(k.to(dev), k.to(dev), v.to(dev), g.to(dev), b.to(dev), pool, src, src + N,
+                 accepted_len=L.to(dev))
+    torch.cuda.synchronize()
+    S = pool[N:].double().cpu().numpy()
+    kk = keys.astype(np.float64)
+    for s in range(N):
+        readout = S[s, 0].T @ kk.T  # [d_v, Ts]: column j = S^T k_j
+        written = [np.allclose(readout[:, j], v[s, j, 0].numpy(), atol=1e-5) for j in range(Ts)]
+        recovered = 0
+        while recovered < Ts and written[recovered]:
+            recovered += 1
+        assert recovered == int(L[s]), (s, recovered, int(L[s]))
+        for j in range(int(L[s]), Ts):
+            np.testing.assert_allclose(readout[:, j], S0[s, 0].double().numpy().T @ kk[j], atol=1e-5)
