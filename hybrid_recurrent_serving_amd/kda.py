@@ -186,7 +186,8 @@ def _device_tensors(**named):
 
 def _same_dtype(ref, **named):
     for name, t in named.items():
-        _expect(t is None or t.dtype == ref.dtype, f"{name}: dtype {t.dtype} != {ref.dtype}")
+        if t is not None:
+            _expect(t.dtype == ref.dtype, f"{name}: dtype {t.dtype} != {ref.dtype}")
 
 
 def _stream(stream) -> int:

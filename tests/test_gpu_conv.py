@@ -23,9 +23,11 @@ def dev():
 def _check_y(name, y_gpu, y_ref, dtype):
     got = U.to_np(y_gpu)
     if dtype == torch.bfloat16:
-        # one rounding of the fp32 sum: within a bf16 unit of the exact value
+        # One rounding of the fp32 sum: every element within half a bf16 unit
+        # of the exact value (this bounds the absolute error by 2^-8 |y|, so
+        # no fixed max-abs bar applies: |y| reaches ~5 with the bias).
         assert U.within_bf16_of(got, y_ref), f"{name}: beyond one bf16 rounding"
-        U.assert_close(name, got, y_ref)
+        U.assert_close(name, got, y_ref, mx=2.0 ** -8 * float(np.abs(y_ref).max()) + 1e-6)
     else:
         U.assert_close(name, got, y_ref, rel=1e-6, mx=1e-5)
 
