@@ -156,8 +156,8 @@ int kda_conv_short(const kda_conv_args* a, kda_stream_t stream_) {
   if (b.x_stride < b.C || b.y_stride < b.C) return fail(KDA_ERR_SHAPE, "conv stride < C");
   const int64_t eb = dtype_bytes(b.dtype);
   if ((b.x_stride * eb) % 16 || (b.y_stride * eb) % 16 || !aligned16(b.x) || !aligned16(b.y) ||
-      !aligned16(b.conv_pool))
-    return fail(KDA_ERR_ALIGN, "conv: x, y or conv_pool not 16-byte aligned");
+      !aligned16(b.conv_pool) || !aligned16(b.weight))
+    return fail(KDA_ERR_ALIGN, "conv: x, y, weight or conv_pool not 16-byte aligned");
   if (b.T_tot / 64 + b.n_seq > 0x7fffffffLL) return fail(KDA_ERR_SHAPE, "conv: too many tokens");
   if (check_enabled()) {
     int st = check_cu(b.cu_seqlens, b.n_seq, b.T_tot, stream);

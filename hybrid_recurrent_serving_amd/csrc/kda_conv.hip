@@ -56,6 +56,31 @@ template <> struct Vec16<float> {
   __device__ static __forceinline__ void st(float* p, const float (&x)[4]) { io<float>::st4(p, x); }
 };
 
+// NB consecutive 16-byte vectors starting at p (16-byte aligned) <-> floats
+template <typename T, int NB>
+__device__ __forceinline__ void ld_blocks(const T* p, float (&x)[NB * Vec16<T>::N]) {
+  constexpr int V = Vec16<T>::N;
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    float t[V];
+    Vec16<T>::ld(p + b * V, t);
+#pragma unroll
+    for (int i = 0; i < V; ++i) x[b * V + i] = t[i];
+  }
+}
+
+template <typename T, int NB>
+__device__ __forceinline__ void st_blocks(T* p, const float (&x)[NB * Vec16<T>::N]) {
+  constexpr int V = Vec16<T>::N;
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    float t[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) t[i] = x[b * V + i];
+    Vec16<T>::st(p + b * V, t);
+  }
+}
+
 __device__ __forceinline__ float conv_finish(float acc, int act) {
   if (act == 1) acc = acc / (1.f + expf(-acc));
   return acc;
@@ -71,14 +96,16 @@ __global__ void __launch_bounds__(CONV_THREADS) conv_kernel(const ConvParams p) 
   const T* xb = static_cast<const T*>(p.x);
   T* yb = static_cast<T*>(p.y);
 
-  // taps of my channels: wt[j][i] = w[c0 + i, j]
+  // taps of my channels: wt[j][i] = w[c0 + i, j]; the V*W taps are
+  // contiguous (W 16-byte vectors)
   float wt[W][V];
   {
-    const T* wp = static_cast<const T*>(p.w) + c0 * W;
+    float flat[W * V];
+    ld_blocks<T, W>(static_cast<const T*>(p.w) + c0 * W, flat);
 #pragma unroll
     for (int i = 0; i < V; ++i)
 #pragma unroll
-      for (int j = 0; j < W; ++j) wt[j][i] = io<T>::ld(wp + i * W + j);
+      for (int j = 0; j < W; ++j) wt[j][i] = flat[i * W + j];
   }
   float bias[V];
 #pragma unroll
@@ -98,11 +125,13 @@ __global__ void __launch_bounds__(CONV_THREADS) conv_kernel(const ConvParams p) 
     // xh[j] = xbar[j] for j < 2*HIST: history then the first HIST tokens
     float xh[2 * HIST][V];
     if (has_src) {
-      const T* sp = static_cast<const T*>(p.pool) + (static_cast<int64_t>(src) * p.C + c0) * HIST;
+      // the V channels' histories are V*HIST contiguous elements (HIST vectors)
+      float flat[HIST * V];
+      ld_blocks<T, HIST>(static_cast<const T*>(p.pool) + (static_cast<int64_t>(src) * p.C + c0) * HIST, flat);
 #pragma unroll
       for (int j = 0; j < HIST; ++j)
 #pragma unroll
-        for (int i = 0; i < V; ++i) xh[j][i] = io<T>::ld(sp + i * HIST + j);
+        for (int i = 0; i < V; ++i) xh[j][i] = flat[i * HIST + j];
     } else {
 #pragma unroll
       for (int j = 0; j < HIST; ++j)
@@ -153,11 +182,12 @@ __global__ void __launch_bounds__(CONV_THREADS) conv_kernel(const ConvParams p) 
       }
     }
     if (has_dst) {
-      T* dp = static_cast<T*>(p.pool) + (static_cast<int64_t>(dst) * p.C + c0) * HIST;
+      float flat[HIST * V];
 #pragma unroll
       for (int j = 0; j < HIST; ++j)
 #pragma unroll
-        for (int i = 0; i < V; ++i) io<T>::st(dp + i * HIST + j, ns[j][i]);
+        for (int i = 0; i < V; ++i) flat[i * HIST + j] = ns[j][i];
+      st_blocks<T, HIST>(static_cast<T*>(p.pool) + (static_cast<int64_t>(dst) * p.C + c0) * HIST, flat);
     }
     return;
   }
