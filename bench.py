@@ -41,7 +41,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", default="decode", choices=["decode", "verify"])
+    ap.add_argument("--workload", default="decode", choices=["decode", "prefill"])
     ap.add_argument("--pools", type=int, default=4, help="rotating state pools (MALL defeat)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle time budget")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
@@ -175,6 +175,9 @@ def bench_decode(args, torch, K, make_workload):
                                         "GB_s": round(state_bytes / cp_us / 1e3, 1)}
         del srcs, dsts, src_t, dst_t
         secondary["verify"] = bench_verify_secondary(torch, K, make_workload, dev)
+        pf = bench_prefill_varlen(torch, K, make_workload, dev, iters=10)
+        secondary["prefill_varlen"] = {k_: pf[k_] for k_ in ("workload", "tokens", "ms", "tokens_per_s",
+                                                             "alg_mfma_frac", "alg_hbm_frac")}
 
     cpu = None
     if not args.no_cpu:
@@ -222,6 +225,108 @@ def bench_verify_secondary(torch, K, make_workload, dev):
             "hbm_frac": round((state_bytes + io) / us / 1e3 / HBM_PEAK_GBS, 4)}
 
 
+PREFILL_BYTES_PER_TOKEN = 16 * (4 * 128 * 2 + 2 + 128 * 2)      # q,k,v,g + beta + o (bf16), H=16
+PREFILL_FLOPS_PER_TOKEN = 16 * (10 * 64 * 128 + 6 * 128 * 128)    # dense chunked count at C=64
+
+
+def bench_prefill_varlen(torch, K, make_workload, dev, iters=20, wl=None):
+    """16 packed sequences, lengths U{512..16384}, H=16, d=128, chunk 64,
+    even sequences from random initial states, final states to fresh slots."""
+    if wl is None:
+        wl = make_workload(2)
+    N, H, D = wl.n_seq, 16, 128
+    q, k, v, g, b = (t.to(dev) for t in (wl.q, wl.k, wl.v, wl.g, wl.beta))
+    T = q.shape[0]
+    pool = torch.zeros(2 * N, H, D, D, device=dev)
+    for s_, i in enumerate(wl.init_index):
+        if i >= 0:
+            pool[s_] = wl.init_states[i].to(dev)
+    src = torch.tensor([s_ if i >= 0 else -1 for s_, i in enumerate(wl.init_index)], dtype=torch.int32,
+                       device=dev)
+    dst = torch.arange(N, 2 * N, dtype=torch.int32, device=dev)
+    cu = wl.cu_seqlens.to(dev)
+    o = torch.empty(T, H, D, dtype=torch.bfloat16, device=dev)
+
+    def run():
+        K.kda_prefill_varlen(q, k, v, g, b, o, cu, pool, src, dst, chunk=64)
+
+    for _ in range(2):
+        run()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+    torch.cuda.synchronize()
+    for e0, e1 in evs:
+        e0.record()
+        run()
+        e1.record()
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b_) for a, b_ in evs) / iters
+    tps = T / (ms * 1e-3)
+    return {"workload": "varlen prefill: 16 seqs, lengths U{512..16384}, H=16, d=128, chunk 64, bf16",
+            "tokens": T, "ms": round(ms, 4), "tokens_per_s": round(tps, 1),
+            "alg_mfma_frac": round(tps * PREFILL_FLOPS_PER_TOKEN / (MFMA_BF16_PEAK_TFLOPS * 1e12), 4),
+            "alg_hbm_frac": round(tps * PREFILL_BYTES_PER_TOKEN / (HBM_PEAK_GBS * 1e9), 4),
+            "wl": wl}
+
+
+def bench_prefill(args, torch, K, make_workload):
+    dev = torch.device("cuda:0")
+    wl = make_workload(2)
+    pf = bench_prefill_varlen(torch, K, make_workload, dev, iters=args.steps, wl=wl)
+    T = pf["tokens"]
+    achieved = T * PREFILL_BYTES_PER_TOKEN / (pf["ms"] * 1e-3) / 1e9
+    roof = {"kernel": "prefill_kernel<128,bf16,bf16> (kda_prefill_varlen)", "bound": "hbm",
+            "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic_for("prefill_kernel_d128_bf16", "kda_prefill.hip", T),
+            "alg_bytes_per_launch": T * PREFILL_BYTES_PER_TOKEN, "avg_launch_us": round(pf["ms"] * 1e3, 2),
+            "mfma": {"alg_flops_per_launch": T * PREFILL_FLOPS_PER_TOKEN,
+                     "achieved_tflops": round(T * PREFILL_FLOPS_PER_TOKEN / (pf["ms"] * 1e-3) / 1e12, 1),
+                     "peak_tflops": MFMA_BF16_PEAK_TFLOPS, "frac": pf["alg_mfma_frac"]}}
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_prefill(args, wl)
+    cfg = {"workload": pf["workload"], "tokens": T, "H": 16, "d": 128, "chunk": 64,
+           "initial_states": "even-indexed sequences"}
+    return {"metric": METRIC, "value": pf["tokens_per_s"], "unit": "tokens/s", "ms_per_step": pf["ms"],
+            "dtype": "bf16-mfma/f32-acc", "config": cfg, "roofline": roof, "cpu_baseline": cpu,
+            "secondary": {}}
+
+
+def cpu_prefill(args, wl):
+    """Oracle on whole (sequence, head) pairs of the same workload until the
+    time budget is spent; tokens/s scaled to all 16 heads."""
+    import numpy as np
+    import oracle
+    orc = oracle.load("f64")
+    threads = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    orc.set_threads(threads)
+    N = wl.n_seq
+    init = np.zeros((N, 16, 128, 128))
+    has = np.zeros(N, np.int32)
+    for s_, i in enumerate(wl.init_index):
+        if i >= 0:
+            init[s_] = wl.init_states[i].double().numpy()
+            has[s_] = 1
+    q, k, v, g, b = (t.float().numpy() for t in (wl.q, wl.k, wl.v, wl.g, wl.beta))
+    lens = (wl.cu_seqlens[1:] - wl.cu_seqlens[:-1]).tolist()
+    order = sorted(range(N), key=lambda s_: lens[s_])   # shortest sequences first
+    tok_heads = 0
+    t0 = time.perf_counter()
+    done = []
+    for s_ in order:
+        pairs = [(s_, h) for h in range(16)]
+        orc.kda_varlen(q, k, v, g, b, wl.cu_seqlens, init=init, has_init=has, pairs=pairs)
+        tok_heads += lens[s_] * 16
+        done.append(s_)
+        if time.perf_counter() - t0 > args.cpu_seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(tok_heads / 16 / dt, 1), "unit": "tokens/s", "cores": orc.threads(),
+            "kind": "oracle", "cpu": cpu_info(),
+            "sample": f"{len(done)} of 16 sequences (all 16 heads each, {tok_heads // 16} tokens), "
+                      f"fp64 oracle, {dt:.1f} s"}
+
+
 def cpu_decode(args, wl, state_bytes):
     import numpy as np
     import oracle
@@ -263,7 +368,7 @@ def main():
     if args.workload == "decode":
         res = bench_decode(args, torch, K, make_workload)
     else:
-        raise SystemExit("verify workload is reported in the decode line's 'secondary' block")
+        res = bench_prefill(args, torch, K, make_workload)
     line = {"metric": res["metric"], "value": res["value"], "unit": res["unit"], "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(res["ms_per_step"], 6),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
