@@ -25,15 +25,15 @@
 // Every exponential factor is at most exp(decay over 16 tokens); the two
 // state factors are <= 1.
 //
-// Work split: a workgroup of 4 waves owns one (sequence, head); two
-// workgroups share a CU (LDS <= 80 KB, <= 256 VGPRs), so one workgroup's
-// matrix-core chain overlaps the other's VALU / LDS operand preparation.
-// Wave w owns columns [32w, 32w + 32) of the d_v axis: its slice of the fp32
-// state lives in matrix-core accumulator registers for the whole sequence,
-// and the state-dependent chain (u, O, state update) never leaves the wave.
-// The chunk-local operands (gates, A, T, P, W) are built cooperatively in
-// LDS.  The next chunk's raw tiles are loaded into registers while the
-// current chunk is processed.
+// Work split: a workgroup of 8 waves (2 per SIMD) owns one (sequence, head).
+// Wave w owns columns [16w, 16w + 16) of the d_v axis: its slice of the fp32
+// state lives in matrix-core accumulator registers (16x16 tiles) for the
+// whole sequence, and the state-dependent chain (u, O, state update) never
+// leaves the wave; the two waves on a SIMD run independent chains, which
+// hides each other's matrix-core and LDS latency.  The chunk-local operands
+// (gates, A, T, P, W) are built cooperatively in LDS (~84 KB).  The next
+// chunk's raw tiles are loaded into registers while the current chunk is
+// processed.
 //
 // Matrix-core precision (bf16 operands, fp32 accumulation); an operand
 // marked "pair" is carried as hi + lo bf16 (hi*hi + hi*lo + lo*hi):
@@ -47,9 +47,10 @@
 //
 // Layout tricks:
 //  * Contractions whose operand comes from accumulator registers (S' over
-//    the key channels, u over chunk rows) use a fixed permutation of the
-//    contracted index inside each block of 16 (groups of four 1 and 2
-//    swapped); the LDS operands on the other side are stored in that order.
+//    the key channels, u over chunk rows) take a fragment from two
+//    vertically adjacent 16x16 accumulator tiles; inside each block of 32
+//    the contracted index is therefore stored in the order pos32 (below) in
+//    the LDS operand on the other side.
 //  * Operands that must be read K-contiguous from a row-major tile (right_k^T,
 //    left_k and V over chunk rows) use the gfx950 LDS transpose read
 //    (ds_read_b64_tr_b16): four lanes of a 16-lane group read one row each,
@@ -62,19 +63,28 @@ namespace kda {
 namespace pf {
 
 constexpr int TILE = 32;   // rows per chunk tile
-constexpr int NT = 256;    // threads per workgroup (4 waves)
+constexpr int NW = 8;      // waves per workgroup
+constexpr int NT = 64 * NW;
 constexpr int MID = 15;    // reference row of the gates
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
-typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 
-// storage position of contracted index c (self-inverse): swap 4-groups 1, 2
-__host__ __device__ constexpr int perm16(int c) {
-  return (c & ~15) | ((((c >> 2) & 3) == 1 ? 2 : (((c >> 2) & 3) == 2 ? 1 : ((c >> 2) & 3))) << 2) | (c & 3);
+// Storage position of contracted index c inside its block of 32: the
+// fragment slot 8g + e (g = lane / 16, e = 0..7) of a contraction fed from
+// accumulator tiles holds row 4g + e (e < 4) of the upper tile and row
+// 16 + 4g + e - 4 (e >= 4) of the lower tile.
+__host__ __device__ constexpr int pos32(int c) {
+  return (c & ~31) | (8 * ((c & 15) >> 2)) | (4 * ((c >> 4) & 1)) | (c & 3);
 }
-__device__ __forceinline__ int swap4(int i) { return i == 1 ? 2 : (i == 2 ? 1 : i); }
+
+// Workgroup barrier that orders LDS traffic only.  Waves exchange data
+// through LDS alone, so outstanding global loads (the prefetched next tile)
+// and stores may stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 // fp32 -> bf16 bits (hardware round to nearest even)
 __device__ __forceinline__ uint32_t cvt2(float a, float b) {
@@ -100,8 +110,15 @@ __device__ __forceinline__ bf16x8 join(s16x4 a, s16x4 b) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
+// store 4 floats as bf16 (8 bytes)
+__device__ __forceinline__ void st4b(bf16_t* p, const float* x) {
+  uint2 u;
+  u.x = cvt2(x[0], x[1]);
+  u.y = cvt2(x[2], x[3]);
+  *reinterpret_cast<uint2*>(p) = u;
+}
 // store 8 floats as bf16 (16 bytes)
-__device__ __forceinline__ void st8(bf16_t* p, const float* x) {
+__device__ __forceinline__ void st8b(bf16_t* p, const float* x) {
   uint4 u;
   u.x = cvt2(x[0], x[1]);
   u.y = cvt2(x[2], x[3]);
@@ -110,14 +127,14 @@ __device__ __forceinline__ void st8(bf16_t* p, const float* x) {
   *reinterpret_cast<uint4*>(p) = u;
 }
 
-// 8 accumulator values [E0, E0 + 8) as a bf16 hi / lo fragment pair
-template <int E0>
-__device__ __forceinline__ void frag_acc_pair(const f32x16& a, bf16x8& hi, bf16x8& lo) {
+// fragment (and hi / lo pair) from two vertically adjacent accumulator tiles
+__device__ __forceinline__ void frag_pair(const f32x4& a, const f32x4& b, bf16x8& hi, bf16x8& lo) {
+  const float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
   float h[8], l[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    h[i] = hi_of(a[E0 + i]);
-    l[i] = a[E0 + i] - h[i];
+    h[i] = hi_of(x[i]);
+    l[i] = x[i] - h[i];
   }
   uint4 uh, ul;
   uh.x = cvt2(h[0], h[1]); uh.y = cvt2(h[2], h[3]); uh.z = cvt2(h[4], h[5]); uh.w = cvt2(h[6], h[7]);
@@ -126,63 +143,52 @@ __device__ __forceinline__ void frag_acc_pair(const f32x16& a, bf16x8& hi, bf16x
   lo = __builtin_bit_cast(bf16x8, ul);
 }
 
-__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// row (within a 32-row tile) of 32x32 accumulator element e held by lane
-__device__ __forceinline__ int acc_row(int e, int lane) { return 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3); }
-
-// Transpose-read fragment (32x32x16 operand, 8 contracted values per lane)
-// of a row-major bf16 tile M[k][x] (row pitch `pitch` elements): lane l gets
-// M[k0 + 8(l/32) + e][x0 + l % 32] for e = 0..7.
-__device__ __forceinline__ bf16x8 frag_tr(const bf16_t* M, int pitch, int k0, int x0, int lane) {
-  const int g = lane >> 4, j = (lane >> 2) & 3, i = lane & 3;
-  const int kk = k0 + 8 * (g >> 1) + j;
-  const int xx = x0 + 16 * (g & 1) + 4 * i;
-  return join(tr4(M + kk * pitch + xx), tr4(M + (kk + 4) * pitch + xx));
-}
-
 // The state slice of a chain wave <-> a pool slot [c][n] (fp32).  Kept out of
-// line: called once per sequence and per checkpoint, and inlining it makes the
-// compiler hold 64 loop-invariant addresses across the chunk loop.
+// line: called once per sequence and per checkpoint; inlined it would hold
+// loop-invariant addresses across the chunk loop.
 template <int D>
-__device__ __attribute__((noinline)) void state_store(float* base, const f32x16* S, int lane, int ncol, int d) {
+__device__ __attribute__((noinline)) void state_store(float* base, const f32x4* S, int lane, int ncol, int d) {
 #pragma unroll
-  for (int t = 0; t < D / 32; ++t)
+  for (int q = 0; q < D / 16; ++q)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int c = 32 * t + acc_row(e, lane);
-      if (c < d) base[c * d + ncol] = S[t][e];
+    for (int i = 0; i < 4; ++i) {
+      const int c = 16 * q + 4 * (lane >> 4) + i;
+      if (c < d) base[c * d + ncol] = S[q][i];
     }
 }
 
 template <int D>
-__device__ __attribute__((noinline)) void state_load(const float* base, f32x16* S, int lane, int ncol, int d) {
+__device__ __attribute__((noinline)) void state_load(const float* base, f32x4* S, int lane, int ncol, int d) {
 #pragma unroll
-  for (int t = 0; t < D / 32; ++t)
+  for (int q = 0; q < D / 16; ++q)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int c = 32 * t + acc_row(e, lane);
+    for (int i = 0; i < 4; ++i) {
+      const int c = 16 * q + 4 * (lane >> 4) + i;
       const float v = base[(c < d ? c : 0) * d + ncol];
-      S[t][e] = c < d ? v : 0.f;
+      S[q][i] = c < d ? v : 0.f;
     }
 }
 
+// Row pitches of the bf16 tiles are padded (by 32 bytes for the [32][D]
+// tiles, to 80 bytes for the [32][32] ones) so that the 16-byte fragment reads
+// of 16 rows and the transpose reads of 4 x 4 rows spread over the LDS banks.
 template <int D, typename TIN>
 struct Smem {
   static constexpr bool F32IN = sizeof(TIN) == 4;
-  bf16_t lq_hi[TILE][D];      // [r][perm(c)]   (reused for output staging)
-  bf16_t lq_lo[TILE][D];
-  bf16_t lk[TILE][D];         // [r][perm(c)]
-  bf16_t lk_lo[F32IN ? TILE : 1][D];
-  bf16_t rk_hi[TILE][D];      // [s][perm(c)]
-  bf16_t rk_lo[TILE][D];
-  bf16_t v_hi[TILE][D];       // [s][n]
-  bf16_t v_lo[F32IN ? TILE : 1][D];
+  static constexpr int PD = D + 16;   // padded pitch of [TILE][D] bf16 tiles
+  static constexpr int PT = TILE + 8; // padded pitch of [TILE][TILE] bf16 tiles
+  bf16_t lq_hi[TILE][PD];     // [r][pos32(c)]   (reused for output staging)
+  bf16_t lq_lo[TILE][PD];
+  bf16_t lk[TILE][PD];        // [r][pos32(c)]
+  bf16_t lk_lo[F32IN ? TILE : 1][PD];
+  bf16_t rk_hi[TILE][PD];     // [s][pos32(c)]
+  bf16_t rk_lo[TILE][PD];
+  bf16_t v_hi[TILE][PD];      // [s][n]
+  bf16_t v_lo[F32IN ? TILE : 1][PD];
   float eg_m[D];              // exp(G_m)
   float eg_e[D];              // exp(G_last - G_m)
   float beta[TILE];
@@ -190,62 +196,63 @@ struct Smem {
     struct {
       TIN g_raw[TILE][D];
       float G[TILE][D];
-      float scan[8][D];
+      float scan[NT];
     } a;
     struct {
       float A[TILE][TILE];
       float Tf[TILE][TILE];
       float X[16][16];
-      bf16_t Tm[TILE][TILE];  // [r][s]
-      bf16_t Tm_lo[F32IN ? TILE : 1][TILE];
-      bf16_t P_hi[TILE][TILE];  // [r][perm(s)]
-      bf16_t P_lo[TILE][TILE];
-      bf16_t Wn[TILE][D];     // -(T left_k) [r][perm(c)]
-      bf16_t Wn_lo[F32IN ? TILE : 1][D];
+      bf16_t Tm[TILE][PT];    // [r][s]
+      bf16_t Tm_lo[F32IN ? TILE : 1][PT];
+      bf16_t P_hi[TILE][PT];  // [r][pos32(s)]
+      bf16_t P_lo[TILE][PT];
+      bf16_t Wn[TILE][PD];    // -(T left_k) [r][pos32(c)]
+      bf16_t Wn_lo[F32IN ? TILE : 1][PD];
     } b;
   } u;
 };
 
-// raw 16-channel slice of one token row (q, k, v, g) as 16-byte vectors
+// raw slice of one token row: channels {c0..c0+3} and {c0+16..c0+19} of q, k, v, g
 template <typename TIN>
 struct RawRow {
-  static constexpr int NV = 16 * sizeof(TIN) / 16;   // uint4 per tensor
-  uint4 q[NV], k[NV], v[NV], g[NV];
+  static constexpr int NU = 4 * sizeof(TIN) / 8;   // 8-byte units per 4-channel group
+  uint2 q[2 * NU], k[2 * NU], v[2 * NU], g[2 * NU];
 };
 
 template <typename TIN>
-__device__ __forceinline__ void to_f32(const uint4 (&w)[RawRow<TIN>::NV], float (&x)[16]) {
+__device__ __forceinline__ void to_f32(const uint2* w, float (&x)[8]) {
   if constexpr (sizeof(TIN) == 2) {
-    const uint32_t u[8] = {w[0].x, w[0].y, w[0].z, w[0].w, w[1].x, w[1].y, w[1].z, w[1].w};
+    const uint32_t u[4] = {w[0].x, w[0].y, w[1].x, w[1].y};
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 4; ++i) {
       x[2 * i] = __uint_as_float(u[i] << 16);
       x[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
     }
   } else {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      x[4 * i] = __uint_as_float(w[i].x);
-      x[4 * i + 1] = __uint_as_float(w[i].y);
-      x[4 * i + 2] = __uint_as_float(w[i].z);
-      x[4 * i + 3] = __uint_as_float(w[i].w);
+      x[2 * i] = __uint_as_float(w[i].x);
+      x[2 * i + 1] = __uint_as_float(w[i].y);
     }
   }
 }
 
 // ---------------------------------------------------------------------------
 template <int D, typename TIN, typename TOUT>
-__global__ void __launch_bounds__(NT, 2) prefill_kernel(const PrefillParams p, const int d, const int CH) {
+__global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, const int d, const int CH) {
   using SM = Smem<D, TIN>;
   __shared__ SM sm;
   constexpr bool HP = SM::F32IN;        // all products as pairs
-  constexpr int NWC = D / 32;           // waves that own state columns
-  constexpr int NB = D / 16;            // 16-channel blocks per row
-  constexpr int NITEM = TILE * NB;      // (row, block) items per chunk
-  constexpr int NV = RawRow<TIN>::NV;
+  constexpr int NWC = D / 16;           // waves that own state columns
+  constexpr int NQ = D / 16;            // 16-row state tiles per wave
+  constexpr int NPB = D / 8;            // 8-position blocks per row
+  constexpr int NITEM = TILE * NPB;     // (row, position block) items per chunk
+  constexpr int NU = RawRow<TIN>::NU;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const int g4 = lane >> 4;             // 16-lane group
+  const int l16 = lane & 15;
   const int s = static_cast<int>(blockIdx.x / p.H);
   const int h = static_cast<int>(blockIdx.x % p.H);
   const int H = p.H;
@@ -262,14 +269,12 @@ __global__ void __launch_bounds__(NT, 2) prefill_kernel(const PrefillParams p, c
   const bool has_src = src >= 0 && src < p.n_slots;
   const bool has_dst = dst >= 0 && dst < p.n_slots;
   const bool chain = wave < NWC;
-  const int ncol = 32 * wave + (lane & 31);   // d_v column of this lane (chain waves)
+  const int ncol = 16 * wave + l16;     // d_v column of this lane (chain waves)
 
-  // ---- state: D x 32 slice per chain wave, fp32 accumulators
-  f32x16 S[D / 32];
+  // ---- state: D x 16 slice per chain wave, NQ tiles of 16 x 16 (fp32)
+  f32x4 S[NQ];
 #pragma unroll
-  for (int t = 0; t < D / 32; ++t)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) S[t][e] = 0.f;
+  for (int q = 0; q < NQ; ++q) S[q] = f32x4{0.f, 0.f, 0.f, 0.f};
   if (chain && has_src && ncol < d) state_load<D>(p.pool + (static_cast<int64_t>(src) * H + h) * d * d, S, lane, ncol, d);
 
   const TIN* qg = static_cast<const TIN*>(p.q);
@@ -279,33 +284,39 @@ __global__ void __launch_bounds__(NT, 2) prefill_kernel(const PrefillParams p, c
   const TIN* bg = static_cast<const TIN*>(p.beta);
   TOUT* og = static_cast<TOUT*>(p.o);
 
-  // raw-tile item of this thread: row ir, channels [16 ib, 16 ib + 16)
+  // raw-tile item of this thread: row ir, positions [8 ib, 8 ib + 8) which
+  // hold channels c0..c0+3 and c0+16..c0+19
   const bool has_item = tid < NITEM;
-  const int ir = tid / NB;
-  const int ib = tid % NB;
+  const int ir = tid / NPB;
+  const int ib = tid % NPB;
+  const int c0 = 32 * (ib >> 2) + 4 * (ib & 3);
 
   auto load_raw = [&](int64_t base, RawRow<TIN>& rr) {
     const int64_t pos = base + ir;
-    const bool valid = has_item && ir < CH && pos >= start && pos < end && 16 * ib < d;
+    const bool valid = has_item && ir < CH && pos >= start && pos < end && c0 < d;
 #pragma unroll
-    for (int w = 0; w < NV; ++w) rr.q[w] = rr.k[w] = rr.v[w] = rr.g[w] = make_uint4(0, 0, 0, 0);
+    for (int w = 0; w < 2 * NU; ++w) rr.q[w] = rr.k[w] = rr.v[w] = rr.g[w] = make_uint2(0, 0);
     if (valid) {
       const int64_t tok = bos + (pos - start);
-      const int64_t off = static_cast<int64_t>(h) * d + 16 * ib;
-      const uint4* qp = reinterpret_cast<const uint4*>(qg + tok * p.q_stride + off);
-      const uint4* kp = reinterpret_cast<const uint4*>(kg + tok * p.k_stride + off);
-      const uint4* vp = reinterpret_cast<const uint4*>(vg + tok * p.v_stride + off);
-      const uint4* gp = reinterpret_cast<const uint4*>(gg + tok * p.g_stride + off);
-      // only the vectors inside d (d = 16 with 16-channel blocks: all of them)
-      const int nv = (16 * ib + 16 <= d) ? NV : ((d - 16 * ib) * static_cast<int>(sizeof(TIN))) / 16;
+      const int64_t off = static_cast<int64_t>(h) * d + c0;
+      const TIN* qp = qg + tok * p.q_stride + off;
+      const TIN* kp = kg + tok * p.k_stride + off;
+      const TIN* vp = vg + tok * p.v_stride + off;
+      const TIN* gp = gg + tok * p.g_stride + off;
+      const bool second = c0 + 16 < d;   // d = 16: only the first group exists
 #pragma unroll
-      for (int w = 0; w < NV; ++w)
-        if (w < nv) {
-          rr.q[w] = qp[w];
-          rr.k[w] = kp[w];
-          rr.v[w] = vp[w];
-          rr.g[w] = gp[w];
+      for (int w = 0; w < NU; ++w) {
+        rr.q[w] = reinterpret_cast<const uint2*>(qp)[w];
+        rr.k[w] = reinterpret_cast<const uint2*>(kp)[w];
+        rr.v[w] = reinterpret_cast<const uint2*>(vp)[w];
+        rr.g[w] = reinterpret_cast<const uint2*>(gp)[w];
+        if (second) {
+          rr.q[NU + w] = reinterpret_cast<const uint2*>(qp + 16)[w];
+          rr.k[NU + w] = reinterpret_cast<const uint2*>(kp + 16)[w];
+          rr.v[NU + w] = reinterpret_cast<const uint2*>(vp + 16)[w];
+          rr.g[NU + w] = reinterpret_cast<const uint2*>(gp + 16)[w];
         }
+      }
     }
   };
 
@@ -314,27 +325,29 @@ __global__ void __launch_bounds__(NT, 2) prefill_kernel(const PrefillParams p, c
   load_raw(first, nxt);
   for (int64_t base = first; base < end; base += CH) {
     // ------------------------------------------------ phase L: commit raw tile, prefetch next
-    RawRow<TIN> cur = nxt;
+    const RawRow<TIN> cur = nxt;
     if (base + CH < end) load_raw(base + CH, nxt);
     if (has_item) {
-      TIN* gr = &sm.u.a.g_raw[ir][16 * ib];
 #pragma unroll
-      for (int w = 0; w < NV; ++w) reinterpret_cast<uint4*>(gr)[w] = cur.g[w];
+      for (int w = 0; w < NU; ++w) {
+        reinterpret_cast<uint2*>(&sm.u.a.g_raw[ir][c0])[w] = cur.g[w];
+        reinterpret_cast<uint2*>(&sm.u.a.g_raw[ir][c0 + 16])[w] = cur.g[NU + w];
+      }
       if constexpr (HP) {
-        float vx[16], vh[16], vl[16];
+        float vx[8], vh[8], vl[8];
         to_f32<TIN>(cur.v, vx);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
+        for (int i = 0; i < 8; ++i) {
           vh[i] = hi_of(vx[i]);
           vl[i] = vx[i] - vh[i];
         }
-        st8(&sm.v_hi[ir][16 * ib], vh);
-        st8(&sm.v_hi[ir][16 * ib + 8], vh + 8);
-        st8(&sm.v_lo[ir][16 * ib], vl);
-        st8(&sm.v_lo[ir][16 * ib + 8], vl + 8);
+        st4b(&sm.v_hi[ir][c0], vh);
+        st4b(&sm.v_hi[ir][c0 + 16], vh + 4);
+        st4b(&sm.v_lo[ir][c0], vl);
+        st4b(&sm.v_lo[ir][c0 + 16], vl + 4);
       } else {
-#pragma unroll
-        for (int w = 0; w < NV; ++w) reinterpret_cast<uint4*>(&sm.v_hi[ir][16 * ib])[w] = cur.v[w];
+        *reinterpret_cast<uint2*>(&sm.v_hi[ir][c0]) = cur.v[0];
+        *reinterpret_cast<uint2*>(&sm.v_hi[ir][c0 + 16]) = cur.v[1];
       }
     }
     if (tid < TILE) {
@@ -343,7 +356,7 @@ __global__ void __launch_bounds__(NT, 2) prefill_kernel(const PrefillParams p, c
       if (tid < CH && pos >= start && pos < end) b = io<TIN>::ld(bg + (bos + (pos - start)) * p.beta_stride + h);
       sm.beta[tid] = b;
     }
-    __syncthreads();
+    lds_barrier();
     // ------------------------------------------------ phase G: cumulative gates
     {
       constexpr int NPART = NT / D;          // threads per channel
@@ -357,13 +370,13 @@ __global__ void __launch_bounds__(NT, 2) prefill_kernel(const PrefillParams p, c
         acc += io<TIN>::ld(&sm.u.a.g_raw[part * RP + i][c]);
         gl[i] = acc;
       }
-      sm.u.a.scan[part][c] = acc;
-      __syncthreads();
+      sm.u.a.scan[part * D + c] = acc;
+      lds_barrier();
       float off = 0.f;
-      for (int q = 0; q < part; ++q) off += sm.u.a.scan[q][c];
+      for (int q = 0; q < part; ++q) off += sm.u.a.scan[q * D + c];
 #pragma unroll
       for (int i = 0; i < RP; ++i) sm.u.a.G[part * RP + i][c] = gl[i] + off;
-      __syncthreads();
+      lds_barrier();
       if (tid < D) {
         const float gm = sm.u.a.G[MID][tid];
         sm.eg_m[tid] = expf(gm);
@@ -372,117 +385,113 @@ __global__ void __launch_bounds__(NT, 2) prefill_kernel(const PrefillParams p, c
     }
     // ------------------------------------------------ phase O: gated operands (row-major)
     if (has_item) {
-      float qx[16], kx[16];
+      float qx[8], kx[8];
       to_f32<TIN>(cur.q, qx);
       to_f32<TIN>(cur.k, kx);
-      // two halves of 8 storage positions; position i of the block holds
-      // channel perm16(i), so each half covers two groups of four channels
+      // positions 8 ib + e hold channels c0 + e (e < 4) and c0 + 16 + e - 4
+      float lq[8], lk[8], rk[8];
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        float lq[8], lk[8], rk[8];
+      for (int gi = 0; gi < 2; ++gi) {
+        const int cc = c0 + 16 * gi;
+        const float4 a = *reinterpret_cast<const float4*>(&sm.u.a.G[ir][cc]);
+        const float4 b = *reinterpret_cast<const float4*>(&sm.u.a.G[MID][cc]);
+        const float x4[4] = {a.x - b.x, a.y - b.y, a.z - b.z, a.w - b.w};
 #pragma unroll
-        for (int gi = 0; gi < 2; ++gi) {
-          const int c0 = perm16(8 * half + 4 * gi);   // first channel of this group of four
-          const float4 a = *reinterpret_cast<const float4*>(&sm.u.a.G[ir][16 * ib + c0]);
-          const float4 b = *reinterpret_cast<const float4*>(&sm.u.a.G[MID][16 * ib + c0]);
-          const float x4[4] = {a.x - b.x, a.y - b.y, a.z - b.z, a.w - b.w};
-#pragma unroll
-          for (int m = 0; m < 4; ++m) {
-            const int i = 4 * gi + m;
-            const float ea = fexp(x4[m]);
-            lq[i] = qx[c0 + m] * ea;
-            lk[i] = kx[c0 + m] * ea;
-            rk[i] = kx[c0 + m] * fexp(-x4[m]);
-          }
+        for (int m = 0; m < 4; ++m) {
+          const int i = 4 * gi + m;
+          const float ea = fexp(x4[m]);
+          lq[i] = qx[i] * ea;
+          lk[i] = kx[i] * ea;
+          rk[i] = kx[i] * fexp(-x4[m]);
         }
-        const int pos = 16 * ib + 8 * half;
-        float hi[8], lo[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          hi[i] = hi_of(lq[i]);
-          lo[i] = lq[i] - hi[i];
-        }
-        st8(&sm.lq_hi[ir][pos], hi);
-        st8(&sm.lq_lo[ir][pos], lo);
-        if constexpr (HP) {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            hi[i] = hi_of(lk[i]);
-            lo[i] = lk[i] - hi[i];
-          }
-          st8(&sm.lk[ir][pos], hi);
-          st8(&sm.lk_lo[ir][pos], lo);
-        } else {
-          st8(&sm.lk[ir][pos], lk);
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          hi[i] = hi_of(rk[i]);
-          lo[i] = rk[i] - hi[i];
-        }
-        st8(&sm.rk_hi[ir][pos], hi);
-        st8(&sm.rk_lo[ir][pos], lo);
       }
+      const int pp = 8 * ib;
+      float hi[8], lo[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        hi[i] = hi_of(lq[i]);
+        lo[i] = lq[i] - hi[i];
+      }
+      st8b(&sm.lq_hi[ir][pp], hi);
+      st8b(&sm.lq_lo[ir][pp], lo);
+      if constexpr (HP) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          hi[i] = hi_of(lk[i]);
+          lo[i] = lk[i] - hi[i];
+        }
+        st8b(&sm.lk[ir][pp], hi);
+        st8b(&sm.lk_lo[ir][pp], lo);
+      } else {
+        st8b(&sm.lk[ir][pp], lk);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        hi[i] = hi_of(rk[i]);
+        lo[i] = rk[i] - hi[i];
+      }
+      st8b(&sm.rk_hi[ir][pp], hi);
+      st8b(&sm.rk_lo[ir][pp], lo);
     }
-    __syncthreads();
+    lds_barrier();
     // ------------------------------------------------ phase AP: A and P (16x16 tiles)
     {
-      const int lr = lane & 15;        // row / column inside a 16x16 tile
-      const int kq = 8 * (lane >> 4);  // k offset of this lane inside a 32-wide K step
-      if (wave == 0) {
-        // A tiles (0,0), (1,0), (1,1): strictly lower part, scaled by beta_row
-#pragma unroll
-        for (int tt = 0; tt < 3; ++tt) {
-          const int I = tt == 0 ? 0 : 1, J = tt == 2 ? 1 : 0;
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int ks = 0; ks < D / 32; ++ks) {
-            const bf16x8 a = frag_lds(&sm.lk[16 * I + lr][32 * ks + kq]);
-            const bf16x8 b = frag_lds(&sm.rk_hi[16 * J + lr][32 * ks + kq]);
-            acc = mfma16(a, b, acc);
-            if constexpr (HP) {
-              acc = mfma16(a, frag_lds(&sm.rk_lo[16 * J + lr][32 * ks + kq]), acc);
-              acc = mfma16(frag_lds(&sm.lk_lo[16 * I + lr][32 * ks + kq]), b, acc);
-            }
-          }
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = 16 * I + 4 * (lane >> 4) + i;
-            const int c = 16 * J + lr;
-            sm.u.b.A[r][c] = r > c ? acc[i] * sm.beta[r] : 0.f;
-          }
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sm.u.b.A[4 * (lane >> 4) + i][16 + lr] = 0.f;  // tile (0,1)
-      } else {
-        // P tile per wave: wave 1 -> (0,0), 2 -> (1,0), 3 -> (1,1); lower incl. diagonal
-        const int I = wave == 1 ? 0 : 1;
-        const int J = wave == 3 ? 1 : 0;
+      const int kq = 8 * g4;   // k offset of this lane inside a 32-wide K step
+      if (wave < 3) {
+        // P tile per wave: 0 -> (0,0), 1 -> (1,0), 2 -> (1,1); lower incl. diagonal
+        const int I = wave == 0 ? 0 : 1;
+        const int J = wave == 2 ? 1 : 0;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < D / 32; ++ks) {
-          const bf16x8 ah = frag_lds(&sm.lq_hi[16 * I + lr][32 * ks + kq]);
-          const bf16x8 bh = frag_lds(&sm.rk_hi[16 * J + lr][32 * ks + kq]);
-          acc = mfma16(ah, bh, acc);
-          acc = mfma16(ah, frag_lds(&sm.rk_lo[16 * J + lr][32 * ks + kq]), acc);
-          acc = mfma16(frag_lds(&sm.lq_lo[16 * I + lr][32 * ks + kq]), bh, acc);
+          const bf16x8 ah = frag_lds(&sm.lq_hi[16 * I + l16][32 * ks + kq]);
+          const bf16x8 bh = frag_lds(&sm.rk_hi[16 * J + l16][32 * ks + kq]);
+          acc = mfma(ah, bh, acc);
+          acc = mfma(ah, frag_lds(&sm.rk_lo[16 * J + l16][32 * ks + kq]), acc);
+          acc = mfma(frag_lds(&sm.lq_lo[16 * I + l16][32 * ks + kq]), bh, acc);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int r = 16 * I + 4 * (lane >> 4) + i;
-          const int c = 16 * J + lr;
+          const int r = 16 * I + 4 * g4 + i;
+          const int c = 16 * J + l16;
           const float v = c <= r ? acc[i] : 0.f;
           const float hv = hi_of(v);
-          sm.u.b.P_hi[r][perm16(c)] = f32_to_bf16(hv);
-          sm.u.b.P_lo[r][perm16(c)] = f32_to_bf16(v - hv);
-          if (wave == 1) {  // tile (0,1) is zero
-            sm.u.b.P_hi[r][perm16(16 + lr)] = 0;
-            sm.u.b.P_lo[r][perm16(16 + lr)] = 0;
+          sm.u.b.P_hi[r][pos32(c)] = f32_to_bf16(hv);
+          sm.u.b.P_lo[r][pos32(c)] = f32_to_bf16(v - hv);
+        }
+      } else if (wave < 6) {
+        // A tile per wave: 3 -> (0,0), 4 -> (1,0), 5 -> (1,1); strictly lower, scaled by beta_row
+        const int I = wave == 3 ? 0 : 1;
+        const int J = wave == 5 ? 1 : 0;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks) {
+          const bf16x8 a = frag_lds(&sm.lk[16 * I + l16][32 * ks + kq]);
+          const bf16x8 b = frag_lds(&sm.rk_hi[16 * J + l16][32 * ks + kq]);
+          acc = mfma(a, b, acc);
+          if constexpr (HP) {
+            acc = mfma(a, frag_lds(&sm.rk_lo[16 * J + l16][32 * ks + kq]), acc);
+            acc = mfma(frag_lds(&sm.lk_lo[16 * I + l16][32 * ks + kq]), b, acc);
           }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * I + 4 * g4 + i;
+          const int c = 16 * J + l16;
+          sm.u.b.A[r][c] = r > c ? acc[i] * sm.beta[r] : 0.f;
+        }
+      } else if (wave == 6) {
+        // tile (0,1) of A and P is zero
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 4 * g4 + i;
+          sm.u.b.A[r][16 + l16] = 0.f;
+          sm.u.b.P_hi[r][pos32(16 + l16)] = 0;
+          sm.u.b.P_lo[r][pos32(16 + l16)] = 0;
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
     // ------------------------------------------------ phase T: (I + A)^{-1} diag(beta)
     // Blocked forward substitution on 16 x 16 blocks (A is strictly lower):
     // D_b = (I + A_bb)^{-1} for the two diagonal blocks, then the lower block
@@ -510,23 +519,23 @@ __global__ void __launch_bounds__(NT, 2) prefill_kernel(const PrefillParams p, c
         sm.u.b.Tf[16 * b + r][16 * (1 - b) + jj] = 0.f;
       }
     }
-    __syncthreads();
-    {
+    lds_barrier();
+    if (tid < 256) {
       const int i = tid >> 4, j = tid & 15;
       float acc = 0.f;
 #pragma unroll
       for (int k = 0; k < 16; ++k) acc += sm.u.b.A[16 + i][k] * sm.u.b.Tf[k][j];
       sm.u.b.X[i][j] = acc;
     }
-    __syncthreads();
-    {
+    lds_barrier();
+    if (tid < 256) {
       const int i = tid >> 4, j = tid & 15;
       float acc = 0.f;
 #pragma unroll
       for (int k = 0; k < 16; ++k) acc += sm.u.b.Tf[16 + i][16 + k] * sm.u.b.X[k][j];
       sm.u.b.Tf[16 + i][j] = -acc;
     }
-    __syncthreads();
+    lds_barrier();
     for (int it = tid; it < TILE * TILE; it += NT) {
       const int r = it / TILE, j = it % TILE;
       const float t = j <= r ? sm.u.b.Tf[r][j] * sm.beta[j] : 0.f;
@@ -534,146 +543,130 @@ __global__ void __launch_bounds__(NT, 2) prefill_kernel(const PrefillParams p, c
       sm.u.b.Tm[r][j] = f32_to_bf16(th);
       if constexpr (HP) sm.u.b.Tm_lo[r][j] = f32_to_bf16(t - th);
     }
-    __syncthreads();
+    lds_barrier();
     // ------------------------------------------------ phase W: W = T left_k (shared), U = T V (own)
-    f32x16 uacc;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) uacc[e] = 0.f;
+    f32x4 U[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
     if (chain) {
-      const int lr = lane & 31;
-      const int kq = 8 * (lane >> 5);
-      f32x16 wacc;
+      // B fragments over chunk rows s = 8 g4 + e (transpose reads), columns 16 wave + l16
+      const int j = (lane >> 2) & 3, i = lane & 3;
+      const int x0 = 16 * wave + 4 * i;
+      const int r0 = 8 * g4 + j;
+      const bf16x8 bk = join(tr4(&sm.lk[r0][x0]), tr4(&sm.lk[r0 + 4][x0]));
+      const bf16x8 bv = join(tr4(&sm.v_hi[r0][x0]), tr4(&sm.v_hi[r0 + 4][x0]));
+      bf16x8 bkl = bk, bvl = bv;
+      if constexpr (HP) {
+        bkl = join(tr4(&sm.lk_lo[r0][x0]), tr4(&sm.lk_lo[r0 + 4][x0]));
+        bvl = join(tr4(&sm.v_lo[r0][x0]), tr4(&sm.v_lo[r0 + 4][x0]));
+      }
 #pragma unroll
-      for (int e = 0; e < 16; ++e) wacc[e] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < TILE / 16; ++ks) {
-        const bf16x8 a = frag_lds(&sm.u.b.Tm[lr][16 * ks + kq]);
-        const bf16x8 bk = frag_tr(&sm.lk[0][0], D, 16 * ks, 32 * wave, lane);
-        const bf16x8 bv = frag_tr(&sm.v_hi[0][0], D, 16 * ks, 32 * wave, lane);
-        wacc = mfma32(a, bk, wacc);
-        uacc = mfma32(a, bv, uacc);
+      for (int mt = 0; mt < 2; ++mt) {
+        const bf16x8 a = frag_lds(&sm.u.b.Tm[16 * mt + l16][8 * g4]);
+        f32x4 w = {0.f, 0.f, 0.f, 0.f};
+        w = mfma(a, bk, w);
+        U[mt] = mfma(a, bv, U[mt]);
         if constexpr (HP) {
-          const bf16x8 al = frag_lds(&sm.u.b.Tm_lo[lr][16 * ks + kq]);
-          wacc = mfma32(a, frag_tr(&sm.lk_lo[0][0], D, 16 * ks, 32 * wave, lane), wacc);
-          wacc = mfma32(al, bk, wacc);
-          uacc = mfma32(a, frag_tr(&sm.v_lo[0][0], D, 16 * ks, 32 * wave, lane), uacc);
-          uacc = mfma32(al, bv, uacc);
+          const bf16x8 al = frag_lds(&sm.u.b.Tm_lo[16 * mt + l16][8 * g4]);
+          w = mfma(a, bkl, w);
+          w = mfma(al, bk, w);
+          U[mt] = mfma(a, bvl, U[mt]);
+          U[mt] = mfma(al, bv, U[mt]);
+        }
+        // W columns come out in storage-position order: store -W as is
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float wv = -w[e];
+          const float wh = hi_of(wv);
+          sm.u.b.Wn[16 * mt + 4 * g4 + e][16 * wave + l16] = f32_to_bf16(wh);
+          if constexpr (HP) sm.u.b.Wn_lo[16 * mt + 4 * g4 + e][16 * wave + l16] = f32_to_bf16(wv - wh);
         }
       }
-      // W columns come out in storage-position order: store -W as is
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float w = -wacc[e];
-        const float wh = hi_of(w);
-        sm.u.b.Wn[acc_row(e, lane)][32 * wave + lr] = f32_to_bf16(wh);
-        if constexpr (HP) sm.u.b.Wn_lo[acc_row(e, lane)][32 * wave + lr] = f32_to_bf16(w - wh);
-      }
     }
-    __syncthreads();
-    // ------------------------------------------------ chain (per wave, own 32 columns)
-    f32x16 oacc;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) oacc[e] = 0.f;
+    lds_barrier();
+    // ------------------------------------------------ chain (per wave, own 16 columns)
+    f32x4 O[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
     if (chain) {
-      const int lr = lane & 31;
-      const int kq = 8 * (lane >> 5);
+      const int kq = 8 * g4;
       // S' = Diag(exp G_m) S
 #pragma unroll
-      for (int t = 0; t < D / 32; ++t)
+      for (int q = 0; q < NQ; ++q) {
+        const float4 f = *reinterpret_cast<const float4*>(&sm.eg_m[16 * q + 4 * g4]);
+        S[q][0] *= f.x; S[q][1] *= f.y; S[q][2] *= f.z; S[q][3] *= f.w;
+      }
+      // u = U - W S' ; O = left_q S'   (K steps of 32 channels)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) S[t][e] *= sm.eg_m[32 * t + acc_row(e, lane)];
-      // u = U - W S' ; O = left_q S'
+      for (int ks = 0; ks < D / 32; ++ks) {
+        bf16x8 sb, sbl;
+        frag_pair(S[2 * ks], S[2 * ks + 1], sb, sbl);
 #pragma unroll
-      for (int t = 0; t < D / 32; ++t) {
-        bf16x8 b0, b0l, b1, b1l;
-        frag_acc_pair<0>(S[t], b0, b0l);
-        frag_acc_pair<8>(S[t], b1, b1l);
-        const bf16x8 w0 = frag_lds(&sm.u.b.Wn[lr][32 * t + kq]);
-        const bf16x8 w1 = frag_lds(&sm.u.b.Wn[lr][32 * t + 16 + kq]);
-        const bf16x8 q0 = frag_lds(&sm.lq_hi[lr][32 * t + kq]);
-        const bf16x8 q1 = frag_lds(&sm.lq_hi[lr][32 * t + 16 + kq]);
-        const bf16x8 q0l = frag_lds(&sm.lq_lo[lr][32 * t + kq]);
-        const bf16x8 q1l = frag_lds(&sm.lq_lo[lr][32 * t + 16 + kq]);
-        uacc = mfma32(w0, b0, uacc);
-        oacc = mfma32(q0, b0, oacc);
-        uacc = mfma32(w1, b1, uacc);
-        oacc = mfma32(q1, b1, oacc);
-        oacc = mfma32(q0, b0l, oacc);
-        oacc = mfma32(q1, b1l, oacc);
-        oacc = mfma32(q0l, b0, oacc);
-        oacc = mfma32(q1l, b1, oacc);
-        if constexpr (HP) {
-          uacc = mfma32(w0, b0l, uacc);
-          uacc = mfma32(w1, b1l, uacc);
-          uacc = mfma32(frag_lds(&sm.u.b.Wn_lo[lr][32 * t + kq]), b0, uacc);
-          uacc = mfma32(frag_lds(&sm.u.b.Wn_lo[lr][32 * t + 16 + kq]), b1, uacc);
+        for (int mt = 0; mt < 2; ++mt) {
+          const int row = 16 * mt + l16;
+          const bf16x8 w = frag_lds(&sm.u.b.Wn[row][32 * ks + kq]);
+          const bf16x8 qh = frag_lds(&sm.lq_hi[row][32 * ks + kq]);
+          const bf16x8 ql = frag_lds(&sm.lq_lo[row][32 * ks + kq]);
+          U[mt] = mfma(w, sb, U[mt]);
+          O[mt] = mfma(qh, sb, O[mt]);
+          O[mt] = mfma(qh, sbl, O[mt]);
+          O[mt] = mfma(ql, sb, O[mt]);
+          if constexpr (HP) {
+            U[mt] = mfma(w, sbl, U[mt]);
+            U[mt] = mfma(frag_lds(&sm.u.b.Wn_lo[row][32 * ks + kq]), sb, U[mt]);
+          }
         }
       }
-      bf16x8 uh0, ul0, uh1, ul1;
-      frag_acc_pair<0>(uacc, uh0, ul0);
-      frag_acc_pair<8>(uacc, uh1, ul1);
+      // u (in U) as a pair over the 32 chunk rows
+      bf16x8 uh, ul;
+      frag_pair(U[0], U[1], uh, ul);
       // O += P u
-      {
-        const bf16x8 ph0 = frag_lds(&sm.u.b.P_hi[lr][kq]), pl0 = frag_lds(&sm.u.b.P_lo[lr][kq]);
-        const bf16x8 ph1 = frag_lds(&sm.u.b.P_hi[lr][16 + kq]), pl1 = frag_lds(&sm.u.b.P_lo[lr][16 + kq]);
-        oacc = mfma32(ph0, uh0, oacc);
-        oacc = mfma32(ph1, uh1, oacc);
-        oacc = mfma32(ph0, ul0, oacc);
-        oacc = mfma32(ph1, ul1, oacc);
-        oacc = mfma32(pl0, uh0, oacc);
-        oacc = mfma32(pl1, uh1, oacc);
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        const bf16x8 ph = frag_lds(&sm.u.b.P_hi[16 * mt + l16][kq]);
+        const bf16x8 pl = frag_lds(&sm.u.b.P_lo[16 * mt + l16][kq]);
+        O[mt] = mfma(ph, uh, O[mt]);
+        O[mt] = mfma(ph, ul, O[mt]);
+        O[mt] = mfma(pl, uh, O[mt]);
       }
-      // S = Diag(exp(G_last - G_m)) (S' + right_k^T u); right_k^T fragments are
-      // transpose reads of right_k [s][perm(c)] whose rows follow u's order and
-      // whose columns come out in channel order.
+      // S = Diag(exp(G_last - G_m)) (S' + right_k^T u); right_k^T fragments
+      // are transpose reads of right_k [s][pos32(c)]: rows follow u's order,
+      // columns are picked so that lane l16 receives channel 16 q + l16.
       {
-        const int g = lane >> 4, j = (lane >> 2) & 3, i = lane & 3;
-        const int krow = 4 * (g >> 1) + j;  // rows krow (e 0..3) and krow + 8 (e 4..7)
+        const int j = (lane >> 2) & 3, i = lane & 3;
+        const int ra = 4 * g4 + j;      // rows for slots 0..3; ra + 16 for slots 4..7
 #pragma unroll
-        for (int t = 0; t < D / 32; ++t) {
-          const int col = 32 * t + 16 * (g & 1) + 4 * swap4(i);
-          bf16x8 kh[2], kl[2];
-#pragma unroll
-          for (int hf = 0; hf < 2; ++hf) {
-            const int r0 = 16 * hf + krow;
-            kh[hf] = join(tr4(&sm.rk_hi[r0][col]), tr4(&sm.rk_hi[r0 + 8][col]));
-            kl[hf] = join(tr4(&sm.rk_lo[r0][col]), tr4(&sm.rk_lo[r0 + 8][col]));
-          }
-          S[t] = mfma32(kh[0], uh0, S[t]);
-          S[t] = mfma32(kh[1], uh1, S[t]);
-          S[t] = mfma32(kh[0], ul0, S[t]);
-          S[t] = mfma32(kh[1], ul1, S[t]);
-          S[t] = mfma32(kl[0], uh0, S[t]);
-          S[t] = mfma32(kl[1], uh1, S[t]);
-#pragma unroll
-          for (int e = 0; e < 16; ++e) S[t][e] *= sm.eg_e[32 * t + acc_row(e, lane)];
+        for (int q = 0; q < NQ; ++q) {
+          const int col = 32 * (q >> 1) + 4 * (q & 1) + 8 * i;
+          const bf16x8 kh = join(tr4(&sm.rk_hi[ra][col]), tr4(&sm.rk_hi[ra + 16][col]));
+          const bf16x8 kl = join(tr4(&sm.rk_lo[ra][col]), tr4(&sm.rk_lo[ra + 16][col]));
+          S[q] = mfma(kh, uh, S[q]);
+          S[q] = mfma(kh, ul, S[q]);
+          S[q] = mfma(kl, uh, S[q]);
+          const float4 f = *reinterpret_cast<const float4*>(&sm.eg_e[16 * q + 4 * g4]);
+          S[q][0] *= f.x; S[q][1] *= f.y; S[q][2] *= f.z; S[q][3] *= f.w;
         }
       }
     }
-    __syncthreads();   // every wave is done reading lq / P / Wn / rk
+    lds_barrier();   // every wave is done reading lq / P / Wn / rk
     // ------------------------------------------------ outputs: stage through LDS, store rows
     if (chain) {
       // stage O (scaled, output type) into the lq area: [32 rows][D columns]
       TOUT* stg = reinterpret_cast<TOUT*>(&sm.lq_hi[0][0]);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int r = acc_row(e, lane);
-        io<TOUT>::st(stg + r * D + ncol, oacc[e] * p.scale);
-      }
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) io<TOUT>::st(stg + (16 * mt + 4 * g4 + e) * D + ncol, O[mt][e] * p.scale);
     }
-    __syncthreads();
+    lds_barrier();
     {
       constexpr int OV = 16 / sizeof(TOUT);   // elements per vector
       constexpr int NOV = D / OV;             // vectors per row
       const TOUT* stg = reinterpret_cast<const TOUT*>(&sm.lq_hi[0][0]);
       for (int it = tid; it < TILE * NOV; it += NT) {
         const int r = it / NOV;
-        const int c0 = (it % NOV) * OV;
+        const int cc = (it % NOV) * OV;
         const int64_t pos = base + r;
-        if (r < CH && pos >= start && pos < end && c0 < d) {
+        if (r < CH && pos >= start && pos < end && cc < d) {
           const int64_t tok = bos + (pos - start);
-          TOUT* dstp = og + tok * p.o_stride + static_cast<int64_t>(h) * d + c0;
-          *reinterpret_cast<uint4*>(dstp) = *reinterpret_cast<const uint4*>(stg + r * D + c0);
+          TOUT* dstp = og + tok * p.o_stride + static_cast<int64_t>(h) * d + cc;
+          *reinterpret_cast<uint4*>(dstp) = *reinterpret_cast<const uint4*>(stg + r * D + cc);
         }
       }
     }
@@ -691,7 +684,7 @@ __global__ void __launch_bounds__(NT, 2) prefill_kernel(const PrefillParams p, c
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
   }
   // ---- final state
   if (chain && has_dst && ncol < d) state_store<D>(p.pool + (static_cast<int64_t>(dst) * H + h) * d * d, S, lane, ncol, d);
