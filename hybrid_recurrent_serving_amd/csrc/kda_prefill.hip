@@ -39,7 +39,7 @@
 // marked "pair" is carried as hi + lo bf16 (hi*hi + hi*lo + lo*hi):
 //     A = left_k right_k^T          single bf16
 //     P = left_q right_k^T          pair x pair
-//     W = T left_k, U = T V         single
+//     W = T left_k, U = T V         fp32 forward substitution (W stored single)
 //     u: W S'                       single
 //     O: left_q S'  pair x pair;    P u   pair x pair
 //     state: right_k^T u            pair x pair
@@ -147,11 +147,10 @@ __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// The state slice of a chain wave <-> a pool slot [c][n] (fp32).  Kept out of
-// line: called once per sequence and per checkpoint; inlined it would hold
-// loop-invariant addresses across the chunk loop.
+// The state slice of a chain wave <-> a pool slot [c][n] (fp32).  Inlined
+// with compile-time tile indices so the slice stays in registers.
 template <int D>
-__device__ __attribute__((noinline)) void state_store(float* base, const f32x4* S, int lane, int ncol, int d) {
+__device__ __forceinline__ void state_store(float* base, const f32x4 (&S)[D / 16], int lane, int ncol, int d) {
 #pragma unroll
   for (int q = 0; q < D / 16; ++q)
 #pragma unroll
@@ -162,7 +161,7 @@ __device__ __attribute__((noinline)) void state_store(float* base, const f32x4* 
 }
 
 template <int D>
-__device__ __attribute__((noinline)) void state_load(const float* base, f32x4* S, int lane, int ncol, int d) {
+__device__ __forceinline__ void state_load(const float* base, f32x4 (&S)[D / 16], int lane, int ncol, int d) {
 #pragma unroll
   for (int q = 0; q < D / 16; ++q)
 #pragma unroll
@@ -192,6 +191,7 @@ struct Smem {
   float eg_m[D];              // exp(G_m)
   float eg_e[D];              // exp(G_last - G_m)
   float beta[TILE];
+  float Ub[TILE][D];          // U = T V (fp32)
   union {
     struct {
       TIN g_raw[TILE][D];
@@ -199,11 +199,7 @@ struct Smem {
       float scan[NT];
     } a;
     struct {
-      float A[TILE][TILE];
-      float Tf[TILE][TILE];
-      float X[16][16];
-      bf16_t Tm[TILE][PT];    // [r][s]
-      bf16_t Tm_lo[F32IN ? TILE : 1][PT];
+      float At[TILE][TILE + 4];  // At[s][r] = beta_r <left_k[r], right_k[s]>, s < r
       bf16_t P_hi[TILE][PT];  // [r][pos32(s)]
       bf16_t P_lo[TILE][PT];
       bf16_t Wn[TILE][PD];    // -(T left_k) [r][pos32(c)]
@@ -478,106 +474,60 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
         for (int i = 0; i < 4; ++i) {
           const int r = 16 * I + 4 * g4 + i;
           const int c = 16 * J + l16;
-          sm.u.b.A[r][c] = r > c ? acc[i] * sm.beta[r] : 0.f;
+          sm.u.b.At[c][r] = r > c ? acc[i] * sm.beta[r] : 0.f;
         }
       } else if (wave == 6) {
         // tile (0,1) of A and P is zero
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = 4 * g4 + i;
-          sm.u.b.A[r][16 + l16] = 0.f;
+          sm.u.b.At[16 + l16][r] = 0.f;
           sm.u.b.P_hi[r][pos32(16 + l16)] = 0;
           sm.u.b.P_lo[r][pos32(16 + l16)] = 0;
         }
       }
     }
     lds_barrier();
-    // ------------------------------------------------ phase T: (I + A)^{-1} diag(beta)
-    // Blocked forward substitution on 16 x 16 blocks (A is strictly lower):
-    // D_b = (I + A_bb)^{-1} for the two diagonal blocks, then the lower block
-    // (I + A)^{-1}_{10} = -D_1 A_10 D_0.
-    if (wave == 0 && lane < TILE) {
-      const int b = lane >> 4;
-      const int jj = lane & 15;
-      float x[16];
+    // ------------------------------------------------ phase X: (I + A) [W | U] = diag(beta) [left_k | V]
+    // Forward substitution over the 32 chunk rows in fp32, one right-hand-side
+    // column per thread (the D columns of left_k, then the D columns of V), in
+    // column order: once X_s is final, its multiple A[r][s] X_s leaves every
+    // later row r, so each step is a set of independent updates.
+    // W = (I + A)^{-1} diag(beta) left_k goes to LDS as -W (bf16, storage
+    // positions as in left_k); U = (I + A)^{-1} diag(beta) V stays fp32.
+    if (tid < 2 * D) {
+      const bool isv = tid >= D;
+      const int c = isv ? tid - D : tid;
+      const bf16_t* Y = isv ? &sm.v_hi[0][c] : &sm.lk[0][c];
+      const bf16_t* Yl = isv ? &sm.v_lo[0][c] : &sm.lk_lo[0][c];
+      float x[TILE];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float acc = r == jj ? 1.f : 0.f;
+      for (int r = 0; r < TILE; ++r) {
+        float y = bf16_to_f32(Y[r * SM::PD]);
+        if constexpr (HP) y += bf16_to_f32(Yl[r * SM::PD]);
+        x[r] = sm.beta[r] * y;
+      }
 #pragma unroll
-        for (int s4 = 0; s4 < r; s4 += 4) {
-          const float4 a4 = *reinterpret_cast<const float4*>(&sm.u.b.A[16 * b + r][16 * b + s4]);
-          acc -= a4.x * x[s4];
-          if (s4 + 1 < r) acc -= a4.y * x[s4 + 1];
-          if (s4 + 2 < r) acc -= a4.z * x[s4 + 2];
-          if (s4 + 3 < r) acc -= a4.w * x[s4 + 3];
+      for (int s = 0; s < TILE - 1; ++s) {
+#pragma unroll
+        for (int r4 = (s + 1) & ~3; r4 < TILE; r4 += 4) {
+          const float4 a4 = *reinterpret_cast<const float4*>(&sm.u.b.At[s][r4]);
+          if (r4 > s) x[r4] -= a4.x * x[s];
+          if (r4 + 1 > s) x[r4 + 1] -= a4.y * x[s];
+          if (r4 + 2 > s) x[r4 + 2] -= a4.z * x[s];
+          x[r4 + 3] -= a4.w * x[s];
         }
-        x[r] = acc;
       }
+      if (isv) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        sm.u.b.Tf[16 * b + r][16 * b + jj] = x[r];
-        sm.u.b.Tf[16 * b + r][16 * (1 - b) + jj] = 0.f;
-      }
-    }
-    lds_barrier();
-    if (tid < 256) {
-      const int i = tid >> 4, j = tid & 15;
-      float acc = 0.f;
+        for (int r = 0; r < TILE; ++r) sm.Ub[r][c] = x[r];
+      } else {
 #pragma unroll
-      for (int k = 0; k < 16; ++k) acc += sm.u.b.A[16 + i][k] * sm.u.b.Tf[k][j];
-      sm.u.b.X[i][j] = acc;
-    }
-    lds_barrier();
-    if (tid < 256) {
-      const int i = tid >> 4, j = tid & 15;
-      float acc = 0.f;
-#pragma unroll
-      for (int k = 0; k < 16; ++k) acc += sm.u.b.Tf[16 + i][16 + k] * sm.u.b.X[k][j];
-      sm.u.b.Tf[16 + i][j] = -acc;
-    }
-    lds_barrier();
-    for (int it = tid; it < TILE * TILE; it += NT) {
-      const int r = it / TILE, j = it % TILE;
-      const float t = j <= r ? sm.u.b.Tf[r][j] * sm.beta[j] : 0.f;
-      const float th = hi_of(t);
-      sm.u.b.Tm[r][j] = f32_to_bf16(th);
-      if constexpr (HP) sm.u.b.Tm_lo[r][j] = f32_to_bf16(t - th);
-    }
-    lds_barrier();
-    // ------------------------------------------------ phase W: W = T left_k (shared), U = T V (own)
-    f32x4 U[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-    if (chain) {
-      // B fragments over chunk rows s = 8 g4 + e (transpose reads), columns 16 wave + l16
-      const int j = (lane >> 2) & 3, i = lane & 3;
-      const int x0 = 16 * wave + 4 * i;
-      const int r0 = 8 * g4 + j;
-      const bf16x8 bk = join(tr4(&sm.lk[r0][x0]), tr4(&sm.lk[r0 + 4][x0]));
-      const bf16x8 bv = join(tr4(&sm.v_hi[r0][x0]), tr4(&sm.v_hi[r0 + 4][x0]));
-      bf16x8 bkl = bk, bvl = bv;
-      if constexpr (HP) {
-        bkl = join(tr4(&sm.lk_lo[r0][x0]), tr4(&sm.lk_lo[r0 + 4][x0]));
-        bvl = join(tr4(&sm.v_lo[r0][x0]), tr4(&sm.v_lo[r0 + 4][x0]));
-      }
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        const bf16x8 a = frag_lds(&sm.u.b.Tm[16 * mt + l16][8 * g4]);
-        f32x4 w = {0.f, 0.f, 0.f, 0.f};
-        w = mfma(a, bk, w);
-        U[mt] = mfma(a, bv, U[mt]);
-        if constexpr (HP) {
-          const bf16x8 al = frag_lds(&sm.u.b.Tm_lo[16 * mt + l16][8 * g4]);
-          w = mfma(a, bkl, w);
-          w = mfma(al, bk, w);
-          U[mt] = mfma(a, bvl, U[mt]);
-          U[mt] = mfma(al, bv, U[mt]);
-        }
-        // W columns come out in storage-position order: store -W as is
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float wv = -w[e];
+        for (int r = 0; r < TILE; ++r) {
+          const float wv = -x[r];
           const float wh = hi_of(wv);
-          sm.u.b.Wn[16 * mt + 4 * g4 + e][16 * wave + l16] = f32_to_bf16(wh);
-          if constexpr (HP) sm.u.b.Wn_lo[16 * mt + 4 * g4 + e][16 * wave + l16] = f32_to_bf16(wv - wh);
+          sm.u.b.Wn[r][c] = f32_to_bf16(wh);
+          if constexpr (HP) sm.u.b.Wn_lo[r][c] = f32_to_bf16(wv - wh);
         }
       }
     }
@@ -586,30 +536,43 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
     f32x4 O[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
     if (chain) {
       const int kq = 8 * g4;
-      // S' = Diag(exp G_m) S
+      f32x4 U[2];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) U[mt][i] = sm.Ub[16 * mt + 4 * g4 + i][ncol];
+      // S' = Diag(exp G_m) S, and its bf16 pair fragments (K steps of 32 channels)
+      bf16x8 sh[NQ / 2], sl[NQ / 2];
 #pragma unroll
       for (int q = 0; q < NQ; ++q) {
         const float4 f = *reinterpret_cast<const float4*>(&sm.eg_m[16 * q + 4 * g4]);
         S[q][0] *= f.x; S[q][1] *= f.y; S[q][2] *= f.z; S[q][3] *= f.w;
       }
-      // u = U - W S' ; O = left_q S'   (K steps of 32 channels)
 #pragma unroll
-      for (int ks = 0; ks < D / 32; ++ks) {
-        bf16x8 sb, sbl;
-        frag_pair(S[2 * ks], S[2 * ks + 1], sb, sbl);
+      for (int ks = 0; ks < NQ / 2; ++ks) frag_pair(S[2 * ks], S[2 * ks + 1], sh[ks], sl[ks]);
+      // u = U - W S' ; O = left_q S'.  Three independent accumulators for the
+      // pair terms keep the matrix-core pipeline fed.
+      f32x4 Ob[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+      f32x4 Oc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int ks = 0; ks < NQ / 2; ++ks) {
+        bf16x8 w[2], qh[2], ql[2];
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
           const int row = 16 * mt + l16;
-          const bf16x8 w = frag_lds(&sm.u.b.Wn[row][32 * ks + kq]);
-          const bf16x8 qh = frag_lds(&sm.lq_hi[row][32 * ks + kq]);
-          const bf16x8 ql = frag_lds(&sm.lq_lo[row][32 * ks + kq]);
-          U[mt] = mfma(w, sb, U[mt]);
-          O[mt] = mfma(qh, sb, O[mt]);
-          O[mt] = mfma(qh, sbl, O[mt]);
-          O[mt] = mfma(ql, sb, O[mt]);
+          w[mt] = frag_lds(&sm.u.b.Wn[row][32 * ks + kq]);
+          qh[mt] = frag_lds(&sm.lq_hi[row][32 * ks + kq]);
+          ql[mt] = frag_lds(&sm.lq_lo[row][32 * ks + kq]);
+        }
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          U[mt] = mfma(w[mt], sh[ks], U[mt]);
+          O[mt] = mfma(qh[mt], sh[ks], O[mt]);
+          Ob[mt] = mfma(qh[mt], sl[ks], Ob[mt]);
+          Oc[mt] = mfma(ql[mt], sh[ks], Oc[mt]);
           if constexpr (HP) {
-            U[mt] = mfma(w, sbl, U[mt]);
-            U[mt] = mfma(frag_lds(&sm.u.b.Wn_lo[row][32 * ks + kq]), sb, U[mt]);
+            U[mt] = mfma(w[mt], sl[ks], U[mt]);
+            U[mt] = mfma(frag_lds(&sm.u.b.Wn_lo[16 * mt + l16][32 * ks + kq]), sh[ks], U[mt]);
           }
         }
       }
@@ -622,12 +585,12 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
         const bf16x8 ph = frag_lds(&sm.u.b.P_hi[16 * mt + l16][kq]);
         const bf16x8 pl = frag_lds(&sm.u.b.P_lo[16 * mt + l16][kq]);
         O[mt] = mfma(ph, uh, O[mt]);
-        O[mt] = mfma(ph, ul, O[mt]);
-        O[mt] = mfma(pl, uh, O[mt]);
+        Ob[mt] = mfma(ph, ul, Ob[mt]);
+        Oc[mt] = mfma(pl, uh, Oc[mt]);
       }
-      // S = Diag(exp(G_last - G_m)) (S' + right_k^T u); right_k^T fragments
-      // are transpose reads of right_k [s][pos32(c)]: rows follow u's order,
-      // columns are picked so that lane l16 receives channel 16 q + l16.
+      // S = Diag(exp(G_last - G_m)) (S' + right_k^T u).  right_k^T fragments
+      // come from transpose reads of right_k [s][pos32(c)]: rows follow u's
+      // order, columns are picked so that lane l16 receives channel 16 q + l16.
       {
         const int j = (lane >> 2) & 3, i = lane & 3;
         const int ra = 4 * g4 + j;      // rows for slots 0..3; ra + 16 for slots 4..7
@@ -639,10 +602,17 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
           S[q] = mfma(kh, uh, S[q]);
           S[q] = mfma(kh, ul, S[q]);
           S[q] = mfma(kl, uh, S[q]);
-          const float4 f = *reinterpret_cast<const float4*>(&sm.eg_e[16 * q + 4 * g4]);
-          S[q][0] *= f.x; S[q][1] *= f.y; S[q][2] *= f.z; S[q][3] *= f.w;
         }
       }
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        const float4 f = *reinterpret_cast<const float4*>(&sm.eg_e[16 * q + 4 * g4]);
+        S[q][0] *= f.x; S[q][1] *= f.y; S[q][2] *= f.z; S[q][3] *= f.w;
+      }
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) O[mt][i] += Ob[mt][i] + Oc[mt][i];
     }
     lds_barrier();   // every wave is done reading lq / P / Wn / rk
     // ------------------------------------------------ outputs: stage through LDS, store rows
