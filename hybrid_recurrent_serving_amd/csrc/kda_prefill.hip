@@ -39,7 +39,8 @@
 // marked "pair" is carried as hi + lo bf16 (hi*hi + hi*lo + lo*hi):
 //     A = left_k right_k^T          single bf16
 //     P = left_q right_k^T          pair x pair
-//     W = T left_k, U = T V         fp32 forward substitution (W stored single)
+//     T = (I + A)^{-1} diag(beta)   fp32 (16-row blocks), stored single
+//     W = T left_k, U = T V         single
 //     u: W S'                       single
 //     O: left_q S'  pair x pair;    P u   pair x pair
 //     state: right_k^T u            pair x pair
@@ -94,6 +95,12 @@ __device__ __forceinline__ uint32_t cvt2(float a, float b) {
 }
 __device__ __forceinline__ float hi_of(float x) { return static_cast<float>(static_cast<__bf16>(x)); }
 
+// An opaque copy of x: values derived from it cannot be hoisted out of a loop.
+__device__ __forceinline__ int launder(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 __device__ __forceinline__ float fexp(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
 
 __device__ __forceinline__ bf16x8 frag_lds(const bf16_t* p) {
@@ -127,6 +134,24 @@ __device__ __forceinline__ void st8b(bf16_t* p, const float* x) {
   *reinterpret_cast<uint4*>(p) = u;
 }
 
+// x broadcast from lane S of each row of 16 lanes (DPP row_newbcast)
+template <int S>
+__device__ __forceinline__ float bcast16(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x150 + S, 0xF, 0xF, true));
+}
+
+// Forward substitution down the 16 lanes of each lane row: lane r holds x_r
+// of one right-hand side and na[s] = -L[r][s] of the unit lower triangular L
+// (zero for s >= r); steps S..14 apply x_r += na[s] x_s with x_s final.
+template <int S, int NG>
+__device__ __forceinline__ void fsub16(float (&x)[NG], const float (&na)[16]) {
+  if constexpr (S < 15) {
+#pragma unroll
+    for (int g = 0; g < NG; ++g) x[g] = __builtin_fmaf(na[S], bcast16<S>(x[g]), x[g]);
+    fsub16<S + 1, NG>(x, na);
+  }
+}
+
 // fragment (and hi / lo pair) from two vertically adjacent accumulator tiles
 __device__ __forceinline__ void frag_pair(const f32x4& a, const f32x4& b, bf16x8& hi, bf16x8& lo) {
   const float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
@@ -148,9 +173,19 @@ __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
 }
 
 // The state slice of a chain wave <-> a pool slot [c][n] (fp32).  Inlined
-// with compile-time tile indices so the slice stays in registers.
+// with compile-time tile indices so the slice stays in registers; when
+// d == D the row stride is a constant and a single per-lane address serves
+// every element.
 template <int D>
 __device__ __forceinline__ void state_store(float* base, const f32x4 (&S)[D / 16], int lane, int ncol, int d) {
+  if (D > 32 || d == D) {   // the launch pairs D = 64, 128 only with d = D
+    float* b = base + 4 * (lane >> 4) * D + ncol;
+#pragma unroll
+    for (int q = 0; q < D / 16; ++q)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) b[(16 * q + i) * D] = S[q][i];
+    return;
+  }
 #pragma unroll
   for (int q = 0; q < D / 16; ++q)
 #pragma unroll
@@ -162,6 +197,14 @@ __device__ __forceinline__ void state_store(float* base, const f32x4 (&S)[D / 16
 
 template <int D>
 __device__ __forceinline__ void state_load(const float* base, f32x4 (&S)[D / 16], int lane, int ncol, int d) {
+  if (D > 32 || d == D) {
+    const float* b = base + 4 * (lane >> 4) * D + ncol;
+#pragma unroll
+    for (int q = 0; q < D / 16; ++q)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) S[q][i] = b[(16 * q + i) * D];
+    return;
+  }
 #pragma unroll
   for (int q = 0; q < D / 16; ++q)
 #pragma unroll
@@ -180,7 +223,7 @@ struct Smem {
   static constexpr bool F32IN = sizeof(TIN) == 4;
   static constexpr int PD = D + 16;   // padded pitch of [TILE][D] bf16 tiles
   static constexpr int PT = TILE + 8; // padded pitch of [TILE][TILE] bf16 tiles
-  bf16_t lq_hi[TILE][PD];     // [r][pos32(c)]   (reused for output staging)
+  alignas(16) bf16_t lq_hi[TILE][PD];     // [r][pos32(c)]   (reused for output staging)
   bf16_t lq_lo[TILE][PD];
   bf16_t lk[TILE][PD];        // [r][pos32(c)]
   bf16_t lk_lo[F32IN ? TILE : 1][PD];
@@ -188,22 +231,25 @@ struct Smem {
   bf16_t rk_lo[TILE][PD];
   bf16_t v_hi[TILE][PD];      // [s][n]
   bf16_t v_lo[F32IN ? TILE : 1][PD];
-  float eg_m[D];              // exp(G_m)
-  float eg_e[D];              // exp(G_last - G_m)
+  alignas(16) float eg_m[D];              // exp(G_m)
+  alignas(16) float eg_e[D];              // exp(G_last - G_m)
   float beta[TILE];
-  float Ub[TILE][D];          // U = T V (fp32)
   union {
     struct {
       TIN g_raw[TILE][D];
-      float G[TILE][D];
+      alignas(16) float G[TILE][D];
       float scan[NT];
     } a;
     struct {
-      float At[TILE][TILE + 4];  // At[s][r] = beta_r <left_k[r], right_k[s]>, s < r
+      alignas(16) float At[TILE][TILE + 4];  // At[s][r] = beta_r <left_k[r], right_k[s]>, s < r
       bf16_t P_hi[TILE][PT];  // [r][pos32(s)]
       bf16_t P_lo[TILE][PT];
       bf16_t Wn[TILE][PD];    // -(T left_k) [r][pos32(c)]
       bf16_t Wn_lo[F32IN ? TILE : 1][PD];
+      alignas(16) float Ms[16][20];       // M = (I + A11)^{-1} A10
+      alignas(16) float Tf[16][20];       // T00 (fp32)
+      bf16_t Tb[TILE][PT];                // T = (I + A)^{-1} diag(beta) [r][s]
+      bf16_t Tb_lo[F32IN ? TILE : 1][PT];
     } b;
   } u;
 };
@@ -320,6 +366,20 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
   RawRow<TIN> nxt;
   load_raw(first, nxt);
   for (int64_t base = first; base < end; base += CH) {
+    // Per-thread indices are derived again in every chunk from an opaque copy
+    // of the thread id; otherwise every LDS address derived from them would be
+    // hoisted out of this loop and held in a register for the whole sequence.
+    const int tid = launder(static_cast<int>(threadIdx.x));
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g4 = lane >> 4;
+    const int l16 = lane & 15;
+    const bool chain = wave < NWC;
+    const int ncol = 16 * wave + l16;
+    const bool has_item = tid < NITEM;
+    const int ir = tid / NPB;
+    const int ib = tid % NPB;
+    const int c0 = 32 * (ib >> 2) + 4 * (ib & 3);
     // ------------------------------------------------ phase L: commit raw tile, prefetch next
     const RawRow<TIN> cur = nxt;
     if (base + CH < end) load_raw(base + CH, nxt);
@@ -488,46 +548,93 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
       }
     }
     lds_barrier();
-    // ------------------------------------------------ phase X: (I + A) [W | U] = diag(beta) [left_k | V]
-    // Forward substitution over the 32 chunk rows in fp32, one right-hand-side
-    // column per thread (the D columns of left_k, then the D columns of V), in
-    // column order: once X_s is final, its multiple A[r][s] X_s leaves every
-    // later row r, so each step is a set of independent updates.
-    // W = (I + A)^{-1} diag(beta) left_k goes to LDS as -W (bf16, storage
-    // positions as in left_k); U = (I + A)^{-1} diag(beta) V stays fp32.
-    if (tid < 2 * D) {
-      const bool isv = tid >= D;
-      const int c = isv ? tid - D : tid;
-      const bf16_t* Y = isv ? &sm.v_hi[0][c] : &sm.lk[0][c];
-      const bf16_t* Yl = isv ? &sm.v_lo[0][c] : &sm.lk_lo[0][c];
-      float x[TILE];
+    // ------------------------------------------------ phase X: T = (I + A)^{-1} diag(beta); W = T left_k, U = T V
+    // Blockwise on the 16-row blocks b, with L_b = I + A_bb:
+    //     T_bb = L_b^{-1} diag(beta_b),  T10 = -M T00,  M = L_1^{-1} A10,
+    // each inverse by fp32 forward substitution down the 16 lanes of a lane
+    // row (lane (g4, r) holds row r of column 4 g + g4, g = 0..3).
+    if (wave < 3) {
+      const int b = wave == 0 ? 0 : 1;
+      float na[16];
 #pragma unroll
-      for (int r = 0; r < TILE; ++r) {
-        float y = bf16_to_f32(Y[r * SM::PD]);
-        if constexpr (HP) y += bf16_to_f32(Yl[r * SM::PD]);
-        x[r] = sm.beta[r] * y;
+      for (int s = 0; s < 16; ++s) na[s] = -sm.u.b.At[16 * b + s][16 * b + l16];
+      float x[4];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int j = 4 * g + g4;
+        x[g] = wave == 2 ? sm.u.b.At[j][16 + l16] : (l16 == j ? 1.f : 0.f);
       }
+      fsub16<0, 4>(x, na);
 #pragma unroll
-      for (int s = 0; s < TILE - 1; ++s) {
-#pragma unroll
-        for (int r4 = (s + 1) & ~3; r4 < TILE; r4 += 4) {
-          const float4 a4 = *reinterpret_cast<const float4*>(&sm.u.b.At[s][r4]);
-          if (r4 > s) x[r4] -= a4.x * x[s];
-          if (r4 + 1 > s) x[r4 + 1] -= a4.y * x[s];
-          if (r4 + 2 > s) x[r4 + 2] -= a4.z * x[s];
-          x[r4 + 3] -= a4.w * x[s];
+      for (int g = 0; g < 4; ++g) {
+        const int j = 4 * g + g4;
+        if (wave == 2) {
+          sm.u.b.Ms[l16][j] = x[g];
+        } else {
+          const float t = x[g] * sm.beta[16 * b + j];
+          if (b == 0) sm.u.b.Tf[l16][j] = t;
+          const float th = hi_of(t);
+          sm.u.b.Tb[16 * b + l16][16 * b + j] = f32_to_bf16(th);
+          if constexpr (HP) sm.u.b.Tb_lo[16 * b + l16][16 * b + j] = f32_to_bf16(t - th);
         }
       }
-      if (isv) {
+    } else if (wave == 3) {
 #pragma unroll
-        for (int r = 0; r < TILE; ++r) sm.Ub[r][c] = x[r];
-      } else {
+      for (int g = 0; g < 4; ++g) {
+        sm.u.b.Tb[l16][16 + 4 * g + g4] = 0;
+        if constexpr (HP) sm.u.b.Tb_lo[l16][16 + 4 * g + g4] = 0;
+      }
+    }
+    lds_barrier();
+    if (wave == 0) {
+      // T10 = -M T00 on fp32 matrix cores (K = 16 in steps of 4)
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int r = 0; r < TILE; ++r) {
-          const float wv = -x[r];
+      for (int kb = 0; kb < 4; ++kb)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sm.u.b.Ms[l16][4 * kb + g4], sm.u.b.Tf[4 * kb + g4][l16], acc, 0, 0, 0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float t = -acc[e];
+        const float th = hi_of(t);
+        sm.u.b.Tb[16 + 4 * g4 + e][l16] = f32_to_bf16(th);
+        if constexpr (HP) sm.u.b.Tb_lo[16 + 4 * g4 + e][l16] = f32_to_bf16(t - th);
+      }
+    }
+    lds_barrier();
+    // W = T left_k (columns of this wave in storage order, kept as -W in LDS)
+    // and U = T V (own d_v columns, kept in registers)
+    f32x4 U[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    if (chain) {
+      // B fragments over chunk rows s = 8 g4 + e (transpose reads), columns 16 wave + l16
+      const int j = (lane >> 2) & 3, i = lane & 3;
+      const int x0 = 16 * wave + 4 * i;
+      const int r0 = 8 * g4 + j;
+      const bf16x8 bk = join(tr4(&sm.lk[r0][x0]), tr4(&sm.lk[r0 + 4][x0]));
+      const bf16x8 bv = join(tr4(&sm.v_hi[r0][x0]), tr4(&sm.v_hi[r0 + 4][x0]));
+      bf16x8 bkl = bk, bvl = bv;
+      if constexpr (HP) {
+        bkl = join(tr4(&sm.lk_lo[r0][x0]), tr4(&sm.lk_lo[r0 + 4][x0]));
+        bvl = join(tr4(&sm.v_lo[r0][x0]), tr4(&sm.v_lo[r0 + 4][x0]));
+      }
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        const bf16x8 a = frag_lds(&sm.u.b.Tb[16 * mt + l16][8 * g4]);
+        f32x4 w = {0.f, 0.f, 0.f, 0.f};
+        w = mfma(a, bk, w);
+        U[mt] = mfma(a, bv, U[mt]);
+        if constexpr (HP) {
+          const bf16x8 al = frag_lds(&sm.u.b.Tb_lo[16 * mt + l16][8 * g4]);
+          w = mfma(a, bkl, w);
+          w = mfma(al, bk, w);
+          U[mt] = mfma(a, bvl, U[mt]);
+          U[mt] = mfma(al, bv, U[mt]);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float wv = -w[e];
           const float wh = hi_of(wv);
-          sm.u.b.Wn[r][c] = f32_to_bf16(wh);
-          if constexpr (HP) sm.u.b.Wn_lo[r][c] = f32_to_bf16(wv - wh);
+          sm.u.b.Wn[16 * mt + 4 * g4 + e][16 * wave + l16] = f32_to_bf16(wh);
+          if constexpr (HP) sm.u.b.Wn_lo[16 * mt + 4 * g4 + e][16 * wave + l16] = f32_to_bf16(wv - wh);
         }
       }
     }
@@ -536,11 +643,6 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
     f32x4 O[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
     if (chain) {
       const int kq = 8 * g4;
-      f32x4 U[2];
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) U[mt][i] = sm.Ub[16 * mt + 4 * g4 + i][ncol];
       // S' = Diag(exp G_m) S, and its bf16 pair fragments (K steps of 32 channels)
       bf16x8 sh[NQ / 2], sl[NQ / 2];
 #pragma unroll
