@@ -218,12 +218,14 @@ __device__ __forceinline__ void state_load(const float* base, f32x4 (&S)[D / 16]
 // Row pitches of the bf16 tiles are padded (by 32 bytes for the [32][D]
 // tiles, to 80 bytes for the [32][32] ones) so that the 16-byte fragment reads
 // of 16 rows and the transpose reads of 4 x 4 rows spread over the LDS banks.
-template <int D, typename TIN>
+template <int D, typename TIN, typename TOUT>
 struct Smem {
   static constexpr bool F32IN = sizeof(TIN) == 4;
   static constexpr int PD = D + 16;   // padded pitch of [TILE][D] bf16 tiles
   static constexpr int PT = TILE + 8; // padded pitch of [TILE][TILE] bf16 tiles
-  alignas(16) bf16_t lq_hi[TILE][PD];     // [r][pos32(c)]   (reused for output staging)
+  static constexpr int PO = D + 16 / static_cast<int>(sizeof(TOUT));  // padded pitch of the output tile
+  alignas(16) TOUT ostg[TILE][PO];  // scaled outputs of the previous chunk, stored during the next one
+  alignas(16) bf16_t lq_hi[TILE][PD];     // [r][pos32(c)]
   bf16_t lq_lo[TILE][PD];
   bf16_t lk[TILE][PD];        // [r][pos32(c)]
   bf16_t lk_lo[F32IN ? TILE : 1][PD];
@@ -238,7 +240,6 @@ struct Smem {
     struct {
       TIN g_raw[TILE][D];
       alignas(16) float G[TILE][D];
-      float scan[NT];
     } a;
     struct {
       alignas(16) float At[TILE][TILE + 4];  // At[s][r] = beta_r <left_k[r], right_k[s]>, s < r
@@ -282,7 +283,7 @@ __device__ __forceinline__ void to_f32(const uint2* w, float (&x)[8]) {
 // ---------------------------------------------------------------------------
 template <int D, typename TIN, typename TOUT>
 __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, const int d, const int CH) {
-  using SM = Smem<D, TIN>;
+  using SM = Smem<D, TIN, TOUT>;
   __shared__ SM sm;
   constexpr bool HP = SM::F32IN;        // all products as pairs
   constexpr int NWC = D / 16;           // waves that own state columns
@@ -318,6 +319,10 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
 #pragma unroll
   for (int q = 0; q < NQ; ++q) S[q] = f32x4{0.f, 0.f, 0.f, 0.f};
   if (chain && has_src && ncol < d) state_load<D>(p.pool + (static_cast<int64_t>(src) * H + h) * d * d, S, lane, ncol, d);
+  // The initial state is complete here: a first use inside the chunk loop
+  // would leave a wait for all outstanding memory operations in every trip.
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) asm volatile("" : "+v"(S[q]));
 
   const TIN* qg = static_cast<const TIN*>(p.q);
   const TIN* kg = static_cast<const TIN*>(p.k);
@@ -363,9 +368,38 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
   };
 
   const int64_t first = len > 0 ? (start / CH) * CH : end;
-  RawRow<TIN> nxt;
-  load_raw(first, nxt);
-  for (int64_t base = first; base < end; base += CH) {
+  // beta of row tid (threads tid < TILE), prefetched like the raw tile and
+  // kept as raw input bits until the next chunk (converting it here would
+  // wait for the whole prefetch)
+  auto load_beta = [&](int64_t base) -> TIN {
+    const int64_t pos = base + tid;
+    TIN b = 0;
+    if (tid < CH && pos >= start && pos < end) b = bg[(bos + (pos - start)) * p.beta_stride + h];
+    return b;
+  };
+  // rows of the staged output tile that belong to the sequence -> o (16-byte stores)
+  auto store_out = [&](int64_t obase) {
+    constexpr int OV = 16 / sizeof(TOUT);   // elements per vector
+    constexpr int NOV = D / OV;             // vectors per row
+    for (int it = static_cast<int>(threadIdx.x); it < TILE * NOV; it += NT) {
+      const int r = it / NOV;
+      const int cc = (it % NOV) * OV;
+      const int64_t pos = obase + r;
+      if (r < CH && pos >= start && pos < end && cc < d) {
+        const int64_t tok = bos + (pos - start);
+        TOUT* dstp = og + tok * p.o_stride + static_cast<int64_t>(h) * d + cc;
+        *reinterpret_cast<uint4*>(dstp) = *reinterpret_cast<const uint4*>(&sm.ostg[r][cc]);
+      }
+    }
+  };
+  // Two raw-tile buffers, used alternately by the two chunk calls of each
+  // loop trip: the tile in flight is never copied, so nothing waits for it
+  // before its own chunk.
+  RawRow<TIN> rawA, rawB;
+  load_raw(first, rawA);
+  TIN betaA = load_beta(first), betaB = 0;
+  auto chunk = [&](const int64_t base, const RawRow<TIN>& cur, const TIN bcur, RawRow<TIN>& nxt,
+                   TIN& bnx) __attribute__((always_inline)) {
     // Per-thread indices are derived again in every chunk from an opaque copy
     // of the thread id; otherwise every LDS address derived from them would be
     // hoisted out of this loop and held in a register for the whole sequence.
@@ -381,8 +415,8 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
     const int ib = tid % NPB;
     const int c0 = 32 * (ib >> 2) + 4 * (ib & 3);
     // ------------------------------------------------ phase L: commit raw tile, prefetch next
-    const RawRow<TIN> cur = nxt;
-    if (base + CH < end) load_raw(base + CH, nxt);
+    // (the tile is committed before the next one is requested, so the wait
+    // for it does not cover the new requests)
     if (has_item) {
 #pragma unroll
       for (int w = 0; w < NU; ++w) {
@@ -406,38 +440,47 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
         *reinterpret_cast<uint2*>(&sm.v_hi[ir][c0 + 16]) = cur.v[1];
       }
     }
-    if (tid < TILE) {
-      const int64_t pos = base + tid;
-      float b = 0.f;
-      if (tid < CH && pos >= start && pos < end) b = io<TIN>::ld(bg + (bos + (pos - start)) * p.beta_stride + h);
-      sm.beta[tid] = b;
+    if (tid < TILE) sm.beta[tid] = io<TIN>::ld(&bcur);
+    if (base + CH < end) {
+      load_raw(base + CH, nxt);
+      bnx = load_beta(base + CH);
     }
     lds_barrier();
+    // outputs of the previous chunk (staged at its end): stored now, so that
+    // no later wait for a load has to cover these stores as well
+    if (base != first) store_out(base - CH);
     // ------------------------------------------------ phase G: cumulative gates
+    // G = inclusive cumulative sum of g down the chunk rows, per key channel:
+    // each wave takes D / NW channels, each lane a run of RP rows of one
+    // channel; the runs are chained by a scan across the lanes of the wave.
     {
-      constexpr int NPART = NT / D;          // threads per channel
-      constexpr int RP = TILE / NPART;       // rows per thread
-      const int c = tid % D;
-      const int part = tid / D;
-      float acc = 0.f;
+      constexpr int CPW = D / NW;
+      constexpr int NPART = 64 / CPW;
+      constexpr int RP = TILE / NPART;
+      const int c = CPW * wave + lane % CPW;
+      const int part = lane / CPW;
       float gl[RP];
+      float acc = 0.f;
 #pragma unroll
       for (int i = 0; i < RP; ++i) {
         acc += io<TIN>::ld(&sm.u.a.g_raw[part * RP + i][c]);
         gl[i] = acc;
       }
-      sm.u.a.scan[part * D + c] = acc;
-      lds_barrier();
-      float off = 0.f;
-      for (int q = 0; q < part; ++q) off += sm.u.a.scan[q * D + c];
+      float incl = acc;
+#pragma unroll
+      for (int o = 1; o < NPART; o <<= 1) {
+        const float y = __shfl_up(incl, o * CPW, 64);
+        if (part >= o) incl += y;
+      }
+      const float off = incl - acc;
 #pragma unroll
       for (int i = 0; i < RP; ++i) sm.u.a.G[part * RP + i][c] = gl[i] + off;
-      lds_barrier();
-      if (tid < D) {
-        const float gm = sm.u.a.G[MID][tid];
-        sm.eg_m[tid] = expf(gm);
-        sm.eg_e[tid] = expf(sm.u.a.G[TILE - 1][tid] - gm);
-      }
+    }
+    lds_barrier();
+    if (tid < D) {
+      const float gm = sm.u.a.G[MID][tid];
+      sm.eg_m[tid] = expf(gm);
+      sm.eg_e[tid] = expf(sm.u.a.G[TILE - 1][tid] - gm);
     }
     // ------------------------------------------------ phase O: gated operands (row-major)
     if (has_item) {
@@ -716,31 +759,12 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
 #pragma unroll
         for (int i = 0; i < 4; ++i) O[mt][i] += Ob[mt][i] + Oc[mt][i];
     }
-    lds_barrier();   // every wave is done reading lq / P / Wn / rk
-    // ------------------------------------------------ outputs: stage through LDS, store rows
+    // ------------------------------------------------ outputs: stage in LDS (stored during the next chunk)
     if (chain) {
-      // stage O (scaled, output type) into the lq area: [32 rows][D columns]
-      TOUT* stg = reinterpret_cast<TOUT*>(&sm.lq_hi[0][0]);
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) io<TOUT>::st(stg + (16 * mt + 4 * g4 + e) * D + ncol, O[mt][e] * p.scale);
-    }
-    lds_barrier();
-    {
-      constexpr int OV = 16 / sizeof(TOUT);   // elements per vector
-      constexpr int NOV = D / OV;             // vectors per row
-      const TOUT* stg = reinterpret_cast<const TOUT*>(&sm.lq_hi[0][0]);
-      for (int it = tid; it < TILE * NOV; it += NT) {
-        const int r = it / NOV;
-        const int cc = (it % NOV) * OV;
-        const int64_t pos = base + r;
-        if (r < CH && pos >= start && pos < end && cc < d) {
-          const int64_t tok = bos + (pos - start);
-          TOUT* dstp = og + tok * p.o_stride + static_cast<int64_t>(h) * d + cc;
-          *reinterpret_cast<uint4*>(dstp) = *reinterpret_cast<const uint4*>(stg + r * D + cc);
-        }
-      }
+        for (int e = 0; e < 4; ++e) io<TOUT>::st(&sm.ostg[16 * mt + 4 * g4 + e][ncol], O[mt][e] * p.scale);
     }
     // ------------------------------------------------ interval checkpoint
     if (p.ckpt_interval > 0 && p.ckpt_cu) {
@@ -757,6 +781,14 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
       }
     }
     lds_barrier();
+  };
+  for (int64_t base = first; base < end; base += 2 * CH) {
+    chunk(base, rawA, betaA, rawB, betaB);
+    if (base + CH < end) chunk(base + CH, rawB, betaB, rawA, betaA);
+  }
+  if (len > 0) {
+    lds_barrier();
+    store_out(first + ((end - 1 - first) / CH) * CH);
   }
   // ---- final state
   if (chain && has_dst && ncol < d) state_store<D>(p.pool + (static_cast<int64_t>(dst) * H + h) * d * d, S, lane, ncol, d);
