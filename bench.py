@@ -246,9 +246,11 @@ def bench_prefill_varlen(torch, K, make_workload, dev, iters=20, wl=None):
     dst = torch.arange(N, 2 * N, dtype=torch.int32, device=dev)
     cu = wl.cu_seqlens.to(dev)
     o = torch.empty(T, H, D, dtype=torch.bfloat16, device=dev)
+    nws = K.kda_prefill_workspace_bytes(q, k, v, g, b, o, cu, pool, src, dst, chunk=64)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
 
     def run():
-        K.kda_prefill_varlen(q, k, v, g, b, o, cu, pool, src, dst, chunk=64)
+        K.kda_prefill_varlen(q, k, v, g, b, o, cu, pool, src, dst, chunk=64, workspace=ws)
 
     for _ in range(2):
         run()

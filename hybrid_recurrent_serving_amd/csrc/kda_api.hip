@@ -289,6 +289,8 @@ static int prefill_validate(const kda_prefill_args* a, kda_prefill_args& b) {
   if (b.ckpt_interval < 0) return fail(KDA_ERR_SHAPE, "ckpt_interval < 0");
   if (b.ckpt_interval > 0 && b.ckpt_interval % b.chunk != 0)
     return fail(KDA_ERR_ALIGN, "ckpt_interval %d not a multiple of chunk %d", b.ckpt_interval, b.chunk);
+  if (b.segment_len > 0 && b.segment_len % b.chunk != 0)
+    return fail(KDA_ERR_ALIGN, "segment_len %d not a multiple of chunk %d", b.segment_len, b.chunk);
   if (b.ckpt_interval > 0 && (!b.ckpt_cu || (b.n_ckpt > 0 && !b.ckpt_slot)))
     return fail(KDA_ERR_NULL, "checkpoints requested without ckpt_cu / ckpt_slot");
   if (!b.cu_seqlens) return fail(KDA_ERR_NULL, "cu_seqlens is NULL");
@@ -310,6 +312,7 @@ static PrefillParams prefill_params(const kda_prefill_args& b) {
   p.beta_stride = b.beta_stride; p.o_stride = b.o_stride;
   p.T_tot = b.T_tot; p.n_slots = b.n_slots; p.n_ckpt = b.n_ckpt; p.workspace_bytes = b.workspace_bytes;
   p.n_seq = b.n_seq; p.H = b.H; p.chunk = b.chunk; p.ckpt_interval = b.ckpt_interval; p.scale = b.scale;
+  p.segment_len = b.segment_len;
   return p;
 }
 

@@ -59,7 +59,18 @@ struct PrefillParams {
   int64_t T_tot, n_slots, n_ckpt, workspace_bytes;
   int32_t n_seq, H, chunk, ckpt_interval;
   float scale;
+  // segment scan (long sequences): set by launch_prefill
+  int32_t segment_len;            // effective length (> 0), or <= 0 = no split
+  int32_t mode;                   // kModeFull / kModeLocal / kModeTransition / kModePassA
+  const int32_t* seg_cu;          // [n_seq + 1] first work item of each sequence, or NULL
+  const int32_t* blk_cu;          // [n_seq + 1] first workspace block of each sequence
+  float* ws_states;               // 3 d x d blocks per head for every block index
+  int64_t ws_max_blocks;
 };
+
+// work modes of the prefill kernel
+enum { kModeFull = 0, kModeLocal = 1, kModeTransition = 2, kModePassA = 3 };
+constexpr int32_t kDefaultSegmentLen = 32768;
 
 int64_t prefill_workspace_bytes(const PrefillParams& p, int D);
 int launch_prefill(const PrefillParams& p, int D, int in_dtype, int out_dtype, hipStream_t stream);

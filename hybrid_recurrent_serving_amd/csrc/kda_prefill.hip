@@ -296,9 +296,33 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
   const int wave = tid >> 6;
   const int g4 = lane >> 4;             // 16-lane group
   const int l16 = lane & 15;
-  const int s = static_cast<int>(blockIdx.x / p.H);
-  const int h = static_cast<int>(blockIdx.x % p.H);
   const int H = p.H;
+  // pass A runs both of its modes in one launch (grid.y = 2)
+  const int mode = p.mode == kModePassA ? kModeLocal + static_cast<int>(blockIdx.y) : p.mode;
+  const int item = static_cast<int>(blockIdx.x / H);
+  const int h = static_cast<int>(blockIdx.x % H);
+  // work item -> (sequence s, segment m): without a segment table every
+  // sequence is one item; with one, seg_cu holds each sequence's first item
+  int s = item, m = 0, nseg = 1;
+  if (p.seg_cu) {
+    if (item >= p.seg_cu[p.n_seq]) return;
+    int a = 0, b = p.n_seq;               // seg_cu[a] <= item < seg_cu[b]
+    while (b - a > 1) {
+      const int mid = (a + b) >> 1;
+      if (p.seg_cu[mid] <= item) a = mid; else b = mid;
+    }
+    s = a;
+    m = item - p.seg_cu[s];
+    nseg = p.seg_cu[s + 1] - p.seg_cu[s];
+  } else if (item >= p.n_seq) {
+    return;
+  }
+  const bool first_seg = m == 0;
+  const bool last_seg = m == nseg - 1;
+  // pass A (local end state / transition) is not needed for a last segment,
+  // and the transition of a first segment is never used
+  if (mode == kModeLocal && last_seg) return;
+  if (mode == kModeTransition && (first_seg || last_seg)) return;
 
   int64_t bos = p.cu[s], eos = p.cu[s + 1];
   bos = bos < 0 ? 0 : (bos > p.T_tot ? p.T_tot : bos);
@@ -307,10 +331,28 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
   int64_t start = p.start_pos ? static_cast<int64_t>(p.start_pos[s]) : 0;
   if (start < 0) start = 0;
   const int64_t end = start + len;
+  // token range [lo, hi) of this work item: the whole sequence, or its part
+  // inside absolute window w0 + m of the segment length
+  int64_t lo = start, hi = end;
+  if (nseg > 1) {
+    const int64_t seg = p.segment_len;
+    const int64_t w0 = start / seg;
+    lo = first_seg ? start : (w0 + m) * seg;
+    hi = (w0 + m + 1) * seg;
+    hi = hi < end ? hi : end;
+  }
+  const bool outputs = mode == kModeFull;
   const int src = p.src_slot[s];
   const int dst = p.dst_slot[s];
   const bool has_src = src >= 0 && src < p.n_slots;
-  const bool has_dst = dst >= 0 && dst < p.n_slots;
+  const bool has_dst = dst >= 0 && dst < p.n_slots && last_seg && outputs;
+  // segment-scan blocks of this item (kind 0: incoming state, 1: local end
+  // state, 2: transition), each a d x d fp32 matrix per head
+  const int64_t blk = p.seg_cu ? static_cast<int64_t>(p.blk_cu[s]) + m : -1;
+  const bool has_blk = nseg > 1 && blk >= 0 && blk < p.ws_max_blocks;
+  auto ws_block = [&](int kind) -> float* {
+    return p.ws_states + (blk * 3 + kind) * H * d * d + static_cast<int64_t>(h) * d * d;
+  };
   const bool chain = wave < NWC;
   const int ncol = 16 * wave + l16;     // d_v column of this lane (chain waves)
 
@@ -318,7 +360,17 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
   f32x4 S[NQ];
 #pragma unroll
   for (int q = 0; q < NQ; ++q) S[q] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (chain && has_src && ncol < d) state_load<D>(p.pool + (static_cast<int64_t>(src) * H + h) * d * d, S, lane, ncol, d);
+  if (mode == kModeTransition) {
+    // transition of the segment: the recurrence applied to S = I with V = 0
+#pragma unroll
+    for (int q = 0; q < NQ; ++q)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) S[q][i] = (16 * q + 4 * g4 + i == ncol) ? 1.f : 0.f;
+  } else if (first_seg) {
+    if (chain && has_src && ncol < d) state_load<D>(p.pool + (static_cast<int64_t>(src) * H + h) * d * d, S, lane, ncol, d);
+  } else if (mode == kModeFull && has_blk) {
+    if (chain && ncol < d) state_load<D>(ws_block(0), S, lane, ncol, d);
+  }
   // The initial state is complete here: a first use inside the chunk loop
   // would leave a wait for all outstanding memory operations in every trip.
 #pragma unroll
@@ -340,7 +392,8 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
 
   auto load_raw = [&](int64_t base, RawRow<TIN>& rr) {
     const int64_t pos = base + ir;
-    const bool valid = has_item && ir < CH && pos >= start && pos < end && c0 < d;
+    const bool valid = has_item && ir < CH && pos >= lo && pos < hi && c0 < d;
+    const bool with_v = mode != kModeTransition;
 #pragma unroll
     for (int w = 0; w < 2 * NU; ++w) rr.q[w] = rr.k[w] = rr.v[w] = rr.g[w] = make_uint2(0, 0);
     if (valid) {
@@ -355,26 +408,26 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
       for (int w = 0; w < NU; ++w) {
         rr.q[w] = reinterpret_cast<const uint2*>(qp)[w];
         rr.k[w] = reinterpret_cast<const uint2*>(kp)[w];
-        rr.v[w] = reinterpret_cast<const uint2*>(vp)[w];
+        if (with_v) rr.v[w] = reinterpret_cast<const uint2*>(vp)[w];
         rr.g[w] = reinterpret_cast<const uint2*>(gp)[w];
         if (second) {
           rr.q[NU + w] = reinterpret_cast<const uint2*>(qp + 16)[w];
           rr.k[NU + w] = reinterpret_cast<const uint2*>(kp + 16)[w];
-          rr.v[NU + w] = reinterpret_cast<const uint2*>(vp + 16)[w];
+          if (with_v) rr.v[NU + w] = reinterpret_cast<const uint2*>(vp + 16)[w];
           rr.g[NU + w] = reinterpret_cast<const uint2*>(gp + 16)[w];
         }
       }
     }
   };
 
-  const int64_t first = len > 0 ? (start / CH) * CH : end;
+  const int64_t first = hi > lo ? (lo / CH) * CH : hi;
   // beta of row tid (threads tid < TILE), prefetched like the raw tile and
   // kept as raw input bits until the next chunk (converting it here would
   // wait for the whole prefetch)
   auto load_beta = [&](int64_t base) -> TIN {
     const int64_t pos = base + tid;
     TIN b = 0;
-    if (tid < CH && pos >= start && pos < end) b = bg[(bos + (pos - start)) * p.beta_stride + h];
+    if (tid < CH && pos >= lo && pos < hi) b = bg[(bos + (pos - start)) * p.beta_stride + h];
     return b;
   };
   // rows of the staged output tile that belong to the sequence -> o (16-byte stores)
@@ -385,7 +438,7 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
       const int r = it / NOV;
       const int cc = (it % NOV) * OV;
       const int64_t pos = obase + r;
-      if (r < CH && pos >= start && pos < end && cc < d) {
+      if (r < CH && pos >= lo && pos < hi && cc < d) {
         const int64_t tok = bos + (pos - start);
         TOUT* dstp = og + tok * p.o_stride + static_cast<int64_t>(h) * d + cc;
         *reinterpret_cast<uint4*>(dstp) = *reinterpret_cast<const uint4*>(&sm.ostg[r][cc]);
@@ -441,14 +494,14 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
       }
     }
     if (tid < TILE) sm.beta[tid] = io<TIN>::ld(&bcur);
-    if (base + CH < end) {
+    if (base + CH < hi) {
       load_raw(base + CH, nxt);
       bnx = load_beta(base + CH);
     }
     lds_barrier();
     // outputs of the previous chunk (staged at its end): stored now, so that
     // no later wait for a load has to cover these stores as well
-    if (base != first) store_out(base - CH);
+    if (outputs && base != first) store_out(base - CH);
     // ------------------------------------------------ phase G: cumulative gates
     // G = inclusive cumulative sum of g down the chunk rows, per key channel:
     // each wave takes D / NW channels, each lane a run of RP rows of one
@@ -760,14 +813,14 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
         for (int i = 0; i < 4; ++i) O[mt][i] += Ob[mt][i] + Oc[mt][i];
     }
     // ------------------------------------------------ outputs: stage in LDS (stored during the next chunk)
-    if (chain) {
+    if (chain && outputs) {
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int e = 0; e < 4; ++e) io<TOUT>::st(&sm.ostg[16 * mt + 4 * g4 + e][ncol], O[mt][e] * p.scale);
     }
     // ------------------------------------------------ interval checkpoint
-    if (p.ckpt_interval > 0 && p.ckpt_cu) {
+    if (outputs && p.ckpt_interval > 0 && p.ckpt_cu) {
       const int64_t after = base + CH;
       if (after < end && after % p.ckpt_interval == 0) {
         const int64_t j = after / p.ckpt_interval - start / p.ckpt_interval - 1;
@@ -782,26 +835,173 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
     }
     lds_barrier();
   };
-  for (int64_t base = first; base < end; base += 2 * CH) {
+  for (int64_t base = first; base < hi; base += 2 * CH) {
     chunk(base, rawA, betaA, rawB, betaB);
-    if (base + CH < end) chunk(base + CH, rawB, betaB, rawA, betaA);
+    if (base + CH < hi) chunk(base + CH, rawB, betaB, rawA, betaA);
   }
-  if (len > 0) {
+  if (outputs && hi > lo) {
     lds_barrier();
-    store_out(first + ((end - 1 - first) / CH) * CH);
+    store_out(first + ((hi - 1 - first) / CH) * CH);
   }
-  // ---- final state
-  if (chain && has_dst && ncol < d) state_store<D>(p.pool + (static_cast<int64_t>(dst) * H + h) * d * d, S, lane, ncol, d);
+  // ---- final state: the destination slot, or a segment-scan block
+  if (chain && ncol < d) {
+    if (has_dst) state_store<D>(p.pool + (static_cast<int64_t>(dst) * H + h) * d * d, S, lane, ncol, d);
+    if (mode == kModeLocal && has_blk) state_store<D>(ws_block(1), S, lane, ncol, d);
+    if (mode == kModeTransition && has_blk) state_store<D>(ws_block(2), S, lane, ncol, d);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Segment plan (one workgroup): per sequence the number of work items (1, or
+// its number of segments when it is split) and of workspace blocks (0, or
+// the same number), as exclusive prefix sums seg_cu / blk_cu.
+__device__ __forceinline__ int seq_segments(const PrefillParams& p, int s) {
+  int64_t bos = p.cu[s], eos = p.cu[s + 1];
+  bos = bos < 0 ? 0 : (bos > p.T_tot ? p.T_tot : bos);
+  eos = eos < bos ? bos : (eos > p.T_tot ? p.T_tot : eos);
+  const int64_t len = eos - bos;
+  int64_t start = p.start_pos ? static_cast<int64_t>(p.start_pos[s]) : 0;
+  if (start < 0) start = 0;
+  const int64_t seg = p.segment_len;
+  if (len < 2 * seg) return 1;
+  return static_cast<int>((start + len - 1) / seg - start / seg + 1);
+}
+
+constexpr int PLAN_T = 256;
+
+__global__ void __launch_bounds__(PLAN_T) segment_plan_kernel(const PrefillParams p, int32_t* seg_cu, int32_t* blk_cu) {
+  __shared__ int64_t part_i[PLAN_T], part_b[PLAN_T];
+  const int t = threadIdx.x;
+  const int per = (p.n_seq + PLAN_T - 1) / PLAN_T;
+  const int a = t * per;
+  const int b = a + per < p.n_seq ? a + per : p.n_seq;
+  int64_t ci = 0, cb = 0;
+  for (int s = a; s < b; ++s) {
+    const int n = seq_segments(p, s);
+    ci += n;
+    cb += n > 1 ? n : 0;
+  }
+  part_i[t] = ci;
+  part_b[t] = cb;
+  __syncthreads();
+  if (t == 0) {
+    int64_t ri = 0, rb = 0;
+    for (int j = 0; j < PLAN_T; ++j) {
+      const int64_t xi = part_i[j], xb = part_b[j];
+      part_i[j] = ri;
+      part_b[j] = rb;
+      ri += xi;
+      rb += xb;
+    }
+    seg_cu[p.n_seq] = static_cast<int32_t>(ri);
+    blk_cu[p.n_seq] = static_cast<int32_t>(rb);
+  }
+  __syncthreads();
+  int64_t ri = part_i[t], rb = part_b[t];
+  for (int s = a; s < b; ++s) {
+    const int n = seq_segments(p, s);
+    seg_cu[s] = static_cast<int32_t>(ri);
+    blk_cu[s] = static_cast<int32_t>(rb);
+    ri += n;
+    rb += n > 1 ? n : 0;
+  }
+}
+
+// Chains the segments of every split sequence, per (sequence, head) and
+// block of 16 state columns, in fp32:
+//     S_in(1) = S_loc(0),   S_in(j+1) = M_j S_in(j) + S_loc(j).
+constexpr int COMB_T = 256;
+
+__global__ void __launch_bounds__(COMB_T) segment_combine_kernel(const PrefillParams p, int d) {
+  __shared__ float X[128][16];
+  const int H = p.H;
+  const int s = static_cast<int>(blockIdx.x / H);
+  const int h = static_cast<int>(blockIdx.x % H);
+  const int c0 = 16 * static_cast<int>(blockIdx.y);
+  const int nseg = p.seg_cu[s + 1] - p.seg_cu[s];
+  const int64_t b0 = p.blk_cu[s];
+  if (nseg < 2 || b0 < 0 || b0 + nseg > p.ws_max_blocks || c0 >= d) return;
+  const int t = threadIdx.x;
+  const int r = t >> 1;            // state row (key channel)
+  const int j0 = 8 * (t & 1);      // first of this thread's 8 columns
+  const bool act = r < d;
+  const int64_t dd = static_cast<int64_t>(d) * d;
+  auto blk = [&](int64_t m, int kind) -> float* {
+    return p.ws_states + ((b0 + m) * 3 + kind) * H * dd + static_cast<int64_t>(h) * dd;
+  };
+  float acc[8];
+  if (act) {
+    const float* sl = blk(0, 1) + static_cast<int64_t>(r) * d + c0 + j0;
+    float* si = blk(1, 0) + static_cast<int64_t>(r) * d + c0 + j0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      acc[j] = (c0 + j0 + j < d) ? sl[j] : 0.f;
+      if (c0 + j0 + j < d) si[j] = acc[j];
+      X[r][j0 + j] = acc[j];
+    }
+  }
+  for (int m = 1; m + 1 < nseg; ++m) {
+    __syncthreads();
+    if (act) {
+      const float* mr = blk(m, 2) + static_cast<int64_t>(r) * d;
+      const float* sl = blk(m, 1) + static_cast<int64_t>(r) * d + c0 + j0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] = (c0 + j0 + j < d) ? sl[j] : 0.f;
+      for (int k = 0; k < d; ++k) {
+        const float mk = mr[k];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] += mk * X[k][j0 + j];
+      }
+    }
+    __syncthreads();
+    if (act) {
+      float* si = blk(m + 1, 0) + static_cast<int64_t>(r) * d + c0 + j0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        X[r][j0 + j] = acc[j];
+        if (c0 + j0 + j < d) si[j] = acc[j];
+      }
+    }
+  }
 }
 
 template <int D, typename TIN, typename TOUT>
-static int launch_t(const PrefillParams& p, int d, int CH, hipStream_t stream) {
-  const int64_t nblk = static_cast<int64_t>(p.n_seq) * p.H;
-  if (nblk > 0x7fffffffLL) return fail(KDA_ERR_SHAPE, "n_seq * H too large");
-  hipLaunchKernelGGL((prefill_kernel<D, TIN, TOUT>), dim3(static_cast<uint32_t>(nblk)), dim3(NT), 0, stream, p, d, CH);
+static int launch_kernel(const PrefillParams& p, int d, int CH, int64_t n_items, int gy, hipStream_t stream) {
+  const int64_t nblk = n_items * p.H;
+  if (nblk > 0x7fffffffLL) return fail(KDA_ERR_SHAPE, "prefill grid too large");
+  if (nblk == 0) return KDA_OK;
+  hipLaunchKernelGGL((prefill_kernel<D, TIN, TOUT>), dim3(static_cast<uint32_t>(nblk), gy), dim3(NT), 0, stream, p, d,
+                     CH);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(KDA_ERR_HIP, "prefill kernel launch: %s", hipGetErrorString(e));
   return KDA_OK;
+}
+
+template <int D, typename TIN, typename TOUT>
+static int launch_t(const PrefillParams& p0, int d, int CH, hipStream_t stream) {
+  PrefillParams p = p0;
+  if (!p.seg_cu) {
+    p.mode = kModeFull;
+    return launch_kernel<D, TIN, TOUT>(p, d, CH, p.n_seq, 1, stream);
+  }
+  // work items: every sequence once, plus the extra segments of split ones
+  // (a split sequence of len tokens adds at most len / seg + 1 <= 1.5 len / seg)
+  const int64_t n_items = p.n_seq + (3 * p.T_tot) / (2 * static_cast<int64_t>(p.segment_len)) + 1;
+  hipLaunchKernelGGL(segment_plan_kernel, dim3(1), dim3(PLAN_T), 0, stream, p, const_cast<int32_t*>(p.seg_cu),
+                     const_cast<int32_t*>(p.blk_cu));
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, "segment plan launch: %s", hipGetErrorString(e));
+  p.mode = kModePassA;
+  int st = launch_kernel<D, TIN, TOUT>(p, d, CH, n_items, 2, stream);
+  if (st) return st;
+  const int64_t ncomb = static_cast<int64_t>(p.n_seq) * p.H;
+  if (ncomb > 0x7fffffffLL) return fail(KDA_ERR_SHAPE, "segment combine grid too large");
+  hipLaunchKernelGGL(segment_combine_kernel, dim3(static_cast<uint32_t>(ncomb), (d + 15) / 16), dim3(COMB_T), 0,
+                     stream, p, d);
+  e = hipGetLastError();
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, "segment combine launch: %s", hipGetErrorString(e));
+  p.mode = kModeFull;
+  return launch_kernel<D, TIN, TOUT>(p, d, CH, n_items, 1, stream);
 }
 
 template <typename TIN, typename TOUT>
@@ -817,11 +1017,42 @@ static int launch_d(const PrefillParams& p, int d, int CH, hipStream_t stream) {
 
 }  // namespace pf
 
-int64_t prefill_workspace_bytes(const PrefillParams&, int) { return 0; }
+// Effective segment length: 0 = the default, < 0 = never split.
+static int64_t effective_segment(const PrefillParams& p) {
+  return p.segment_len == 0 ? kDefaultSegmentLen : p.segment_len;
+}
 
-int launch_prefill(const PrefillParams& p, int D, int in_dtype, int out_dtype, hipStream_t stream) {
+static int64_t round256(int64_t x) { return (x + 255) / 256 * 256; }
+
+// Workspace layout: seg_cu [n_seq + 1] and blk_cu [n_seq + 1] (int32, each
+// rounded up to 256 bytes), then 3 fp32 blocks [H][d][d] per block index.
+// A split sequence of len >= 2 seg tokens spans at most 2 len / seg
+// segments, so 2 T_tot / seg + 1 block indices always suffice.
+int64_t prefill_workspace_bytes(const PrefillParams& p, int D) {
+  const int64_t seg = effective_segment(p);
+  if (seg <= 0 || p.T_tot < 2 * seg) return 0;
+  const int64_t blocks = 2 * p.T_tot / seg + 1;
+  return 2 * round256(4 * (static_cast<int64_t>(p.n_seq) + 1)) +
+         blocks * 3 * p.H * static_cast<int64_t>(D) * D * 4;
+}
+
+int launch_prefill(const PrefillParams& p0, int D, int in_dtype, int out_dtype, hipStream_t stream) {
   // chunk 64 runs as two chunks of 32 (identical result up to rounding)
-  const int CH = p.chunk == 16 ? 16 : 32;
+  const int CH = p0.chunk == 16 ? 16 : 32;
+  PrefillParams p = p0;
+  p.seg_cu = p.blk_cu = nullptr;
+  p.ws_states = nullptr;
+  p.ws_max_blocks = 0;
+  if (prefill_workspace_bytes(p0, D) > 0) {
+    const int64_t seg = effective_segment(p0);
+    char* w = static_cast<char*>(p.workspace);
+    const int64_t idx = round256(4 * (static_cast<int64_t>(p.n_seq) + 1));
+    p.segment_len = static_cast<int32_t>(seg);
+    p.seg_cu = reinterpret_cast<const int32_t*>(w);
+    p.blk_cu = reinterpret_cast<const int32_t*>(w + idx);
+    p.ws_states = reinterpret_cast<float*>(w + 2 * idx);
+    p.ws_max_blocks = 2 * p.T_tot / seg + 1;
+  }
   if (in_dtype == KDA_BF16) {
     if (out_dtype == KDA_BF16) return pf::launch_d<bf16_t, bf16_t>(p, D, CH, stream);
     return pf::launch_d<bf16_t, float>(p, D, CH, stream);

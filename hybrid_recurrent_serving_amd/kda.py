@@ -55,7 +55,7 @@ class PrefillArgs(ctypes.Structure):
         ("T_tot", c_i64), ("n_slots", c_i64), ("workspace_bytes", c_i64), ("n_ckpt", c_i64),
         ("n_seq", c_i32), ("H", c_i32), ("d_k", c_i32), ("d_v", c_i32), ("chunk", c_i32),
         ("in_dtype", c_i32), ("out_dtype", c_i32), ("ckpt_interval", c_i32), ("scale", c_f32),
-        ("reserved", c_i32),
+        ("segment_len", c_i32),
     ]
 
 
@@ -270,7 +270,8 @@ def kda_ckpt_plan(cu_seqlens, interval: int, chunk: int, start_pos=None):
 
 
 def _prefill_args(q, k, v, g, beta, o, cu_seqlens, state_pool, src_slot, dst_slot, chunk,
-                  start_pos, ckpt_interval, ckpt_cu, ckpt_slot, ckpt_pos_out, workspace, scale):
+                  start_pos, ckpt_interval, ckpt_cu, ckpt_slot, ckpt_pos_out, workspace, scale,
+                  segment_len=0):
     import torch
     _expect(q.dim() == 3 and v.dim() == 3 and beta.dim() == 2, "q/k/v/g [T, H, d], beta [T, H]")
     T, H, dk = q.shape
@@ -307,14 +308,15 @@ def _prefill_args(q, k, v, g, beta, o, cu_seqlens, state_pool, src_slot, dst_slo
     a.chunk = chunk
     a.in_dtype, a.out_dtype = _dtype_code(q), _dtype_code(o)
     a.ckpt_interval, a.scale = ckpt_interval, scale
+    a.segment_len = int(segment_len)
     return a
 
 
 def kda_prefill_workspace_bytes(q, k, v, g, beta, o, cu_seqlens, state_pool, src_slot, dst_slot,
                                 *, chunk=64, start_pos=None, ckpt_interval=0, ckpt_cu=None,
-                                ckpt_slot=None, scale=1.0) -> int:
+                                ckpt_slot=None, scale=1.0, segment_len=0) -> int:
     a = _prefill_args(q, k, v, g, beta, o, cu_seqlens, state_pool, src_slot, dst_slot, chunk,
-                      start_pos, ckpt_interval, ckpt_cu, ckpt_slot, None, None, scale)
+                      start_pos, ckpt_interval, ckpt_cu, ckpt_slot, None, None, scale, segment_len)
     n = load_library().kda_prefill_workspace_bytes(ctypes.byref(a))
     if n < 0:
         raise KDAError(8, "KDA_ERR_ARG", kda_last_error())
@@ -323,11 +325,23 @@ def kda_prefill_workspace_bytes(q, k, v, g, beta, o, cu_seqlens, state_pool, src
 
 def kda_prefill_varlen(q, k, v, g, beta, o, cu_seqlens, state_pool, src_slot, dst_slot, *,
                        chunk=64, start_pos=None, ckpt_interval=0, ckpt_cu=None, ckpt_slot=None,
-                       ckpt_pos_out=None, workspace=None, scale=1.0, stream=None):
-    """Chunked varlen prefill; see include/kda.h for the argument contract."""
+                       ckpt_pos_out=None, workspace=None, scale=1.0, segment_len=0, stream=None):
+    """Chunked varlen prefill; see include/kda.h for the argument contract.
+
+    ``workspace``: a device tensor of at least kda_prefill_workspace_bytes()
+    bytes, needed when a sequence may be split (``segment_len``).  When it is
+    None and the call needs one, a byte tensor is allocated on q's device."""
     a = _prefill_args(q, k, v, g, beta, o, cu_seqlens, state_pool, src_slot, dst_slot, chunk,
-                      start_pos, ckpt_interval, ckpt_cu, ckpt_slot, ckpt_pos_out, workspace, scale)
-    _check(load_library().kda_prefill_varlen(ctypes.byref(a), _stream(stream)))
+                      start_pos, ckpt_interval, ckpt_cu, ckpt_slot, ckpt_pos_out, workspace, scale,
+                      segment_len)
+    lib = load_library()
+    if workspace is None:
+        need = lib.kda_prefill_workspace_bytes(ctypes.byref(a))
+        if need > 0:
+            import torch
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+            a.workspace, a.workspace_bytes = _ptr(workspace), need
+    _check(lib.kda_prefill_varlen(ctypes.byref(a), _stream(stream)))
     return o
 
 

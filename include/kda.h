@@ -170,10 +170,20 @@ int kda_ckpt_plan(const int32_t *cu_seqlens, const int32_t *start_pos, int32_t n
  *
  * Chunk boundaries are aligned to absolute positions (multiples of chunk),
  * so a sequence may start mid-chunk; checkpoints therefore always fall on
- * chunk boundaries.  Long sequences are split into segments processed in
- * parallel and joined by a transition-matrix combine; the split needs the
- * workspace (size from kda_prefill_workspace_bytes for the same args; 0 is
- * possible for short batches).
+ * chunk boundaries.
+ *
+ * Segment scan.  A sequence of at least 2 * segment_len tokens is split at
+ * the absolute multiples of segment_len into segments that run in parallel:
+ * every segment but the last first computes, from a zero state (the first
+ * segment: from its true initial state), its end state S_loc and its
+ * transition M (the same recurrence applied to S = I with v = 0); then
+ * S_in(j+1) = M_j S_in(j) + S_loc(j) chains the segments (fp32), and every
+ * segment reruns from its S_in with outputs and checkpoints.  The result is
+ * the same function of the inputs as the unsplit run (up to rounding).  The
+ * split needs the workspace: its size comes from kda_prefill_workspace_bytes
+ * for the same args (0 when T_tot < 2 * segment_len, since nothing can be
+ * split then).  segment_len: 0 = the library default (32768), < 0 = never
+ * split, > 0 = that length, a multiple of chunk (else KDA_ERR_ALIGN).
  * ---------------------------------------------------------------------- */
 typedef struct kda_prefill_args {
     size_t struct_size;          /* sizeof(kda_prefill_args) */
@@ -203,7 +213,7 @@ typedef struct kda_prefill_args {
     int32_t in_dtype, out_dtype;
     int32_t ckpt_interval;       /* 0 = no checkpoints; multiple of chunk */
     float scale;
-    int32_t reserved;
+    int32_t segment_len;         /* segment scan length: 0 default, < 0 off */
 } kda_prefill_args;
 
 /* Workspace bytes kda_prefill_varlen needs for these args (host-only). */

@@ -138,6 +138,24 @@ def test_prefill_validation(lib):
     assert _call(lib, "kda_prefill_varlen", _prefill_args(cu_seqlens=None)) == 1
     assert _call(lib, "kda_prefill_varlen", _prefill_args(n_seq=0)) == 0
     assert lib.kda_prefill_workspace_bytes(ctypes.byref(_prefill_args(chunk=48))) == -1
+    assert _call(lib, "kda_prefill_varlen", _prefill_args(segment_len=100)) == 4
+    # a batch long enough to be split needs the workspace
+    assert _call(lib, "kda_prefill_varlen", _prefill_args(T_tot=65536)) == 5
+
+
+def test_prefill_workspace_bytes(lib):
+    """Segment-scan workspace: seg_cu and blk_cu (int32 [n_seq + 1], 256-byte
+    rounded) plus three H x d x d fp32 blocks per block index, with
+    2 T_tot / seg + 1 block indices; nothing when T_tot < 2 seg."""
+    ws = lambda **kw: lib.kda_prefill_workspace_bytes(ctypes.byref(_prefill_args(**kw)))
+    H, d = 2, 64
+    blk = 3 * H * d * d * 4
+    assert ws(T_tot=100) == 0
+    assert ws(T_tot=65535) == 0                         # < 2 x 32768: nothing can split
+    assert ws(T_tot=65536) == 2 * 256 + (2 * 65536 // 32768 + 1) * blk
+    assert ws(T_tot=65536, segment_len=-1) == 0
+    assert ws(T_tot=4096, segment_len=1024) == 2 * 256 + 9 * blk
+    assert ws(T_tot=2047, segment_len=1024) == 0
 
 
 def test_ckpt_plan_matches_oracle_enumeration(oracle64):

@@ -32,7 +32,7 @@ def _init_arrays(wl):
 
 
 def run_prefill(dev, wl, *, chunk, out_dtype=torch.bfloat16, start_pos=None, ckpt_interval=0,
-                scale=1.0):
+                scale=1.0, segment_len=0):
     """Run the GPU prefill with source slots [0, N) (zero where the workload
     has no initial state) and destination slots [N, 2N); checkpoints (if any)
     go to slots from 2N on.  Returns dict of host tensors."""
@@ -61,7 +61,7 @@ def run_prefill(dev, wl, *, chunk, out_dtype=torch.bfloat16, start_pos=None, ckp
         kw["ckpt_pos_out"] = torch.full((max(n_ck, 1),), -1, dtype=torch.int32, device=dev)
     before = pool[:N].clone()
     K.kda_prefill_varlen(q, k, v, g, b, o, wl.cu_seqlens.to(dev), pool, src, dst, chunk=chunk,
-                         scale=scale, **kw)
+                         scale=scale, segment_len=segment_len, **kw)
     torch.cuda.synchronize()
     assert torch.equal(pool[:N], before), "source slots were modified"
     res = {"o": o.float().cpu(), "final": pool[N:2 * N].cpu(), "init": init, "has": has}
@@ -239,3 +239,60 @@ def test_prefill_long_65536_full(dev, oracle64):
     U.assert_close("o", r["o"].numpy(), ref["o"])
     U.assert_close("ckpt+final", np.concatenate([r["ckpt"].numpy(), r["final"].numpy()]),
                    np.concatenate([ref["ckpt"], ref["final"]]))
+
+
+# ------------------------------------------------------------------ segment scan
+@pytest.mark.parametrize("d", [64, 128])
+def test_prefill_segment_scan_slow_decay(dev, oracle64, d):
+    """Sequences of >= 2 segment lengths run as parallel segments joined by
+    the transition combine.  Slow decay (alpha ~ 0.98) keeps the transitions
+    far from zero; unaligned starts, initial states, checkpoints that fall on
+    and between segment boundaries.  Against the oracle, and against the same
+    call without splitting."""
+    U.say(f"prefill segment scan, slow decay, d={d}")
+    lens = [1000, 300, 2100, 530]
+    starts = [0, 40, 96, 7]
+    wl = make_workload(2, lengths=lens, H=2, d=d, mu_g=4.0)
+    r = run_prefill(dev, wl, chunk=64, start_pos=starts, ckpt_interval=128, segment_len=256)
+    ref = oracle_run(oracle64, wl, r["init"], r["has"], start_pos=np.array(starts, np.int32),
+                     ckpt_interval=128)
+    assert r["ckpt_pos"] == list(ref["ckpt_pos"]) == r["ckpt_plan"]
+    U.assert_close("o", r["o"].numpy(), ref["o"])
+    U.assert_close("state", r["final"].numpy(), ref["final"])
+    U.assert_close("ckpt", r["ckpt"].numpy(), ref["ckpt"])
+    whole = run_prefill(dev, wl, chunk=64, start_pos=starts, ckpt_interval=128, segment_len=-1)
+    U.assert_close("o(split vs whole)", r["o"].numpy(), whole["o"].numpy())
+    U.assert_close("state(split vs whole)", r["final"].numpy(), whole["final"].numpy())
+
+
+def test_prefill_segment_scan_tiny_fp32(dev, oracle64):
+    """The tiny fp32 workload (chunk 16) split into 16-token segments."""
+    U.say("prefill segment scan, tiny fp32")
+    wl = make_workload(0, mu_g=3.0)
+    r = run_prefill(dev, wl, chunk=16, out_dtype=torch.float32, segment_len=16)
+    ref = oracle_run(oracle64, wl, r["init"], r["has"])
+    U.assert_close("o", r["o"].numpy(), ref["o"], rel=2e-4, mx=1e-3)
+    U.assert_close("state", r["final"].numpy(), ref["final"], rel=2e-4, mx=1e-3)
+
+
+def test_prefill_long_1m_segments(dev, oracle64):
+    """B=1, T=1,048,576, H=16, d=128, chunk 64, checkpoints every 32,768 (31
+    interior + final), run as 32 parallel segments.  The oracle resumes from
+    the GPU's own checkpoints on two segments (the second and the last) and
+    must reproduce that segment's outputs and its end state; every output is
+    finite and the checkpoint positions are exact."""
+    U.say("prefill long T=1,048,576 (segments resumed by the oracle)")
+    T, I = 1048576, 32768
+    wl = make_workload(3, device=dev)
+    r = run_prefill(dev, wl, chunk=64, ckpt_interval=I)
+    assert r["ckpt_pos"] == [I * j for j in range(1, 32)] == r["ckpt_plan"]
+    assert torch.isfinite(r["o"]).all()
+    ends = list(r["ckpt"].numpy()) + [r["final"][0].numpy()]
+    for j in (1, 31):
+        lo, hi = I * j, I * (j + 1)
+        q, k, v, g, b = (t[lo:hi].cpu() for t in (wl.q, wl.k, wl.v, wl.g, wl.beta))
+        init = r["ckpt"][j - 1].double().numpy()[None]
+        ref = oracle64.kda_varlen(q, k, v, g, b, torch.tensor([0, I], dtype=torch.int32), init=init,
+                                  has_init=np.ones(1, np.int32), start_pos=np.array([lo], np.int32))
+        U.assert_close(f"o(segment {j})", r["o"][lo:hi].numpy(), ref["o"])
+        U.assert_close(f"end state(segment {j})", ends[j], ref["final"][0])
