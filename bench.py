@@ -41,11 +41,16 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", default="decode", choices=["decode", "prefill"])
+    ap.add_argument("--workload", default="decode", choices=["decode", "prefill", "long"])
     ap.add_argument("--pools", type=int, default=4, help="rotating state pools (MALL defeat)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle time budget")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--pmc-pass", action="store_true",
+                    help="run only the launches a rocprofv3 --pmc pass measures: a 256 MiB copy "
+                         "(calibration), 8 decode steps, 2 varlen prefills")
+    ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn the counter CSVs of two --pmc-pass runs into profiles/traffic.json")
     return ap.parse_args()
 
 
@@ -69,6 +74,84 @@ def traffic_for(kernel_key: str, src_name: str, per_launch_units: float):
     if ent.get("units_per_launch") != per_launch_units:
         return None
     return float(ent["hbm_bytes_per_launch"])
+
+
+COPY_BYTES = 256 * 2 ** 20
+
+
+def pmc_pass(torch, K, make_workload):
+    """The launches the counter passes read: a plain device copy of a known
+    size (the calibration), decode steps over rotating pools, varlen prefills."""
+    dev = torch.device("cuda:0")
+    a = torch.ones(COPY_BYTES // 4, device=dev)
+    b = torch.empty_like(a)
+    for _ in range(4):
+        b.copy_(a)
+    del a, b
+    wl = make_workload(1)
+    N, H, D, P = 128, 16, 128, 4
+    q, k, v, g, bt = (t.to(dev) for t in (wl.q, wl.k, wl.v, wl.g, wl.beta))
+    pool = torch.empty(P * N, H, D, D, device=dev)
+    for i in range(P):
+        pool[i * N:(i + 1) * N] = wl.init_states.to(dev)
+    o = torch.empty(N, H, D, dtype=torch.bfloat16, device=dev)
+    for i in range(8):
+        s_ = torch.arange((i % P) * N, (i % P + 1) * N, dtype=torch.int32, device=dev)
+        K.kda_decode(q, k, v, g, bt, o, pool, s_, s_)
+    del pool
+    bench_prefill_varlen(torch, K, make_workload, dev, iters=1)
+    torch.cuda.synchronize()
+
+
+def varlen_tokens():
+    from hybrid_recurrent_serving_amd.inputs import make_workload
+    return int(make_workload(2).cu_seqlens[-1])
+
+
+def ingest_pmc(fetch_csv, write_csv):
+    """Per-launch HBM bytes of the decode and prefill kernels from FETCH_SIZE
+    and WRITE_SIZE (KiB per dispatch), each scaled by the factor that makes
+    the calibration copy read and write exactly COPY_BYTES."""
+    import csv
+    out = {}
+    rows = {}
+    for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows[name] = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == name]
+
+    def sel(name, pred):
+        return [float(r["Counter_Value"]) * 1024 for r in rows[name] if pred(r)]
+
+    def is_copy(r):
+        return r["Kernel_Name"].startswith("__amd_rocclr_copyBuffer")
+
+    cw = [x for x in sel("WRITE_SIZE", is_copy) if abs(x - COPY_BYTES) < 0.25 * COPY_BYTES]
+    cf = sel("FETCH_SIZE", is_copy)
+    cf = sorted(cf)[-len(cw):] if cw else []
+    if not cw or not cf:
+        raise SystemExit("calibration copy not found in the counter files")
+    f_scale = COPY_BYTES / (sum(cf) / len(cf))
+    w_scale = COPY_BYTES / (sum(cw) / len(cw))
+    for key, pred, src, units, pick in (
+            ("decode_step_kernel_d128_bf16", lambda r: "step_kernel<128" in r["Kernel_Name"], "kda_step.hip",
+             128 * 16, "all"),
+            ("prefill_kernel_d128_bf16", lambda r: "prefill_kernel<128" in r["Kernel_Name"], "kda_prefill.hip",
+             varlen_tokens(), "max")):
+        f = sel("FETCH_SIZE", pred)
+        w = sel("WRITE_SIZE", pred)
+        if not f or not w:
+            continue
+        if pick == "max":
+            f, w = [max(f)], [max(w)]
+        fb = sum(f) / len(f) * f_scale
+        wb = sum(w) / len(w) * w_scale
+        out[key] = {"hbm_bytes_per_launch": round(fb + wb), "fetch_bytes": round(fb), "write_bytes": round(wb),
+                    "source_sha256_16": kernel_source_hash(src), "units_per_launch": units,
+                    "dispatches": len(f)}
+    out["calibration"] = {"copy_bytes": COPY_BYTES, "fetch_scale": round(f_scale, 4),
+                          "write_scale": round(w_scale, 4),
+                          "note": "FETCH_SIZE / WRITE_SIZE of a plain device copy of copy_bytes, "
+                                  "scaled to read and write exactly copy_bytes"}
+    return out
 
 
 def cpu_info():
@@ -178,6 +261,7 @@ def bench_decode(args, torch, K, make_workload):
         pf = bench_prefill_varlen(torch, K, make_workload, dev, iters=10)
         secondary["prefill_varlen"] = {k_: pf[k_] for k_ in ("workload", "tokens", "ms", "tokens_per_s",
                                                              "alg_mfma_frac", "alg_hbm_frac")}
+        secondary["prefill_long_1m"] = bench_prefill_long(torch, K, make_workload, dev)
 
     cpu = None
     if not args.no_cpu:
@@ -270,6 +354,47 @@ def bench_prefill_varlen(torch, K, make_workload, dev, iters=20, wl=None):
             "wl": wl}
 
 
+def bench_prefill_long(torch, K, make_workload, dev, iters=3):
+    """B=1, T=1,048,576, H=16, d=128, chunk 64, checkpoints every 32,768 (31
+    interior + final), run as 32 segments by the segment scan.  Inputs are
+    drawn on the GPU (17 GB bf16)."""
+    wl = make_workload(3, device=dev)
+    T, H, D, I = wl.q.shape[0], 16, 128, wl.ckpt_interval
+    cu = wl.cu_seqlens.to(dev)
+    ck_cu, _ = K.kda_ckpt_plan(wl.cu_seqlens.cpu().numpy(), I, 64)
+    n_ck = ck_cu[-1]
+    pool = torch.zeros(1 + n_ck, H, D, D, device=dev)
+    src = torch.tensor([-1], dtype=torch.int32, device=dev)
+    dst = torch.tensor([0], dtype=torch.int32, device=dev)
+    ck_cu_d = torch.tensor(ck_cu, dtype=torch.int32, device=dev)
+    ck_slot = torch.arange(1, 1 + n_ck, dtype=torch.int32, device=dev)
+    o = torch.empty(T, H, D, dtype=torch.bfloat16, device=dev)
+    kw = dict(chunk=64, ckpt_interval=I, ckpt_cu=ck_cu_d, ckpt_slot=ck_slot)
+    nws = K.kda_prefill_workspace_bytes(wl.q, wl.k, wl.v, wl.g, wl.beta, o, cu, pool, src, dst, **kw)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+
+    def run():
+        K.kda_prefill_varlen(wl.q, wl.k, wl.v, wl.g, wl.beta, o, cu, pool, src, dst, workspace=ws, **kw)
+
+    run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    tps = T / (ms * 1e-3)
+    del wl, o, ws, pool
+    torch.cuda.empty_cache()
+    return {"workload": "long prefill: B=1, T=1048576, H=16, d=128, chunk 64, ckpt every 32768, "
+                        "32 segments", "tokens": T, "ms": round(ms, 3), "tokens_per_s": round(tps, 1),
+            "alg_mfma_frac": round(tps * PREFILL_FLOPS_PER_TOKEN / (MFMA_BF16_PEAK_TFLOPS * 1e12), 4),
+            "alg_hbm_frac": round(tps * PREFILL_BYTES_PER_TOKEN / (HBM_PEAK_GBS * 1e9), 4),
+            "workspace_bytes": nws}
+
+
 def bench_prefill(args, torch, K, make_workload):
     dev = torch.device("cuda:0")
     wl = make_workload(2)
@@ -289,9 +414,58 @@ def bench_prefill(args, torch, K, make_workload):
         cpu = cpu_prefill(args, wl)
     cfg = {"workload": pf["workload"], "tokens": T, "H": 16, "d": 128, "chunk": 64,
            "initial_states": "even-indexed sequences"}
+    secondary = {}
+    if not args.no_secondary:
+        secondary["prefill_long_1m"] = bench_prefill_long(torch, K, make_workload, torch.device("cuda:0"))
+    return {"metric": METRIC, "value": pf["tokens_per_s"], "unit": "tokens/s", "ms_per_step": pf["ms"],
+            "dtype": "bf16-mfma/f32-acc", "config": cfg, "roofline": roof, "cpu_baseline": cpu,
+            "secondary": secondary}
+
+
+def bench_long(args, torch, K, make_workload):
+    dev = torch.device("cuda:0")
+    pf = bench_prefill_long(torch, K, make_workload, dev, iters=max(1, min(args.steps, 10)))
+    T = pf["tokens"]
+    achieved = T * PREFILL_BYTES_PER_TOKEN / (pf["ms"] * 1e-3) / 1e9
+    roof = {"kernel": "prefill_kernel<128,bf16,bf16> (kda_prefill_varlen, segment scan: pass A + pass B)",
+            "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "alg_bytes_per_launch": T * PREFILL_BYTES_PER_TOKEN, "avg_launch_us": round(pf["ms"] * 1e3, 2),
+            "mfma": {"alg_flops_per_launch": T * PREFILL_FLOPS_PER_TOKEN,
+                     "achieved_tflops": round(T * PREFILL_FLOPS_PER_TOKEN / (pf["ms"] * 1e-3) / 1e12, 1),
+                     "peak_tflops": MFMA_BF16_PEAK_TFLOPS, "frac": pf["alg_mfma_frac"]}}
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_long(args, make_workload)
+    cfg = {"workload": pf["workload"], "tokens": T, "H": 16, "d": 128, "chunk": 64,
+           "ckpt_interval": 32768, "segments": 32}
     return {"metric": METRIC, "value": pf["tokens_per_s"], "unit": "tokens/s", "ms_per_step": pf["ms"],
             "dtype": "bf16-mfma/f32-acc", "config": cfg, "roofline": roof, "cpu_baseline": cpu,
             "secondary": {}}
+
+
+def cpu_long(args, make_workload):
+    """Oracle on the first segment (32,768 tokens, 16 heads) of the long
+    workload."""
+    import numpy as np
+    import torch
+    import oracle
+    orc = oracle.load("f64")
+    threads = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    orc.set_threads(threads)
+    wl = make_workload(3, device=torch.device("cuda:0"))
+    I = 32768
+    q, k, v, g, b = (t[:I].float().cpu().numpy() for t in (wl.q, wl.k, wl.v, wl.g, wl.beta))
+    del wl
+    torch.cuda.empty_cache()
+    # all 16 heads of the first segment in one call (parallel over heads)
+    cu = torch.tensor([0, I], dtype=torch.int32)
+    t0 = time.perf_counter()
+    orc.kda_varlen(q, k, v, g, b, cu)
+    dt = time.perf_counter() - t0
+    return {"value": round(I / dt, 1), "unit": "tokens/s", "cores": orc.threads(),
+            "kind": "oracle", "cpu": cpu_info(),
+            "sample": f"first 32768 tokens (one segment), all 16 heads, fp64 oracle, {dt:.1f} s"}
 
 
 def cpu_prefill(args, wl):
@@ -356,6 +530,11 @@ def cpu_decode(args, wl, state_bytes):
 
 def main():
     args = parse()
+    if args.ingest_pmc:
+        data = ingest_pmc(*args.ingest_pmc)
+        TRAFFIC_FILE.write_text(json.dumps(data, indent=1) + "\n")
+        print(json.dumps(data))
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}))
@@ -367,8 +546,14 @@ def main():
     from hybrid_recurrent_serving_amd import kda as K
     from hybrid_recurrent_serving_amd.inputs import make_workload
     K.load_library()
+    if args.pmc_pass:
+        pmc_pass(torch, K, make_workload)
+        print(json.dumps({"pmc_pass": "done"}))
+        return
     if args.workload == "decode":
         res = bench_decode(args, torch, K, make_workload)
+    elif args.workload == "long":
+        res = bench_long(args, torch, K, make_workload)
     else:
         res = bench_prefill(args, torch, K, make_workload)
     line = {"metric": res["metric"], "value": res["value"], "unit": res["unit"], "n_gpus": 1,
