@@ -186,12 +186,15 @@ def bench_decode(args, torch, K, make_workload):
     cu = wl.cu_seqlens.to(dev)
     y = torch.empty_like(x)
 
+    # argument structs checked once; the timed loop only enqueues
+    conv_call = K.prepare_conv_short(x, cw, cu, cpool, cslots, cslots, y=y)
+    dec_calls = [K.prepare_decode(q, k, v, g, b, o, pool, s_, s_) for s_ in slot_sets]
+
     def step(i, ev=None):
-        K.kda_conv_short(x, cw, cu, cpool, cslots, cslots, y=y)
-        s = slot_sets[i % P]
+        conv_call()
         if ev is not None:
             ev[0].record()
-        K.kda_decode(q, k, v, g, b, o, pool, s, s)
+        dec_calls[i % P]()
         if ev is not None:
             ev[1].record()
 

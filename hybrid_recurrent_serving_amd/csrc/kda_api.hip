@@ -158,7 +158,8 @@ int kda_conv_short(const kda_conv_args* a, kda_stream_t stream_) {
   if ((b.x_stride * eb) % 16 || (b.y_stride * eb) % 16 || !aligned16(b.x) || !aligned16(b.y) ||
       !aligned16(b.conv_pool) || !aligned16(b.weight))
     return fail(KDA_ERR_ALIGN, "conv: x, y, weight or conv_pool not 16-byte aligned");
-  if (b.T_tot / 64 + b.n_seq > 0x7fffffffLL) return fail(KDA_ERR_SHAPE, "conv: too many tokens");
+  if (b.T_tot / 16 + b.n_seq + 1 > 0x7fffffffLL) return fail(KDA_ERR_SHAPE, "conv: too many tokens");
+  if (b.act != 0 && b.act != 1) return fail(KDA_ERR_ARG, "conv: act = %d (0 none, 1 SiLU)", b.act);
   if (check_enabled()) {
     int st = check_cu(b.cu_seqlens, b.n_seq, b.T_tot, stream);
     if (st) return st;

@@ -26,12 +26,20 @@
 
 namespace kda {
 
-constexpr int CONV_TT = 64;      // tokens per body item
+constexpr int CONV_TT = 16;      // tokens per body item
 constexpr int CONV_THREADS = 256;
 
 template <typename T> struct Vec16;
 template <> struct Vec16<bf16_t> {
   static constexpr int N = 8;
+  __device__ static __forceinline__ void cvt(const uint4& t, float (&x)[8]) {
+    const uint32_t w[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = __uint_as_float(w[i] << 16);
+      x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
   __device__ static __forceinline__ void ld(const bf16_t* p, float (&x)[8]) {
     uint4 t = *reinterpret_cast<const uint4*>(p);
     uint32_t w[4] = {t.x, t.y, t.z, t.w};
@@ -52,6 +60,10 @@ template <> struct Vec16<bf16_t> {
 };
 template <> struct Vec16<float> {
   static constexpr int N = 4;
+  __device__ static __forceinline__ void cvt(const uint4& t, float (&x)[4]) {
+    x[0] = __uint_as_float(t.x); x[1] = __uint_as_float(t.y);
+    x[2] = __uint_as_float(t.z); x[3] = __uint_as_float(t.w);
+  }
   __device__ static __forceinline__ void ld(const float* p, float (&x)[4]) { io<float>::ld4(p, x); }
   __device__ static __forceinline__ void st(float* p, const float (&x)[4]) { io<float>::st4(p, x); }
 };
@@ -92,7 +104,9 @@ __global__ void __launch_bounds__(CONV_THREADS) conv_kernel(const ConvParams p) 
   constexpr int HIST = W - 1;
   const int item = blockIdx.x;
   const int64_t c0 = (static_cast<int64_t>(blockIdx.y) * CONV_THREADS + threadIdx.x) * V;
-  if (c0 >= p.C) return;
+  // threads past the last channel stay for the workgroup barrier of body items
+  const bool active = c0 < p.C;
+  if (!active && item < p.n_seq) return;
   const T* xb = static_cast<const T*>(p.x);
   T* yb = static_cast<T*>(p.y);
 
@@ -101,7 +115,7 @@ __global__ void __launch_bounds__(CONV_THREADS) conv_kernel(const ConvParams p) 
   float wt[W][V];
   {
     float flat[W * V];
-    ld_blocks<T, W>(static_cast<const T*>(p.w) + c0 * W, flat);
+    ld_blocks<T, W>(static_cast<const T*>(p.w) + (active ? c0 : 0) * W, flat);
 #pragma unroll
     for (int i = 0; i < V; ++i)
 #pragma unroll
@@ -109,7 +123,7 @@ __global__ void __launch_bounds__(CONV_THREADS) conv_kernel(const ConvParams p) 
   }
   float bias[V];
 #pragma unroll
-  for (int i = 0; i < V; ++i) bias[i] = p.bias ? io<T>::ld(static_cast<const T*>(p.bias) + c0 + i) : 0.f;
+  for (int i = 0; i < V; ++i) bias[i] = p.bias ? io<T>::ld(static_cast<const T*>(p.bias) + (active ? c0 : 0) + i) : 0.f;
 
   if (item < p.n_seq) {
     // ---------------- head item: tokens that need the history + new state
@@ -193,6 +207,10 @@ __global__ void __launch_bounds__(CONV_THREADS) conv_kernel(const ConvParams p) 
   }
 
   // ---------------- body item: packed tokens [t0, t1)
+  // Tokens at position >= W-1 inside their sequence (the others belong to the
+  // head item).  The tile's rows and the W-1 rows before it are loaded at
+  // once (independent 16-byte loads), then every output is formed from
+  // registers.
   const int64_t t0 = static_cast<int64_t>(item - p.n_seq) * CONV_TT;
   if (t0 >= p.T_tot) return;
   const int64_t t1 = t0 + CONV_TT < p.T_tot ? t0 + CONV_TT : p.T_tot;
@@ -202,44 +220,49 @@ __global__ void __launch_bounds__(CONV_THREADS) conv_kernel(const ConvParams p) 
     const int mid = (lo + hi) >> 1;
     if (p.cu[mid] <= t0) lo = mid; else hi = mid;
   }
-  int s = lo;
-  int64_t bos = p.cu[s], eos = p.cu[s + 1];
-  float win[HIST][V];  // rows t-HIST .. t-1
-  bool have_win = false;
-  for (int64_t t = t0; t < t1; ++t) {
-    while (t >= eos && s < p.n_seq - 1) {
-      ++s;
-      bos = p.cu[s];
-      eos = p.cu[s + 1];
-      have_win = false;
+  // the boundaries cu[lo .. lo + CONV_THREADS) in LDS, then the start of
+  // each tile token's sequence (or "skip" when the token is outside every
+  // sequence or among its sequence's first W-1 tokens)
+  __shared__ int32_t cus[CONV_THREADS];
+  __shared__ int32_t tok_ok[CONV_TT];
+  if (lo + static_cast<int>(threadIdx.x) <= p.n_seq) cus[threadIdx.x] = p.cu[lo + threadIdx.x];
+  __syncthreads();
+  if (threadIdx.x < CONV_TT) {
+    const int64_t t = t0 + threadIdx.x;
+    auto cu_at = [&](int i) -> int64_t { return i - lo < CONV_THREADS ? cus[i - lo] : p.cu[i]; };
+    int a = lo, b = p.n_seq;     // cu[a] <= t; the answer lies in [a, b)
+    while (b - a > 1) {
+      const int mid = (a + b) >> 1;
+      if (cu_at(mid) <= t) a = mid; else b = mid;
     }
-    if (t < bos || t >= eos || t - bos < HIST || t < HIST) {
-      have_win = false;
-      continue;
-    }
-    if (!have_win) {
+    const int64_t bos = cu_at(a), eos = cu_at(a + 1);
+    tok_ok[threadIdx.x] = (t < t1 && t >= bos && t < eos && t - bos >= HIST) ? 1 : 0;
+  }
+  __syncthreads();
+  if (!active) return;
+  uint4 raw[HIST + CONV_TT];
 #pragma unroll
-      for (int j = 0; j < HIST; ++j) Vec16<T>::ld(xb + (t - HIST + j) * p.x_stride + c0, win[j]);
-      have_win = true;
-    }
-    float cur[V];
-    Vec16<T>::ld(xb + t * p.x_stride + c0, cur);
+  for (int j = 0; j < HIST + CONV_TT; ++j) {
+    const int64_t row = t0 - HIST + j;
+    raw[j] = make_uint4(0, 0, 0, 0);
+    if (row >= 0 && row < t1) raw[j] = *reinterpret_cast<const uint4*>(xb + row * p.x_stride + c0);
+  }
+#pragma unroll
+  for (int i = 0; i < CONV_TT; ++i) {
+    if (!tok_ok[i]) continue;
     float out[V];
 #pragma unroll
-    for (int i = 0; i < V; ++i) {
-      float acc = bias[i];
+    for (int v = 0; v < V; ++v) out[v] = bias[v];
 #pragma unroll
-      for (int j = 0; j < HIST; ++j) acc = fmaf(wt[j][i], win[j][i], acc);
-      acc = fmaf(wt[HIST][i], cur[i], acc);
-      out[i] = conv_finish(acc, p.act);
+    for (int j = 0; j < W; ++j) {
+      float xr[V];
+      Vec16<T>::cvt(raw[i + j], xr);
+#pragma unroll
+      for (int v = 0; v < V; ++v) out[v] = fmaf(wt[j][v], xr[v], out[v]);
     }
-    Vec16<T>::st(yb + t * p.y_stride + c0, out);
 #pragma unroll
-    for (int j = 0; j + 1 < HIST; ++j)
-#pragma unroll
-      for (int i = 0; i < V; ++i) win[j][i] = win[j + 1][i];
-#pragma unroll
-    for (int i = 0; i < V; ++i) win[HIST - 1][i] = cur[i];
+    for (int v = 0; v < V; ++v) out[v] = conv_finish(out[v], p.act);
+    Vec16<T>::st(yb + (t0 + i) * p.y_stride + c0, out);
   }
 }
 

@@ -214,13 +214,7 @@ def kda_args_sizeof(which: int) -> int:
     return load_library().kda_args_sizeof(which)
 
 
-def kda_conv_short(x, weight, cu_seqlens, conv_pool, src_slot, dst_slot, *, y=None, bias=None,
-                   act: int = 0, advance_len=None, stream=None):
-    """Short causal conv.  x [T, C]; weight [C, W]; conv_pool [S, C, W-1].
-    Returns y (allocated by torch when not given)."""
-    import torch
-    if y is None:
-        y = torch.empty_like(x)
+def _conv_args(x, weight, cu_seqlens, conv_pool, src_slot, dst_slot, y, bias, act, advance_len):
     _expect(x.dim() == 2 and y.shape == x.shape, "x and y must be [T, C]")
     T, C = x.shape
     _expect(weight.dim() == 2 and weight.shape[0] == C, "weight must be [C, W]")
@@ -244,8 +238,48 @@ def kda_conv_short(x, weight, cu_seqlens, conv_pool, src_slot, dst_slot, *, y=No
     a.T_tot, a.n_slots = x.shape[0], conv_pool.shape[0]
     a.n_seq, a.C, a.W = cu_seqlens.numel() - 1, x.shape[1], weight.shape[1]
     a.dtype, a.act = _dtype_code(x), act
+    return a
+
+
+def kda_conv_short(x, weight, cu_seqlens, conv_pool, src_slot, dst_slot, *, y=None, bias=None,
+                   act: int = 0, advance_len=None, stream=None):
+    """Short causal conv.  x [T, C]; weight [C, W]; conv_pool [S, C, W-1].
+    Returns y (allocated by torch when not given)."""
+    import torch
+    if y is None:
+        y = torch.empty_like(x)
+    a = _conv_args(x, weight, cu_seqlens, conv_pool, src_slot, dst_slot, y, bias, act, advance_len)
     _check(load_library().kda_conv_short(ctypes.byref(a), _stream(stream)))
     return y
+
+
+class Prepared:
+    """An argument struct checked once and bound to its entry point, for
+    loops that launch the same call on the same buffers: calling it enqueues
+    the call again (only the status is checked).  It holds references to the
+    tensors whose addresses it carries."""
+
+    __slots__ = ("_fn", "_args", "_keep")
+
+    def __init__(self, fn, args, keep):
+        self._fn, self._args, self._keep = fn, args, keep
+
+    def __call__(self, stream=None):
+        _check(self._fn(ctypes.byref(self._args), _stream(stream)))
+
+
+def prepare_decode(q, k, v, g, beta, o, state_pool, src_slot, dst_slot, *, scale=1.0) -> Prepared:
+    """kda_decode with fixed buffers, as a Prepared call."""
+    a = _decode_args(q, k, v, g, beta, o, state_pool, src_slot, dst_slot, scale)
+    return Prepared(load_library().kda_decode, a, (q, k, v, g, beta, o, state_pool, src_slot, dst_slot))
+
+
+def prepare_conv_short(x, weight, cu_seqlens, conv_pool, src_slot, dst_slot, *, y, bias=None, act: int = 0,
+                       advance_len=None) -> Prepared:
+    """kda_conv_short with fixed buffers, as a Prepared call."""
+    a = _conv_args(x, weight, cu_seqlens, conv_pool, src_slot, dst_slot, y, bias, act, advance_len)
+    return Prepared(load_library().kda_conv_short, a,
+                    (x, weight, cu_seqlens, conv_pool, src_slot, dst_slot, y, bias, advance_len))
 
 
 def kda_ckpt_plan(cu_seqlens, interval: int, chunk: int, start_pos=None):
@@ -345,8 +379,7 @@ def kda_prefill_varlen(q, k, v, g, beta, o, cu_seqlens, state_pool, src_slot, ds
     return o
 
 
-def kda_decode(q, k, v, g, beta, o, state_pool, src_slot, dst_slot, *, scale=1.0, stream=None):
-    """One token per sequence.  q, k, v, g [N, H, d]; beta [N, H]; o [N, H, d]."""
+def _decode_args(q, k, v, g, beta, o, state_pool, src_slot, dst_slot, scale):
     import torch
     _expect(q.dim() == 3 and v.dim() == 3 and beta.dim() == 2, "q/k/v/g [N, H, d], beta [N, H]")
     N, H, dk = q.shape
@@ -370,6 +403,12 @@ def kda_decode(q, k, v, g, beta, o, state_pool, src_slot, dst_slot, *, scale=1.0
     a.n_slots = state_pool.shape[0]
     a.n_seq, a.H, a.d_k, a.d_v = q.shape[0], q.shape[1], q.shape[2], v.shape[2]
     a.in_dtype, a.out_dtype, a.scale = _dtype_code(q), _dtype_code(o), scale
+    return a
+
+
+def kda_decode(q, k, v, g, beta, o, state_pool, src_slot, dst_slot, *, scale=1.0, stream=None):
+    """One token per sequence.  q, k, v, g [N, H, d]; beta [N, H]; o [N, H, d]."""
+    a = _decode_args(q, k, v, g, beta, o, state_pool, src_slot, dst_slot, scale)
     _check(load_library().kda_decode(ctypes.byref(a), _stream(stream)))
     return o
 

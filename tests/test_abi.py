@@ -116,6 +116,7 @@ def test_conv_validation(lib):
     assert _call(lib, "kda_conv_short", _conv_args(C=12)) == 2     # not a multiple of 8 (bf16)
     assert _call(lib, "kda_conv_short", _conv_args(dtype=3)) == 3
     assert _call(lib, "kda_conv_short", _conv_args(x_stride=65)) == 4
+    assert _call(lib, "kda_conv_short", _conv_args(act=2)) == 8
     assert _call(lib, "kda_conv_short", _conv_args(n_seq=0)) == 0
 
 
