@@ -9,8 +9,11 @@
 // [rg*RPL, rg*RPL + RPL) x columns [4cg, 4cg + 4) of the slice, loaded and
 // stored as 16-byte vectors, so one load instruction covers RG rows x
 // (COLS * 4) contiguous bytes.  The reductions over key channels
-// (S^T k and S^T q) only cross lanes of the same wave (shuffles), so the
-// waves of a head never synchronise.
+// (S^T k and S^T q) only cross lanes of the same wave (shuffles).  The
+// token inputs (k, q, v, exp(g), beta for all tokens of the call) are staged
+// in LDS by one round of loads that overlaps the state load, and the outputs
+// are staged there and stored after the last token, so the token loop itself
+// touches no global memory except the state commit.
 //
 // Recurrence (per token, decay first, correction against the decayed state,
 // output from the updated state):
@@ -36,10 +39,26 @@ struct StepLayout {
   static_assert(RPL >= 1 && RPL * RG == D, "layout");
 };
 
-template <int D, typename Tin, typename Tout>
+constexpr int STEP_TMAX = 16;   // most tokens per sequence in one call
+
+// STAGED: token inputs and outputs go through LDS (several tokens per call);
+// without it (one token, the decode step) every lane loads its own rows and
+// stores its own outputs directly.
+template <int D, typename Tin, typename Tout, bool STAGED>
 __global__ void __launch_bounds__(64 * StepLayout<D>::WPH)
 step_kernel(const StepParams p) {
   using L = StepLayout<D>;
+  constexpr int NTH = 64 * L::WPH;
+  // per-token inputs of this (sequence, head), staged once: alpha = exp(g),
+  // k, q (fp32, [token][row]), v ([token][col]), beta; outputs staged the
+  // same way and stored after the last token
+  constexpr int TS = STAGED ? STEP_TMAX : 1;
+  __shared__ __align__(16) float s_a[TS][D];
+  __shared__ __align__(16) float s_k[TS][D];
+  __shared__ __align__(16) float s_q[TS][D];
+  __shared__ __align__(16) float s_v[TS][D];
+  __shared__ __align__(16) float s_o[TS][D];
+  __shared__ float s_b[TS];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int64_t sh = blockIdx.x;
@@ -69,6 +88,7 @@ step_kernel(const StepParams p) {
   const bool do_store = valid && has_dst;
   const int n_tok = p.o ? p.T_spec : (valid ? Lc : 0);
 
+  // state slice (in flight while the token inputs are staged)
   float S[L::RPL][4];
   if (has_src) {
     const float* sp = p.pool + ((static_cast<int64_t>(src) * p.H + h) * D + row0) * D + col;
@@ -78,44 +98,73 @@ step_kernel(const StepParams p) {
 #pragma unroll
     for (int i = 0; i < L::RPL; ++i) S[i][0] = S[i][1] = S[i][2] = S[i][3] = 0.f;
   }
-  float* dp = has_dst ? p.pool + ((static_cast<int64_t>(dst) * p.H + h) * D + row0) * D + col : nullptr;
-  if (do_store && Lc == 0) {
-#pragma unroll
-    for (int i = 0; i < L::RPL; ++i) io<float>::st4(dp + static_cast<int64_t>(i) * D, S[i]);
-  }
 
   const Tin* qb = static_cast<const Tin*>(p.q);
   const Tin* kb = static_cast<const Tin*>(p.k);
   const Tin* vb = static_cast<const Tin*>(p.v);
   const Tin* gb = static_cast<const Tin*>(p.g);
   const Tin* bb = static_cast<const Tin*>(p.beta);
+  if constexpr (STAGED) {
+    // 4 consecutive elements per thread and pass (one 8- or 16-byte load per tensor)
+    for (int e = 4 * static_cast<int>(threadIdx.x); e < n_tok * D; e += 4 * NTH) {
+      const int j = e / D, c = e % D;
+      const int64_t off = (static_cast<int64_t>(s) * p.T_spec + j);
+      const int64_t hc = static_cast<int64_t>(h) * D + c;
+      float k4[4], q4[4], v4[4], g4[4];
+      io<Tin>::ld4(kb + off * p.k_stride + hc, k4);
+      io<Tin>::ld4(qb + off * p.q_stride + hc, q4);
+      io<Tin>::ld4(vb + off * p.v_stride + hc, v4);
+      io<Tin>::ld4(gb + off * p.g_stride + hc, g4);
+      *reinterpret_cast<float4*>(&s_k[j][c]) = make_float4(k4[0], k4[1], k4[2], k4[3]);
+      *reinterpret_cast<float4*>(&s_q[j][c]) = make_float4(q4[0], q4[1], q4[2], q4[3]);
+      *reinterpret_cast<float4*>(&s_v[j][c]) = make_float4(v4[0], v4[1], v4[2], v4[3]);
+      *reinterpret_cast<float4*>(&s_a[j][c]) = make_float4(expf(g4[0]), expf(g4[1]), expf(g4[2]), expf(g4[3]));
+      if (c == 0) s_b[j] = io<Tin>::ld(bb + off * p.beta_stride + h);
+    }
+    __syncthreads();
+  }
+
+  float* dp = has_dst ? p.pool + ((static_cast<int64_t>(dst) * p.H + h) * D + row0) * D + col : nullptr;
+  if (do_store && Lc == 0) {
+#pragma unroll
+    for (int i = 0; i < L::RPL; ++i) io<float>::st4(dp + static_cast<int64_t>(i) * D, S[i]);
+  }
 
   for (int j = 0; j < n_tok; ++j) {
+    float kr[L::RPL], qr[L::RPL], ar[L::RPL], vc[4];
+    float beta;
     const int64_t tok = static_cast<int64_t>(s) * p.T_spec + j;
-    float kr[L::RPL], qr[L::RPL], gr[L::RPL], vc[4];
-    if constexpr (L::RPL >= 4) {
-      ld_vec<Tin, L::RPL>(kb + tok * p.k_stride + static_cast<int64_t>(h) * D + row0, kr);
-      ld_vec<Tin, L::RPL>(qb + tok * p.q_stride + static_cast<int64_t>(h) * D + row0, qr);
-      ld_vec<Tin, L::RPL>(gb + tok * p.g_stride + static_cast<int64_t>(h) * D + row0, gr);
-    } else {
+    if constexpr (STAGED) {
 #pragma unroll
-      for (int i = 0; i < L::RPL; ++i) {
-        kr[i] = io<Tin>::ld(kb + tok * p.k_stride + static_cast<int64_t>(h) * D + row0 + i);
-        qr[i] = io<Tin>::ld(qb + tok * p.q_stride + static_cast<int64_t>(h) * D + row0 + i);
-        gr[i] = io<Tin>::ld(gb + tok * p.g_stride + static_cast<int64_t>(h) * D + row0 + i);
+      for (int i = 0; i < L::RPL; i += 4) {
+        const float4 k4 = *reinterpret_cast<const float4*>(&s_k[j][row0 + i]);
+        const float4 q4 = *reinterpret_cast<const float4*>(&s_q[j][row0 + i]);
+        const float4 a4 = *reinterpret_cast<const float4*>(&s_a[j][row0 + i]);
+        kr[i] = k4.x; kr[i + 1] = k4.y; kr[i + 2] = k4.z; kr[i + 3] = k4.w;
+        qr[i] = q4.x; qr[i + 1] = q4.y; qr[i + 2] = q4.z; qr[i + 3] = q4.w;
+        ar[i] = a4.x; ar[i + 1] = a4.y; ar[i + 2] = a4.z; ar[i + 3] = a4.w;
       }
+      const float4 v4 = *reinterpret_cast<const float4*>(&s_v[j][col]);
+      vc[0] = v4.x; vc[1] = v4.y; vc[2] = v4.z; vc[3] = v4.w;
+      beta = s_b[j];
+    } else {
+      const int64_t hr = static_cast<int64_t>(h) * D + row0;
+      ld_vec<Tin, L::RPL>(kb + tok * p.k_stride + hr, kr);
+      ld_vec<Tin, L::RPL>(qb + tok * p.q_stride + hr, qr);
+      ld_vec<Tin, L::RPL>(gb + tok * p.g_stride + hr, ar);
+#pragma unroll
+      for (int i = 0; i < L::RPL; ++i) ar[i] = expf(ar[i]);
+      io<Tin>::ld4(vb + tok * p.v_stride + static_cast<int64_t>(h) * D + col, vc);
+      beta = io<Tin>::ld(bb + tok * p.beta_stride + h);
     }
-    io<Tin>::ld4(vb + tok * p.v_stride + static_cast<int64_t>(h) * D + col, vc);
-    const float beta = io<Tin>::ld(bb + tok * p.beta_stride + h);
 
     // Diag(alpha) S and the partial prediction S^T k over this lane's rows
     float w[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < L::RPL; ++i) {
-      const float a = expf(gr[i]);
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        S[i][c] *= a;
+        S[i][c] *= ar[i];
         w[c] = fmaf(S[i][c], kr[i], w[c]);
       }
     }
@@ -139,13 +188,26 @@ step_kernel(const StepParams p) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) o[c] = wave_sum_from<L::LPR>(o[c]) * p.scale;
       if (rg == 0) {
-        Tout* ob = static_cast<Tout*>(p.o) + tok * p.o_stride + static_cast<int64_t>(h) * D + col;
-        io<Tout>::st4(ob, o);
+        if constexpr (STAGED) {
+          *reinterpret_cast<float4*>(&s_o[j][col]) = make_float4(o[0], o[1], o[2], o[3]);
+        } else {
+          io<Tout>::st4(static_cast<Tout*>(p.o) + tok * p.o_stride + static_cast<int64_t>(h) * D + col, o);
+        }
       }
     }
     if (do_store && j + 1 == Lc) {
 #pragma unroll
       for (int i = 0; i < L::RPL; ++i) io<float>::st4(dp + static_cast<int64_t>(i) * D, S[i]);
+    }
+  }
+  if (STAGED && p.o) {
+    __syncthreads();
+    Tout* ob = static_cast<Tout*>(p.o);
+    for (int e = 4 * threadIdx.x; e < n_tok * D; e += 4 * NTH) {
+      const int j = e / D, c = e % D;
+      const float4 o4 = *reinterpret_cast<const float4*>(&s_o[j][c]);
+      const float ov[4] = {o4.x, o4.y, o4.z, o4.w};
+      io<Tout>::st4(ob + (static_cast<int64_t>(s) * p.T_spec + j) * p.o_stride + static_cast<int64_t>(h) * D + c, ov);
     }
   }
 }
@@ -155,7 +217,10 @@ static int launch_step_t(const StepParams& p, hipStream_t stream) {
   using L = StepLayout<D>;
   dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(p.n_seq) * p.H));
   dim3 block(64 * L::WPH);
-  hipLaunchKernelGGL((step_kernel<D, Tin, Tout>), grid, block, 0, stream, p);
+  if (p.T_spec == 1)
+    hipLaunchKernelGGL((step_kernel<D, Tin, Tout, false>), grid, block, 0, stream, p);
+  else
+    hipLaunchKernelGGL((step_kernel<D, Tin, Tout, true>), grid, block, 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(KDA_ERR_HIP, "step kernel launch: %s", hipGetErrorString(e));
   return KDA_OK;
