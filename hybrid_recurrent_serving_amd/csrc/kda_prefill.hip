@@ -233,14 +233,12 @@ struct Smem {
   bf16_t rk_lo[TILE][PD];
   bf16_t v_hi[TILE][PD];      // [s][n]
   bf16_t v_lo[F32IN ? TILE : 1][PD];
-  alignas(16) float eg_m[D];              // exp(G_m)
-  alignas(16) float eg_e[D];              // exp(G_last - G_m)
+  alignas(16) float eg_m[2][D];           // exp(G_m), by chunk parity
+  alignas(16) float eg_e[2][D];           // exp(G_last - G_m), by chunk parity
+  alignas(16) TIN g_raw[TILE][D];         // raw gates of the next chunk
+  alignas(16) float G[TILE][D];           // cumulative gates of the next chunk
   float beta[TILE];
   union {
-    struct {
-      TIN g_raw[TILE][D];
-      alignas(16) float G[TILE][D];
-    } a;
     struct {
       alignas(16) float At[TILE][TILE + 4];  // At[s][r] = beta_r <left_k[r], right_k[s]>, s < r
       bf16_t P_hi[TILE][PT];  // [r][pos32(s)]
@@ -390,46 +388,146 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
   const int ib = tid % NPB;
   const int c0 = 32 * (ib >> 2) + 4 * (ib & 3);
 
-  auto load_raw = [&](int64_t base, RawRow<TIN>& rr) {
+  // Raw rows in registers.  Item (row ir, position block ib) holds channels
+  // c0..c0+3 and c0+16..c0+19: q and k of the next chunk (consumed by its
+  // gated-operand phase), g and v (and beta of row tid) of the chunk after
+  // the current one, committed to LDS one chunk ahead.
+  struct QKRow {
+    uint2 q[2 * NU], k[2 * NU];
+  } qk;
+  struct GVRow {
+    uint2 g[2 * NU], v[2 * NU];
+    TIN b;
+  } gv;
+  // Registers that receive a load are never written by ALU code before the
+  // load is known complete (that write would wait for every memory
+  // operation in flight): rows outside the sequence are masked where the
+  // values are consumed instead of zeroed here.
+  auto row_ok = [&](int64_t pos) { return has_item && ir < CH && pos >= lo && pos < hi && c0 < d; };
+  auto load_qk = [&](int64_t base) {
     const int64_t pos = base + ir;
-    const bool valid = has_item && ir < CH && pos >= lo && pos < hi && c0 < d;
-    const bool with_v = mode != kModeTransition;
-#pragma unroll
-    for (int w = 0; w < 2 * NU; ++w) rr.q[w] = rr.k[w] = rr.v[w] = rr.g[w] = make_uint2(0, 0);
-    if (valid) {
+    if (row_ok(pos)) {
       const int64_t tok = bos + (pos - start);
       const int64_t off = static_cast<int64_t>(h) * d + c0;
       const TIN* qp = qg + tok * p.q_stride + off;
       const TIN* kp = kg + tok * p.k_stride + off;
-      const TIN* vp = vg + tok * p.v_stride + off;
-      const TIN* gp = gg + tok * p.g_stride + off;
       const bool second = c0 + 16 < d;   // d = 16: only the first group exists
 #pragma unroll
       for (int w = 0; w < NU; ++w) {
-        rr.q[w] = reinterpret_cast<const uint2*>(qp)[w];
-        rr.k[w] = reinterpret_cast<const uint2*>(kp)[w];
-        if (with_v) rr.v[w] = reinterpret_cast<const uint2*>(vp)[w];
-        rr.g[w] = reinterpret_cast<const uint2*>(gp)[w];
+        qk.q[w] = reinterpret_cast<const uint2*>(qp)[w];
+        qk.k[w] = reinterpret_cast<const uint2*>(kp)[w];
         if (second) {
-          rr.q[NU + w] = reinterpret_cast<const uint2*>(qp + 16)[w];
-          rr.k[NU + w] = reinterpret_cast<const uint2*>(kp + 16)[w];
-          if (with_v) rr.v[NU + w] = reinterpret_cast<const uint2*>(vp + 16)[w];
-          rr.g[NU + w] = reinterpret_cast<const uint2*>(gp + 16)[w];
+          qk.q[NU + w] = reinterpret_cast<const uint2*>(qp + 16)[w];
+          qk.k[NU + w] = reinterpret_cast<const uint2*>(kp + 16)[w];
         }
       }
     }
   };
+  auto load_gv = [&](int64_t base) {
+    const int64_t pos = base + ir;
+    const bool with_v = mode != kModeTransition;   // the transition runs with v = 0
+    if (row_ok(pos)) {
+      const int64_t tok = bos + (pos - start);
+      const int64_t off = static_cast<int64_t>(h) * d + c0;
+      const TIN* vp = vg + tok * p.v_stride + off;
+      const TIN* gp = gg + tok * p.g_stride + off;
+      const bool second = c0 + 16 < d;
+#pragma unroll
+      for (int w = 0; w < NU; ++w) {
+        if (with_v) gv.v[w] = reinterpret_cast<const uint2*>(vp)[w];
+        gv.g[w] = reinterpret_cast<const uint2*>(gp)[w];
+        if (second) {
+          if (with_v) gv.v[NU + w] = reinterpret_cast<const uint2*>(vp + 16)[w];
+          gv.g[NU + w] = reinterpret_cast<const uint2*>(gp + 16)[w];
+        }
+      }
+    }
+    // beta stays in raw input bits until it is committed
+    const int64_t bpos = base + tid;
+    if (tid < CH && bpos >= lo && bpos < hi) gv.b = bg[(bos + (bpos - start)) * p.beta_stride + h];
+  };
+  // (uint2 pair of one 4-channel group) or zeros
+  auto masked = [](const uint2& x, bool ok) { return ok ? x : make_uint2(0, 0); };
+  // g and beta of chunk nbase -> LDS (after the last use of the current ones)
+  auto commit_g = [&](int64_t nbase) {
+    if (has_item) {
+      const bool ok = row_ok(nbase + ir), ok2 = ok && c0 + 16 < d;
+#pragma unroll
+      for (int w = 0; w < NU; ++w) {
+        reinterpret_cast<uint2*>(&sm.g_raw[ir][c0])[w] = masked(gv.g[w], ok);
+        reinterpret_cast<uint2*>(&sm.g_raw[ir][c0 + 16])[w] = masked(gv.g[NU + w], ok2);
+      }
+    }
+    if (tid < TILE) {
+      const int64_t bpos = nbase + tid;
+      const bool ok = tid < CH && bpos >= lo && bpos < hi;
+      sm.beta[tid] = ok ? io<TIN>::ld(&gv.b) : 0.f;
+    }
+  };
+  // v of chunk nbase -> LDS (after the current W / U products)
+  auto commit_v = [&](int64_t nbase) {
+    if (has_item) {
+      const bool ok = row_ok(nbase + ir) && mode != kModeTransition, ok2 = ok && c0 + 16 < d;
+      uint2 vv[2 * NU];
+#pragma unroll
+      for (int w = 0; w < NU; ++w) {
+        vv[w] = masked(gv.v[w], ok);
+        vv[NU + w] = masked(gv.v[NU + w], ok2);
+      }
+      if constexpr (HP) {
+        float vx[8], vh[8], vl[8];
+        to_f32<TIN>(vv, vx);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          vh[i] = hi_of(vx[i]);
+          vl[i] = vx[i] - vh[i];
+        }
+        st4b(&sm.v_hi[ir][c0], vh);
+        st4b(&sm.v_hi[ir][c0 + 16], vh + 4);
+        st4b(&sm.v_lo[ir][c0], vl);
+        st4b(&sm.v_lo[ir][c0 + 16], vl + 4);
+      } else {
+        *reinterpret_cast<uint2*>(&sm.v_hi[ir][c0]) = vv[0];
+        *reinterpret_cast<uint2*>(&sm.v_hi[ir][c0 + 16]) = vv[1];
+      }
+    }
+  };
+  // G = inclusive cumulative sum of g down the chunk rows, per key channel,
+  // from g_raw; exp(G_m) and exp(G_last - G_m) into eg[par].  Each wave
+  // takes D / NW channels, each lane a run of RP rows of one channel; the
+  // runs are chained by a scan across the lanes of the wave.
+  auto gates = [&](int par) {
+    constexpr int CPW = D / NW;
+    constexpr int NPART = 64 / CPW;
+    constexpr int RP = TILE / NPART;
+    const int c = CPW * wave + lane % CPW;
+    const int part = lane / CPW;
+    float gl[RP];
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < RP; ++i) {
+      acc += io<TIN>::ld(&sm.g_raw[part * RP + i][c]);
+      gl[i] = acc;
+    }
+    float incl = acc;
+#pragma unroll
+    for (int o = 1; o < NPART; o <<= 1) {
+      const float y = __shfl_up(incl, o * CPW, 64);
+      if (part >= o) incl += y;
+    }
+    const float off = incl - acc;
+#pragma unroll
+    for (int i = 0; i < RP; ++i) sm.G[part * RP + i][c] = gl[i] + off;
+    // G at the reference row and at the last row, from the lanes that hold them
+    const float gm = __shfl(gl[MID % RP] + off, (MID / RP) * CPW + lane % CPW, 64);
+    const float ge = __shfl(gl[RP - 1] + off, (NPART - 1) * CPW + lane % CPW, 64);
+    if (part == 0) {
+      sm.eg_m[par][c] = expf(gm);
+      sm.eg_e[par][c] = expf(ge - gm);
+    }
+  };
 
   const int64_t first = hi > lo ? (lo / CH) * CH : hi;
-  // beta of row tid (threads tid < TILE), prefetched like the raw tile and
-  // kept as raw input bits until the next chunk (converting it here would
-  // wait for the whole prefetch)
-  auto load_beta = [&](int64_t base) -> TIN {
-    const int64_t pos = base + tid;
-    TIN b = 0;
-    if (tid < CH && pos >= lo && pos < hi) b = bg[(bos + (pos - start)) * p.beta_stride + h];
-    return b;
-  };
   // rows of the staged output tile that belong to the sequence -> o (16-byte stores)
   auto store_out = [&](int64_t obase) {
     constexpr int OV = 16 / sizeof(TOUT);   // elements per vector
@@ -445,14 +543,19 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
       }
     }
   };
-  // Two raw-tile buffers, used alternately by the two chunk calls of each
-  // loop trip: the tile in flight is never copied, so nothing waits for it
-  // before its own chunk.
-  RawRow<TIN> rawA, rawB;
-  load_raw(first, rawA);
-  TIN betaA = load_beta(first), betaB = 0;
-  auto chunk = [&](const int64_t base, const RawRow<TIN>& cur, const TIN bcur, RawRow<TIN>& nxt,
-                   TIN& bnx) __attribute__((always_inline)) {
+  // prologue: the first chunk's g, v, beta in LDS, its gates, q / k in
+  // registers, and the second chunk's g, v, beta requested
+  if (hi > lo) {
+    load_gv(first);
+    load_qk(first);
+    commit_g(first);
+    commit_v(first);
+    lds_barrier();
+    gates(0);
+    if (first + CH < hi) load_gv(first + CH);
+    lds_barrier();
+  }
+  auto chunk = [&](const int64_t base, const int par) __attribute__((always_inline)) {
     // Per-thread indices are derived again in every chunk from an opaque copy
     // of the thread id; otherwise every LDS address derived from them would be
     // hoisted out of this loop and held in a register for the whole sequence.
@@ -467,86 +570,30 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
     const int ir = tid / NPB;
     const int ib = tid % NPB;
     const int c0 = 32 * (ib >> 2) + 4 * (ib & 3);
-    // ------------------------------------------------ phase L: commit raw tile, prefetch next
-    // (the tile is committed before the next one is requested, so the wait
-    // for it does not cover the new requests)
-    if (has_item) {
-#pragma unroll
-      for (int w = 0; w < NU; ++w) {
-        reinterpret_cast<uint2*>(&sm.u.a.g_raw[ir][c0])[w] = cur.g[w];
-        reinterpret_cast<uint2*>(&sm.u.a.g_raw[ir][c0 + 16])[w] = cur.g[NU + w];
-      }
-      if constexpr (HP) {
-        float vx[8], vh[8], vl[8];
-        to_f32<TIN>(cur.v, vx);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          vh[i] = hi_of(vx[i]);
-          vl[i] = vx[i] - vh[i];
-        }
-        st4b(&sm.v_hi[ir][c0], vh);
-        st4b(&sm.v_hi[ir][c0 + 16], vh + 4);
-        st4b(&sm.v_lo[ir][c0], vl);
-        st4b(&sm.v_lo[ir][c0 + 16], vl + 4);
-      } else {
-        *reinterpret_cast<uint2*>(&sm.v_hi[ir][c0]) = cur.v[0];
-        *reinterpret_cast<uint2*>(&sm.v_hi[ir][c0 + 16]) = cur.v[1];
-      }
-    }
-    if (tid < TILE) sm.beta[tid] = io<TIN>::ld(&bcur);
-    if (base + CH < hi) {
-      load_raw(base + CH, nxt);
-      bnx = load_beta(base + CH);
-    }
-    lds_barrier();
-    // outputs of the previous chunk (staged at its end): stored now, so that
-    // no later wait for a load has to cover these stores as well
-    if (outputs && base != first) store_out(base - CH);
-    // ------------------------------------------------ phase G: cumulative gates
-    // G = inclusive cumulative sum of g down the chunk rows, per key channel:
-    // each wave takes D / NW channels, each lane a run of RP rows of one
-    // channel; the runs are chained by a scan across the lanes of the wave.
-    {
-      constexpr int CPW = D / NW;
-      constexpr int NPART = 64 / CPW;
-      constexpr int RP = TILE / NPART;
-      const int c = CPW * wave + lane % CPW;
-      const int part = lane / CPW;
-      float gl[RP];
-      float acc = 0.f;
-#pragma unroll
-      for (int i = 0; i < RP; ++i) {
-        acc += io<TIN>::ld(&sm.u.a.g_raw[part * RP + i][c]);
-        gl[i] = acc;
-      }
-      float incl = acc;
-#pragma unroll
-      for (int o = 1; o < NPART; o <<= 1) {
-        const float y = __shfl_up(incl, o * CPW, 64);
-        if (part >= o) incl += y;
-      }
-      const float off = incl - acc;
-#pragma unroll
-      for (int i = 0; i < RP; ++i) sm.u.a.G[part * RP + i][c] = gl[i] + off;
-    }
-    lds_barrier();
-    if (tid < D) {
-      const float gm = sm.u.a.G[MID][tid];
-      sm.eg_m[tid] = expf(gm);
-      sm.eg_e[tid] = expf(sm.u.a.G[TILE - 1][tid] - gm);
-    }
+    const bool more = base + CH < hi;
     // ------------------------------------------------ phase O: gated operands (row-major)
     if (has_item) {
       float qx[8], kx[8];
-      to_f32<TIN>(cur.q, qx);
-      to_f32<TIN>(cur.k, kx);
+      {
+        const bool ok = row_ok(base + ir), ok2 = ok && c0 + 16 < d;
+        uint2 qq[2 * NU], kk[2 * NU];
+#pragma unroll
+        for (int w = 0; w < NU; ++w) {
+          qq[w] = masked(qk.q[w], ok);
+          kk[w] = masked(qk.k[w], ok);
+          qq[NU + w] = masked(qk.q[NU + w], ok2);
+          kk[NU + w] = masked(qk.k[NU + w], ok2);
+        }
+        to_f32<TIN>(qq, qx);
+        to_f32<TIN>(kk, kx);
+      }
       // positions 8 ib + e hold channels c0 + e (e < 4) and c0 + 16 + e - 4
       float lq[8], lk[8], rk[8];
 #pragma unroll
       for (int gi = 0; gi < 2; ++gi) {
         const int cc = c0 + 16 * gi;
-        const float4 a = *reinterpret_cast<const float4*>(&sm.u.a.G[ir][cc]);
-        const float4 b = *reinterpret_cast<const float4*>(&sm.u.a.G[MID][cc]);
+        const float4 a = *reinterpret_cast<const float4*>(&sm.G[ir][cc]);
+        const float4 b = *reinterpret_cast<const float4*>(&sm.G[MID][cc]);
         const float x4[4] = {a.x - b.x, a.y - b.y, a.z - b.z, a.w - b.w};
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
@@ -585,6 +632,11 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
       st8b(&sm.rk_hi[ir][pp], hi);
       st8b(&sm.rk_lo[ir][pp], lo);
     }
+    // outputs of the previous chunk (staged at its end), then the next
+    // chunk's q / k: both after this chunk's q / k are consumed, so that the
+    // wait for those covers neither
+    if (outputs && base != first) store_out(base - CH);
+    if (more) load_qk(base + CH);
     lds_barrier();
     // ------------------------------------------------ phase AP: A and P (16x16 tiles)
     {
@@ -734,6 +786,8 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
         }
       }
     }
+    // this chunk's g and beta are no longer read: the next chunk's go in
+    if (more) commit_g(base + CH);
     lds_barrier();
     // ------------------------------------------------ chain (per wave, own 16 columns)
     f32x4 O[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
@@ -743,7 +797,7 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
       bf16x8 sh[NQ / 2], sl[NQ / 2];
 #pragma unroll
       for (int q = 0; q < NQ; ++q) {
-        const float4 f = *reinterpret_cast<const float4*>(&sm.eg_m[16 * q + 4 * g4]);
+        const float4 f = *reinterpret_cast<const float4*>(&sm.eg_m[par][16 * q + 4 * g4]);
         S[q][0] *= f.x; S[q][1] *= f.y; S[q][2] *= f.z; S[q][3] *= f.w;
       }
 #pragma unroll
@@ -804,13 +858,19 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
       }
 #pragma unroll
       for (int q = 0; q < NQ; ++q) {
-        const float4 f = *reinterpret_cast<const float4*>(&sm.eg_e[16 * q + 4 * g4]);
+        const float4 f = *reinterpret_cast<const float4*>(&sm.eg_e[par][16 * q + 4 * g4]);
         S[q][0] *= f.x; S[q][1] *= f.y; S[q][2] *= f.z; S[q][3] *= f.w;
       }
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) O[mt][i] += Ob[mt][i] + Oc[mt][i];
+    }
+    // ------------------------------------------------ next chunk: gates, v, and the request for the one after
+    if (more) {
+      gates(par ^ 1);
+      commit_v(base + CH);
+      if (base + 2 * CH < hi) load_gv(base + 2 * CH);
     }
     // ------------------------------------------------ outputs: stage in LDS (stored during the next chunk)
     if (chain && outputs) {
@@ -835,9 +895,10 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
     }
     lds_barrier();
   };
-  for (int64_t base = first; base < hi; base += 2 * CH) {
-    chunk(base, rawA, betaA, rawB, betaB);
-    if (base + CH < hi) chunk(base + CH, rawB, betaB, rawA, betaA);
+  int par = 0;
+  for (int64_t base = first; base < hi; base += CH) {
+    chunk(base, par);
+    par ^= 1;
   }
   if (outputs && hi > lo) {
     lds_barrier();
