@@ -67,6 +67,7 @@ constexpr int TILE = 32;   // rows per chunk tile
 constexpr int NW = 8;      // waves per workgroup
 constexpr int NT = 64 * NW;
 constexpr int MID = 15;    // reference row of the gates
+constexpr int GATE_WAVES = 4;  // waves that form the next chunk's gates during the solve
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
@@ -237,7 +238,7 @@ struct Smem {
   alignas(16) float eg_e[2][D];           // exp(G_last - G_m), by chunk parity
   alignas(16) TIN g_raw[TILE][D];         // raw gates of the next chunk
   alignas(16) float G[TILE][D];           // cumulative gates of the next chunk
-  float beta[TILE];
+  float beta[2][TILE];                    // by chunk parity
   union {
     struct {
       alignas(16) float At[TILE][TILE + 4];  // At[s][r] = beta_r <left_k[r], right_k[s]>, s < r
@@ -245,7 +246,6 @@ struct Smem {
       bf16_t P_lo[TILE][PT];
       bf16_t Wn[TILE][PD];    // -(T left_k) [r][pos32(c)]
       bf16_t Wn_lo[F32IN ? TILE : 1][PD];
-      alignas(16) float Ms[16][20];       // M = (I + A11)^{-1} A10
       alignas(16) float Tf[16][20];       // T00 (fp32)
       bf16_t Tb[TILE][PT];                // T = (I + A)^{-1} diag(beta) [r][s]
       bf16_t Tb_lo[F32IN ? TILE : 1][PT];
@@ -448,8 +448,8 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
   };
   // (uint2 pair of one 4-channel group) or zeros
   auto masked = [](const uint2& x, bool ok) { return ok ? x : make_uint2(0, 0); };
-  // g and beta of chunk nbase -> LDS (after the last use of the current ones)
-  auto commit_g = [&](int64_t nbase) {
+  // g and beta of chunk nbase (parity npar) -> LDS
+  auto commit_g = [&](int64_t nbase, int npar) {
     if (has_item) {
       const bool ok = row_ok(nbase + ir), ok2 = ok && c0 + 16 < d;
 #pragma unroll
@@ -461,7 +461,7 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
     if (tid < TILE) {
       const int64_t bpos = nbase + tid;
       const bool ok = tid < CH && bpos >= lo && bpos < hi;
-      sm.beta[tid] = ok ? io<TIN>::ld(&gv.b) : 0.f;
+      sm.beta[npar][tid] = ok ? io<TIN>::ld(&gv.b) : 0.f;
     }
   };
   // v of chunk nbase -> LDS (after the current W / U products)
@@ -493,14 +493,15 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
     }
   };
   // G = inclusive cumulative sum of g down the chunk rows, per key channel,
-  // from g_raw; exp(G_m) and exp(G_last - G_m) into eg[par].  Each wave
-  // takes D / NW channels, each lane a run of RP rows of one channel; the
-  // runs are chained by a scan across the lanes of the wave.
-  auto gates = [&](int par) {
-    constexpr int CPW = D / NW;
+  // from g_raw; exp(G_m) and exp(G_last - G_m) into eg[par].  Run by
+  // GATE_WAVES waves (gw = 0 ..): each takes D / GATE_WAVES channels, each
+  // lane a run of RP rows of one channel; the runs are chained by a scan
+  // across the lanes of the wave.
+  auto gates = [&](int par, int gw) {
+    constexpr int CPW = D / GATE_WAVES;
     constexpr int NPART = 64 / CPW;
     constexpr int RP = TILE / NPART;
-    const int c = CPW * wave + lane % CPW;
+    const int c = CPW * gw + lane % CPW;
     const int part = lane / CPW;
     float gl[RP];
     float acc = 0.f;
@@ -548,10 +549,10 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
   if (hi > lo) {
     load_gv(first);
     load_qk(first);
-    commit_g(first);
+    commit_g(first, 0);
     commit_v(first);
     lds_barrier();
-    gates(0);
+    if (wave < GATE_WAVES) gates(0, wave);
     if (first + CH < hi) load_gv(first + CH);
     lds_barrier();
   }
@@ -682,7 +683,7 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
         for (int i = 0; i < 4; ++i) {
           const int r = 16 * I + 4 * g4 + i;
           const int c = 16 * J + l16;
-          sm.u.b.At[c][r] = r > c ? acc[i] * sm.beta[r] : 0.f;
+          sm.u.b.At[c][r] = r > c ? acc[i] * sm.beta[par][r] : 0.f;
         }
       } else if (wave == 6) {
         // tile (0,1) of A and P is zero
@@ -695,51 +696,61 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
         }
       }
     }
+    // the next chunk's g and beta (its gates are formed during phase X)
+    if (more) commit_g(base + CH, par ^ 1);
     lds_barrier();
     // ------------------------------------------------ phase X: T = (I + A)^{-1} diag(beta); W = T left_k, U = T V
     // Blockwise on the 16-row blocks b, with L_b = I + A_bb:
     //     T_bb = L_b^{-1} diag(beta_b),  T10 = -M T00,  M = L_1^{-1} A10,
     // each inverse by fp32 forward substitution down the 16 lanes of a lane
     // row (lane (g4, r) holds row r of column 4 g + g4, g = 0..3).
-    if (wave < 3) {
-      const int b = wave == 0 ? 0 : 1;
+    if (wave < 2) {
+      // T_bb = L_b^{-1} diag(beta_b), b = wave
+      const int b = wave;
       float na[16];
 #pragma unroll
       for (int s = 0; s < 16; ++s) na[s] = -sm.u.b.At[16 * b + s][16 * b + l16];
       float x[4];
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int j = 4 * g + g4;
-        x[g] = wave == 2 ? sm.u.b.At[j][16 + l16] : (l16 == j ? 1.f : 0.f);
-      }
+      for (int g = 0; g < 4; ++g) x[g] = l16 == 4 * g + g4 ? 1.f : 0.f;
       fsub16<0, 4>(x, na);
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int j = 4 * g + g4;
-        if (wave == 2) {
-          sm.u.b.Ms[l16][j] = x[g];
-        } else {
-          const float t = x[g] * sm.beta[16 * b + j];
-          if (b == 0) sm.u.b.Tf[l16][j] = t;
-          const float th = hi_of(t);
-          sm.u.b.Tb[16 * b + l16][16 * b + j] = f32_to_bf16(th);
-          if constexpr (HP) sm.u.b.Tb_lo[16 * b + l16][16 * b + j] = f32_to_bf16(t - th);
-        }
+        const float t = x[g] * sm.beta[par][16 * b + j];
+        const float th = hi_of(t);
+        sm.u.b.Tb[16 * b + l16][16 * b + j] = f32_to_bf16(th);
+        if constexpr (HP) sm.u.b.Tb_lo[16 * b + l16][16 * b + j] = f32_to_bf16(t - th);
       }
-    } else if (wave == 3) {
+    } else if (wave == 2) {
+      // T10 = -M T00 with M = L_1^{-1} A10: both factors by forward
+      // substitution in this wave, the product on fp32 matrix cores
+      float na0[16], na1[16];
+#pragma unroll
+      for (int s = 0; s < 16; ++s) {
+        na0[s] = -sm.u.b.At[s][l16];
+        na1[s] = -sm.u.b.At[16 + s][16 + l16];
+      }
+      float x[4], m[4];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        sm.u.b.Tb[l16][16 + 4 * g + g4] = 0;
-        if constexpr (HP) sm.u.b.Tb_lo[l16][16 + 4 * g + g4] = 0;
+        const int j = 4 * g + g4;
+        x[g] = l16 == j ? 1.f : 0.f;
+        m[g] = sm.u.b.At[j][16 + l16];     // A10[r][j] = A[16 + r][j]
       }
-    }
-    lds_barrier();
-    if (wave == 0) {
-      // T10 = -M T00 on fp32 matrix cores (K = 16 in steps of 4)
+      fsub16<0, 4>(x, na0);
+      fsub16<0, 4>(m, na1);
+      // T00 in LDS for the transposed operand; lane (g4, r) then reads
+      // T00[4 kb + g4][r] (this wave's own writes: its LDS operations complete
+      // in order)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) sm.u.b.Tf[l16][4 * g + g4] = x[g] * sm.beta[par][4 * g + g4];
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_wave_barrier();
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sm.u.b.Ms[l16][4 * kb + g4], sm.u.b.Tf[4 * kb + g4][l16], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(m[kb], sm.u.b.Tf[4 * kb + g4][l16], acc, 0, 0, 0);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float t = -acc[e];
@@ -747,6 +758,15 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
         sm.u.b.Tb[16 + 4 * g4 + e][l16] = f32_to_bf16(th);
         if constexpr (HP) sm.u.b.Tb_lo[16 + 4 * g4 + e][l16] = f32_to_bf16(t - th);
       }
+    } else if (wave == 3) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        sm.u.b.Tb[l16][16 + 4 * g + g4] = 0;
+        if constexpr (HP) sm.u.b.Tb_lo[l16][16 + 4 * g + g4] = 0;
+      }
+    } else if (more) {
+      // the next chunk's gates, on the waves the solve leaves free
+      gates(par ^ 1, wave - (NW - GATE_WAVES));
     }
     lds_barrier();
     // W = T left_k (columns of this wave in storage order, kept as -W in LDS)
@@ -786,8 +806,6 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
         }
       }
     }
-    // this chunk's g and beta are no longer read: the next chunk's go in
-    if (more) commit_g(base + CH);
     lds_barrier();
     // ------------------------------------------------ chain (per wave, own 16 columns)
     f32x4 O[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
@@ -866,9 +884,8 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
 #pragma unroll
         for (int i = 0; i < 4; ++i) O[mt][i] += Ob[mt][i] + Oc[mt][i];
     }
-    // ------------------------------------------------ next chunk: gates, v, and the request for the one after
+    // ------------------------------------------------ next chunk: v, and the g / v / beta request for the one after
     if (more) {
-      gates(par ^ 1);
       commit_v(base + CH);
       if (base + 2 * CH < hi) load_gv(base + 2 * CH);
     }
