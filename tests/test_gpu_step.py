@@ -257,3 +257,29 @@ def test_verify_commit_index_probe(dev):
         assert recovered == int(L[s]), (s, recovered, int(L[s]))
         for j in range(int(L[s]), Ts):
             np.testing.assert_allclose(readout[:, j], S0[s, 0].double().numpy().T @ kk[j], atol=1e-5)
+
+
+@pytest.mark.parametrize("T_spec,d,dtype", [(16, 128, torch.bfloat16), (3, 64, torch.bfloat16),
+                                            (16, 32, torch.float32), (2, 16, torch.float32)])
+def test_verify_token_counts_and_sizes(dev, oracle64, T_spec, d, dtype):
+    """Verify over the supported range of draft counts (up to 16 tokens, the
+    most one call stages) and head sizes, bf16 and fp32 inputs, with accepted
+    lengths spanning 0..T_spec."""
+    U.say(f"verify T_spec={T_spec} d={d} {dtype}")
+    N, H = 24, 3
+    wl = make_workload(4, n_seq=N, H=H, d=d, T=T_spec)
+    q, k, v, g, b = (t.to(dtype) for t in (wl.q, wl.k, wl.v, wl.g, wl.beta))
+    L = torch.arange(N, dtype=torch.int32) % (T_spec + 1)
+    ref = oracle64.kda_verify(q, k, v, g, b, wl.init_states, L)
+    pool = torch.cat([wl.init_states, torch.zeros_like(wl.init_states)]).to(dev)
+    src = torch.arange(N, dtype=torch.int32, device=dev)
+    dst = src + N
+    o = torch.empty(N, T_spec, H, d, dtype=dtype, device=dev)
+    clen = torch.full((N,), -7, dtype=torch.int32, device=dev)
+    K.kda_verify(q.to(dev), k.to(dev), v.to(dev), g.to(dev), b.to(dev), pool, src, dst, o=o,
+                 accepted_len=L.to(dev), committed_len_out=clen)
+    torch.cuda.synchronize()
+    assert torch.equal(clen.cpu(), L)
+    tol = {} if dtype == torch.bfloat16 else {"rel": 1e-5, "mx": 1e-4}
+    U.assert_close("o", U.to_np(o), ref["o"], **tol)
+    U.assert_close("committed", U.to_np(pool[N:]), ref["committed"], rel=1e-5, mx=1e-4)
