@@ -52,13 +52,16 @@ step_kernel(const StepParams p) {
   // per-token inputs of this (sequence, head), staged once: alpha = exp(g),
   // k, q (fp32, [token][row]), v ([token][col]), beta; outputs staged the
   // same way and stored after the last token
-  constexpr int TS = STAGED ? STEP_TMAX : 1;
-  __shared__ __align__(16) float s_a[TS][D];
-  __shared__ __align__(16) float s_k[TS][D];
-  __shared__ __align__(16) float s_q[TS][D];
-  __shared__ __align__(16) float s_v[TS][D];
-  __shared__ __align__(16) float s_o[TS][D];
-  __shared__ float s_b[TS];
+  // dynamic LDS sized for the call's T_spec: five [T_spec][D] fp32 arrays
+  // (alpha, k, q, v, o) and beta [T_spec]
+  extern __shared__ __align__(16) float s_dyn[];
+  const int TD = p.T_spec * D;
+  float* const s_a = s_dyn;
+  float* const s_k = s_dyn + TD;
+  float* const s_q = s_dyn + 2 * TD;
+  float* const s_v = s_dyn + 3 * TD;
+  float* const s_o = s_dyn + 4 * TD;
+  float* const s_b = s_dyn + 5 * TD;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int64_t sh = blockIdx.x;
@@ -115,10 +118,10 @@ step_kernel(const StepParams p) {
       io<Tin>::ld4(qb + off * p.q_stride + hc, q4);
       io<Tin>::ld4(vb + off * p.v_stride + hc, v4);
       io<Tin>::ld4(gb + off * p.g_stride + hc, g4);
-      *reinterpret_cast<float4*>(&s_k[j][c]) = make_float4(k4[0], k4[1], k4[2], k4[3]);
-      *reinterpret_cast<float4*>(&s_q[j][c]) = make_float4(q4[0], q4[1], q4[2], q4[3]);
-      *reinterpret_cast<float4*>(&s_v[j][c]) = make_float4(v4[0], v4[1], v4[2], v4[3]);
-      *reinterpret_cast<float4*>(&s_a[j][c]) = make_float4(expf(g4[0]), expf(g4[1]), expf(g4[2]), expf(g4[3]));
+      *reinterpret_cast<float4*>(&s_k[j * D + c]) = make_float4(k4[0], k4[1], k4[2], k4[3]);
+      *reinterpret_cast<float4*>(&s_q[j * D + c]) = make_float4(q4[0], q4[1], q4[2], q4[3]);
+      *reinterpret_cast<float4*>(&s_v[j * D + c]) = make_float4(v4[0], v4[1], v4[2], v4[3]);
+      *reinterpret_cast<float4*>(&s_a[j * D + c]) = make_float4(expf(g4[0]), expf(g4[1]), expf(g4[2]), expf(g4[3]));
       if (c == 0) s_b[j] = io<Tin>::ld(bb + off * p.beta_stride + h);
     }
     __syncthreads();
@@ -137,14 +140,14 @@ step_kernel(const StepParams p) {
     if constexpr (STAGED) {
 #pragma unroll
       for (int i = 0; i < L::RPL; i += 4) {
-        const float4 k4 = *reinterpret_cast<const float4*>(&s_k[j][row0 + i]);
-        const float4 q4 = *reinterpret_cast<const float4*>(&s_q[j][row0 + i]);
-        const float4 a4 = *reinterpret_cast<const float4*>(&s_a[j][row0 + i]);
+        const float4 k4 = *reinterpret_cast<const float4*>(&s_k[j * D + row0 + i]);
+        const float4 q4 = *reinterpret_cast<const float4*>(&s_q[j * D + row0 + i]);
+        const float4 a4 = *reinterpret_cast<const float4*>(&s_a[j * D + row0 + i]);
         kr[i] = k4.x; kr[i + 1] = k4.y; kr[i + 2] = k4.z; kr[i + 3] = k4.w;
         qr[i] = q4.x; qr[i + 1] = q4.y; qr[i + 2] = q4.z; qr[i + 3] = q4.w;
         ar[i] = a4.x; ar[i + 1] = a4.y; ar[i + 2] = a4.z; ar[i + 3] = a4.w;
       }
-      const float4 v4 = *reinterpret_cast<const float4*>(&s_v[j][col]);
+      const float4 v4 = *reinterpret_cast<const float4*>(&s_v[j * D + col]);
       vc[0] = v4.x; vc[1] = v4.y; vc[2] = v4.z; vc[3] = v4.w;
       beta = s_b[j];
     } else {
@@ -189,7 +192,7 @@ step_kernel(const StepParams p) {
       for (int c = 0; c < 4; ++c) o[c] = wave_sum_from<L::LPR>(o[c]) * p.scale;
       if (rg == 0) {
         if constexpr (STAGED) {
-          *reinterpret_cast<float4*>(&s_o[j][col]) = make_float4(o[0], o[1], o[2], o[3]);
+          *reinterpret_cast<float4*>(&s_o[j * D + col]) = make_float4(o[0], o[1], o[2], o[3]);
         } else {
           io<Tout>::st4(static_cast<Tout*>(p.o) + tok * p.o_stride + static_cast<int64_t>(h) * D + col, o);
         }
@@ -205,7 +208,7 @@ step_kernel(const StepParams p) {
     Tout* ob = static_cast<Tout*>(p.o);
     for (int e = 4 * threadIdx.x; e < n_tok * D; e += 4 * NTH) {
       const int j = e / D, c = e % D;
-      const float4 o4 = *reinterpret_cast<const float4*>(&s_o[j][c]);
+      const float4 o4 = *reinterpret_cast<const float4*>(&s_o[j * D + c]);
       const float ov[4] = {o4.x, o4.y, o4.z, o4.w};
       io<Tout>::st4(ob + (static_cast<int64_t>(s) * p.T_spec + j) * p.o_stride + static_cast<int64_t>(h) * D + c, ov);
     }
@@ -217,10 +220,12 @@ static int launch_step_t(const StepParams& p, hipStream_t stream) {
   using L = StepLayout<D>;
   dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(p.n_seq) * p.H));
   dim3 block(64 * L::WPH);
-  if (p.T_spec == 1)
+  if (p.T_spec == 1) {
     hipLaunchKernelGGL((step_kernel<D, Tin, Tout, false>), grid, block, 0, stream, p);
-  else
-    hipLaunchKernelGGL((step_kernel<D, Tin, Tout, true>), grid, block, 0, stream, p);
+  } else {
+    const size_t lds = (5 * static_cast<size_t>(p.T_spec) * D + p.T_spec) * sizeof(float);
+    hipLaunchKernelGGL((step_kernel<D, Tin, Tout, true>), grid, block, lds, stream, p);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(KDA_ERR_HIP, "step kernel launch: %s", hipGetErrorString(e));
   return KDA_OK;
