@@ -29,6 +29,17 @@
 
 namespace kda {
 
+// State rows stream through once per call: non-temporal 16-byte accesses
+typedef __attribute__((ext_vector_type(4))) float nt4;
+__device__ __forceinline__ void ld4_stream(const float* p, float (&x)[4]) {
+  const nt4 v = __builtin_nontemporal_load(reinterpret_cast<const nt4*>(p));
+  x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+}
+__device__ __forceinline__ void st4_stream(float* p, const float (&x)[4]) {
+  const nt4 v = {x[0], x[1], x[2], x[3]};
+  __builtin_nontemporal_store(v, reinterpret_cast<nt4*>(p));
+}
+
 template <int D>
 struct StepLayout {
   static constexpr int COLS = D < 32 ? D : 32;  // columns per wave
@@ -96,7 +107,7 @@ step_kernel(const StepParams p) {
   if (has_src) {
     const float* sp = p.pool + ((static_cast<int64_t>(src) * p.H + h) * D + row0) * D + col;
 #pragma unroll
-    for (int i = 0; i < L::RPL; ++i) io<float>::ld4(sp + static_cast<int64_t>(i) * D, S[i]);
+    for (int i = 0; i < L::RPL; ++i) ld4_stream(sp + static_cast<int64_t>(i) * D, S[i]);
   } else {
 #pragma unroll
     for (int i = 0; i < L::RPL; ++i) S[i][0] = S[i][1] = S[i][2] = S[i][3] = 0.f;
@@ -130,7 +141,7 @@ step_kernel(const StepParams p) {
   float* dp = has_dst ? p.pool + ((static_cast<int64_t>(dst) * p.H + h) * D + row0) * D + col : nullptr;
   if (do_store && Lc == 0) {
 #pragma unroll
-    for (int i = 0; i < L::RPL; ++i) io<float>::st4(dp + static_cast<int64_t>(i) * D, S[i]);
+    for (int i = 0; i < L::RPL; ++i) st4_stream(dp + static_cast<int64_t>(i) * D, S[i]);
   }
 
   for (int j = 0; j < n_tok; ++j) {
@@ -200,7 +211,7 @@ step_kernel(const StepParams p) {
     }
     if (do_store && j + 1 == Lc) {
 #pragma unroll
-      for (int i = 0; i < L::RPL; ++i) io<float>::st4(dp + static_cast<int64_t>(i) * D, S[i]);
+      for (int i = 0; i < L::RPL; ++i) st4_stream(dp + static_cast<int64_t>(i) * D, S[i]);
     }
   }
   if (STAGED && p.o) {
