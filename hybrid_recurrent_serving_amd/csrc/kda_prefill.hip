@@ -809,7 +809,10 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
     lds_barrier();
     // ------------------------------------------------ chain (per wave, own 16 columns)
     f32x4 O[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-    if (chain) {
+    // WITH_O: the recurrence alone (segment pass A) skips every product that
+    // only feeds the outputs.
+    auto chain_step = [&](auto with_o) {
+      constexpr bool WITH_O = decltype(with_o)::value;
       const int kq = 8 * g4;
       // S' = Diag(exp G_m) S, and its bf16 pair fragments (K steps of 32 channels)
       bf16x8 sh[NQ / 2], sl[NQ / 2];
@@ -831,15 +834,19 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
         for (int mt = 0; mt < 2; ++mt) {
           const int row = 16 * mt + l16;
           w[mt] = frag_lds(&sm.u.b.Wn[row][32 * ks + kq]);
-          qh[mt] = frag_lds(&sm.lq_hi[row][32 * ks + kq]);
-          ql[mt] = frag_lds(&sm.lq_lo[row][32 * ks + kq]);
+          if constexpr (WITH_O) {
+            qh[mt] = frag_lds(&sm.lq_hi[row][32 * ks + kq]);
+            ql[mt] = frag_lds(&sm.lq_lo[row][32 * ks + kq]);
+          }
         }
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
           U[mt] = mfma(w[mt], sh[ks], U[mt]);
-          O[mt] = mfma(qh[mt], sh[ks], O[mt]);
-          Ob[mt] = mfma(qh[mt], sl[ks], Ob[mt]);
-          Oc[mt] = mfma(ql[mt], sh[ks], Oc[mt]);
+          if constexpr (WITH_O) {
+            O[mt] = mfma(qh[mt], sh[ks], O[mt]);
+            Ob[mt] = mfma(qh[mt], sl[ks], Ob[mt]);
+            Oc[mt] = mfma(ql[mt], sh[ks], Oc[mt]);
+          }
           if constexpr (HP) {
             U[mt] = mfma(w[mt], sl[ks], U[mt]);
             U[mt] = mfma(frag_lds(&sm.u.b.Wn_lo[16 * mt + l16][32 * ks + kq]), sh[ks], U[mt]);
@@ -851,7 +858,7 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
       frag_pair(U[0], U[1], uh, ul);
       // O += P u
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
+      for (int mt = 0; mt < 2 && WITH_O; ++mt) {
         const bf16x8 ph = frag_lds(&sm.u.b.P_hi[16 * mt + l16][kq]);
         const bf16x8 pl = frag_lds(&sm.u.b.P_lo[16 * mt + l16][kq]);
         O[mt] = mfma(ph, uh, O[mt]);
@@ -880,9 +887,13 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
         S[q][0] *= f.x; S[q][1] *= f.y; S[q][2] *= f.z; S[q][3] *= f.w;
       }
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+      for (int mt = 0; mt < 2 && WITH_O; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) O[mt][i] += Ob[mt][i] + Oc[mt][i];
+    };
+    if (chain) {
+      if (outputs) chain_step(std::true_type{});
+      else chain_step(std::false_type{});
     }
     // ------------------------------------------------ next chunk: v, and the g / v / beta request for the one after
     if (more) {
