@@ -29,18 +29,24 @@
 // Wave w owns columns [16w, 16w + 16) of the d_v axis: its slice of the fp32
 // state lives in matrix-core accumulator registers (16x16 tiles) for the
 // whole sequence, and the state-dependent chain (u, O, state update) never
-// leaves the wave; the two waves on a SIMD run independent chains, which
-// hides each other's matrix-core and LDS latency.  The chunk-local operands
-// (gates, A, T, P, W) are built cooperatively in LDS (~84 KB).  The next
-// chunk's raw tiles are loaded into registers while the current chunk is
-// processed.
+// leaves the wave.  The chunk-local operands (gates, gated q / k, A, T, P,
+// W, U) depend only on the chunk's own inputs, so the loop is a software
+// pipeline: while the chain of chunk n runs, the operands of chunk n + 1 are
+// built in the same three barrier-separated phases (the chain in the first,
+// the products and the triangular solve in the second, W / U and the gated
+// operands in the third).  Operands read by a chain while the next chunk's
+// are formed are double-buffered in LDS; raw rows are prefetched into
+// registers one or two chunks ahead.
 //
 // Matrix-core precision (bf16 operands, fp32 accumulation); an operand
 // marked "pair" is carried as hi + lo bf16 (hi*hi + hi*lo + lo*hi):
 //     A = left_k right_k^T          single bf16
 //     P = left_q right_k^T          pair x pair
-//     T = (I + A)^{-1} diag(beta)   fp32 (16-row blocks), stored single
-//     W = T left_k, U = T V         single
+//     T = (I + A)^{-1} diag(beta)   fp32 (16-row blocks), stored single;
+//                                   its block T10 = -M T00 is applied as
+//                                   (-M) (T00 X) with -M a pair
+//     W = T left_k, U = T V         single (the T00 U part a pair inside
+//                                   the T10 correction)
 //     u: W S'                       single
 //     O: left_q S'  pair x pair;    P u   pair x pair
 //     state: right_k^T u            pair x pair
@@ -67,7 +73,7 @@ constexpr int TILE = 32;   // rows per chunk tile
 constexpr int NW = 8;      // waves per workgroup
 constexpr int NT = 64 * NW;
 constexpr int MID = 15;    // reference row of the gates
-constexpr int GATE_WAVES = 4;  // waves that form the next chunk's gates during the solve
+constexpr int GATE_WAVES = 2;  // waves that form the next chunk's gates during the solve
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
@@ -102,7 +108,7 @@ __device__ __forceinline__ int launder(int x) {
   return x;
 }
 
-__device__ __forceinline__ float fexp(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
+constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ bf16x8 frag_lds(const bf16_t* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
@@ -135,38 +141,66 @@ __device__ __forceinline__ void st8b(bf16_t* p, const float* x) {
   *reinterpret_cast<uint4*>(p) = u;
 }
 
-// x broadcast from lane S of each row of 16 lanes (DPP row_newbcast)
+// x += bcast_S(x) * a, where bcast_S(x) is x of lane S of the lane's row of
+// 16 lanes: one v_fmac_f32 with a DPP row_newbcast source.  A DPP source
+// must not be written by either of the two preceding VALU instructions; the
+// callers interleave at least three independent updates between writes.
 template <int S>
-__device__ __forceinline__ float bcast16(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x150 + S, 0xF, 0xF, true));
+__device__ __forceinline__ void fmac_bcast16(float& x, float a) {
+  asm volatile("v_fmac_f32_dpp %0, %0, %1 row_newbcast:%2 row_mask:0xf bank_mask:0xf" : "+v"(x) : "v"(a), "n"(S));
 }
 
 // Forward substitution down the 16 lanes of each lane row: lane r holds x_r
-// of one right-hand side and na[s] = -L[r][s] of the unit lower triangular L
-// (zero for s >= r); steps S..14 apply x_r += na[s] x_s with x_s final.
+// of NG right-hand sides per system and na[s] = -L[r][s] of the unit lower
+// triangular L (zero for s >= r); steps S..14 apply x_r += na[s] x_s with
+// x_s final.  Two independent systems (x, na) and (y, nb) are interleaved.
 template <int S, int NG>
-__device__ __forceinline__ void fsub16(float (&x)[NG], const float (&na)[16]) {
+__device__ __forceinline__ void fsub16x2(float (&x)[NG], const float (&na)[16], float (&y)[NG], const float (&nb)[16]) {
   if constexpr (S < 15) {
 #pragma unroll
-    for (int g = 0; g < NG; ++g) x[g] = __builtin_fmaf(na[S], bcast16<S>(x[g]), x[g]);
+    for (int g = 0; g < NG; ++g) fmac_bcast16<S>(x[g], na[S]);
+#pragma unroll
+    for (int g = 0; g < NG; ++g) fmac_bcast16<S>(y[g], nb[S]);
+    fsub16x2<S + 1, NG>(x, na, y, nb);
+  }
+}
+template <int S, int NG>
+__device__ __forceinline__ void fsub16(float (&x)[NG], const float (&na)[16]) {
+  static_assert(NG >= 3, "DPP source hazard: at least three interleaved updates");
+  if constexpr (S < 15) {
+#pragma unroll
+    for (int g = 0; g < NG; ++g) fmac_bcast16<S>(x[g], na[S]);
     fsub16<S + 1, NG>(x, na);
   }
 }
 
+// hi / lo bf16 pair of two floats, each packed in 32 bits: hi = bf16(x),
+// lo = bf16(x - hi); the packed hi is unpacked by shifts, not converted back
+__device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t& lo) {
+  hi = cvt2(a, b);
+  lo = cvt2(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xffff0000u));
+}
+
 // fragment (and hi / lo pair) from two vertically adjacent accumulator tiles
 __device__ __forceinline__ void frag_pair(const f32x4& a, const f32x4& b, bf16x8& hi, bf16x8& lo) {
-  const float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-  float h[8], l[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    h[i] = hi_of(x[i]);
-    l[i] = x[i] - h[i];
-  }
   uint4 uh, ul;
-  uh.x = cvt2(h[0], h[1]); uh.y = cvt2(h[2], h[3]); uh.z = cvt2(h[4], h[5]); uh.w = cvt2(h[6], h[7]);
-  ul.x = cvt2(l[0], l[1]); ul.y = cvt2(l[2], l[3]); ul.z = cvt2(l[4], l[5]); ul.w = cvt2(l[6], l[7]);
+  split2(a[0], a[1], uh.x, ul.x);
+  split2(a[2], a[3], uh.y, ul.y);
+  split2(b[0], b[1], uh.z, ul.z);
+  split2(b[2], b[3], uh.w, ul.w);
   hi = __builtin_bit_cast(bf16x8, uh);
   lo = __builtin_bit_cast(bf16x8, ul);
+}
+
+// 8 floats as hi / lo bf16 pairs (16 bytes each)
+__device__ __forceinline__ void st8b_pair(bf16_t* ph, bf16_t* pl, const float* x) {
+  uint4 uh, ul;
+  split2(x[0], x[1], uh.x, ul.x);
+  split2(x[2], x[3], uh.y, ul.y);
+  split2(x[4], x[5], uh.z, ul.z);
+  split2(x[6], x[7], uh.w, ul.w);
+  *reinterpret_cast<uint4*>(ph) = uh;
+  *reinterpret_cast<uint4*>(pl) = ul;
 }
 
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -224,32 +258,44 @@ struct Smem {
   static constexpr bool F32IN = sizeof(TIN) == 4;
   static constexpr int PD = D + 16;   // padded pitch of [TILE][D] bf16 tiles
   static constexpr int PT = TILE + 8; // padded pitch of [TILE][TILE] bf16 tiles
-  static constexpr int PO = D + 16 / static_cast<int>(sizeof(TOUT));  // padded pitch of the output tile
-  alignas(16) TOUT ostg[TILE][PO];  // scaled outputs of the previous chunk, stored during the next one
-  alignas(16) bf16_t lq_hi[TILE][PD];     // [r][pos32(c)]
-  bf16_t lq_lo[TILE][PD];
-  bf16_t lk[TILE][PD];        // [r][pos32(c)]
-  bf16_t lk_lo[F32IN ? TILE : 1][PD];
-  bf16_t rk_hi[TILE][PD];     // [s][pos32(c)]
-  bf16_t rk_lo[TILE][PD];
+  // bf16 outputs are staged for 16-byte stores (padded pitch); fp32 outputs
+  // leave from registers (64-byte row segments) and need no tile
+  static constexpr bool STAGE_O = sizeof(TOUT) == 2;
+  static constexpr int PO = D + 8;
+  alignas(16) TOUT ostg[STAGE_O ? TILE : 1][PO];  // scaled outputs of a chunk, stored in the same step
+  // gated operands: two copies, by chunk parity (those of the next chunk
+  // are formed while the current chunk's are still read)
+  alignas(16) bf16_t lq_hi[2][TILE][PD];  // [r][pos32(c)]
+  bf16_t lq_lo[2][TILE][PD];
+  bf16_t rk_hi[2][TILE][PD];  // [s][pos32(c)]
+  bf16_t rk_lo[2][TILE][PD];
+  bf16_t lk[2][TILE][PD];     // [r][pos32(c)]
+  bf16_t lk_lo[2][F32IN ? TILE : 1][PD];
+  bf16_t P_hi[TILE][PT];      // [r][pos32(s)]
+  bf16_t P_lo[TILE][PT];
   bf16_t v_hi[TILE][PD];      // [s][n]
   bf16_t v_lo[F32IN ? TILE : 1][PD];
   alignas(16) float eg_m[2][D];           // exp(G_m), by chunk parity
   alignas(16) float eg_e[2][D];           // exp(G_last - G_m), by chunk parity
-  alignas(16) TIN g_raw[TILE][D];         // raw gates of the next chunk
-  alignas(16) float G[TILE][D];           // cumulative gates of the next chunk
+  alignas(16) float eg_c[2][D];           // exp(G_last - G_m) of the chunk before times exp(G_m)
+  alignas(16) float G[TILE][D];           // cumulative gates (log2 units) of the next chunk
   float beta[2][TILE];                    // by chunk parity
+  bf16_t Tb[TILE][PT];                    // T = (I + A)^{-1} diag(beta) [r][s], block (1,0) zero
+  bf16_t Tb_lo[F32IN ? TILE : 1][PT];
+  alignas(16) bf16_t Mb[16][PT];          // -M = -L_1^{-1} A10: hi in columns 0..15, lo in 16..31
+
+  alignas(16) TIN g_raw[TILE][D];         // raw gates of the next chunk
   union {
+    // the solve: 16x16 blocks of A, transposed ([c][r] = A[r][c]), in the
+    // waves that form them (3: A00; 4: A10, A11; 5: A11)
     struct {
-      alignas(16) float At[TILE][TILE + 4];  // At[s][r] = beta_r <left_k[r], right_k[s]>, s < r
-      bf16_t P_hi[TILE][PT];  // [r][pos32(s)]
-      bf16_t P_lo[TILE][PT];
+      float At[4][16][17];
+    } x;
+    // from the W product to the chain
+    struct {
       bf16_t Wn[TILE][PD];    // -(T left_k) [r][pos32(c)]
       bf16_t Wn_lo[F32IN ? TILE : 1][PD];
-      alignas(16) float Tf[16][20];       // T00 (fp32)
-      bf16_t Tb[TILE][PT];                // T = (I + A)^{-1} diag(beta) [r][s]
-      bf16_t Tb_lo[F32IN ? TILE : 1][PT];
-    } b;
+    } w;
   } u;
 };
 
@@ -389,16 +435,20 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
   const int c0 = 32 * (ib >> 2) + 4 * (ib & 3);
 
   // Raw rows in registers.  Item (row ir, position block ib) holds channels
-  // c0..c0+3 and c0+16..c0+19: q and k of the next chunk (consumed by its
-  // gated-operand phase), g and v (and beta of row tid) of the chunk after
-  // the current one, committed to LDS one chunk ahead.
+  // c0..c0+3 and c0+16..c0+19 of a row: q and k of the chunk after next
+  // (consumed by its gated operands at the end of a step), v of the next
+  // chunk and g (with beta of row tid) of the chunk after it, each committed
+  // to LDS at the start of a step.
   struct QKRow {
     uint2 q[2 * NU], k[2 * NU];
   } qk;
-  struct GVRow {
-    uint2 g[2 * NU], v[2 * NU];
+  struct GRow {
+    uint2 g[2 * NU];
     TIN b;
-  } gv;
+  } gr;
+  struct VRow {
+    uint2 v[2 * NU];
+  } vr;
   // Registers that receive a load are never written by ALU code before the
   // load is known complete (that write would wait for every memory
   // operation in flight): rows outside the sequence are masked where the
@@ -423,28 +473,35 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
       }
     }
   };
-  auto load_gv = [&](int64_t base) {
+  auto load_g = [&](int64_t base) {
     const int64_t pos = base + ir;
-    const bool with_v = mode != kModeTransition;   // the transition runs with v = 0
     if (row_ok(pos)) {
       const int64_t tok = bos + (pos - start);
-      const int64_t off = static_cast<int64_t>(h) * d + c0;
-      const TIN* vp = vg + tok * p.v_stride + off;
-      const TIN* gp = gg + tok * p.g_stride + off;
+      const TIN* gp = gg + tok * p.g_stride + static_cast<int64_t>(h) * d + c0;
       const bool second = c0 + 16 < d;
 #pragma unroll
       for (int w = 0; w < NU; ++w) {
-        if (with_v) gv.v[w] = reinterpret_cast<const uint2*>(vp)[w];
-        gv.g[w] = reinterpret_cast<const uint2*>(gp)[w];
-        if (second) {
-          if (with_v) gv.v[NU + w] = reinterpret_cast<const uint2*>(vp + 16)[w];
-          gv.g[NU + w] = reinterpret_cast<const uint2*>(gp + 16)[w];
-        }
+        gr.g[w] = reinterpret_cast<const uint2*>(gp)[w];
+        if (second) gr.g[NU + w] = reinterpret_cast<const uint2*>(gp + 16)[w];
       }
     }
     // beta stays in raw input bits until it is committed
     const int64_t bpos = base + tid;
-    if (tid < CH && bpos >= lo && bpos < hi) gv.b = bg[(bos + (bpos - start)) * p.beta_stride + h];
+    if (tid < CH && bpos >= lo && bpos < hi) gr.b = bg[(bos + (bpos - start)) * p.beta_stride + h];
+  };
+  auto load_v = [&](int64_t base) {
+    const int64_t pos = base + ir;
+    // the transition runs with v = 0
+    if (row_ok(pos) && mode != kModeTransition) {
+      const int64_t tok = bos + (pos - start);
+      const TIN* vp = vg + tok * p.v_stride + static_cast<int64_t>(h) * d + c0;
+      const bool second = c0 + 16 < d;
+#pragma unroll
+      for (int w = 0; w < NU; ++w) {
+        vr.v[w] = reinterpret_cast<const uint2*>(vp)[w];
+        if (second) vr.v[NU + w] = reinterpret_cast<const uint2*>(vp + 16)[w];
+      }
+    }
   };
   // (uint2 pair of one 4-channel group) or zeros
   auto masked = [](const uint2& x, bool ok) { return ok ? x : make_uint2(0, 0); };
@@ -454,14 +511,14 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
       const bool ok = row_ok(nbase + ir), ok2 = ok && c0 + 16 < d;
 #pragma unroll
       for (int w = 0; w < NU; ++w) {
-        reinterpret_cast<uint2*>(&sm.g_raw[ir][c0])[w] = masked(gv.g[w], ok);
-        reinterpret_cast<uint2*>(&sm.g_raw[ir][c0 + 16])[w] = masked(gv.g[NU + w], ok2);
+        reinterpret_cast<uint2*>(&sm.g_raw[ir][c0])[w] = masked(gr.g[w], ok);
+        reinterpret_cast<uint2*>(&sm.g_raw[ir][c0 + 16])[w] = masked(gr.g[NU + w], ok2);
       }
     }
     if (tid < TILE) {
       const int64_t bpos = nbase + tid;
       const bool ok = tid < CH && bpos >= lo && bpos < hi;
-      sm.beta[npar][tid] = ok ? io<TIN>::ld(&gv.b) : 0.f;
+      sm.beta[npar][tid] = ok ? io<TIN>::ld(&gr.b) : 0.f;
     }
   };
   // v of chunk nbase -> LDS (after the current W / U products)
@@ -471,8 +528,8 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
       uint2 vv[2 * NU];
 #pragma unroll
       for (int w = 0; w < NU; ++w) {
-        vv[w] = masked(gv.v[w], ok);
-        vv[NU + w] = masked(gv.v[NU + w], ok2);
+        vv[w] = masked(vr.v[w], ok);
+        vv[NU + w] = masked(vr.v[NU + w], ok2);
       }
       if constexpr (HP) {
         float vx[8], vh[8], vl[8];
@@ -493,7 +550,8 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
     }
   };
   // G = inclusive cumulative sum of g down the chunk rows, per key channel,
-  // from g_raw; exp(G_m) and exp(G_last - G_m) into eg[par].  Run by
+  // from g_raw, kept in log2 units (g log2 e summed); exp(G_m) and
+  // exp(G_last - G_m) into eg[par].  Run by
   // GATE_WAVES waves (gw = 0 ..): each takes D / GATE_WAVES channels, each
   // lane a run of RP rows of one channel; the runs are chained by a scan
   // across the lanes of the wave.
@@ -507,7 +565,7 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
     float acc = 0.f;
 #pragma unroll
     for (int i = 0; i < RP; ++i) {
-      acc += io<TIN>::ld(&sm.g_raw[part * RP + i][c]);
+      acc += io<TIN>::ld(&sm.g_raw[part * RP + i][c]) * kLog2e;
       gl[i] = acc;
     }
     float incl = acc;
@@ -523,8 +581,11 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
     const float gm = __shfl(gl[MID % RP] + off, (MID / RP) * CPW + lane % CPW, 64);
     const float ge = __shfl(gl[RP - 1] + off, (NPART - 1) * CPW + lane % CPW, 64);
     if (part == 0) {
-      sm.eg_m[par][c] = expf(gm);
-      sm.eg_e[par][c] = expf(ge - gm);
+      const float em = __builtin_amdgcn_exp2f(gm);
+      sm.eg_m[par][c] = em;
+      sm.eg_e[par][c] = __builtin_amdgcn_exp2f(ge - gm);
+      // this lane wrote eg_e of the chunk before (same channel)
+      sm.eg_c[par][c] = sm.eg_e[par ^ 1][c] * em;
     }
   };
 
@@ -533,6 +594,7 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
   auto store_out = [&](int64_t obase) {
     constexpr int OV = 16 / sizeof(TOUT);   // elements per vector
     constexpr int NOV = D / OV;             // vectors per row
+    if constexpr (SM::STAGE_O)
     for (int it = static_cast<int>(threadIdx.x); it < TILE * NOV; it += NT) {
       const int r = it / NOV;
       const int cc = (it % NOV) * OV;
@@ -544,39 +606,20 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
       }
     }
   };
-  // prologue: the first chunk's g, v, beta in LDS, its gates, q / k in
-  // registers, and the second chunk's g, v, beta requested
-  if (hi > lo) {
-    load_gv(first);
-    load_qk(first);
-    commit_g(first, 0);
-    commit_v(first);
-    lds_barrier();
-    if (wave < GATE_WAVES) gates(0, wave);
-    if (first + CH < hi) load_gv(first + CH);
-    lds_barrier();
-  }
-  auto chunk = [&](const int64_t base, const int par) __attribute__((always_inline)) {
-    // Per-thread indices are derived again in every chunk from an opaque copy
-    // of the thread id; otherwise every LDS address derived from them would be
-    // hoisted out of this loop and held in a register for the whole sequence.
-    const int tid = launder(static_cast<int>(threadIdx.x));
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int g4 = lane >> 4;
-    const int l16 = lane & 15;
-    const bool chain = wave < NWC;
-    const int ncol = 16 * wave + l16;
-    const bool has_item = tid < NITEM;
+  // Gated operands of chunk c (parity par) from its q / k rows in registers
+  // and its cumulative gates:
+  //   left_q = q exp(G_r - G_m), left_k = k exp(G_r - G_m), right_k = k exp(G_m - G_r)
+  // (row-major, position 8 ib + e holds channel c0 + e (e < 4) or
+  // c0 + 16 + e - 4).  Then the q / k request of chunk c + CH, issued after
+  // this chunk's rows are consumed so that no wait covers it.
+  auto gated_operands = [&](const int64_t c, const int par, const int tid) __attribute__((always_inline)) {
     const int ir = tid / NPB;
     const int ib = tid % NPB;
     const int c0 = 32 * (ib >> 2) + 4 * (ib & 3);
-    const bool more = base + CH < hi;
-    // ------------------------------------------------ phase O: gated operands (row-major)
-    if (has_item) {
+    if (NITEM >= NT || tid < NITEM) {
       float qx[8], kx[8];
       {
-        const bool ok = row_ok(base + ir), ok2 = ok && c0 + 16 < d;
+        const bool ok = row_ok(c + ir), ok2 = ok && c0 + 16 < d;
         uint2 qq[2 * NU], kk[2 * NU];
 #pragma unroll
         for (int w = 0; w < NU; ++w) {
@@ -588,60 +631,234 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
         to_f32<TIN>(qq, qx);
         to_f32<TIN>(kk, kx);
       }
-      // positions 8 ib + e hold channels c0 + e (e < 4) and c0 + 16 + e - 4
       float lq[8], lk[8], rk[8];
 #pragma unroll
       for (int gi = 0; gi < 2; ++gi) {
         const int cc = c0 + 16 * gi;
         const float4 a = *reinterpret_cast<const float4*>(&sm.G[ir][cc]);
-        const float4 b = *reinterpret_cast<const float4*>(&sm.G[MID][cc]);
-        const float x4[4] = {a.x - b.x, a.y - b.y, a.z - b.z, a.w - b.w};
+        const float4 m4 = *reinterpret_cast<const float4*>(&sm.G[MID][cc]);
+        const float x4[4] = {a.x - m4.x, a.y - m4.y, a.z - m4.z, a.w - m4.w};
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const int i = 4 * gi + m;
-          const float ea = fexp(x4[m]);
+        for (int mm = 0; mm < 4; ++mm) {
+          const int i = 4 * gi + mm;
+          const float ea = __builtin_amdgcn_exp2f(x4[mm]);
           lq[i] = qx[i] * ea;
           lk[i] = kx[i] * ea;
-          rk[i] = kx[i] * fexp(-x4[m]);
+          rk[i] = kx[i] * __builtin_amdgcn_exp2f(-x4[mm]);
         }
       }
       const int pp = 8 * ib;
-      float hi[8], lo[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        hi[i] = hi_of(lq[i]);
-        lo[i] = lq[i] - hi[i];
-      }
-      st8b(&sm.lq_hi[ir][pp], hi);
-      st8b(&sm.lq_lo[ir][pp], lo);
+      st8b_pair(&sm.lq_hi[par][ir][pp], &sm.lq_lo[par][ir][pp], lq);
       if constexpr (HP) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          hi[i] = hi_of(lk[i]);
-          lo[i] = lk[i] - hi[i];
-        }
-        st8b(&sm.lk[ir][pp], hi);
-        st8b(&sm.lk_lo[ir][pp], lo);
+        st8b_pair(&sm.lk[par][ir][pp], &sm.lk_lo[par][ir][pp], lk);
       } else {
-        st8b(&sm.lk[ir][pp], lk);
+        st8b(&sm.lk[par][ir][pp], lk);
       }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        hi[i] = hi_of(rk[i]);
-        lo[i] = rk[i] - hi[i];
-      }
-      st8b(&sm.rk_hi[ir][pp], hi);
-      st8b(&sm.rk_lo[ir][pp], lo);
+      st8b_pair(&sm.rk_hi[par][ir][pp], &sm.rk_lo[par][ir][pp], rk);
     }
-    // outputs of the previous chunk (staged at its end), then the next
-    // chunk's q / k: both after this chunk's q / k are consumed, so that the
-    // wait for those covers neither
-    if (outputs && base != first) store_out(base - CH);
-    if (more) load_qk(base + CH);
+    load_qk(c + CH);   // rows past the end of the item load nothing
+  };
+
+  // prologue: the first chunk's g and beta in LDS, its gates and gated
+  // operands formed; in registers its v, the second chunk's g / beta and q / k
+  if (hi > lo) {
+    load_v(first);
+    load_g(first);
+    load_qk(first);
+    commit_g(first, 0);
+    load_g(first + CH);
     lds_barrier();
-    // ------------------------------------------------ phase AP: A and P (16x16 tiles)
-    {
-      const int kq = 8 * g4;   // k offset of this lane inside a 32-wide K step
+    if (wave < GATE_WAVES) gates(0, wave);
+    lds_barrier();
+    gated_operands(first, 0, tid);
+    lds_barrier();
+  }
+  // Interval checkpoint taken after position `after` (absolute): its index
+  // in the checkpoint table, or -1
+  auto ckpt_index = [&](const int64_t after) -> int64_t {
+    if (!outputs || p.ckpt_interval <= 0 || !p.ckpt_cu) return -1;
+    if (after >= end || after % p.ckpt_interval != 0) return -1;
+    const int64_t j = after / p.ckpt_interval - start / p.ckpt_interval - 1;
+    const int64_t idx = static_cast<int64_t>(p.ckpt_cu[s]) + j;
+    return (j >= 0 && idx < p.ckpt_cu[s + 1] && idx < p.n_ckpt) ? idx : -1;
+  };
+  // S = Diag(f) S on a chain wave's slice
+  auto scale_state = [&](const float* f, const int g4_) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const float4 x = *reinterpret_cast<const float4*>(&f[16 * q + 4 * g4_]);
+      S[q][0] *= x.x; S[q][1] *= x.y; S[q][2] *= x.z; S[q][3] *= x.w;
+    }
+  };
+  // the state enters the first chunk scaled by its exp(G_m)
+  if (hi > lo && chain) scale_state(sm.eg_m[0], g4);
+  // U = T V of the chunk whose chain runs next (own d_v columns)
+  f32x4 U[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+
+  // One pipeline step: the chain of chunk n (parity cp) runs alongside the
+  // chunk-local stages of chunk b = n + CH (parity lp = cp ^ 1), which need
+  // nothing from the state.  Three phases separated by workgroup barriers:
+  //   I    chain of n: state update, outputs  | v of b, g / beta of b + CH to LDS;
+  //                                           | their requests for b + CH, b + 2 CH
+  //   II   outputs of n stored                | P and T of b (A inside the solve waves);
+  //                                           | gates of b + CH
+  //   III                                     | W = T left_k, U = T V of b;
+  //                                           | gated operands of b + CH
+  // CHAIN = false runs the local stages of the first chunk alone; MORE =
+  // false (no chunk b) the chain alone.
+  auto step = [&](const int64_t n, const int cp, auto chain_t, auto more_t, auto out_t) __attribute__((always_inline)) {
+    constexpr bool CHAIN = decltype(chain_t)::value;
+    constexpr bool MORE = decltype(more_t)::value;
+    constexpr bool WITH_O = decltype(out_t)::value;
+    const int lp = cp ^ 1;
+    const int64_t b = n + CH;
+    const bool more2 = b + CH < hi;      // a chunk after b exists
+    // Per-thread indices are derived again in every step from an opaque copy
+    // of the thread id; otherwise every LDS address derived from them would be
+    // hoisted out of the loop and held in a register for the whole sequence.
+    const int tid = launder(static_cast<int>(threadIdx.x));
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g4 = lane >> 4;
+    const int l16 = lane & 15;
+    const int kq = 8 * g4;   // k offset of this lane inside a 32-wide K step
+    const bool chain = NWC == NW || wave < NWC;
+    const int ncol = 16 * wave + l16;
+    const int64_t ck = CHAIN ? ckpt_index(n + CH) : -1;
+
+    // ================================================ phase I
+    if constexpr (MORE) {
+      // v of chunk b and g / beta of chunk b + CH to LDS, then the requests
+      // of v of b + CH and g / beta of b + 2 CH (rows past the end of the
+      // item load nothing); first in the step, so that no store of this step
+      // is pending at the wait for the rows
+      commit_v(b);
+      if (more2) commit_g(b + CH, cp);
+      load_v(b + CH);
+      load_g(b + 2 * CH);
+    }
+    if (CHAIN && chain) {
+      // The LDS fragments of each product are read one stage ahead, behind
+      // scheduling fences, so that their latency hides behind the work
+      // before the product instead of stalling each matrix operation.
+      // W fragments, read while S' = Diag(exp G_m) S (the register state
+      // enters the chunk already scaled) becomes bf16 pair fragments
+      bf16x8 wf[NQ / 2][2];
+#pragma unroll
+      for (int ks = 0; ks < NQ / 2; ++ks)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) wf[ks][mt] = frag_lds(&sm.u.w.Wn[16 * mt + l16][32 * ks + kq]);
+      __builtin_amdgcn_sched_barrier(0);
+      bf16x8 sh[NQ / 2], sl[NQ / 2], uh, ul;
+#pragma unroll
+      for (int ks = 0; ks < NQ / 2; ++ks) frag_pair(S[2 * ks], S[2 * ks + 1], sh[ks], sl[ks]);
+      // u = U - W S'
+#pragma unroll
+      for (int ks = 0; ks < NQ / 2; ++ks) {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          U[mt] = mfma(wf[ks][mt], sh[ks], U[mt]);
+          if constexpr (HP) {
+            U[mt] = mfma(wf[ks][mt], sl[ks], U[mt]);
+            U[mt] = mfma(frag_lds(&sm.u.w.Wn_lo[16 * mt + l16][32 * ks + kq]), sh[ks], U[mt]);
+          }
+        }
+      }
+      // right_k^T fragments (transpose reads of right_k [s][pos32(c)]: rows
+      // follow u's order, columns are picked so that lane l16 receives
+      // channel 16 q + l16), read while u becomes a pair
+      bf16x8 kh[NQ], kl[NQ];
+      {
+        const int j = (lane >> 2) & 3, i = lane & 3;
+        const int ra = 4 * g4 + j;      // rows for slots 0..3; ra + 16 for slots 4..7
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+          const int col = 32 * (q >> 1) + 4 * (q & 1) + 8 * i;
+          kh[q] = join(tr4(&sm.rk_hi[cp][ra][col]), tr4(&sm.rk_hi[cp][ra + 16][col]));
+          kl[q] = join(tr4(&sm.rk_lo[cp][ra][col]), tr4(&sm.rk_lo[cp][ra + 16][col]));
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // u (in U) as a pair over the 32 chunk rows
+      frag_pair(U[0], U[1], uh, ul);
+      // S' + right_k^T u, with the output operands read behind it
+      bf16x8 qf[NQ / 2][2][2], pf[2][2];
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        S[q] = mfma(kh[q], uh, S[q]);
+        S[q] = mfma(kh[q], ul, S[q]);
+        S[q] = mfma(kl[q], uh, S[q]);
+        if constexpr (WITH_O) {
+          // two of the output fragments per state tile
+          const int ks = q >> 1, mt = q & 1, row = 16 * mt + l16;
+          qf[ks][mt][0] = frag_lds(&sm.lq_hi[cp][row][32 * ks + kq]);
+          qf[ks][mt][1] = frag_lds(&sm.lq_lo[cp][row][32 * ks + kq]);
+          if (q < 2) {
+            pf[q][0] = frag_lds(&sm.P_hi[16 * q + l16][kq]);
+            pf[q][1] = frag_lds(&sm.P_lo[16 * q + l16][kq]);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if constexpr (WITH_O) {
+        // O = scale (left_q S' + P u) with three independent accumulators for
+        // the pair terms, staged in LDS
+        f32x4 O[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        f32x4 Ob[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        f32x4 Oc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int ks = 0; ks < NQ / 2; ++ks) {
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt) {
+            O[mt] = mfma(qf[ks][mt][0], sh[ks], O[mt]);
+            Ob[mt] = mfma(qf[ks][mt][0], sl[ks], Ob[mt]);
+            Oc[mt] = mfma(qf[ks][mt][1], sh[ks], Oc[mt]);
+          }
+        }
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          O[mt] = mfma(pf[mt][0], uh, O[mt]);
+          Ob[mt] = mfma(pf[mt][0], ul, Ob[mt]);
+          Oc[mt] = mfma(pf[mt][1], uh, Oc[mt]);
+        }
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 16 * mt + 4 * g4 + e;
+            const float ov = (O[mt][e] + Ob[mt][e] + Oc[mt][e]) * p.scale;
+            if constexpr (SM::STAGE_O) {
+              io<TOUT>::st(&sm.ostg[r][ncol], ov);
+            } else {
+              const int64_t pos = n + r;
+              if (r < CH && pos >= lo && pos < hi && ncol < d)
+                io<TOUT>::st(og + (bos + (pos - start)) * p.o_stride + static_cast<int64_t>(h) * d + ncol, ov);
+            }
+          }
+      }
+      // S = Diag(exp(G_last - G_m)) (S' + right_k^T u) is the state after
+      // chunk n; it enters chunk b as Diag(exp G_m(b)) S, both factors in one
+      // product unless the state after n is stored
+      if (MORE && ck < 0) {
+        scale_state(sm.eg_c[lp], g4);
+      } else {
+        scale_state(sm.eg_e[cp], g4);
+        if (ck >= 0) {
+          const int slot = p.ckpt_slot[ck];
+          if (slot >= 0 && slot < p.n_slots && ncol < d)
+            state_store<D>(p.pool + (static_cast<int64_t>(slot) * H + h) * d * d, S, lane, ncol, d);
+        }
+        if constexpr (MORE) scale_state(sm.eg_m[lp], g4);
+      }
+    }
+    if (CHAIN && ck >= 0 && tid == 0 && h == 0 && p.ckpt_pos_out) p.ckpt_pos_out[ck] = static_cast<int32_t>(n + CH);
+    lds_barrier();
+    // ================================================ phase II
+    // outputs of chunk n (no wait for a prefetched row follows before the
+    // next phase: a wait on a load while stores are pending covers every
+    // outstanding memory operation)
+    if constexpr (CHAIN && WITH_O && SM::STAGE_O) store_out(n);
+    if constexpr (MORE) {
       if (wave < 3) {
         // P tile per wave: 0 -> (0,0), 1 -> (1,0), 2 -> (1,1); lower incl. diagonal
         const int I = wave == 0 ? 0 : 1;
@@ -649,11 +866,11 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < D / 32; ++ks) {
-          const bf16x8 ah = frag_lds(&sm.lq_hi[16 * I + l16][32 * ks + kq]);
-          const bf16x8 bh = frag_lds(&sm.rk_hi[16 * J + l16][32 * ks + kq]);
+          const bf16x8 ah = frag_lds(&sm.lq_hi[lp][16 * I + l16][32 * ks + kq]);
+          const bf16x8 bh = frag_lds(&sm.rk_hi[lp][16 * J + l16][32 * ks + kq]);
           acc = mfma(ah, bh, acc);
-          acc = mfma(ah, frag_lds(&sm.rk_lo[16 * J + l16][32 * ks + kq]), acc);
-          acc = mfma(frag_lds(&sm.lq_lo[16 * I + l16][32 * ks + kq]), bh, acc);
+          acc = mfma(ah, frag_lds(&sm.rk_lo[lp][16 * J + l16][32 * ks + kq]), acc);
+          acc = mfma(frag_lds(&sm.lq_lo[lp][16 * I + l16][32 * ks + kq]), bh, acc);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -661,276 +878,191 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
           const int c = 16 * J + l16;
           const float v = c <= r ? acc[i] : 0.f;
           const float hv = hi_of(v);
-          sm.u.b.P_hi[r][pos32(c)] = f32_to_bf16(hv);
-          sm.u.b.P_lo[r][pos32(c)] = f32_to_bf16(v - hv);
+          sm.P_hi[r][pos32(c)] = f32_to_bf16(hv);
+          sm.P_lo[r][pos32(c)] = f32_to_bf16(v - hv);
+          if (wave == 0) {   // block (0,1) of P is zero
+            sm.P_hi[4 * g4 + i][pos32(16 + l16)] = 0;
+            sm.P_lo[4 * g4 + i][pos32(16 + l16)] = 0;
+          }
         }
       } else if (wave < 6) {
-        // A tile per wave: 3 -> (0,0), 4 -> (1,0), 5 -> (1,1); strictly lower, scaled by beta_row
-        const int I = wave == 3 ? 0 : 1;
-        const int J = wave == 5 ? 1 : 0;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        // T = (I + A)^{-1} diag(beta) blockwise on the 16-row blocks, with
+        // L_bb = I + A_bb:  T_bb = L_bb^{-1} diag(beta_bb), and
+        // T10 = -M T00 with M = L_1^{-1} A10, which the W / U products apply
+        // as a correction of the second row block.  Inverses by fp32 forward
+        // substitution down the 16 lanes of a lane row (lane (g4, r) holds
+        // row r of column 4 g + g4, g = 0..3).  Each wave forms the blocks of
+        // A = strict-lower(diag(beta) left_k right_k^T) it needs: wave 3 A00
+        // (-> T00), wave 4 A10, A11 (-> M), wave 5 A11 (-> T11).
+        // A block (I, J) into the wave's LDS tile t, transposed:
+        // At[t][c][r] = beta_r <left_k[16 I + r], right_k[16 J + c]>
+        auto a_block = [&](const int I, const int J, const int t) __attribute__((always_inline)) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < D / 32; ++ks) {
-          const bf16x8 a = frag_lds(&sm.lk[16 * I + l16][32 * ks + kq]);
-          const bf16x8 b = frag_lds(&sm.rk_hi[16 * J + l16][32 * ks + kq]);
-          acc = mfma(a, b, acc);
-          if constexpr (HP) {
-            acc = mfma(a, frag_lds(&sm.rk_lo[16 * J + l16][32 * ks + kq]), acc);
-            acc = mfma(frag_lds(&sm.lk_lo[16 * I + l16][32 * ks + kq]), b, acc);
+          for (int ks = 0; ks < D / 32; ++ks) {
+            const bf16x8 a = frag_lds(&sm.lk[lp][16 * I + l16][32 * ks + kq]);
+            const bf16x8 bb = frag_lds(&sm.rk_hi[lp][16 * J + l16][32 * ks + kq]);
+            acc = mfma(a, bb, acc);
+            if constexpr (HP) {
+              acc = mfma(a, frag_lds(&sm.rk_lo[lp][16 * J + l16][32 * ks + kq]), acc);
+              acc = mfma(frag_lds(&sm.lk_lo[lp][16 * I + l16][32 * ks + kq]), bb, acc);
+            }
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = 4 * g4 + i;
+            sm.u.x.At[t][l16][r] = (I > J || r > l16) ? acc[i] * sm.beta[lp][16 * I + r] : 0.f;
+          }
+        };
+        if (wave != 4) {
+          const int bb = wave == 3 ? 0 : 1;
+          const int t = wave == 3 ? 0 : 1;
+          a_block(bb, bb, t);
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+          __builtin_amdgcn_wave_barrier();
+          float na[16];
+#pragma unroll
+          for (int s2 = 0; s2 < 16; ++s2) na[s2] = -sm.u.x.At[t][s2][l16];
+          float x[4];
+#pragma unroll
+          for (int g = 0; g < 4; ++g) x[g] = l16 == 4 * g + g4 ? 1.f : 0.f;
+          // x was just written by VALU: two wait states before a DPP read
+          asm volatile("s_nop 1" ::"v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]));
+          fsub16<0, 4>(x, na);
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int j = 4 * g + g4;
+            const float tv = x[g] * sm.beta[lp][16 * bb + j];
+            const float th = hi_of(tv);
+            sm.Tb[16 * bb + l16][16 * bb + j] = f32_to_bf16(th);
+            if constexpr (HP) sm.Tb_lo[16 * bb + l16][16 * bb + j] = f32_to_bf16(tv - th);
+            // the off-diagonal blocks of Tb are zero
+            sm.Tb[16 * bb + l16][16 * (1 - bb) + j] = 0;
+            if constexpr (HP) sm.Tb_lo[16 * bb + l16][16 * (1 - bb) + j] = 0;
+          }
+        } else {
+          a_block(1, 0, 2);
+          a_block(1, 1, 3);
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+          __builtin_amdgcn_wave_barrier();
+          float na1[16];
+#pragma unroll
+          for (int s2 = 0; s2 < 16; ++s2) na1[s2] = -sm.u.x.At[3][s2][l16];
+          float m4[4];
+#pragma unroll
+          for (int g = 0; g < 4; ++g) m4[g] = sm.u.x.At[2][4 * g + g4][l16];   // A10[r][j]
+          // m4 was just written by a load: wait states before a DPP read
+          asm volatile("s_waitcnt lgkmcnt(0)\n\ts_nop 1" ::"v"(m4[0]), "v"(m4[1]), "v"(m4[2]), "v"(m4[3]));
+          fsub16<0, 4>(m4, na1);
+          // -M as a bf16 pair: hi in columns 0..15, lo in columns 16..31
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const float mv = -m4[g];
+            const float mh = hi_of(mv);
+            sm.Mb[l16][4 * g + g4] = f32_to_bf16(mh);
+            sm.Mb[l16][16 + 4 * g + g4] = f32_to_bf16(mv - mh);
           }
         }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 16 * I + 4 * g4 + i;
-          const int c = 16 * J + l16;
-          sm.u.b.At[c][r] = r > c ? acc[i] * sm.beta[par][r] : 0.f;
-        }
-      } else if (wave == 6) {
-        // tile (0,1) of A and P is zero
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 4 * g4 + i;
-          sm.u.b.At[16 + l16][r] = 0.f;
-          sm.u.b.P_hi[r][pos32(16 + l16)] = 0;
-          sm.u.b.P_lo[r][pos32(16 + l16)] = 0;
-        }
+      } else if (more2) {
+        // the gates of chunk b + CH
+        gates(cp, wave - (NW - GATE_WAVES));
       }
-    }
-    // the next chunk's g and beta (its gates are formed during phase X)
-    if (more) commit_g(base + CH, par ^ 1);
-    lds_barrier();
-    // ------------------------------------------------ phase X: T = (I + A)^{-1} diag(beta); W = T left_k, U = T V
-    // Blockwise on the 16-row blocks b, with L_b = I + A_bb:
-    //     T_bb = L_b^{-1} diag(beta_b),  T10 = -M T00,  M = L_1^{-1} A10,
-    // each inverse by fp32 forward substitution down the 16 lanes of a lane
-    // row (lane (g4, r) holds row r of column 4 g + g4, g = 0..3).
-    if (wave < 2) {
-      // T_bb = L_b^{-1} diag(beta_b), b = wave
-      const int b = wave;
-      float na[16];
-#pragma unroll
-      for (int s = 0; s < 16; ++s) na[s] = -sm.u.b.At[16 * b + s][16 * b + l16];
-      float x[4];
-#pragma unroll
-      for (int g = 0; g < 4; ++g) x[g] = l16 == 4 * g + g4 ? 1.f : 0.f;
-      fsub16<0, 4>(x, na);
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int j = 4 * g + g4;
-        const float t = x[g] * sm.beta[par][16 * b + j];
-        const float th = hi_of(t);
-        sm.u.b.Tb[16 * b + l16][16 * b + j] = f32_to_bf16(th);
-        if constexpr (HP) sm.u.b.Tb_lo[16 * b + l16][16 * b + j] = f32_to_bf16(t - th);
-      }
-    } else if (wave == 2) {
-      // T10 = -M T00 with M = L_1^{-1} A10: both factors by forward
-      // substitution in this wave, the product on fp32 matrix cores
-      float na0[16], na1[16];
-#pragma unroll
-      for (int s = 0; s < 16; ++s) {
-        na0[s] = -sm.u.b.At[s][l16];
-        na1[s] = -sm.u.b.At[16 + s][16 + l16];
-      }
-      float x[4], m[4];
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int j = 4 * g + g4;
-        x[g] = l16 == j ? 1.f : 0.f;
-        m[g] = sm.u.b.At[j][16 + l16];     // A10[r][j] = A[16 + r][j]
-      }
-      fsub16<0, 4>(x, na0);
-      fsub16<0, 4>(m, na1);
-      // T00 in LDS for the transposed operand; lane (g4, r) then reads
-      // T00[4 kb + g4][r] (this wave's own writes: its LDS operations complete
-      // in order)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) sm.u.b.Tf[l16][4 * g + g4] = x[g] * sm.beta[par][4 * g + g4];
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      __builtin_amdgcn_wave_barrier();
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(m[kb], sm.u.b.Tf[4 * kb + g4][l16], acc, 0, 0, 0);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float t = -acc[e];
-        const float th = hi_of(t);
-        sm.u.b.Tb[16 + 4 * g4 + e][l16] = f32_to_bf16(th);
-        if constexpr (HP) sm.u.b.Tb_lo[16 + 4 * g4 + e][l16] = f32_to_bf16(t - th);
-      }
-    } else if (wave == 3) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        sm.u.b.Tb[l16][16 + 4 * g + g4] = 0;
-        if constexpr (HP) sm.u.b.Tb_lo[l16][16 + 4 * g + g4] = 0;
-      }
-    } else if (more) {
-      // the next chunk's gates, on the waves the solve leaves free
-      gates(par ^ 1, wave - (NW - GATE_WAVES));
-    }
-    lds_barrier();
-    // W = T left_k (columns of this wave in storage order, kept as -W in LDS)
-    // and U = T V (own d_v columns, kept in registers)
-    f32x4 U[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-    if (chain) {
-      // B fragments over chunk rows s = 8 g4 + e (transpose reads), columns 16 wave + l16
-      const int j = (lane >> 2) & 3, i = lane & 3;
-      const int x0 = 16 * wave + 4 * i;
-      const int r0 = 8 * g4 + j;
-      const bf16x8 bk = join(tr4(&sm.lk[r0][x0]), tr4(&sm.lk[r0 + 4][x0]));
-      const bf16x8 bv = join(tr4(&sm.v_hi[r0][x0]), tr4(&sm.v_hi[r0 + 4][x0]));
-      bf16x8 bkl = bk, bvl = bv;
-      if constexpr (HP) {
-        bkl = join(tr4(&sm.lk_lo[r0][x0]), tr4(&sm.lk_lo[r0 + 4][x0]));
-        bvl = join(tr4(&sm.v_lo[r0][x0]), tr4(&sm.v_lo[r0 + 4][x0]));
-      }
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        const bf16x8 a = frag_lds(&sm.u.b.Tb[16 * mt + l16][8 * g4]);
-        f32x4 w = {0.f, 0.f, 0.f, 0.f};
-        w = mfma(a, bk, w);
-        U[mt] = mfma(a, bv, U[mt]);
-        if constexpr (HP) {
-          const bf16x8 al = frag_lds(&sm.u.b.Tb_lo[16 * mt + l16][8 * g4]);
-          w = mfma(a, bkl, w);
-          w = mfma(al, bk, w);
-          U[mt] = mfma(a, bvl, U[mt]);
-          U[mt] = mfma(al, bv, U[mt]);
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float wv = -w[e];
-          const float wh = hi_of(wv);
-          sm.u.b.Wn[16 * mt + 4 * g4 + e][16 * wave + l16] = f32_to_bf16(wh);
-          if constexpr (HP) sm.u.b.Wn_lo[16 * mt + 4 * g4 + e][16 * wave + l16] = f32_to_bf16(wv - wh);
-        }
-      }
-    }
-    lds_barrier();
-    // ------------------------------------------------ chain (per wave, own 16 columns)
-    f32x4 O[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-    // WITH_O: the recurrence alone (segment pass A) skips every product that
-    // only feeds the outputs.
-    auto chain_step = [&](auto with_o) {
-      constexpr bool WITH_O = decltype(with_o)::value;
-      const int kq = 8 * g4;
-      // S' = Diag(exp G_m) S, and its bf16 pair fragments (K steps of 32 channels)
-      bf16x8 sh[NQ / 2], sl[NQ / 2];
-#pragma unroll
-      for (int q = 0; q < NQ; ++q) {
-        const float4 f = *reinterpret_cast<const float4*>(&sm.eg_m[par][16 * q + 4 * g4]);
-        S[q][0] *= f.x; S[q][1] *= f.y; S[q][2] *= f.z; S[q][3] *= f.w;
-      }
-#pragma unroll
-      for (int ks = 0; ks < NQ / 2; ++ks) frag_pair(S[2 * ks], S[2 * ks + 1], sh[ks], sl[ks]);
-      // u = U - W S' ; O = left_q S'.  Three independent accumulators for the
-      // pair terms keep the matrix-core pipeline fed.
-      f32x4 Ob[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-      f32x4 Oc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-      for (int ks = 0; ks < NQ / 2; ++ks) {
-        bf16x8 w[2], qh[2], ql[2];
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-          const int row = 16 * mt + l16;
-          w[mt] = frag_lds(&sm.u.b.Wn[row][32 * ks + kq]);
-          if constexpr (WITH_O) {
-            qh[mt] = frag_lds(&sm.lq_hi[row][32 * ks + kq]);
-            ql[mt] = frag_lds(&sm.lq_lo[row][32 * ks + kq]);
-          }
-        }
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-          U[mt] = mfma(w[mt], sh[ks], U[mt]);
-          if constexpr (WITH_O) {
-            O[mt] = mfma(qh[mt], sh[ks], O[mt]);
-            Ob[mt] = mfma(qh[mt], sl[ks], Ob[mt]);
-            Oc[mt] = mfma(ql[mt], sh[ks], Oc[mt]);
-          }
-          if constexpr (HP) {
-            U[mt] = mfma(w[mt], sl[ks], U[mt]);
-            U[mt] = mfma(frag_lds(&sm.u.b.Wn_lo[16 * mt + l16][32 * ks + kq]), sh[ks], U[mt]);
-          }
-        }
-      }
-      // u (in U) as a pair over the 32 chunk rows
-      bf16x8 uh, ul;
-      frag_pair(U[0], U[1], uh, ul);
-      // O += P u
-#pragma unroll
-      for (int mt = 0; mt < 2 && WITH_O; ++mt) {
-        const bf16x8 ph = frag_lds(&sm.u.b.P_hi[16 * mt + l16][kq]);
-        const bf16x8 pl = frag_lds(&sm.u.b.P_lo[16 * mt + l16][kq]);
-        O[mt] = mfma(ph, uh, O[mt]);
-        Ob[mt] = mfma(ph, ul, Ob[mt]);
-        Oc[mt] = mfma(pl, uh, Oc[mt]);
-      }
-      // S = Diag(exp(G_last - G_m)) (S' + right_k^T u).  right_k^T fragments
-      // come from transpose reads of right_k [s][pos32(c)]: rows follow u's
-      // order, columns are picked so that lane l16 receives channel 16 q + l16.
-      {
+      lds_barrier();
+      // ================================================ phase III
+      // W = T left_k (columns of this wave in storage order, kept as -W in
+      // LDS) and U = T V (own d_v columns, kept in registers)
+      if (chain) {
+        // B fragments over chunk rows s = 8 g4 + e (transpose reads), columns 16 wave + l16
         const int j = (lane >> 2) & 3, i = lane & 3;
-        const int ra = 4 * g4 + j;      // rows for slots 0..3; ra + 16 for slots 4..7
+        const int x0 = 16 * wave + 4 * i;
+        const int r0 = 8 * g4 + j;
+        const bf16x8 bk = join(tr4(&sm.lk[lp][r0][x0]), tr4(&sm.lk[lp][r0 + 4][x0]));
+        const bf16x8 bv = join(tr4(&sm.v_hi[r0][x0]), tr4(&sm.v_hi[r0 + 4][x0]));
+        bf16x8 bkl = bk, bvl = bv;
+        if constexpr (HP) {
+          bkl = join(tr4(&sm.lk_lo[lp][r0][x0]), tr4(&sm.lk_lo[lp][r0 + 4][x0]));
+          bvl = join(tr4(&sm.v_lo[r0][x0]), tr4(&sm.v_lo[r0 + 4][x0]));
+        }
+        // M fragments (A operand of the 16x16x16 products: row l16, K = 4 g4 .. 4 g4 + 3)
+        const s16x4 mh = *reinterpret_cast<const s16x4*>(&sm.Mb[l16][4 * g4]);
+        const s16x4 ml = *reinterpret_cast<const s16x4*>(&sm.Mb[l16][16 + 4 * g4]);
+        f32x4 w0 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int q = 0; q < NQ; ++q) {
-          const int col = 32 * (q >> 1) + 4 * (q & 1) + 8 * i;
-          const bf16x8 kh = join(tr4(&sm.rk_hi[ra][col]), tr4(&sm.rk_hi[ra + 16][col]));
-          const bf16x8 kl = join(tr4(&sm.rk_lo[ra][col]), tr4(&sm.rk_lo[ra + 16][col]));
-          S[q] = mfma(kh, uh, S[q]);
-          S[q] = mfma(kh, ul, S[q]);
-          S[q] = mfma(kl, uh, S[q]);
+        for (int mt = 0; mt < 2; ++mt) {
+          const bf16x8 a = frag_lds(&sm.Tb[16 * mt + l16][8 * g4]);
+          f32x4 w = {0.f, 0.f, 0.f, 0.f};
+          f32x4 uu = {0.f, 0.f, 0.f, 0.f};
+          w = mfma(a, bk, w);
+          uu = mfma(a, bv, uu);
+          if constexpr (HP) {
+            const bf16x8 al = frag_lds(&sm.Tb_lo[16 * mt + l16][8 * g4]);
+            w = mfma(a, bkl, w);
+            w = mfma(al, bk, w);
+            uu = mfma(a, bvl, uu);
+            uu = mfma(al, bv, uu);
+          }
+          if (mt == 0) {
+            w0 = w;
+          } else {
+            // second row block: T10 (.) = -M (T00 .), added as (-M) W0 and
+            // (-M) U0.  The first block's results are the B operands of
+            // 16x16x16 products as they stand (K = rows 4 g4 + e in this
+            // lane's accumulator order).  -M and U0 as pairs; W0 single
+            // (pair with fp32 inputs).
+            uint32_t wb[2], wl[2], ub[2], ubl[2];
+            split2(w0[0], w0[1], wb[0], wl[0]);
+            split2(w0[2], w0[3], wb[1], wl[1]);
+            split2(U[0][0], U[0][1], ub[0], ubl[0]);
+            split2(U[0][2], U[0][3], ub[1], ubl[1]);
+            const s16x4 wbv = __builtin_bit_cast(s16x4, make_uint2(wb[0], wb[1]));
+            const s16x4 ubv = __builtin_bit_cast(s16x4, make_uint2(ub[0], ub[1]));
+            const s16x4 ulv = __builtin_bit_cast(s16x4, make_uint2(ubl[0], ubl[1]));
+            w = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(mh, wbv, w, 0, 0, 0);
+            if constexpr (HP) {
+              const s16x4 wlv = __builtin_bit_cast(s16x4, make_uint2(wl[0], wl[1]));
+              w = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(mh, wlv, w, 0, 0, 0);
+              w = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ml, wbv, w, 0, 0, 0);
+            }
+            uu = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(mh, ubv, uu, 0, 0, 0);
+            uu = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(mh, ulv, uu, 0, 0, 0);
+            uu = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ml, ubv, uu, 0, 0, 0);
+          }
+          U[mt] = uu;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float wv = -w[e];
+            const float wh = hi_of(wv);
+            sm.u.w.Wn[16 * mt + 4 * g4 + e][16 * wave + l16] = f32_to_bf16(wh);
+            if constexpr (HP) sm.u.w.Wn_lo[16 * mt + 4 * g4 + e][16 * wave + l16] = f32_to_bf16(wv - wh);
+          }
         }
       }
-#pragma unroll
-      for (int q = 0; q < NQ; ++q) {
-        const float4 f = *reinterpret_cast<const float4*>(&sm.eg_e[par][16 * q + 4 * g4]);
-        S[q][0] *= f.x; S[q][1] *= f.y; S[q][2] *= f.z; S[q][3] *= f.w;
-      }
-#pragma unroll
-      for (int mt = 0; mt < 2 && WITH_O; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) O[mt][i] += Ob[mt][i] + Oc[mt][i];
-    };
-    if (chain) {
-      if (outputs) chain_step(std::true_type{});
-      else chain_step(std::false_type{});
+      // gated operands of chunk b + CH
+      if (more2) gated_operands(b + CH, cp, tid);
+      lds_barrier();
     }
-    // ------------------------------------------------ next chunk: v, and the g / v / beta request for the one after
-    if (more) {
-      commit_v(base + CH);
-      if (base + 2 * CH < hi) load_gv(base + 2 * CH);
-    }
-    // ------------------------------------------------ outputs: stage in LDS (stored during the next chunk)
-    if (chain && outputs) {
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) io<TOUT>::st(&sm.ostg[16 * mt + 4 * g4 + e][ncol], O[mt][e] * p.scale);
-    }
-    // ------------------------------------------------ interval checkpoint
-    if (outputs && p.ckpt_interval > 0 && p.ckpt_cu) {
-      const int64_t after = base + CH;
-      if (after < end && after % p.ckpt_interval == 0) {
-        const int64_t j = after / p.ckpt_interval - start / p.ckpt_interval - 1;
-        const int64_t idx = static_cast<int64_t>(p.ckpt_cu[s]) + j;
-        if (j >= 0 && idx < p.ckpt_cu[s + 1] && idx < p.n_ckpt) {
-          const int slot = p.ckpt_slot[idx];
-          if (chain && slot >= 0 && slot < p.n_slots && ncol < d)
-            state_store<D>(p.pool + (static_cast<int64_t>(slot) * H + h) * d * d, S, lane, ncol, d);
-          if (tid == 0 && h == 0 && p.ckpt_pos_out) p.ckpt_pos_out[idx] = static_cast<int32_t>(after);
-        }
-      }
-    }
-    lds_barrier();
   };
-  int par = 0;
-  for (int64_t base = first; base < hi; base += CH) {
-    chunk(base, par);
-    par ^= 1;
-  }
-  if (outputs && hi > lo) {
-    lds_barrier();
-    store_out(first + ((hi - 1 - first) / CH) * CH);
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  // one step variant per loop, so that nothing in the loop body joins
+  // register values from different variants
+  auto run = [&](auto out_t) __attribute__((always_inline)) {
+    int cp = 0;
+    int64_t n = first;
+    for (; n + CH < hi; n += CH) {
+      step(n, cp, T_{}, T_{}, out_t);
+      cp ^= 1;
+    }
+    step(n, cp, T_{}, F_{}, out_t);
+  };
+  if (hi > lo) {
+    step(first - CH, 1, F_{}, T_{}, F_{});
+    if (outputs) {
+      run(T_{});
+
+    } else {
+      run(F_{});
+    }
   }
   // ---- final state: the destination slot, or a segment-scan block
   if (chain && ncol < d) {
