@@ -727,16 +727,20 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
     const int64_t ck = CHAIN ? ckpt_index(n + CH) : -1;
 
     // ================================================ phase I
-    if constexpr (MORE) {
-      // v of chunk b and g / beta of chunk b + CH to LDS, then the requests
-      // of v of b + CH and g / beta of b + 2 CH (rows past the end of the
-      // item load nothing); first in the step, so that no store of this step
-      // is pending at the wait for the rows
-      commit_v(b);
-      if (more2) commit_g(b + CH, cp);
-      load_v(b + CH);
-      load_g(b + 2 * CH);
-    }
+    // v of chunk b and g / beta of chunk b + CH to LDS, then the requests of
+    // v of b + CH and g / beta of b + 2 CH (rows past the end of the item
+    // load nothing).  Before any store of this step, so that no store is
+    // pending at the wait for the rows; on chain waves in the shadow of the
+    // u products.
+    auto rows = [&]() __attribute__((always_inline)) {
+      if constexpr (MORE) {
+        commit_v(b);
+        if (more2) commit_g(b + CH, cp);
+        load_v(b + CH);
+        load_g(b + 2 * CH);
+      }
+    };
+    if (!(CHAIN && chain)) rows();
     if (CHAIN && chain) {
       // The LDS fragments of each product are read one stage ahead, behind
       // scheduling fences, so that their latency hides behind the work
@@ -764,6 +768,7 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
           }
         }
       }
+      rows();
       // right_k^T fragments (transpose reads of right_k [s][pos32(c)]: rows
       // follow u's order, columns are picked so that lane l16 receives
       // channel 16 q + l16), read while u becomes a pair
@@ -800,9 +805,18 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
         }
         __builtin_amdgcn_sched_barrier(0);
       }
+      // S = Diag(exp(G_last - G_m)) (S' + right_k^T u) is the state after
+      // chunk n; it enters chunk b as Diag(exp G_m(b)) S, both factors in one
+      // product unless the state after n is stored
+      const float* fs = (MORE && ck < 0) ? sm.eg_c[lp] : sm.eg_e[cp];
+      auto scale_tile = [&](const int q) __attribute__((always_inline)) {
+        const float4 x = *reinterpret_cast<const float4*>(&fs[16 * q + 4 * g4]);
+        S[q][0] *= x.x; S[q][1] *= x.y; S[q][2] *= x.z; S[q][3] *= x.w;
+      };
       if constexpr (WITH_O) {
         // O = scale (left_q S' + P u) with three independent accumulators for
-        // the pair terms, staged in LDS
+        // the pair terms, staged in LDS; the state scaling runs between the
+        // products
         f32x4 O[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
         f32x4 Ob[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
         f32x4 Oc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
@@ -814,6 +828,8 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
             Ob[mt] = mfma(qf[ks][mt][0], sl[ks], Ob[mt]);
             Oc[mt] = mfma(qf[ks][mt][1], sh[ks], Oc[mt]);
           }
+          scale_tile(2 * ks);
+          scale_tile(2 * ks + 1);
         }
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
@@ -835,19 +851,14 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
                 io<TOUT>::st(og + (bos + (pos - start)) * p.o_stride + static_cast<int64_t>(h) * d + ncol, ov);
             }
           }
-      }
-      // S = Diag(exp(G_last - G_m)) (S' + right_k^T u) is the state after
-      // chunk n; it enters chunk b as Diag(exp G_m(b)) S, both factors in one
-      // product unless the state after n is stored
-      if (MORE && ck < 0) {
-        scale_state(sm.eg_c[lp], g4);
       } else {
-        scale_state(sm.eg_e[cp], g4);
-        if (ck >= 0) {
-          const int slot = p.ckpt_slot[ck];
-          if (slot >= 0 && slot < p.n_slots && ncol < d)
-            state_store<D>(p.pool + (static_cast<int64_t>(slot) * H + h) * d * d, S, lane, ncol, d);
-        }
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) scale_tile(q);
+      }
+      if (ck >= 0) {
+        const int slot = p.ckpt_slot[ck];
+        if (slot >= 0 && slot < p.n_slots && ncol < d)
+          state_store<D>(p.pool + (static_cast<int64_t>(slot) * H + h) * d * d, S, lane, ncol, d);
         if constexpr (MORE) scale_state(sm.eg_m[lp], g4);
       }
     }
