@@ -740,7 +740,41 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
         load_g(b + 2 * CH);
       }
     };
-    if (!(CHAIN && chain)) rows();
+    // the A products of the solve waves (left_k right_k^T blocks of chunk b,
+    // whose operands are complete since the previous step): wave 3 block
+    // (0,0), wave 4 blocks (1,0) and (1,1), wave 5 block (1,1); kept in
+    // registers until phase II.  On chain waves they run beside the VALU
+    // work that forms the S' fragments.
+    f32x4 ablk[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    auto a_products = [&]() __attribute__((always_inline)) {
+      if constexpr (MORE) {
+        if (wave >= 3 && wave < 6) {
+          auto a_prod = [&](const int I, const int J, f32x4& acc) __attribute__((always_inline)) {
+#pragma unroll
+            for (int ks = 0; ks < D / 32; ++ks) {
+              const bf16x8 a = frag_lds(&sm.lk[lp][16 * I + l16][32 * ks + kq]);
+              const bf16x8 bb = frag_lds(&sm.rk_hi[lp][16 * J + l16][32 * ks + kq]);
+              acc = mfma(a, bb, acc);
+              if constexpr (HP) {
+                acc = mfma(a, frag_lds(&sm.rk_lo[lp][16 * J + l16][32 * ks + kq]), acc);
+                acc = mfma(frag_lds(&sm.lk_lo[lp][16 * I + l16][32 * ks + kq]), bb, acc);
+              }
+            }
+          };
+          if (wave == 4) {
+            a_prod(1, 0, ablk[0]);
+            a_prod(1, 1, ablk[1]);
+          } else {
+            const int bb = wave == 3 ? 0 : 1;
+            a_prod(bb, bb, ablk[0]);
+          }
+        }
+      }
+    };
+    if (!(CHAIN && chain)) {
+      rows();
+      a_products();
+    }
     if (CHAIN && chain) {
       // The LDS fragments of each product are read one stage ahead, behind
       // scheduling fences, so that their latency hides behind the work
@@ -753,6 +787,7 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) wf[ks][mt] = frag_lds(&sm.u.w.Wn[16 * mt + l16][32 * ks + kq]);
       __builtin_amdgcn_sched_barrier(0);
+      a_products();
       bf16x8 sh[NQ / 2], sl[NQ / 2], uh, ul;
 #pragma unroll
       for (int ks = 0; ks < NQ / 2; ++ks) frag_pair(S[2 * ks], S[2 * ks + 1], sh[ks], sl[ks]);
@@ -905,20 +940,10 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
         // row r of column 4 g + g4, g = 0..3).  Each wave forms the blocks of
         // A = strict-lower(diag(beta) left_k right_k^T) it needs: wave 3 A00
         // (-> T00), wave 4 A10, A11 (-> M), wave 5 A11 (-> T11).
-        // A block (I, J) into the wave's LDS tile t, transposed:
+        // A block (I, J) from its product (formed in phase I) into the
+        // wave's LDS tile t, transposed:
         // At[t][c][r] = beta_r <left_k[16 I + r], right_k[16 J + c]>
-        auto a_block = [&](const int I, const int J, const int t) __attribute__((always_inline)) {
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int ks = 0; ks < D / 32; ++ks) {
-            const bf16x8 a = frag_lds(&sm.lk[lp][16 * I + l16][32 * ks + kq]);
-            const bf16x8 bb = frag_lds(&sm.rk_hi[lp][16 * J + l16][32 * ks + kq]);
-            acc = mfma(a, bb, acc);
-            if constexpr (HP) {
-              acc = mfma(a, frag_lds(&sm.rk_lo[lp][16 * J + l16][32 * ks + kq]), acc);
-              acc = mfma(frag_lds(&sm.lk_lo[lp][16 * I + l16][32 * ks + kq]), bb, acc);
-            }
-          }
+        auto a_block = [&](const f32x4& acc, const int I, const int J, const int t) __attribute__((always_inline)) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int r = 4 * g4 + i;
@@ -928,7 +953,7 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
         if (wave != 4) {
           const int bb = wave == 3 ? 0 : 1;
           const int t = wave == 3 ? 0 : 1;
-          a_block(bb, bb, t);
+          a_block(ablk[0], bb, bb, t);
           asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
           __builtin_amdgcn_wave_barrier();
           float na[16];
@@ -952,8 +977,8 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
             if constexpr (HP) sm.Tb_lo[16 * bb + l16][16 * (1 - bb) + j] = 0;
           }
         } else {
-          a_block(1, 0, 2);
-          a_block(1, 1, 3);
+          a_block(ablk[0], 1, 0, 2);
+          a_block(ablk[1], 1, 1, 3);
           asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
           __builtin_amdgcn_wave_barrier();
           float na1[16];
