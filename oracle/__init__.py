@@ -201,6 +201,45 @@ class Oracle:
         return y, ns
 
 
+    # -- fused decode step -------------------------------------------------
+    def kda_decode_conv(self, x, w, g, beta, init, conv_state, *, H, d, bias=None, act=0,
+                        qk_l2norm=1, norm_eps=1e-6, scale=1.0):
+        """The decode step with the short convolution in front of the
+        recurrence, one token per sequence.
+
+        x [N, 3 H d]: the token's raw projections, channels ordered q block,
+        k block, v block, each [H, d]; w [3 H d, W]; bias [3 H d] or None;
+        conv_state [N, 3 H d, W-1] (oldest first; zeros = no history);
+        g [N, H, d]; beta [N, H]; init [N, H, d, d].
+
+        Per sequence: y = conv(conv_state ++ x) (+ SiLU when act == 1), the
+        same definition as :meth:`conv_short`, kept unrounded; q, k, v are the
+        three blocks of y, per head; when qk_l2norm, q <- q / sqrt(|q|^2 + eps)
+        and k likewise (per token and head); then one recurrence step from
+        init as :meth:`kda_verify` with T_spec = 1.
+
+        Returns dict o [N, H, d], state [N, H, d, d], conv_state [N, 3 H d, W-1].
+        """
+        x = np.asarray(_as_f32(x), np.float64)
+        N, C = x.shape
+        if C != 3 * H * d:
+            raise ValueError("x must have 3 * H * d channels")
+        cu = np.arange(N + 1, dtype=np.int32)
+        st = _as_f32(conv_state)
+        y, ns = self.conv_short(x.astype(np.float32), w, cu, bias=bias, act=act, state=st)
+        y = np.asarray(y, np.float64).reshape(N, 3, H, d)
+        q, k, v = y[:, 0], y[:, 1], y[:, 2]
+        if qk_l2norm:
+            q = q / np.sqrt((q * q).sum(-1, keepdims=True) + norm_eps)
+            k = k / np.sqrt((k * k).sum(-1, keepdims=True) + norm_eps)
+        # the recurrence consumes float32 operands (the rounding of an fp64
+        # conv output to float32 is far below every comparison tolerance)
+        res = self.kda_verify(q[:, None].astype(np.float32), k[:, None].astype(np.float32),
+                              v[:, None].astype(np.float32), _as_f32(g)[:, None],
+                              _as_f32(beta)[:, None], init, scale=scale)
+        return {"o": res["o"][:, 0], "state": res["committed"], "conv_state": ns}
+
+
 _cache: dict = {}
 
 

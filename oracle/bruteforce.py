@@ -13,6 +13,9 @@ against each other:
       Phi(t, s) = A_t A_{t-1} ... A_{s+1}   (identity when s = t),
   and o_t = scale * S_t^T q_t, with every product formed from scratch.
 * ``conv_form``: the causal depthwise convolution via numpy.convolve.
+* ``decode_conv_form``: one fused decode step (convolution, optional SiLU,
+  per-head L2 normalisation of q and k, one recurrence step) with every sum
+  written out.
 """
 
 from __future__ import annotations
@@ -82,3 +85,38 @@ def conv_form(x, w, state=None, bias=None, act=0):
     if act == 1:
         y = y / (1 + np.exp(-y))
     return y, new
+
+
+def decode_conv_form(x, w, g, beta, S0, conv_state, H, d, bias=None, act=0, qk_l2norm=1,
+                     norm_eps=1e-6, scale=1.0):
+    """One sequence, one token.  x [3 H d]; w [3 H d, W]; conv_state
+    [3 H d, W-1]; g [H, d]; beta [H]; S0 [H, d, d].  Returns o [H, d] and the
+    new state [H, d, d]."""
+    x = np.asarray(x, np.float64)
+    w = np.asarray(w, np.float64)
+    hist = np.asarray(conv_state, np.float64)
+    C, W = w.shape
+    y = np.zeros(C)
+    for c in range(C):
+        acc = 0.0 if bias is None else float(bias[c])
+        for j in range(W):
+            # tap W-1 multiplies the current token, tap j the token W-1-j back
+            xv = x[c] if j == W - 1 else hist[c, j]
+            acc += w[c, j] * xv
+        if act == 1:
+            acc = acc / (1.0 + np.exp(-acc))
+        y[c] = acc
+    o = np.zeros((H, d))
+    S = np.zeros((H, d, d))
+    for h in range(H):
+        q = y[h * d:(h + 1) * d]
+        k = y[H * d + h * d:H * d + (h + 1) * d]
+        v = y[2 * H * d + h * d:2 * H * d + (h + 1) * d]
+        if qk_l2norm:
+            q = q / np.sqrt(sum(t * t for t in q) + norm_eps)
+            k = k / np.sqrt(sum(t * t for t in k) + norm_eps)
+        o_h, S_h = matrix_form(q[None], k[None], v[None], np.asarray(g, np.float64)[h][None],
+                               np.array([beta[h]], np.float64), S0[h], scale)
+        o[h] = o_h[0]
+        S[h] = S_h
+    return o, S

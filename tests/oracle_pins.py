@@ -286,5 +286,65 @@ def pin_conv(orc):
         assert np.array_equal(sa, sb)
 
 
+def decode_conv_case(seed, N=3, H=2, d=5, W=4):
+    r = _rng(seed)
+    C = 3 * H * d
+    x = r.standard_normal((N, C)).astype(np.float32)
+    w = r.uniform(-0.5, 0.5, (C, W)).astype(np.float32)
+    bias = (0.1 * r.standard_normal(C)).astype(np.float32)
+    cst = r.standard_normal((N, C, W - 1)).astype(np.float32)
+    g = (-np.log1p(np.exp(-r.standard_normal((N, H, d))))).astype(np.float32)
+    beta = (1 / (1 + np.exp(-r.standard_normal((N, H))))).astype(np.float32)
+    S0 = r.standard_normal((N, H, d, d)) * 0.5
+    return x, w, bias, cst, g, beta, S0
+
+
+def pin_decode_conv(orc):
+    """Fused decode step: brute force with every sum written out; with the
+    current-token tap alone and no activation / normalisation it is the plain
+    decode step on the raw projections; with normalisation, positive scalings
+    of the q and k projections change nothing; the conv state advances by the
+    token.  The composed oracle hands q, k, v to the recurrence as float32
+    (rounding ~6e-8 relative), hence the 1e-6 floor on the tolerance."""
+    tol = max(_tol(orc) * 10, 1e-6)
+    H, d, W = 2, 5, 4
+    for seed, act, norm in ((51, 1, 1), (52, 0, 1), (53, 1, 0)):
+        x, w, bias, cst, g, beta, S0 = decode_conv_case(seed, H=H, d=d, W=W)
+        res = orc.kda_decode_conv(x, w, g, beta, S0, cst, H=H, d=d, bias=bias, act=act,
+                                  qk_l2norm=norm, scale=0.7)
+        for s in range(x.shape[0]):
+            ob, Sb = bruteforce.decode_conv_form(x[s], w, g[s], beta[s], S0[s], cst[s], H, d,
+                                                 bias=bias, act=act, qk_l2norm=norm, scale=0.7)
+            np.testing.assert_allclose(res["o"][s], ob, rtol=tol, atol=tol)
+            np.testing.assert_allclose(res["state"][s], Sb, rtol=tol, atol=tol)
+            # the conv state is the history shifted by one token
+            assert np.array_equal(res["conv_state"][s][:, :-1], cst[s][:, 1:])
+            assert np.array_equal(res["conv_state"][s][:, -1], x[s])
+    # current-token tap only: q, k, v are the raw projections
+    x, w, bias, cst, g, beta, S0 = decode_conv_case(54, H=H, d=d, W=W)
+    w1 = np.zeros_like(w)
+    w1[:, W - 1] = 1
+    res = orc.kda_decode_conv(x, w1, g, beta, S0, cst, H=H, d=d, act=0, qk_l2norm=0)
+    N = x.shape[0]
+    xr = x.reshape(N, 3, H, d)
+    ref = orc.kda_verify(xr[:, 0][:, None], xr[:, 1][:, None], xr[:, 2][:, None], g[:, None],
+                         beta[:, None], S0)
+    np.testing.assert_allclose(res["o"], ref["o"][:, 0], rtol=tol, atol=tol)
+    np.testing.assert_allclose(res["state"], ref["committed"], rtol=tol, atol=tol)
+    # normalisation: the q and k blocks of x scaled by positive constants
+    # (linear conv, no activation, no bias, eps = 0) leave everything unchanged
+    a = orc.kda_decode_conv(x, w, g, beta, S0, cst, H=H, d=d, act=0, qk_l2norm=1, norm_eps=0.0)
+    xs = x.copy().reshape(N, 3, H * d)
+    cs = cst.copy().reshape(N, 3, H * d, W - 1)
+    xs[:, 0] *= 4.0
+    cs[:, 0] *= 4.0
+    xs[:, 1] *= 0.25
+    cs[:, 1] *= 0.25
+    b = orc.kda_decode_conv(xs.reshape(N, -1), w, g, beta, S0, cs.reshape(N, -1, W - 1), H=H, d=d,
+                            act=0, qk_l2norm=1, norm_eps=0.0)
+    np.testing.assert_allclose(a["o"], b["o"], rtol=tol, atol=tol)
+    np.testing.assert_allclose(a["state"], b["state"], rtol=tol, atol=tol)
+
+
 ALL_PINS = [pin_bruteforce, pin_readback, pin_pure_decay, pin_linearity, pin_resume,
-            pin_varlen_independent, pin_verify, pin_ckpt_positions, pin_conv]
+            pin_varlen_independent, pin_verify, pin_ckpt_positions, pin_conv, pin_decode_conv]
