@@ -30,6 +30,21 @@ struct StepParams {
 
 int launch_step(const StepParams& p, int D, int in_dtype, int out_dtype, hipStream_t stream);
 
+// decode step with the short convolution fused in
+struct DecodeConvParams {
+  const void *x, *w, *bias, *g, *beta;
+  void* cpool;
+  void* o;
+  float* pool;
+  const int32_t *csrc, *cdst, *src_slot, *dst_slot;
+  int64_t x_stride, g_stride, beta_stride, o_stride;
+  int64_t n_slots, n_cslots;
+  int32_t n_seq, H, W, act, qk_l2norm;
+  float eps, scale;
+};
+
+int launch_decode_conv(const DecodeConvParams& p, int D, int in_dtype, int out_dtype, hipStream_t stream);
+
 // ---------------------------------------------------------------- conv
 struct ConvParams {
   const void* x;

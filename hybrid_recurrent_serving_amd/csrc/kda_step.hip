@@ -250,6 +250,244 @@ static int launch_step_d(const StepParams& p, int in_dtype, int out_dtype, hipSt
   return launch_step_t<D, float, float>(p, stream);
 }
 
+// ---------------------------------------------------------------------------
+// Decode step with the short convolution fused in.  The workgroup of a
+// (sequence, head) first issues its state-slice loads (the bulk of the
+// traffic), then forms the head's q, k, v from the raw projections: one
+// 16-byte vector of V channels per conv item, 3 d / V items (q, k and v
+// blocks), each reading its taps, its conv history and the token, writing
+// y (fp32) to LDS and the advanced history to the conv pool.  After one
+// barrier every wave reads the q / k norms from LDS (redundantly, no second
+// barrier) and runs the decode step of step_kernel on LDS operands.
+template <typename T> struct Vec16x;
+template <> struct Vec16x<bf16_t> {
+  static constexpr int N = 8;
+  __device__ static __forceinline__ void ld(const bf16_t* p, float (&x)[8]) {
+    const uint4 t = *reinterpret_cast<const uint4*>(p);
+    const uint32_t w[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = __uint_as_float(w[i] << 16);
+      x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+  __device__ static __forceinline__ void st(bf16_t* p, const float (&x)[8]) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = static_cast<uint32_t>(f32_to_bf16(x[2 * i])) | (static_cast<uint32_t>(f32_to_bf16(x[2 * i + 1])) << 16);
+    *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+};
+template <> struct Vec16x<float> {
+  static constexpr int N = 4;
+  __device__ static __forceinline__ void ld(const float* p, float (&x)[4]) { io<float>::ld4(p, x); }
+  __device__ static __forceinline__ void st(float* p, const float (&x)[4]) { io<float>::st4(p, x); }
+};
+
+template <int D, typename Tin, typename Tout, int W>
+__global__ void __launch_bounds__(64 * StepLayout<D>::WPH)
+decode_conv_kernel(const DecodeConvParams p) {
+  using L = StepLayout<D>;
+  constexpr int V = Vec16x<Tin>::N;       // channels per conv item
+  constexpr int NCI = 3 * D / V;          // conv items of one head
+  constexpr int HW = W - 1;               // history length
+  static_assert(NCI <= 64 * L::WPH, "one conv item per thread");
+  __shared__ __align__(16) float s_y[3 * D];   // q | k | v of this head (fp32)
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t sh = blockIdx.x;
+  const int s = static_cast<int>(sh / p.H);
+  const int h = static_cast<int>(sh % p.H);
+  const int cg = lane % L::LPR;
+  const int rg = lane / L::LPR;
+  const int col = wave * L::COLS + 4 * cg;
+  const int row0 = rg * L::RPL;
+
+  const int src = p.src_slot[s];
+  const int dst = p.dst_slot[s];
+  const bool has_src = src >= 0 && src < p.n_slots;
+  const bool has_dst = dst >= 0 && dst < p.n_slots;
+
+  // state slice first: the longest-latency traffic of the step
+  float S[L::RPL][4];
+  if (has_src) {
+    const float* sp = p.pool + ((static_cast<int64_t>(src) * p.H + h) * D + row0) * D + col;
+#pragma unroll
+    for (int i = 0; i < L::RPL; ++i) ld4_stream(sp + static_cast<int64_t>(i) * D, S[i]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < L::RPL; ++i) S[i][0] = S[i][1] = S[i][2] = S[i][3] = 0.f;
+  }
+  // decay and beta of this lane's rows
+  const Tin* gb = static_cast<const Tin*>(p.g);
+  float ar[L::RPL];
+  ld_vec<Tin, L::RPL>(gb + static_cast<int64_t>(s) * p.g_stride + static_cast<int64_t>(h) * D + row0, ar);
+  const float beta = io<Tin>::ld(static_cast<const Tin*>(p.beta) + static_cast<int64_t>(s) * p.beta_stride + h);
+
+  // ---- convolution of this head's q, k, v channels
+  if (static_cast<int>(threadIdx.x) < NCI) {
+    const int t = threadIdx.x;
+    const int blk = t / (D / V);                 // 0 q, 1 k, 2 v
+    const int cc = (t % (D / V)) * V;            // channel inside the head's block
+    const int64_t C = 3LL * p.H * D;
+    const int64_t ch = static_cast<int64_t>(blk) * p.H * D + static_cast<int64_t>(h) * D + cc;
+    // taps: the V * W values of channels ch .. ch + V - 1 are contiguous
+    // (W 16-byte vectors); wt[i][j] = weight[ch + i, j]
+    float wt[V][W];
+    {
+      const Tin* wp = static_cast<const Tin*>(p.w) + ch * W;
+#pragma unroll
+      for (int b = 0; b < W; ++b) {
+        float f[V];
+        Vec16x<Tin>::ld(wp + b * V, f);
+#pragma unroll
+        for (int e = 0; e < V; ++e) wt[(b * V + e) / W][(b * V + e) % W] = f[e];
+      }
+    }
+    // history: V * (W-1) contiguous values, hist[i][j] = pool[slot, ch + i, j]
+    float hist[V][HW];
+#pragma unroll
+    for (int i = 0; i < V; ++i)
+#pragma unroll
+      for (int j = 0; j < HW; ++j) hist[i][j] = 0.f;
+    const int csrc = p.csrc[s];
+    const int cdst = p.cdst[s];
+    if (csrc >= 0 && csrc < p.n_cslots) {
+      const Tin* hp = static_cast<const Tin*>(p.cpool) + (static_cast<int64_t>(csrc) * C + ch) * HW;
+#pragma unroll
+      for (int b = 0; b < HW; ++b) {
+        float f[V];
+        Vec16x<Tin>::ld(hp + b * V, f);
+#pragma unroll
+        for (int e = 0; e < V; ++e) hist[(b * V + e) / HW][(b * V + e) % HW] = f[e];
+      }
+    }
+    float xt[V];
+    Vec16x<Tin>::ld(static_cast<const Tin*>(p.x) + static_cast<int64_t>(s) * p.x_stride + ch, xt);
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      // tap W-1 multiplies the token, tap j < W-1 the history value j
+      float acc = p.bias ? io<Tin>::ld(static_cast<const Tin*>(p.bias) + ch + i) : 0.f;
+#pragma unroll
+      for (int j = 0; j < HW; ++j) acc = fmaf(wt[i][j], hist[i][j], acc);
+      acc = fmaf(wt[i][HW], xt[i], acc);
+      if (p.act == 1) acc = acc / (1.f + expf(-acc));
+      s_y[blk * D + cc + i] = acc;
+    }
+    // advanced history: hist[1 .. W-2] ++ token
+    if (cdst >= 0 && cdst < p.n_cslots) {
+      float nh[V * HW];
+#pragma unroll
+      for (int i = 0; i < V; ++i)
+#pragma unroll
+        for (int j = 0; j < HW; ++j) nh[i * HW + j] = j + 1 < HW ? hist[i][j + 1] : xt[i];
+      Tin* np_ = static_cast<Tin*>(p.cpool) + (static_cast<int64_t>(cdst) * C + ch) * HW;
+#pragma unroll
+      for (int b = 0; b < HW; ++b) {
+        float f[V];
+#pragma unroll
+        for (int e = 0; e < V; ++e) f[e] = nh[b * V + e];
+        Vec16x<Tin>::st(np_ + b * V, f);
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- q / k normalisation factors (every wave, from LDS)
+  float inv_q = 1.f, inv_k = 1.f;
+  if (p.qk_l2norm) {
+    float sq = 0.f, sk = 0.f;
+#pragma unroll
+    for (int c = lane; c < D; c += 64) {
+      sq = fmaf(s_y[c], s_y[c], sq);
+      sk = fmaf(s_y[D + c], s_y[D + c], sk);
+    }
+    sq = wave_sum_from<1>(sq);
+    sk = wave_sum_from<1>(sk);
+    inv_q = 1.f / sqrtf(sq + p.eps);
+    inv_k = 1.f / sqrtf(sk + p.eps);
+  }
+
+  // ---- the decode step on LDS operands (as step_kernel)
+  float kr[L::RPL], qr[L::RPL], vc[4];
+#pragma unroll
+  for (int i = 0; i < L::RPL; ++i) {
+    qr[i] = s_y[row0 + i] * inv_q;
+    kr[i] = s_y[D + row0 + i] * inv_k;
+    ar[i] = expf(ar[i]);
+  }
+#pragma unroll
+  for (int c = 0; c < 4; ++c) vc[c] = s_y[2 * D + col + c];
+  float w[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < L::RPL; ++i) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      S[i][c] *= ar[i];
+      w[c] = fmaf(S[i][c], kr[i], w[c]);
+    }
+  }
+  float u[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    w[c] = wave_sum_from<L::LPR>(w[c]);
+    u[c] = beta * (vc[c] - w[c]);
+  }
+  float o[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < L::RPL; ++i) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      S[i][c] = fmaf(kr[i], u[c], S[i][c]);
+      o[c] = fmaf(S[i][c], qr[i], o[c]);
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < 4; ++c) o[c] = wave_sum_from<L::LPR>(o[c]) * p.scale;
+  if (rg == 0)
+    io<Tout>::st4(static_cast<Tout*>(p.o) + static_cast<int64_t>(s) * p.o_stride + static_cast<int64_t>(h) * D + col, o);
+  if (has_dst) {
+    float* dp = p.pool + ((static_cast<int64_t>(dst) * p.H + h) * D + row0) * D + col;
+#pragma unroll
+    for (int i = 0; i < L::RPL; ++i) st4_stream(dp + static_cast<int64_t>(i) * D, S[i]);
+  }
+}
+
+template <int D, typename Tin, typename Tout>
+static int launch_decode_conv_t(const DecodeConvParams& p, hipStream_t stream) {
+  using L = StepLayout<D>;
+  dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(p.n_seq) * p.H));
+  dim3 block(64 * L::WPH);
+  switch (p.W) {
+    case 2: hipLaunchKernelGGL((decode_conv_kernel<D, Tin, Tout, 2>), grid, block, 0, stream, p); break;
+    case 3: hipLaunchKernelGGL((decode_conv_kernel<D, Tin, Tout, 3>), grid, block, 0, stream, p); break;
+    case 4: hipLaunchKernelGGL((decode_conv_kernel<D, Tin, Tout, 4>), grid, block, 0, stream, p); break;
+    default: return fail(KDA_ERR_UNSUPPORTED, "decode_conv: W = %d (2..4)", p.W);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, "decode_conv kernel launch: %s", hipGetErrorString(e));
+  return KDA_OK;
+}
+
+template <int D>
+static int launch_decode_conv_d(const DecodeConvParams& p, int in_dtype, int out_dtype, hipStream_t stream) {
+  if (in_dtype == KDA_BF16 && out_dtype == KDA_BF16) return launch_decode_conv_t<D, bf16_t, bf16_t>(p, stream);
+  if (in_dtype == KDA_BF16 && out_dtype == KDA_F32) return launch_decode_conv_t<D, bf16_t, float>(p, stream);
+  if (in_dtype == KDA_F32 && out_dtype == KDA_BF16) return launch_decode_conv_t<D, float, bf16_t>(p, stream);
+  return launch_decode_conv_t<D, float, float>(p, stream);
+}
+
+int launch_decode_conv(const DecodeConvParams& p, int D, int in_dtype, int out_dtype, hipStream_t stream) {
+  switch (D) {
+    case 16: return launch_decode_conv_d<16>(p, in_dtype, out_dtype, stream);
+    case 32: return launch_decode_conv_d<32>(p, in_dtype, out_dtype, stream);
+    case 64: return launch_decode_conv_d<64>(p, in_dtype, out_dtype, stream);
+    case 128: return launch_decode_conv_d<128>(p, in_dtype, out_dtype, stream);
+    default: return fail(KDA_ERR_UNSUPPORTED, "d = %d not built (16, 32, 64, 128)", D);
+  }
+}
+
 int launch_step(const StepParams& p, int D, int in_dtype, int out_dtype, hipStream_t stream) {
   switch (D) {
     case 16: return launch_step_d<16>(p, in_dtype, out_dtype, stream);

@@ -71,6 +71,21 @@ class DecodeArgs(ctypes.Structure):
     ]
 
 
+class DecodeConvArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", c_size),
+        ("x", c_vp), ("conv_weight", c_vp), ("conv_bias", c_vp), ("conv_pool", c_vp),
+        ("conv_src_slot", c_vp), ("conv_dst_slot", c_vp),
+        ("g", c_vp), ("beta", c_vp), ("o", c_vp),
+        ("state_pool", c_vp), ("src_slot", c_vp), ("dst_slot", c_vp),
+        ("x_stride", c_i64), ("g_stride", c_i64), ("beta_stride", c_i64), ("o_stride", c_i64),
+        ("n_slots", c_i64), ("n_conv_slots", c_i64),
+        ("n_seq", c_i32), ("H", c_i32), ("d", c_i32), ("W", c_i32), ("act", c_i32),
+        ("qk_l2norm", c_i32), ("norm_eps", c_f32), ("in_dtype", c_i32), ("out_dtype", c_i32),
+        ("scale", c_f32),
+    ]
+
+
 class VerifyArgs(ctypes.Structure):
     _fields_ = [
         ("struct_size", c_size),
@@ -86,7 +101,7 @@ class VerifyArgs(ctypes.Structure):
 
 EXPORTS = ["kda_status_str", "kda_abi_version", "kda_last_error", "kda_args_sizeof",
            "kda_conv_short", "kda_ckpt_plan", "kda_prefill_workspace_bytes",
-           "kda_prefill_varlen", "kda_decode", "kda_verify"]
+           "kda_prefill_varlen", "kda_decode", "kda_verify", "kda_decode_conv"]
 
 _lib = None
 
@@ -118,7 +133,9 @@ def load_library(path: Optional[Path] = None):
     lib.kda_prefill_varlen.argtypes = [ctypes.POINTER(PrefillArgs), c_vp]
     lib.kda_decode.argtypes = [ctypes.POINTER(DecodeArgs), c_vp]
     lib.kda_verify.argtypes = [ctypes.POINTER(VerifyArgs), c_vp]
-    for name in ("kda_conv_short", "kda_ckpt_plan", "kda_prefill_varlen", "kda_decode", "kda_verify"):
+    lib.kda_decode_conv.argtypes = [ctypes.POINTER(DecodeConvArgs), c_vp]
+    for name in ("kda_conv_short", "kda_ckpt_plan", "kda_prefill_varlen", "kda_decode", "kda_verify",
+                 "kda_decode_conv"):
         getattr(lib, name).restype = ctypes.c_int
     if path is None:
         _lib = lib
@@ -411,6 +428,71 @@ def kda_decode(q, k, v, g, beta, o, state_pool, src_slot, dst_slot, *, scale=1.0
     a = _decode_args(q, k, v, g, beta, o, state_pool, src_slot, dst_slot, scale)
     _check(load_library().kda_decode(ctypes.byref(a), _stream(stream)))
     return o
+
+
+def _decode_conv_args(x, conv_weight, conv_pool, conv_src_slot, conv_dst_slot, g, beta, o, state_pool,
+                      src_slot, dst_slot, conv_bias, act, qk_l2norm, norm_eps, scale):
+    import torch
+    _expect(x.dim() == 2 and g.dim() == 3 and beta.dim() == 2 and o.dim() == 3,
+            "x [N, 3 H d], g [N, H, d], beta [N, H], o [N, H, d]")
+    N, H, d = g.shape
+    _expect(x.shape[0] == N and x.shape[1] == 3 * H * d, "x must be [N, 3 H d]")
+    _same_lead([("o", o)], (N, H, d), "g")
+    _same_lead([("beta", beta)], (N, H), "g")
+    _expect(conv_weight.dim() == 2 and conv_weight.shape[0] == 3 * H * d and conv_weight.is_contiguous(),
+            "conv_weight must be contiguous [3 H d, W]")
+    W = conv_weight.shape[1]
+    _expect(conv_pool.dim() == 3 and tuple(conv_pool.shape[1:]) == (3 * H * d, W - 1)
+            and conv_pool.is_contiguous(), "conv_pool must be contiguous [n_slots, 3 H d, W-1]")
+    _expect(conv_bias is None or (conv_bias.numel() == 3 * H * d and conv_bias.is_contiguous()),
+            "conv_bias must be contiguous [3 H d]")
+    _expect(state_pool.dim() == 4 and tuple(state_pool.shape[1:]) == (H, d, d)
+            and state_pool.dtype == torch.float32 and state_pool.is_contiguous(),
+            "state_pool must be contiguous float32 [n_slots, H, d, d]")
+    for nm, t in (("src_slot", src_slot), ("dst_slot", dst_slot), ("conv_src_slot", conv_src_slot),
+                  ("conv_dst_slot", conv_dst_slot)):
+        _expect(t.numel() >= N, f"{nm} shorter than n_seq")
+    _device_tensors(x=x, conv_weight=conv_weight, conv_pool=conv_pool, conv_src_slot=conv_src_slot,
+                    conv_dst_slot=conv_dst_slot, g=g, beta=beta, o=o, state_pool=state_pool,
+                    src_slot=src_slot, dst_slot=dst_slot)
+    _same_dtype(x, conv_weight=conv_weight, conv_pool=conv_pool, g=g, beta=beta)
+    _expect(x.stride(1) == 1, "x rows must be contiguous")
+    a = DecodeConvArgs()
+    a.struct_size = ctypes.sizeof(DecodeConvArgs)
+    a.x, a.conv_weight, a.conv_bias, a.conv_pool = map(_ptr, (x, conv_weight, conv_bias, conv_pool))
+    a.conv_src_slot, a.conv_dst_slot = _ptr(conv_src_slot), _ptr(conv_dst_slot)
+    a.g, a.beta, a.o = _ptr(g), _ptr(beta), _ptr(o)
+    a.state_pool, a.src_slot, a.dst_slot = _ptr(state_pool), _ptr(src_slot), _ptr(dst_slot)
+    a.x_stride = x.stride(0)
+    a.g_stride, a.beta_stride, a.o_stride = _tok_stride(g, 2), _tok_stride(beta, 1), _tok_stride(o, 2)
+    a.n_slots, a.n_conv_slots = state_pool.shape[0], conv_pool.shape[0]
+    a.n_seq, a.H, a.d, a.W = N, H, d, W
+    a.act, a.qk_l2norm, a.norm_eps = int(act), int(qk_l2norm), float(norm_eps)
+    a.in_dtype, a.out_dtype, a.scale = _dtype_code(x), _dtype_code(o), scale
+    return a
+
+
+def kda_decode_conv(x, conv_weight, conv_pool, conv_src_slot, conv_dst_slot, g, beta, o, state_pool,
+                    src_slot, dst_slot, *, conv_bias=None, act: int = 0, qk_l2norm: bool = True,
+                    norm_eps: float = 1e-6, scale=1.0, stream=None):
+    """Decode step with the short convolution fused in.  x [N, 3 H d] (q | k | v
+    projections of the token); conv_weight [3 H d, W]; conv_pool
+    [n_conv_slots, 3 H d, W-1]; g [N, H, d]; beta [N, H]; o [N, H, d]."""
+    a = _decode_conv_args(x, conv_weight, conv_pool, conv_src_slot, conv_dst_slot, g, beta, o, state_pool,
+                          src_slot, dst_slot, conv_bias, act, qk_l2norm, norm_eps, scale)
+    _check(load_library().kda_decode_conv(ctypes.byref(a), _stream(stream)))
+    return o
+
+
+def prepare_decode_conv(x, conv_weight, conv_pool, conv_src_slot, conv_dst_slot, g, beta, o, state_pool,
+                        src_slot, dst_slot, *, conv_bias=None, act: int = 0, qk_l2norm: bool = True,
+                        norm_eps: float = 1e-6, scale=1.0) -> Prepared:
+    """kda_decode_conv with fixed buffers, as a Prepared call."""
+    a = _decode_conv_args(x, conv_weight, conv_pool, conv_src_slot, conv_dst_slot, g, beta, o, state_pool,
+                          src_slot, dst_slot, conv_bias, act, qk_l2norm, norm_eps, scale)
+    return Prepared(load_library().kda_decode_conv, a,
+                    (x, conv_weight, conv_pool, conv_src_slot, conv_dst_slot, g, beta, o, state_pool,
+                     src_slot, dst_slot, conv_bias))
 
 
 def kda_verify(q, k, v, g, beta, state_pool, src_slot, dst_slot, *, o=None, accepted_len=None,

@@ -83,7 +83,7 @@ int kda_abi_version(void);
 /* One-line reason for the calling thread's most recent non-OK status. */
 const char *kda_last_error(void);
 /* sizeof() of each args struct as compiled into the library: which = 0 conv,
- * 1 prefill, 2 decode, 3 verify.  Returns 0 for other values. */
+ * 1 prefill, 2 decode, 3 verify, 4 decode_conv.  Returns 0 for other values. */
 size_t kda_args_sizeof(int which);
 
 /* ------------------------------------------------------------------------
@@ -247,6 +247,67 @@ typedef struct kda_decode_args {
 } kda_decode_args;
 
 int kda_decode(const kda_decode_args *args, kda_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * kda_decode_conv -- the decode step with the short convolution fused in.
+ *
+ * The KDA decode kernel runs the q/k/v short convolution and the recurrence
+ * in one launch ("Kimi K3 on vLLM", section "Kimi Delta Attention: a hybrid
+ * recurrent + full-attention stack"; Day-0 Integration page, section
+ * "Separate Prefill/Decode Code Paths").  For sequence s and head h:
+ *
+ *   xbar[c]  = conv state of channel c (W-1 raw inputs, oldest first) ++ x[s, c]
+ *   y[c]     = bias[c] + sum_j weight[c, j] * xbar[c][j]   (+ SiLU when act = 1)
+ *   q, k, v  = the head-h slices of the q, k and v blocks of y (fp32, unrounded)
+ *   qk_l2norm: q <- q / sqrt(|q|^2 + norm_eps), k likewise
+ *   then the kda_decode step with g[s, h], beta[s, h]:
+ *   S <- Diag(exp g) S;  S <- S + beta k (v - S^T k)^T;  o = scale S^T q.
+ *
+ * Channels of x, weight, bias and the conv pool are ordered [q block | k
+ * block | v block], each block [H, d] (C = 3 H d).  The conv state of the
+ * sequence advances by the token (xbar[1..W-1] to conv_dst_slot; -1 = no
+ * write; conv_src_slot -1 = zero history); the recurrent state goes from
+ * src_slot to dst_slot as in kda_decode.  Each (sequence, head) reads and
+ * writes only its own channels and state, so in-place slots are race free.
+ *
+ *   x            [n_seq, 3 H d] in_dtype, row stride x_stride (0 = packed)
+ *   conv_weight  [3 H d, W] in_dtype;  conv_bias [3 H d] or NULL
+ *   conv_pool    [n_conv_slots, 3 H d, W-1] in_dtype
+ *   g [n_seq, H, d], beta [n_seq, H] in_dtype; o [n_seq, H, d] out_dtype
+ *   state_pool   fp32 [n_slots, H, d, d]
+ * Errors: W outside 2..4 -> KDA_ERR_UNSUPPORTED; d not 16/32/64/128 ->
+ * KDA_ERR_UNSUPPORTED; x, conv_weight, conv_pool, g, o or state_pool not
+ * 16-byte aligned, or an x stride that breaks 16-byte rows -> KDA_ERR_ALIGN;
+ * act not 0/1, qk_l2norm not 0/1 or norm_eps < 0 -> KDA_ERR_ARG.
+ * ---------------------------------------------------------------------- */
+typedef struct kda_decode_conv_args {
+    size_t struct_size;          /* sizeof(kda_decode_conv_args) */
+    const void *x;               /* [n_seq, 3 H d] raw projections of the token */
+    const void *conv_weight;     /* [3 H d, W] */
+    const void *conv_bias;       /* [3 H d] or NULL */
+    void *conv_pool;             /* [n_conv_slots, 3 H d, W-1] */
+    const int32_t *conv_src_slot; /* [n_seq]; -1 = zero history */
+    const int32_t *conv_dst_slot; /* [n_seq]; -1 = do not write */
+    const void *g;               /* [n_seq, H, d] */
+    const void *beta;            /* [n_seq, H] */
+    void *o;                     /* [n_seq, H, d] out_dtype */
+    float *state_pool;           /* [n_slots, H, d, d] */
+    const int32_t *src_slot;     /* [n_seq] */
+    const int32_t *dst_slot;     /* [n_seq] */
+    int64_t x_stride, g_stride, beta_stride, o_stride; /* per sequence; 0 = packed */
+    int64_t n_slots;
+    int64_t n_conv_slots;
+    int32_t n_seq;
+    int32_t H, d;
+    int32_t W;                   /* conv width, 2..4 */
+    int32_t act;                 /* 0 none, 1 SiLU */
+    int32_t qk_l2norm;           /* 0 / 1 */
+    float norm_eps;              /* >= 0 */
+    int32_t in_dtype, out_dtype;
+    float scale;
+} kda_decode_conv_args;
+
+int kda_decode_conv(const kda_decode_conv_args *args, kda_stream_t stream);
 
 /* ------------------------------------------------------------------------
  * kda_verify -- speculative verification with a commit at the accepted

@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_abi_version_and_struct_sizes(lib):
     assert lib.kda_abi_version() == 1
-    for which, cls in enumerate([K.ConvArgs, K.PrefillArgs, K.DecodeArgs, K.VerifyArgs]):
+    for which, cls in enumerate([K.ConvArgs, K.PrefillArgs, K.DecodeArgs, K.VerifyArgs, K.DecodeConvArgs]):
         assert lib.kda_args_sizeof(which) == ctypes.sizeof(cls), cls.__name__
     assert lib.kda_args_sizeof(7) == 0
 
@@ -61,6 +61,41 @@ def _decode_args(**kw):
     for k, v in kw.items():
         setattr(a, k, v)
     return a
+
+
+def _decode_conv_args(**kw):
+    a = K.DecodeConvArgs()
+    a.struct_size = ctypes.sizeof(K.DecodeConvArgs)
+    fake = 1 << 20  # a 16-byte aligned fake device address: never dereferenced on these paths
+    for f in ("x", "conv_weight", "conv_pool", "conv_src_slot", "conv_dst_slot", "g", "beta", "o",
+              "state_pool", "src_slot", "dst_slot"):
+        setattr(a, f, fake)
+    a.n_seq, a.H, a.d, a.W, a.n_slots, a.n_conv_slots = 4, 2, 128, 4, 4, 4
+    a.in_dtype, a.out_dtype, a.scale, a.norm_eps, a.qk_l2norm = 0, 0, 1.0, 1e-6, 1
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_decode_conv_validation(lib):
+    f = "kda_decode_conv"
+    assert lib.kda_decode_conv(None, None) == 1
+    assert _call(lib, f, _decode_conv_args(struct_size=8)) == 8
+    assert _call(lib, f, _decode_conv_args(n_seq=0)) == 0          # no-op
+    assert _call(lib, f, _decode_conv_args(x=None)) == 1
+    assert _call(lib, f, _decode_conv_args(conv_pool=None)) == 1
+    assert _call(lib, f, _decode_conv_args(d=96)) == 6
+    assert _call(lib, f, _decode_conv_args(W=5)) == 6
+    assert _call(lib, f, _decode_conv_args(W=1)) == 6
+    assert _call(lib, f, _decode_conv_args(act=2)) == 8
+    assert _call(lib, f, _decode_conv_args(qk_l2norm=3)) == 8
+    assert _call(lib, f, _decode_conv_args(norm_eps=-1.0)) == 8
+    assert _call(lib, f, _decode_conv_args(in_dtype=5)) == 3
+    assert _call(lib, f, _decode_conv_args(H=0)) == 2
+    assert _call(lib, f, _decode_conv_args(x=(1 << 20) + 2)) == 4
+    assert _call(lib, f, _decode_conv_args(x_stride=100)) == 2       # < 3 H d
+    assert _call(lib, f, _decode_conv_args(x_stride=769)) == 4       # rows not 16-byte aligned
+    assert b"aligned" in lib.kda_last_error()
 
 
 def test_decode_validation(lib):
