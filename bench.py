@@ -81,7 +81,8 @@ COPY_BYTES = 256 * 2 ** 20
 
 def pmc_pass(torch, K, make_workload):
     """The launches the counter passes read: a plain device copy of a known
-    size (the calibration), decode steps over rotating pools, varlen prefills."""
+    size (the calibration), decode and fused decode steps over rotating
+    pools, varlen prefills."""
     dev = torch.device("cuda:0")
     a = torch.ones(COPY_BYTES // 4, device=dev)
     b = torch.empty_like(a)
@@ -98,6 +99,13 @@ def pmc_pass(torch, K, make_workload):
     for i in range(8):
         s_ = torch.arange((i % P) * N, (i % P + 1) * N, dtype=torch.int32, device=dev)
         K.kda_decode(q, k, v, g, bt, o, pool, s_, s_)
+    wlc = make_workload(1, with_conv=True)
+    x, cw = wlc.conv_x.to(dev), wlc.conv_w.to(dev)
+    cpool = wlc.conv_state.to(dev).clone()
+    cs = torch.arange(N, dtype=torch.int32, device=dev)
+    for i in range(8):
+        s_ = torch.arange((i % P) * N, (i % P + 1) * N, dtype=torch.int32, device=dev)
+        K.kda_decode_conv(x, cw, cpool, cs, cs, g, bt, o, pool, s_, s_, act=1, qk_l2norm=True)
     del pool
     bench_prefill_varlen(torch, K, make_workload, dev, iters=1)
     torch.cuda.synchronize()
@@ -134,6 +142,8 @@ def ingest_pmc(fetch_csv, write_csv):
     for key, pred, src, units, pick in (
             ("decode_step_kernel_d128_bf16", lambda r: "step_kernel<128" in r["Kernel_Name"], "kda_step.hip",
              128 * 16, "all"),
+            ("decode_conv_kernel_d128_bf16", lambda r: "decode_conv_kernel<128" in r["Kernel_Name"],
+             "kda_step.hip", 128 * 16, "all"),
             ("prefill_kernel_d128_bf16", lambda r: "prefill_kernel<128" in r["Kernel_Name"], "kda_prefill.hip",
              varlen_tokens(), "max")):
         f = sel("FETCH_SIZE", pred)
@@ -186,11 +196,47 @@ def bench_decode(args, torch, K, make_workload):
     cu = wl.cu_seqlens.to(dev)
     y = torch.empty_like(x)
 
-    # argument structs checked once; the timed loop only enqueues
+    # argument structs checked once; the timed loops only enqueue
     conv_call = K.prepare_conv_short(x, cw, cu, cpool, cslots, cslots, y=y)
     dec_calls = [K.prepare_decode(q, k, v, g, b, o, pool, s_, s_) for s_ in slot_sets]
+    # the fused step: conv (+ SiLU) of the token's q / k / v projections,
+    # per-head q / k L2 normalisation and the recurrence in one launch; the
+    # conv history advances in place like the state
+    fused_calls = [K.prepare_decode_conv(x, cw, cpool, cslots, cslots, g, b, o, pool, s_, s_, act=1,
+                                         qk_l2norm=True) for s_ in slot_sets]
 
-    def step(i, ev=None):
+    def timed(step_fn, nsteps, nwarm):
+        """Per-step time over nsteps back-to-back steps, then (in a second
+        pass, so that the event records do not stretch the steps) the average
+        duration of the recurrent kernel's launch from HIP events around it
+        on its stream."""
+        for i in range(nwarm):
+            step_fn(i, None)
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        w0 = time.perf_counter()
+        t0.record()
+        for i in range(nsteps):
+            step_fn(i, None)
+        t1.record()
+        torch.cuda.synchronize()
+        wall_ = time.perf_counter() - w0
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(nsteps)]
+        for i in range(nsteps):
+            step_fn(i, evs[i])
+        torch.cuda.synchronize()
+        return (t0.elapsed_time(t1) / nsteps, sum(a_.elapsed_time(b_) for a_, b_ in evs) / nsteps, wall_)
+
+    def fused_step(i, ev):
+        if ev is not None:
+            ev[0].record()
+        fused_calls[i % P]()
+        if ev is not None:
+            ev[1].record()
+
+    def two_call_step(i, ev):
         conv_call()
         if ev is not None:
             ev[0].record()
@@ -198,37 +244,37 @@ def bench_decode(args, torch, K, make_workload):
         if ev is not None:
             ev[1].record()
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    t0.record()
-    for i in range(args.steps):
-        step(i, evs[i])
-    t1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms_step = t0.elapsed_time(t1) / args.steps
-    k_ms = sum(a.elapsed_time(b_) for a, b_ in evs) / args.steps
+    ms_step, _, wall = timed(fused_step, args.steps, args.warmup)
+    # one launch per step: the launch's average duration is the timed
+    # region (HIP events on the launch stream) over the launch count
+    k_ms = ms_step
 
     state_bytes = N * H * D * D * 4 * 2                   # read + write
-    io_bytes = N * H * (4 * D * 2 + 2 + D * 2)            # q,k,v,g + beta + o (bf16)
-    alg_bytes = state_bytes + io_bytes                    # per launch of the decode kernel
+    # fused step per launch: state r+w, the token's q/k/v projections, the
+    # conv history r+w, g and beta in, o out (bf16), the conv taps once
+    conv_hist_bytes = N * C * (W - 1) * 2 * 2
+    io_bytes = N * C * 2 + N * H * (D * 2 + 2 + D * 2) + C * W * 2
+    alg_bytes = state_bytes + conv_hist_bytes + io_bytes
     value = state_bytes / (ms_step * 1e-3) / 1e9
     achieved = alg_bytes / (k_ms * 1e-3) / 1e9
-    traffic = traffic_for("decode_step_kernel_d128_bf16", "kda_step.hip", N * H)
-    roof = {"kernel": "step_kernel<128,bf16,bf16> (kda_decode)", "bound": "hbm",
+    traffic = traffic_for("decode_conv_kernel_d128_bf16", "kda_step.hip", N * H)
+    roof = {"kernel": "decode_conv_kernel<128,bf16,bf16,4> (kda_decode_conv)", "bound": "hbm",
             "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
             "alg_bytes_per_launch": alg_bytes, "avg_launch_us": round(k_ms * 1e3, 3)}
 
     secondary = {}
     if not args.no_secondary:
+        # the same step as two launches: kda_conv_short, then kda_decode on
+        # separately drawn (normalised) q / k / v
+        ms2, k2, _ = timed(two_call_step, min(args.steps, 200), 10)
+        dec_alg = state_bytes + N * H * (4 * D * 2 + 2 + D * 2)
+        secondary["two_call_step"] = {
+            "step": "kda_conv_short + kda_decode", "us_per_step": round(ms2 * 1e3, 2),
+            "state_GB_s": round(state_bytes / (ms2 * 1e-3) / 1e9, 1),
+            "decode_kernel": {"avg_launch_us": round(k2 * 1e3, 3), "alg_bytes_per_launch": dec_alg,
+                              "GB_s": round(dec_alg / (k2 * 1e-3) / 1e9, 1),
+                              "traffic": traffic_for("decode_step_kernel_d128_bf16", "kda_step.hip", N * H)}}
         # hot: one pool only (state may sit in the Infinity Cache) -- labelled, not the value
         s0 = slot_sets[0]
         for _ in range(20):
@@ -242,7 +288,7 @@ def bench_decode(args, torch, K, make_workload):
         torch.cuda.synchronize()
         hot_us = a_.elapsed_time(b2) / 200 * 1e3
         secondary["decode_hot_single_pool"] = {"us": round(hot_us, 2),
-                                               "GB_s": round(alg_bytes / hot_us / 1e3, 1)}
+                                               "GB_s": round(dec_alg / hot_us / 1e3, 1)}
         # plain device copy of the same bytes (torch copy kernel) as a practical ceiling
         src_t = torch.empty(state_bytes // 8, dtype=torch.float32, device=dev)
         dst_t = torch.empty_like(src_t)
@@ -272,7 +318,8 @@ def bench_decode(args, torch, K, make_workload):
     cfg = {"workload": "batched decode: 128 seqs x 1 token, H=16, d_k=d_v=128, conv W=4 "
                        "over 6144 q/k/v channels, bf16 inputs, fp32 state",
            "n_seq": N, "H": H, "d": D, "conv_W": W, "state_pools_rotated": P,
-           "step": "kda_conv_short + kda_decode", "value_counts": "recurrent state read+write"}
+           "step": "kda_decode_conv (conv + SiLU of the q/k/v projections, q/k L2 norm, recurrence; "
+                   "one launch)", "value_counts": "recurrent state read+write"}
     return {"metric": METRIC, "value": round(value, 1), "unit": "GB/s", "ms_per_step": ms_step,
             "dtype": "f32", "config": cfg, "roofline": roof, "cpu_baseline": cpu,
             "secondary": secondary, "wall_s": round(wall, 3)}
@@ -514,20 +561,21 @@ def cpu_decode(args, wl, state_bytes):
     orc.set_threads(threads)
     init = wl.init_states.double().numpy()
     has = np.ones(wl.n_seq, np.int32)
-    q, k, v, g, b = (t.float().numpy() for t in (wl.q, wl.k, wl.v, wl.g, wl.beta))
+    g, b = (t.float().numpy() for t in (wl.g, wl.beta))
     cx, cw, cs = wl.conv_x.float().numpy(), wl.conv_w.float().numpy(), wl.conv_state.float().numpy()
+    del has
     reps = 0
     t0 = time.perf_counter()
     while True:
-        orc.conv_short(cx, cw, wl.cu_seqlens, state=cs)
-        orc.kda_varlen(q, k, v, g, b, wl.cu_seqlens, init=init, has_init=has)
+        orc.kda_decode_conv(cx, cw, g, b, init, cs, H=wl.H, d=wl.dk, act=1, qk_l2norm=1)
         reps += 1
         if time.perf_counter() - t0 > args.cpu_seconds:
             break
     dt = time.perf_counter() - t0
     return {"value": round(state_bytes * reps / dt / 1e9, 3), "unit": "GB/s", "cores": orc.threads(),
             "kind": "oracle", "cpu": cpu_info(),
-            "sample": f"{reps} whole decode steps (conv + 128 seqs x 16 heads x 1 token, fp64 oracle), "
+            "sample": f"{reps} whole fused decode steps (conv + SiLU + q/k norm + 128 seqs x 16 heads "
+                      f"x 1 token, fp64 oracle), "
                       f"{dt:.1f} s"}
 
 

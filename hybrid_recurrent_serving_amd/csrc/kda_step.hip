@@ -309,7 +309,33 @@ decode_conv_kernel(const DecodeConvParams p) {
   const bool has_src = src >= 0 && src < p.n_slots;
   const bool has_dst = dst >= 0 && dst < p.n_slots;
 
-  // state slice first: the longest-latency traffic of the step
+  // The conv items' few loads go out first, then the state slice (the bulk
+  // of the traffic): the convolution is then done while the slice streams in.
+  const bool conv_item = static_cast<int>(threadIdx.x) < NCI;
+  const int t = conv_item ? static_cast<int>(threadIdx.x) : 0;
+  const int blk = t / (D / V);                 // 0 q, 1 k, 2 v
+  const int cc = (t % (D / V)) * V;            // channel inside the head's block
+  const int64_t C = 3LL * p.H * D;
+  const int64_t ch = static_cast<int64_t>(blk) * p.H * D + static_cast<int64_t>(h) * D + cc;
+  const int csrc = p.csrc[s];
+  const int cdst = p.cdst[s];
+  const bool has_hist = conv_item && csrc >= 0 && csrc < p.n_cslots;
+  // taps: the V * W values of channels ch .. ch + V - 1 are contiguous
+  // (W 16-byte vectors), tapf[b][e] = weight[(b V + e) / W, (b V + e) % W];
+  // history likewise (W - 1 vectors); the token (one vector)
+  float tapf[W][V], histf[HW > 0 ? HW : 1][V], xt[V];
+  if (conv_item) {
+    const Tin* wp = static_cast<const Tin*>(p.w) + ch * W;
+#pragma unroll
+    for (int b = 0; b < W; ++b) Vec16x<Tin>::ld(wp + b * V, tapf[b]);
+    Vec16x<Tin>::ld(static_cast<const Tin*>(p.x) + static_cast<int64_t>(s) * p.x_stride + ch, xt);
+  }
+  if (has_hist) {
+    const Tin* hp = static_cast<const Tin*>(p.cpool) + (static_cast<int64_t>(csrc) * C + ch) * HW;
+#pragma unroll
+    for (int b = 0; b < HW; ++b) Vec16x<Tin>::ld(hp + b * V, histf[b]);
+  }
+
   float S[L::RPL][4];
   if (has_src) {
     const float* sp = p.pool + ((static_cast<int64_t>(src) * p.H + h) * D + row0) * D + col;
@@ -326,45 +352,16 @@ decode_conv_kernel(const DecodeConvParams p) {
   const float beta = io<Tin>::ld(static_cast<const Tin*>(p.beta) + static_cast<int64_t>(s) * p.beta_stride + h);
 
   // ---- convolution of this head's q, k, v channels
-  if (static_cast<int>(threadIdx.x) < NCI) {
-    const int t = threadIdx.x;
-    const int blk = t / (D / V);                 // 0 q, 1 k, 2 v
-    const int cc = (t % (D / V)) * V;            // channel inside the head's block
-    const int64_t C = 3LL * p.H * D;
-    const int64_t ch = static_cast<int64_t>(blk) * p.H * D + static_cast<int64_t>(h) * D + cc;
-    // taps: the V * W values of channels ch .. ch + V - 1 are contiguous
-    // (W 16-byte vectors); wt[i][j] = weight[ch + i, j]
-    float wt[V][W];
-    {
-      const Tin* wp = static_cast<const Tin*>(p.w) + ch * W;
+  if (conv_item) {
+    float wt[V][W], hist[V][HW > 0 ? HW : 1];
 #pragma unroll
-      for (int b = 0; b < W; ++b) {
-        float f[V];
-        Vec16x<Tin>::ld(wp + b * V, f);
+    for (int b = 0; b < W; ++b)
 #pragma unroll
-        for (int e = 0; e < V; ++e) wt[(b * V + e) / W][(b * V + e) % W] = f[e];
-      }
-    }
-    // history: V * (W-1) contiguous values, hist[i][j] = pool[slot, ch + i, j]
-    float hist[V][HW];
+      for (int e = 0; e < V; ++e) wt[(b * V + e) / W][(b * V + e) % W] = tapf[b][e];
 #pragma unroll
-    for (int i = 0; i < V; ++i)
+    for (int b = 0; b < HW; ++b)
 #pragma unroll
-      for (int j = 0; j < HW; ++j) hist[i][j] = 0.f;
-    const int csrc = p.csrc[s];
-    const int cdst = p.cdst[s];
-    if (csrc >= 0 && csrc < p.n_cslots) {
-      const Tin* hp = static_cast<const Tin*>(p.cpool) + (static_cast<int64_t>(csrc) * C + ch) * HW;
-#pragma unroll
-      for (int b = 0; b < HW; ++b) {
-        float f[V];
-        Vec16x<Tin>::ld(hp + b * V, f);
-#pragma unroll
-        for (int e = 0; e < V; ++e) hist[(b * V + e) / HW][(b * V + e) % HW] = f[e];
-      }
-    }
-    float xt[V];
-    Vec16x<Tin>::ld(static_cast<const Tin*>(p.x) + static_cast<int64_t>(s) * p.x_stride + ch, xt);
+      for (int e = 0; e < V; ++e) hist[(b * V + e) / HW][(b * V + e) % HW] = has_hist ? histf[b][e] : 0.f;
 #pragma unroll
     for (int i = 0; i < V; ++i) {
       // tap W-1 multiplies the token, tap j < W-1 the history value j
