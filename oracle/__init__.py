@@ -239,6 +239,49 @@ class Oracle:
                               _as_f32(beta)[:, None], init, scale=scale)
         return {"o": res["o"][:, 0], "state": res["committed"], "conv_state": ns}
 
+    def kda_verify_conv(self, x, w, g, beta, init, conv_state, accepted_len=None, *, H, d, bias=None,
+                        act=0, qk_l2norm=1, norm_eps=1e-6, scale=1.0):
+        """Speculative verify with the short convolution in front.
+
+        x [N, Ts, 3 H d] (the Ts tokens' raw q | k | v projections);
+        conv_state [N, 3 H d, W-1]; g [N, Ts, H, d]; beta [N, Ts, H];
+        init [N, H, d, d]; accepted_len [N] or None (= Ts).
+
+        Per sequence: y = conv(conv_state ++ x) over the Ts tokens (+ SiLU),
+        q, k, v its blocks, q / k normalised per token and head when
+        qk_l2norm, then :meth:`kda_verify`.  The conv history is advanced by
+        the accepted length (the W-1 raw inputs ending at token L-1).
+
+        Returns dict o [N, Ts, H, d], committed [N, H, d, d] (NaN where
+        rejected), committed_len [N], conv_state [N, 3 H d, W-1] (NaN where
+        rejected)."""
+        x = np.asarray(_as_f32(x), np.float64)
+        N, Ts, C = x.shape
+        if C != 3 * H * d:
+            raise ValueError("x must have 3 * H * d channels")
+        st = np.asarray(_as_f32(conv_state), np.float32)
+        W = st.shape[-1] + 1
+        cu = (np.arange(N + 1) * Ts).astype(np.int32)
+        y, _ = self.conv_short(x.reshape(N * Ts, C).astype(np.float32), w, cu, bias=bias, act=act,
+                               state=st)
+        y = np.asarray(y, np.float64).reshape(N, Ts, 3, H, d)
+        q, k, v = y[:, :, 0], y[:, :, 1], y[:, :, 2]
+        if qk_l2norm:
+            q = q / np.sqrt((q * q).sum(-1, keepdims=True) + norm_eps)
+            k = k / np.sqrt((k * k).sum(-1, keepdims=True) + norm_eps)
+        res = self.kda_verify(q.astype(np.float32), k.astype(np.float32), v.astype(np.float32), g, beta,
+                              init, accepted_len, scale=scale)
+        # conv history after L tokens: the last W-1 entries of history ++ x[:L]
+        L = np.full(N, Ts, np.int64) if accepted_len is None else np.asarray(_as_i32(accepted_len), np.int64)
+        ns = np.full((N, C, W - 1), np.nan)
+        for s in range(N):
+            if 0 <= L[s] <= Ts:
+                xb = np.concatenate([st[s].astype(np.float64), x[s, :L[s]].T], axis=1)  # [C, W-1+L]
+                ns[s] = xb[:, -(W - 1):]
+        out = dict(res)
+        out["conv_state"] = ns
+        return out
+
 
 _cache: dict = {}
 

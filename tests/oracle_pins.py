@@ -346,5 +346,49 @@ def pin_decode_conv(orc):
     np.testing.assert_allclose(a["state"], b["state"], rtol=tol, atol=tol)
 
 
+def pin_verify_conv(orc):
+    """Fused verify: with Ts = 1 it is the fused decode step; stepping the
+    fused decode step token by token gives every output and, after L steps,
+    the committed state and conv history; a rejected length commits
+    nothing."""
+    tol = max(_tol(orc) * 10, 1e-6)
+    r = _rng(61)
+    N, Ts, H, d, W = 3, 4, 2, 5, 4
+    C = 3 * H * d
+    x = r.standard_normal((N, Ts, C)).astype(np.float32)
+    w = r.uniform(-0.5, 0.5, (C, W)).astype(np.float32)
+    bias = (0.1 * r.standard_normal(C)).astype(np.float32)
+    cst = r.standard_normal((N, C, W - 1)).astype(np.float32)
+    g = (-np.log1p(np.exp(-r.standard_normal((N, Ts, H, d))))).astype(np.float32)
+    beta = (1 / (1 + np.exp(-r.standard_normal((N, Ts, H))))).astype(np.float32)
+    S0 = r.standard_normal((N, H, d, d)) * 0.5
+    L = np.array([2, 4, 7], np.int32)   # the third is rejected
+    res = orc.kda_verify_conv(x, w, g, beta, S0, cst, L, H=H, d=d, bias=bias, act=1, qk_l2norm=1,
+                              scale=0.8)
+    one = orc.kda_verify_conv(x[:, :1], w, g[:, :1], beta[:, :1], S0, cst, None, H=H, d=d, bias=bias,
+                              act=1, qk_l2norm=1, scale=0.8)
+    dec = orc.kda_decode_conv(x[:, 0], w, g[:, 0], beta[:, 0], S0, cst, H=H, d=d, bias=bias, act=1,
+                              qk_l2norm=1, scale=0.8)
+    np.testing.assert_allclose(one["o"][:, 0], dec["o"], rtol=tol, atol=tol)
+    np.testing.assert_allclose(one["committed"], dec["state"], rtol=tol, atol=tol)
+    assert np.array_equal(one["conv_state"], dec["conv_state"].astype(np.float64))
+    # token by token through the fused decode step
+    S = S0.copy()
+    hist = cst.copy()
+    for t in range(Ts):
+        step = orc.kda_decode_conv(x[:, t], w, g[:, t], beta[:, t], S, hist, H=H, d=d, bias=bias, act=1,
+                                   qk_l2norm=1, scale=0.8)
+        np.testing.assert_allclose(res["o"][:, t], step["o"], rtol=tol, atol=tol)
+        S = step["state"]
+        hist = step["conv_state"].astype(np.float32)
+        for s in range(N):
+            if L[s] == t + 1:
+                np.testing.assert_allclose(res["committed"][s], S[s], rtol=tol, atol=tol)
+                assert np.array_equal(res["conv_state"][s], hist[s].astype(np.float64))
+    assert res["committed_len"][2] == -1
+    assert np.all(np.isnan(res["committed"][2])) and np.all(np.isnan(res["conv_state"][2]))
+
+
 ALL_PINS = [pin_bruteforce, pin_readback, pin_pure_decay, pin_linearity, pin_resume,
-            pin_varlen_independent, pin_verify, pin_ckpt_positions, pin_conv, pin_decode_conv]
+            pin_varlen_independent, pin_verify, pin_ckpt_positions, pin_conv, pin_decode_conv,
+            pin_verify_conv]
