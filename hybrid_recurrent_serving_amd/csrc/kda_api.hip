@@ -133,6 +133,7 @@ size_t kda_args_sizeof(int which) {
     case 2: return sizeof(kda_decode_args);
     case 3: return sizeof(kda_verify_args);
     case 4: return sizeof(kda_decode_conv_args);
+    case 5: return sizeof(kda_verify_conv_args);
     default: return 0;
   }
 }
@@ -298,6 +299,57 @@ int kda_decode_conv(const kda_decode_conv_args* a, kda_stream_t stream_) {
   p.n_seq = b.n_seq; p.H = b.H; p.W = b.W; p.act = b.act; p.qk_l2norm = b.qk_l2norm;
   p.eps = b.norm_eps; p.scale = b.scale;
   return launch_decode_conv(p, b.d, in_dt, out_dt, stream);
+}
+
+int kda_verify_conv(const kda_verify_conv_args* a, kda_stream_t stream_) {
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  if (!a) return fail(KDA_ERR_NULL, "args is NULL");
+  if (a->struct_size != sizeof(kda_verify_conv_args)) return fail(KDA_ERR_ARG, "struct_size mismatch");
+  if (a->n_seq < 0 || a->n_slots < 0 || a->n_conv_slots < 0) return fail(KDA_ERR_SHAPE, "negative size");
+  if (a->T_spec < 1 || a->T_spec > 16) return fail(KDA_ERR_SHAPE, "T_spec = %d (1..16)", a->T_spec);
+  if (a->n_seq == 0) return KDA_OK;
+  kda_verify_conv_args b = *a;
+  const int in_dt = b.in_dtype, out_dt = b.out_dtype;
+  if (in_dt != KDA_BF16 && in_dt != KDA_F32) return fail(KDA_ERR_DTYPE, "in_dtype %d", in_dt);
+  if (out_dt != KDA_BF16 && out_dt != KDA_F32) return fail(KDA_ERR_DTYPE, "out_dtype %d", out_dt);
+  if (b.H <= 0) return fail(KDA_ERR_SHAPE, "H = %d", b.H);
+  if (!supported_d(b.d, b.d)) return fail(KDA_ERR_UNSUPPORTED, "d = %d (16/32/64/128)", b.d);
+  if (b.W < 2 || b.W > 4) return fail(KDA_ERR_UNSUPPORTED, "verify_conv: W = %d (2..4)", b.W);
+  if (b.act != 0 && b.act != 1) return fail(KDA_ERR_ARG, "verify_conv: act = %d (0 none, 1 SiLU)", b.act);
+  if (b.qk_l2norm != 0 && b.qk_l2norm != 1) return fail(KDA_ERR_ARG, "verify_conv: qk_l2norm = %d", b.qk_l2norm);
+  if (!(b.norm_eps >= 0.f)) return fail(KDA_ERR_ARG, "verify_conv: norm_eps < 0");
+  if (!b.o && !b.accepted_len) return fail(KDA_ERR_NULL, "verify_conv: neither o nor accepted_len given");
+  if (!b.x || !b.conv_weight || !b.conv_pool || !b.conv_src_slot || !b.conv_dst_slot || !b.g || !b.beta ||
+      !b.state_pool || !b.src_slot || !b.dst_slot)
+    return fail(KDA_ERR_NULL, "verify_conv: required pointer is NULL");
+  const int64_t C = 3LL * b.H * b.d;
+  const int64_t eb = dtype_bytes(in_dt);
+  if (b.x_stride == 0) b.x_stride = C;
+  if (b.x_stride < C) return fail(KDA_ERR_SHAPE, "verify_conv: x_stride < 3 H d");
+  if (!aligned16(b.x) || !aligned16(b.conv_weight) || !aligned16(b.conv_pool) || !aligned16(b.g) ||
+      (b.o && !aligned16(b.o)) || !aligned16(b.state_pool) || (b.x_stride * eb) % 16)
+    return fail(KDA_ERR_ALIGN, "verify_conv: x, conv_weight, conv_pool, g, o or state_pool not 16-byte aligned");
+  int st;
+  if ((st = fix_stride(b.g_stride, (int64_t)b.H * b.d, in_dt, "g"))) return st;
+  if ((st = fix_stride(b.o_stride, (int64_t)b.H * b.d, out_dt, "o"))) return st;
+  if ((st = fix_beta_stride(b.beta_stride, b.H))) return st;
+  if ((int64_t)b.n_seq * b.H > 0x7fffffffLL) return fail(KDA_ERR_SHAPE, "n_seq * H too large");
+  if (check_enabled()) {
+    st = check_slots(b.src_slot, b.dst_slot, b.n_seq, b.n_slots, nullptr, stream);
+    if (st) return st;
+    st = check_slots(b.conv_src_slot, b.conv_dst_slot, b.n_seq, b.n_conv_slots, nullptr, stream);
+    if (st) return st;
+  }
+  DecodeConvParams p{};
+  p.x = b.x; p.w = b.conv_weight; p.bias = b.conv_bias; p.g = b.g; p.beta = b.beta;
+  p.cpool = b.conv_pool; p.o = b.o; p.pool = b.state_pool;
+  p.csrc = b.conv_src_slot; p.cdst = b.conv_dst_slot; p.src_slot = b.src_slot; p.dst_slot = b.dst_slot;
+  p.x_stride = b.x_stride; p.g_stride = b.g_stride; p.beta_stride = b.beta_stride; p.o_stride = b.o_stride;
+  p.n_slots = b.n_slots; p.n_cslots = b.n_conv_slots;
+  p.n_seq = b.n_seq; p.H = b.H; p.W = b.W; p.act = b.act; p.qk_l2norm = b.qk_l2norm;
+  p.eps = b.norm_eps; p.scale = b.scale;
+  p.T_spec = b.T_spec; p.accepted_len = b.accepted_len; p.committed_len_out = b.committed_len_out;
+  return launch_verify_conv(p, b.d, in_dt, out_dt, stream);
 }
 
 int kda_verify(const kda_verify_args* a, kda_stream_t stream_) {

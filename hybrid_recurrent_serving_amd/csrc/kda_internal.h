@@ -41,9 +41,15 @@ struct DecodeConvParams {
   int64_t n_slots, n_cslots;
   int32_t n_seq, H, W, act, qk_l2norm;
   float eps, scale;
+  // verify only: tokens per sequence (x, g, beta, o strides are per token)
+  // and the commit at the accepted length (NULL: outputs only, no commit)
+  int32_t T_spec;
+  const int32_t* accepted_len;
+  int32_t* committed_len_out;
 };
 
 int launch_decode_conv(const DecodeConvParams& p, int D, int in_dtype, int out_dtype, hipStream_t stream);
+int launch_verify_conv(const DecodeConvParams& p, int D, int in_dtype, int out_dtype, hipStream_t stream);
 
 // ---------------------------------------------------------------- conv
 struct ConvParams {

@@ -485,6 +485,296 @@ int launch_decode_conv(const DecodeConvParams& p, int D, int in_dtype, int out_d
   }
 }
 
+// ---------------------------------------------------------------------------
+// Speculative verify with the short convolution fused in.  As the staged
+// verify of step_kernel, with q, k, v of the T_spec tokens formed in LDS by
+// the conv items: each owns V channels of the head's q, k or v block, keeps
+// the T_spec raw token vectors and a W-tap sliding window in registers, and
+// writes y (fp32) per token.  The q / k norms of token j are formed in the
+// token loop from LDS (every wave, no extra barrier).  The conv history is
+// committed with the state: the W-1 raw inputs ending at token L-1.
+template <int D, typename Tin, typename Tout, int W>
+__global__ void __launch_bounds__(64 * StepLayout<D>::WPH)
+verify_conv_kernel(const DecodeConvParams p) {
+  using L = StepLayout<D>;
+  constexpr int NTH = 64 * L::WPH;
+  constexpr int V = Vec16x<Tin>::N;
+  constexpr int NCI = 3 * D / V;
+  constexpr int HW = W - 1;
+  static_assert(NCI <= NTH, "one conv item per thread");
+  extern __shared__ __align__(16) float s_dyn[];
+  const int T = p.T_spec;
+  const int TD = T * D;
+  float* const s_a = s_dyn;            // exp(g) [T][D]
+  float* const s_k = s_dyn + TD;       // k [T][D]
+  float* const s_q = s_dyn + 2 * TD;   // q [T][D]
+  float* const s_v = s_dyn + 3 * TD;   // v [T][D]
+  float* const s_o = s_dyn + 4 * TD;   // o [T][D]
+  float* const s_b = s_dyn + 5 * TD;   // beta [T]
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t sh = blockIdx.x;
+  const int s = static_cast<int>(sh / p.H);
+  const int h = static_cast<int>(sh % p.H);
+  const int cg = lane % L::LPR;
+  const int rg = lane / L::LPR;
+  const int col = wave * L::COLS + 4 * cg;
+  const int row0 = rg * L::RPL;
+
+  const int src = p.src_slot[s];
+  const int dst = p.dst_slot[s];
+  const bool has_src = src >= 0 && src < p.n_slots;
+  const bool has_dst = dst >= 0 && dst < p.n_slots;
+  int Lc = -1;
+  bool valid = false;
+  if (p.accepted_len) {
+    Lc = p.accepted_len[s];
+    valid = Lc >= 0 && Lc <= T;
+    if (h == 0 && threadIdx.x == 0 && p.committed_len_out) p.committed_len_out[s] = valid ? Lc : -1;
+  }
+  const bool do_store = valid && has_dst;
+  const int n_tok = p.o ? T : (valid ? Lc : 0);
+
+  // conv items: taps, history and the T raw token vectors first
+  const bool conv_item = static_cast<int>(threadIdx.x) < NCI;
+  const int t = conv_item ? static_cast<int>(threadIdx.x) : 0;
+  const int blk = t / (D / V);
+  const int cc = (t % (D / V)) * V;
+  const int64_t C = 3LL * p.H * D;
+  const int64_t ch = static_cast<int64_t>(blk) * p.H * D + static_cast<int64_t>(h) * D + cc;
+  const int csrc = p.csrc[s];
+  const int cdst = p.cdst[s];
+  const bool has_hist = conv_item && csrc >= 0 && csrc < p.n_cslots;
+  const Tin* xs = static_cast<const Tin*>(p.x) + static_cast<int64_t>(s) * T * p.x_stride + ch;
+  float tapf[W][V], histf[HW][V];
+  uint4 raw[STEP_TMAX];
+  if (conv_item) {
+    const Tin* wp = static_cast<const Tin*>(p.w) + ch * W;
+#pragma unroll
+    for (int b = 0; b < W; ++b) Vec16x<Tin>::ld(wp + b * V, tapf[b]);
+#pragma unroll
+    for (int j = 0; j < STEP_TMAX; ++j)
+      if (j < T) raw[j] = *reinterpret_cast<const uint4*>(xs + static_cast<int64_t>(j) * p.x_stride);
+  }
+  if (has_hist) {
+    const Tin* hp = static_cast<const Tin*>(p.cpool) + (static_cast<int64_t>(csrc) * C + ch) * HW;
+#pragma unroll
+    for (int b = 0; b < HW; ++b) Vec16x<Tin>::ld(hp + b * V, histf[b]);
+  }
+
+  // the convolution over the tokens: y_j = bias + sum_i w[i] xbar[j + i]
+  if (conv_item) {
+    float wt[V][W], win[V][W];
+#pragma unroll
+    for (int b = 0; b < W; ++b)
+#pragma unroll
+      for (int e = 0; e < V; ++e) wt[(b * V + e) / W][(b * V + e) % W] = tapf[b][e];
+#pragma unroll
+    for (int b = 0; b < HW; ++b)
+#pragma unroll
+      for (int e = 0; e < V; ++e) win[(b * V + e) / HW][(b * V + e) % HW] = has_hist ? histf[b][e] : 0.f;
+    float bias[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) bias[i] = p.bias ? io<Tin>::ld(static_cast<const Tin*>(p.bias) + ch + i) : 0.f;
+    float* yb = blk == 0 ? s_q : (blk == 1 ? s_k : s_v);
+#pragma unroll
+    for (int j = 0; j < STEP_TMAX; ++j) {
+      if (j < n_tok) {
+        float xt[V];
+        if constexpr (sizeof(Tin) == 2) {
+          const uint32_t wv[4] = {raw[j].x, raw[j].y, raw[j].z, raw[j].w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            xt[2 * q] = __uint_as_float(wv[q] << 16);
+            xt[2 * q + 1] = __uint_as_float(wv[q] & 0xffff0000u);
+          }
+        } else {
+          xt[0] = __uint_as_float(raw[j].x); xt[1] = __uint_as_float(raw[j].y);
+          xt[2] = __uint_as_float(raw[j].z); xt[3] = __uint_as_float(raw[j].w);
+        }
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+          win[i][HW] = xt[i];
+          float acc = bias[i];
+#pragma unroll
+          for (int k = 0; k < W; ++k) acc = fmaf(wt[i][k], win[i][k], acc);
+          if (p.act == 1) acc = acc / (1.f + expf(-acc));
+          yb[j * D + cc + i] = acc;
+#pragma unroll
+          for (int k = 0; k < HW; ++k) win[i][k] = win[i][k + 1];
+        }
+      }
+    }
+    // conv history after the accepted tokens: xbar[Lc .. Lc + W - 2] with
+    // xbar = history ++ tokens (token values re-read from x)
+    if (valid && cdst >= 0 && cdst < p.n_cslots) {
+      float nh[V * HW];
+#pragma unroll
+      for (int j = 0; j < HW; ++j) {
+        const int idx = Lc + j;
+        float val[V];
+        if (idx < HW) {
+#pragma unroll
+          for (int i = 0; i < V; ++i) {
+            float hv = 0.f;
+#pragma unroll
+            for (int k = 0; k < HW; ++k)
+              if (k == idx) hv = has_hist ? histf[(i * HW + k) / V][(i * HW + k) % V] : 0.f;
+            val[i] = hv;
+          }
+        } else {
+          Vec16x<Tin>::ld(xs + static_cast<int64_t>(idx - HW) * p.x_stride, val);
+        }
+#pragma unroll
+        for (int i = 0; i < V; ++i) nh[i * HW + j] = val[i];
+      }
+      Tin* np_ = static_cast<Tin*>(p.cpool) + (static_cast<int64_t>(cdst) * C + ch) * HW;
+#pragma unroll
+      for (int b = 0; b < HW; ++b) {
+        float f[V];
+#pragma unroll
+        for (int e = 0; e < V; ++e) f[e] = nh[b * V + e];
+        Vec16x<Tin>::st(np_ + b * V, f);
+      }
+    }
+  }
+  // state slice (the conv registers are dead by now), then exp(g) and beta
+  // of the tokens into LDS
+  float S[L::RPL][4];
+  if (has_src) {
+    const float* sp = p.pool + ((static_cast<int64_t>(src) * p.H + h) * D + row0) * D + col;
+#pragma unroll
+    for (int i = 0; i < L::RPL; ++i) ld4_stream(sp + static_cast<int64_t>(i) * D, S[i]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < L::RPL; ++i) S[i][0] = S[i][1] = S[i][2] = S[i][3] = 0.f;
+  }
+  // exp(g) and beta of the tokens into LDS
+  {
+    const Tin* gb = static_cast<const Tin*>(p.g);
+    const Tin* bb = static_cast<const Tin*>(p.beta);
+    for (int e = 4 * static_cast<int>(threadIdx.x); e < n_tok * D; e += 4 * NTH) {
+      const int j = e / D, c = e % D;
+      const int64_t tok = static_cast<int64_t>(s) * T + j;
+      float g4[4];
+      io<Tin>::ld4(gb + tok * p.g_stride + static_cast<int64_t>(h) * D + c, g4);
+      *reinterpret_cast<float4*>(&s_a[j * D + c]) = make_float4(expf(g4[0]), expf(g4[1]), expf(g4[2]), expf(g4[3]));
+      if (c == 0) s_b[j] = io<Tin>::ld(bb + tok * p.beta_stride + h);
+    }
+  }
+  __syncthreads();
+
+  float* dp = has_dst ? p.pool + ((static_cast<int64_t>(dst) * p.H + h) * D + row0) * D + col : nullptr;
+  if (do_store && Lc == 0) {
+#pragma unroll
+    for (int i = 0; i < L::RPL; ++i) st4_stream(dp + static_cast<int64_t>(i) * D, S[i]);
+  }
+  for (int j = 0; j < n_tok; ++j) {
+    float inv_q = 1.f, inv_k = 1.f;
+    if (p.qk_l2norm) {
+      float sq = 0.f, sk = 0.f;
+#pragma unroll
+      for (int c = lane; c < D; c += 64) {
+        sq = fmaf(s_q[j * D + c], s_q[j * D + c], sq);
+        sk = fmaf(s_k[j * D + c], s_k[j * D + c], sk);
+      }
+      inv_q = 1.f / sqrtf(wave_sum_from<1>(sq) + p.eps);
+      inv_k = 1.f / sqrtf(wave_sum_from<1>(sk) + p.eps);
+    }
+    float kr[L::RPL], qr[L::RPL], ar[L::RPL], vc[4];
+#pragma unroll
+    for (int i = 0; i < L::RPL; i += 4) {
+      const float4 k4 = *reinterpret_cast<const float4*>(&s_k[j * D + row0 + i]);
+      const float4 q4 = *reinterpret_cast<const float4*>(&s_q[j * D + row0 + i]);
+      const float4 a4 = *reinterpret_cast<const float4*>(&s_a[j * D + row0 + i]);
+      kr[i] = k4.x * inv_k; kr[i + 1] = k4.y * inv_k; kr[i + 2] = k4.z * inv_k; kr[i + 3] = k4.w * inv_k;
+      qr[i] = q4.x * inv_q; qr[i + 1] = q4.y * inv_q; qr[i + 2] = q4.z * inv_q; qr[i + 3] = q4.w * inv_q;
+      ar[i] = a4.x; ar[i + 1] = a4.y; ar[i + 2] = a4.z; ar[i + 3] = a4.w;
+    }
+    const float4 v4 = *reinterpret_cast<const float4*>(&s_v[j * D + col]);
+    vc[0] = v4.x; vc[1] = v4.y; vc[2] = v4.z; vc[3] = v4.w;
+    const float beta = s_b[j];
+    float w[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < L::RPL; ++i) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        S[i][c] *= ar[i];
+        w[c] = fmaf(S[i][c], kr[i], w[c]);
+      }
+    }
+    float u[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      w[c] = wave_sum_from<L::LPR>(w[c]);
+      u[c] = beta * (vc[c] - w[c]);
+    }
+    float o[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < L::RPL; ++i) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        S[i][c] = fmaf(kr[i], u[c], S[i][c]);
+        o[c] = fmaf(S[i][c], qr[i], o[c]);
+      }
+    }
+    if (p.o) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) o[c] = wave_sum_from<L::LPR>(o[c]) * p.scale;
+      if (rg == 0) *reinterpret_cast<float4*>(&s_o[j * D + col]) = make_float4(o[0], o[1], o[2], o[3]);
+    }
+    if (do_store && j + 1 == Lc) {
+#pragma unroll
+      for (int i = 0; i < L::RPL; ++i) st4_stream(dp + static_cast<int64_t>(i) * D, S[i]);
+    }
+  }
+  if (p.o) {
+    __syncthreads();
+    Tout* ob = static_cast<Tout*>(p.o);
+    for (int e = 4 * threadIdx.x; e < n_tok * D; e += 4 * NTH) {
+      const int j = e / D, c = e % D;
+      const float4 o4 = *reinterpret_cast<const float4*>(&s_o[j * D + c]);
+      const float ov[4] = {o4.x, o4.y, o4.z, o4.w};
+      io<Tout>::st4(ob + (static_cast<int64_t>(s) * T + j) * p.o_stride + static_cast<int64_t>(h) * D + c, ov);
+    }
+  }
+}
+
+template <int D, typename Tin, typename Tout>
+static int launch_verify_conv_t(const DecodeConvParams& p, hipStream_t stream) {
+  using L = StepLayout<D>;
+  dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(p.n_seq) * p.H));
+  dim3 block(64 * L::WPH);
+  const size_t lds = (5 * static_cast<size_t>(p.T_spec) * D + p.T_spec) * sizeof(float);
+  switch (p.W) {
+    case 2: hipLaunchKernelGGL((verify_conv_kernel<D, Tin, Tout, 2>), grid, block, lds, stream, p); break;
+    case 3: hipLaunchKernelGGL((verify_conv_kernel<D, Tin, Tout, 3>), grid, block, lds, stream, p); break;
+    case 4: hipLaunchKernelGGL((verify_conv_kernel<D, Tin, Tout, 4>), grid, block, lds, stream, p); break;
+    default: return fail(KDA_ERR_UNSUPPORTED, "verify_conv: W = %d (2..4)", p.W);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, "verify_conv kernel launch: %s", hipGetErrorString(e));
+  return KDA_OK;
+}
+
+template <int D>
+static int launch_verify_conv_d(const DecodeConvParams& p, int in_dtype, int out_dtype, hipStream_t stream) {
+  if (in_dtype == KDA_BF16 && out_dtype == KDA_BF16) return launch_verify_conv_t<D, bf16_t, bf16_t>(p, stream);
+  if (in_dtype == KDA_BF16 && out_dtype == KDA_F32) return launch_verify_conv_t<D, bf16_t, float>(p, stream);
+  if (in_dtype == KDA_F32 && out_dtype == KDA_BF16) return launch_verify_conv_t<D, float, bf16_t>(p, stream);
+  return launch_verify_conv_t<D, float, float>(p, stream);
+}
+
+int launch_verify_conv(const DecodeConvParams& p, int D, int in_dtype, int out_dtype, hipStream_t stream) {
+  switch (D) {
+    case 16: return launch_verify_conv_d<16>(p, in_dtype, out_dtype, stream);
+    case 32: return launch_verify_conv_d<32>(p, in_dtype, out_dtype, stream);
+    case 64: return launch_verify_conv_d<64>(p, in_dtype, out_dtype, stream);
+    case 128: return launch_verify_conv_d<128>(p, in_dtype, out_dtype, stream);
+    default: return fail(KDA_ERR_UNSUPPORTED, "d = %d not built (16, 32, 64, 128)", D);
+  }
+}
+
 int launch_step(const StepParams& p, int D, int in_dtype, int out_dtype, hipStream_t stream) {
   switch (D) {
     case 16: return launch_step_d<16>(p, in_dtype, out_dtype, stream);

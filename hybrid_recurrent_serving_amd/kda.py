@@ -86,6 +86,22 @@ class DecodeConvArgs(ctypes.Structure):
     ]
 
 
+class VerifyConvArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", c_size),
+        ("x", c_vp), ("conv_weight", c_vp), ("conv_bias", c_vp), ("conv_pool", c_vp),
+        ("conv_src_slot", c_vp), ("conv_dst_slot", c_vp),
+        ("g", c_vp), ("beta", c_vp), ("o", c_vp),
+        ("state_pool", c_vp), ("src_slot", c_vp), ("dst_slot", c_vp),
+        ("accepted_len", c_vp), ("committed_len_out", c_vp),
+        ("x_stride", c_i64), ("g_stride", c_i64), ("beta_stride", c_i64), ("o_stride", c_i64),
+        ("n_slots", c_i64), ("n_conv_slots", c_i64),
+        ("n_seq", c_i32), ("T_spec", c_i32), ("H", c_i32), ("d", c_i32), ("W", c_i32), ("act", c_i32),
+        ("qk_l2norm", c_i32), ("norm_eps", c_f32), ("in_dtype", c_i32), ("out_dtype", c_i32),
+        ("scale", c_f32), ("reserved", c_i32),
+    ]
+
+
 class VerifyArgs(ctypes.Structure):
     _fields_ = [
         ("struct_size", c_size),
@@ -101,7 +117,7 @@ class VerifyArgs(ctypes.Structure):
 
 EXPORTS = ["kda_status_str", "kda_abi_version", "kda_last_error", "kda_args_sizeof",
            "kda_conv_short", "kda_ckpt_plan", "kda_prefill_workspace_bytes",
-           "kda_prefill_varlen", "kda_decode", "kda_verify", "kda_decode_conv"]
+           "kda_prefill_varlen", "kda_decode", "kda_verify", "kda_decode_conv", "kda_verify_conv"]
 
 _lib = None
 
@@ -134,8 +150,9 @@ def load_library(path: Optional[Path] = None):
     lib.kda_decode.argtypes = [ctypes.POINTER(DecodeArgs), c_vp]
     lib.kda_verify.argtypes = [ctypes.POINTER(VerifyArgs), c_vp]
     lib.kda_decode_conv.argtypes = [ctypes.POINTER(DecodeConvArgs), c_vp]
+    lib.kda_verify_conv.argtypes = [ctypes.POINTER(VerifyConvArgs), c_vp]
     for name in ("kda_conv_short", "kda_ckpt_plan", "kda_prefill_varlen", "kda_decode", "kda_verify",
-                 "kda_decode_conv"):
+                 "kda_decode_conv", "kda_verify_conv"):
         getattr(lib, name).restype = ctypes.c_int
     if path is None:
         _lib = lib
@@ -493,6 +510,63 @@ def prepare_decode_conv(x, conv_weight, conv_pool, conv_src_slot, conv_dst_slot,
     return Prepared(load_library().kda_decode_conv, a,
                     (x, conv_weight, conv_pool, conv_src_slot, conv_dst_slot, g, beta, o, state_pool,
                      src_slot, dst_slot, conv_bias))
+
+
+def kda_verify_conv(x, conv_weight, conv_pool, conv_src_slot, conv_dst_slot, g, beta, state_pool, src_slot,
+                    dst_slot, *, o=None, accepted_len=None, committed_len_out=None, conv_bias=None,
+                    act: int = 0, qk_l2norm: bool = True, norm_eps: float = 1e-6, scale=1.0, stream=None):
+    """Speculative verify with the short convolution fused in.  x [N, T_spec,
+    3 H d] (q | k | v projections of the tokens); g [N, T_spec, H, d]; beta
+    [N, T_spec, H]; o [N, T_spec, H, d] or None; conv and state pools as
+    kda_decode_conv."""
+    import torch
+    _expect(x.dim() == 3 and g.dim() == 4 and beta.dim() == 3,
+            "x [N, T_spec, 3 H d], g [N, T_spec, H, d], beta [N, T_spec, H]")
+    N, Ts, H, d = g.shape
+    _expect(tuple(x.shape) == (N, Ts, 3 * H * d), "x must be [N, T_spec, 3 H d]")
+    _same_lead([("beta", beta)], (N, Ts, H), "g")
+    _same_lead([("o", o)], (N, Ts, H, d), "g")
+    _expect(conv_weight.dim() == 2 and conv_weight.shape[0] == 3 * H * d and conv_weight.is_contiguous(),
+            "conv_weight must be contiguous [3 H d, W]")
+    W = conv_weight.shape[1]
+    _expect(conv_pool.dim() == 3 and tuple(conv_pool.shape[1:]) == (3 * H * d, W - 1)
+            and conv_pool.is_contiguous(), "conv_pool must be contiguous [n_slots, 3 H d, W-1]")
+    _expect(conv_bias is None or (conv_bias.numel() == 3 * H * d and conv_bias.is_contiguous()),
+            "conv_bias must be contiguous [3 H d]")
+    _expect(state_pool.dim() == 4 and tuple(state_pool.shape[1:]) == (H, d, d)
+            and state_pool.dtype == torch.float32 and state_pool.is_contiguous(),
+            "state_pool must be contiguous float32 [n_slots, H, d, d]")
+    for nm, t in (("src_slot", src_slot), ("dst_slot", dst_slot), ("conv_src_slot", conv_src_slot),
+                  ("conv_dst_slot", conv_dst_slot)):
+        _expect(t.numel() >= N, f"{nm} shorter than n_seq")
+    _expect(accepted_len is None or accepted_len.numel() >= N, "accepted_len shorter than n_seq")
+    _expect(committed_len_out is None or committed_len_out.numel() >= N, "committed_len_out shorter than n_seq")
+    _expect(x.stride(2) == 1 and x.stride(0) == Ts * x.stride(1), "x must be [N, T_spec, C] with token rows")
+    _device_tensors(x=x, conv_weight=conv_weight, conv_pool=conv_pool, conv_src_slot=conv_src_slot,
+                    conv_dst_slot=conv_dst_slot, g=g, beta=beta, o=o, state_pool=state_pool,
+                    src_slot=src_slot, dst_slot=dst_slot, accepted_len=accepted_len,
+                    committed_len_out=committed_len_out)
+    _same_dtype(x, conv_weight=conv_weight, conv_pool=conv_pool, g=g, beta=beta)
+    a = VerifyConvArgs()
+    a.struct_size = ctypes.sizeof(VerifyConvArgs)
+    a.x, a.conv_weight, a.conv_bias, a.conv_pool = map(_ptr, (x, conv_weight, conv_bias, conv_pool))
+    a.conv_src_slot, a.conv_dst_slot = _ptr(conv_src_slot), _ptr(conv_dst_slot)
+    a.g, a.beta, a.o = _ptr(g), _ptr(beta), _ptr(o)
+    a.state_pool, a.src_slot, a.dst_slot = _ptr(state_pool), _ptr(src_slot), _ptr(dst_slot)
+    a.accepted_len, a.committed_len_out = _ptr(accepted_len), _ptr(committed_len_out)
+    a.x_stride = x.stride(1)
+    for nm, t in (("g", g), ("beta", beta), ("o", o)):
+        _expect(t is None or t.stride(0) == Ts * t.stride(1), f"{nm}: sequence stride must be T_spec tokens")
+    a.g_stride, a.beta_stride = _tok_stride(g, 2), _tok_stride(beta, 1)
+    a.o_stride = _tok_stride(o, 2) if o is not None else 0
+    a.n_slots, a.n_conv_slots = state_pool.shape[0], conv_pool.shape[0]
+    a.n_seq, a.T_spec, a.H, a.d, a.W = N, Ts, H, d, W
+    a.act, a.qk_l2norm, a.norm_eps = int(act), int(qk_l2norm), float(norm_eps)
+    a.in_dtype = _dtype_code(x)
+    a.out_dtype = _dtype_code(o) if o is not None else KDA_BF16
+    a.scale = scale
+    _check(load_library().kda_verify_conv(ctypes.byref(a), _stream(stream)))
+    return o
 
 
 def kda_verify(q, k, v, g, beta, state_pool, src_slot, dst_slot, *, o=None, accepted_len=None,

@@ -83,7 +83,8 @@ int kda_abi_version(void);
 /* One-line reason for the calling thread's most recent non-OK status. */
 const char *kda_last_error(void);
 /* sizeof() of each args struct as compiled into the library: which = 0 conv,
- * 1 prefill, 2 decode, 3 verify, 4 decode_conv.  Returns 0 for other values. */
+ * 1 prefill, 2 decode, 3 verify, 4 decode_conv, 5 verify_conv.  Returns 0
+ * for other values. */
 size_t kda_args_sizeof(int which);
 
 /* ------------------------------------------------------------------------
@@ -308,6 +309,57 @@ typedef struct kda_decode_conv_args {
 } kda_decode_conv_args;
 
 int kda_decode_conv(const kda_decode_conv_args *args, kda_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * kda_verify_conv -- speculative verification with the short convolution
+ * fused in.
+ *
+ * kda_verify on q, k, v formed as in kda_decode_conv from the T_spec
+ * tokens' raw projections: the conv runs over (conv history ++ the tokens),
+ * q and k are normalised per token and head when qk_l2norm.  The accepted
+ * length commits both states: the recurrent state after L tokens to
+ * dst_slot and the conv history after L tokens (the W-1 raw inputs ending
+ * at token L-1) to conv_dst_slot.  Modes, accepted_len semantics and
+ * committed_len_out as kda_verify (outputs-only calls write neither state).
+ *
+ *   x   [n_seq, T_spec, 3 H d] in_dtype, token stride x_stride (0 = packed;
+ *       sequence stride T_spec * x_stride)
+ *   g   [n_seq, T_spec, H, d], beta [n_seq, T_spec, H], o [n_seq, T_spec, H, d]
+ *   other arguments as kda_decode_conv.
+ * Errors as kda_decode_conv; T_spec outside 1..16 -> KDA_ERR_SHAPE.
+ * ---------------------------------------------------------------------- */
+typedef struct kda_verify_conv_args {
+    size_t struct_size;          /* sizeof(kda_verify_conv_args) */
+    const void *x;               /* [n_seq, T_spec, 3 H d] raw projections */
+    const void *conv_weight;     /* [3 H d, W] */
+    const void *conv_bias;       /* [3 H d] or NULL */
+    void *conv_pool;             /* [n_conv_slots, 3 H d, W-1] */
+    const int32_t *conv_src_slot; /* [n_seq]; -1 = zero history */
+    const int32_t *conv_dst_slot; /* [n_seq]; -1 = do not write */
+    const void *g;               /* [n_seq, T_spec, H, d] */
+    const void *beta;            /* [n_seq, T_spec, H] */
+    void *o;                     /* [n_seq, T_spec, H, d] out_dtype, or NULL */
+    float *state_pool;           /* [n_slots, H, d, d] */
+    const int32_t *src_slot;     /* [n_seq] */
+    const int32_t *dst_slot;     /* [n_seq] */
+    const int32_t *accepted_len; /* [n_seq] or NULL */
+    int32_t *committed_len_out;  /* [n_seq] or NULL */
+    int64_t x_stride, g_stride, beta_stride, o_stride; /* per token; 0 = packed */
+    int64_t n_slots;
+    int64_t n_conv_slots;
+    int32_t n_seq;
+    int32_t T_spec;              /* 1..16 */
+    int32_t H, d;
+    int32_t W;                   /* conv width, 2..4 */
+    int32_t act;                 /* 0 none, 1 SiLU */
+    int32_t qk_l2norm;           /* 0 / 1 */
+    float norm_eps;              /* >= 0 */
+    int32_t in_dtype, out_dtype;
+    float scale;
+    int32_t reserved;
+} kda_verify_conv_args;
+
+int kda_verify_conv(const kda_verify_conv_args *args, kda_stream_t stream);
 
 /* ------------------------------------------------------------------------
  * kda_verify -- speculative verification with a commit at the accepted

@@ -35,7 +35,8 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_abi_version_and_struct_sizes(lib):
     assert lib.kda_abi_version() == 1
-    for which, cls in enumerate([K.ConvArgs, K.PrefillArgs, K.DecodeArgs, K.VerifyArgs, K.DecodeConvArgs]):
+    for which, cls in enumerate([K.ConvArgs, K.PrefillArgs, K.DecodeArgs, K.VerifyArgs, K.DecodeConvArgs,
+                                 K.VerifyConvArgs]):
         assert lib.kda_args_sizeof(which) == ctypes.sizeof(cls), cls.__name__
     assert lib.kda_args_sizeof(7) == 0
 
@@ -96,6 +97,35 @@ def test_decode_conv_validation(lib):
     assert _call(lib, f, _decode_conv_args(x_stride=100)) == 2       # < 3 H d
     assert _call(lib, f, _decode_conv_args(x_stride=769)) == 4       # rows not 16-byte aligned
     assert b"aligned" in lib.kda_last_error()
+
+
+def test_verify_conv_validation(lib):
+    f = "kda_verify_conv"
+    fake = 1 << 20
+
+    def args(**kw):
+        a = K.VerifyConvArgs()
+        a.struct_size = ctypes.sizeof(K.VerifyConvArgs)
+        for fld in ("x", "conv_weight", "conv_pool", "conv_src_slot", "conv_dst_slot", "g", "beta", "o",
+                    "state_pool", "src_slot", "dst_slot"):
+            setattr(a, fld, fake)
+        a.n_seq, a.T_spec, a.H, a.d, a.W, a.n_slots, a.n_conv_slots = 4, 8, 2, 128, 4, 4, 4
+        a.in_dtype, a.out_dtype, a.scale, a.norm_eps, a.qk_l2norm = 0, 0, 1.0, 1e-6, 1
+        for k, v in kw.items():
+            setattr(a, k, v)
+        return a
+
+    assert lib.kda_verify_conv(None, None) == 1
+    assert _call(lib, f, args(struct_size=8)) == 8
+    assert _call(lib, f, args(n_seq=0)) == 0
+    assert _call(lib, f, args(T_spec=0)) == 2
+    assert _call(lib, f, args(T_spec=17)) == 2
+    assert _call(lib, f, args(o=None)) == 1                 # neither o nor accepted_len
+    assert _call(lib, f, args(x=None)) == 1
+    assert _call(lib, f, args(d=96)) == 6
+    assert _call(lib, f, args(W=5)) == 6
+    assert _call(lib, f, args(act=3)) == 8
+    assert _call(lib, f, args(x_stride=769)) == 4
 
 
 def test_decode_validation(lib):

@@ -127,3 +127,103 @@ def test_decode_conv_fp32_small(dev, oracle64, d):
     U.assert_close("o", U.to_np(o), ref["o"], rel=1e-5, mx=1e-5)
     U.assert_close("state", U.to_np(st), ref["state"], rel=1e-5, mx=1e-5)
     _check_conv_state(cs, x, hist)
+
+
+def _verify_case(N, Ts, H, d, W, dtype, seed):
+    wl = make_workload(4, n_seq=N, H=H, d=d, seed=seed)
+    gen = torch.Generator().manual_seed(2000 + seed)
+    C = 3 * H * d
+    w, st, x = draw_conv(gen, N * Ts, C, W, N, dtype, torch.device("cpu"))
+    x = x.reshape(N, Ts, C)
+    return x, w, st, wl.g[:, :Ts].to(dtype).contiguous(), wl.beta[:, :Ts].to(dtype).contiguous(), wl.init_states
+
+
+def _run_verify(dev, x, w, cst, g, b, init, L, *, out_dtype, with_o=True, commit=True, conv_src=None,
+                act=1, norm=1):
+    N, Ts, C = x.shape
+    H, d = g.shape[2], g.shape[3]
+    W = w.shape[1]
+    cpool = torch.zeros(2 * N, C, W - 1, dtype=x.dtype, device=dev)
+    cpool[:N] = cst.to(dev)
+    pool = torch.zeros(2 * N, H, d, d, device=dev)
+    pool[:N] = init.to(dev)
+    pool[N:] = float("nan")           # destinations hold NaN until written
+    cpool[N:] = float("nan")
+    src = torch.arange(N, dtype=torch.int32, device=dev)
+    dst = src + N
+    csrc = torch.tensor(conv_src if conv_src is not None else list(range(N)), dtype=torch.int32, device=dev)
+    o = torch.empty(N, Ts, H, d, dtype=out_dtype, device=dev) if with_o else None
+    acc = torch.tensor(L, dtype=torch.int32, device=dev) if commit else None
+    clen = torch.full((N,), -7, dtype=torch.int32, device=dev)
+    K.kda_verify_conv(x.to(dev), w.to(dev), cpool, csrc, dst, g.to(dev), b.to(dev), pool, src, dst, o=o,
+                      accepted_len=acc, committed_len_out=clen if commit else None, act=act, qk_l2norm=norm)
+    torch.cuda.synchronize()
+    return o, pool[N:], cpool[N:], clen, pool[:N], cpool[:N]
+
+
+def _verify_reference(orc, x, w, cst, g, b, init, L, conv_src, act=1, norm=1):
+    N = x.shape[0]
+    H, d = g.shape[2], g.shape[3]
+    hist = cst.float().numpy().copy()
+    for s in range(N):
+        if conv_src[s] < 0:
+            hist[s] = 0.0
+    return orc.kda_verify_conv(x, w, g, b, init.double().numpy(), hist, L, H=H, d=d, act=act,
+                               qk_l2norm=norm), hist
+
+
+def test_verify_conv_batched_128x8(dev, oracle64):
+    """128 sequences x 8 tokens, H=16, d=128, W=4, bf16: outputs for all
+    positions, state and conv history committed at L ~ U{1..8} (one rejected
+    length, one L = 0), odd sequences without conv history."""
+    U.say("verify_conv batched 128 x 8 x H16 x d128")
+    N, Ts, H, d, W = 128, 8, 16, 128, 4
+    x, w, cst, g, b, init = _verify_case(N, Ts, H, d, W, torch.bfloat16, seed=41)
+    gen = torch.Generator().manual_seed(7)
+    L = torch.randint(1, Ts + 1, (N,), generator=gen).tolist()
+    L[3], L[10] = 9, 0
+    conv_src = [s if s % 2 == 0 else -1 for s in range(N)]
+    o, st, cs, clen, st_src, cs_src = _run_verify(dev, x, w, cst, g, b, init, L, out_dtype=torch.bfloat16,
+                                                  conv_src=conv_src)
+    ref, hist = _verify_reference(oracle64, x, w, cst, g, b, init, L, conv_src)
+    U.assert_close("o", U.to_np(o), ref["o"])
+    ok = np.array([0 <= v <= Ts for v in L])
+    assert clen.cpu().tolist() == [v if 0 <= v <= Ts else -1 for v in L]
+    U.assert_close("committed", U.to_np(st)[ok], ref["committed"][ok])
+    assert torch.isnan(st[3]).all() and torch.isnan(cs[3]).all()   # rejected: not written
+    got = cs.to("cpu", torch.float32).numpy()[ok]
+    assert np.array_equal(got, ref["conv_state"][ok].astype(np.float32))
+    # sources are never written
+    assert torch.equal(st_src.cpu(), init)
+    assert torch.equal(cs_src.cpu(), cst)
+
+
+def test_verify_conv_modes(dev, oracle64):
+    """Outputs-only writes no state; commit-only equals the fused call's
+    commit."""
+    U.say("verify_conv modes")
+    N, Ts, H, d, W = 16, 5, 4, 64, 3
+    x, w, cst, g, b, init = _verify_case(N, Ts, H, d, W, torch.bfloat16, seed=43)
+    L = [(i % (Ts + 1)) for i in range(N)]
+    ref, _ = _verify_reference(oracle64, x, w, cst, g, b, init, L, list(range(N)))
+    o, st, cs, _, _, _ = _run_verify(dev, x, w, cst, g, b, init, L, out_dtype=torch.float32, commit=False)
+    U.assert_close("o (outputs only)", U.to_np(o), ref["o"])
+    assert torch.isnan(st).all() and torch.isnan(cs).all()
+    _, st2, cs2, clen, _, _ = _run_verify(dev, x, w, cst, g, b, init, L, out_dtype=torch.float32, with_o=False)
+    U.assert_close("committed (commit only)", U.to_np(st2), ref["committed"])
+    assert np.array_equal(cs2.to("cpu", torch.float32).numpy(), ref["conv_state"].astype(np.float32))
+    assert clen.cpu().tolist() == L
+
+
+@pytest.mark.parametrize("d,W", [(16, 2), (32, 4)])
+def test_verify_conv_fp32_small(dev, oracle64, d, W):
+    """fp32 inputs and outputs, small heads, T_spec = 3."""
+    U.say(f"verify_conv fp32 d={d} W={W}")
+    N, Ts, H = 6, 3, 2
+    x, w, cst, g, b, init = _verify_case(N, Ts, H, d, W, torch.float32, seed=50 + d)
+    L = [3, 1, 2, 0, 3, 2]
+    o, st, cs, clen, _, _ = _run_verify(dev, x, w, cst, g, b, init, L, out_dtype=torch.float32)
+    ref, _ = _verify_reference(oracle64, x, w, cst, g, b, init, L, list(range(N)))
+    U.assert_close("o", U.to_np(o), ref["o"], rel=1e-5, mx=1e-5)
+    U.assert_close("committed", U.to_np(st), ref["committed"], rel=1e-5, mx=1e-5)
+    assert np.array_equal(cs.cpu().numpy(), ref["conv_state"].astype(np.float32))
