@@ -353,10 +353,38 @@ def bench_verify_secondary(torch, K, make_workload, dev):
     us = a_.elapsed_time(b2) / n * 1e3
     state_bytes = N * H * D * D * 4 * 2
     io = N * Ts * H * (4 * D * 2 + 2 + D * 2)
-    return {"workload": "verify 128 x 8 tokens, fused commit at L~U{1..8}", "us": round(us, 2),
-            "state_GB_s": round(state_bytes / us / 1e3, 1),
-            "alg_GB_s": round((state_bytes + io) / us / 1e3, 1),
-            "hbm_frac": round((state_bytes + io) / us / 1e3 / HBM_PEAK_GBS, 4)}
+    res = {"workload": "verify 128 x 8 tokens, fused commit at L~U{1..8}", "us": round(us, 2),
+           "state_GB_s": round(state_bytes / us / 1e3, 1),
+           "alg_GB_s": round((state_bytes + io) / us / 1e3, 1),
+           "hbm_frac": round((state_bytes + io) / us / 1e3 / HBM_PEAK_GBS, 4)}
+    # the same verify from the tokens' raw q/k/v projections with the conv
+    # (+ SiLU), q/k normalisation and both commits fused (kda_verify_conv)
+    from hybrid_recurrent_serving_amd.inputs import draw_conv
+    C, W = 3 * H * D, 4
+    gen = torch.Generator().manual_seed(4)
+    cw, cst, x = draw_conv(gen, N * Ts, C, W, N, torch.bfloat16, torch.device("cpu"))
+    x = x.reshape(N, Ts, C).to(dev)
+    cw = cw.to(dev)
+    cpool = cst.to(dev)
+    cs = torch.arange(N, dtype=torch.int32, device=dev)
+    for i in range(10):
+        s = slot_sets[i % P]
+        K.kda_verify_conv(x, cw, cpool, cs, cs, g, b, pool, s, s, o=o, accepted_len=L, act=1)
+    torch.cuda.synchronize()
+    a_.record()
+    for i in range(n):
+        s = slot_sets[i % P]
+        K.kda_verify_conv(x, cw, cpool, cs, cs, g, b, pool, s, s, o=o, accepted_len=L, act=1)
+    b2.record()
+    torch.cuda.synchronize()
+    us2 = a_.elapsed_time(b2) / n * 1e3
+    io2 = N * Ts * (C * 2 + H * (D * 2 + 2 + D * 2)) + N * C * (W - 1) * 2 * 2 + C * W * 2
+    res["fused_conv"] = {"call": "kda_verify_conv (conv + SiLU + q/k norm + verify, state and conv history "
+                                 "committed at L)", "us": round(us2, 2),
+                         "state_GB_s": round(state_bytes / us2 / 1e3, 1),
+                         "alg_GB_s": round((state_bytes + io2) / us2 / 1e3, 1),
+                         "hbm_frac": round((state_bytes + io2) / us2 / 1e3 / HBM_PEAK_GBS, 4)}
+    return res
 
 
 PREFILL_BYTES_PER_TOKEN = 16 * (4 * 128 * 2 + 2 + 128 * 2)      # q,k,v,g + beta + o (bf16), H=16

@@ -285,6 +285,12 @@ template <> struct Vec16x<float> {
   __device__ static __forceinline__ void st(float* p, const float (&x)[4]) { io<float>::st4(p, x); }
 };
 
+// SiLU x / (1 + exp(-x)) from the hardware exp2 and reciprocal (each within
+// about one ulp)
+__device__ __forceinline__ float silu_fast(float x) {
+  return x * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-x * 1.4426950408889634f));
+}
+
 template <int D, typename Tin, typename Tout, int W>
 __global__ void __launch_bounds__(64 * StepLayout<D>::WPH)
 decode_conv_kernel(const DecodeConvParams p) {
@@ -369,7 +375,7 @@ decode_conv_kernel(const DecodeConvParams p) {
 #pragma unroll
       for (int j = 0; j < HW; ++j) acc = fmaf(wt[i][j], hist[i][j], acc);
       acc = fmaf(wt[i][HW], xt[i], acc);
-      if (p.act == 1) acc = acc / (1.f + expf(-acc));
+      if (p.act == 1) acc = silu_fast(acc);
       s_y[blk * D + cc + i] = acc;
     }
     // advanced history: hist[1 .. W-2] ++ token
@@ -535,111 +541,23 @@ verify_conv_kernel(const DecodeConvParams p) {
   const bool do_store = valid && has_dst;
   const int n_tok = p.o ? T : (valid ? Lc : 0);
 
-  // conv items: taps, history and the T raw token vectors first
-  const bool conv_item = static_cast<int>(threadIdx.x) < NCI;
-  const int t = conv_item ? static_cast<int>(threadIdx.x) : 0;
-  const int blk = t / (D / V);
-  const int cc = (t % (D / V)) * V;
+  // The conv works on (channel vector, token) items: item it = c + NCI * j
+  // owns channels ch(c) .. ch(c) + V - 1 of token j, spread over all
+  // threads.  Its taps and xbar vectors (history or earlier tokens) are
+  // mostly cache hits; the state slice is requested first.
   const int64_t C = 3LL * p.H * D;
-  const int64_t ch = static_cast<int64_t>(blk) * p.H * D + static_cast<int64_t>(h) * D + cc;
   const int csrc = p.csrc[s];
   const int cdst = p.cdst[s];
-  const bool has_hist = conv_item && csrc >= 0 && csrc < p.n_cslots;
-  const Tin* xs = static_cast<const Tin*>(p.x) + static_cast<int64_t>(s) * T * p.x_stride + ch;
-  float tapf[W][V], histf[HW][V];
-  uint4 raw[STEP_TMAX];
-  if (conv_item) {
-    const Tin* wp = static_cast<const Tin*>(p.w) + ch * W;
-#pragma unroll
-    for (int b = 0; b < W; ++b) Vec16x<Tin>::ld(wp + b * V, tapf[b]);
-#pragma unroll
-    for (int j = 0; j < STEP_TMAX; ++j)
-      if (j < T) raw[j] = *reinterpret_cast<const uint4*>(xs + static_cast<int64_t>(j) * p.x_stride);
-  }
-  if (has_hist) {
-    const Tin* hp = static_cast<const Tin*>(p.cpool) + (static_cast<int64_t>(csrc) * C + ch) * HW;
-#pragma unroll
-    for (int b = 0; b < HW; ++b) Vec16x<Tin>::ld(hp + b * V, histf[b]);
-  }
+  const bool hist_ok = csrc >= 0 && csrc < p.n_cslots;
+  const Tin* xs = static_cast<const Tin*>(p.x) + static_cast<int64_t>(s) * T * p.x_stride;
+  const Tin* hs = static_cast<const Tin*>(p.cpool) + static_cast<int64_t>(hist_ok ? csrc : 0) * C * HW;
+  const int n_items = NCI * n_tok;
+  auto item_ch = [&](int c) -> int64_t {
+    const int blk = c / (D / V), cc = (c % (D / V)) * V;
+    return static_cast<int64_t>(blk) * p.H * D + static_cast<int64_t>(h) * D + cc;
+  };
 
-  // the convolution over the tokens: y_j = bias + sum_i w[i] xbar[j + i]
-  if (conv_item) {
-    float wt[V][W], win[V][W];
-#pragma unroll
-    for (int b = 0; b < W; ++b)
-#pragma unroll
-      for (int e = 0; e < V; ++e) wt[(b * V + e) / W][(b * V + e) % W] = tapf[b][e];
-#pragma unroll
-    for (int b = 0; b < HW; ++b)
-#pragma unroll
-      for (int e = 0; e < V; ++e) win[(b * V + e) / HW][(b * V + e) % HW] = has_hist ? histf[b][e] : 0.f;
-    float bias[V];
-#pragma unroll
-    for (int i = 0; i < V; ++i) bias[i] = p.bias ? io<Tin>::ld(static_cast<const Tin*>(p.bias) + ch + i) : 0.f;
-    float* yb = blk == 0 ? s_q : (blk == 1 ? s_k : s_v);
-#pragma unroll
-    for (int j = 0; j < STEP_TMAX; ++j) {
-      if (j < n_tok) {
-        float xt[V];
-        if constexpr (sizeof(Tin) == 2) {
-          const uint32_t wv[4] = {raw[j].x, raw[j].y, raw[j].z, raw[j].w};
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            xt[2 * q] = __uint_as_float(wv[q] << 16);
-            xt[2 * q + 1] = __uint_as_float(wv[q] & 0xffff0000u);
-          }
-        } else {
-          xt[0] = __uint_as_float(raw[j].x); xt[1] = __uint_as_float(raw[j].y);
-          xt[2] = __uint_as_float(raw[j].z); xt[3] = __uint_as_float(raw[j].w);
-        }
-#pragma unroll
-        for (int i = 0; i < V; ++i) {
-          win[i][HW] = xt[i];
-          float acc = bias[i];
-#pragma unroll
-          for (int k = 0; k < W; ++k) acc = fmaf(wt[i][k], win[i][k], acc);
-          if (p.act == 1) acc = acc / (1.f + expf(-acc));
-          yb[j * D + cc + i] = acc;
-#pragma unroll
-          for (int k = 0; k < HW; ++k) win[i][k] = win[i][k + 1];
-        }
-      }
-    }
-    // conv history after the accepted tokens: xbar[Lc .. Lc + W - 2] with
-    // xbar = history ++ tokens (token values re-read from x)
-    if (valid && cdst >= 0 && cdst < p.n_cslots) {
-      float nh[V * HW];
-#pragma unroll
-      for (int j = 0; j < HW; ++j) {
-        const int idx = Lc + j;
-        float val[V];
-        if (idx < HW) {
-#pragma unroll
-          for (int i = 0; i < V; ++i) {
-            float hv = 0.f;
-#pragma unroll
-            for (int k = 0; k < HW; ++k)
-              if (k == idx) hv = has_hist ? histf[(i * HW + k) / V][(i * HW + k) % V] : 0.f;
-            val[i] = hv;
-          }
-        } else {
-          Vec16x<Tin>::ld(xs + static_cast<int64_t>(idx - HW) * p.x_stride, val);
-        }
-#pragma unroll
-        for (int i = 0; i < V; ++i) nh[i * HW + j] = val[i];
-      }
-      Tin* np_ = static_cast<Tin*>(p.cpool) + (static_cast<int64_t>(cdst) * C + ch) * HW;
-#pragma unroll
-      for (int b = 0; b < HW; ++b) {
-        float f[V];
-#pragma unroll
-        for (int e = 0; e < V; ++e) f[e] = nh[b * V + e];
-        Vec16x<Tin>::st(np_ + b * V, f);
-      }
-    }
-  }
-  // state slice (the conv registers are dead by now), then exp(g) and beta
-  // of the tokens into LDS
+  // state slice, then exp(g) and beta of the tokens into LDS
   float S[L::RPL][4];
   if (has_src) {
     const float* sp = p.pool + ((static_cast<int64_t>(src) * p.H + h) * D + row0) * D + col;
@@ -649,7 +567,6 @@ verify_conv_kernel(const DecodeConvParams p) {
 #pragma unroll
     for (int i = 0; i < L::RPL; ++i) S[i][0] = S[i][1] = S[i][2] = S[i][3] = 0.f;
   }
-  // exp(g) and beta of the tokens into LDS
   {
     const Tin* gb = static_cast<const Tin*>(p.g);
     const Tin* bb = static_cast<const Tin*>(p.beta);
@@ -660,6 +577,69 @@ verify_conv_kernel(const DecodeConvParams p) {
       io<Tin>::ld4(gb + tok * p.g_stride + static_cast<int64_t>(h) * D + c, g4);
       *reinterpret_cast<float4*>(&s_a[j * D + c]) = make_float4(expf(g4[0]), expf(g4[1]), expf(g4[2]), expf(g4[3]));
       if (c == 0) s_b[j] = io<Tin>::ld(bb + tok * p.beta_stride + h);
+    }
+  }
+  // the convolution: y = bias + sum_k w[k] xbar[j + k] (+ SiLU)
+  for (int it = static_cast<int>(threadIdx.x); it < n_items; it += NTH) {
+    const int c = it % NCI, j = it / NCI;
+    const int blk = c / (D / V), cc = (c % (D / V)) * V;
+    const int64_t ch = item_ch(c);
+    float tapf[W][V], xbf[W][V];
+#pragma unroll
+    for (int b = 0; b < W; ++b) Vec16x<Tin>::ld(static_cast<const Tin*>(p.w) + ch * W + b * V, tapf[b]);
+    // xbar[j + k], k = 0 .. W-1: history entry j + k (< W-1) or token j + k - (W-1)
+#pragma unroll
+    for (int k = 0; k < W; ++k) {
+      const int idx = j + k;
+      if (idx >= HW) {
+        Vec16x<Tin>::ld(xs + static_cast<int64_t>(idx - HW) * p.x_stride + ch, xbf[k]);
+      } else if (hist_ok) {
+        // entry idx of channels ch .. ch + V - 1: elements (ch + i) * HW + idx
+#pragma unroll
+        for (int i = 0; i < V; ++i) xbf[k][i] = io<Tin>::ld(hs + (ch + i) * HW + idx);
+      } else {
+#pragma unroll
+        for (int i = 0; i < V; ++i) xbf[k][i] = 0.f;
+      }
+    }
+    float* yb = blk == 0 ? s_q : (blk == 1 ? s_k : s_v);
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      float acc = p.bias ? io<Tin>::ld(static_cast<const Tin*>(p.bias) + ch + i) : 0.f;
+#pragma unroll
+      for (int k = 0; k < W; ++k) acc = fmaf(tapf[(i * W + k) / V][(i * W + k) % V], xbf[k][i], acc);
+      if (p.act == 1) acc = silu_fast(acc);
+      yb[j * D + cc + i] = acc;
+    }
+  }
+  // conv history after the accepted tokens: xbar[Lc .. Lc + W - 2] with
+  // xbar = history ++ tokens, one item per channel vector
+  if (valid && cdst >= 0 && cdst < p.n_cslots && static_cast<int>(threadIdx.x) < NCI) {
+    const int64_t ch = item_ch(threadIdx.x);
+    float nh[V * HW];
+#pragma unroll
+    for (int j = 0; j < HW; ++j) {
+      const int idx = Lc + j;
+      float val[V];
+      if (idx >= HW) {
+        Vec16x<Tin>::ld(xs + static_cast<int64_t>(idx - HW) * p.x_stride + ch, val);
+      } else if (hist_ok) {
+#pragma unroll
+        for (int i = 0; i < V; ++i) val[i] = io<Tin>::ld(hs + (ch + i) * HW + idx);
+      } else {
+#pragma unroll
+        for (int i = 0; i < V; ++i) val[i] = 0.f;
+      }
+#pragma unroll
+      for (int i = 0; i < V; ++i) nh[i * HW + j] = val[i];
+    }
+    Tin* np_ = static_cast<Tin*>(p.cpool) + (static_cast<int64_t>(cdst) * C + ch) * HW;
+#pragma unroll
+    for (int b = 0; b < HW; ++b) {
+      float f[V];
+#pragma unroll
+      for (int e = 0; e < V; ++e) f[e] = nh[b * V + e];
+      Vec16x<Tin>::st(np_ + b * V, f);
     }
   }
   __syncthreads();
