@@ -134,6 +134,7 @@ size_t kda_args_sizeof(int which) {
     case 3: return sizeof(kda_verify_args);
     case 4: return sizeof(kda_decode_conv_args);
     case 5: return sizeof(kda_verify_conv_args);
+    case 6: return sizeof(kda_plan_args);
     default: return 0;
   }
 }
@@ -203,6 +204,33 @@ int kda_ckpt_plan(const int32_t* cu, const int32_t* start_pos, int32_t n_seq, in
   *n_total = (int32_t)total;
   if (total > cap) return fail(KDA_ERR_CAPACITY, "ckpt_plan: %lld checkpoints > cap %d", (long long)total, cap);
   return KDA_OK;
+}
+
+int kda_ckpt_plan_device(const kda_plan_args* a, kda_stream_t stream_) {
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  if (!a) return fail(KDA_ERR_NULL, "args is NULL");
+  if (a->struct_size != sizeof(kda_plan_args)) return fail(KDA_ERR_ARG, "struct_size mismatch");
+  if (a->n_seq < 0 || a->cap < 0 || a->n_free < 0 || a->T_tot < 0)
+    return fail(KDA_ERR_SHAPE, "ckpt_plan_device: negative size");
+  if (a->chunk != 16 && a->chunk != 32 && a->chunk != 64) return fail(KDA_ERR_UNSUPPORTED, "chunk %d", a->chunk);
+  if (a->interval <= 0 || a->interval % a->chunk != 0)
+    return fail(KDA_ERR_ALIGN, "interval %d not a positive multiple of chunk %d", a->interval, a->chunk);
+  if (!a->cu_seqlens || !a->ckpt_cu) return fail(KDA_ERR_NULL, "ckpt_plan_device: cu_seqlens or ckpt_cu is NULL");
+  if (a->n_free > 0 && !a->free_slots) return fail(KDA_ERR_NULL, "ckpt_plan_device: free_slots is NULL");
+  PlanParams p{};
+  p.cu = a->cu_seqlens;
+  p.start_pos = a->start_pos;
+  p.free_slots = a->free_slots;
+  p.ckpt_cu = a->ckpt_cu;
+  p.ckpt_pos = a->ckpt_pos;
+  p.ckpt_slot = a->ckpt_slot;
+  p.n_total = a->n_total;
+  p.T_tot = a->T_tot;
+  p.n_seq = a->n_seq;
+  p.interval = a->interval;
+  p.cap = a->cap;
+  p.n_free = a->n_free;
+  return launch_plan(p, stream);
 }
 
 // ------------------------------------------------------------------ decode / verify

@@ -51,6 +51,17 @@ struct DecodeConvParams {
 int launch_decode_conv(const DecodeConvParams& p, int D, int in_dtype, int out_dtype, hipStream_t stream);
 int launch_verify_conv(const DecodeConvParams& p, int D, int in_dtype, int out_dtype, hipStream_t stream);
 
+// ---------------------------------------------------------------- plan
+// device-side checkpoint plan (kda_ckpt_plan_device)
+struct PlanParams {
+  const int32_t *cu, *start_pos, *free_slots;
+  int32_t *ckpt_cu, *ckpt_pos, *ckpt_slot, *n_total;
+  int64_t T_tot;
+  int32_t n_seq, interval, cap, n_free;
+};
+
+int launch_plan(const PlanParams& p, hipStream_t stream);
+
 // ---------------------------------------------------------------- conv
 struct ConvParams {
   const void* x;

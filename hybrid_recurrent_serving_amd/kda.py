@@ -43,6 +43,17 @@ class ConvArgs(ctypes.Structure):
     ]
 
 
+class PlanArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", c_size),
+        ("cu_seqlens", c_vp), ("start_pos", c_vp), ("free_slots", c_vp), ("ckpt_cu", c_vp),
+        ("ckpt_pos", c_vp), ("ckpt_slot", c_vp), ("n_total", c_vp),
+        ("T_tot", c_i64),
+        ("n_seq", c_i32), ("interval", c_i32), ("chunk", c_i32), ("cap", c_i32), ("n_free", c_i32),
+        ("reserved", c_i32),
+    ]
+
+
 class PrefillArgs(ctypes.Structure):
     _fields_ = [
         ("struct_size", c_size),
@@ -116,7 +127,7 @@ class VerifyArgs(ctypes.Structure):
 
 
 EXPORTS = ["kda_status_str", "kda_abi_version", "kda_last_error", "kda_args_sizeof",
-           "kda_conv_short", "kda_ckpt_plan", "kda_prefill_workspace_bytes",
+           "kda_conv_short", "kda_ckpt_plan", "kda_ckpt_plan_device", "kda_prefill_workspace_bytes",
            "kda_prefill_varlen", "kda_decode", "kda_verify", "kda_decode_conv", "kda_verify_conv"]
 
 _lib = None
@@ -144,6 +155,7 @@ def load_library(path: Optional[Path] = None):
     lib.kda_args_sizeof.argtypes = [ctypes.c_int]
     lib.kda_conv_short.argtypes = [ctypes.POINTER(ConvArgs), c_vp]
     lib.kda_ckpt_plan.argtypes = [c_vp, c_vp, c_i32, c_i32, c_i32, c_vp, c_vp, c_i32, c_vp]
+    lib.kda_ckpt_plan_device.argtypes = [ctypes.POINTER(PlanArgs), c_vp]
     lib.kda_prefill_workspace_bytes.restype = c_i64
     lib.kda_prefill_workspace_bytes.argtypes = [ctypes.POINTER(PrefillArgs)]
     lib.kda_prefill_varlen.argtypes = [ctypes.POINTER(PrefillArgs), c_vp]
@@ -151,7 +163,7 @@ def load_library(path: Optional[Path] = None):
     lib.kda_verify.argtypes = [ctypes.POINTER(VerifyArgs), c_vp]
     lib.kda_decode_conv.argtypes = [ctypes.POINTER(DecodeConvArgs), c_vp]
     lib.kda_verify_conv.argtypes = [ctypes.POINTER(VerifyConvArgs), c_vp]
-    for name in ("kda_conv_short", "kda_ckpt_plan", "kda_prefill_varlen", "kda_decode", "kda_verify",
+    for name in ("kda_conv_short", "kda_ckpt_plan", "kda_ckpt_plan_device", "kda_prefill_varlen", "kda_decode", "kda_verify",
                  "kda_decode_conv", "kda_verify_conv"):
         getattr(lib, name).restype = ctypes.c_int
     if path is None:
@@ -214,7 +226,8 @@ def _device_tensors(**named):
             continue
         _expect(isinstance(t, torch.Tensor) and t.is_cuda, f"{name} must be a GPU tensor")
         if name in ("cu_seqlens", "src_slot", "dst_slot", "advance_len", "start_pos", "ckpt_cu",
-                    "ckpt_slot", "ckpt_pos_out", "accepted_len", "committed_len_out"):
+                    "ckpt_slot", "ckpt_pos_out", "accepted_len", "committed_len_out",
+                    "free_slots", "ckpt_pos", "n_total"):
             _expect(t.dtype == torch.int32 and t.is_contiguous(), f"{name} must be contiguous int32")
 
 
@@ -335,6 +348,41 @@ def kda_ckpt_plan(cu_seqlens, interval: int, chunk: int, start_pos=None):
     _check(lib.kda_ckpt_plan(vp(cu), vp(sp), n, int(interval), int(chunk), vp(ck_cu), vp(pos),
                              total.value, ctypes.byref(total)), lib)
     return ck_cu.tolist(), pos[:total.value].tolist()
+
+
+def kda_ckpt_plan_device(cu_seqlens, interval: int, chunk: int, T_tot: int, *, cap: int,
+                         start_pos=None, free_slots=None, ckpt_cu=None, ckpt_pos=None,
+                         ckpt_slot=None, n_total=None, stream=None):
+    """Device checkpoint plan; see include/kda.h for the contract.
+
+    cu_seqlens / start_pos / free_slots: device int32.  Outputs that are None
+    are allocated here (int32, on cu_seqlens' device); pass them all to keep
+    the call allocation-free, e.g. inside graph capture.  ``ckpt_pos`` and
+    ``ckpt_slot`` hold ``cap`` entries.  Returns (ckpt_cu, ckpt_pos,
+    ckpt_slot, n_total)."""
+    import torch
+    n_seq = cu_seqlens.numel() - 1
+    _expect(n_seq >= 0 and cap >= 0, "cu_seqlens needs n_seq + 1 entries; cap >= 0")
+    dev = cu_seqlens.device
+
+    def out(t, n):
+        return torch.empty(n, dtype=torch.int32, device=dev) if t is None else t
+
+    ckpt_cu, ckpt_pos = out(ckpt_cu, n_seq + 1), out(ckpt_pos, max(cap, 1))
+    ckpt_slot, n_total = out(ckpt_slot, max(cap, 1)), out(n_total, 1)
+    _device_tensors(cu_seqlens=cu_seqlens, start_pos=start_pos, free_slots=free_slots, ckpt_cu=ckpt_cu,
+                    ckpt_pos=ckpt_pos, ckpt_slot=ckpt_slot, n_total=n_total)
+    _expect(ckpt_cu.numel() >= n_seq + 1 and n_total.numel() >= 1, "ckpt_cu / n_total too small")
+    _expect(ckpt_pos.numel() >= cap and ckpt_slot.numel() >= cap, "ckpt_pos / ckpt_slot hold fewer than cap")
+    _expect(start_pos is None or start_pos.numel() >= n_seq, "start_pos holds fewer than n_seq")
+    a = PlanArgs()
+    a.struct_size = ctypes.sizeof(PlanArgs)
+    a.cu_seqlens, a.start_pos, a.free_slots = _ptr(cu_seqlens), _ptr(start_pos), _ptr(free_slots)
+    a.ckpt_cu, a.ckpt_pos, a.ckpt_slot, a.n_total = _ptr(ckpt_cu), _ptr(ckpt_pos), _ptr(ckpt_slot), _ptr(n_total)
+    a.T_tot, a.n_seq, a.interval, a.chunk, a.cap = int(T_tot), n_seq, int(interval), int(chunk), int(cap)
+    a.n_free = 0 if free_slots is None else free_slots.numel()
+    _check(load_library().kda_ckpt_plan_device(ctypes.byref(a), _stream(stream)))
+    return ckpt_cu, ckpt_pos, ckpt_slot, n_total
 
 
 def _prefill_args(q, k, v, g, beta, o, cu_seqlens, state_pool, src_slot, dst_slot, chunk,

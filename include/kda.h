@@ -83,7 +83,7 @@ int kda_abi_version(void);
 /* One-line reason for the calling thread's most recent non-OK status. */
 const char *kda_last_error(void);
 /* sizeof() of each args struct as compiled into the library: which = 0 conv,
- * 1 prefill, 2 decode, 3 verify, 4 decode_conv, 5 verify_conv.  Returns 0
+ * 1 prefill, 2 decode, 3 verify, 4 decode_conv, 5 verify_conv, 6 plan.  Returns 0
  * for other values. */
 size_t kda_args_sizeof(int which);
 
@@ -156,6 +156,55 @@ int kda_conv_short(const kda_conv_args *args, kda_stream_t stream);
 int kda_ckpt_plan(const int32_t *cu_seqlens, const int32_t *start_pos, int32_t n_seq,
                   int32_t interval, int32_t chunk, int32_t *ckpt_cu, int32_t *ckpt_pos,
                   int32_t cap, int32_t *n_total);
+
+/* ------------------------------------------------------------------------
+ * kda_ckpt_plan_device -- the checkpoint plan of kda_ckpt_plan, built on the
+ * device from device cu_seqlens, with checkpoint slots taken from a device
+ * free list.
+ *
+ * The Day-0 Integration page (section "Separate Prefill/Decode Code Paths")
+ * reports per-batch metadata preparation as a batch-1 bottleneck and moves
+ * it into dedicated kernels.  This call keeps the checkpoint table of
+ * interval retention (same page, section "Agentic Serving: Cache Retention
+ * Across Turns") off the host: two small kernels whose launch shapes depend
+ * only on n_seq and cap, no allocation and no synchronisation, so it can be
+ * recorded in a HIP graph together with kda_prefill_varlen.
+ *
+ * Per sequence s, with the clamping kda_prefill_varlen applies
+ * (bos = clamp(cu[s], 0, T_tot), eos = clamp(cu[s+1], bos, T_tot),
+ * len = eos - bos, start = max(start_pos[s], 0)):
+ *   count(s)     = len > 0 ? floor((start+len-1)/interval) - floor(start/interval) : 0
+ *   ckpt_cu      exclusive prefix sums of count, ckpt_cu[0] = 0
+ *   ckpt_pos[i]  = (floor(start/interval) + 1 + i - ckpt_cu[s]) * interval
+ *                  for ckpt_cu[s] <= i < ckpt_cu[s+1]
+ *   ckpt_slot[i] = free_slots[i] for i < n_free, else -1 (a slot of -1 makes
+ *                  kda_prefill_varlen skip that checkpoint)
+ *   n_total[0]   = ckpt_cu[n_seq]
+ * Entries i >= cap of ckpt_pos / ckpt_slot are not written; pass the same
+ * cap as kda_prefill_args.n_ckpt and the prefill skips checkpoints past it.
+ * Counts saturate at 2^31 - 1.  n_seq == 0 still writes ckpt_cu[0] = 0
+ * and n_total.  For valid inputs (lengths >= 0, starts
+ * >= 0) the table equals the one kda_ckpt_plan builds on the host.
+ * ---------------------------------------------------------------------- */
+typedef struct kda_plan_args {
+    size_t struct_size;          /* sizeof(kda_plan_args) */
+    const int32_t *cu_seqlens;   /* [n_seq + 1] */
+    const int32_t *start_pos;    /* [n_seq] absolute start, or NULL (all 0) */
+    const int32_t *free_slots;   /* [n_free] pool slots, or NULL when n_free == 0 */
+    int32_t *ckpt_cu;            /* [n_seq + 1] out */
+    int32_t *ckpt_pos;           /* [cap] out, or NULL */
+    int32_t *ckpt_slot;          /* [cap] out, or NULL */
+    int32_t *n_total;            /* [1] out, or NULL: total checkpoints (may exceed cap) */
+    int64_t T_tot;               /* tokens of the packed batch (>= 0) */
+    int32_t n_seq;               /* >= 0 */
+    int32_t interval;            /* > 0 and a multiple of chunk (else KDA_ERR_ALIGN) */
+    int32_t chunk;               /* 16, 32 or 64 */
+    int32_t cap;                 /* >= 0: capacity of ckpt_pos / ckpt_slot */
+    int32_t n_free;              /* >= 0: length of free_slots */
+    int32_t reserved;
+} kda_plan_args;
+
+int kda_ckpt_plan_device(const kda_plan_args *args, kda_stream_t stream);
 
 /* ------------------------------------------------------------------------
  * kda_prefill_varlen -- chunked prefill of packed sequences.

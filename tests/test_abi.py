@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported(lib):
 def test_abi_version_and_struct_sizes(lib):
     assert lib.kda_abi_version() == 1
     for which, cls in enumerate([K.ConvArgs, K.PrefillArgs, K.DecodeArgs, K.VerifyArgs, K.DecodeConvArgs,
-                                 K.VerifyConvArgs]):
+                                 K.VerifyConvArgs, K.PlanArgs]):
         assert lib.kda_args_sizeof(which) == ctypes.sizeof(cls), cls.__name__
     assert lib.kda_args_sizeof(7) == 0
 
@@ -255,3 +255,32 @@ def test_ckpt_plan_errors(lib):
     vp = lambda a: a.ctypes.data_as(ctypes.c_void_p)  # noqa: E731
     st = lib.kda_ckpt_plan(vp(cu), None, 1, 64, 64, vp(ck_cu), vp(pos), 2, ctypes.byref(total))
     assert st == 9 and total.value == 15 and ck_cu[1] == 15
+
+
+def _plan_args(**kw):
+    a = K.PlanArgs()
+    a.struct_size = ctypes.sizeof(K.PlanArgs)
+    fake = 1 << 20  # never dereferenced on these paths
+    a.cu_seqlens = a.ckpt_cu = a.ckpt_pos = a.ckpt_slot = a.n_total = fake
+    a.T_tot, a.n_seq, a.interval, a.chunk, a.cap, a.n_free = 1000, 3, 128, 64, 16, 0
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(struct_size=8), "KDA_ERR_ARG"),
+    (dict(n_seq=-1), "KDA_ERR_SHAPE"),
+    (dict(cap=-1), "KDA_ERR_SHAPE"),
+    (dict(n_free=-2), "KDA_ERR_SHAPE"),
+    (dict(T_tot=-1), "KDA_ERR_SHAPE"),
+    (dict(chunk=48), "KDA_ERR_UNSUPPORTED"),
+    (dict(interval=100), "KDA_ERR_ALIGN"),
+    (dict(interval=0), "KDA_ERR_ALIGN"),
+    (dict(cu_seqlens=None), "KDA_ERR_NULL"),
+    (dict(ckpt_cu=None), "KDA_ERR_NULL"),
+    (dict(n_free=4, free_slots=None), "KDA_ERR_NULL"),
+])
+def test_ckpt_plan_device_validation(lib, kw, status):
+    st = lib.kda_ckpt_plan_device(ctypes.byref(_plan_args(**kw)), None)
+    assert lib.kda_status_str(st).decode() == status, lib.kda_last_error()
