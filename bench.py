@@ -307,6 +307,7 @@ def bench_decode(args, torch, K, make_workload):
                                         "GB_s": round(state_bytes / cp_us / 1e3, 1)}
         del srcs, dsts, src_t, dst_t
         secondary["verify"] = bench_verify_secondary(torch, K, make_workload, dev)
+        secondary["ckpt_plan_device"] = bench_planner_secondary(torch, K, dev)
         pf = bench_prefill_varlen(torch, K, make_workload, dev, iters=10)
         secondary["prefill_varlen"] = {k_: pf[k_] for k_ in ("workload", "tokens", "ms", "tokens_per_s",
                                                              "alg_mfma_frac", "alg_hbm_frac")}
@@ -323,6 +324,61 @@ def bench_decode(args, torch, K, make_workload):
     return {"metric": METRIC, "value": round(value, 1), "unit": "GB/s", "ms_per_step": ms_step,
             "dtype": "f32", "config": cfg, "roofline": roof, "cpu_baseline": cpu,
             "secondary": secondary, "wall_s": round(wall, 3)}
+
+
+def bench_planner_secondary(torch, K, dev, iters=200):
+    """Latency of the device checkpoint plan (kda_ckpt_plan_device): device
+    time per call from a HIP graph that holds `iters` back-to-back calls
+    (replay time over the call count, so host enqueue cost is excluded), and
+    the host time to enqueue one call eagerly through the binding (argument
+    marshalling, validation, two launches).  Checkpoint interval 4096,
+    chunk 64."""
+    gen = torch.Generator().manual_seed(4242)
+    cases = {"batch1_32k": [32768],
+             "varlen16": (16, 512, 16384),
+             "batch1024": (1024, 1, 16384)}
+    out = {}
+    for name, spec in cases.items():
+        if isinstance(spec, list):
+            lens = torch.tensor(spec)
+        else:
+            n, lo, hi = spec
+            lens = torch.randint(lo, hi + 1, (n,), generator=gen)
+        cu = torch.zeros(lens.numel() + 1, dtype=torch.int32)
+        cu[1:] = torch.cumsum(lens, 0)
+        n_seq, T = lens.numel(), int(cu[-1])
+        cap = int(sum((int(L) - 1) // 4096 for L in lens.tolist())) + 1
+        cu_d = cu.to(dev)
+        free = torch.arange(cap, dtype=torch.int32, device=dev)
+        outs = dict(ckpt_cu=torch.empty(n_seq + 1, dtype=torch.int32, device=dev),
+                    ckpt_pos=torch.empty(cap, dtype=torch.int32, device=dev),
+                    ckpt_slot=torch.empty(cap, dtype=torch.int32, device=dev),
+                    n_total=torch.empty(1, dtype=torch.int32, device=dev))
+        call = lambda: K.kda_ckpt_plan_device(cu_d, 4096, 64, T, cap=cap, free_slots=free, **outs)  # noqa: E731
+        for _ in range(10):
+            call()
+        torch.cuda.synchronize()
+        w0 = time.perf_counter()
+        for _ in range(iters):
+            call()
+        host_us = (time.perf_counter() - w0) / iters * 1e6
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(iters):
+                call()
+        graph.replay()
+        torch.cuda.synchronize()
+        a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a_.record()
+        graph.replay()
+        b_.record()
+        torch.cuda.synchronize()
+        out[name] = {"n_seq": n_seq, "checkpoints": int(outs["n_total"].item()),
+                     "graph_us_per_call": round(a_.elapsed_time(b_) / iters * 1e3, 2),
+                     "host_enqueue_us_per_call": round(host_us, 2)}
+        del graph
+    return out
 
 
 def bench_verify_secondary(torch, K, make_workload, dev):
