@@ -140,9 +140,9 @@ def ingest_pmc(fetch_csv, write_csv):
     f_scale = COPY_BYTES / (sum(cf) / len(cf))
     w_scale = COPY_BYTES / (sum(cw) / len(cw))
     for key, pred, src, units, pick in (
-            ("decode_step_kernel_d128_bf16", lambda r: "step_kernel<128" in r["Kernel_Name"], "kda_step.hip",
+            ("decode_step_kernel_d128_bf16", lambda r: is_decode128(r["Kernel_Name"], 0), "kda_step.hip",
              128 * 16, "all"),
-            ("decode_conv_kernel_d128_bf16", lambda r: "decode_conv_kernel<128" in r["Kernel_Name"],
+            ("decode_conv_kernel_d128_bf16", lambda r: is_decode128(r["Kernel_Name"], 4),
              "kda_step.hip", 128 * 16, "all"),
             ("prefill_kernel_d128_bf16", lambda r: "prefill_kernel<128" in r["Kernel_Name"], "kda_prefill.hip",
              varlen_tokens(), "max")):
@@ -162,6 +162,13 @@ def ingest_pmc(fetch_csv, write_csv):
                           "note": "FETCH_SIZE / WRITE_SIZE of a plain device copy of copy_bytes, "
                                   "scaled to read and write exactly copy_bytes"}
     return out
+
+
+def is_decode128(kernel_name: str, W: int) -> bool:
+    """The d = 128 decode kernel: plain (W = 0, two workgroups of 64 columns
+    per head) or with the W-tap conv fused in (one workgroup per head)."""
+    cols = 64 if W == 0 else 128
+    return "decode128_kernel<" in kernel_name and kernel_name.replace(" ", "").endswith(f",{W},{cols}>(kda::Dec128Args)")
 
 
 def cpu_info():
@@ -258,7 +265,7 @@ def bench_decode(args, torch, K, make_workload):
     value = state_bytes / (ms_step * 1e-3) / 1e9
     achieved = alg_bytes / (k_ms * 1e-3) / 1e9
     traffic = traffic_for("decode_conv_kernel_d128_bf16", "kda_step.hip", N * H)
-    roof = {"kernel": "decode_conv_kernel<128,bf16,bf16,4> (kda_decode_conv)", "bound": "hbm",
+    roof = {"kernel": "decode128_kernel<bf16,bf16,W=4,128 columns> (kda_decode_conv)", "bound": "hbm",
             "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
             "alg_bytes_per_launch": alg_bytes, "avg_launch_us": round(k_ms * 1e3, 3)}

@@ -63,6 +63,18 @@ __device__ __forceinline__ void ld_vec(const T* p, float (&x)[N]) {
   }
 }
 
+// Recurrent state rows stream through once per call: non-temporal 16-byte
+// accesses
+typedef __attribute__((ext_vector_type(4))) float nt4;
+__device__ __forceinline__ void ld4_stream(const float* p, float (&x)[4]) {
+  const nt4 v = __builtin_nontemporal_load(reinterpret_cast<const nt4*>(p));
+  x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+}
+__device__ __forceinline__ void st4_stream(float* p, const float (&x)[4]) {
+  const nt4 v = {x[0], x[1], x[2], x[3]};
+  __builtin_nontemporal_store(v, reinterpret_cast<nt4*>(p));
+}
+
 // Sum over the lanes that differ only in bits >= log2(FIRST) of the lane id.
 template <int FIRST>
 __device__ __forceinline__ float wave_sum_from(float x) {

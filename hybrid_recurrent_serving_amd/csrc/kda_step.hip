@@ -29,17 +29,6 @@
 
 namespace kda {
 
-// State rows stream through once per call: non-temporal 16-byte accesses
-typedef __attribute__((ext_vector_type(4))) float nt4;
-__device__ __forceinline__ void ld4_stream(const float* p, float (&x)[4]) {
-  const nt4 v = __builtin_nontemporal_load(reinterpret_cast<const nt4*>(p));
-  x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
-}
-__device__ __forceinline__ void st4_stream(float* p, const float (&x)[4]) {
-  const nt4 v = {x[0], x[1], x[2], x[3]};
-  __builtin_nontemporal_store(v, reinterpret_cast<nt4*>(p));
-}
-
 template <int D>
 struct StepLayout {
   static constexpr int COLS = D < 32 ? D : 32;  // columns per wave
@@ -49,6 +38,10 @@ struct StepLayout {
   static constexpr int WPH = D / COLS;          // waves per head
   static_assert(RPL >= 1 && RPL * RG == D, "layout");
 };
+
+// the decode step at d = 128 (defined below, after the fused conv decode)
+template <typename Tin, typename Tout> static int launch_decode128_plain(const StepParams& p, hipStream_t stream);
+template <typename Tin, typename Tout> static int launch_decode128_conv(const DecodeConvParams& p, hipStream_t stream);
 
 constexpr int STEP_TMAX = 16;   // most tokens per sequence in one call
 
@@ -232,6 +225,7 @@ static int launch_step_t(const StepParams& p, hipStream_t stream) {
   dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(p.n_seq) * p.H));
   dim3 block(64 * L::WPH);
   if (p.T_spec == 1) {
+    if constexpr (D == 128) return launch_decode128_plain<Tin, Tout>(p, stream);
     hipLaunchKernelGGL((step_kernel<D, Tin, Tout, false>), grid, block, 0, stream, p);
   } else {
     const size_t lds = (5 * static_cast<size_t>(p.T_spec) * D + p.T_spec) * sizeof(float);
@@ -459,6 +453,7 @@ decode_conv_kernel(const DecodeConvParams p) {
 
 template <int D, typename Tin, typename Tout>
 static int launch_decode_conv_t(const DecodeConvParams& p, hipStream_t stream) {
+  if constexpr (D == 128) return launch_decode128_conv<Tin, Tout>(p, stream);
   using L = StepLayout<D>;
   dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(p.n_seq) * p.H));
   dim3 block(64 * L::WPH);
@@ -488,6 +483,298 @@ int launch_decode_conv(const DecodeConvParams& p, int D, int in_dtype, int out_d
     case 64: return launch_decode_conv_d<64>(p, in_dtype, out_dtype, stream);
     case 128: return launch_decode_conv_d<128>(p, in_dtype, out_dtype, stream);
     default: return fail(KDA_ERR_UNSUPPORTED, "d = %d not built (16, 32, 64, 128)", D);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// The decode step at d = 128, plain (W = 0) or with the short convolution
+// fused in (W >= 2), laid out for streaming: a lane holds 4 rows x 4 columns
+// of the state (four 16-byte vectors).  A plain copy of the same bytes runs
+// markedly faster with a few 16-byte accesses per lane than with sixteen,
+// so the rows of a head are split across waves instead of the columns:
+// wave w of a workgroup owns rows [16 w, 16 w + 16) of the workgroup's CPW
+// columns, 16 lanes cover 64 columns (256 contiguous bytes of a row), and
+// the reductions over rows (S^T k, S^T q) finish across waves through LDS,
+// in a fixed wave order.  CPW = 64 splits a head over two workgroups, whose
+// blocks are numbered so that both land on the same XCD (block b runs on
+// XCD b mod 8); the fused conv keeps the whole head in one workgroup
+// (CPW = 128), so that each history vector is read and rewritten by one
+// thread even when the conv state is updated in place.
+struct Dec128Args {
+  const void *q, *k, *v;                // plain inputs [n_seq, H, 128] (W = 0)
+  const void *x, *w, *bias;             // conv inputs (W >= 2)
+  void* cpool;
+  const int32_t *csrc, *cdst;
+  int64_t x_stride, n_cslots;
+  int32_t act, qk_l2norm;
+  float eps;
+  const void *g, *beta;
+  void* o;
+  float* pool;
+  const int32_t *src_slot, *dst_slot;
+  int64_t q_stride, k_stride, v_stride, g_stride, beta_stride, o_stride, n_slots;
+  int32_t n_seq, H;
+  float scale;
+};
+
+namespace d128 {
+constexpr int D = 128;
+constexpr int RPL = 4;                  // rows per lane
+template <int CPW> struct Shape {
+  static constexpr int PARTS = D / CPW; // workgroups per (sequence, head)
+  static constexpr int LPR = CPW / 4;   // lanes per row
+  static constexpr int RG = 64 / LPR;   // row groups per wave
+  static constexpr int RPW = RG * RPL;  // rows per wave
+  static constexpr int NW = D / RPW;    // waves per workgroup
+};
+}  // namespace d128
+
+template <typename Tin, typename Tout, int W, int CPW>
+__global__ void __launch_bounds__(64 * d128::Shape<CPW>::NW) decode128_kernel(const Dec128Args p) {
+  using namespace d128;
+  using SH = Shape<CPW>;
+  constexpr bool CONV = W >= 2;
+  static_assert(!CONV || SH::PARTS == 1, "the fused conv keeps a head in one workgroup");
+  constexpr int NW = SH::NW, LPR = SH::LPR, RPW = SH::RPW, PARTS = SH::PARTS;
+  constexpr int V = Vec16x<Tin>::N;     // channels per conv item
+  constexpr int NCI = 3 * D / V;        // conv items of one head
+  constexpr int HW = CONV ? W - 1 : 1;  // history length
+  static_assert(!CONV || NCI <= 64 * NW, "one conv item per thread");
+  __shared__ __align__(16) float s_y[CONV ? 3 * D : 4];   // q | k | v of the head (fp32)
+  __shared__ __align__(16) float s_w[NW][CPW], s_o[NW][CPW];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  int64_t item;
+  int part;
+  {
+    const int64_t b = blockIdx.x;
+    const int64_t n_items = static_cast<int64_t>(p.n_seq) * p.H;
+    const int64_t full = (n_items / 8) * 8 * PARTS;
+    if (PARTS > 1 && b < full) {
+      item = (b / (8 * PARTS)) * 8 + b % 8;
+      part = static_cast<int>((b / 8) % PARTS);
+    } else {
+      item = b / PARTS;
+      part = static_cast<int>(b % PARTS);
+    }
+  }
+  const int s = static_cast<int>(item / p.H);
+  const int h = static_cast<int>(item % p.H);
+  const int cg = lane % LPR;
+  const int rg = lane / LPR;
+  const int lc = 4 * cg;                // column inside the workgroup's block
+  const int col = CPW * part + lc;
+  const int row0 = RPW * wave + RPL * rg;
+  const int src = p.src_slot[s];
+  const int dst = p.dst_slot[s];
+  const bool has_src = src >= 0 && src < p.n_slots;
+  const bool has_dst = dst >= 0 && dst < p.n_slots;
+
+  // The convolution (conv waves only, before their own state loads: their
+  // conv data and their state slice are never live together, which keeps
+  // the register count of the 16-wave workgroup low).  Item t < NCI owns V
+  // channels of the head's q, k or v block.
+  if constexpr (CONV) {
+    if (wave < (NCI + 63) / 64) {
+      const int t = static_cast<int>(threadIdx.x);
+      const int64_t C = 3LL * p.H * D;
+      const int csrc = p.csrc[s];
+      const int cdst = p.cdst[s];
+      if (t < NCI) {
+        const int blk = t / (D / V);    // 0 q, 1 k, 2 v
+        const int cc = (t % (D / V)) * V;
+        const int64_t ch = static_cast<int64_t>(blk) * p.H * D + static_cast<int64_t>(h) * D + cc;
+        const bool has_hist = csrc >= 0 && csrc < p.n_cslots;
+        // taps: the V * W values of channels ch .. ch + V - 1 are contiguous
+        // (W 16-byte vectors), tapf[b][e] = weight[(b V + e) / W, (b V + e) % W];
+        // history likewise (W - 1 vectors); the token (one vector)
+        float tapf[W][V], histf[HW][V], xt[V];
+        const Tin* wp = static_cast<const Tin*>(p.w) + ch * W;
+#pragma unroll
+        for (int b = 0; b < W; ++b) Vec16x<Tin>::ld(wp + b * V, tapf[b]);
+        Vec16x<Tin>::ld(static_cast<const Tin*>(p.x) + static_cast<int64_t>(s) * p.x_stride + ch, xt);
+        if (has_hist) {
+          const Tin* hp = static_cast<const Tin*>(p.cpool) + (static_cast<int64_t>(csrc) * C + ch) * HW;
+#pragma unroll
+          for (int b = 0; b < HW; ++b) Vec16x<Tin>::ld(hp + b * V, histf[b]);
+        }
+        float wt[V][W], hist[V][HW];
+#pragma unroll
+        for (int b = 0; b < W; ++b)
+#pragma unroll
+          for (int e = 0; e < V; ++e) wt[(b * V + e) / W][(b * V + e) % W] = tapf[b][e];
+#pragma unroll
+        for (int b = 0; b < HW; ++b)
+#pragma unroll
+          for (int e = 0; e < V; ++e) hist[(b * V + e) / HW][(b * V + e) % HW] = has_hist ? histf[b][e] : 0.f;
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+          // tap W-1 multiplies the token, tap j < W-1 the history value j
+          float acc = p.bias ? io<Tin>::ld(static_cast<const Tin*>(p.bias) + ch + i) : 0.f;
+#pragma unroll
+          for (int j = 0; j < HW; ++j) acc = fmaf(wt[i][j], hist[i][j], acc);
+          acc = fmaf(wt[i][HW], xt[i], acc);
+          if (p.act == 1) acc = silu_fast(acc);
+          s_y[blk * D + cc + i] = acc;
+        }
+        // advanced history: hist[1 .. W-2] ++ token (read and rewritten by this thread only)
+        if (cdst >= 0 && cdst < p.n_cslots) {
+          float nh[V * HW];
+#pragma unroll
+          for (int i = 0; i < V; ++i)
+#pragma unroll
+            for (int j = 0; j < HW; ++j) nh[i * HW + j] = j + 1 < HW ? hist[i][j + 1] : xt[i];
+          Tin* np_ = static_cast<Tin*>(p.cpool) + (static_cast<int64_t>(cdst) * C + ch) * HW;
+#pragma unroll
+          for (int b = 0; b < HW; ++b) {
+            float f[V];
+#pragma unroll
+            for (int e = 0; e < V; ++e) f[e] = nh[b * V + e];
+            Vec16x<Tin>::st(np_ + b * V, f);
+          }
+        }
+      }
+    }
+  }
+
+  float S[RPL][4];
+  if (has_src) {
+    const float* sp = p.pool + ((static_cast<int64_t>(src) * p.H + h) * D + row0) * D + col;
+#pragma unroll
+    for (int i = 0; i < RPL; ++i) ld4_stream(sp + static_cast<int64_t>(i) * D, S[i]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < RPL; ++i) S[i][0] = S[i][1] = S[i][2] = S[i][3] = 0.f;
+  }
+  float ar[RPL], kr[RPL], qr[RPL], vc[4];
+  ld_vec<Tin, RPL>(static_cast<const Tin*>(p.g) + static_cast<int64_t>(s) * p.g_stride + static_cast<int64_t>(h) * D + row0,
+                   ar);
+  const float beta = io<Tin>::ld(static_cast<const Tin*>(p.beta) + static_cast<int64_t>(s) * p.beta_stride + h);
+  if constexpr (!CONV) {
+    ld_vec<Tin, RPL>(static_cast<const Tin*>(p.k) + static_cast<int64_t>(s) * p.k_stride + static_cast<int64_t>(h) * D + row0,
+                     kr);
+    ld_vec<Tin, RPL>(static_cast<const Tin*>(p.q) + static_cast<int64_t>(s) * p.q_stride + static_cast<int64_t>(h) * D + row0,
+                     qr);
+    io<Tin>::ld4(static_cast<const Tin*>(p.v) + static_cast<int64_t>(s) * p.v_stride + static_cast<int64_t>(h) * D + col, vc);
+  } else {
+    __syncthreads();
+    float inv_q = 1.f, inv_k = 1.f;
+    if (p.qk_l2norm) {
+      float sq = 0.f, sk = 0.f;
+#pragma unroll
+      for (int c = lane; c < D; c += 64) {
+        sq = fmaf(s_y[c], s_y[c], sq);
+        sk = fmaf(s_y[D + c], s_y[D + c], sk);
+      }
+      sq = wave_sum_from<1>(sq);
+      sk = wave_sum_from<1>(sk);
+      inv_q = 1.f / sqrtf(sq + p.eps);
+      inv_k = 1.f / sqrtf(sk + p.eps);
+    }
+#pragma unroll
+    for (int i = 0; i < RPL; ++i) {
+      qr[i] = s_y[row0 + i] * inv_q;
+      kr[i] = s_y[D + row0 + i] * inv_k;
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) vc[c] = s_y[2 * D + col + c];
+  }
+#pragma unroll
+  for (int i = 0; i < RPL; ++i) ar[i] = expf(ar[i]);
+
+  // Diag(alpha) S and the partial S^T k of the lane's rows, summed over the
+  // wave's rows, then over the waves (in order)
+  float w[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < RPL; ++i)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      S[i][c] *= ar[i];
+      w[c] = fmaf(S[i][c], kr[i], w[c]);
+    }
+#pragma unroll
+  for (int c = 0; c < 4; ++c) w[c] = wave_sum_from<LPR>(w[c]);
+  if (rg == 0) *reinterpret_cast<float4*>(&s_w[wave][lc]) = make_float4(w[0], w[1], w[2], w[3]);
+  __syncthreads();
+  float u[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ww = 0; ww < NW; ++ww) {
+    const float4 a = *reinterpret_cast<const float4*>(&s_w[ww][lc]);
+    u[0] += a.x;
+    u[1] += a.y;
+    u[2] += a.z;
+    u[3] += a.w;
+  }
+#pragma unroll
+  for (int c = 0; c < 4; ++c) u[c] = beta * (vc[c] - u[c]);
+  // rank-1 correction, state out, partial read-out S^T q
+  float o[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < RPL; ++i)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      S[i][c] = fmaf(kr[i], u[c], S[i][c]);
+      o[c] = fmaf(S[i][c], qr[i], o[c]);
+    }
+  if (has_dst) {
+    float* dp = p.pool + ((static_cast<int64_t>(dst) * p.H + h) * D + row0) * D + col;
+#pragma unroll
+    for (int i = 0; i < RPL; ++i) st4_stream(dp + static_cast<int64_t>(i) * D, S[i]);
+  }
+#pragma unroll
+  for (int c = 0; c < 4; ++c) o[c] = wave_sum_from<LPR>(o[c]);
+  if (rg == 0) *reinterpret_cast<float4*>(&s_o[wave][lc]) = make_float4(o[0], o[1], o[2], o[3]);
+  __syncthreads();
+  if (wave == 0 && rg == 0) {
+    float ov[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) {
+      const float4 a = *reinterpret_cast<const float4*>(&s_o[ww][lc]);
+      ov[0] += a.x;
+      ov[1] += a.y;
+      ov[2] += a.z;
+      ov[3] += a.w;
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) ov[c] *= p.scale;
+    io<Tout>::st4(static_cast<Tout*>(p.o) + static_cast<int64_t>(s) * p.o_stride + static_cast<int64_t>(h) * D + col, ov);
+  }
+}
+
+template <typename Tin, typename Tout, int W, int CPW>
+static int launch_decode128(const Dec128Args& a, hipStream_t stream) {
+  using SH = d128::Shape<CPW>;
+  const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(a.n_seq) * a.H * SH::PARTS));
+  hipLaunchKernelGGL((decode128_kernel<Tin, Tout, W, CPW>), grid, dim3(64 * SH::NW), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, "decode kernel launch: %s", hipGetErrorString(e));
+  return KDA_OK;
+}
+
+template <typename Tin, typename Tout>
+static int launch_decode128_plain(const StepParams& p, hipStream_t stream) {
+  Dec128Args a{};
+  a.q = p.q; a.k = p.k; a.v = p.v; a.g = p.g; a.beta = p.beta; a.o = p.o; a.pool = p.pool;
+  a.src_slot = p.src_slot; a.dst_slot = p.dst_slot;
+  a.q_stride = p.q_stride; a.k_stride = p.k_stride; a.v_stride = p.v_stride; a.g_stride = p.g_stride;
+  a.beta_stride = p.beta_stride; a.o_stride = p.o_stride; a.n_slots = p.n_slots;
+  a.n_seq = p.n_seq; a.H = p.H; a.scale = p.scale;
+  return launch_decode128<Tin, Tout, 0, 64>(a, stream);
+}
+
+template <typename Tin, typename Tout>
+static int launch_decode128_conv(const DecodeConvParams& p, hipStream_t stream) {
+  Dec128Args a{};
+  a.x = p.x; a.w = p.w; a.bias = p.bias; a.cpool = p.cpool; a.csrc = p.csrc; a.cdst = p.cdst;
+  a.x_stride = p.x_stride; a.n_cslots = p.n_cslots; a.act = p.act; a.qk_l2norm = p.qk_l2norm; a.eps = p.eps;
+  a.g = p.g; a.beta = p.beta; a.o = p.o; a.pool = p.pool; a.src_slot = p.src_slot; a.dst_slot = p.dst_slot;
+  a.g_stride = p.g_stride; a.beta_stride = p.beta_stride; a.o_stride = p.o_stride; a.n_slots = p.n_slots;
+  a.n_seq = p.n_seq; a.H = p.H; a.scale = p.scale;
+  switch (p.W) {
+    case 2: return launch_decode128<Tin, Tout, 2, 128>(a, stream);
+    case 3: return launch_decode128<Tin, Tout, 3, 128>(a, stream);
+    case 4: return launch_decode128<Tin, Tout, 4, 128>(a, stream);
+    default: return fail(KDA_ERR_UNSUPPORTED, "decode_conv: W = %d (2..4)", p.W);
   }
 }
 

@@ -283,3 +283,62 @@ def test_verify_token_counts_and_sizes(dev, oracle64, T_spec, d, dtype):
     tol = {} if dtype == torch.bfloat16 else {"rel": 1e-5, "mx": 1e-4}
     U.assert_close("o", U.to_np(o), ref["o"], **tol)
     U.assert_close("committed", U.to_np(pool[N:]), ref["committed"], rel=1e-5, mx=1e-4)
+
+
+@pytest.mark.parametrize("T_spec,dtype,mu_g", [(8, torch.float32, 0.0), (5, torch.bfloat16, 0.0),
+                                               (2, torch.float32, 0.0), (8, torch.float32, 4.0),
+                                               (7, torch.bfloat16, 4.0)])
+def test_verify_d128_window_form(dev, oracle64, T_spec, dtype, mu_g):
+    """d = 128 with 2..8 tokens: outputs and committed states against the
+    oracle for accepted lengths 0..T_spec, fast (E[alpha] = 0.5) and slow
+    (alpha ~ 0.98) decay, a zero source and a rejected length."""
+    U.say(f"verify d128 window T_spec={T_spec} {dtype} mu_g={mu_g}")
+    N, H, d = 20, 2, 128
+    wl = make_workload(4, n_seq=N, H=H, d=d, T=T_spec, mu_g=mu_g)
+    q, k, v, g, b = (t.to(dtype) for t in (wl.q, wl.k, wl.v, wl.g, wl.beta))
+    L = torch.arange(N, dtype=torch.int32) % (T_spec + 1)
+    L[N - 1] = T_spec + 3   # rejected
+    init = wl.init_states.clone()
+    init[3] = 0.0           # the oracle's zero state for the sequence given src = -1
+    ref = oracle64.kda_verify(q, k, v, g, b, init, L)
+    pool = torch.cat([wl.init_states, torch.full_like(wl.init_states, 5.0)]).to(dev)
+    src = torch.arange(N, dtype=torch.int32, device=dev)
+    src[3] = -1
+    dst = torch.arange(N, dtype=torch.int32, device=dev) + N
+    o = torch.empty(N, T_spec, H, d, dtype=dtype, device=dev)
+    clen = torch.full((N,), -7, dtype=torch.int32, device=dev)
+    K.kda_verify(q.to(dev), k.to(dev), v.to(dev), g.to(dev), b.to(dev), pool, src, dst, o=o,
+                 accepted_len=L.to(dev), committed_len_out=clen)
+    torch.cuda.synchronize()
+    expect = L.clone()
+    expect[N - 1] = -1
+    assert torch.equal(clen.cpu(), expect)
+    tol = {} if dtype == torch.bfloat16 else {"rel": 1e-5, "mx": 1e-4}
+    U.assert_close("o", U.to_np(o), ref["o"], **tol)
+    U.assert_close("committed", U.to_np(pool[N:2 * N - 1]), ref["committed"][:N - 1], rel=1e-5, mx=1e-4)
+    assert torch.all(pool[2 * N - 1] == 5.0), "rejected sequence wrote its destination"
+    assert torch.equal(pool[:N].cpu(), wl.init_states), "source states modified"
+
+
+def test_verify_d128_decay_spikes(dev, oracle64):
+    """Per-token log-decay spikes of -20 on random channels (states decayed
+    towards zero on those channels within one token): outputs and committed
+    states stay finite and match the oracle."""
+    U.say("verify d128 decay spikes")
+    N, H, d, T_spec = 8, 2, 128, 8
+    wl = make_workload(4, n_seq=N, H=H, d=d, T=T_spec)
+    g = wl.g.clone()
+    r = torch.Generator().manual_seed(11)
+    spike = torch.rand(g.shape, generator=r) < 0.05
+    g[spike] = -20.0
+    L = torch.full((N,), T_spec, dtype=torch.int32)
+    ref = oracle64.kda_verify(wl.q, wl.k, wl.v, g, wl.beta, wl.init_states, L)
+    pool = torch.cat([wl.init_states, torch.zeros_like(wl.init_states)]).to(dev)
+    src = torch.arange(N, dtype=torch.int32, device=dev)
+    o = torch.empty(N, T_spec, H, d, device=dev)
+    K.kda_verify(wl.q.to(dev), wl.k.to(dev), wl.v.to(dev), g.to(dev), wl.beta.to(dev), pool, src, src + N,
+                 o=o, accepted_len=L.to(dev))
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all() and torch.isfinite(pool).all()
+    U.assert_close("o", U.to_np(o), ref["o"], rel=1e-5, mx=1e-4)
+    U.assert_close("committed", U.to_np(pool[N:]), ref["committed"], rel=1e-5, mx=1e-4)
