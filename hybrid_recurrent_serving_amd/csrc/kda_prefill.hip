@@ -285,6 +285,7 @@ struct Smem {
   alignas(16) bf16_t Mb[16][PT];          // -M = -L_1^{-1} A10: hi in columns 0..15, lo in 16..31
 
   alignas(16) TIN g_raw[TILE][D];         // raw gates of the next chunk
+  uint32_t nonzero[NW];                   // transition mode: wave's state slice not all zero
   union {
     // the solve: 16x16 blocks of A, transposed ([c][r] = A[r][c]), in the
     // waves that form them (3: A00; 4: A10, A11; 5: A11)
@@ -1080,14 +1081,49 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
   };
   using T_ = std::true_type;
   using F_ = std::false_type;
+  // Transition mode: M evolves with V = 0, so once every entry of M is
+  // exactly zero it stays exactly zero (u = U - W S' = 0 and the state update
+  // adds right_k^T 0), and the rest of the segment can be skipped without
+  // changing a bit of the result.  Checked every ZCHK chunks (after a step,
+  // whose last act is a barrier); with the usual decay M underflows to exact
+  // zeros within a few hundred tokens, while a slowly decaying M (values held
+  // at denormals) simply keeps running.
+  constexpr int ZCHK = 16;
+  auto m_is_zero = [&]() __attribute__((always_inline)) -> bool {
+    const int tid = launder(static_cast<int>(threadIdx.x));
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    if (NWC == NW || wave < NWC) {
+      uint32_t bits = 0;
+#pragma unroll
+      for (int q = 0; q < NQ; ++q)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) bits |= __float_as_uint(S[q][i]) & 0x7fffffffu;
+      const uint64_t nzm = __ballot(bits != 0u);
+      if (lane == 0) sm.nonzero[wave] = nzm != 0 ? 1u : 0u;
+    }
+    lds_barrier();
+    uint32_t any = 0;
+#pragma unroll
+    for (int w = 0; w < NWC; ++w) any |= sm.nonzero[w];
+    return any == 0;
+  };
   // one step variant per loop, so that nothing in the loop body joins
   // register values from different variants
   auto run = [&](auto out_t) __attribute__((always_inline)) {
+    constexpr bool WITH_O = decltype(out_t)::value;
     int cp = 0;
     int64_t n = first;
+    int since = 0;
     for (; n + CH < hi; n += CH) {
       step(n, cp, T_{}, T_{}, out_t);
       cp ^= 1;
+      if constexpr (!WITH_O) {
+        if (mode == kModeTransition && ++since == ZCHK) {
+          since = 0;
+          if (m_is_zero()) return;   // M = 0 from here to the segment's end
+        }
+      }
     }
     step(n, cp, T_{}, F_{}, out_t);
   };

@@ -265,6 +265,28 @@ def test_prefill_segment_scan_slow_decay(dev, oracle64, d):
     U.assert_close("state(split vs whole)", r["final"].numpy(), whole["final"].numpy())
 
 
+def test_prefill_segment_scan_fast_decay(dev, oracle64):
+    """Segments of 2,048 tokens with the usual decay (E[alpha] = 0.5): the
+    transition of a segment underflows to exact zeros within a few hundred
+    tokens and its chain stops at the next check, which must leave every
+    output, checkpoint and final state as the oracle has them, and as the
+    same call without splitting."""
+    U.say("prefill segment scan, fast decay (transition stops at exact zero)")
+    lens = [5000, 7000, 4100]
+    starts = [0, 64, 32]
+    wl = make_workload(2, lengths=lens, H=2, d=128)
+    r = run_prefill(dev, wl, chunk=64, start_pos=starts, ckpt_interval=1024, segment_len=2048)
+    ref = oracle_run(oracle64, wl, r["init"], r["has"], start_pos=np.array(starts, np.int32),
+                     ckpt_interval=1024)
+    assert r["ckpt_pos"] == list(ref["ckpt_pos"]) == r["ckpt_plan"]
+    U.assert_close("o", r["o"].numpy(), ref["o"])
+    U.assert_close("state", r["final"].numpy(), ref["final"])
+    U.assert_close("ckpt", r["ckpt"].numpy(), ref["ckpt"])
+    whole = run_prefill(dev, wl, chunk=64, start_pos=starts, ckpt_interval=1024, segment_len=-1)
+    U.assert_close("o(split vs whole)", r["o"].numpy(), whole["o"].numpy())
+    U.assert_close("state(split vs whole)", r["final"].numpy(), whole["final"].numpy())
+
+
 def test_prefill_segment_scan_tiny_fp32(dev, oracle64):
     """The tiny fp32 workload (chunk 16) split into 16-token segments."""
     U.say("prefill segment scan, tiny fp32")
