@@ -568,7 +568,7 @@ def bench_long(args, torch, K, make_workload):
     pf = bench_prefill_long(torch, K, make_workload, dev, iters=max(1, min(args.steps, 10)))
     T = pf["tokens"]
     achieved = T * PREFILL_BYTES_PER_TOKEN / (pf["ms"] * 1e-3) / 1e9
-    roof = {"kernel": "prefill_kernel<128,bf16,bf16> (kda_prefill_varlen, segment scan: pass A + pass B)",
+    roof = {"kernel": "prefill_kernel<128,bf16,bf16> (kda_prefill_varlen, segment scan: zero-started segments + transitions, combine, fix-up)",
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
             "alg_bytes_per_launch": T * PREFILL_BYTES_PER_TOKEN, "avg_launch_us": round(pf["ms"] * 1e3, 2),

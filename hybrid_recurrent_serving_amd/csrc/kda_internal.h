@@ -93,15 +93,16 @@ struct PrefillParams {
   float scale;
   // segment scan (long sequences): set by launch_prefill
   int32_t segment_len;            // effective length (> 0), or <= 0 = no split
-  int32_t mode;                   // kModeFull / kModeLocal / kModeTransition / kModePassA
+  int32_t mode;                   // kModeFull / kModeLocal / kModeTransition / kModePassA / kModeFixup
   const int32_t* seg_cu;          // [n_seq + 1] first work item of each sequence, or NULL
   const int32_t* blk_cu;          // [n_seq + 1] first workspace block of each sequence
   float* ws_states;               // 3 d x d blocks per head for every block index
+  int32_t* ws_zero;               // per block index and head: chunks after which the transition is exactly 0, or -1
   int64_t ws_max_blocks;
 };
 
 // work modes of the prefill kernel
-enum { kModeFull = 0, kModeLocal = 1, kModeTransition = 2, kModePassA = 3 };
+enum { kModeFull = 0, kModeLocal = 1, kModeTransition = 2, kModePassA = 3, kModeFixup = 4 };
 constexpr int32_t kDefaultSegmentLen = 32768;
 
 int64_t prefill_workspace_bytes(const PrefillParams& p, int D);

@@ -342,7 +342,14 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
   const int g4 = lane >> 4;             // 16-lane group
   const int l16 = lane & 15;
   const int H = p.H;
-  // pass A runs both of its modes in one launch (grid.y = 2)
+  // Modes.  Full: an unsplit launch.  Segment scan, pass A (one launch,
+  // grid.y = 2): local (y = 0) runs every segment with outputs and
+  // checkpoints, the first one from its true initial state and the others
+  // from zero, and keeps each end state S_loc; transition (y = 1) runs M of
+  // every later segment from I with v = 0 and records after how many chunks
+  // M was exactly zero.  Fix-up (pass B, after the combine): every later
+  // segment reruns, from its combined incoming state, the chunks before its
+  // M became zero.
   const int mode = p.mode == kModePassA ? kModeLocal + static_cast<int>(blockIdx.y) : p.mode;
   const int item = static_cast<int>(blockIdx.x / H);
   const int h = static_cast<int>(blockIdx.x % H);
@@ -364,10 +371,10 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
   }
   const bool first_seg = m == 0;
   const bool last_seg = m == nseg - 1;
-  // pass A (local end state / transition) is not needed for a last segment,
-  // and the transition of a first segment is never used
-  if (mode == kModeLocal && last_seg) return;
-  if (mode == kModeTransition && (first_seg || last_seg)) return;
+  // The transition of a first segment is never needed; a first segment (and
+  // an unsplit sequence) is final after pass A and has no fix-up
+  if (mode == kModeTransition && first_seg) return;
+  if (mode == kModeFixup && first_seg) return;
 
   int64_t bos = p.cu[s], eos = p.cu[s + 1];
   bos = bos < 0 ? 0 : (bos > p.T_tot ? p.T_tot : bos);
@@ -386,15 +393,30 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
     hi = (w0 + m + 1) * seg;
     hi = hi < end ? hi : end;
   }
-  const bool outputs = mode == kModeFull;
+  const bool outputs = mode != kModeTransition;
   const int src = p.src_slot[s];
   const int dst = p.dst_slot[s];
   const bool has_src = src >= 0 && src < p.n_slots;
-  const bool has_dst = dst >= 0 && dst < p.n_slots && last_seg && outputs;
   // segment-scan blocks of this item (kind 0: incoming state, 1: local end
   // state, 2: transition), each a d x d fp32 matrix per head
   const int64_t blk = p.seg_cu ? static_cast<int64_t>(p.blk_cu[s]) + m : -1;
   const bool has_blk = nseg > 1 && blk >= 0 && blk < p.ws_max_blocks;
+  // Fix-up (pass B) of a later segment: the state entering the segment is
+  // the combined one, and only the chunks before the segment's transition
+  // became exactly zero are run again (all of them if it never did); past
+  // that point the local chain of pass A, started from zero, is the state.
+  bool full_run = true;
+  if (mode == kModeFixup) {
+    const int32_t kz = has_blk && p.ws_zero ? p.ws_zero[blk * H + h] : -1;
+    if (kz >= 0) {
+      const int64_t stop = (lo / CH) * CH + static_cast<int64_t>(kz) * CH;
+      if (stop < hi) {
+        hi = stop;
+        full_run = false;
+      }
+    }
+  }
+  const bool has_dst = dst >= 0 && dst < p.n_slots && last_seg && outputs && full_run;
   auto ws_block = [&](int kind) -> float* {
     return p.ws_states + (blk * 3 + kind) * H * d * d + static_cast<int64_t>(h) * d * d;
   };
@@ -413,7 +435,7 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
       for (int i = 0; i < 4; ++i) S[q][i] = (16 * q + 4 * g4 + i == ncol) ? 1.f : 0.f;
   } else if (first_seg) {
     if (chain && has_src && ncol < d) state_load<D>(p.pool + (static_cast<int64_t>(src) * H + h) * d * d, S, lane, ncol, d);
-  } else if (mode == kModeFull && has_blk) {
+  } else if (mode == kModeFixup && has_blk) {
     if (chain && ncol < d) state_load<D>(ws_block(0), S, lane, ncol, d);
   }
   // The initial state is complete here: a first use inside the chunk loop
@@ -1110,18 +1132,23 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
   };
   // one step variant per loop, so that nothing in the loop body joins
   // register values from different variants
+  int32_t zero_after = -1;   // transition: chunks after which M was exactly zero
   auto run = [&](auto out_t) __attribute__((always_inline)) {
     constexpr bool WITH_O = decltype(out_t)::value;
     int cp = 0;
     int64_t n = first;
-    int since = 0;
+    int since = 0, done = 0;
     for (; n + CH < hi; n += CH) {
       step(n, cp, T_{}, T_{}, out_t);
       cp ^= 1;
+      ++done;
       if constexpr (!WITH_O) {
         if (mode == kModeTransition && ++since == ZCHK) {
           since = 0;
-          if (m_is_zero()) return;   // M = 0 from here to the segment's end
+          if (m_is_zero()) {   // M = 0 from here to the segment's end
+            zero_after = done;
+            return;
+          }
         }
       }
     }
@@ -1139,9 +1166,10 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
   // ---- final state: the destination slot, or a segment-scan block
   if (chain && ncol < d) {
     if (has_dst) state_store<D>(p.pool + (static_cast<int64_t>(dst) * H + h) * d * d, S, lane, ncol, d);
-    if (mode == kModeLocal && has_blk) state_store<D>(ws_block(1), S, lane, ncol, d);
+    if (mode == kModeLocal && has_blk && !last_seg) state_store<D>(ws_block(1), S, lane, ncol, d);
     if (mode == kModeTransition && has_blk) state_store<D>(ws_block(2), S, lane, ncol, d);
   }
+  if (mode == kModeTransition && has_blk && p.ws_zero && threadIdx.x == 0) p.ws_zero[blk * H + h] = zero_after;
 }
 
 // ---------------------------------------------------------------------------
@@ -1293,7 +1321,7 @@ static int launch_t(const PrefillParams& p0, int d, int CH, hipStream_t stream) 
                      stream, p, d);
   e = hipGetLastError();
   if (e != hipSuccess) return fail(KDA_ERR_HIP, "segment combine launch: %s", hipGetErrorString(e));
-  p.mode = kModeFull;
+  p.mode = kModeFixup;
   return launch_kernel<D, TIN, TOUT>(p, d, CH, n_items, 1, stream);
 }
 
@@ -1318,15 +1346,16 @@ static int64_t effective_segment(const PrefillParams& p) {
 static int64_t round256(int64_t x) { return (x + 255) / 256 * 256; }
 
 // Workspace layout: seg_cu [n_seq + 1] and blk_cu [n_seq + 1] (int32, each
-// rounded up to 256 bytes), then 3 fp32 blocks [H][d][d] per block index.
-// A split sequence of len >= 2 seg tokens spans at most 2 len / seg
-// segments, so 2 T_tot / seg + 1 block indices always suffice.
+// rounded up to 256 bytes), then 3 fp32 blocks [H][d][d] per block index,
+// then one int32 per block index and head (where the transition became
+// exactly zero).  A split sequence of len >= 2 seg tokens spans at most
+// 2 len / seg segments, so 2 T_tot / seg + 1 block indices always suffice.
 int64_t prefill_workspace_bytes(const PrefillParams& p, int D) {
   const int64_t seg = effective_segment(p);
   if (seg <= 0 || p.T_tot < 2 * seg) return 0;
   const int64_t blocks = 2 * p.T_tot / seg + 1;
   return 2 * round256(4 * (static_cast<int64_t>(p.n_seq) + 1)) +
-         blocks * 3 * p.H * static_cast<int64_t>(D) * D * 4;
+         blocks * 3 * p.H * static_cast<int64_t>(D) * D * 4 + round256(blocks * p.H * 4);
 }
 
 int launch_prefill(const PrefillParams& p0, int D, int in_dtype, int out_dtype, hipStream_t stream) {
@@ -1335,6 +1364,7 @@ int launch_prefill(const PrefillParams& p0, int D, int in_dtype, int out_dtype, 
   PrefillParams p = p0;
   p.seg_cu = p.blk_cu = nullptr;
   p.ws_states = nullptr;
+  p.ws_zero = nullptr;
   p.ws_max_blocks = 0;
   if (prefill_workspace_bytes(p0, D) > 0) {
     const int64_t seg = effective_segment(p0);
@@ -1345,6 +1375,7 @@ int launch_prefill(const PrefillParams& p0, int D, int in_dtype, int out_dtype, 
     p.blk_cu = reinterpret_cast<const int32_t*>(w + idx);
     p.ws_states = reinterpret_cast<float*>(w + 2 * idx);
     p.ws_max_blocks = 2 * p.T_tot / seg + 1;
+    p.ws_zero = reinterpret_cast<int32_t*>(p.ws_states + p.ws_max_blocks * 3 * p.H * static_cast<int64_t>(D) * D);
   }
   if (in_dtype == KDA_BF16) {
     if (out_dtype == KDA_BF16) return pf::launch_d<bf16_t, bf16_t>(p, D, CH, stream);

@@ -224,12 +224,16 @@ int kda_ckpt_plan_device(const kda_plan_args *args, kda_stream_t stream);
  *
  * Segment scan.  A sequence of at least 2 * segment_len tokens is split at
  * the absolute multiples of segment_len into segments that run in parallel:
- * every segment but the last first computes, from a zero state (the first
- * segment: from its true initial state), its end state S_loc and its
- * transition M (the same recurrence applied to S = I with v = 0); then
+ * every segment runs with outputs and checkpoints from a zero state (the
+ * first segment: from its true initial state, which makes it final), ending
+ * in its state S_loc; every later segment also computes its transition M
+ * (the same recurrence applied to S = I with v = 0), which stops once M is
+ * exactly zero (it stays zero from there on).  Then
  * S_in(j+1) = M_j S_in(j) + S_loc(j) chains the segments (fp32), and every
- * segment reruns from its S_in with outputs and checkpoints.  The result is
- * the same function of the inputs as the unsplit run (up to rounding).  The
+ * later segment reruns from its S_in the chunks before its M became zero
+ * (all of them if it never did), overwriting those outputs and checkpoints;
+ * past that point the zero-started state is the state.  The result is the
+ * same function of the inputs as the unsplit run (up to rounding).  The
  * split needs the workspace: its size comes from kda_prefill_workspace_bytes
  * for the same args (0 when T_tot < 2 * segment_len, since nothing can be
  * split then).  segment_len: 0 = the library default (32768), < 0 = never
