@@ -79,6 +79,9 @@ def traffic_for(kernel_key: str, src_name: str, per_launch_units: float):
 COPY_BYTES = 256 * 2 ** 20
 
 
+PMC_PREFILL_CALLS = 3   # varlen prefill calls in a counter pass (2 warm-up + 1)
+
+
 def pmc_pass(torch, K, make_workload):
     """The launches the counter passes read: a plain device copy of a known
     size (the calibration), decode and fused decode steps over rotating
@@ -107,7 +110,7 @@ def pmc_pass(torch, K, make_workload):
         s_ = torch.arange((i % P) * N, (i % P + 1) * N, dtype=torch.int32, device=dev)
         K.kda_decode_conv(x, cw, cpool, cs, cs, g, bt, o, pool, s_, s_, act=1, qk_l2norm=True)
     del pool
-    bench_prefill_varlen(torch, K, make_workload, dev, iters=1)
+    bench_prefill_varlen(torch, K, make_workload, dev, iters=PMC_PREFILL_CALLS - 2)   # + 2 warm-up calls
     torch.cuda.synchronize()
 
 
@@ -145,13 +148,13 @@ def ingest_pmc(fetch_csv, write_csv):
             ("decode_conv_kernel_d128_bf16", lambda r: is_decode128(r["Kernel_Name"], 4),
              "kda_step.hip", 128 * 16, "all"),
             ("prefill_kernel_d128_bf16", lambda r: "prefill_kernel<128" in r["Kernel_Name"], "kda_prefill.hip",
-             varlen_tokens(), "max")):
+             varlen_tokens(), "per_call")):
         f = sel("FETCH_SIZE", pred)
         w = sel("WRITE_SIZE", pred)
         if not f or not w:
             continue
-        if pick == "max":
-            f, w = [max(f)], [max(w)]
+        if pick == "per_call":   # every prefill-kernel dispatch of the pass's varlen calls, per call
+            f, w = [sum(f) / PMC_PREFILL_CALLS], [sum(w) / PMC_PREFILL_CALLS]
         fb = sum(f) / len(f) * f_scale
         wb = sum(w) / len(w) * w_scale
         out[key] = {"hbm_bytes_per_launch": round(fb + wb), "fetch_bytes": round(fb), "write_bytes": round(wb),
@@ -454,6 +457,12 @@ PREFILL_BYTES_PER_TOKEN = 16 * (4 * 128 * 2 + 2 + 128 * 2)      # q,k,v,g + beta
 PREFILL_FLOPS_PER_TOKEN = 16 * (10 * 64 * 128 + 6 * 128 * 128)    # dense chunked count at C=64
 
 
+# Segment length of the varlen prefill: sequences of >= 2 segments run as
+# parallel segments (a caller-chosen launch parameter; same function of the
+# inputs up to rounding), which shortens the longest sequence's chain.
+VARLEN_SEGMENT = 4096
+
+
 def bench_prefill_varlen(torch, K, make_workload, dev, iters=20, wl=None):
     """16 packed sequences, lengths U{512..16384}, H=16, d=128, chunk 64,
     even sequences from random initial states, final states to fresh slots."""
@@ -471,11 +480,13 @@ def bench_prefill_varlen(torch, K, make_workload, dev, iters=20, wl=None):
     dst = torch.arange(N, 2 * N, dtype=torch.int32, device=dev)
     cu = wl.cu_seqlens.to(dev)
     o = torch.empty(T, H, D, dtype=torch.bfloat16, device=dev)
-    nws = K.kda_prefill_workspace_bytes(q, k, v, g, b, o, cu, pool, src, dst, chunk=64)
+    nws = K.kda_prefill_workspace_bytes(q, k, v, g, b, o, cu, pool, src, dst, chunk=64,
+                                        segment_len=VARLEN_SEGMENT)
     ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
 
     def run():
-        K.kda_prefill_varlen(q, k, v, g, b, o, cu, pool, src, dst, chunk=64, workspace=ws)
+        K.kda_prefill_varlen(q, k, v, g, b, o, cu, pool, src, dst, chunk=64, workspace=ws,
+                             segment_len=VARLEN_SEGMENT)
 
     for _ in range(2):
         run()
@@ -542,7 +553,8 @@ def bench_prefill(args, torch, K, make_workload):
     pf = bench_prefill_varlen(torch, K, make_workload, dev, iters=args.steps, wl=wl)
     T = pf["tokens"]
     achieved = T * PREFILL_BYTES_PER_TOKEN / (pf["ms"] * 1e-3) / 1e9
-    roof = {"kernel": "prefill_kernel<128,bf16,bf16> (kda_prefill_varlen)", "bound": "hbm",
+    roof = {"kernel": "prefill_kernel<128,bf16,bf16> (kda_prefill_varlen call: segment plan, pass A, combine, "
+                      "fix-up)", "bound": "hbm",
             "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic_for("prefill_kernel_d128_bf16", "kda_prefill.hip", T),
@@ -554,7 +566,7 @@ def bench_prefill(args, torch, K, make_workload):
     if not args.no_cpu:
         cpu = cpu_prefill(args, wl)
     cfg = {"workload": pf["workload"], "tokens": T, "H": 16, "d": 128, "chunk": 64,
-           "initial_states": "even-indexed sequences"}
+           "initial_states": "even-indexed sequences", "segment_len": VARLEN_SEGMENT}
     secondary = {}
     if not args.no_secondary:
         secondary["prefill_long_1m"] = bench_prefill_long(torch, K, make_workload, torch.device("cuda:0"))

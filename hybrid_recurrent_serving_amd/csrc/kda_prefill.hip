@@ -1262,13 +1262,15 @@ __global__ void __launch_bounds__(COMB_T) segment_combine_kernel(const PrefillPa
     }
   }
   for (int m = 1; m + 1 < nseg; ++m) {
+    // a transition recorded as exactly zero contributes exactly nothing
+    const bool m_zero = p.ws_zero && p.ws_zero[(b0 + m) * H + h] >= 0;
     __syncthreads();
     if (act) {
       const float* mr = blk(m, 2) + static_cast<int64_t>(r) * d;
       const float* sl = blk(m, 1) + static_cast<int64_t>(r) * d + c0 + j0;
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc[j] = (c0 + j0 + j < d) ? sl[j] : 0.f;
-      for (int k = 0; k < d; ++k) {
+      for (int k = 0; k < (m_zero ? 0 : d); ++k) {
         const float mk = mr[k];
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[j] += mk * X[k][j0 + j];

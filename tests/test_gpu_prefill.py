@@ -204,13 +204,16 @@ def test_prefill_deterministic(dev):
 
 
 # ------------------------------------------------------------------ full-size workloads
-def test_prefill_varlen_16_sequences_sampled(dev, oracle64):
+@pytest.mark.parametrize("segment_len", [0, 4096])
+def test_prefill_varlen_16_sequences_sampled(dev, oracle64, segment_len):
     """16 packed sequences, lengths U{512..16384}, H=16, d=128, chunk 64, bf16;
     even sequences from random initial states.  The oracle recomputes sampled
-    (sequence, head) pairs -- the longest and shortest sequence among them."""
-    U.say("prefill 16-sequence varlen (sampled oracle)")
+    (sequence, head) pairs -- the longest and shortest sequence among them.
+    Unsplit (the default segment length exceeds every sequence) and with the
+    4,096-token segments the benchmark runs."""
+    U.say(f"prefill 16-sequence varlen (sampled oracle), segment_len={segment_len}")
     wl = make_workload(2)
-    r = run_prefill(dev, wl, chunk=64)
+    r = run_prefill(dev, wl, chunk=64, segment_len=segment_len)
     lens = (wl.cu_seqlens[1:] - wl.cu_seqlens[:-1]).tolist()
     s_long = int(np.argmax(lens))
     s_short = int(np.argmin(lens))
