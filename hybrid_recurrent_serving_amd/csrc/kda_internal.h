@@ -98,6 +98,8 @@ struct PrefillParams {
   const int32_t* blk_cu;          // [n_seq + 1] first workspace block of each sequence
   float* ws_states;               // 3 d x d blocks per head for every block index
   int32_t* ws_zero;               // per block index and head: chunks after which the transition is exactly 0, or -1
+  int32_t* item_order;            // work items by decreasing token count (segment plan), or NULL
+  int64_t max_items;              // capacity of item_order
   int64_t ws_max_blocks;
 };
 

@@ -351,13 +351,15 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
   // segment reruns, from its combined incoming state, the chunks before its
   // M became zero.
   const int mode = p.mode == kModePassA ? kModeLocal + static_cast<int>(blockIdx.y) : p.mode;
-  const int item = static_cast<int>(blockIdx.x / H);
+  int item = static_cast<int>(blockIdx.x / H);
   const int h = static_cast<int>(blockIdx.x % H);
   // work item -> (sequence s, segment m): without a segment table every
-  // sequence is one item; with one, seg_cu holds each sequence's first item
+  // sequence is one item; with one, seg_cu holds each sequence's first item,
+  // and blocks take the items longest first (the plan's order table)
   int s = item, m = 0, nseg = 1;
   if (p.seg_cu) {
     if (item >= p.seg_cu[p.n_seq]) return;
+    if (p.item_order) item = p.item_order[item];
     int a = 0, b = p.n_seq;               // seg_cu[a] <= item < seg_cu[b]
     while (b - a > 1) {
       const int mid = (a + b) >> 1;
@@ -1184,11 +1186,29 @@ __device__ __forceinline__ int seq_segments(const PrefillParams& p, int s) {
   int64_t start = p.start_pos ? static_cast<int64_t>(p.start_pos[s]) : 0;
   if (start < 0) start = 0;
   const int64_t seg = p.segment_len;
-  if (len < 2 * seg) return 1;
+  if (len <= seg) return 1;
   return static_cast<int>((start + len - 1) / seg - start / seg + 1);
 }
 
 constexpr int PLAN_T = 256;
+constexpr int PLAN_ORDER_MAX = 2048;   // items the order table ranks (LDS; quadratic ranking)
+
+// tokens of segment m (of nseg) of sequence s
+__device__ __forceinline__ int item_tokens(const PrefillParams& p, int s, int m, int nseg) {
+  int64_t bos = p.cu[s], eos = p.cu[s + 1];
+  bos = bos < 0 ? 0 : (bos > p.T_tot ? p.T_tot : bos);
+  eos = eos < bos ? bos : (eos > p.T_tot ? p.T_tot : eos);
+  int64_t start = p.start_pos ? static_cast<int64_t>(p.start_pos[s]) : 0;
+  if (start < 0) start = 0;
+  const int64_t end = start + (eos - bos);
+  if (nseg <= 1) return static_cast<int>(end - start);
+  const int64_t seg = p.segment_len;
+  const int64_t w0 = start / seg;
+  const int64_t lo = m == 0 ? start : (w0 + m) * seg;
+  int64_t hi = (w0 + m + 1) * seg;
+  hi = hi < end ? hi : end;
+  return static_cast<int>(hi > lo ? hi - lo : 0);
+}
 
 __global__ void __launch_bounds__(PLAN_T) segment_plan_kernel(const PrefillParams p, int32_t* seg_cu, int32_t* blk_cu) {
   __shared__ int64_t part_i[PLAN_T], part_b[PLAN_T];
@@ -1225,6 +1245,37 @@ __global__ void __launch_bounds__(PLAN_T) segment_plan_kernel(const PrefillParam
     blk_cu[s] = static_cast<int32_t>(rb);
     ri += n;
     rb += n > 1 ? n : 0;
+  }
+  // Order table: items by decreasing token count (ties by item index), so
+  // that the longest chains are dispatched first and the short ones fill the
+  // gaps at the end.  Identity when there are more items than LDS slots.
+  if (!p.item_order) return;
+  __syncthreads();
+  const int total = seg_cu[p.n_seq];
+  __shared__ int32_t len_of[PLAN_ORDER_MAX];
+  const bool sort = total <= PLAN_ORDER_MAX && total <= p.max_items;
+  for (int i = t; i < total && i < p.max_items; i += PLAN_T) {
+    if (!sort) {
+      p.item_order[i] = i;
+      continue;
+    }
+    int lo_s = 0, hi_s = p.n_seq;          // seg_cu[lo_s] <= i < seg_cu[hi_s]
+    while (hi_s - lo_s > 1) {
+      const int mid = (lo_s + hi_s) >> 1;
+      if (seg_cu[mid] <= i) lo_s = mid; else hi_s = mid;
+    }
+    len_of[i] = item_tokens(p, lo_s, i - seg_cu[lo_s], seg_cu[lo_s + 1] - seg_cu[lo_s]);
+  }
+  if (!sort) return;
+  __syncthreads();
+  for (int i = t; i < total; i += PLAN_T) {
+    const int li = len_of[i];
+    int rank = 0;
+    for (int j = 0; j < total; ++j) {
+      const int lj = len_of[j];
+      rank += (lj > li || (lj == li && j < i)) ? 1 : 0;
+    }
+    p.item_order[rank] = i;
   }
 }
 
@@ -1308,8 +1359,8 @@ static int launch_t(const PrefillParams& p0, int d, int CH, hipStream_t stream) 
     return launch_kernel<D, TIN, TOUT>(p, d, CH, p.n_seq, 1, stream);
   }
   // work items: every sequence once, plus the extra segments of split ones
-  // (a split sequence of len tokens adds at most len / seg + 1 <= 1.5 len / seg)
-  const int64_t n_items = p.n_seq + (3 * p.T_tot) / (2 * static_cast<int64_t>(p.segment_len)) + 1;
+  // (a split sequence of len > seg tokens spans at most len / seg + 2 < 3 len / seg segments)
+  const int64_t n_items = p.n_seq + (3 * p.T_tot) / static_cast<int64_t>(p.segment_len) + 1;
   hipLaunchKernelGGL(segment_plan_kernel, dim3(1), dim3(PLAN_T), 0, stream, p, const_cast<int32_t*>(p.seg_cu),
                      const_cast<int32_t*>(p.blk_cu));
   hipError_t e = hipGetLastError();
@@ -1350,14 +1401,16 @@ static int64_t round256(int64_t x) { return (x + 255) / 256 * 256; }
 // Workspace layout: seg_cu [n_seq + 1] and blk_cu [n_seq + 1] (int32, each
 // rounded up to 256 bytes), then 3 fp32 blocks [H][d][d] per block index,
 // then one int32 per block index and head (where the transition became
-// exactly zero).  A split sequence of len >= 2 seg tokens spans at most
-// 2 len / seg segments, so 2 T_tot / seg + 1 block indices always suffice.
+// exactly zero), then the item order table (int32 per work item).  A sequence is split when it is longer than seg; it then
+// spans at most len / seg + 2 < 3 len / seg segments, so 3 T_tot / seg + 1
+// block indices always suffice.
 int64_t prefill_workspace_bytes(const PrefillParams& p, int D) {
   const int64_t seg = effective_segment(p);
-  if (seg <= 0 || p.T_tot < 2 * seg) return 0;
-  const int64_t blocks = 2 * p.T_tot / seg + 1;
+  if (seg <= 0 || p.T_tot <= seg) return 0;
+  const int64_t blocks = 3 * p.T_tot / seg + 1;
+  const int64_t items = p.n_seq + 3 * p.T_tot / seg + 1;
   return 2 * round256(4 * (static_cast<int64_t>(p.n_seq) + 1)) +
-         blocks * 3 * p.H * static_cast<int64_t>(D) * D * 4 + round256(blocks * p.H * 4);
+         blocks * 3 * p.H * static_cast<int64_t>(D) * D * 4 + round256(blocks * p.H * 4) + round256(items * 4);
 }
 
 int launch_prefill(const PrefillParams& p0, int D, int in_dtype, int out_dtype, hipStream_t stream) {
@@ -1367,6 +1420,8 @@ int launch_prefill(const PrefillParams& p0, int D, int in_dtype, int out_dtype, 
   p.seg_cu = p.blk_cu = nullptr;
   p.ws_states = nullptr;
   p.ws_zero = nullptr;
+  p.item_order = nullptr;
+  p.max_items = 0;
   p.ws_max_blocks = 0;
   if (prefill_workspace_bytes(p0, D) > 0) {
     const int64_t seg = effective_segment(p0);
@@ -1376,8 +1431,10 @@ int launch_prefill(const PrefillParams& p0, int D, int in_dtype, int out_dtype, 
     p.seg_cu = reinterpret_cast<const int32_t*>(w);
     p.blk_cu = reinterpret_cast<const int32_t*>(w + idx);
     p.ws_states = reinterpret_cast<float*>(w + 2 * idx);
-    p.ws_max_blocks = 2 * p.T_tot / seg + 1;
+    p.ws_max_blocks = 3 * p.T_tot / seg + 1;
     p.ws_zero = reinterpret_cast<int32_t*>(p.ws_states + p.ws_max_blocks * 3 * p.H * static_cast<int64_t>(D) * D);
+    p.max_items = p.n_seq + 3 * p.T_tot / seg + 1;
+    p.item_order = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(p.ws_zero) + round256(p.ws_max_blocks * p.H * 4));
   }
   if (in_dtype == KDA_BF16) {
     if (out_dtype == KDA_BF16) return pf::launch_d<bf16_t, bf16_t>(p, D, CH, stream);

@@ -222,7 +222,7 @@ int kda_ckpt_plan_device(const kda_plan_args *args, kda_stream_t stream);
  * so a sequence may start mid-chunk; checkpoints therefore always fall on
  * chunk boundaries.
  *
- * Segment scan.  A sequence of at least 2 * segment_len tokens is split at
+ * Segment scan.  A sequence longer than segment_len tokens is split at
  * the absolute multiples of segment_len into segments that run in parallel:
  * every segment runs with outputs and checkpoints from a zero state (the
  * first segment: from its true initial state, which makes it final), ending
@@ -235,7 +235,7 @@ int kda_ckpt_plan_device(const kda_plan_args *args, kda_stream_t stream);
  * past that point the zero-started state is the state.  The result is the
  * same function of the inputs as the unsplit run (up to rounding).  The
  * split needs the workspace: its size comes from kda_prefill_workspace_bytes
- * for the same args (0 when T_tot < 2 * segment_len, since nothing can be
+ * for the same args (0 when T_tot <= segment_len, since nothing can be
  * split then).  segment_len: 0 = the library default (32768), < 0 = never
  * split, > 0 = that length, a multiple of chunk (else KDA_ERR_ALIGN).
  * ---------------------------------------------------------------------- */

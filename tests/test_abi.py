@@ -211,20 +211,29 @@ def test_prefill_validation(lib):
 
 def test_prefill_workspace_bytes(lib):
     """Segment-scan workspace: seg_cu and blk_cu (int32 [n_seq + 1], 256-byte
-    rounded) plus three H x d x d fp32 blocks per block index and one int32
-    per block index and head (256-byte rounded), with 2 T_tot / seg + 1
-    block indices; nothing when T_tot < 2 seg."""
+    rounded) plus three H x d x d fp32 blocks per block index, one int32 per
+    block index and head, and the item order table (int32 per work item,
+    n_seq + 3 T_tot / seg + 1 items), each 256-byte rounded, with
+    3 T_tot / seg + 1 block indices; nothing when T_tot <= seg (no sequence
+    can be split)."""
     ws = lambda **kw: lib.kda_prefill_workspace_bytes(ctypes.byref(_prefill_args(**kw)))
     H, d = 2, 64
     blk = 3 * H * d * d * 4
     r256 = lambda x: (x + 255) // 256 * 256
+    n_seq = _prefill_args().n_seq
+
+    def want(T, seg):
+        nb = 3 * T // seg + 1
+        items = n_seq + 3 * T // seg + 1
+        return 2 * r256(4 * (n_seq + 1)) + nb * blk + r256(nb * H * 4) + r256(items * 4)
+
     assert ws(T_tot=100) == 0
-    assert ws(T_tot=65535) == 0                         # < 2 x 32768: nothing can split
-    nb = 2 * 65536 // 32768 + 1
-    assert ws(T_tot=65536) == 2 * 256 + nb * blk + r256(nb * H * 4)
+    assert ws(T_tot=32768) == 0                         # <= 32768: nothing can split
+    assert ws(T_tot=32769) == want(32769, 32768)
+    assert ws(T_tot=65536) == want(65536, 32768)
     assert ws(T_tot=65536, segment_len=-1) == 0
-    assert ws(T_tot=4096, segment_len=1024) == 2 * 256 + 9 * blk + r256(9 * H * 4)
-    assert ws(T_tot=2047, segment_len=1024) == 0
+    assert ws(T_tot=4096, segment_len=1024) == want(4096, 1024)
+    assert ws(T_tot=1024, segment_len=1024) == 0
 
 
 def test_ckpt_plan_matches_oracle_enumeration(oracle64):

@@ -247,7 +247,7 @@ def test_prefill_long_65536_full(dev, oracle64):
 # ------------------------------------------------------------------ segment scan
 @pytest.mark.parametrize("d", [64, 128])
 def test_prefill_segment_scan_slow_decay(dev, oracle64, d):
-    """Sequences of >= 2 segment lengths run as parallel segments joined by
+    """Sequences longer than the segment length run as parallel segments joined by
     the transition combine.  Slow decay (alpha ~ 0.98) keeps the transitions
     far from zero; unaligned starts, initial states, checkpoints that fall on
     and between segment boundaries.  Against the oracle, and against the same
