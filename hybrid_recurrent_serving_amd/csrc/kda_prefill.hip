@@ -438,7 +438,12 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
   } else if (first_seg) {
     if (chain && has_src && ncol < d) state_load<D>(p.pool + (static_cast<int64_t>(src) * H + h) * d * d, S, lane, ncol, d);
   } else if (mode == kModeFixup && has_blk) {
-    if (chain && ncol < d) state_load<D>(ws_block(0), S, lane, ncol, d);
+    // S_in(m) = M_{m-1} S_in(m-1) + S_loc(m-1): S_loc(m-1) itself for m = 1
+    // or an exactly zero M_{m-1}, else the combine's result
+    const bool direct = m == 1 || (p.ws_zero && p.ws_zero[(blk - 1) * H + h] >= 0);
+    const float* sin = direct ? p.ws_states + ((blk - 1) * 3 + 1) * H * d * d + static_cast<int64_t>(h) * d * d
+                              : ws_block(0);
+    if (chain && ncol < d) state_load<D>(sin, S, lane, ncol, d);
   }
   // The initial state is complete here: a first use inside the chunk loop
   // would leave a wait for all outstanding memory operations in every trip.
@@ -1190,6 +1195,14 @@ __device__ __forceinline__ int seq_segments(const PrefillParams& p, int s) {
   return static_cast<int>((start + len - 1) / seg - start / seg + 1);
 }
 
+// Work items of a segment-scan launch: a sequence of len tokens spans at
+// most len / seg + 2 segments (1 when it is not split), so there are at most
+// min(n_seq + 3 T_tot / seg, T_tot / seg + 2 n_seq) + 1 of them.
+__host__ __device__ inline int64_t max_work_items(int64_t n_seq, int64_t T_tot, int64_t seg) {
+  const int64_t a = n_seq + 3 * T_tot / seg, b = T_tot / seg + 2 * n_seq;
+  return (a < b ? a : b) + 1;
+}
+
 constexpr int PLAN_T = 256;
 constexpr int PLAN_ORDER_MAX = 2048;   // items the order table ranks (LDS; quadratic ranking)
 
@@ -1293,6 +1306,14 @@ __global__ void __launch_bounds__(COMB_T) segment_combine_kernel(const PrefillPa
   const int nseg = p.seg_cu[s + 1] - p.seg_cu[s];
   const int64_t b0 = p.blk_cu[s];
   if (nseg < 2 || b0 < 0 || b0 + nseg > p.ws_max_blocks || c0 >= d) return;
+  // The fix-up of segment j reads S_loc(j-1) itself when M_{j-1} is exactly
+  // zero (then S_in(j) = S_loc(j-1)); the chain is only needed when some
+  // transition is not.
+  if (p.ws_zero) {
+    bool all_zero = true;
+    for (int m = 1; m + 1 < nseg; ++m) all_zero = all_zero && p.ws_zero[(b0 + m) * H + h] >= 0;
+    if (all_zero) return;
+  }
   const int t = threadIdx.x;
   const int r = t >> 1;            // state row (key channel)
   const int j0 = 8 * (t & 1);      // first of this thread's 8 columns
@@ -1359,8 +1380,7 @@ static int launch_t(const PrefillParams& p0, int d, int CH, hipStream_t stream) 
     return launch_kernel<D, TIN, TOUT>(p, d, CH, p.n_seq, 1, stream);
   }
   // work items: every sequence once, plus the extra segments of split ones
-  // (a split sequence of len > seg tokens spans at most len / seg + 2 < 3 len / seg segments)
-  const int64_t n_items = p.n_seq + (3 * p.T_tot) / static_cast<int64_t>(p.segment_len) + 1;
+  const int64_t n_items = max_work_items(p.n_seq, p.T_tot, p.segment_len);
   hipLaunchKernelGGL(segment_plan_kernel, dim3(1), dim3(PLAN_T), 0, stream, p, const_cast<int32_t*>(p.seg_cu),
                      const_cast<int32_t*>(p.blk_cu));
   hipError_t e = hipGetLastError();
@@ -1408,7 +1428,7 @@ int64_t prefill_workspace_bytes(const PrefillParams& p, int D) {
   const int64_t seg = effective_segment(p);
   if (seg <= 0 || p.T_tot <= seg) return 0;
   const int64_t blocks = 3 * p.T_tot / seg + 1;
-  const int64_t items = p.n_seq + 3 * p.T_tot / seg + 1;
+  const int64_t items = pf::max_work_items(p.n_seq, p.T_tot, seg);
   return 2 * round256(4 * (static_cast<int64_t>(p.n_seq) + 1)) +
          blocks * 3 * p.H * static_cast<int64_t>(D) * D * 4 + round256(blocks * p.H * 4) + round256(items * 4);
 }
@@ -1433,7 +1453,7 @@ int launch_prefill(const PrefillParams& p0, int D, int in_dtype, int out_dtype, 
     p.ws_states = reinterpret_cast<float*>(w + 2 * idx);
     p.ws_max_blocks = 3 * p.T_tot / seg + 1;
     p.ws_zero = reinterpret_cast<int32_t*>(p.ws_states + p.ws_max_blocks * 3 * p.H * static_cast<int64_t>(D) * D);
-    p.max_items = p.n_seq + 3 * p.T_tot / seg + 1;
+    p.max_items = pf::max_work_items(p.n_seq, p.T_tot, seg);
     p.item_order = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(p.ws_zero) + round256(p.ws_max_blocks * p.H * 4));
   }
   if (in_dtype == KDA_BF16) {

@@ -213,7 +213,8 @@ def test_prefill_workspace_bytes(lib):
     """Segment-scan workspace: seg_cu and blk_cu (int32 [n_seq + 1], 256-byte
     rounded) plus three H x d x d fp32 blocks per block index, one int32 per
     block index and head, and the item order table (int32 per work item,
-    n_seq + 3 T_tot / seg + 1 items), each 256-byte rounded, with
+    min(n_seq + 3 T_tot / seg, T_tot / seg + 2 n_seq) + 1 items), each
+    256-byte rounded, with
     3 T_tot / seg + 1 block indices; nothing when T_tot <= seg (no sequence
     can be split)."""
     ws = lambda **kw: lib.kda_prefill_workspace_bytes(ctypes.byref(_prefill_args(**kw)))
@@ -224,7 +225,7 @@ def test_prefill_workspace_bytes(lib):
 
     def want(T, seg):
         nb = 3 * T // seg + 1
-        items = n_seq + 3 * T // seg + 1
+        items = min(n_seq + 3 * T // seg, T // seg + 2 * n_seq) + 1
         return 2 * r256(4 * (n_seq + 1)) + nb * blk + r256(nb * H * 4) + r256(items * 4)
 
     assert ws(T_tot=100) == 0
