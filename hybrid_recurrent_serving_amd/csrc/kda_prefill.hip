@@ -1117,7 +1117,7 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
   // whose last act is a barrier); with the usual decay M underflows to exact
   // zeros within a few hundred tokens, while a slowly decaying M (values held
   // at denormals) simply keeps running.
-  constexpr int ZCHK = 4;
+  constexpr int ZCHK = 1;
   auto m_is_zero = [&]() __attribute__((always_inline)) -> bool {
     const int tid = launder(static_cast<int>(threadIdx.x));
     const int lane = tid & 63;
