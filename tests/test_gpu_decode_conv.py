@@ -113,10 +113,11 @@ def test_decode_conv_widths_in_place(dev, oracle64, W):
     _check_conv_state(cs, x, hist)
 
 
-@pytest.mark.parametrize("d", [16, 32])
+@pytest.mark.parametrize("d", [16, 32, 128])
 def test_decode_conv_fp32_small(dev, oracle64, d):
-    """fp32 inputs and outputs at small head sizes: the only roundings left
-    are the fp32 accumulation orders."""
+    """fp32 inputs and outputs (small head sizes, and d = 128 with its
+    16-wave layout and fp32 conv items on two waves): the only roundings
+    left are the fp32 accumulation orders."""
     U.say(f"decode_conv fp32 d={d}")
     N, H, W = 9, 3, 4
     x, w, bias, cst, g, b, init = _case(N, H, d, W, torch.float32, seed=30 + d)

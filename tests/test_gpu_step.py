@@ -342,3 +342,28 @@ def test_verify_d128_decay_spikes(dev, oracle64):
     assert torch.isfinite(o).all() and torch.isfinite(pool).all()
     U.assert_close("o", U.to_np(o), ref["o"], rel=1e-5, mx=1e-4)
     U.assert_close("committed", U.to_np(pool[N:]), ref["committed"], rel=1e-5, mx=1e-4)
+
+
+def test_decode_d128_item_count_not_multiple_of_8(dev, oracle64):
+    """d = 128 decode with 5 sequences x 3 heads = 15 (sequence, head) items:
+    the blocks past the last whole group of 8 items take the plain block
+    order (the two halves of a head are otherwise placed on one XCD).  fp32
+    in and out against the oracle, in place and copy-on-write."""
+    U.say("decode d128, 15 items")
+    wl = make_workload(1, n_seq=5, H=3, d=128)
+    init, has = _oracle_states(wl)
+    q, k, v, g, b = (t.float() for t in (wl.q, wl.k, wl.v, wl.g, wl.beta))
+    ref = oracle64.kda_varlen(q, k, v, g, b, wl.cu_seqlens, init=init, has_init=has, scale=0.7)
+    pool = torch.cat([wl.init_states, torch.zeros_like(wl.init_states)]).to(dev)
+    src = torch.arange(5, dtype=torch.int32, device=dev)
+    o = torch.empty(5, 3, 128, device=dev)
+    K.kda_decode(q.to(dev), k.to(dev), v.to(dev), g.to(dev), b.to(dev), o, pool, src, src + 5, scale=0.7)
+    torch.cuda.synchronize()
+    U.assert_close("o", U.to_np(o), ref["o"], rel=1e-5, mx=1e-5)
+    U.assert_close("state", U.to_np(pool[5:]), ref["final"], rel=1e-5, mx=1e-5)
+    assert torch.equal(pool[:5].cpu(), wl.init_states), "source states modified"
+    pool2 = wl.init_states.to(dev).clone()
+    o2 = torch.empty(5, 3, 128, device=dev)
+    K.kda_decode(q.to(dev), k.to(dev), v.to(dev), g.to(dev), b.to(dev), o2, pool2, src, src, scale=0.7)
+    torch.cuda.synchronize()
+    assert torch.equal(o2, o) and torch.equal(pool2, pool[5:])
