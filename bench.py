@@ -34,6 +34,7 @@ HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 METRIC = "KDA prefill tokens/s (H=16,d=128) + decode/verify state GB/s vs HBM peak"
 TRAFFIC_FILE = ROOT / "profiles" / "traffic.json"
+MFMA_FILE = ROOT / "profiles" / "mfma.json"
 
 
 def parse():
@@ -51,6 +52,11 @@ def parse():
                          "(calibration), 8 decode steps, 2 varlen prefills")
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn the counter CSVs of two --pmc-pass runs into profiles/traffic.json")
+    ap.add_argument("--pmc-long", action="store_true",
+                    help="with --pmc-pass: also 2 calls of the 1M-token prefill (inputs drawn on the GPU)")
+    ap.add_argument("--ingest-mfma", nargs="+", metavar="CSV",
+                    help="turn the MFMA / VALU counter CSVs of --pmc-pass runs (MfmaUtil, VALUBusy, "
+                         "SQ_INSTS_VALU_MFMA_MOPS_BF16, GRBM_GUI_ACTIVE) into profiles/mfma.json")
     return ap.parse_args()
 
 
@@ -80,18 +86,31 @@ COPY_BYTES = 256 * 2 ** 20
 
 
 PMC_PREFILL_CALLS = 3   # varlen prefill calls in a counter pass (2 warm-up + 1)
+PMC_LONG_CALLS = 2      # 1M-token prefill calls in a counter pass with --pmc-long (1 warm-up + 1)
 
 
-def pmc_pass(torch, K, make_workload):
+GEMM_N = 8192   # the MFMA calibration: a library bf16 GEMM of 2 GEMM_N^3 flops
+
+
+def pmc_pass(torch, K, make_workload, long=False):
     """The launches the counter passes read: a plain device copy of a known
-    size (the calibration), decode and fused decode steps over rotating
-    pools, varlen prefills."""
+    size and a library bf16 GEMM of known flops (the calibrations), decode
+    and fused decode steps over rotating pools, varlen prefills (and, with
+    long, 1M-token prefills)."""
     dev = torch.device("cuda:0")
     a = torch.ones(COPY_BYTES // 4, device=dev)
     b = torch.empty_like(a)
     for _ in range(4):
         b.copy_(a)
     del a, b
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0)
+    ga = torch.randn(GEMM_N, GEMM_N, device=dev, generator=gen).to(torch.bfloat16).contiguous()
+    gb = torch.randn(GEMM_N, GEMM_N, device=dev, generator=gen).to(torch.bfloat16).contiguous()
+    for _ in range(2):
+        gc = torch.mm(ga, gb)
+    torch.cuda.synchronize()
+    del ga, gb, gc
     wl = make_workload(1)
     N, H, D, P = 128, 16, 128, 4
     q, k, v, g, bt = (t.to(dev) for t in (wl.q, wl.k, wl.v, wl.g, wl.beta))
@@ -112,6 +131,10 @@ def pmc_pass(torch, K, make_workload):
     del pool
     bench_prefill_varlen(torch, K, make_workload, dev, iters=PMC_PREFILL_CALLS - 2)   # + 2 warm-up calls
     torch.cuda.synchronize()
+    if long:
+        torch.cuda.empty_cache()
+        bench_prefill_long(torch, K, make_workload, dev, iters=PMC_LONG_CALLS - 1)   # + 1 warm-up call
+        torch.cuda.synchronize()
 
 
 def varlen_tokens():
@@ -142,29 +165,129 @@ def ingest_pmc(fetch_csv, write_csv):
         raise SystemExit("calibration copy not found in the counter files")
     f_scale = COPY_BYTES / (sum(cf) / len(cf))
     w_scale = COPY_BYTES / (sum(cw) / len(cw))
-    for key, pred, src, units, pick in (
+    for key, pred, src, units in (
             ("decode_step_kernel_d128_bf16", lambda r: is_decode128(r["Kernel_Name"], 0), "kda_step.hip",
-             128 * 16, "all"),
+             128 * 16),
             ("decode_conv_kernel_d128_bf16", lambda r: is_decode128(r["Kernel_Name"], 4),
-             "kda_step.hip", 128 * 16, "all"),
-            ("prefill_kernel_d128_bf16", lambda r: "prefill_kernel<128" in r["Kernel_Name"], "kda_prefill.hip",
-             varlen_tokens(), "per_call")):
+             "kda_step.hip", 128 * 16)):
         f = sel("FETCH_SIZE", pred)
         w = sel("WRITE_SIZE", pred)
         if not f or not w:
             continue
-        if pick == "per_call":   # every prefill-kernel dispatch of the pass's varlen calls, per call
-            f, w = [sum(f) / PMC_PREFILL_CALLS], [sum(w) / PMC_PREFILL_CALLS]
         fb = sum(f) / len(f) * f_scale
         wb = sum(w) / len(w) * w_scale
         out[key] = {"hbm_bytes_per_launch": round(fb + wb), "fetch_bytes": round(fb), "write_bytes": round(wb),
                     "source_sha256_16": kernel_source_hash(src), "units_per_launch": units,
                     "dispatches": len(f)}
+    # prefill calls: each starts with its segment plan launch; the pass's
+    # varlen calls come first, then (with --pmc-long) the 1M-token ones.  Per
+    # call: every prefill-kernel dispatch of the call, averaged over calls.
+    per_call = {}
+    for name in ("FETCH_SIZE", "WRITE_SIZE"):
+        calls = []
+        for r in sorted(rows[name], key=lambda r: int(r["Dispatch_Id"])):
+            if "segment_plan_kernel" in r["Kernel_Name"]:
+                calls.append(0.0)
+            elif calls and "prefill_kernel<128" in r["Kernel_Name"]:
+                calls[-1] += float(r["Counter_Value"]) * 1024
+        per_call[name] = calls
+    for key, c0, nc, units in (("prefill_kernel_d128_bf16", 0, PMC_PREFILL_CALLS, varlen_tokens()),
+                               ("prefill_long_kernel_d128_bf16", PMC_PREFILL_CALLS, PMC_LONG_CALLS, 1 << 20)):
+        f = per_call["FETCH_SIZE"][c0:c0 + nc]
+        w = per_call["WRITE_SIZE"][c0:c0 + nc]
+        if len(f) != nc or len(w) != nc:
+            continue
+        fb = sum(f) / nc * f_scale
+        wb = sum(w) / nc * w_scale
+        out[key] = {"hbm_bytes_per_launch": round(fb + wb), "fetch_bytes": round(fb), "write_bytes": round(wb),
+                    "source_sha256_16": kernel_source_hash("kda_prefill.hip"), "units_per_launch": units,
+                    "calls": nc}
     out["calibration"] = {"copy_bytes": COPY_BYTES, "fetch_scale": round(f_scale, 4),
                           "write_scale": round(w_scale, 4),
                           "note": "FETCH_SIZE / WRITE_SIZE of a plain device copy of copy_bytes, "
                                   "scaled to read and write exactly copy_bytes"}
     return out
+
+
+def ingest_mfma(paths):
+    """Per-call MFMA and VALU figures of the prefill kernels from the counter
+    CSVs of --pmc-pass runs: executed bf16 MFMA flops (SQ_INSTS_VALU_MFMA_MOPS_BF16
+    x 512), and MfmaUtil / VALUBusy averaged over the call's dispatches with
+    GRBM_GUI_ACTIVE (active cycles) as the weight.  The calibration is the
+    pass's library GEMM of 2 GEMM_N^3 flops: its executed flops check the x 512
+    scale, its MfmaUtil shows what a dense library kernel reaches."""
+    import csv
+    out = {}
+    want = GEMM_N ** 3 * 2
+    for path in paths:
+        disp = {}
+        for r in csv.DictReader(open(path)):
+            d = disp.setdefault(int(r["Dispatch_Id"]), {"name": r["Kernel_Name"]})
+            d[r["Counter_Name"]] = float(r["Counter_Value"])
+        order = [disp[i] for i in sorted(disp)]
+        need = ("MfmaUtil", "VALUBusy", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "GRBM_GUI_ACTIVE")
+        order = [d for d in order if all(c in d for c in need)]
+        gemm = [d for d in order if abs(d["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512 - want) < 0.1 * want]
+        if gemm and "calibration_gemm" not in out:
+            g = gemm[-1]
+            out["calibration_gemm"] = {
+                "flops": want, "executed_flops": g["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512,
+                "mfma_util": round(g["MfmaUtil"] / 100, 4), "valu_busy": round(g["VALUBusy"] / 100, 4),
+                "kernel": g["name"][:120],
+                "note": f"torch.mm of two {GEMM_N} x {GEMM_N} bf16 matrices (library GEMM)"}
+        # calls: each prefill call starts with its segment plan launch
+        calls, cur = [], None
+        for d in order:
+            if "segment_plan_kernel" in d["name"]:
+                cur = []
+                calls.append(cur)
+            elif cur is not None and ("prefill_kernel<" in d["name"] or "segment_combine_kernel" in d["name"]):
+                cur.append(d)
+        groups = [("prefill_varlen", calls[:PMC_PREFILL_CALLS], varlen_tokens())]
+        if len(calls) >= PMC_PREFILL_CALLS + PMC_LONG_CALLS:
+            groups.append(("prefill_long_1m", calls[PMC_PREFILL_CALLS:PMC_PREFILL_CALLS + PMC_LONG_CALLS],
+                           1 << 20))
+        for key, grp, tokens in groups:
+            if not grp or key in out:
+                continue
+            last = grp[-1]   # the measured call (the ones before it warm up)
+            w = sum(d["GRBM_GUI_ACTIVE"] for d in last)
+            ex = sum(d["SQ_INSTS_VALU_MFMA_MOPS_BF16"] for d in last) * 512
+            alg = tokens * PREFILL_FLOPS_PER_TOKEN
+            out[key] = {
+                "tokens": tokens, "dispatches": len(last), "alg_flops": alg, "executed_bf16_flops": ex,
+                "executed_over_alg": round(ex / alg, 4),
+                "mfma_util": round(sum(d["MfmaUtil"] * d["GRBM_GUI_ACTIVE"] for d in last) / w / 100, 4),
+                "valu_busy": round(sum(d["VALUBusy"] * d["GRBM_GUI_ACTIVE"] for d in last) / w / 100, 4),
+                "per_dispatch": [{"kernel": d["name"].split("(")[0][-60:],
+                                  "role": ("combine" if "combine" in d["name"] else
+                                           "pass A" if i == 0 else "fix-up"),
+                                  "mfma_util": round(d["MfmaUtil"] / 100, 4),
+                                  "valu_busy": round(d["VALUBusy"] / 100, 4),
+                                  "executed_bf16_flops": d["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512}
+                                 for i, d in enumerate(last)],
+                "source_sha256_16": kernel_source_hash("kda_prefill.hip")}
+    return out
+
+
+def mfma_counters(key: str, tokens: int, ms: float):
+    """The committed counter figures of a prefill workload (None when missing
+    or when the kernel source has changed since), with the executed MFMA rate
+    at this run's call time."""
+    if not MFMA_FILE.exists():
+        return None
+    try:
+        ent = json.loads(MFMA_FILE.read_text())[key]
+    except (KeyError, ValueError):
+        return None
+    if ent.get("source_sha256_16") != kernel_source_hash("kda_prefill.hip") or ent.get("tokens") != tokens:
+        return None
+    rate = ent["executed_bf16_flops"] / (ms * 1e-3) / 1e12
+    return {"executed_bf16_flops_per_call": ent["executed_bf16_flops"],
+            "executed_over_alg": ent["executed_over_alg"],
+            "executed_tflops": round(rate, 1), "executed_frac": round(rate / MFMA_BF16_PEAK_TFLOPS, 4),
+            "mfma_util": ent["mfma_util"], "valu_busy": ent["valu_busy"],
+            "source": "rocprofv3 --pmc MfmaUtil VALUBusy SQ_INSTS_VALU_MFMA_MOPS_BF16 GRBM_GUI_ACTIVE"}
 
 
 def is_decode128(kernel_name: str, W: int) -> bool:
@@ -321,7 +444,10 @@ def bench_decode(args, torch, K, make_workload):
         pf = bench_prefill_varlen(torch, K, make_workload, dev, iters=10)
         secondary["prefill_varlen"] = {k_: pf[k_] for k_ in ("workload", "tokens", "ms", "tokens_per_s",
                                                              "alg_mfma_frac", "alg_hbm_frac")}
-        secondary["prefill_long_1m"] = bench_prefill_long(torch, K, make_workload, dev)
+        secondary["prefill_varlen"]["mfma_counters"] = mfma_counters("prefill_varlen", pf["tokens"], pf["ms"])
+        lp = bench_prefill_long(torch, K, make_workload, dev)
+        lp["mfma_counters"] = mfma_counters("prefill_long_1m", lp["tokens"], lp["ms"])
+        secondary["prefill_long_1m"] = lp
 
     cpu = None
     if not args.no_cpu:
@@ -561,7 +687,8 @@ def bench_prefill(args, torch, K, make_workload):
             "alg_bytes_per_launch": T * PREFILL_BYTES_PER_TOKEN, "avg_launch_us": round(pf["ms"] * 1e3, 2),
             "mfma": {"alg_flops_per_launch": T * PREFILL_FLOPS_PER_TOKEN,
                      "achieved_tflops": round(T * PREFILL_FLOPS_PER_TOKEN / (pf["ms"] * 1e-3) / 1e12, 1),
-                     "peak_tflops": MFMA_BF16_PEAK_TFLOPS, "frac": pf["alg_mfma_frac"]}}
+                     "peak_tflops": MFMA_BF16_PEAK_TFLOPS, "frac": pf["alg_mfma_frac"],
+                     "counters": mfma_counters("prefill_varlen", T, pf["ms"])}}
     cpu = None
     if not args.no_cpu:
         cpu = cpu_prefill(args, wl)
@@ -582,11 +709,13 @@ def bench_long(args, torch, K, make_workload):
     achieved = T * PREFILL_BYTES_PER_TOKEN / (pf["ms"] * 1e-3) / 1e9
     roof = {"kernel": "prefill_kernel<128,bf16,bf16> (kda_prefill_varlen, segment scan: zero-started segments + transitions, combine, fix-up)",
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic_for("prefill_long_kernel_d128_bf16", "kda_prefill.hip", T),
             "alg_bytes_per_launch": T * PREFILL_BYTES_PER_TOKEN, "avg_launch_us": round(pf["ms"] * 1e3, 2),
             "mfma": {"alg_flops_per_launch": T * PREFILL_FLOPS_PER_TOKEN,
                      "achieved_tflops": round(T * PREFILL_FLOPS_PER_TOKEN / (pf["ms"] * 1e-3) / 1e12, 1),
-                     "peak_tflops": MFMA_BF16_PEAK_TFLOPS, "frac": pf["alg_mfma_frac"]}}
+                     "peak_tflops": MFMA_BF16_PEAK_TFLOPS, "frac": pf["alg_mfma_frac"],
+                     "counters": mfma_counters("prefill_long_1m", T, pf["ms"])}}
     cpu = None
     if not args.no_cpu:
         cpu = cpu_long(args, make_workload)
@@ -689,6 +818,11 @@ def main():
         TRAFFIC_FILE.write_text(json.dumps(data, indent=1) + "\n")
         print(json.dumps(data))
         return
+    if args.ingest_mfma:
+        data = ingest_mfma(args.ingest_mfma)
+        MFMA_FILE.write_text(json.dumps(data, indent=1) + "\n")
+        print(json.dumps(data))
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}))
@@ -701,7 +835,7 @@ def main():
     from hybrid_recurrent_serving_amd.inputs import make_workload
     K.load_library()
     if args.pmc_pass:
-        pmc_pass(torch, K, make_workload)
+        pmc_pass(torch, K, make_workload, long=args.pmc_long)
         print(json.dumps({"pmc_pass": "done"}))
         return
     if args.workload == "decode":
