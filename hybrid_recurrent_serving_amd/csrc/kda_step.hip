@@ -780,32 +780,80 @@ static int launch_decode128_conv(const DecodeConvParams& p, hipStream_t stream) 
 
 // ---------------------------------------------------------------------------
 // Speculative verify with the short convolution fused in.  As the staged
-// verify of step_kernel, with q, k, v of the T_spec tokens formed in LDS by
-// the conv items: each owns V channels of the head's q, k or v block, keeps
-// the T_spec raw token vectors and a W-tap sliding window in registers, and
-// writes y (fp32) per token.  The q / k norms of token j are formed in the
-// token loop from LDS (every wave, no extra barrier).  The conv history is
-// committed with the state: the W-1 raw inputs ending at token L-1.
+// verify of step_kernel, with q, k, v of the T_spec tokens formed by the
+// short convolution of the head's q, k, v channels (+ SiLU) and the q / k
+// norms of token j formed in the token loop from LDS (every wave, no extra
+// barrier).  The conv history is committed with the state: the W-1 raw
+// inputs ending at token L-1.
+//
+// Every conv input of the workgroup (history, taps, bias, the token rows of
+// the head's channels, the gates) is requested first, as 16-byte units
+// spread over all threads, then the state slice: the load counter is in
+// order, so the conv can run from LDS once its own units have arrived while
+// the state is still in flight.  A state source that is absent reads through
+// a buffer resource of size 0 (every load returns 0), so the state loads are
+// issued on every path and no wait has to cover them early.
+
+// 16-byte units of conv inputs staged per workgroup: history [3][D][W-1],
+// taps [3][D][W], bias [3][D], token rows [n_tok][3][D], gates [n_tok][D]
+template <int D, typename Tin, int W>
+__host__ __device__ constexpr int vconv_units(int n_tok) {
+  constexpr int UPB = D * static_cast<int>(sizeof(Tin)) / 16;
+  return 3 * (W - 1) * UPB + 3 * W * UPB + 3 * UPB + n_tok * 4 * UPB;
+}
+// staged units per thread, and the staging area in units: every thread
+// stores all of its units (those past the end into the area's tail), so no
+// load sits behind a condition the compiler could sink it into
+template <int D, typename Tin, int W>
+__host__ __device__ constexpr int vconv_per_thread() {
+  return (vconv_units<D, Tin, W>(STEP_TMAX) + 64 * StepLayout<D>::WPH - 1) / (64 * StepLayout<D>::WPH);
+}
+template <int D, typename Tin, int W>
+__host__ __device__ constexpr int vconv_stage_units() {
+  return vconv_per_thread<D, Tin, W>() * 64 * StepLayout<D>::WPH;
+}
+
+constexpr int kBufWord3 = 0x00020000;   // raw 32-bit buffer (gfx9 descriptor word 3)
+constexpr int kBufNonTemporal = 2;
+
+// A buffer resource from values that are the same on every lane, held in
+// scalar registers (the compiler cannot always prove that by itself).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* base, int bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
+  void* ua = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(ua, 0, __builtin_amdgcn_readfirstlane(bytes), kBufWord3);
+}
+
 template <int D, typename Tin, typename Tout, int W>
 __global__ void __launch_bounds__(64 * StepLayout<D>::WPH)
 verify_conv_kernel(const DecodeConvParams p) {
   using L = StepLayout<D>;
   constexpr int NTH = 64 * L::WPH;
-  constexpr int V = Vec16x<Tin>::N;
-  constexpr int NCI = 3 * D / V;
+  constexpr int V = Vec16x<Tin>::N;       // channels per 16-byte unit
+  constexpr int UPB = D / V;              // units per D channels
+  constexpr int NCI = 3 * D / V;          // conv items per token
   constexpr int HW = W - 1;
+  constexpr int U_HIST = 3 * HW * UPB;
+  constexpr int U_TAPS = 3 * W * UPB;
+  constexpr int U_FIX = U_HIST + U_TAPS + 3 * UPB;
+  constexpr int NU = vconv_per_thread<D, Tin, W>();   // staged units per thread
   static_assert(NCI <= NTH, "one conv item per thread");
   extern __shared__ __align__(16) float s_dyn[];
   const int T = p.T_spec;
   const int TD = T * D;
-  float* const s_a = s_dyn;            // exp(g) [T][D]
-  float* const s_k = s_dyn + TD;       // k [T][D]
-  float* const s_q = s_dyn + 2 * TD;   // q [T][D]
-  float* const s_v = s_dyn + 3 * TD;   // v [T][D]
-  float* const s_o = s_dyn + 4 * TD;   // o [T][D]
-  float* const s_b = s_dyn + 5 * TD;   // beta [T]
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  uint4* const stg = reinterpret_cast<uint4*>(s_dyn);              // staged units
+  float* const fl = s_dyn + 4 * vconv_stage_units<D, Tin, W>();
+  float* const s_a = fl;               // exp(g) [T][D]
+  float* const s_k = fl + TD;          // k [T][D]
+  float* const s_q = fl + 2 * TD;      // q [T][D]
+  float* const s_v = fl + 3 * TD;      // v [T][D]
+  float* const s_b = fl + 4 * TD;      // beta [T] (one slot per thread: every thread stores one)
+  float* const s_o = s_dyn;            // o [T][D], over the staged units (dead once the conv has run)
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   const int64_t sh = blockIdx.x;
   const int s = static_cast<int>(sh / p.H);
   const int h = static_cast<int>(sh % p.H);
@@ -823,104 +871,130 @@ verify_conv_kernel(const DecodeConvParams p) {
   if (p.accepted_len) {
     Lc = p.accepted_len[s];
     valid = Lc >= 0 && Lc <= T;
-    if (h == 0 && threadIdx.x == 0 && p.committed_len_out) p.committed_len_out[s] = valid ? Lc : -1;
+    if (h == 0 && tid == 0 && p.committed_len_out) p.committed_len_out[s] = valid ? Lc : -1;
   }
   const bool do_store = valid && has_dst;
   const int n_tok = p.o ? T : (valid ? Lc : 0);
 
-  // The conv works on (channel vector, token) items: item it = c + NCI * j
-  // owns channels ch(c) .. ch(c) + V - 1 of token j, spread over all
-  // threads.  Its taps and xbar vectors (history or earlier tokens) are
-  // mostly cache hits; the state slice is requested first.
   const int64_t C = 3LL * p.H * D;
+  const int64_t HD = static_cast<int64_t>(p.H) * D;
+  const int64_t hd = static_cast<int64_t>(h) * D;
   const int csrc = p.csrc[s];
   const int cdst = p.cdst[s];
   const bool hist_ok = csrc >= 0 && csrc < p.n_cslots;
-  const Tin* xs = static_cast<const Tin*>(p.x) + static_cast<int64_t>(s) * T * p.x_stride;
-  const Tin* hs = static_cast<const Tin*>(p.cpool) + static_cast<int64_t>(hist_ok ? csrc : 0) * C * HW;
-  const int n_items = NCI * n_tok;
-  auto item_ch = [&](int c) -> int64_t {
-    const int blk = c / (D / V), cc = (c % (D / V)) * V;
-    return static_cast<int64_t>(blk) * p.H * D + static_cast<int64_t>(h) * D + cc;
-  };
+  const Tin* const wt = static_cast<const Tin*>(p.w);
+  const Tin* const xs = static_cast<const Tin*>(p.x) + static_cast<int64_t>(s) * T * p.x_stride;
+  const Tin* const hs = static_cast<const Tin*>(p.cpool) + static_cast<int64_t>(hist_ok ? csrc : 0) * C * HW;
+  const Tin* const bs = static_cast<const Tin*>(p.bias);
+  const Tin* const gs = static_cast<const Tin*>(p.g) + static_cast<int64_t>(s) * T * p.g_stride;
 
-  // state slice, then exp(g) and beta of the tokens into LDS
-  float S[L::RPL][4];
-  if (has_src) {
-    const float* sp = p.pool + ((static_cast<int64_t>(src) * p.H + h) * D + row0) * D + col;
+  // 1. conv input units (an absent history or bias reads the taps instead;
+  //    every thread issues NU loads, those past the end repeat the last
+  //    unit), and beta
+  const int n_units = U_FIX + 4 * UPB * n_tok;
+  uint4 raw[NU];
 #pragma unroll
-    for (int i = 0; i < L::RPL; ++i) ld4_stream(sp + static_cast<int64_t>(i) * D, S[i]);
-  } else {
-#pragma unroll
-    for (int i = 0; i < L::RPL; ++i) S[i][0] = S[i][1] = S[i][2] = S[i][3] = 0.f;
-  }
-  {
-    const Tin* gb = static_cast<const Tin*>(p.g);
-    const Tin* bb = static_cast<const Tin*>(p.beta);
-    for (int e = 4 * static_cast<int>(threadIdx.x); e < n_tok * D; e += 4 * NTH) {
-      const int j = e / D, c = e % D;
-      const int64_t tok = static_cast<int64_t>(s) * T + j;
-      float g4[4];
-      io<Tin>::ld4(gb + tok * p.g_stride + static_cast<int64_t>(h) * D + c, g4);
-      *reinterpret_cast<float4*>(&s_a[j * D + c]) = make_float4(expf(g4[0]), expf(g4[1]), expf(g4[2]), expf(g4[3]));
-      if (c == 0) s_b[j] = io<Tin>::ld(bb + tok * p.beta_stride + h);
+  for (int k = 0; k < NU; ++k) {
+    {
+      const int u = k * NTH + tid < n_units ? k * NTH + tid : n_units - 1;
+      const Tin* a;
+      if (u < U_HIST) {
+        const int blk = u / (HW * UPB), r = u % (HW * UPB);
+        a = hist_ok ? hs + (blk * HD + hd) * HW + r * V : wt;
+      } else if (u < U_HIST + U_TAPS) {
+        const int v = u - U_HIST, blk = v / (W * UPB), r = v % (W * UPB);
+        a = wt + (blk * HD + hd) * W + r * V;
+      } else if (u < U_FIX) {
+        const int v = u - U_HIST - U_TAPS, blk = v / UPB, r = v % UPB;
+        a = bs ? bs + blk * HD + hd + r * V : wt;
+      } else if (u < U_FIX + 3 * UPB * n_tok) {
+        const int v = u - U_FIX, t = v / (3 * UPB), r = v % (3 * UPB);
+        a = xs + t * p.x_stride + (r / UPB) * HD + hd + (r % UPB) * V;
+      } else {
+        const int v = u - U_FIX - 3 * UPB * n_tok, t = v / UPB, r = v % UPB;
+        a = gs + t * p.g_stride + hd + r * V;
+      }
+      raw[k] = *reinterpret_cast<const uint4*>(a);
     }
   }
-  // the convolution: y = bias + sum_k w[k] xbar[j + k] (+ SiLU)
-  for (int it = static_cast<int>(threadIdx.x); it < n_items; it += NTH) {
+  const Tin braw = static_cast<const Tin*>(p.beta)[(static_cast<int64_t>(s) * T + (tid < T ? tid : T - 1)) *
+                                                      p.beta_stride + h];
+
+  // 2. the state slice (zeros when there is no source)
+  float S[L::RPL][4];
+  {
+    const float* head = p.pool + (static_cast<int64_t>(has_src ? src : 0) * p.H + h) * D * D;
+    const __amdgpu_buffer_rsrc_t rs = uniform_rsrc(head, has_src ? D * D * 4 : 0);
+    const int vo = (row0 * D + col) * 4;
+#pragma unroll
+    for (int i = 0; i < L::RPL; ++i) {
+      const auto x = __builtin_amdgcn_raw_buffer_load_b128(rs, vo, i * D * 4, kBufNonTemporal);
+      S[i][0] = __uint_as_float(x[0]); S[i][1] = __uint_as_float(x[1]);
+      S[i][2] = __uint_as_float(x[2]); S[i][3] = __uint_as_float(x[3]);
+    }
+  }
+
+  // 3. units and beta to LDS
+#pragma unroll
+  for (int k = 0; k < NU; ++k)
+    stg[k * NTH + tid] = raw[k];
+  s_b[tid] = io<Tin>::ld(&braw);
+  __syncthreads();
+
+  // 4. exp(g), the convolution y = bias + sum_k w[k] xbar[j + k] (+ SiLU)
+  //    with xbar = history ++ tokens, and the new conv history
+  //    xbar[Lc .. Lc + W - 2], all from the staged units
+  const Tin* const st = reinterpret_cast<const Tin*>(stg);
+  const Tin* const st_taps = st + U_HIST * V;
+  const Tin* const st_bias = st + (U_HIST + U_TAPS) * V;
+  const Tin* const st_x = st + U_FIX * V;
+  const Tin* const st_g = st_x + 3 * D * n_tok;
+  for (int e = 4 * tid; e < n_tok * D; e += 4 * NTH) {
+    float g4[4];
+    io<Tin>::ld4(st_g + e, g4);
+    *reinterpret_cast<float4*>(&s_a[e]) = make_float4(expf(g4[0]), expf(g4[1]), expf(g4[2]), expf(g4[3]));
+  }
+  // xbar[idx] of channels cc .. cc + V - 1 of block blk
+  auto xbar = [&](const int idx, const int blk, const int cc, float (&x)[V]) __attribute__((always_inline)) {
+    if (idx >= HW) {
+      Vec16x<Tin>::ld(st_x + (static_cast<int64_t>(idx - HW) * 3 + blk) * D + cc, x);
+    } else if (hist_ok) {
+#pragma unroll
+      for (int i = 0; i < V; ++i) x[i] = io<Tin>::ld(st + (blk * D + cc + i) * HW + idx);
+    } else {
+#pragma unroll
+      for (int i = 0; i < V; ++i) x[i] = 0.f;
+    }
+  };
+  for (int it = tid; it < n_tok * NCI; it += NTH) {
     const int c = it % NCI, j = it / NCI;
-    const int blk = c / (D / V), cc = (c % (D / V)) * V;
-    const int64_t ch = item_ch(c);
+    const int blk = c / UPB, cc = (c % UPB) * V;
     float tapf[W][V], xbf[W][V];
 #pragma unroll
-    for (int b = 0; b < W; ++b) Vec16x<Tin>::ld(static_cast<const Tin*>(p.w) + ch * W + b * V, tapf[b]);
-    // xbar[j + k], k = 0 .. W-1: history entry j + k (< W-1) or token j + k - (W-1)
+    for (int b = 0; b < W; ++b) Vec16x<Tin>::ld(st_taps + (blk * D + cc) * W + b * V, tapf[b]);
 #pragma unroll
-    for (int k = 0; k < W; ++k) {
-      const int idx = j + k;
-      if (idx >= HW) {
-        Vec16x<Tin>::ld(xs + static_cast<int64_t>(idx - HW) * p.x_stride + ch, xbf[k]);
-      } else if (hist_ok) {
-        // entry idx of channels ch .. ch + V - 1: elements (ch + i) * HW + idx
-#pragma unroll
-        for (int i = 0; i < V; ++i) xbf[k][i] = io<Tin>::ld(hs + (ch + i) * HW + idx);
-      } else {
-#pragma unroll
-        for (int i = 0; i < V; ++i) xbf[k][i] = 0.f;
-      }
-    }
+    for (int k = 0; k < W; ++k) xbar(j + k, blk, cc, xbf[k]);
     float* yb = blk == 0 ? s_q : (blk == 1 ? s_k : s_v);
 #pragma unroll
     for (int i = 0; i < V; ++i) {
-      float acc = p.bias ? io<Tin>::ld(static_cast<const Tin*>(p.bias) + ch + i) : 0.f;
+      float acc = bs ? io<Tin>::ld(st_bias + blk * D + cc + i) : 0.f;
 #pragma unroll
       for (int k = 0; k < W; ++k) acc = fmaf(tapf[(i * W + k) / V][(i * W + k) % V], xbf[k][i], acc);
       if (p.act == 1) acc = silu_fast(acc);
       yb[j * D + cc + i] = acc;
     }
   }
-  // conv history after the accepted tokens: xbar[Lc .. Lc + W - 2] with
-  // xbar = history ++ tokens, one item per channel vector
-  if (valid && cdst >= 0 && cdst < p.n_cslots && static_cast<int>(threadIdx.x) < NCI) {
-    const int64_t ch = item_ch(threadIdx.x);
+  if (valid && cdst >= 0 && cdst < p.n_cslots && tid < NCI) {
+    const int blk = tid / UPB, cc = (tid % UPB) * V;
     float nh[V * HW];
 #pragma unroll
     for (int j = 0; j < HW; ++j) {
-      const int idx = Lc + j;
       float val[V];
-      if (idx >= HW) {
-        Vec16x<Tin>::ld(xs + static_cast<int64_t>(idx - HW) * p.x_stride + ch, val);
-      } else if (hist_ok) {
-#pragma unroll
-        for (int i = 0; i < V; ++i) val[i] = io<Tin>::ld(hs + (ch + i) * HW + idx);
-      } else {
-#pragma unroll
-        for (int i = 0; i < V; ++i) val[i] = 0.f;
-      }
+      xbar(Lc + j, blk, cc, val);
 #pragma unroll
       for (int i = 0; i < V; ++i) nh[i * HW + j] = val[i];
     }
-    Tin* np_ = static_cast<Tin*>(p.cpool) + (static_cast<int64_t>(cdst) * C + ch) * HW;
+    Tin* np_ = static_cast<Tin*>(p.cpool) + (static_cast<int64_t>(cdst) * C + blk * HD + hd + cc) * HW;
 #pragma unroll
     for (int b = 0; b < HW; ++b) {
       float f[V];
@@ -1012,11 +1086,16 @@ static int launch_verify_conv_t(const DecodeConvParams& p, hipStream_t stream) {
   using L = StepLayout<D>;
   dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(p.n_seq) * p.H));
   dim3 block(64 * L::WPH);
-  const size_t lds = (5 * static_cast<size_t>(p.T_spec) * D + p.T_spec) * sizeof(float);
+  const size_t fl = (4 * static_cast<size_t>(p.T_spec) * D + 64 * L::WPH) * sizeof(float);
+  auto lds = [&](int W) -> size_t {
+    const int u = W == 2 ? vconv_stage_units<D, Tin, 2>()
+                         : (W == 3 ? vconv_stage_units<D, Tin, 3>() : vconv_stage_units<D, Tin, 4>());
+    return 16 * static_cast<size_t>(u) + fl;
+  };
   switch (p.W) {
-    case 2: hipLaunchKernelGGL((verify_conv_kernel<D, Tin, Tout, 2>), grid, block, lds, stream, p); break;
-    case 3: hipLaunchKernelGGL((verify_conv_kernel<D, Tin, Tout, 3>), grid, block, lds, stream, p); break;
-    case 4: hipLaunchKernelGGL((verify_conv_kernel<D, Tin, Tout, 4>), grid, block, lds, stream, p); break;
+    case 2: hipLaunchKernelGGL((verify_conv_kernel<D, Tin, Tout, 2>), grid, block, lds(2), stream, p); break;
+    case 3: hipLaunchKernelGGL((verify_conv_kernel<D, Tin, Tout, 3>), grid, block, lds(3), stream, p); break;
+    case 4: hipLaunchKernelGGL((verify_conv_kernel<D, Tin, Tout, 4>), grid, block, lds(4), stream, p); break;
     default: return fail(KDA_ERR_UNSUPPORTED, "verify_conv: W = %d (2..4)", p.W);
   }
   hipError_t e = hipGetLastError();

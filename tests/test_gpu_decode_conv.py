@@ -131,7 +131,7 @@ def test_decode_conv_fp32_small(dev, oracle64, d):
 
 
 def _verify_case(N, Ts, H, d, W, dtype, seed):
-    wl = make_workload(4, n_seq=N, H=H, d=d, seed=seed)
+    wl = make_workload(4, n_seq=N, H=H, d=d, T=max(Ts, 8), seed=seed)
     gen = torch.Generator().manual_seed(2000 + seed)
     C = 3 * H * d
     w, st, x = draw_conv(gen, N * Ts, C, W, N, dtype, torch.device("cpu"))
@@ -140,7 +140,7 @@ def _verify_case(N, Ts, H, d, W, dtype, seed):
 
 
 def _run_verify(dev, x, w, cst, g, b, init, L, *, out_dtype, with_o=True, commit=True, conv_src=None,
-                act=1, norm=1):
+                act=1, norm=1, bias=None, state_src=None):
     N, Ts, C = x.shape
     H, d = g.shape[2], g.shape[3]
     W = w.shape[1]
@@ -150,27 +150,33 @@ def _run_verify(dev, x, w, cst, g, b, init, L, *, out_dtype, with_o=True, commit
     pool[:N] = init.to(dev)
     pool[N:] = float("nan")           # destinations hold NaN until written
     cpool[N:] = float("nan")
-    src = torch.arange(N, dtype=torch.int32, device=dev)
-    dst = src + N
+    src = torch.tensor(state_src if state_src is not None else list(range(N)), dtype=torch.int32, device=dev)
+    dst = torch.arange(N, dtype=torch.int32, device=dev) + N
     csrc = torch.tensor(conv_src if conv_src is not None else list(range(N)), dtype=torch.int32, device=dev)
     o = torch.empty(N, Ts, H, d, dtype=out_dtype, device=dev) if with_o else None
     acc = torch.tensor(L, dtype=torch.int32, device=dev) if commit else None
     clen = torch.full((N,), -7, dtype=torch.int32, device=dev)
     K.kda_verify_conv(x.to(dev), w.to(dev), cpool, csrc, dst, g.to(dev), b.to(dev), pool, src, dst, o=o,
-                      accepted_len=acc, committed_len_out=clen if commit else None, act=act, qk_l2norm=norm)
+                      accepted_len=acc, committed_len_out=clen if commit else None, act=act, qk_l2norm=norm,
+                      conv_bias=None if bias is None else bias.to(dev))
     torch.cuda.synchronize()
     return o, pool[N:], cpool[N:], clen, pool[:N], cpool[:N]
 
 
-def _verify_reference(orc, x, w, cst, g, b, init, L, conv_src, act=1, norm=1):
+def _verify_reference(orc, x, w, cst, g, b, init, L, conv_src, act=1, norm=1, bias=None, state_src=None):
     N = x.shape[0]
     H, d = g.shape[2], g.shape[3]
     hist = cst.float().numpy().copy()
     for s in range(N):
         if conv_src[s] < 0:
             hist[s] = 0.0
-    return orc.kda_verify_conv(x, w, g, b, init.double().numpy(), hist, L, H=H, d=d, act=act,
-                               qk_l2norm=norm), hist
+    S0 = init.double().numpy().copy()
+    if state_src is not None:
+        for s in range(N):
+            if state_src[s] < 0:
+                S0[s] = 0.0
+    return orc.kda_verify_conv(x, w, g, b, S0, hist, L, H=H, d=d, act=act, qk_l2norm=norm,
+                               bias=None if bias is None else bias.float().numpy()), hist
 
 
 def test_verify_conv_batched_128x8(dev, oracle64):
@@ -228,3 +234,45 @@ def test_verify_conv_fp32_small(dev, oracle64, d, W):
     U.assert_close("o", U.to_np(o), ref["o"], rel=1e-5, mx=1e-5)
     U.assert_close("committed", U.to_np(st), ref["committed"], rel=1e-5, mx=1e-5)
     assert np.array_equal(cs.cpu().numpy(), ref["conv_state"].astype(np.float32))
+
+
+def test_verify_conv_16_tokens_bias_absent_sources(dev, oracle64):
+    """The longest window (16 tokens), H=4, d=128, W=4, bf16, with a conv
+    bias: every conv input unit of a workgroup is staged (the most units per
+    thread); sequences without a state source start from zero, sequences
+    without conv history from a zero history; L over {0..16} plus one
+    rejected length."""
+    U.say("verify_conv 32 x 16 x H4 x d128, bias, absent sources")
+    N, Ts, H, d, W = 32, 16, 4, 128, 4
+    x, w, cst, g, b, init = _verify_case(N, Ts, H, d, W, torch.bfloat16, seed=61)
+    bias = (torch.rand(3 * H * d, generator=torch.Generator().manual_seed(62)) - 0.5).to(torch.bfloat16)
+    gen = torch.Generator().manual_seed(63)
+    L = torch.randint(0, Ts + 1, (N,), generator=gen).tolist()
+    L[5] = Ts + 1
+    conv_src = [s if s % 3 else -1 for s in range(N)]
+    state_src = [s if s % 4 != 1 else -1 for s in range(N)]
+    o, st, cs, clen, st_src, cs_src = _run_verify(dev, x, w, cst, g, b, init, L, out_dtype=torch.bfloat16,
+                                                  conv_src=conv_src, bias=bias, state_src=state_src)
+    ref, _ = _verify_reference(oracle64, x, w, cst, g, b, init, L, conv_src, bias=bias, state_src=state_src)
+    U.assert_close("o", U.to_np(o), ref["o"])
+    ok = np.array([0 <= v <= Ts for v in L])
+    assert clen.cpu().tolist() == [v if 0 <= v <= Ts else -1 for v in L]
+    U.assert_close("committed", U.to_np(st)[ok], ref["committed"][ok])
+    assert torch.isnan(st[5]).all() and torch.isnan(cs[5]).all()
+    assert np.array_equal(cs.to("cpu", torch.float32).numpy()[ok], ref["conv_state"][ok].astype(np.float32))
+    assert torch.equal(st_src.cpu(), init) and torch.equal(cs_src.cpu(), cst)
+
+
+def test_verify_conv_fp32_d128_16_tokens(dev, oracle64):
+    """fp32 inputs and outputs at d = 128 with 16 tokens: the largest LDS
+    footprint of the fused verify (staged units and token arrays)."""
+    U.say("verify_conv fp32 d=128 T=16")
+    N, Ts, H, d, W = 4, 16, 2, 128, 4
+    x, w, cst, g, b, init = _verify_case(N, Ts, H, d, W, torch.float32, seed=64)
+    L = [16, 0, 7, 12]
+    o, st, cs, clen, _, _ = _run_verify(dev, x, w, cst, g, b, init, L, out_dtype=torch.float32)
+    ref, _ = _verify_reference(oracle64, x, w, cst, g, b, init, L, list(range(N)))
+    U.assert_close("o", U.to_np(o), ref["o"], rel=1e-5, mx=1e-5)
+    U.assert_close("committed", U.to_np(st), ref["committed"], rel=1e-5, mx=1e-5)
+    assert np.array_equal(cs.cpu().numpy(), ref["conv_state"].astype(np.float32))
+    assert clen.cpu().tolist() == L
