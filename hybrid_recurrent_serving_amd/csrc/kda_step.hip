@@ -45,6 +45,23 @@ template <typename Tin, typename Tout> static int launch_decode128_conv(const De
 
 constexpr int STEP_TMAX = 16;   // most tokens per sequence in one call
 
+// State slices through a buffer resource: one whose size is 0 makes every
+// load return 0, so a slice with no source needs no branch and its loads are
+// issued on every path (which keeps the compiler's load-counter waits exact).
+constexpr int kBufWord3 = 0x00020000;   // raw 32-bit buffer (gfx9 descriptor word 3)
+constexpr int kBufNonTemporal = 2;
+
+// A buffer resource from values that are the same on every lane, held in
+// scalar registers (the compiler cannot always prove that by itself).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* base, int bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
+  void* ua = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(ua, 0, __builtin_amdgcn_readfirstlane(bytes), kBufWord3);
+}
+
+
 // STAGED: token inputs and outputs go through LDS (several tokens per call);
 // without it (one token, the decode step) every lane loads its own rows and
 // stores its own outputs directly.
@@ -57,7 +74,7 @@ step_kernel(const StepParams p) {
   // k, q (fp32, [token][row]), v ([token][col]), beta; outputs staged the
   // same way and stored after the last token
   // dynamic LDS sized for the call's T_spec: five [T_spec][D] fp32 arrays
-  // (alpha, k, q, v, o) and beta [T_spec]
+  // (alpha, k, q, v, o) and beta (one slot per thread: every thread stores one)
   extern __shared__ __align__(16) float s_dyn[];
   const int TD = p.T_spec * D;
   float* const s_a = s_dyn;
@@ -95,40 +112,82 @@ step_kernel(const StepParams p) {
   const bool do_store = valid && has_dst;
   const int n_tok = p.o ? p.T_spec : (valid ? Lc : 0);
 
-  // state slice (in flight while the token inputs are staged)
-  float S[L::RPL][4];
-  if (has_src) {
-    const float* sp = p.pool + ((static_cast<int64_t>(src) * p.H + h) * D + row0) * D + col;
-#pragma unroll
-    for (int i = 0; i < L::RPL; ++i) ld4_stream(sp + static_cast<int64_t>(i) * D, S[i]);
-  } else {
-#pragma unroll
-    for (int i = 0; i < L::RPL; ++i) S[i][0] = S[i][1] = S[i][2] = S[i][3] = 0.f;
-  }
-
   const Tin* qb = static_cast<const Tin*>(p.q);
   const Tin* kb = static_cast<const Tin*>(p.k);
   const Tin* vb = static_cast<const Tin*>(p.v);
   const Tin* gb = static_cast<const Tin*>(p.g);
   const Tin* bb = static_cast<const Tin*>(p.beta);
+  float S[L::RPL][4];
   if constexpr (STAGED) {
-    // 4 consecutive elements per thread and pass (one 8- or 16-byte load per tensor)
-    for (int e = 4 * static_cast<int>(threadIdx.x); e < n_tok * D; e += 4 * NTH) {
+    // The token inputs are requested before the state slice, NE groups of 4
+    // elements per thread and tensor (sized for the longest window; groups
+    // past the end repeat the last one, so every load and LDS store is
+    // unconditional and none is sunk behind a condition), plus one beta per
+    // thread.  The load counter is in order: staging them in LDS then waits
+    // only for them, with the state loads still in flight.
+    constexpr int NE = (STEP_TMAX * D / 4 + NTH - 1) / NTH;
+    constexpr int NW4 = 4 * sizeof(Tin) / 4;   // 32-bit words per 4 elements
+    typedef __attribute__((ext_vector_type(NW4))) uint32_t raw4;
+    const int last = n_tok * D - 4 > 0 ? n_tok * D - 4 : 0;
+    raw4 rk[NE], rq[NE], rv[NE], rgg[NE];
+#pragma unroll
+    for (int t = 0; t < NE; ++t) {
+      const int e0 = 4 * (t * NTH + static_cast<int>(threadIdx.x));
+      const int e = e0 < last ? e0 : last;
       const int j = e / D, c = e % D;
-      const int64_t off = (static_cast<int64_t>(s) * p.T_spec + j);
+      const int64_t off = static_cast<int64_t>(s) * p.T_spec + j;
       const int64_t hc = static_cast<int64_t>(h) * D + c;
-      float k4[4], q4[4], v4[4], g4[4];
-      io<Tin>::ld4(kb + off * p.k_stride + hc, k4);
-      io<Tin>::ld4(qb + off * p.q_stride + hc, q4);
-      io<Tin>::ld4(vb + off * p.v_stride + hc, v4);
-      io<Tin>::ld4(gb + off * p.g_stride + hc, g4);
-      *reinterpret_cast<float4*>(&s_k[j * D + c]) = make_float4(k4[0], k4[1], k4[2], k4[3]);
-      *reinterpret_cast<float4*>(&s_q[j * D + c]) = make_float4(q4[0], q4[1], q4[2], q4[3]);
-      *reinterpret_cast<float4*>(&s_v[j * D + c]) = make_float4(v4[0], v4[1], v4[2], v4[3]);
-      *reinterpret_cast<float4*>(&s_a[j * D + c]) = make_float4(expf(g4[0]), expf(g4[1]), expf(g4[2]), expf(g4[3]));
-      if (c == 0) s_b[j] = io<Tin>::ld(bb + off * p.beta_stride + h);
+      rk[t] = *reinterpret_cast<const raw4*>(kb + off * p.k_stride + hc);
+      rq[t] = *reinterpret_cast<const raw4*>(qb + off * p.q_stride + hc);
+      rv[t] = *reinterpret_cast<const raw4*>(vb + off * p.v_stride + hc);
+      rgg[t] = *reinterpret_cast<const raw4*>(gb + off * p.g_stride + hc);
     }
+    const int jb = static_cast<int>(threadIdx.x) < p.T_spec ? static_cast<int>(threadIdx.x) : p.T_spec - 1;
+    const Tin braw = bb[(static_cast<int64_t>(s) * p.T_spec + jb) * p.beta_stride + h];
+    // the state slice (zeros without a source: a buffer resource of size 0)
+    {
+      const float* head = p.pool + (static_cast<int64_t>(has_src ? src : 0) * p.H + h) * D * D;
+      const __amdgpu_buffer_rsrc_t rs = uniform_rsrc(head, has_src ? D * D * 4 : 0);
+      const int vo = (row0 * D + col) * 4;
+#pragma unroll
+      for (int i = 0; i < L::RPL; ++i) {
+        const auto x = __builtin_amdgcn_raw_buffer_load_b128(rs, vo, i * D * 4, kBufNonTemporal);
+        S[i][0] = __uint_as_float(x[0]); S[i][1] = __uint_as_float(x[1]);
+        S[i][2] = __uint_as_float(x[2]); S[i][3] = __uint_as_float(x[3]);
+      }
+    }
+    auto unpack = [](const raw4& r, float (&x)[4]) __attribute__((always_inline)) {
+      if constexpr (sizeof(Tin) == 2) {
+        x[0] = __uint_as_float(r[0] << 16); x[1] = __uint_as_float(r[0] & 0xffff0000u);
+        x[2] = __uint_as_float(r[1] << 16); x[3] = __uint_as_float(r[1] & 0xffff0000u);
+      } else {
+        x[0] = __uint_as_float(r[0]); x[1] = __uint_as_float(r[1]);
+        x[2] = __uint_as_float(r[2]); x[3] = __uint_as_float(r[3]);
+      }
+    };
+#pragma unroll
+    for (int t = 0; t < NE; ++t) {
+      const int e0 = 4 * (t * NTH + static_cast<int>(threadIdx.x));
+      const int e = e0 < last ? e0 : last;
+      float k4[4], q4[4], v4[4], g4[4];
+      unpack(rk[t], k4); unpack(rq[t], q4); unpack(rv[t], v4); unpack(rgg[t], g4);
+      *reinterpret_cast<float4*>(&s_k[e]) = make_float4(k4[0], k4[1], k4[2], k4[3]);
+      *reinterpret_cast<float4*>(&s_q[e]) = make_float4(q4[0], q4[1], q4[2], q4[3]);
+      *reinterpret_cast<float4*>(&s_v[e]) = make_float4(v4[0], v4[1], v4[2], v4[3]);
+      *reinterpret_cast<float4*>(&s_a[e]) = make_float4(expf(g4[0]), expf(g4[1]), expf(g4[2]), expf(g4[3]));
+    }
+    s_b[threadIdx.x] = io<Tin>::ld(&braw);
     __syncthreads();
+  } else {
+    // state slice
+    if (has_src) {
+      const float* sp = p.pool + ((static_cast<int64_t>(src) * p.H + h) * D + row0) * D + col;
+#pragma unroll
+      for (int i = 0; i < L::RPL; ++i) ld4_stream(sp + static_cast<int64_t>(i) * D, S[i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < L::RPL; ++i) S[i][0] = S[i][1] = S[i][2] = S[i][3] = 0.f;
+    }
   }
 
   float* dp = has_dst ? p.pool + ((static_cast<int64_t>(dst) * p.H + h) * D + row0) * D + col : nullptr;
@@ -228,7 +287,7 @@ static int launch_step_t(const StepParams& p, hipStream_t stream) {
     if constexpr (D == 128) return launch_decode128_plain<Tin, Tout>(p, stream);
     hipLaunchKernelGGL((step_kernel<D, Tin, Tout, false>), grid, block, 0, stream, p);
   } else {
-    const size_t lds = (5 * static_cast<size_t>(p.T_spec) * D + p.T_spec) * sizeof(float);
+    const size_t lds = (5 * static_cast<size_t>(p.T_spec) * D + 64 * L::WPH) * sizeof(float);
     hipLaunchKernelGGL((step_kernel<D, Tin, Tout, true>), grid, block, lds, stream, p);
   }
   hipError_t e = hipGetLastError();
@@ -811,19 +870,6 @@ __host__ __device__ constexpr int vconv_per_thread() {
 template <int D, typename Tin, int W>
 __host__ __device__ constexpr int vconv_stage_units() {
   return vconv_per_thread<D, Tin, W>() * 64 * StepLayout<D>::WPH;
-}
-
-constexpr int kBufWord3 = 0x00020000;   // raw 32-bit buffer (gfx9 descriptor word 3)
-constexpr int kBufNonTemporal = 2;
-
-// A buffer resource from values that are the same on every lane, held in
-// scalar registers (the compiler cannot always prove that by itself).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* base, int bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
-  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
-  void* ua = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
-  return __builtin_amdgcn_make_buffer_rsrc(ua, 0, __builtin_amdgcn_readfirstlane(bytes), kBufWord3);
 }
 
 template <int D, typename Tin, typename Tout, int W>
