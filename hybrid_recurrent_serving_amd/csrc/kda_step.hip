@@ -61,6 +61,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* base,
   return __builtin_amdgcn_make_buffer_rsrc(ua, 0, __builtin_amdgcn_readfirstlane(bytes), kBufWord3);
 }
 
+// 16 bytes of a state slice through a buffer resource (non-temporal; dropped
+// when the resource has size 0)
+__device__ __forceinline__ void st4_rsrc(__amdgpu_buffer_rsrc_t r, int voff, int soff, const float (&x)[4]) {
+  typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+  const u32x4 v = {__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3])};
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, voff, soff, kBufNonTemporal);
+}
+
 
 // STAGED: token inputs and outputs go through LDS (several tokens per call);
 // without it (one token, the decode step) every lane loads its own rows and
@@ -190,10 +198,14 @@ step_kernel(const StepParams p) {
     }
   }
 
-  float* dp = has_dst ? p.pool + ((static_cast<int64_t>(dst) * p.H + h) * D + row0) * D + col : nullptr;
+  // the destination slice through a buffer resource: one scalar base and the
+  // lane offset, no per-row 64-bit addresses held across the token loop
+  const __amdgpu_buffer_rsrc_t rd =
+      uniform_rsrc(p.pool + (static_cast<int64_t>(has_dst ? dst : 0) * p.H + h) * D * D, has_dst ? D * D * 4 : 0);
+  const int vd = (row0 * D + col) * 4;
   if (do_store && Lc == 0) {
 #pragma unroll
-    for (int i = 0; i < L::RPL; ++i) st4_stream(dp + static_cast<int64_t>(i) * D, S[i]);
+    for (int i = 0; i < L::RPL; ++i) st4_rsrc(rd, vd, i * D * 4, S[i]);
   }
 
   for (int j = 0; j < n_tok; ++j) {
@@ -263,7 +275,7 @@ step_kernel(const StepParams p) {
     }
     if (do_store && j + 1 == Lc) {
 #pragma unroll
-      for (int i = 0; i < L::RPL; ++i) st4_stream(dp + static_cast<int64_t>(i) * D, S[i]);
+      for (int i = 0; i < L::RPL; ++i) st4_rsrc(rd, vd, i * D * 4, S[i]);
     }
   }
   if (STAGED && p.o) {
@@ -1051,10 +1063,14 @@ verify_conv_kernel(const DecodeConvParams p) {
   }
   __syncthreads();
 
-  float* dp = has_dst ? p.pool + ((static_cast<int64_t>(dst) * p.H + h) * D + row0) * D + col : nullptr;
+  // the destination slice through a buffer resource: one scalar base and the
+  // lane offset, no per-row 64-bit addresses held across the token loop
+  const __amdgpu_buffer_rsrc_t rd =
+      uniform_rsrc(p.pool + (static_cast<int64_t>(has_dst ? dst : 0) * p.H + h) * D * D, has_dst ? D * D * 4 : 0);
+  const int vd = (row0 * D + col) * 4;
   if (do_store && Lc == 0) {
 #pragma unroll
-    for (int i = 0; i < L::RPL; ++i) st4_stream(dp + static_cast<int64_t>(i) * D, S[i]);
+    for (int i = 0; i < L::RPL; ++i) st4_rsrc(rd, vd, i * D * 4, S[i]);
   }
   for (int j = 0; j < n_tok; ++j) {
     float inv_q = 1.f, inv_k = 1.f;
@@ -1074,8 +1090,8 @@ verify_conv_kernel(const DecodeConvParams p) {
       const float4 k4 = *reinterpret_cast<const float4*>(&s_k[j * D + row0 + i]);
       const float4 q4 = *reinterpret_cast<const float4*>(&s_q[j * D + row0 + i]);
       const float4 a4 = *reinterpret_cast<const float4*>(&s_a[j * D + row0 + i]);
-      kr[i] = k4.x * inv_k; kr[i + 1] = k4.y * inv_k; kr[i + 2] = k4.z * inv_k; kr[i + 3] = k4.w * inv_k;
-      qr[i] = q4.x * inv_q; qr[i + 1] = q4.y * inv_q; qr[i + 2] = q4.z * inv_q; qr[i + 3] = q4.w * inv_q;
+      kr[i] = k4.x; kr[i + 1] = k4.y; kr[i + 2] = k4.z; kr[i + 3] = k4.w;
+      qr[i] = q4.x; qr[i + 1] = q4.y; qr[i + 2] = q4.z; qr[i + 3] = q4.w;
       ar[i] = a4.x; ar[i + 1] = a4.y; ar[i + 2] = a4.z; ar[i + 3] = a4.w;
     }
     const float4 v4 = *reinterpret_cast<const float4*>(&s_v[j * D + col]);
@@ -1090,29 +1106,31 @@ verify_conv_kernel(const DecodeConvParams p) {
         w[c] = fmaf(S[i][c], kr[i], w[c]);
       }
     }
-    float u[4];
+    // the norms act on the reduced values: w = inv_k S^T k, S += k (inv_k u)^T,
+    // o = inv_q S^T q
+    float uk[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      w[c] = wave_sum_from<L::LPR>(w[c]);
-      u[c] = beta * (vc[c] - w[c]);
+      w[c] = wave_sum_from<L::LPR>(w[c]) * inv_k;
+      uk[c] = beta * (vc[c] - w[c]) * inv_k;
     }
     float o[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < L::RPL; ++i) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        S[i][c] = fmaf(kr[i], u[c], S[i][c]);
+        S[i][c] = fmaf(kr[i], uk[c], S[i][c]);
         o[c] = fmaf(S[i][c], qr[i], o[c]);
       }
     }
     if (p.o) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) o[c] = wave_sum_from<L::LPR>(o[c]) * p.scale;
+      for (int c = 0; c < 4; ++c) o[c] = wave_sum_from<L::LPR>(o[c]) * (inv_q * p.scale);
       if (rg == 0) *reinterpret_cast<float4*>(&s_o[j * D + col]) = make_float4(o[0], o[1], o[2], o[3]);
     }
     if (do_store && j + 1 == Lc) {
 #pragma unroll
-      for (int i = 0; i < L::RPL; ++i) st4_stream(dp + static_cast<int64_t>(i) * D, S[i]);
+      for (int i = 0; i < L::RPL; ++i) st4_rsrc(rd, vd, i * D * 4, S[i]);
     }
   }
   if (p.o) {
