@@ -95,8 +95,8 @@ GEMM_N = 8192   # the MFMA calibration: a library bf16 GEMM of 2 GEMM_N^3 flops
 def pmc_pass(torch, K, make_workload, long=False):
     """The launches the counter passes read: a plain device copy of a known
     size and a library bf16 GEMM of known flops (the calibrations), decode
-    and fused decode steps over rotating pools, varlen prefills (and, with
-    long, 1M-token prefills)."""
+    and fused decode steps over rotating pools, verify and fused verify
+    calls, varlen prefills (and, with long, 1M-token prefills)."""
     dev = torch.device("cuda:0")
     a = torch.ones(COPY_BYTES // 4, device=dev)
     b = torch.empty_like(a)
@@ -129,6 +129,8 @@ def pmc_pass(torch, K, make_workload, long=False):
         s_ = torch.arange((i % P) * N, (i % P + 1) * N, dtype=torch.int32, device=dev)
         K.kda_decode_conv(x, cw, cpool, cs, cs, g, bt, o, pool, s_, s_, act=1, qk_l2norm=True)
     del pool
+    bench_verify_secondary(torch, K, make_workload, dev, n=2, warm=2)   # 4 verify + 4 fused verify calls
+    torch.cuda.empty_cache()
     bench_prefill_varlen(torch, K, make_workload, dev, iters=PMC_PREFILL_CALLS - 2)   # + 2 warm-up calls
     torch.cuda.synchronize()
     if long:
@@ -213,7 +215,8 @@ def ingest_mfma(paths):
     """Per-call MFMA and VALU figures of the prefill kernels from the counter
     CSVs of --pmc-pass runs: executed bf16 MFMA flops (SQ_INSTS_VALU_MFMA_MOPS_BF16
     x 512), and MfmaUtil / VALUBusy averaged over the call's dispatches with
-    GRBM_GUI_ACTIVE (active cycles) as the weight.  The calibration is the
+    GRBM_GUI_ACTIVE (active cycles) as the weight; the same busy figures for
+    the decode and verify kernels.  The calibration is the
     pass's library GEMM of 2 GEMM_N^3 flops: its executed flops check the x 512
     scale, its MfmaUtil shows what a dense library kernel reaches."""
     import csv
@@ -235,6 +238,20 @@ def ingest_mfma(paths):
                 "mfma_util": round(g["MfmaUtil"] / 100, 4), "valu_busy": round(g["VALUBusy"] / 100, 4),
                 "kernel": g["name"][:120],
                 "note": f"torch.mm of two {GEMM_N} x {GEMM_N} bf16 matrices (library GEMM)"}
+        # the decode and verify kernels: MfmaUtil / VALUBusy averaged over
+        # their dispatches, weighted by active cycles
+        for key, pred in (("decode_conv_kernel_d128_bf16", lambda n: is_decode128(n, 4)),
+                          ("decode_step_kernel_d128_bf16", lambda n: is_decode128(n, 0)),
+                          ("verify_kernel_d128_bf16", lambda n: n.startswith("void kda::step_kernel<128, unsigned short, unsigned short, true>")),
+                          ("verify_conv_kernel_d128_bf16", lambda n: n.startswith("void kda::verify_conv_kernel<128, unsigned short, unsigned short, 4>"))):
+            ds = [d for d in order if pred(d["name"])]
+            if not ds or key in out:
+                continue
+            w = sum(d["GRBM_GUI_ACTIVE"] for d in ds)
+            out[key] = {"dispatches": len(ds),
+                        "mfma_util": round(sum(d["MfmaUtil"] * d["GRBM_GUI_ACTIVE"] for d in ds) / w / 100, 4),
+                        "valu_busy": round(sum(d["VALUBusy"] * d["GRBM_GUI_ACTIVE"] for d in ds) / w / 100, 4),
+                        "source_sha256_16": kernel_source_hash("kda_step.hip")}
         # calls: each prefill call starts with its segment plan launch
         calls, cur = [], None
         for d in order:
@@ -517,9 +534,9 @@ def bench_planner_secondary(torch, K, dev, iters=200):
     return out
 
 
-def bench_verify_secondary(torch, K, make_workload, dev):
+def bench_verify_secondary(torch, K, make_workload, dev, n=200, warm=10):
     """Speculative verify (128 x 8 tokens, fused commit) -- reported beside the
-    decode line."""
+    decode line.  n timed calls of each form after warm untimed ones."""
     wl = make_workload(4)
     N, Ts, H, D = 128, 8, 16, 128
     q, k, v, g, b = (t.to(dev) for t in (wl.q, wl.k, wl.v, wl.g, wl.beta))
@@ -530,13 +547,12 @@ def bench_verify_secondary(torch, K, make_workload, dev):
     slot_sets = [torch.arange(i * N, (i + 1) * N, dtype=torch.int32, device=dev) for i in range(P)]
     L = wl.accepted_len.to(dev)
     o = torch.empty(N, Ts, H, D, dtype=torch.bfloat16, device=dev)
-    for i in range(10):
+    for i in range(warm):
         s = slot_sets[i % P]
         K.kda_verify(q, k, v, g, b, pool, s, s, o=o, accepted_len=L)
     a_, b2 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     a_.record()
-    n = 200
     for i in range(n):
         s = slot_sets[i % P]
         K.kda_verify(q, k, v, g, b, pool, s, s, o=o, accepted_len=L)
@@ -559,7 +575,7 @@ def bench_verify_secondary(torch, K, make_workload, dev):
     cw = cw.to(dev)
     cpool = cst.to(dev)
     cs = torch.arange(N, dtype=torch.int32, device=dev)
-    for i in range(10):
+    for i in range(warm):
         s = slot_sets[i % P]
         K.kda_verify_conv(x, cw, cpool, cs, cs, g, b, pool, s, s, o=o, accepted_len=L, act=1)
     torch.cuda.synchronize()
