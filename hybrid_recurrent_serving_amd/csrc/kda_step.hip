@@ -62,11 +62,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* base,
 }
 
 // 16 bytes of a state slice through a buffer resource (non-temporal; dropped
-// when the resource has size 0)
-__device__ __forceinline__ void st4_rsrc(__amdgpu_buffer_rsrc_t r, int voff, int soff, const float (&x)[4]) {
+// when the resource has size 0).  The whole offset goes in the vector
+// offset and the scalar offset is the constant 0: with a scalar register
+// there, the compiler inserts no wait before a vector write to the store's
+// data registers, and measured stores then took some lanes' first dword
+// from the next value written to that register.
+__device__ __forceinline__ void st4_rsrc(__amdgpu_buffer_rsrc_t r, int voff, int off, const float (&x)[4]) {
   typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
   const u32x4 v = {__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3])};
-  __builtin_amdgcn_raw_buffer_store_b128(v, r, voff, soff, kBufNonTemporal);
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, voff + off, 0, kBufNonTemporal);
 }
 
 
