@@ -1,0 +1,85 @@
+"""Host logic of the benchmark's counter ingestion (no GPU): per-call grouping
+of prefill dispatches by their segment-plan launch, the active-cycle
+weighting of MfmaUtil / VALUBusy, the GEMM calibration and the copy
+calibration of FETCH_SIZE / WRITE_SIZE, on synthetic rocprofv3 CSV rows."""
+import csv
+
+import pytest
+
+import bench
+
+PLAN = "kda::pf::segment_plan_kernel(kda::PrefillParams, int*, int*)"
+PF = "void kda::pf::prefill_kernel<128, unsigned short, unsigned short>(kda::PrefillParams, int, int)"
+COMB = "kda::pf::segment_combine_kernel(kda::PrefillParams, int)"
+VER = "void kda::step_kernel<128, unsigned short, unsigned short, true>(kda::StepParams)"
+COPY = "__amd_rocclr_copyBuffer"
+
+
+@pytest.fixture
+def tokens(monkeypatch):
+    monkeypatch.setattr(bench, "varlen_tokens", lambda: 1000)
+    return 1000
+
+
+def _write(path, rows):
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        w.writerows(rows)
+
+
+def test_ingest_mfma_groups_and_weights(tmp_path, tokens):
+    rows, did = [], [0]
+
+    def add(name, util, valu, mops, grbm):
+        did[0] += 1
+        for c, v in (("MfmaUtil", util), ("VALUBusy", valu), ("SQ_INSTS_VALU_MFMA_MOPS_BF16", mops),
+                     ("GRBM_GUI_ACTIVE", grbm)):
+            rows.append({"Dispatch_Id": did[0], "Kernel_Name": name, "Counter_Name": c, "Counter_Value": v})
+
+    add(COPY, 0, 1, 0, 100)
+    add("Cijk_gemm", 70, 20, 2 * bench.GEMM_N ** 3 / 512, 1000)
+    add(VER, 0, 60, 0, 300)
+    add(VER, 0, 40, 0, 100)
+    for call in range(bench.PMC_PREFILL_CALLS + bench.PMC_LONG_CALLS):
+        add(PLAN, 0, 5, 0, 10)
+        add(PF, 20, 40, 1000 * (call + 1), 300)   # pass A
+        add(COMB, 0, 2, 0, 10)
+        add(PF, 10, 30, 100, 100)                 # fix-up
+    path = tmp_path / "mfma.csv"
+    _write(path, rows)
+    out = bench.ingest_mfma([str(path)])
+    assert out["calibration_gemm"]["executed_flops"] == 2 * bench.GEMM_N ** 3
+    v = out["verify_kernel_d128_bf16"]
+    assert v["dispatches"] == 2 and v["valu_busy"] == pytest.approx((60 * 300 + 40 * 100) / 400 / 100)
+    pv = out["prefill_varlen"]
+    last = bench.PMC_PREFILL_CALLS   # the measured varlen call is the last of its group
+    assert pv["tokens"] == tokens and pv["dispatches"] == 3
+    assert pv["executed_bf16_flops"] == (1000 * last + 100) * 512
+    assert pv["mfma_util"] == pytest.approx((20 * 300 + 0 * 10 + 10 * 100) / 410 / 100, abs=1e-4)
+    assert [d["role"] for d in pv["per_dispatch"]] == ["pass A", "combine", "fix-up"]
+    pl = out["prefill_long_1m"]
+    assert pl["executed_bf16_flops"] == (1000 * (last + bench.PMC_LONG_CALLS) + 100) * 512
+
+
+def test_ingest_pmc_calibrates_and_splits_calls(tmp_path, tokens):
+    def rows_for(counter, copy_val, pf_val):
+        rows, did = [], 0
+        for name, val in [(COPY, copy_val)] + [(x, y) for _ in range(bench.PMC_PREFILL_CALLS + bench.PMC_LONG_CALLS)
+                                               for x, y in ((PLAN, 1.0), (PF, pf_val), (COMB, 1.0), (PF, pf_val))]:
+            did += 1
+            rows.append({"Dispatch_Id": did, "Kernel_Name": name, "Counter_Name": counter, "Counter_Value": val})
+        return rows
+
+    kib = bench.COPY_BYTES / 1024
+    fp, wp = tmp_path / "f.csv", tmp_path / "w.csv"
+    _write(fp, rows_for("FETCH_SIZE", kib / 2, 10.0))   # fetch reads half the copy: scale 2
+    _write(wp, rows_for("WRITE_SIZE", kib, 4.0))
+    out = bench.ingest_pmc(str(fp), str(wp))
+    assert out["calibration"]["fetch_scale"] == pytest.approx(2.0)
+    assert out["calibration"]["write_scale"] == pytest.approx(1.0)
+    for key, units in (("prefill_kernel_d128_bf16", tokens), ("prefill_long_kernel_d128_bf16", 1 << 20)):
+        e = out[key]
+        assert e["units_per_launch"] == units
+        assert e["fetch_bytes"] == round(2 * 10.0 * 1024 * 2)   # two dispatches per call, scaled x 2
+        assert e["write_bytes"] == round(2 * 4.0 * 1024)
