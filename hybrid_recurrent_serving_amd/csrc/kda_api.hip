@@ -2,6 +2,7 @@
 // KDA_CHECK=1 validation of device index arrays, and dispatch to the kernel
 // launchers.  No allocation, no synchronisation (outside KDA_CHECK=1).
 
+#include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -97,6 +98,63 @@ static int check_cu(const int32_t* cu, int n_seq, int64_t T_tot, hipStream_t str
     if (h[i + 1] < h[i]) return fail(KDA_ERR_ARG, "cu_seqlens decreases at %d", i);
   if (h[n_seq] > T_tot) return fail(KDA_ERR_ARG, "cu_seqlens[n_seq] = %d > T_tot", h[n_seq]);
   if (out) *out = h;
+  return KDA_OK;
+}
+
+// KDA_CHECK=1: the decay range the chunked prefill is exact for.  Inside a
+// tile of `tile` tokens at absolute multiples of `tile`, the chunked form
+// scales rows by exp(+-(G_r - G_15)), G the cumulative log decay of the tile
+// (rows outside the sequence contribute 0); every such exponent must stay
+// within +-kGateLimit nats so that no factor leaves the fp32 range.
+constexpr double kGateLimit = 80.0;
+
+static int check_gate_range(const void* g, int dtype, int64_t g_stride, const std::vector<int32_t>& cu,
+                            const int32_t* start_pos, int n_seq, int H, int d, int tile, int64_t T_tot,
+                            hipStream_t stream) {
+  std::vector<int32_t> sp;
+  if (start_pos && !copy_to_host(sp, start_pos, (size_t)n_seq, stream))
+    return fail(KDA_ERR_HIP, "KDA_CHECK: copying start_pos failed");
+  const int64_t rows = T_tot;
+  const size_t elems = (size_t)(rows > 0 ? (rows - 1) * g_stride + (int64_t)H * d : 0);
+  std::vector<uint16_t> g16;
+  std::vector<float> g32;
+  if (dtype == KDA_BF16) {
+    if (!copy_to_host(g16, static_cast<const uint16_t*>(g), elems, stream))
+      return fail(KDA_ERR_HIP, "KDA_CHECK: copying g failed");
+  } else if (!copy_to_host(g32, static_cast<const float*>(g), elems, stream)) {
+    return fail(KDA_ERR_HIP, "KDA_CHECK: copying g failed");
+  }
+  auto at = [&](int64_t i) -> double {
+    if (dtype == KDA_BF16) {
+      const uint32_t u = static_cast<uint32_t>(g16[i]) << 16;
+      float f;
+      memcpy(&f, &u, 4);
+      return f;
+    }
+    return g32[i];
+  };
+  std::vector<double> cum(tile);
+  for (int s = 0; s < n_seq; ++s) {
+    const int64_t bos = cu[s], len = (int64_t)cu[s + 1] - cu[s];
+    if (len <= 0) continue;
+    const int64_t start = sp.empty() ? 0 : (sp[s] > 0 ? sp[s] : 0);
+    for (int64_t t0 = (start / tile) * tile; t0 < start + len; t0 += tile)
+      for (int h = 0; h < H; ++h)
+        for (int c = 0; c < d; ++c) {
+          double acc = 0.0;
+          for (int r = 0; r < tile; ++r) {
+            const int64_t pos = t0 + r;
+            if (pos >= start && pos < start + len) acc += at((bos + pos - start) * g_stride + (int64_t)h * d + c);
+            cum[r] = acc;
+          }
+          for (int r = 0; r < tile; ++r)
+            if (fabs(cum[r] - cum[15]) > kGateLimit)
+              return fail(KDA_ERR_ARG,
+                          "g out of range: sequence %d head %d channel %d, tile at position %lld sums to "
+                          "%.1f over rows %d..15 (limit %.0f)",
+                          s, h, c, (long long)t0, cum[r] - cum[15], r, kGateLimit);
+        }
+  }
   return KDA_OK;
 }
 
@@ -474,6 +532,9 @@ int kda_prefill_varlen(const kda_prefill_args* a, kda_stream_t stream_) {
         if (c < -1 || c >= b.n_slots) return fail(KDA_ERR_ARG, "ckpt_slot %d out of range", c);
     }
     st = check_slots(b.src_slot, b.dst_slot, b.n_seq, b.n_slots, &ck, stream);
+    if (st) return st;
+    st = check_gate_range(b.g, b.in_dtype, b.g_stride, hcu, b.start_pos, b.n_seq, b.H, b.d_k,
+                          b.chunk == 16 ? 16 : 32, b.T_tot, stream);
     if (st) return st;
   }
   return launch_prefill(p, b.d_k, b.in_dtype, b.out_dtype, stream);

@@ -418,7 +418,11 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
       }
     }
   }
-  const bool has_dst = dst >= 0 && dst < p.n_slots && last_seg && outputs && full_run;
+  // The final state of a split sequence is written by the fix-up launch only:
+  // pass A also runs the first segment, which reads src_slot when it starts,
+  // so a pass-A write of dst_slot would race with it when src == dst.
+  const bool dst_ok = dst >= 0 && dst < p.n_slots;
+  const bool has_dst = dst_ok && last_seg && outputs && full_run && (mode != kModeLocal || nseg == 1);
   auto ws_block = [&](int kind) -> float* {
     return p.ws_states + (blk * 3 + kind) * H * d * d + static_cast<int64_t>(h) * d * d;
   };
@@ -1173,8 +1177,17 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
   // ---- final state: the destination slot, or a segment-scan block
   if (chain && ncol < d) {
     if (has_dst) state_store<D>(p.pool + (static_cast<int64_t>(dst) * H + h) * d * d, S, lane, ncol, d);
-    if (mode == kModeLocal && has_blk && !last_seg) state_store<D>(ws_block(1), S, lane, ncol, d);
+    // every split segment keeps its local end state (the last one's is the
+    // final state when its fix-up stops early)
+    if (mode == kModeLocal && has_blk) state_store<D>(ws_block(1), S, lane, ncol, d);
     if (mode == kModeTransition && has_blk) state_store<D>(ws_block(2), S, lane, ncol, d);
+    // fix-up of the last segment cut short: past the point where its
+    // transition became exactly zero the local chain of pass A is the state,
+    // so its end state is the final state
+    if (mode == kModeFixup && last_seg && !full_run && dst_ok && has_blk) {
+      state_load<D>(ws_block(1), S, lane, ncol, d);
+      state_store<D>(p.pool + (static_cast<int64_t>(dst) * H + h) * d * d, S, lane, ncol, d);
+    }
   }
   if (mode == kModeTransition && has_blk && p.ws_zero && threadIdx.x == 0) p.ws_zero[blk * H + h] = zero_after;
 }

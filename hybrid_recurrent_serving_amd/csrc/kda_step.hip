@@ -300,7 +300,13 @@ static int launch_step_t(const StepParams& p, hipStream_t stream) {
   dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(p.n_seq) * p.H));
   dim3 block(64 * L::WPH);
   if (p.T_spec == 1) {
-    if constexpr (D == 128) return launch_decode128_plain<Tin, Tout>(p, stream);
+    // The streaming layout serves the plain decode step only (outputs, store
+    // after the token); a one-token verify keeps its commit semantics
+    // (accepted length 0 / rejected, commit index, commit-only calls without
+    // outputs) in the general step kernel.
+    if constexpr (D == 128) {
+      if (p.commit_all && p.o) return launch_decode128_plain<Tin, Tout>(p, stream);
+    }
     hipLaunchKernelGGL((step_kernel<D, Tin, Tout, false>), grid, block, 0, stream, p);
   } else {
     const size_t lds = (5 * static_cast<size_t>(p.T_spec) * D + 64 * L::WPH) * sizeof(float);

@@ -238,6 +238,20 @@ int kda_ckpt_plan_device(const kda_plan_args *args, kda_stream_t stream);
  * for the same args (0 when T_tot <= segment_len, since nothing can be
  * split then).  segment_len: 0 = the library default (32768), < 0 = never
  * split, > 0 = that length, a multiple of chunk (else KDA_ERR_ALIGN).
+ *
+ * In place: src_slot[s] == dst_slot[s] is allowed, also for split
+ * sequences (the final state is written only after every segment has read
+ * its starting state).
+ *
+ * Decay range (precondition).  The chunked form scales the rows of a tile
+ * (32 tokens at absolute multiples of 32; 16 when chunk == 16) by
+ * exp(+-(G_r - G_15)), G being the running sum of g over the tile's rows.
+ * Results are exact to the stated tolerance while every such exponent stays
+ * within +-80 (nats) for every key channel -- e.g. whenever each g lies in
+ * [-5, 0], or isolated tokens reach far lower (a single -20 is fine).
+ * Beyond it a factor leaves the fp32 range and outputs and states may be
+ * non-finite.  Checked under KDA_CHECK=1 (KDA_ERR_ARG naming the sequence,
+ * head, channel and tile).
  * ---------------------------------------------------------------------- */
 typedef struct kda_prefill_args {
     size_t struct_size;          /* sizeof(kda_prefill_args) */

@@ -306,11 +306,4 @@ def load_mutant(mutant: int, outdir: Path, real: str = "f64") -> Oracle:
     return Oracle(path)
 
 
-def bf16_round(x: np.ndarray) -> np.ndarray:
-    """Round float64 values to bfloat16 (round to nearest even), returned as
-    float64 -- used to express comparisons in the kernel's output precision."""
-    import torch
-    return torch.from_numpy(np.asarray(x, np.float64)).to(torch.bfloat16).to(torch.float64).numpy()
-
-
-__all__ = ["Oracle", "load", "load_mutant", "build", "bf16_round"]
+__all__ = ["Oracle", "load", "load_mutant", "build"]

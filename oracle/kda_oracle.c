@@ -7,14 +7,15 @@
  * fallback for it.
  *
  * What it computes (Kimi Delta Attention, per sequence and per head, token by
- * token).  The pages describe KDA as a linear-attention layer that keeps a
- * fixed-size matrix-like recurrent state per layer together with a short
- * causal-convolution state ("Kimi K3 + vLLM: Inside the Day-0 Production
- * Integration", section "Kimi Delta Attention: When Prefix Caching Meets
- * Recurrent State"; "Kimi K3 on vLLM: Up to 370 Tokens/sec", section "Kimi
- * Delta Attention: a hybrid recurrent + full-attention stack").  They print
- * no equation; the oracle takes the gated delta rule with per-key-channel
- * decay as the plainest reading:
+ * token).  Per head, a KDA layer carries a matrix of fixed size that every
+ * token updates, and beside it the recent inputs of a short causal
+ * convolution; caching a prefix means keeping both ("Kimi K3 + vLLM: Inside
+ * the Day-0 Production Integration", section "Kimi Delta Attention: When
+ * Prefix Caching Meets Recurrent State"; "Kimi K3 on vLLM: Up to 370
+ * Tokens/sec", section "Kimi Delta Attention: a hybrid recurrent +
+ * full-attention stack").  The pages give no equation for the update; the
+ * oracle takes the gated delta rule with per-key-channel decay as the
+ * plainest reading:
  *
  *     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T
  *     o_t = scale * S_t^T q_t,            alpha_t = exp(g_t)

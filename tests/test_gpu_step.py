@@ -367,3 +367,34 @@ def test_decode_d128_item_count_not_multiple_of_8(dev, oracle64):
     K.kda_decode(q.to(dev), k.to(dev), v.to(dev), g.to(dev), b.to(dev), o2, pool2, src, src, scale=0.7)
     torch.cuda.synchronize()
     assert torch.equal(o2, o) and torch.equal(pool2, pool[5:])
+
+
+@pytest.mark.parametrize("with_o", [True, False])
+def test_verify_one_token_d128(dev, oracle64, with_o):
+    """A one-token verify at d = 128 keeps the verify semantics: L = 1 commits
+    the state after the token, L = 0 commits the source state, L = -1 / 2 are
+    rejected (committed length -1, destination untouched), and a commit-only
+    call (o = NULL) writes no outputs."""
+    U.say(f"verify T_spec=1 d=128 with_o={with_o}")
+    wl = make_workload(4, n_seq=8, H=4)
+    q, k, v, g, b = (t[:, :1].contiguous() for t in (wl.q, wl.k, wl.v, wl.g, wl.beta))
+    L = torch.tensor([1, 0, -1, 2, 1, 0, 1, -1], dtype=torch.int32)
+    ref = oracle64.kda_verify(q, k, v, g, b, wl.init_states, L)
+    pool = torch.cat([wl.init_states, torch.full_like(wl.init_states, 7.0)]).to(dev)
+    src = torch.arange(8, dtype=torch.int32, device=dev)
+    clen = torch.full((8,), -7, dtype=torch.int32, device=dev)
+    o = torch.full((8, 1, 4, 128), float("nan"), device=dev) if with_o else None
+    K.kda_verify(*(t.to(dev) for t in (q, k, v, g, b)), pool, src, src + 8, o=o,
+                 accepted_len=L.to(dev), committed_len_out=clen)
+    torch.cuda.synchronize()
+    assert clen.cpu().tolist() == [1, 0, -1, -1, 1, 0, 1, -1]
+    assert torch.equal(pool[:8].cpu(), wl.init_states), "source states modified"
+    for s in range(8):
+        if L[s] in (-1, 2):
+            assert torch.all(pool[8 + s] == 7.0), f"rejected sequence {s} wrote its destination"
+        elif L[s] == 0:
+            assert torch.equal(pool[8 + s].cpu(), wl.init_states[s])
+        else:
+            U.assert_close(f"committed[{s}]", U.to_np(pool[8 + s]), ref["committed"][s], rel=1e-5, mx=1e-4)
+    if with_o:
+        U.assert_close("o", U.to_np(o), ref["o"], rel=1e-5, mx=1e-4)
