@@ -278,6 +278,7 @@ struct Smem {
   alignas(16) float eg_m[2][D];           // exp(G_m), by chunk parity
   alignas(16) float eg_e[2][D];           // exp(G_last - G_m), by chunk parity
   alignas(16) float eg_c[2][D];           // exp(G_last - G_m) of the chunk before times exp(G_m)
+  uint32_t eg_split[2][GATE_WAVES];       // that product is below the normal fp32 range somewhere
   alignas(16) float G[TILE][D];           // cumulative gates (log2 units) of the next chunk
   float beta[2][TILE];                    // by chunk parity
   bf16_t Tb[TILE][PT];                    // T = (I + A)^{-1} diag(beta) [r][s], block (1,0) zero
@@ -614,13 +615,21 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
     // G at the reference row and at the last row, from the lanes that hold them
     const float gm = __shfl(gl[MID % RP] + off, (MID / RP) * CPW + lane % CPW, 64);
     const float ge = __shfl(gl[RP - 1] + off, (NPART - 1) * CPW + lane % CPW, 64);
+    bool tiny = false;
     if (part == 0) {
       const float em = __builtin_amdgcn_exp2f(gm);
       sm.eg_m[par][c] = em;
       sm.eg_e[par][c] = __builtin_amdgcn_exp2f(ge - gm);
       // this lane wrote eg_e of the chunk before (same channel)
-      sm.eg_c[par][c] = sm.eg_e[par ^ 1][c] * em;
+      const float ec = sm.eg_e[par ^ 1][c] * em;
+      sm.eg_c[par][c] = ec;
+      // two factors of up to 16 tokens of decay each can multiply to below
+      // the normal range while each alone and the scaled state stay in it;
+      // the chain then applies them one after the other
+      tiny = !(ec >= 1.17549435e-38f);
     }
+    const uint64_t tb = __ballot(tiny);
+    if (lane == 0) sm.eg_split[par][gw] = tb != 0 ? 1u : 0u;
   };
 
   const int64_t first = hi > lo ? (lo / CH) * CH : hi;
@@ -877,7 +886,15 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
       // S = Diag(exp(G_last - G_m)) (S' + right_k^T u) is the state after
       // chunk n; it enters chunk b as Diag(exp G_m(b)) S, both factors in one
       // product unless the state after n is stored
-      const float* fs = (MORE && ck < 0) ? sm.eg_c[lp] : sm.eg_e[cp];
+      bool split = false;
+      if constexpr (MORE) {
+        uint32_t sp = 0;
+#pragma unroll
+        for (int gw = 0; gw < GATE_WAVES; ++gw) sp |= sm.eg_split[lp][gw];
+        split = __builtin_amdgcn_readfirstlane(sp) != 0u;
+      }
+      const bool combined = MORE && ck < 0 && !split;
+      const float* fs = combined ? sm.eg_c[lp] : sm.eg_e[cp];
       auto scale_tile = [&](const int q) __attribute__((always_inline)) {
         const float4 x = *reinterpret_cast<const float4*>(&fs[16 * q + 4 * g4]);
         S[q][0] *= x.x; S[q][1] *= x.y; S[q][2] *= x.z; S[q][3] *= x.w;
@@ -928,7 +945,9 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
         const int slot = p.ckpt_slot[ck];
         if (slot >= 0 && slot < p.n_slots && ncol < d)
           state_store<D>(p.pool + (static_cast<int64_t>(slot) * H + h) * d * d, S, lane, ncol, d);
-        if constexpr (MORE) scale_state(sm.eg_m[lp], g4);
+      }
+      if constexpr (MORE) {
+        if (!combined) scale_state(sm.eg_m[lp], g4);
       }
     }
     if (CHAIN && ck >= 0 && tid == 0 && h == 0 && p.ckpt_pos_out) p.ckpt_pos_out[ck] = static_cast<int32_t>(n + CH);
