@@ -8,6 +8,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
 #include <vector>
 
 #include "kda_internal.h"
@@ -536,6 +537,71 @@ int kda_prefill_varlen(const kda_prefill_args* a, kda_stream_t stream_) {
     st = check_gate_range(b.g, b.in_dtype, b.g_stride, hcu, b.start_pos, b.n_seq, b.H, b.d_k,
                           b.chunk == 16 ? 16 : 32, b.T_tot, stream);
     if (st) return st;
+  }
+  return launch_prefill(p, b.d_k, b.in_dtype, b.out_dtype, stream);
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------------ prefill without allocation
+// The segment-scan workspace of kda_prefill_varlen_noalloc lives in this
+// static device array: the code object carries it, so each GPU the library
+// runs on holds one copy (kScratchBytes) until the process ends.  Host code
+// must use its device address, looked up once per device; the array's name
+// itself is a host-side stand-in.
+namespace kda {
+constexpr int64_t kScratchBytes = int64_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on the current device (looked up on the first
+// call per device, with that device current).
+static int scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(KDA_ERR_UNSUPPORTED, "device %d (at most %d devices)", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(KDA_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return KDA_OK;
+}
+}  // namespace kda
+
+extern "C" {
+
+int64_t kda_prefill_noalloc_max_bytes(void) { return kScratchBytes; }
+
+int kda_prefill_varlen_noalloc(const kda_prefill_args* a, kda_stream_t stream_) {
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  kda_prefill_args b;
+  int st = prefill_validate(a, b);
+  if (st) return st;
+  if (b.workspace || b.workspace_bytes)
+    return fail(KDA_ERR_ARG, "prefill_noalloc: workspace must be NULL and workspace_bytes 0 (the library's scratch is used)");
+  if (b.n_seq == 0) return KDA_OK;
+  PrefillParams p = prefill_params(b);
+  const int64_t need = prefill_workspace_bytes(p, b.d_k);
+  if (need > kScratchBytes)
+    return fail(KDA_ERR_WORKSPACE,
+                "prefill_noalloc: the segment scan of this call needs %lld bytes of scratch, more than the %lld "
+                "the library holds; use kda_prefill_varlen with a workspace, or a longer segment_len",
+                (long long)need, (long long)kScratchBytes);
+  if (need > 0) {
+    void* ws = nullptr;
+    st = scratch_address(&ws);
+    if (st) return st;
+    p.workspace = ws;
+    p.workspace_bytes = kScratchBytes;
   }
   return launch_prefill(p, b.d_k, b.in_dtype, b.out_dtype, stream);
 }

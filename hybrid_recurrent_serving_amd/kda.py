@@ -128,7 +128,8 @@ class VerifyArgs(ctypes.Structure):
 
 EXPORTS = ["kda_status_str", "kda_abi_version", "kda_last_error", "kda_args_sizeof",
            "kda_conv_short", "kda_ckpt_plan", "kda_ckpt_plan_device", "kda_prefill_workspace_bytes",
-           "kda_prefill_varlen", "kda_decode", "kda_verify", "kda_decode_conv", "kda_verify_conv"]
+           "kda_prefill_varlen", "kda_decode", "kda_verify", "kda_decode_conv", "kda_verify_conv",
+           "kda_prefill_varlen_noalloc", "kda_prefill_noalloc_max_bytes"]
 
 _lib = None
 
@@ -159,12 +160,15 @@ def load_library(path: Optional[Path] = None):
     lib.kda_prefill_workspace_bytes.restype = c_i64
     lib.kda_prefill_workspace_bytes.argtypes = [ctypes.POINTER(PrefillArgs)]
     lib.kda_prefill_varlen.argtypes = [ctypes.POINTER(PrefillArgs), c_vp]
+    lib.kda_prefill_varlen_noalloc.argtypes = [ctypes.POINTER(PrefillArgs), c_vp]
+    lib.kda_prefill_noalloc_max_bytes.restype = c_i64
+    lib.kda_prefill_noalloc_max_bytes.argtypes = []
     lib.kda_decode.argtypes = [ctypes.POINTER(DecodeArgs), c_vp]
     lib.kda_verify.argtypes = [ctypes.POINTER(VerifyArgs), c_vp]
     lib.kda_decode_conv.argtypes = [ctypes.POINTER(DecodeConvArgs), c_vp]
     lib.kda_verify_conv.argtypes = [ctypes.POINTER(VerifyConvArgs), c_vp]
     for name in ("kda_conv_short", "kda_ckpt_plan", "kda_ckpt_plan_device", "kda_prefill_varlen", "kda_decode", "kda_verify",
-                 "kda_decode_conv", "kda_verify_conv"):
+                 "kda_decode_conv", "kda_verify_conv", "kda_prefill_varlen_noalloc"):
         getattr(lib, name).restype = ctypes.c_int
     if path is None:
         _lib = lib
@@ -459,6 +463,22 @@ def kda_prefill_varlen(q, k, v, g, beta, o, cu_seqlens, state_pool, src_slot, ds
             a.workspace, a.workspace_bytes = _ptr(workspace), need
     _check(lib.kda_prefill_varlen(ctypes.byref(a), _stream(stream)))
     return o
+
+
+def kda_prefill_varlen_noalloc(q, k, v, g, beta, o, cu_seqlens, state_pool, src_slot, dst_slot, *,
+                               chunk=64, start_pos=None, ckpt_interval=0, ckpt_cu=None, ckpt_slot=None,
+                               ckpt_pos_out=None, scale=1.0, segment_len=0, stream=None):
+    """kda_prefill_varlen without a workspace: the library's own scratch array
+    serves the segment scan, and nothing is allocated (see include/kda.h)."""
+    a = _prefill_args(q, k, v, g, beta, o, cu_seqlens, state_pool, src_slot, dst_slot, chunk,
+                      start_pos, ckpt_interval, ckpt_cu, ckpt_slot, ckpt_pos_out, None, scale,
+                      segment_len)
+    _check(load_library().kda_prefill_varlen_noalloc(ctypes.byref(a), _stream(stream)))
+    return o
+
+
+def kda_prefill_noalloc_max_bytes() -> int:
+    return int(load_library().kda_prefill_noalloc_max_bytes())
 
 
 def _decode_args(q, k, v, g, beta, o, state_pool, src_slot, dst_slot, scale):

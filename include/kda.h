@@ -289,6 +289,32 @@ int64_t kda_prefill_workspace_bytes(const kda_prefill_args *args);
 int kda_prefill_varlen(const kda_prefill_args *args, kda_stream_t stream);
 
 /* ------------------------------------------------------------------------
+ * kda_prefill_varlen_noalloc -- kda_prefill_varlen for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).
+ *
+ * Same arguments, results and errors as kda_prefill_varlen, except:
+ * - `workspace` must be NULL and `workspace_bytes` 0 (else KDA_ERR_ARG):
+ *   the segment scan uses a scratch array of kda_prefill_noalloc_max_bytes()
+ *   bytes (64 MiB) that the library holds on every GPU it runs on until the
+ *   process ends.  A call whose split needs more (kda_prefill_workspace_bytes
+ *   of the same args) returns KDA_ERR_WORKSPACE and launches nothing; calls
+ *   that split nothing (T_tot <= segment_len, or segment_len < 0) need none.
+ *   At H = 16, d = 128 the limit admits T_tot up to about 6.6 segment
+ *   lengths.
+ * - Nothing in the scratch has to start at zero; every call on a GPU shares
+ *   that GPU's array and leaves its own contents in it, so calls that
+ *   overlap on one GPU (different streams, or host threads) race and must
+ *   be ordered by the caller.
+ * - The stream must belong to the current device (the scratch address is
+ *   the current device's).
+ * - No KDA_CHECK=1 validation (it would allocate host buffers).
+ * ---------------------------------------------------------------------- */
+int kda_prefill_varlen_noalloc(const kda_prefill_args *args, kda_stream_t stream);
+/* Bytes of the scratch array kda_prefill_varlen_noalloc uses (host-only). */
+int64_t kda_prefill_noalloc_max_bytes(void);
+
+/* ------------------------------------------------------------------------
  * kda_decode -- one token per sequence, state updated in place.
  *
  * The decode step of the KDA layer (Day-0 Integration page, section
