@@ -3,18 +3,25 @@
 
 Default workload: batched decode (128 sequences x 1 token, H=16,
 d_k=d_v=128, bf16 inputs, fp32 recurrent state, short conv W=4 over the
-3*H*d q/k/v channels).  One step = kda_conv_short on the step's 128 token
-rows (carried conv state updated in place) + kda_decode (recurrent state
-updated in place).  The recurrent state rotates over 4 pools of 128 MiB so
-it cannot be served from the 256 MB Infinity Cache.
+3*H*d q/k/v channels).  One step = one kda_decode_conv launch: the conv
+(+ SiLU) of the token's q/k/v projections with the carried conv history,
+per-head q/k L2 normalisation and the recurrence, both states advanced in
+place.  The recurrent state rotates over 4 pools of 128 MiB so it cannot be
+served from the 256 MB Infinity Cache.
 
 Prints ONE JSON line.  ``value`` = recurrent-state bytes read + written per
-step / step time (GB/s).  ``roofline`` = the decode kernel's algorithmic
-bytes per launch / its average launch time (HIP events around each launch in
-the timed region) against 8 TB/s.  ``cpu_baseline`` = the CPU oracle on the
-same workload (a bounded number of whole steps), timed on the host cores.
+step / step time (GB/s).  ``roofline`` = the fused kernel's algorithmic
+bytes per launch / its average launch time (HIP events on the launch stream
+over the timed region) against 8 TB/s.  ``cpu_baseline`` = the CPU oracle on
+the same workload (a bounded number of whole steps), timed on the host cores.
 
-Other workloads (``--workload verify|prefill|long``) print the same format.
+``secondary`` carries the other rows of the metric, each with its own
+``roofline`` and ``cpu_baseline``: speculative verify (128 x 8 tokens), the
+16-sequence varlen prefill, the 1M-token prefill (oracle resumed from the
+GPU's checkpoints on a sample of segments, plus a continuous 65,536-token
+run), the short conv at prefill scale, and the device checkpoint planner.
+
+``--workload prefill|long`` makes a prefill workload the main line.
 """
 
 from __future__ import annotations
@@ -46,6 +53,8 @@ def parse():
     ap.add_argument("--pools", type=int, default=4, help="rotating state pools (MALL defeat)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU oracle time budget")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--long-cpu-segments", type=int, default=32,
+                    help="segments of the 1M-token workload the oracle resumes (of 32)")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="run only the launches a rocprofv3 --pmc pass measures: a 256 MiB copy "
@@ -456,15 +465,16 @@ def bench_decode(args, torch, K, make_workload):
         secondary["copy_same_bytes"] = {"us": round(cp_us, 2),
                                         "GB_s": round(state_bytes / cp_us / 1e3, 1)}
         del srcs, dsts, src_t, dst_t
-        secondary["verify"] = bench_verify_secondary(torch, K, make_workload, dev)
+        cs = 0.0 if args.no_cpu else args.cpu_seconds
+        secondary["verify"] = bench_verify_secondary(torch, K, make_workload, dev, cpu_seconds=min(cs, 4.0))
         secondary["ckpt_plan_device"] = bench_planner_secondary(torch, K, dev)
-        pf = bench_prefill_varlen(torch, K, make_workload, dev, iters=10)
-        secondary["prefill_varlen"] = {k_: pf[k_] for k_ in ("workload", "tokens", "ms", "tokens_per_s",
-                                                             "alg_mfma_frac", "alg_hbm_frac")}
-        secondary["prefill_varlen"]["mfma_counters"] = mfma_counters("prefill_varlen", pf["tokens"], pf["ms"])
-        lp = bench_prefill_long(torch, K, make_workload, dev)
-        lp["mfma_counters"] = mfma_counters("prefill_long_1m", lp["tokens"], lp["ms"])
-        secondary["prefill_long_1m"] = lp
+        wl2 = make_workload(2)
+        secondary["prefill_varlen"] = bench_prefill_varlen(torch, K, make_workload, dev, iters=10, wl=wl2,
+                                                           cpu_seconds=cs)
+        secondary["conv_prefill_scale"] = bench_conv_prefill(torch, K, wl2, dev)
+        del wl2
+        secondary["prefill_long_1m"] = bench_prefill_long(
+            torch, K, make_workload, dev, cpu_segments=0 if args.no_cpu else args.long_cpu_segments)
 
     cpu = None
     if not args.no_cpu:
@@ -534,7 +544,7 @@ def bench_planner_secondary(torch, K, dev, iters=200):
     return out
 
 
-def bench_verify_secondary(torch, K, make_workload, dev, n=200, warm=10):
+def bench_verify_secondary(torch, K, make_workload, dev, n=200, warm=10, cpu_seconds=0.0):
     """Speculative verify (128 x 8 tokens, fused commit) -- reported beside the
     decode line.  n timed calls of each form after warm untimed ones."""
     wl = make_workload(4)
@@ -561,10 +571,18 @@ def bench_verify_secondary(torch, K, make_workload, dev, n=200, warm=10):
     us = a_.elapsed_time(b2) / n * 1e3
     state_bytes = N * H * D * D * 4 * 2
     io = N * Ts * H * (4 * D * 2 + 2 + D * 2)
+    alg = state_bytes + io
     res = {"workload": "verify 128 x 8 tokens, fused commit at L~U{1..8}", "us": round(us, 2),
            "state_GB_s": round(state_bytes / us / 1e3, 1),
-           "alg_GB_s": round((state_bytes + io) / us / 1e3, 1),
-           "hbm_frac": round((state_bytes + io) / us / 1e3 / HBM_PEAK_GBS, 4)}
+           "alg_GB_s": round(alg / us / 1e3, 1),
+           "hbm_frac": round(alg / us / 1e3 / HBM_PEAK_GBS, 4),
+           "roofline": {"kernel": "step_kernel<128,bf16,bf16,staged> (kda_verify, one launch per call)",
+                        "bound": "hbm", "achieved": round(alg / us / 1e3, 1), "peak": HBM_PEAK_GBS,
+                        "unit": "GB/s", "frac": round(alg / us / 1e3 / HBM_PEAK_GBS, 4),
+                        "traffic": traffic_for("verify_step_kernel_d128_bf16", "kda_step.hip", N * H),
+                        "alg_bytes_per_launch": alg, "avg_launch_us": round(us, 3)}}
+    if cpu_seconds > 0:
+        res["cpu_baseline"] = cpu_verify(wl, state_bytes, cpu_seconds)
     # the same verify from the tokens' raw q/k/v projections with the conv
     # (+ SiLU), q/k normalisation and both commits fused (kda_verify_conv)
     from hybrid_recurrent_serving_amd.inputs import draw_conv
@@ -605,7 +623,7 @@ PREFILL_FLOPS_PER_TOKEN = 16 * (10 * 64 * 128 + 6 * 128 * 128)    # dense chunke
 VARLEN_SEGMENT = 4096
 
 
-def bench_prefill_varlen(torch, K, make_workload, dev, iters=20, wl=None):
+def bench_prefill_varlen(torch, K, make_workload, dev, iters=20, wl=None, cpu_seconds=0.0):
     """16 packed sequences, lengths U{512..16384}, H=16, d=128, chunk 64,
     even sequences from random initial states, final states to fresh slots."""
     if wl is None:
@@ -641,17 +659,78 @@ def bench_prefill_varlen(torch, K, make_workload, dev, iters=20, wl=None):
     torch.cuda.synchronize()
     ms = sum(a.elapsed_time(b_) for a, b_ in evs) / iters
     tps = T / (ms * 1e-3)
-    return {"workload": "varlen prefill: 16 seqs, lengths U{512..16384}, H=16, d=128, chunk 64, bf16",
-            "tokens": T, "ms": round(ms, 4), "tokens_per_s": round(tps, 1),
-            "alg_mfma_frac": round(tps * PREFILL_FLOPS_PER_TOKEN / (MFMA_BF16_PEAK_TFLOPS * 1e12), 4),
-            "alg_hbm_frac": round(tps * PREFILL_BYTES_PER_TOKEN / (HBM_PEAK_GBS * 1e9), 4),
-            "wl": wl}
+    res = {"workload": "varlen prefill: 16 seqs, lengths U{512..16384}, H=16, d=128, chunk 64, bf16",
+           "tokens": T, "ms": round(ms, 4), "tokens_per_s": round(tps, 1),
+           "alg_mfma_frac": round(tps * PREFILL_FLOPS_PER_TOKEN / (MFMA_BF16_PEAK_TFLOPS * 1e12), 4),
+           "alg_hbm_frac": round(tps * PREFILL_BYTES_PER_TOKEN / (HBM_PEAK_GBS * 1e9), 4),
+           "roofline": prefill_roofline("prefill_kernel<128,bf16,bf16> (kda_prefill_varlen call: segment plan, "
+                                        "pass A, combine, fix-up)", T, ms, "prefill_varlen",
+                                        "prefill_kernel_d128_bf16")}
+    if cpu_seconds > 0:
+        res["cpu_baseline"] = cpu_prefill(cpu_seconds, wl)
+    return res
 
 
-def bench_prefill_long(torch, K, make_workload, dev, iters=3):
+def prefill_roofline(kernel, T, ms, counters_key, traffic_key):
+    """Both rooflines of a prefill call: algorithmic bytes against 8 TB/s
+    (the tighter bound at these shapes) and algorithmic MFMA flops against
+    the bf16 dense peak; the call's whole time (all its launches)."""
+    achieved = T * PREFILL_BYTES_PER_TOKEN / (ms * 1e-3) / 1e9
+    tflops = T * PREFILL_FLOPS_PER_TOKEN / (ms * 1e-3) / 1e12
+    return {"kernel": kernel, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic_for(traffic_key, "kda_prefill.hip", T),
+            "alg_bytes_per_launch": T * PREFILL_BYTES_PER_TOKEN, "avg_launch_us": round(ms * 1e3, 2),
+            "mfma": {"alg_flops_per_launch": T * PREFILL_FLOPS_PER_TOKEN, "achieved_tflops": round(tflops, 1),
+                     "peak_tflops": MFMA_BF16_PEAK_TFLOPS, "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "counters": mfma_counters(counters_key, T, ms)}}
+
+
+def bench_conv_prefill(torch, K, wl, dev, iters=20):
+    """kda_conv_short at prefill scale: the varlen workload's 16 sequences
+    (140,625 tokens) over the 3 H d = 6,144 q/k/v channels, W = 4, bf16,
+    carried conv history read from and written to per-sequence slots.
+    Algorithmic bytes: x in and y out (2 B each per element), the history
+    read and written, the taps."""
+    from hybrid_recurrent_serving_amd.inputs import draw_conv
+    N, C, W = wl.n_seq, 3 * 16 * 128, 4
+    T = int(wl.cu_seqlens[-1])
+    gen = torch.Generator().manual_seed(2)
+    cw, cst, x = draw_conv(gen, T, C, W, N, torch.bfloat16, torch.device("cpu"))
+    x, cw = x.to(dev), cw.to(dev)
+    cpool = torch.cat([cst, torch.zeros_like(cst)]).to(dev)
+    src = torch.arange(N, dtype=torch.int32, device=dev)
+    dst = src + N
+    cu = wl.cu_seqlens.to(dev)
+    y = torch.empty_like(x)
+    call = K.prepare_conv_short(x, cw, cu, cpool, src, dst, y=y)
+    for _ in range(3):
+        call()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(iters):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / iters * 1e3
+    alg = 2 * T * C * 2 + 2 * N * C * (W - 1) * 2 + C * W * 2
+    gbs = alg / us / 1e3
+    return {"workload": f"short conv, {T} tokens (16 packed sequences) x {C} channels, W=4, bf16, "
+                        "carried history in slots", "us": round(us, 2),
+            "roofline": {"kernel": "conv_kernel<bf16,4> (kda_conv_short)", "bound": "hbm",
+                         "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "traffic": traffic_for("conv_kernel_prefill_bf16", "kda_conv.hip", T),
+                         "alg_bytes_per_launch": alg, "avg_launch_us": round(us, 3)}}
+
+
+def bench_prefill_long(torch, K, make_workload, dev, iters=3, cpu_segments=0):
     """B=1, T=1,048,576, H=16, d=128, chunk 64, checkpoints every 32,768 (31
     interior + final), run as 32 segments by the segment scan.  Inputs are
-    drawn on the GPU (17 GB bf16)."""
+    drawn on the GPU (17 GB bf16).  With cpu_segments > 0 the oracle is timed
+    resuming from the GPU's checkpoints on that many segments spread over the
+    sequence (plus a continuous run over the first 65,536 tokens)."""
     wl = make_workload(3, device=dev)
     T, H, D, I = wl.q.shape[0], 16, 128, wl.ckpt_interval
     cu = wl.cu_seqlens.to(dev)
@@ -680,93 +759,90 @@ def bench_prefill_long(torch, K, make_workload, dev, iters=3):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / iters
     tps = T / (ms * 1e-3)
+    res = {"workload": "long prefill: B=1, T=1048576, H=16, d=128, chunk 64, ckpt every 32768, "
+                       "32 segments", "tokens": T, "ms": round(ms, 3), "tokens_per_s": round(tps, 1),
+           "alg_mfma_frac": round(tps * PREFILL_FLOPS_PER_TOKEN / (MFMA_BF16_PEAK_TFLOPS * 1e12), 4),
+           "alg_hbm_frac": round(tps * PREFILL_BYTES_PER_TOKEN / (HBM_PEAK_GBS * 1e9), 4),
+           "workspace_bytes": nws,
+           "roofline": prefill_roofline("prefill_kernel<128,bf16,bf16> (kda_prefill_varlen call, segment scan: "
+                                        "zero-started segments + transitions, combine, fix-up)", T, ms,
+                                        "prefill_long_1m", "prefill_long_kernel_d128_bf16")}
+    if cpu_segments > 0:
+        states = torch.cat([torch.zeros(1, H, D, D, device=dev), pool[1:]]).cpu()   # state entering segment j
+        res["cpu_baseline"] = cpu_long(wl, states, I, cpu_segments)
     del wl, o, ws, pool
     torch.cuda.empty_cache()
-    return {"workload": "long prefill: B=1, T=1048576, H=16, d=128, chunk 64, ckpt every 32768, "
-                        "32 segments", "tokens": T, "ms": round(ms, 3), "tokens_per_s": round(tps, 1),
-            "alg_mfma_frac": round(tps * PREFILL_FLOPS_PER_TOKEN / (MFMA_BF16_PEAK_TFLOPS * 1e12), 4),
-            "alg_hbm_frac": round(tps * PREFILL_BYTES_PER_TOKEN / (HBM_PEAK_GBS * 1e9), 4),
-            "workspace_bytes": nws}
+    return res
 
 
 def bench_prefill(args, torch, K, make_workload):
     dev = torch.device("cuda:0")
     wl = make_workload(2)
-    pf = bench_prefill_varlen(torch, K, make_workload, dev, iters=args.steps, wl=wl)
-    T = pf["tokens"]
-    achieved = T * PREFILL_BYTES_PER_TOKEN / (pf["ms"] * 1e-3) / 1e9
-    roof = {"kernel": "prefill_kernel<128,bf16,bf16> (kda_prefill_varlen call: segment plan, pass A, combine, "
-                      "fix-up)", "bound": "hbm",
-            "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": traffic_for("prefill_kernel_d128_bf16", "kda_prefill.hip", T),
-            "alg_bytes_per_launch": T * PREFILL_BYTES_PER_TOKEN, "avg_launch_us": round(pf["ms"] * 1e3, 2),
-            "mfma": {"alg_flops_per_launch": T * PREFILL_FLOPS_PER_TOKEN,
-                     "achieved_tflops": round(T * PREFILL_FLOPS_PER_TOKEN / (pf["ms"] * 1e-3) / 1e12, 1),
-                     "peak_tflops": MFMA_BF16_PEAK_TFLOPS, "frac": pf["alg_mfma_frac"],
-                     "counters": mfma_counters("prefill_varlen", T, pf["ms"])}}
-    cpu = None
-    if not args.no_cpu:
-        cpu = cpu_prefill(args, wl)
-    cfg = {"workload": pf["workload"], "tokens": T, "H": 16, "d": 128, "chunk": 64,
+    pf = bench_prefill_varlen(torch, K, make_workload, dev, iters=args.steps, wl=wl,
+                              cpu_seconds=0 if args.no_cpu else args.cpu_seconds)
+    cfg = {"workload": pf["workload"], "tokens": pf["tokens"], "H": 16, "d": 128, "chunk": 64,
            "initial_states": "even-indexed sequences", "segment_len": VARLEN_SEGMENT}
     secondary = {}
     if not args.no_secondary:
         secondary["prefill_long_1m"] = bench_prefill_long(torch, K, make_workload, torch.device("cuda:0"))
     return {"metric": METRIC, "value": pf["tokens_per_s"], "unit": "tokens/s", "ms_per_step": pf["ms"],
-            "dtype": "bf16-mfma/f32-acc", "config": cfg, "roofline": roof, "cpu_baseline": cpu,
-            "secondary": secondary}
+            "dtype": "bf16-mfma/f32-acc", "config": cfg, "roofline": pf["roofline"],
+            "cpu_baseline": pf.get("cpu_baseline"), "secondary": secondary}
 
 
 def bench_long(args, torch, K, make_workload):
     dev = torch.device("cuda:0")
-    pf = bench_prefill_long(torch, K, make_workload, dev, iters=max(1, min(args.steps, 10)))
-    T = pf["tokens"]
-    achieved = T * PREFILL_BYTES_PER_TOKEN / (pf["ms"] * 1e-3) / 1e9
-    roof = {"kernel": "prefill_kernel<128,bf16,bf16> (kda_prefill_varlen, segment scan: zero-started segments + transitions, combine, fix-up)",
-            "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": traffic_for("prefill_long_kernel_d128_bf16", "kda_prefill.hip", T),
-            "alg_bytes_per_launch": T * PREFILL_BYTES_PER_TOKEN, "avg_launch_us": round(pf["ms"] * 1e3, 2),
-            "mfma": {"alg_flops_per_launch": T * PREFILL_FLOPS_PER_TOKEN,
-                     "achieved_tflops": round(T * PREFILL_FLOPS_PER_TOKEN / (pf["ms"] * 1e-3) / 1e12, 1),
-                     "peak_tflops": MFMA_BF16_PEAK_TFLOPS, "frac": pf["alg_mfma_frac"],
-                     "counters": mfma_counters("prefill_long_1m", T, pf["ms"])}}
-    cpu = None
-    if not args.no_cpu:
-        cpu = cpu_long(args, make_workload)
-    cfg = {"workload": pf["workload"], "tokens": T, "H": 16, "d": 128, "chunk": 64,
+    pf = bench_prefill_long(torch, K, make_workload, dev, iters=max(1, min(args.steps, 10)),
+                            cpu_segments=0 if args.no_cpu else args.long_cpu_segments)
+    cfg = {"workload": pf["workload"], "tokens": pf["tokens"], "H": 16, "d": 128, "chunk": 64,
            "ckpt_interval": 32768, "segments": 32}
     return {"metric": METRIC, "value": pf["tokens_per_s"], "unit": "tokens/s", "ms_per_step": pf["ms"],
-            "dtype": "bf16-mfma/f32-acc", "config": cfg, "roofline": roof, "cpu_baseline": cpu,
-            "secondary": {}}
+            "dtype": "bf16-mfma/f32-acc", "config": cfg, "roofline": pf["roofline"],
+            "cpu_baseline": pf.get("cpu_baseline"), "secondary": {}}
 
 
-def cpu_long(args, make_workload):
-    """Oracle on the first segment (32,768 tokens, 16 heads) of the long
-    workload."""
+def cpu_long(wl, states, I, n_seg):
+    """The oracle on the 1M-token workload, resumed from the GPU's checkpoints:
+    n_seg of the 32 segments (32,768 tokens, all 16 heads each), spread over
+    the sequence, in one packed call; then, separately, one continuous run
+    over the first 65,536 tokens.  tokens/s of the resumed segments."""
     import numpy as np
     import torch
     import oracle
     orc = oracle.load("f64")
     threads = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
     orc.set_threads(threads)
-    wl = make_workload(3, device=torch.device("cuda:0"))
-    I = 32768
-    q, k, v, g, b = (t[:I].float().cpu().numpy() for t in (wl.q, wl.k, wl.v, wl.g, wl.beta))
-    del wl
-    torch.cuda.empty_cache()
-    # all 16 heads of the first segment in one call (parallel over heads)
-    cu = torch.tensor([0, I], dtype=torch.int32)
-    t0 = time.perf_counter()
-    orc.kda_varlen(q, k, v, g, b, cu)
-    dt = time.perf_counter() - t0
-    return {"value": round(I / dt, 1), "unit": "tokens/s", "cores": orc.threads(),
+    nseg_all = wl.q.shape[0] // I
+    pick = sorted({int(round(j * (nseg_all - 1) / max(n_seg - 1, 1))) for j in range(n_seg)})
+    dt = 0.0
+    G = 4   # segments per oracle call (one packed batch), which bounds the host memory
+    for i0 in range(0, len(pick), G):
+        grp = pick[i0:i0 + G]
+        parts = [[t[j * I:(j + 1) * I].float().cpu() for j in grp] for t in (wl.q, wl.k, wl.v, wl.g, wl.beta)]
+        q, k, v, g, b = (torch.cat(x).numpy() for x in parts)
+        init = states[grp].double().numpy()
+        cu = torch.arange(0, len(grp) * I + 1, I, dtype=torch.int32)
+        t0 = time.perf_counter()
+        orc.kda_varlen(q, k, v, g, b, cu, init=init, has_init=np.ones(len(grp), np.int32),
+                       start_pos=np.array([j * I for j in grp], np.int32))
+        dt += time.perf_counter() - t0
+        del q, k, v, g, b, parts
+    T2 = 2 * I
+    q, k, v, g, b = (t[:T2].float().cpu().numpy() for t in (wl.q, wl.k, wl.v, wl.g, wl.beta))
+    t1 = time.perf_counter()
+    orc.kda_varlen(q, k, v, g, b, torch.tensor([0, T2], dtype=torch.int32))
+    dt2 = time.perf_counter() - t1
+    return {"value": round(len(pick) * I / dt, 1), "unit": "tokens/s", "cores": orc.threads(),
             "kind": "oracle", "cpu": cpu_info(),
-            "sample": f"first 32768 tokens (one segment), all 16 heads, fp64 oracle, {dt:.1f} s"}
+            "sample": (f"all {nseg_all} segments" if len(pick) == nseg_all else
+                       f"{len(pick)} of {nseg_all} segments ({pick})") +
+                      f", 32768 tokens x 16 heads each, resumed from the GPU's checkpoints (4 segments per "
+                      f"oracle call), fp64 oracle, {dt:.1f} s",
+            "continuous_65536": {"value": round(T2 / dt2, 1), "unit": "tokens/s",
+                                 "sample": f"tokens 0..65535 from the zero state, 16 heads, {dt2:.1f} s"}}
 
 
-def cpu_prefill(args, wl):
+def cpu_prefill(cpu_seconds, wl):
     """Oracle on whole (sequence, head) pairs of the same workload until the
     time budget is spent; tokens/s scaled to all 16 heads."""
     import numpy as np
@@ -792,13 +868,38 @@ def cpu_prefill(args, wl):
         orc.kda_varlen(q, k, v, g, b, wl.cu_seqlens, init=init, has_init=has, pairs=pairs)
         tok_heads += lens[s_] * 16
         done.append(s_)
-        if time.perf_counter() - t0 > args.cpu_seconds:
+        if time.perf_counter() - t0 > cpu_seconds:
             break
     dt = time.perf_counter() - t0
     return {"value": round(tok_heads / 16 / dt, 1), "unit": "tokens/s", "cores": orc.threads(),
             "kind": "oracle", "cpu": cpu_info(),
             "sample": f"{len(done)} of 16 sequences (all 16 heads each, {tok_heads // 16} tokens), "
                       f"fp64 oracle, {dt:.1f} s"}
+
+
+def cpu_verify(wl, state_bytes, cpu_seconds):
+    """The oracle on the whole verify workload (128 sequences x 8 tokens x 16
+    heads, fused commit), repeated until the time budget is spent; state GB/s
+    with the GPU's byte count."""
+    import oracle
+    orc = oracle.load("f64")
+    threads = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    orc.set_threads(threads)
+    q, k, v, g, b = (t.float().numpy() for t in (wl.q, wl.k, wl.v, wl.g, wl.beta))
+    init = wl.init_states.double().numpy()
+    L = wl.accepted_len.numpy()
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        orc.kda_verify(q, k, v, g, b, init, L)
+        reps += 1
+        if time.perf_counter() - t0 > cpu_seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(state_bytes * reps / dt / 1e9, 3), "unit": "GB/s", "cores": orc.threads(),
+            "kind": "oracle", "cpu": cpu_info(),
+            "sample": f"{reps} whole verify calls (128 seqs x 8 tokens x 16 heads, commit at L), fp64 oracle, "
+                      f"{dt:.1f} s"}
 
 
 def cpu_decode(args, wl, state_bytes):
