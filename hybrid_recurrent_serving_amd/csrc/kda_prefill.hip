@@ -287,12 +287,10 @@ struct Smem {
 
   alignas(16) TIN g_raw[TILE][D];         // raw gates of the next chunk
   uint32_t nonzero[NW];                   // transition mode: wave's state slice not all zero
+  // 16x16 blocks of A, transposed ([c][r] = A[r][c]): A00, A11, A10, formed
+  // by waves 0-2 in phase I, read by the solve waves in phase II
+  float At[3][16][17];
   union {
-    // the solve: 16x16 blocks of A, transposed ([c][r] = A[r][c]), in the
-    // waves that form them (3: A00; 4: A10, A11; 5: A11)
-    struct {
-      float At[4][16][17];
-    } x;
     // from the W product to the chain
     struct {
       bf16_t Wn[TILE][PD];    // -(T left_k) [r][pos32(c)]
@@ -783,15 +781,15 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
         load_g(b + 2 * CH);
       }
     };
-    // the A products of the solve waves (left_k right_k^T blocks of chunk b,
-    // whose operands are complete since the previous step): wave 3 block
-    // (0,0), wave 4 blocks (1,0) and (1,1), wave 5 block (1,1); kept in
-    // registers until phase II.  On chain waves they run beside the VALU
-    // work that forms the S' fragments.
-    f32x4 ablk[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    // The blocks of A = strict-lower(diag(beta) left_k right_k^T) of chunk
+    // b (operands complete since the previous step), one per wave on waves
+    // 0-2 -- the chain waves whose own work ends first -- written transposed
+    // to the At tiles for the solve waves of phase II:
+    // At[t][c][r] = beta_r <left_k[16 I + r], right_k[16 J + c]>, t = 0: A00,
+    // 1: A11, 2: A10.
     auto a_products = [&]() __attribute__((always_inline)) {
       if constexpr (MORE) {
-        if (wave >= 3 && wave < 6) {
+        if (wave < 3) {
           auto a_prod = [&](const int I, const int J, f32x4& acc) __attribute__((always_inline)) {
 #pragma unroll
             for (int ks = 0; ks < D / 32; ++ks) {
@@ -804,12 +802,15 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
               }
             }
           };
-          if (wave == 4) {
-            a_prod(1, 0, ablk[0]);
-            a_prod(1, 1, ablk[1]);
-          } else {
-            const int bb = wave == 3 ? 0 : 1;
-            a_prod(bb, bb, ablk[0]);
+          const int I = wave == 0 ? 0 : 1;
+          const int J = wave == 2 ? 1 : 0;
+          const int tt = wave == 0 ? 0 : (wave == 1 ? 2 : 1);
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+          a_prod(I, J, acc);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = 4 * g4 + i;
+            sm.At[tt][l16][r] = (I > J || r > l16) ? acc[i] * sm.beta[lp][16 * I + r] : 0.f;
           }
         }
       }
@@ -990,28 +991,15 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
         // T10 = -M T00 with M = L_1^{-1} A10, which the W / U products apply
         // as a correction of the second row block.  Inverses by fp32 forward
         // substitution down the 16 lanes of a lane row (lane (g4, r) holds
-        // row r of column 4 g + g4, g = 0..3).  Each wave forms the blocks of
-        // A = strict-lower(diag(beta) left_k right_k^T) it needs: wave 3 A00
-        // (-> T00), wave 4 A10, A11 (-> M), wave 5 A11 (-> T11).
-        // A block (I, J) from its product (formed in phase I) into the
-        // wave's LDS tile t, transposed:
-        // At[t][c][r] = beta_r <left_k[16 I + r], right_k[16 J + c]>
-        auto a_block = [&](const f32x4& acc, const int I, const int J, const int t) __attribute__((always_inline)) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = 4 * g4 + i;
-            sm.u.x.At[t][l16][r] = (I > J || r > l16) ? acc[i] * sm.beta[lp][16 * I + r] : 0.f;
-          }
-        };
+        // row r of column 4 g + g4, g = 0..3), from the blocks of A formed
+        // in phase I: wave 3 A00 (-> T00), wave 4 A10, A11 (-> M), wave 5
+        // A11 (-> T11).
         if (wave != 4) {
           const int bb = wave == 3 ? 0 : 1;
           const int t = wave == 3 ? 0 : 1;
-          a_block(ablk[0], bb, bb, t);
-          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-          __builtin_amdgcn_wave_barrier();
           float na[16];
 #pragma unroll
-          for (int s2 = 0; s2 < 16; ++s2) na[s2] = -sm.u.x.At[t][s2][l16];
+          for (int s2 = 0; s2 < 16; ++s2) na[s2] = -sm.At[t][s2][l16];
           float x[4];
 #pragma unroll
           for (int g = 0; g < 4; ++g) x[g] = l16 == 4 * g + g4 ? 1.f : 0.f;
@@ -1030,16 +1018,12 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
             if constexpr (HP) sm.Tb_lo[16 * bb + l16][16 * (1 - bb) + j] = 0;
           }
         } else {
-          a_block(ablk[0], 1, 0, 2);
-          a_block(ablk[1], 1, 1, 3);
-          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-          __builtin_amdgcn_wave_barrier();
           float na1[16];
 #pragma unroll
-          for (int s2 = 0; s2 < 16; ++s2) na1[s2] = -sm.u.x.At[3][s2][l16];
+          for (int s2 = 0; s2 < 16; ++s2) na1[s2] = -sm.At[1][s2][l16];
           float m4[4];
 #pragma unroll
-          for (int g = 0; g < 4; ++g) m4[g] = sm.u.x.At[2][4 * g + g4][l16];   // A10[r][j]
+          for (int g = 0; g < 4; ++g) m4[g] = sm.At[2][4 * g + g4][l16];   // A10[r][j]
           // m4 was just written by a load: wait states before a DPP read
           asm volatile("s_waitcnt lgkmcnt(0)\n\ts_nop 1" ::"v"(m4[0]), "v"(m4[1]), "v"(m4[2]), "v"(m4[3]));
           fsub16<0, 4>(m4, na1);
