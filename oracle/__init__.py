@@ -203,7 +203,8 @@ class Oracle:
 
     # -- fused decode step -------------------------------------------------
     def kda_decode_conv(self, x, w, g, beta, init, conv_state, *, H, d, bias=None, act=0,
-                        qk_l2norm=1, norm_eps=1e-6, scale=1.0):
+                        qk_l2norm=1, norm_eps=1e-6, scale=1.0, out_gate=None, norm_weight=None,
+                        out_norm_eps=1e-6):
         """The decode step with the short convolution in front of the
         recurrence, one token per sequence.
 
@@ -216,7 +217,9 @@ class Oracle:
         same definition as :meth:`conv_short`, kept unrounded; q, k, v are the
         three blocks of y, per head; when qk_l2norm, q <- q / sqrt(|q|^2 + eps)
         and k likewise (per token and head); then one recurrence step from
-        init as :meth:`kda_verify` with T_spec = 1.
+        init as :meth:`kda_verify` with T_spec = 1.  With out_gate [N, H, d]
+        and norm_weight [d], the output then passes through
+        :func:`gated_rmsnorm`.
 
         Returns dict o [N, H, d], state [N, H, d, d], conv_state [N, 3 H d, W-1].
         """
@@ -237,10 +240,14 @@ class Oracle:
         res = self.kda_verify(q[:, None].astype(np.float32), k[:, None].astype(np.float32),
                               v[:, None].astype(np.float32), _as_f32(g)[:, None],
                               _as_f32(beta)[:, None], init, scale=scale)
-        return {"o": res["o"][:, 0], "state": res["committed"], "conv_state": ns}
+        o = res["o"][:, 0]
+        if out_gate is not None:
+            o = gated_rmsnorm(o, out_gate, norm_weight, out_norm_eps)
+        return {"o": o, "state": res["committed"], "conv_state": ns}
 
     def kda_verify_conv(self, x, w, g, beta, init, conv_state, accepted_len=None, *, H, d, bias=None,
-                        act=0, qk_l2norm=1, norm_eps=1e-6, scale=1.0):
+                        act=0, qk_l2norm=1, norm_eps=1e-6, scale=1.0, out_gate=None, norm_weight=None,
+                        out_norm_eps=1e-6):
         """Speculative verify with the short convolution in front.
 
         x [N, Ts, 3 H d] (the Ts tokens' raw q | k | v projections);
@@ -250,7 +257,9 @@ class Oracle:
         Per sequence: y = conv(conv_state ++ x) over the Ts tokens (+ SiLU),
         q, k, v its blocks, q / k normalised per token and head when
         qk_l2norm, then :meth:`kda_verify`.  The conv history is advanced by
-        the accepted length (the W-1 raw inputs ending at token L-1).
+        the accepted length (the W-1 raw inputs ending at token L-1).  With
+        out_gate [N, Ts, H, d] and norm_weight [d], every output passes
+        through :func:`gated_rmsnorm`.
 
         Returns dict o [N, Ts, H, d], committed [N, H, d, d] (NaN where
         rejected), committed_len [N], conv_state [N, 3 H d, W-1] (NaN where
@@ -279,8 +288,26 @@ class Oracle:
                 xb = np.concatenate([st[s].astype(np.float64), x[s, :L[s]].T], axis=1)  # [C, W-1+L]
                 ns[s] = xb[:, -(W - 1):]
         out = dict(res)
+        if out_gate is not None:
+            out["o"] = gated_rmsnorm(res["o"], out_gate, norm_weight, out_norm_eps)
         out["conv_state"] = ns
         return out
+
+
+def gated_rmsnorm(o, z, weight, eps=1e-6):
+    """Output gate of the fused decode step (one reading of the output norm
+    and gate the Day-0 Integration page's fused decode kernel folds in,
+    section "Separate Prefill/Decode Code Paths"): per token and head, the
+    output o is divided by its root mean square over the d_v channels (eps
+    added under the root), scaled channel-wise by the norm weight (shared by
+    the heads), and multiplied by the logistic sigmoid of the gate input z.
+
+    o [..., d] (any float), z [..., d], weight [d].  Returns float64."""
+    o = np.asarray(o, np.float64)
+    z = np.asarray(_as_f32(z), np.float64)
+    wv = np.asarray(_as_f32(weight), np.float64)
+    ms = np.mean(o * o, axis=-1, keepdims=True)
+    return o / np.sqrt(ms + eps) * wv * (1.0 / (1.0 + np.exp(-z)))
 
 
 _cache: dict = {}
@@ -306,4 +333,4 @@ def load_mutant(mutant: int, outdir: Path, real: str = "f64") -> Oracle:
     return Oracle(path)
 
 
-__all__ = ["Oracle", "load", "load_mutant", "build"]
+__all__ = ["Oracle", "load", "load_mutant", "build", "gated_rmsnorm"]

@@ -389,6 +389,52 @@ def pin_verify_conv(orc):
     assert np.all(np.isnan(res["committed"][2])) and np.all(np.isnan(res["conv_state"][2]))
 
 
+def pin_output_gate(orc):
+    """Gated RMS norm of the fused step's output, by its properties rather
+    than its formula: with unit weight and an open gate (sigmoid = 1) the
+    output of every (token, head) has root mean square 1 over its channels
+    (a sum instead of a mean, or a missing root, fails); positive scalings of
+    one head's output change no output (the norm axis is per head: a norm
+    over all heads fails); a gate of zero halves the output (sigmoid(0) =
+    1/2); a one-hot weight keeps one channel; a zero output stays zero with
+    eps > 0.  Then, wired into the fused decode step: its gated output times
+    the root mean square of its ungated output is the ungated output (the
+    gate acts on o, not on q, k or v)."""
+    import oracle as O
+    r = _rng(71)
+    N, H, d = 4, 3, 8
+    o = r.standard_normal((N, H, d)) * r.uniform(0.1, 5.0, (N, H, 1))
+    w1 = np.ones(d, np.float32)
+    zo = np.full((N, H, d), 40.0, np.float32)        # sigmoid(40) = 1 - 4e-18
+    y = O.gated_rmsnorm(o, zo, w1, eps=0.0)
+    np.testing.assert_allclose(np.sqrt(np.mean(y * y, axis=-1)), 1.0, rtol=1e-12)
+    np.testing.assert_allclose(y * np.sqrt(np.mean(o * o, axis=-1, keepdims=True)), o, rtol=1e-12)
+    z = r.standard_normal((N, H, d)).astype(np.float32)
+    wr = r.uniform(0.5, 1.5, d).astype(np.float32)
+    a = O.gated_rmsnorm(o, z, wr, eps=0.0)
+    o2 = o.copy()
+    o2[1, 2] *= 7.5
+    o2[3, 0] *= 0.01
+    np.testing.assert_allclose(O.gated_rmsnorm(o2, z, wr, eps=0.0), a, rtol=1e-12, atol=1e-14)
+    half = O.gated_rmsnorm(o, np.zeros((N, H, d), np.float32), w1, eps=0.0)
+    np.testing.assert_allclose(2.0 * half, O.gated_rmsnorm(o, zo, w1, eps=0.0), rtol=1e-12)
+    e3 = np.zeros(d, np.float32)
+    e3[3] = 1.0
+    y3 = O.gated_rmsnorm(o, z, e3, eps=0.0)
+    assert np.all(y3[..., np.arange(d) != 3] == 0.0) and np.all(y3[..., 3] != 0.0)
+    assert np.all(O.gated_rmsnorm(np.zeros((N, H, d)), z, wr, eps=1e-6) == 0.0)
+    # in the fused decode step
+    tol = max(_tol(orc) * 10, 1e-6)
+    x, w, bias, cst, g, beta, S0 = decode_conv_case(72, N=3, H=2, d=5)
+    plain = orc.kda_decode_conv(x, w, g, beta, S0, cst, H=2, d=5, bias=bias, act=1, qk_l2norm=1)
+    gated = orc.kda_decode_conv(x, w, g, beta, S0, cst, H=2, d=5, bias=bias, act=1, qk_l2norm=1,
+                                out_gate=np.full((3, 2, 5), 40.0, np.float32),
+                                norm_weight=np.ones(5, np.float32), out_norm_eps=0.0)
+    rms = np.sqrt(np.mean(plain["o"] ** 2, axis=-1, keepdims=True))
+    np.testing.assert_allclose(gated["o"] * rms, plain["o"], rtol=tol, atol=tol)
+    assert np.array_equal(gated["state"], plain["state"])
+
+
 ALL_PINS = [pin_bruteforce, pin_readback, pin_pure_decay, pin_linearity, pin_resume,
             pin_varlen_independent, pin_verify, pin_ckpt_positions, pin_conv, pin_decode_conv,
-            pin_verify_conv]
+            pin_verify_conv, pin_output_gate]

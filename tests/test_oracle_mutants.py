@@ -25,3 +25,42 @@ def test_mutant_is_caught(m, tmp_path):
         except AssertionError:
             failed.append(pin.__name__)
     assert failed, f"planted mistake {m} ({MUTANTS[m]}) passed every pin"
+
+
+def _planted_gate_norms():
+    """Plausible mistakes in the output gate's norm (each a function with the
+    signature of oracle.gated_rmsnorm)."""
+    import numpy as np
+
+    def sig(z):
+        return 1.0 / (1.0 + np.exp(-np.asarray(z, np.float64)))
+
+    def sum_not_mean(o, z, w, eps=1e-6):
+        o = np.asarray(o, np.float64)
+        return o / np.sqrt(np.sum(o * o, -1, keepdims=True) + eps) * np.asarray(w, np.float64) * sig(z)
+
+    def all_heads(o, z, w, eps=1e-6):
+        o = np.asarray(o, np.float64)
+        ms = np.mean(o * o, axis=(-2, -1), keepdims=True)
+        return o / np.sqrt(ms + eps) * np.asarray(w, np.float64) * sig(z)
+
+    def no_root(o, z, w, eps=1e-6):
+        o = np.asarray(o, np.float64)
+        return o / (np.mean(o * o, -1, keepdims=True) + eps) * np.asarray(w, np.float64) * sig(z)
+
+    def silu_gate(o, z, w, eps=1e-6):
+        o = np.asarray(o, np.float64)
+        z = np.asarray(z, np.float64)
+        return o / np.sqrt(np.mean(o * o, -1, keepdims=True) + eps) * np.asarray(w, np.float64) * z * sig(z)
+
+    return [sum_not_mean, all_heads, no_root, silu_gate]
+
+
+@pytest.mark.parametrize("planted", _planted_gate_norms(), ids=lambda f: f.__name__)
+def test_output_gate_pin_catches_planted_mistake(planted, oracle64, monkeypatch):
+    """Each planted mistake in the output gate's norm fails pin_output_gate."""
+    import oracle
+    import oracle_pins as P
+    monkeypatch.setattr(oracle, "gated_rmsnorm", planted)
+    with pytest.raises(AssertionError):
+        P.pin_output_gate(oracle64)
