@@ -340,6 +340,17 @@ int kda_decode(const kda_decode_args* a, kda_stream_t stream_) {
   return launch_step(p, b.d_k, b.in_dtype, b.out_dtype, stream);
 }
 
+// the optional gated RMS norm of the fused steps' output
+static int out_gate_common(const void* gate, const void* weight, int64_t& stride, float eps, int H, int d,
+                           int in_dt, const char* who) {
+  if (!gate) return KDA_OK;
+  if (!weight) return fail(KDA_ERR_NULL, "%s: out_gate given without out_norm_weight", who);
+  if (!(eps >= 0.f)) return fail(KDA_ERR_ARG, "%s: out_norm_eps < 0", who);
+  if (!aligned16(gate) || !aligned16(weight))
+    return fail(KDA_ERR_ALIGN, "%s: out_gate or out_norm_weight not 16-byte aligned", who);
+  return fix_stride(stride, (int64_t)H * d, in_dt, "out_gate");
+}
+
 int kda_decode_conv(const kda_decode_conv_args* a, kda_stream_t stream_) {
   hipStream_t stream = static_cast<hipStream_t>(stream_);
   if (!a) return fail(KDA_ERR_NULL, "args is NULL");
@@ -370,6 +381,9 @@ int kda_decode_conv(const kda_decode_conv_args* a, kda_stream_t stream_) {
   if ((st = fix_stride(b.g_stride, (int64_t)b.H * b.d, in_dt, "g"))) return st;
   if ((st = fix_stride(b.o_stride, (int64_t)b.H * b.d, out_dt, "o"))) return st;
   if ((st = fix_beta_stride(b.beta_stride, b.H))) return st;
+  if ((st = out_gate_common(b.out_gate, b.out_norm_weight, b.out_gate_stride, b.out_norm_eps, b.H, b.d, in_dt,
+                            "decode_conv")))
+    return st;
   if ((int64_t)b.n_seq * b.H > 0x7fffffffLL) return fail(KDA_ERR_SHAPE, "n_seq * H too large");
   if (check_enabled()) {
     st = check_slots(b.src_slot, b.dst_slot, b.n_seq, b.n_slots, nullptr, stream);
@@ -385,6 +399,8 @@ int kda_decode_conv(const kda_decode_conv_args* a, kda_stream_t stream_) {
   p.n_slots = b.n_slots; p.n_cslots = b.n_conv_slots;
   p.n_seq = b.n_seq; p.H = b.H; p.W = b.W; p.act = b.act; p.qk_l2norm = b.qk_l2norm;
   p.eps = b.norm_eps; p.scale = b.scale;
+  p.ogate = b.out_gate; p.onorm_w = b.out_norm_weight; p.ogate_stride = b.out_gate_stride;
+  p.onorm_eps = b.out_norm_eps;
   return launch_decode_conv(p, b.d, in_dt, out_dt, stream);
 }
 
@@ -420,6 +436,9 @@ int kda_verify_conv(const kda_verify_conv_args* a, kda_stream_t stream_) {
   if ((st = fix_stride(b.g_stride, (int64_t)b.H * b.d, in_dt, "g"))) return st;
   if ((st = fix_stride(b.o_stride, (int64_t)b.H * b.d, out_dt, "o"))) return st;
   if ((st = fix_beta_stride(b.beta_stride, b.H))) return st;
+  if ((st = out_gate_common(b.out_gate, b.out_norm_weight, b.out_gate_stride, b.out_norm_eps, b.H, b.d, in_dt,
+                            "verify_conv")))
+    return st;
   if ((int64_t)b.n_seq * b.H > 0x7fffffffLL) return fail(KDA_ERR_SHAPE, "n_seq * H too large");
   if (check_enabled()) {
     st = check_slots(b.src_slot, b.dst_slot, b.n_seq, b.n_slots, nullptr, stream);
@@ -436,6 +455,8 @@ int kda_verify_conv(const kda_verify_conv_args* a, kda_stream_t stream_) {
   p.n_seq = b.n_seq; p.H = b.H; p.W = b.W; p.act = b.act; p.qk_l2norm = b.qk_l2norm;
   p.eps = b.norm_eps; p.scale = b.scale;
   p.T_spec = b.T_spec; p.accepted_len = b.accepted_len; p.committed_len_out = b.committed_len_out;
+  p.ogate = b.out_gate; p.onorm_w = b.out_norm_weight; p.ogate_stride = b.out_gate_stride;
+  p.onorm_eps = b.out_norm_eps;
   return launch_verify_conv(p, b.d, in_dt, out_dt, stream);
 }
 

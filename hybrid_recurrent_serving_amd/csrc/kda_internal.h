@@ -46,6 +46,11 @@ struct DecodeConvParams {
   int32_t T_spec;
   const int32_t* accepted_len;
   int32_t* committed_len_out;
+  // gated RMS norm of the output: NULL ogate = none
+  const void* ogate;
+  const void* onorm_w;
+  int64_t ogate_stride;           // per sequence (decode) or per token (verify)
+  float onorm_eps;
 };
 
 int launch_decode_conv(const DecodeConvParams& p, int D, int in_dtype, int out_dtype, hipStream_t stream);

@@ -365,6 +365,25 @@ template <> struct Vec16x<float> {
 __device__ __forceinline__ float silu_fast(float x) {
   return x * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-x * 1.4426950408889634f));
 }
+__device__ __forceinline__ float sigmoid_fast(float x) {
+  return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-x * 1.4426950408889634f));
+}
+
+// Gated RMS norm of one output vector of D channels held 4 per lane by
+// D / 4 consecutive lanes (sum of squares across them by butterfly
+// shuffles): o <- o / sqrt(mean o^2 + eps) * weight * sigmoid(gate).
+template <int D, typename Tin>
+__device__ __forceinline__ void gate_norm4(float (&o)[4], const Tin* gate, const Tin* weight, float eps) {
+  float ss = o[0] * o[0] + o[1] * o[1] + o[2] * o[2] + o[3] * o[3];
+#pragma unroll
+  for (int m = 1; m < D / 4; m <<= 1) ss += __shfl_xor(ss, m, 64);
+  const float inv = 1.f / sqrtf(ss * (1.f / D) + eps);
+  float z[4], w[4];
+  io<Tin>::ld4(gate, z);
+  io<Tin>::ld4(weight, w);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) o[c] = o[c] * inv * w[c] * sigmoid_fast(z[c]);
+}
 
 template <int D, typename Tin, typename Tout, int W>
 __global__ void __launch_bounds__(64 * StepLayout<D>::WPH)
@@ -523,8 +542,25 @@ decode_conv_kernel(const DecodeConvParams p) {
   }
 #pragma unroll
   for (int c = 0; c < 4; ++c) o[c] = wave_sum_from<L::LPR>(o[c]) * p.scale;
-  if (rg == 0)
-    io<Tout>::st4(static_cast<Tout*>(p.o) + static_cast<int64_t>(s) * p.o_stride + static_cast<int64_t>(h) * D + col, o);
+  Tout* const orow = static_cast<Tout*>(p.o) + static_cast<int64_t>(s) * p.o_stride + static_cast<int64_t>(h) * D;
+  if (p.ogate) {
+    // gated RMS norm over the head's D outputs: they are gathered in LDS and
+    // the first D / 4 lanes of wave 0 take 4 each
+    __shared__ __align__(16) float s_ob[D];
+    if (rg == 0) *reinterpret_cast<float4*>(&s_ob[col]) = make_float4(o[0], o[1], o[2], o[3]);
+    __syncthreads();
+    if (threadIdx.x < D / 4) {
+      const int c4 = 4 * threadIdx.x;
+      const float4 x = *reinterpret_cast<const float4*>(&s_ob[c4]);
+      float ov[4] = {x.x, x.y, x.z, x.w};
+      gate_norm4<D, Tin>(ov, static_cast<const Tin*>(p.ogate) + static_cast<int64_t>(s) * p.ogate_stride +
+                                 static_cast<int64_t>(h) * D + c4,
+                         static_cast<const Tin*>(p.onorm_w) + c4, p.onorm_eps);
+      io<Tout>::st4(orow + c4, ov);
+    }
+  } else if (rg == 0) {
+    io<Tout>::st4(orow + col, o);
+  }
   if (has_dst) {
     float* dp = p.pool + ((static_cast<int64_t>(dst) * p.H + h) * D + row0) * D + col;
 #pragma unroll
@@ -596,6 +632,9 @@ struct Dec128Args {
   int64_t q_stride, k_stride, v_stride, g_stride, beta_stride, o_stride, n_slots;
   int32_t n_seq, H;
   float scale;
+  const void *ogate, *onorm_w;          // gated RMS norm of the output (conv form), or NULL
+  int64_t ogate_stride;
+  float onorm_eps;
 };
 
 namespace d128 {
@@ -623,6 +662,7 @@ __global__ void __launch_bounds__(64 * d128::Shape<CPW>::NW) decode128_kernel(co
   static_assert(!CONV || NCI <= 64 * NW, "one conv item per thread");
   __shared__ __align__(16) float s_y[CONV ? 3 * D : 4];   // q | k | v of the head (fp32)
   __shared__ __align__(16) float s_w[NW][CPW], s_o[NW][CPW];
+  __shared__ __align__(16) float s_gz[CONV ? D : 4], s_gw[CONV ? D : 4];   // output gate and norm weight
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   int64_t item;
@@ -651,6 +691,15 @@ __global__ void __launch_bounds__(64 * d128::Shape<CPW>::NW) decode128_kernel(co
   const bool has_src = src >= 0 && src < p.n_slots;
   const bool has_dst = dst >= 0 && dst < p.n_slots;
 
+  // The output gate and norm weight (gated output only): requested first by
+  // the lanes that apply them at the end, put in LDS with the conv results.
+  float gz[4] = {0.f, 0.f, 0.f, 0.f}, gw[4] = {0.f, 0.f, 0.f, 0.f};
+  const bool gate_lane = CONV && p.ogate && threadIdx.x < D / 4;
+  if (gate_lane) {
+    io<Tin>::ld4(static_cast<const Tin*>(p.ogate) + static_cast<int64_t>(s) * p.ogate_stride +
+                     static_cast<int64_t>(h) * D + 4 * threadIdx.x, gz);
+    io<Tin>::ld4(static_cast<const Tin*>(p.onorm_w) + 4 * threadIdx.x, gw);
+  }
   // The convolution (conv waves only, before their own state loads: their
   // conv data and their state slice are never live together, which keeps
   // the register count of the 16-wave workgroup low).  Item t < NCI owns V
@@ -738,6 +787,10 @@ __global__ void __launch_bounds__(64 * d128::Shape<CPW>::NW) decode128_kernel(co
                      qr);
     io<Tin>::ld4(static_cast<const Tin*>(p.v) + static_cast<int64_t>(s) * p.v_stride + static_cast<int64_t>(h) * D + col, vc);
   } else {
+    if (gate_lane) {
+      *reinterpret_cast<float4*>(&s_gz[4 * threadIdx.x]) = make_float4(gz[0], gz[1], gz[2], gz[3]);
+      *reinterpret_cast<float4*>(&s_gw[4 * threadIdx.x]) = make_float4(gw[0], gw[1], gw[2], gw[3]);
+    }
     __syncthreads();
     float inv_q = 1.f, inv_k = 1.f;
     if (p.qk_l2norm) {
@@ -818,6 +871,15 @@ __global__ void __launch_bounds__(64 * d128::Shape<CPW>::NW) decode128_kernel(co
     }
 #pragma unroll
     for (int c = 0; c < 4; ++c) ov[c] *= p.scale;
+    if (CONV && p.ogate) {
+      // gated RMS norm: the D outputs are held 4 per lane by lanes 0 .. D/4 - 1
+      float ss = ov[0] * ov[0] + ov[1] * ov[1] + ov[2] * ov[2] + ov[3] * ov[3];
+#pragma unroll
+      for (int m = 1; m < LPR; m <<= 1) ss += __shfl_xor(ss, m, 64);
+      const float inv = 1.f / sqrtf(ss * (1.f / D) + p.onorm_eps);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) ov[c] = ov[c] * inv * s_gw[lc + c] * sigmoid_fast(s_gz[lc + c]);
+    }
     io<Tout>::st4(static_cast<Tout*>(p.o) + static_cast<int64_t>(s) * p.o_stride + static_cast<int64_t>(h) * D + col, ov);
   }
 }
@@ -851,6 +913,7 @@ static int launch_decode128_conv(const DecodeConvParams& p, hipStream_t stream) 
   a.g = p.g; a.beta = p.beta; a.o = p.o; a.pool = p.pool; a.src_slot = p.src_slot; a.dst_slot = p.dst_slot;
   a.g_stride = p.g_stride; a.beta_stride = p.beta_stride; a.o_stride = p.o_stride; a.n_slots = p.n_slots;
   a.n_seq = p.n_seq; a.H = p.H; a.scale = p.scale;
+  a.ogate = p.ogate; a.onorm_w = p.onorm_w; a.ogate_stride = p.ogate_stride; a.onorm_eps = p.onorm_eps;
   switch (p.W) {
     case 2: return launch_decode128<Tin, Tout, 2, 128>(a, stream);
     case 3: return launch_decode128<Tin, Tout, 3, 128>(a, stream);
@@ -1146,10 +1209,17 @@ verify_conv_kernel(const DecodeConvParams p) {
   if (p.o) {
     __syncthreads();
     Tout* ob = static_cast<Tout*>(p.o);
+    // a token's D outputs are stored by D / 4 consecutive lanes (the gated
+    // norm sums across exactly those lanes; every iteration covers whole
+    // tokens, so the lanes of a token are active together)
     for (int e = 4 * threadIdx.x; e < n_tok * D; e += 4 * NTH) {
       const int j = e / D, c = e % D;
       const float4 o4 = *reinterpret_cast<const float4*>(&s_o[j * D + c]);
-      const float ov[4] = {o4.x, o4.y, o4.z, o4.w};
+      float ov[4] = {o4.x, o4.y, o4.z, o4.w};
+      if (p.ogate)
+        gate_norm4<D, Tin>(ov, static_cast<const Tin*>(p.ogate) + (static_cast<int64_t>(s) * T + j) * p.ogate_stride +
+                                   static_cast<int64_t>(h) * D + c,
+                           static_cast<const Tin*>(p.onorm_w) + c, p.onorm_eps);
       io<Tout>::st4(ob + (static_cast<int64_t>(s) * T + j) * p.o_stride + static_cast<int64_t>(h) * D + c, ov);
     }
   }

@@ -94,6 +94,8 @@ class DecodeConvArgs(ctypes.Structure):
         ("n_seq", c_i32), ("H", c_i32), ("d", c_i32), ("W", c_i32), ("act", c_i32),
         ("qk_l2norm", c_i32), ("norm_eps", c_f32), ("in_dtype", c_i32), ("out_dtype", c_i32),
         ("scale", c_f32),
+        ("out_gate", c_vp), ("out_norm_weight", c_vp), ("out_gate_stride", c_i64),
+        ("out_norm_eps", c_f32), ("reserved", c_i32),
     ]
 
 
@@ -110,6 +112,8 @@ class VerifyConvArgs(ctypes.Structure):
         ("n_seq", c_i32), ("T_spec", c_i32), ("H", c_i32), ("d", c_i32), ("W", c_i32), ("act", c_i32),
         ("qk_l2norm", c_i32), ("norm_eps", c_f32), ("in_dtype", c_i32), ("out_dtype", c_i32),
         ("scale", c_f32), ("reserved", c_i32),
+        ("out_gate", c_vp), ("out_norm_weight", c_vp), ("out_gate_stride", c_i64),
+        ("out_norm_eps", c_f32), ("reserved2", c_i32),
     ]
 
 
@@ -515,8 +519,26 @@ def kda_decode(q, k, v, g, beta, o, state_pool, src_slot, dst_slot, *, scale=1.0
     return o
 
 
+def _out_gate_fields(a, out_gate, out_norm_weight, out_norm_eps, lead, H, d, ref):
+    """The optional gated RMS norm of the fused steps' output: out_gate
+    [*lead, H, d] (packed inner dims), out_norm_weight [d], same dtype as the
+    inputs."""
+    if out_gate is None:
+        _expect(out_norm_weight is None, "out_norm_weight given without out_gate")
+        return
+    _expect(out_norm_weight is not None, "out_gate needs out_norm_weight")
+    _expect(tuple(out_gate.shape) == tuple(lead) + (H, d), f"out_gate must be {tuple(lead) + (H, d)}")
+    _expect(out_norm_weight.numel() == d and out_norm_weight.is_contiguous(), "out_norm_weight must be [d]")
+    _device_tensors(out_gate=out_gate, out_norm_weight=out_norm_weight)
+    _same_dtype(ref, out_gate=out_gate, out_norm_weight=out_norm_weight)
+    a.out_gate, a.out_norm_weight = _ptr(out_gate), _ptr(out_norm_weight)
+    a.out_gate_stride = _tok_stride(out_gate, 2)
+    a.out_norm_eps = float(out_norm_eps)
+
+
 def _decode_conv_args(x, conv_weight, conv_pool, conv_src_slot, conv_dst_slot, g, beta, o, state_pool,
-                      src_slot, dst_slot, conv_bias, act, qk_l2norm, norm_eps, scale):
+                      src_slot, dst_slot, conv_bias, act, qk_l2norm, norm_eps, scale, out_gate=None,
+                      out_norm_weight=None, out_norm_eps=1e-6):
     import torch
     _expect(x.dim() == 2 and g.dim() == 3 and beta.dim() == 2 and o.dim() == 3,
             "x [N, 3 H d], g [N, H, d], beta [N, H], o [N, H, d]")
@@ -554,39 +576,47 @@ def _decode_conv_args(x, conv_weight, conv_pool, conv_src_slot, conv_dst_slot, g
     a.n_seq, a.H, a.d, a.W = N, H, d, W
     a.act, a.qk_l2norm, a.norm_eps = int(act), int(qk_l2norm), float(norm_eps)
     a.in_dtype, a.out_dtype, a.scale = _dtype_code(x), _dtype_code(o), scale
+    _out_gate_fields(a, out_gate, out_norm_weight, out_norm_eps, (N,), H, d, x)
     return a
 
 
 def kda_decode_conv(x, conv_weight, conv_pool, conv_src_slot, conv_dst_slot, g, beta, o, state_pool,
                     src_slot, dst_slot, *, conv_bias=None, act: int = 0, qk_l2norm: bool = True,
-                    norm_eps: float = 1e-6, scale=1.0, stream=None):
+                    norm_eps: float = 1e-6, scale=1.0, out_gate=None, out_norm_weight=None,
+                    out_norm_eps: float = 1e-6, stream=None):
     """Decode step with the short convolution fused in.  x [N, 3 H d] (q | k | v
     projections of the token); conv_weight [3 H d, W]; conv_pool
-    [n_conv_slots, 3 H d, W-1]; g [N, H, d]; beta [N, H]; o [N, H, d]."""
+    [n_conv_slots, 3 H d, W-1]; g [N, H, d]; beta [N, H]; o [N, H, d];
+    out_gate [N, H, d] and out_norm_weight [d] (optional gated RMS norm of o)."""
     a = _decode_conv_args(x, conv_weight, conv_pool, conv_src_slot, conv_dst_slot, g, beta, o, state_pool,
-                          src_slot, dst_slot, conv_bias, act, qk_l2norm, norm_eps, scale)
+                          src_slot, dst_slot, conv_bias, act, qk_l2norm, norm_eps, scale, out_gate,
+                          out_norm_weight, out_norm_eps)
     _check(load_library().kda_decode_conv(ctypes.byref(a), _stream(stream)))
     return o
 
 
 def prepare_decode_conv(x, conv_weight, conv_pool, conv_src_slot, conv_dst_slot, g, beta, o, state_pool,
                         src_slot, dst_slot, *, conv_bias=None, act: int = 0, qk_l2norm: bool = True,
-                        norm_eps: float = 1e-6, scale=1.0) -> Prepared:
+                        norm_eps: float = 1e-6, scale=1.0, out_gate=None, out_norm_weight=None,
+                        out_norm_eps: float = 1e-6) -> Prepared:
     """kda_decode_conv with fixed buffers, as a Prepared call."""
     a = _decode_conv_args(x, conv_weight, conv_pool, conv_src_slot, conv_dst_slot, g, beta, o, state_pool,
-                          src_slot, dst_slot, conv_bias, act, qk_l2norm, norm_eps, scale)
+                          src_slot, dst_slot, conv_bias, act, qk_l2norm, norm_eps, scale, out_gate,
+                          out_norm_weight, out_norm_eps)
     return Prepared(load_library().kda_decode_conv, a,
                     (x, conv_weight, conv_pool, conv_src_slot, conv_dst_slot, g, beta, o, state_pool,
-                     src_slot, dst_slot, conv_bias))
+                     src_slot, dst_slot, conv_bias, out_gate, out_norm_weight))
 
 
 def kda_verify_conv(x, conv_weight, conv_pool, conv_src_slot, conv_dst_slot, g, beta, state_pool, src_slot,
                     dst_slot, *, o=None, accepted_len=None, committed_len_out=None, conv_bias=None,
-                    act: int = 0, qk_l2norm: bool = True, norm_eps: float = 1e-6, scale=1.0, stream=None):
+                    act: int = 0, qk_l2norm: bool = True, norm_eps: float = 1e-6, scale=1.0, out_gate=None,
+                    out_norm_weight=None, out_norm_eps: float = 1e-6, stream=None):
     """Speculative verify with the short convolution fused in.  x [N, T_spec,
     3 H d] (q | k | v projections of the tokens); g [N, T_spec, H, d]; beta
     [N, T_spec, H]; o [N, T_spec, H, d] or None; conv and state pools as
-    kda_decode_conv."""
+    kda_decode_conv; out_gate [N, T_spec, H, d] and out_norm_weight [d]
+    (optional gated RMS norm of every output)."""
     import torch
     _expect(x.dim() == 3 and g.dim() == 4 and beta.dim() == 3,
             "x [N, T_spec, 3 H d], g [N, T_spec, H, d], beta [N, T_spec, H]")
@@ -633,6 +663,9 @@ def kda_verify_conv(x, conv_weight, conv_pool, conv_src_slot, conv_dst_slot, g, 
     a.in_dtype = _dtype_code(x)
     a.out_dtype = _dtype_code(o) if o is not None else KDA_BF16
     a.scale = scale
+    if out_gate is not None:
+        _expect(out_gate.stride(0) == Ts * out_gate.stride(1), "out_gate: sequence stride must be T_spec tokens")
+    _out_gate_fields(a, out_gate, out_norm_weight, out_norm_eps, (N, Ts), H, d, x)
     _check(load_library().kda_verify_conv(ctypes.byref(a), _stream(stream)))
     return o
 

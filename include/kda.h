@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 1
+#define KDA_ABI_VERSION 2
 
 typedef enum kda_status {
     KDA_OK = 0,
@@ -356,6 +356,11 @@ int kda_decode(const kda_decode_args *args, kda_stream_t stream);
  *   qk_l2norm: q <- q / sqrt(|q|^2 + norm_eps), k likewise
  *   then the kda_decode step with g[s, h], beta[s, h]:
  *   S <- Diag(exp g) S;  S <- S + beta k (v - S^T k)^T;  o = scale S^T q.
+ *   With out_gate (the output gate the fused kernel folds in, section
+ *   "Separate Prefill/Decode Code Paths"; the pages name it without a
+ *   formula -- this library reads it as a gated RMS norm per head):
+ *   o <- o / sqrt(mean_c o[c]^2 + out_norm_eps) * out_norm_weight[c]
+ *        * sigmoid(out_gate[s, h, c])        (the mean over the d channels)
  *
  * Channels of x, weight, bias and the conv pool are ordered [q block | k
  * block | v block], each block [H, d] (C = 3 H d).  The conv state of the
@@ -369,10 +374,15 @@ int kda_decode(const kda_decode_args *args, kda_stream_t stream);
  *   conv_pool    [n_conv_slots, 3 H d, W-1] in_dtype
  *   g [n_seq, H, d], beta [n_seq, H] in_dtype; o [n_seq, H, d] out_dtype
  *   state_pool   fp32 [n_slots, H, d, d]
+ *   out_gate     [n_seq, H, d] in_dtype, row stride out_gate_stride (0 =
+ *                packed), or NULL (o as computed); out_norm_weight [d]
+ *                in_dtype, shared by the heads, required with out_gate
  * Errors: W outside 2..4 -> KDA_ERR_UNSUPPORTED; d not 16/32/64/128 ->
- * KDA_ERR_UNSUPPORTED; x, conv_weight, conv_pool, g, o or state_pool not
- * 16-byte aligned, or an x stride that breaks 16-byte rows -> KDA_ERR_ALIGN;
- * act not 0/1, qk_l2norm not 0/1 or norm_eps < 0 -> KDA_ERR_ARG.
+ * KDA_ERR_UNSUPPORTED; x, conv_weight, conv_pool, g, o, state_pool,
+ * out_gate or out_norm_weight not 16-byte aligned, or an x or out_gate
+ * stride that breaks 16-byte rows -> KDA_ERR_ALIGN; act not 0/1, qk_l2norm
+ * not 0/1, norm_eps or out_norm_eps < 0 -> KDA_ERR_ARG; out_gate without
+ * out_norm_weight -> KDA_ERR_NULL.
  * ---------------------------------------------------------------------- */
 typedef struct kda_decode_conv_args {
     size_t struct_size;          /* sizeof(kda_decode_conv_args) */
@@ -399,6 +409,11 @@ typedef struct kda_decode_conv_args {
     float norm_eps;              /* >= 0 */
     int32_t in_dtype, out_dtype;
     float scale;
+    const void *out_gate;        /* [n_seq, H, d] or NULL: no output gate / norm */
+    const void *out_norm_weight; /* [d]; required with out_gate */
+    int64_t out_gate_stride;     /* per sequence; 0 = packed (H d) */
+    float out_norm_eps;          /* >= 0 */
+    int32_t reserved;
 } kda_decode_conv_args;
 
 int kda_decode_conv(const kda_decode_conv_args *args, kda_stream_t stream);
@@ -418,6 +433,9 @@ int kda_decode_conv(const kda_decode_conv_args *args, kda_stream_t stream);
  *   x   [n_seq, T_spec, 3 H d] in_dtype, token stride x_stride (0 = packed;
  *       sequence stride T_spec * x_stride)
  *   g   [n_seq, T_spec, H, d], beta [n_seq, T_spec, H], o [n_seq, T_spec, H, d]
+ *   out_gate [n_seq, T_spec, H, d] (token stride out_gate_stride) or NULL:
+ *       every output position passes through the gated RMS norm of
+ *       kda_decode_conv
  *   other arguments as kda_decode_conv.
  * Errors as kda_decode_conv; T_spec outside 1..16 -> KDA_ERR_SHAPE.
  * ---------------------------------------------------------------------- */
@@ -450,6 +468,11 @@ typedef struct kda_verify_conv_args {
     int32_t in_dtype, out_dtype;
     float scale;
     int32_t reserved;
+    const void *out_gate;        /* [n_seq, T_spec, H, d] or NULL */
+    const void *out_norm_weight; /* [d]; required with out_gate */
+    int64_t out_gate_stride;     /* per token; 0 = packed (H d) */
+    float out_norm_eps;          /* >= 0 */
+    int32_t reserved2;
 } kda_verify_conv_args;
 
 int kda_verify_conv(const kda_verify_conv_args *args, kda_stream_t stream);

@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_struct_sizes(lib):
-    assert lib.kda_abi_version() == 1
+    assert lib.kda_abi_version() == 2
     for which, cls in enumerate([K.ConvArgs, K.PrefillArgs, K.DecodeArgs, K.VerifyArgs, K.DecodeConvArgs,
                                  K.VerifyConvArgs, K.PlanArgs]):
         assert lib.kda_args_sizeof(which) == ctypes.sizeof(cls), cls.__name__
@@ -97,6 +97,11 @@ def test_decode_conv_validation(lib):
     assert _call(lib, f, _decode_conv_args(x_stride=100)) == 2       # < 3 H d
     assert _call(lib, f, _decode_conv_args(x_stride=769)) == 4       # rows not 16-byte aligned
     assert b"aligned" in lib.kda_last_error()
+    fake = 1 << 20
+    assert _call(lib, f, _decode_conv_args(out_gate=fake)) == 1      # gate without norm weight
+    assert _call(lib, f, _decode_conv_args(out_gate=fake, out_norm_weight=fake, out_norm_eps=-1.0)) == 8
+    assert _call(lib, f, _decode_conv_args(out_gate=fake + 8, out_norm_weight=fake)) == 4
+    assert _call(lib, f, _decode_conv_args(out_gate=fake, out_norm_weight=fake, out_gate_stride=100)) == 2
 
 
 def test_verify_conv_validation(lib):
@@ -126,6 +131,8 @@ def test_verify_conv_validation(lib):
     assert _call(lib, f, args(W=5)) == 6
     assert _call(lib, f, args(act=3)) == 8
     assert _call(lib, f, args(x_stride=769)) == 4
+    assert _call(lib, f, args(out_gate=fake)) == 1
+    assert _call(lib, f, args(out_gate=fake, out_norm_weight=fake + 4)) == 4
 
 
 def test_decode_validation(lib):

@@ -36,7 +36,7 @@ def _case(N, H, d, W, dtype, seed):
 
 
 def _run(dev, x, w, bias, cst, g, b, init, *, act, norm, out_dtype, conv_src, in_place=False,
-         scale=1.0):
+         scale=1.0, gate=None, gw=None):
     N, C = x.shape
     H, d = g.shape[1], g.shape[2]
     W = w.shape[1]
@@ -53,12 +53,26 @@ def _run(dev, x, w, bias, cst, g, b, init, *, act, norm, out_dtype, conv_src, in
     o = torch.empty(N, H, d, dtype=out_dtype, device=dev)
     K.kda_decode_conv(x.to(dev), w.to(dev), cpool, csrc, cdst, g.to(dev), b.to(dev), o, pool, src, dst,
                       conv_bias=None if bias is None else bias.to(dev), act=act, qk_l2norm=norm,
-                      scale=scale)
+                      scale=scale, out_gate=gate, out_norm_weight=gw)
     torch.cuda.synchronize()
     return o, pool[dst.long()], cpool[cdst.long()]
 
 
-def _reference(orc, x, w, bias, cst, g, b, init, conv_src, *, act, norm, scale=1.0):
+def _gate(gen, shape, dtype, d):
+    """Output gate logits N(0, 1) and norm weights 1 + 0.1 N(0, 1)."""
+    z = torch.randn(*shape, generator=gen).to(dtype)
+    wt = (1.0 + 0.1 * torch.randn(d, generator=gen)).to(dtype)
+    return z, wt
+
+
+def _gated_bf16_max_abs(ref):
+    """Normalised outputs reach |o| ~ 4, where one bf16 rounding alone is up
+    to 2^-9 |o|: the element bound scales with the largest output (2^-7 of
+    it, one rounding plus the error carried in from the unnormalised o)."""
+    return max(U.MAX_ABS_TOL, 2.0 ** -7 * float(np.abs(ref).max()))
+
+
+def _reference(orc, x, w, bias, cst, g, b, init, conv_src, *, act, norm, scale=1.0, gate=None, gw=None):
     N = x.shape[0]
     H, d = g.shape[1], g.shape[2]
     hist = cst.float().numpy().copy()
@@ -66,7 +80,7 @@ def _reference(orc, x, w, bias, cst, g, b, init, conv_src, *, act, norm, scale=1
         if conv_src[s] < 0:
             hist[s] = 0.0
     return orc.kda_decode_conv(x, w, g, b, init.double().numpy(), hist, H=H, d=d, bias=bias,
-                               act=act, qk_l2norm=norm, scale=scale), hist
+                               act=act, qk_l2norm=norm, scale=scale, out_gate=gate, norm_weight=gw), hist
 
 
 def _check_conv_state(got, x, hist):
@@ -130,6 +144,42 @@ def test_decode_conv_fp32_small(dev, oracle64, d):
     _check_conv_state(cs, x, hist)
 
 
+def test_decode_conv_gated_norm_128(dev, oracle64):
+    """The output passes the gated RMS norm: 128 sequences x 1 token, H=16,
+    d=128, W=4, bf16 gate and weight, bf16 outputs."""
+    U.say("decode_conv gated norm 128 x H16 x d128")
+    N, H, d, W = 128, 16, 128, 4
+    x, w, bias, cst, g, b, init = _case(N, H, d, W, torch.bfloat16, seed=12)
+    z, wt = _gate(torch.Generator().manual_seed(312), (N, H, d), torch.bfloat16, d)
+    conv_src = list(range(N))
+    o, st, cs = _run(dev, x, w, bias, cst, g, b, init, act=1, norm=1, out_dtype=torch.bfloat16,
+                     conv_src=conv_src, gate=z.to(dev), gw=wt.to(dev))
+    ref, hist = _reference(oracle64, x, w, bias, cst, g, b, init, conv_src, act=1, norm=1, gate=z, gw=wt)
+    U.assert_close("o", U.to_np(o), ref["o"], mx=_gated_bf16_max_abs(ref["o"]))
+    U.assert_close("state", U.to_np(st), ref["state"])
+    _check_conv_state(cs, x, hist)
+
+
+@pytest.mark.parametrize("d", [16, 32, 64, 128])
+def test_decode_conv_gated_norm_fp32(dev, oracle64, d):
+    """Gated RMS norm with fp32 inputs and outputs, every head size, the gate
+    read with a padded token stride (a view into a wider buffer)."""
+    U.say(f"decode_conv gated norm fp32 d={d}")
+    N, H, W = 7, 3, 3
+    x, w, bias, cst, g, b, init = _case(N, H, d, W, torch.float32, seed=60 + d)
+    z, wt = _gate(torch.Generator().manual_seed(360 + d), (N, H, d), torch.float32, d)
+    wide = torch.zeros(N, H * d + 8, device=dev)
+    wide[:, :H * d] = z.reshape(N, H * d).to(dev)
+    zv = wide[:, :H * d].view(N, H, d)
+    conv_src = [s if s % 3 else -1 for s in range(N)]
+    o, st, cs = _run(dev, x, w, bias, cst, g, b, init, act=1, norm=1, out_dtype=torch.float32,
+                     conv_src=conv_src, gate=zv, gw=wt.to(dev), scale=d ** -0.5)
+    ref, hist = _reference(oracle64, x, w, bias, cst, g, b, init, conv_src, act=1, norm=1, gate=z, gw=wt,
+                           scale=d ** -0.5)
+    U.assert_close("o", U.to_np(o), ref["o"], rel=1e-5, mx=1e-5)
+    U.assert_close("state", U.to_np(st), ref["state"], rel=1e-5, mx=1e-5)
+
+
 def _verify_case(N, Ts, H, d, W, dtype, seed):
     wl = make_workload(4, n_seq=N, H=H, d=d, T=max(Ts, 8), seed=seed)
     gen = torch.Generator().manual_seed(2000 + seed)
@@ -140,7 +190,7 @@ def _verify_case(N, Ts, H, d, W, dtype, seed):
 
 
 def _run_verify(dev, x, w, cst, g, b, init, L, *, out_dtype, with_o=True, commit=True, conv_src=None,
-                act=1, norm=1, bias=None, state_src=None):
+                act=1, norm=1, bias=None, state_src=None, gate=None, gw=None):
     N, Ts, C = x.shape
     H, d = g.shape[2], g.shape[3]
     W = w.shape[1]
@@ -158,12 +208,13 @@ def _run_verify(dev, x, w, cst, g, b, init, L, *, out_dtype, with_o=True, commit
     clen = torch.full((N,), -7, dtype=torch.int32, device=dev)
     K.kda_verify_conv(x.to(dev), w.to(dev), cpool, csrc, dst, g.to(dev), b.to(dev), pool, src, dst, o=o,
                       accepted_len=acc, committed_len_out=clen if commit else None, act=act, qk_l2norm=norm,
-                      conv_bias=None if bias is None else bias.to(dev))
+                      conv_bias=None if bias is None else bias.to(dev), out_gate=gate, out_norm_weight=gw)
     torch.cuda.synchronize()
     return o, pool[N:], cpool[N:], clen, pool[:N], cpool[:N]
 
 
-def _verify_reference(orc, x, w, cst, g, b, init, L, conv_src, act=1, norm=1, bias=None, state_src=None):
+def _verify_reference(orc, x, w, cst, g, b, init, L, conv_src, act=1, norm=1, bias=None, state_src=None,
+                      gate=None, gw=None):
     N = x.shape[0]
     H, d = g.shape[2], g.shape[3]
     hist = cst.float().numpy().copy()
@@ -176,7 +227,8 @@ def _verify_reference(orc, x, w, cst, g, b, init, L, conv_src, act=1, norm=1, bi
             if state_src[s] < 0:
                 S0[s] = 0.0
     return orc.kda_verify_conv(x, w, g, b, S0, hist, L, H=H, d=d, act=act, qk_l2norm=norm,
-                               bias=None if bias is None else bias.float().numpy()), hist
+                               bias=None if bias is None else bias.float().numpy(), out_gate=gate,
+                               norm_weight=gw), hist
 
 
 def test_verify_conv_batched_128x8(dev, oracle64):
@@ -276,3 +328,36 @@ def test_verify_conv_fp32_d128_16_tokens(dev, oracle64):
     U.assert_close("committed", U.to_np(st), ref["committed"], rel=1e-5, mx=1e-5)
     assert np.array_equal(cs.cpu().numpy(), ref["conv_state"].astype(np.float32))
     assert clen.cpu().tolist() == L
+
+
+def test_verify_conv_gated_norm_128x8(dev, oracle64):
+    """Every verified output passes the gated RMS norm: 128 sequences x 8
+    tokens, H=16, d=128, bf16; the commit is unaffected by the gate."""
+    U.say("verify_conv gated norm 128 x 8 x H16 x d128")
+    N, Ts, H, d, W = 128, 8, 16, 128, 4
+    x, w, cst, g, b, init = _verify_case(N, Ts, H, d, W, torch.bfloat16, seed=44)
+    z, wt = _gate(torch.Generator().manual_seed(344), (N, Ts, H, d), torch.bfloat16, d)
+    L = torch.randint(0, Ts + 1, (N,), generator=torch.Generator().manual_seed(8)).tolist()
+    o, st, cs, clen, _, _ = _run_verify(dev, x, w, cst, g, b, init, L, out_dtype=torch.bfloat16,
+                                        gate=z.to(dev), gw=wt.to(dev))
+    ref, _ = _verify_reference(oracle64, x, w, cst, g, b, init, L, list(range(N)), gate=z, gw=wt)
+    U.assert_close("o", U.to_np(o), ref["o"], mx=_gated_bf16_max_abs(ref["o"]))
+    U.assert_close("committed", U.to_np(st), ref["committed"])
+    assert np.array_equal(cs.to("cpu", torch.float32).numpy(), ref["conv_state"].astype(np.float32))
+    assert clen.cpu().tolist() == L
+
+
+@pytest.mark.parametrize("d,Ts", [(16, 3), (64, 5), (128, 16)])
+def test_verify_conv_gated_norm_fp32(dev, oracle64, d, Ts):
+    """Gated RMS norm on the verify outputs with fp32 inputs and outputs,
+    small and large heads, up to the longest window."""
+    U.say(f"verify_conv gated norm fp32 d={d} T={Ts}")
+    N, H, W = 5, 2, 4
+    x, w, cst, g, b, init = _verify_case(N, Ts, H, d, W, torch.float32, seed=70 + d)
+    z, wt = _gate(torch.Generator().manual_seed(370 + d), (N, Ts, H, d), torch.float32, d)
+    L = [Ts, 1, 0, Ts - 1, 2]
+    o, st, _, _, _, _ = _run_verify(dev, x, w, cst, g, b, init, L, out_dtype=torch.float32,
+                                    gate=z.to(dev), gw=wt.to(dev))
+    ref, _ = _verify_reference(oracle64, x, w, cst, g, b, init, L, list(range(N)), gate=z, gw=wt)
+    U.assert_close("o", U.to_np(o), ref["o"], rel=1e-5, mx=1e-5)
+    U.assert_close("committed", U.to_np(st), ref["committed"], rel=1e-5, mx=1e-5)
