@@ -5,9 +5,10 @@ Default workload: batched decode (128 sequences x 1 token, H=16,
 d_k=d_v=128, bf16 inputs, fp32 recurrent state, short conv W=4 over the
 3*H*d q/k/v channels).  One step = one kda_decode_conv launch: the conv
 (+ SiLU) of the token's q/k/v projections with the carried conv history,
-per-head q/k L2 normalisation and the recurrence, both states advanced in
-place.  The recurrent state rotates over 4 pools of 128 MiB so it cannot be
-served from the 256 MB Infinity Cache.
+per-head q/k L2 normalisation, the recurrence and the sigmoid-gated RMS
+norm of the output, both states advanced in place.  The recurrent state
+rotates over 4 pools of 128 MiB so it cannot be served from the 256 MB
+Infinity Cache.
 
 Prints ONE JSON line.  ``value`` = recurrent-state bytes read + written per
 step / step time (GB/s).  ``roofline`` = the fused kernel's algorithmic
@@ -134,9 +135,11 @@ def pmc_pass(torch, K, make_workload, long=False):
     x, cw = wlc.conv_x.to(dev), wlc.conv_w.to(dev)
     cpool = wlc.conv_state.to(dev).clone()
     cs = torch.arange(N, dtype=torch.int32, device=dev)
+    z, gw = (t.to(dev) for t in out_gate_inputs(torch, (N, H, D), D, 401))
     for i in range(8):
         s_ = torch.arange((i % P) * N, (i % P + 1) * N, dtype=torch.int32, device=dev)
-        K.kda_decode_conv(x, cw, cpool, cs, cs, g, bt, o, pool, s_, s_, act=1, qk_l2norm=True)
+        K.kda_decode_conv(x, cw, cpool, cs, cs, g, bt, o, pool, s_, s_, act=1, qk_l2norm=True, out_gate=z,
+                          out_norm_weight=gw)
     del pool
     bench_verify_secondary(torch, K, make_workload, dev, n=2, warm=2)   # 4 verify + 4 fused verify calls
     torch.cuda.empty_cache()
@@ -336,6 +339,15 @@ def cpu_info():
 
 
 # ---------------------------------------------------------------- decode
+def out_gate_inputs(torch, shape, D, seed):
+    """Output gate logits N(0, 1) and the shared norm weight 1 + 0.1 N(0, 1)
+    (bf16, on the host)."""
+    gen = torch.Generator().manual_seed(seed)
+    z = torch.randn(*shape, generator=gen).to(torch.bfloat16)
+    w = (1.0 + 0.1 * torch.randn(D, generator=gen)).to(torch.bfloat16)
+    return z, w
+
+
 def bench_decode(args, torch, K, make_workload):
     dev = torch.device("cuda:0")
     N, H, D, W = 128, 16, 128, 4
@@ -359,10 +371,13 @@ def bench_decode(args, torch, K, make_workload):
     conv_call = K.prepare_conv_short(x, cw, cu, cpool, cslots, cslots, y=y)
     dec_calls = [K.prepare_decode(q, k, v, g, b, o, pool, s_, s_) for s_ in slot_sets]
     # the fused step: conv (+ SiLU) of the token's q / k / v projections,
-    # per-head q / k L2 normalisation and the recurrence in one launch; the
-    # conv history advances in place like the state
+    # per-head q / k L2 normalisation, the recurrence and the gated RMS norm
+    # of the output in one launch; the conv history advances in place like
+    # the state
+    z_h, gw_h = out_gate_inputs(torch, (N, H, D), D, 401)
+    z, gw = z_h.to(dev), gw_h.to(dev)
     fused_calls = [K.prepare_decode_conv(x, cw, cpool, cslots, cslots, g, b, o, pool, s_, s_, act=1,
-                                         qk_l2norm=True) for s_ in slot_sets]
+                                         qk_l2norm=True, out_gate=z, out_norm_weight=gw) for s_ in slot_sets]
 
     def timed(step_fn, nsteps, nwarm):
         """Per-step time over nsteps back-to-back steps, then (in a second
@@ -410,9 +425,10 @@ def bench_decode(args, torch, K, make_workload):
 
     state_bytes = N * H * D * D * 4 * 2                   # read + write
     # fused step per launch: state r+w, the token's q/k/v projections, the
-    # conv history r+w, g and beta in, o out (bf16), the conv taps once
+    # conv history r+w, g, beta and the output gate in, o out (bf16), the
+    # conv taps and the norm weight once
     conv_hist_bytes = N * C * (W - 1) * 2 * 2
-    io_bytes = N * C * 2 + N * H * (D * 2 + 2 + D * 2) + C * W * 2
+    io_bytes = N * C * 2 + N * H * (D * 2 + 2 + D * 2 + D * 2) + C * W * 2 + D * 2
     alg_bytes = state_bytes + conv_hist_bytes + io_bytes
     value = state_bytes / (ms_step * 1e-3) / 1e9
     achieved = alg_bytes / (k_ms * 1e-3) / 1e9
@@ -478,12 +494,13 @@ def bench_decode(args, torch, K, make_workload):
 
     cpu = None
     if not args.no_cpu:
-        cpu = cpu_decode(args, wl, state_bytes)
+        cpu = cpu_decode(args, wl, state_bytes, z_h, gw_h)
     cfg = {"workload": "batched decode: 128 seqs x 1 token, H=16, d_k=d_v=128, conv W=4 "
                        "over 6144 q/k/v channels, bf16 inputs, fp32 state",
            "n_seq": N, "H": H, "d": D, "conv_W": W, "state_pools_rotated": P,
-           "step": "kda_decode_conv (conv + SiLU of the q/k/v projections, q/k L2 norm, recurrence; "
-                   "one launch)", "value_counts": "recurrent state read+write"}
+           "step": "kda_decode_conv (conv + SiLU of the q/k/v projections, q/k L2 norm, recurrence, "
+                   "sigmoid-gated RMS norm of the output; one launch)",
+           "value_counts": "recurrent state read+write"}
     return {"metric": METRIC, "value": round(value, 1), "unit": "GB/s", "ms_per_step": ms_step,
             "dtype": "f32", "config": cfg, "roofline": roof, "cpu_baseline": cpu,
             "secondary": secondary, "wall_s": round(wall, 3)}
@@ -593,20 +610,23 @@ def bench_verify_secondary(torch, K, make_workload, dev, n=200, warm=10, cpu_sec
     cw = cw.to(dev)
     cpool = cst.to(dev)
     cs = torch.arange(N, dtype=torch.int32, device=dev)
+    z, gw = (t.to(dev) for t in out_gate_inputs(torch, (N, Ts, H, D), D, 404))
     for i in range(warm):
         s = slot_sets[i % P]
-        K.kda_verify_conv(x, cw, cpool, cs, cs, g, b, pool, s, s, o=o, accepted_len=L, act=1)
+        K.kda_verify_conv(x, cw, cpool, cs, cs, g, b, pool, s, s, o=o, accepted_len=L, act=1, out_gate=z,
+                          out_norm_weight=gw)
     torch.cuda.synchronize()
     a_.record()
     for i in range(n):
         s = slot_sets[i % P]
-        K.kda_verify_conv(x, cw, cpool, cs, cs, g, b, pool, s, s, o=o, accepted_len=L, act=1)
+        K.kda_verify_conv(x, cw, cpool, cs, cs, g, b, pool, s, s, o=o, accepted_len=L, act=1, out_gate=z,
+                          out_norm_weight=gw)
     b2.record()
     torch.cuda.synchronize()
     us2 = a_.elapsed_time(b2) / n * 1e3
-    io2 = N * Ts * (C * 2 + H * (D * 2 + 2 + D * 2)) + N * C * (W - 1) * 2 * 2 + C * W * 2
-    res["fused_conv"] = {"call": "kda_verify_conv (conv + SiLU + q/k norm + verify, state and conv history "
-                                 "committed at L)", "us": round(us2, 2),
+    io2 = N * Ts * (C * 2 + H * (D * 2 + 2 + D * 2 + D * 2)) + N * C * (W - 1) * 2 * 2 + C * W * 2 + D * 2
+    res["fused_conv"] = {"call": "kda_verify_conv (conv + SiLU + q/k norm + verify + gated output norm, "
+                                 "state and conv history committed at L)", "us": round(us2, 2),
                          "state_GB_s": round(state_bytes / us2 / 1e3, 1),
                          "alg_GB_s": round((state_bytes + io2) / us2 / 1e3, 1),
                          "hbm_frac": round((state_bytes + io2) / us2 / 1e3 / HBM_PEAK_GBS, 4)}
@@ -902,7 +922,7 @@ def cpu_verify(wl, state_bytes, cpu_seconds):
                       f"{dt:.1f} s"}
 
 
-def cpu_decode(args, wl, state_bytes):
+def cpu_decode(args, wl, state_bytes, z, gw):
     import numpy as np
     import oracle
     orc = oracle.load("f64")
@@ -916,7 +936,8 @@ def cpu_decode(args, wl, state_bytes):
     reps = 0
     t0 = time.perf_counter()
     while True:
-        orc.kda_decode_conv(cx, cw, g, b, init, cs, H=wl.H, d=wl.dk, act=1, qk_l2norm=1)
+        orc.kda_decode_conv(cx, cw, g, b, init, cs, H=wl.H, d=wl.dk, act=1, qk_l2norm=1, out_gate=z,
+                            norm_weight=gw)
         reps += 1
         if time.perf_counter() - t0 > args.cpu_seconds:
             break
@@ -924,7 +945,7 @@ def cpu_decode(args, wl, state_bytes):
     return {"value": round(state_bytes * reps / dt / 1e9, 3), "unit": "GB/s", "cores": orc.threads(),
             "kind": "oracle", "cpu": cpu_info(),
             "sample": f"{reps} whole fused decode steps (conv + SiLU + q/k norm + 128 seqs x 16 heads "
-                      f"x 1 token, fp64 oracle), "
+                      f"x 1 token + gated output norm, fp64 oracle), "
                       f"{dt:.1f} s"}
 
 

@@ -691,15 +691,6 @@ __global__ void __launch_bounds__(64 * d128::Shape<CPW>::NW) decode128_kernel(co
   const bool has_src = src >= 0 && src < p.n_slots;
   const bool has_dst = dst >= 0 && dst < p.n_slots;
 
-  // The output gate and norm weight (gated output only): requested first by
-  // the lanes that apply them at the end, put in LDS with the conv results.
-  float gz[4] = {0.f, 0.f, 0.f, 0.f}, gw[4] = {0.f, 0.f, 0.f, 0.f};
-  const bool gate_lane = CONV && p.ogate && threadIdx.x < D / 4;
-  if (gate_lane) {
-    io<Tin>::ld4(static_cast<const Tin*>(p.ogate) + static_cast<int64_t>(s) * p.ogate_stride +
-                     static_cast<int64_t>(h) * D + 4 * threadIdx.x, gz);
-    io<Tin>::ld4(static_cast<const Tin*>(p.onorm_w) + 4 * threadIdx.x, gw);
-  }
   // The convolution (conv waves only, before their own state loads: their
   // conv data and their state slice are never live together, which keeps
   // the register count of the 16-wave workgroup low).  Item t < NCI owns V
@@ -780,6 +771,20 @@ __global__ void __launch_bounds__(64 * d128::Shape<CPW>::NW) decode128_kernel(co
   ld_vec<Tin, RPL>(static_cast<const Tin*>(p.g) + static_cast<int64_t>(s) * p.g_stride + static_cast<int64_t>(h) * D + row0,
                    ar);
   const float beta = io<Tin>::ld(static_cast<const Tin*>(p.beta) + static_cast<int64_t>(s) * p.beta_stride + h);
+  // The output gate and norm weight (gated output only), put in LDS with the
+  // conv results by the first wave that runs no conv, after its own state
+  // loads: their registers are then never live across the conv, whose
+  // register peak sets the kernel's occupancy.
+  constexpr int GATE_WAVE = (NCI + 63) / 64;
+  static_assert(!CONV || GATE_WAVE < NW, "a wave without conv items");
+  const int gt = static_cast<int>(threadIdx.x) - 64 * GATE_WAVE;
+  const bool gate_lane = CONV && p.ogate && gt >= 0 && gt < D / 4;
+  float gz[4] = {0.f, 0.f, 0.f, 0.f}, gw[4] = {0.f, 0.f, 0.f, 0.f};
+  if (gate_lane) {
+    io<Tin>::ld4(static_cast<const Tin*>(p.ogate) + static_cast<int64_t>(s) * p.ogate_stride +
+                     static_cast<int64_t>(h) * D + 4 * gt, gz);
+    io<Tin>::ld4(static_cast<const Tin*>(p.onorm_w) + 4 * gt, gw);
+  }
   if constexpr (!CONV) {
     ld_vec<Tin, RPL>(static_cast<const Tin*>(p.k) + static_cast<int64_t>(s) * p.k_stride + static_cast<int64_t>(h) * D + row0,
                      kr);
@@ -788,8 +793,8 @@ __global__ void __launch_bounds__(64 * d128::Shape<CPW>::NW) decode128_kernel(co
     io<Tin>::ld4(static_cast<const Tin*>(p.v) + static_cast<int64_t>(s) * p.v_stride + static_cast<int64_t>(h) * D + col, vc);
   } else {
     if (gate_lane) {
-      *reinterpret_cast<float4*>(&s_gz[4 * threadIdx.x]) = make_float4(gz[0], gz[1], gz[2], gz[3]);
-      *reinterpret_cast<float4*>(&s_gw[4 * threadIdx.x]) = make_float4(gw[0], gw[1], gw[2], gw[3]);
+      *reinterpret_cast<float4*>(&s_gz[4 * gt]) = make_float4(gz[0], gz[1], gz[2], gz[3]);
+      *reinterpret_cast<float4*>(&s_gw[4 * gt]) = make_float4(gw[0], gw[1], gw[2], gw[3]);
     }
     __syncthreads();
     float inv_q = 1.f, inv_k = 1.f;
