@@ -201,6 +201,40 @@ class Oracle:
         return y, ns
 
 
+    # -- prefill with the short convolution in front --------------------------
+    def kda_prefill_conv(self, x, w, g, beta, cu_seqlens, *, H, d, bias=None, act=0, conv_state=None,
+                         has_conv_state=None, qk_l2norm=1, norm_eps=1e-6, operand_dtype="bf16",
+                         init=None, has_init=None, start_pos=None, scale=1.0, ckpt_interval=0):
+        """The prefill of a packed batch from the tokens' raw projections.
+
+        x [T, 3 H d] (channels ordered q block, k block, v block, each
+        [H, d]); w [3 H d, W]; bias [3 H d] or None; conv_state [N, 3 H d,
+        W-1] and has_conv_state [N] (0 = no history) or None; g [T, H, d];
+        beta [T, H]; init / has_init / start_pos / ckpt_interval as
+        :meth:`kda_varlen`.
+
+        Per sequence: y = conv(history ++ tokens) (+ SiLU when act == 1) as
+        :meth:`conv_short`, unrounded; q, k, v from y by :func:`conv_operands`
+        (per-head normalisation of q and k, then one rounding to the
+        recurrence's input type); then :meth:`kda_varlen`.  The new conv
+        history of each sequence is the last W-1 raw inputs of history ++
+        tokens.
+
+        Returns the dict of :meth:`kda_varlen` plus conv_state [N, 3 H d, W-1]
+        and the operands q, k, v [T, H, d] (float32)."""
+        xa = np.asarray(_as_f32(x), np.float32)
+        T, C = xa.shape
+        if C != 3 * H * d:
+            raise ValueError("x must have 3 * H * d channels")
+        y, ns = self.conv_short(xa, w, cu_seqlens, bias=bias, act=act, state=conv_state,
+                                has_state=has_conv_state)
+        q, k, v = conv_operands(y, H, d, qk_l2norm, norm_eps, operand_dtype)
+        res = self.kda_varlen(q, k, v, g, beta, cu_seqlens, init=init, has_init=has_init,
+                              start_pos=start_pos, scale=scale, ckpt_interval=ckpt_interval)
+        res["conv_state"] = ns
+        res["q"], res["k"], res["v"] = q, k, v
+        return res
+
     # -- fused decode step -------------------------------------------------
     def kda_decode_conv(self, x, w, g, beta, init, conv_state, *, H, d, bias=None, act=0,
                         qk_l2norm=1, norm_eps=1e-6, scale=1.0, out_gate=None, norm_weight=None,
@@ -292,6 +326,32 @@ class Oracle:
             out["o"] = gated_rmsnorm(res["o"], out_gate, norm_weight, out_norm_eps)
         out["conv_state"] = ns
         return out
+
+
+def conv_operands(y, H, d, qk_l2norm, norm_eps, operand_dtype):
+    """q, k, v of the chunked prefill from the conv output y [T, 3 H d]
+    (fp64): the three channel blocks, per head; q and k divided by
+    sqrt(|.|^2 + eps) per token and head when qk_l2norm; then each rounded
+    to the recurrence's input type ("bf16": round to nearest even by torch's
+    conversion, "f32": to float32).  Returns three [T, H, d] float32 arrays."""
+    import torch
+    T = y.shape[0]
+    y = np.asarray(y, np.float64).reshape(T, 3, H, d)
+    q, k, v = y[:, 0], y[:, 1], y[:, 2]
+    if qk_l2norm:
+        q = q / np.sqrt((q * q).sum(-1, keepdims=True) + norm_eps)
+        k = k / np.sqrt((k * k).sum(-1, keepdims=True) + norm_eps)
+    out = []
+    for t in (q, k, v):
+        t32 = np.ascontiguousarray(t, np.float32)
+        if operand_dtype == "bf16":
+            # fp64 -> fp32 -> bf16: the second rounding decides unless the
+            # fp64 value lies within 2^-24 relative of a bf16 midpoint
+            t32 = torch.from_numpy(t32).to(torch.bfloat16).float().numpy()
+        elif operand_dtype != "f32":
+            raise ValueError("operand_dtype must be 'bf16' or 'f32'")
+        out.append(t32)
+    return out
 
 
 def gated_rmsnorm(o, z, weight, eps=1e-6):

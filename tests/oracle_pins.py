@@ -435,6 +435,111 @@ def pin_output_gate(orc):
     assert np.array_equal(gated["state"], plain["state"])
 
 
+def prefill_conv_case(seed, lengths=(6, 1, 9), H=2, d=5, W=4):
+    """A packed batch of raw projections: sequence 0 with conv history and
+    an initial state, sequence 1 (one token) with history only, sequence 2
+    with neither."""
+    r = _rng(seed)
+    C = 3 * H * d
+    T = sum(lengths)
+    N = len(lengths)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    x = r.standard_normal((T, C)).astype(np.float32)
+    w = r.uniform(-0.5, 0.5, (C, W)).astype(np.float32)
+    bias = (0.1 * r.standard_normal(C)).astype(np.float32)
+    cst = r.standard_normal((N, C, W - 1)).astype(np.float32)
+    has_c = np.array([1, 1, 0][:N], np.int32)
+    g = (-np.log1p(np.exp(-r.standard_normal((T, H, d))))).astype(np.float32)
+    beta = (1 / (1 + np.exp(-r.standard_normal((T, H))))).astype(np.float32)
+    S0 = r.standard_normal((N, H, d, d)) * 0.5
+    has_s = np.array([1, 0, 0][:N], np.int32)
+    return x, w, bias, cst, has_c, g, beta, S0, has_s, cu
+
+
+def pin_prefill_conv(orc):
+    """Prefill from raw projections: with the current-token tap alone and no
+    activation or normalisation it is the plain prefill of the projections'
+    blocks, bit for bit; stepped token by token through the fused decode step
+    (a separately written composition) it gives every output, the final state
+    and the conv history; split at a token and resumed from the carried conv
+    history and state it equals the continuous run bit for bit; positive
+    scalings of the q and k projections change nothing under normalisation;
+    bf16 operands are bf16 values within half a bf16 unit of the unrounded
+    ones."""
+    tol = max(_tol(orc) * 10, 1e-6)
+    H, d, W = 2, 5, 4
+    x, w, bias, cst, has_c, g, beta, S0, has_s, cu = prefill_conv_case(81, H=H, d=d, W=W)
+    T, C = x.shape
+    N = cu.size - 1
+    # current-token tap only: the blocks of x are q, k, v
+    w1 = np.zeros_like(w)
+    w1[:, W - 1] = 1
+    a = orc.kda_prefill_conv(x, w1, g, beta, cu, H=H, d=d, act=0, conv_state=cst, has_conv_state=has_c,
+                             qk_l2norm=0, operand_dtype="f32", init=S0, has_init=has_s, scale=0.6)
+    xb = x.reshape(T, 3, H, d)
+    ref = orc.kda_varlen(xb[:, 0], xb[:, 1], xb[:, 2], g, beta, cu, init=S0, has_init=has_s, scale=0.6)
+    assert np.array_equal(a["o"], ref["o"]) and np.array_equal(a["final"], ref["final"])
+    # the new history: the last W-1 raw inputs of history ++ tokens
+    for s in range(N):
+        hist = cst[s] if has_c[s] else np.zeros_like(cst[s])
+        full = np.concatenate([hist, x[cu[s]:cu[s + 1]].T], axis=1)
+        assert np.array_equal(a["conv_state"][s], full[:, -(W - 1):])
+    # token by token through the fused decode step
+    res = orc.kda_prefill_conv(x, w, g, beta, cu, H=H, d=d, bias=bias, act=1, conv_state=cst,
+                               has_conv_state=has_c, qk_l2norm=1, operand_dtype="f32", init=S0,
+                               has_init=has_s, scale=0.6)
+    for s in range(N):
+        S = S0[s:s + 1] if has_s[s] else np.zeros_like(S0[s:s + 1])
+        hist = (cst[s:s + 1] if has_c[s] else np.zeros_like(cst[s:s + 1])).astype(np.float32)
+        for t in range(cu[s], cu[s + 1]):
+            step = orc.kda_decode_conv(x[t:t + 1], w, g[t:t + 1], beta[t:t + 1], S, hist, H=H, d=d,
+                                       bias=bias, act=1, qk_l2norm=1, scale=0.6)
+            np.testing.assert_allclose(res["o"][t], step["o"][0], rtol=tol, atol=tol)
+            S = step["state"]
+            hist = step["conv_state"].astype(np.float32)
+        np.testing.assert_allclose(res["final"][s], S[0], rtol=tol, atol=tol)
+        assert np.array_equal(res["conv_state"][s], hist[0].astype(np.float64))
+    # split sequence 2 after 4 tokens and resume
+    p = int(cu[2]) + 4
+    one = orc.kda_prefill_conv(x[cu[2]:p], w, g[cu[2]:p], beta[cu[2]:p], np.array([0, 4], np.int32), H=H,
+                               d=d, bias=bias, act=1, qk_l2norm=1)
+    two = orc.kda_prefill_conv(x[p:cu[3]], w, g[p:cu[3]], beta[p:cu[3]],
+                               np.array([0, cu[3] - p], np.int32), H=H, d=d, bias=bias, act=1,
+                               conv_state=one["conv_state"].astype(np.float32), qk_l2norm=1,
+                               init=one["final"], start_pos=np.array([4], np.int32))
+    full = orc.kda_prefill_conv(x[cu[2]:cu[3]], w, g[cu[2]:cu[3]], beta[cu[2]:cu[3]],
+                                np.array([0, cu[3] - cu[2]], np.int32), H=H, d=d, bias=bias, act=1,
+                                qk_l2norm=1)
+    assert np.array_equal(np.concatenate([one["o"], two["o"]]), full["o"])
+    assert np.array_equal(two["final"], full["final"])
+    assert np.array_equal(two["conv_state"], full["conv_state"])
+    # normalisation: positive scalings of the q and k projections (linear
+    # conv, no activation, no bias, eps = 0) leave everything unchanged
+    b0 = orc.kda_prefill_conv(x, w, g, beta, cu, H=H, d=d, conv_state=cst, has_conv_state=has_c,
+                              qk_l2norm=1, norm_eps=0.0, operand_dtype="f32")
+    xs = x.copy().reshape(T, 3, H * d)
+    cs = cst.copy().reshape(N, 3, H * d, W - 1)
+    xs[:, 0] *= 3.0
+    cs[:, 0] *= 3.0
+    xs[:, 1] *= 0.2
+    cs[:, 1] *= 0.2
+    b1 = orc.kda_prefill_conv(xs.reshape(T, C), w, g, beta, cu, H=H, d=d, conv_state=cs.reshape(N, C, W - 1),
+                              has_conv_state=has_c, qk_l2norm=1, norm_eps=0.0, operand_dtype="f32")
+    np.testing.assert_allclose(b1["o"], b0["o"], rtol=tol, atol=tol)
+    np.testing.assert_allclose(b1["final"], b0["final"], rtol=tol, atol=tol)
+    # bf16 operands
+    r16 = orc.kda_prefill_conv(x, w, g, beta, cu, H=H, d=d, bias=bias, act=1, conv_state=cst,
+                               has_conv_state=has_c, qk_l2norm=1, operand_dtype="bf16")
+    for name in ("q", "k", "v"):
+        o16, o32 = r16[name].astype(np.float64), res[name].astype(np.float64)
+        hi = (r16[name].view(np.uint32) & 0xFFFF0000).view(np.float32)
+        assert np.array_equal(r16[name], hi), f"{name}: not bf16 values"
+        # nearest: within half a unit in the last place of bf16 (8
+        # significant bits) at the operand's binade
+        half_ulp = np.ldexp(1.0, np.floor(np.log2(np.abs(o32) + 1e-300)).astype(int) - 8)
+        assert np.all(np.abs(o16 - o32) <= half_ulp), name
+
+
 ALL_PINS = [pin_bruteforce, pin_readback, pin_pure_decay, pin_linearity, pin_resume,
             pin_varlen_independent, pin_verify, pin_ckpt_positions, pin_conv, pin_decode_conv,
-            pin_verify_conv, pin_output_gate]
+            pin_verify_conv, pin_output_gate, pin_prefill_conv]

@@ -64,3 +64,48 @@ def test_output_gate_pin_catches_planted_mistake(planted, oracle64, monkeypatch)
     monkeypatch.setattr(oracle, "gated_rmsnorm", planted)
     with pytest.raises(AssertionError):
         P.pin_output_gate(oracle64)
+
+
+def _planted_conv_operands():
+    """Plausible mistakes in forming the prefill's q, k, v from the conv
+    output (each a function with the signature of oracle.conv_operands)."""
+    import numpy as np
+
+    real = oracle.conv_operands
+
+    def swap_qk(y, H, d, qk_l2norm, norm_eps, operand_dtype):
+        q, k, v = real(y, H, d, qk_l2norm, norm_eps, operand_dtype)
+        return k, q, v
+
+    def blocks_reversed(y, H, d, qk_l2norm, norm_eps, operand_dtype):
+        T = y.shape[0]
+        yr = np.asarray(y).reshape(T, 3, H * d)[:, ::-1].reshape(T, -1)
+        return real(yr, H, d, qk_l2norm, norm_eps, operand_dtype)
+
+    def v_normalised(y, H, d, qk_l2norm, norm_eps, operand_dtype):
+        q, k, v = real(y, H, d, qk_l2norm, norm_eps, operand_dtype)
+        if qk_l2norm:
+            v = (v / np.sqrt((v.astype(np.float64) ** 2).sum(-1, keepdims=True) + norm_eps)).astype(np.float32)
+        return q, k, v
+
+    def norm_over_heads(y, H, d, qk_l2norm, norm_eps, operand_dtype):
+        q, k, v = real(y, H, d, 0, norm_eps, operand_dtype)
+        if qk_l2norm:
+            T = q.shape[0]
+            q = (q / np.sqrt((q.astype(np.float64) ** 2).reshape(T, -1).sum(-1)[:, None, None] + norm_eps))
+            k = (k / np.sqrt((k.astype(np.float64) ** 2).reshape(T, -1).sum(-1)[:, None, None] + norm_eps))
+        return q.astype(np.float32), k.astype(np.float32), v
+
+    def no_rounding(y, H, d, qk_l2norm, norm_eps, operand_dtype):
+        return real(y, H, d, qk_l2norm, norm_eps, "f32")
+
+    return [swap_qk, blocks_reversed, v_normalised, norm_over_heads, no_rounding]
+
+
+@pytest.mark.parametrize("planted", _planted_conv_operands(), ids=lambda f: f.__name__)
+def test_prefill_conv_pin_catches_planted_mistake(planted, oracle64, monkeypatch):
+    """Each planted mistake in the prefill's operand forming fails
+    pin_prefill_conv."""
+    monkeypatch.setattr(oracle, "conv_operands", planted)
+    with pytest.raises(AssertionError):
+        P.pin_prefill_conv(oracle64)
