@@ -20,7 +20,9 @@ the same workload (a bounded number of whole steps), timed on the host cores.
 ``roofline`` and ``cpu_baseline``: speculative verify (128 x 8 tokens), the
 16-sequence varlen prefill, the 1M-token prefill (oracle resumed from the
 GPU's checkpoints on a sample of segments, plus a continuous 65,536-token
-run), the short conv at prefill scale, and the device checkpoint planner.
+run), the short conv at prefill scale, the varlen prefill from raw q/k/v
+projections (conv + SiLU + q/k norm + prefill in one call), and the device
+checkpoint planner.
 
 ``--workload prefill|long`` makes a prefill workload the main line.
 """
@@ -144,6 +146,9 @@ def pmc_pass(torch, K, make_workload, long=False):
     bench_verify_secondary(torch, K, make_workload, dev, n=2, warm=2)   # 4 verify + 4 fused verify calls
     torch.cuda.empty_cache()
     bench_prefill_varlen(torch, K, make_workload, dev, iters=PMC_PREFILL_CALLS - 2)   # + 2 warm-up calls
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    bench_prefill_conv(torch, K, make_workload(2), dev, iters=1)   # 3 conv + 6 prefill launches
     torch.cuda.synchronize()
     if long:
         torch.cuda.empty_cache()
@@ -488,7 +493,10 @@ def bench_decode(args, torch, K, make_workload):
         secondary["prefill_varlen"] = bench_prefill_varlen(torch, K, make_workload, dev, iters=10, wl=wl2,
                                                            cpu_seconds=cs)
         secondary["conv_prefill_scale"] = bench_conv_prefill(torch, K, wl2, dev)
+        torch.cuda.empty_cache()
+        secondary["prefill_conv"] = bench_prefill_conv(torch, K, wl2, dev, cpu_seconds=cs)
         del wl2
+        torch.cuda.empty_cache()
         secondary["prefill_long_1m"] = bench_prefill_long(
             torch, K, make_workload, dev, cpu_segments=0 if args.no_cpu else args.long_cpu_segments)
 
@@ -708,8 +716,8 @@ def prefill_roofline(kernel, T, ms, counters_key, traffic_key):
 
 def bench_conv_prefill(torch, K, wl, dev, iters=20):
     """kda_conv_short at prefill scale: the varlen workload's 16 sequences
-    (140,625 tokens) over the 3 H d = 6,144 q/k/v channels, W = 4, bf16,
-    carried conv history read from and written to per-sequence slots.
+    (140,625 tokens) over the 3 H d = 6,144 q/k/v channels, W = 4 with SiLU,
+    bf16, carried conv history read from and written to per-sequence slots.
     Algorithmic bytes: x in and y out (2 B each per element), the history
     read and written, the taps."""
     from hybrid_recurrent_serving_amd.inputs import draw_conv
@@ -723,7 +731,7 @@ def bench_conv_prefill(torch, K, wl, dev, iters=20):
     dst = src + N
     cu = wl.cu_seqlens.to(dev)
     y = torch.empty_like(x)
-    call = K.prepare_conv_short(x, cw, cu, cpool, src, dst, y=y)
+    call = K.prepare_conv_short(x, cw, cu, cpool, src, dst, y=y, act=1)
     for _ in range(3):
         call()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -736,13 +744,97 @@ def bench_conv_prefill(torch, K, wl, dev, iters=20):
     us = e0.elapsed_time(e1) / iters * 1e3
     alg = 2 * T * C * 2 + 2 * N * C * (W - 1) * 2 + C * W * 2
     gbs = alg / us / 1e3
-    return {"workload": f"short conv, {T} tokens (16 packed sequences) x {C} channels, W=4, bf16, "
+    return {"workload": f"short conv + SiLU, {T} tokens (16 packed sequences) x {C} channels, W=4, bf16, "
                         "carried history in slots", "us": round(us, 2),
             "roofline": {"kernel": "conv_kernel<bf16,4> (kda_conv_short)", "bound": "hbm",
                          "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(gbs / HBM_PEAK_GBS, 4),
                          "traffic": traffic_for("conv_kernel_prefill_bf16", "kda_conv.hip", T),
                          "alg_bytes_per_launch": alg, "avg_launch_us": round(us, 3)}}
+
+
+def bench_prefill_conv(torch, K, wl, dev, iters=10, cpu_seconds=0.0):
+    """kda_prefill_varlen_conv on the varlen workload: the 16 sequences'
+    raw q / k / v projections (6,144 channels, bf16) through the conv
+    (W = 4, carried history, SiLU), the per-head q / k normalisation and the
+    chunked prefill (chunk 64, 4,096-token segments), gates, beta and initial
+    states as the varlen row.  Two launches per call (conv + norm, then the
+    prefill); each is also timed alone on the same data (the conv through
+    kda_conv_short with the same normalisation, the prefill through
+    kda_prefill_varlen on the formed operands).  Run back to back inside the
+    call, the prefill reads what the conv has just written and measures
+    somewhat slower than alone."""
+    from hybrid_recurrent_serving_amd.inputs import draw_conv
+    N, H, D, W = wl.n_seq, 16, 128, 4
+    C = 3 * H * D
+    T = int(wl.cu_seqlens[-1])
+    gen = torch.Generator().manual_seed(2)
+    cw, cst, x = draw_conv(gen, T, C, W, N, torch.bfloat16, torch.device("cpu"))
+    x_d, cw_d = x.to(dev), cw.to(dev)
+    cpool = torch.cat([cst, torch.zeros_like(cst)]).to(dev)
+    csrc = torch.arange(N, dtype=torch.int32, device=dev)
+    cdst = csrc + N
+    g, b = wl.g.to(dev), wl.beta.to(dev)
+    pool = torch.zeros(2 * N, H, D, D, device=dev)
+    for s_, i in enumerate(wl.init_index):
+        if i >= 0:
+            pool[s_] = wl.init_states[i].to(dev)
+    src = torch.tensor([s_ if i >= 0 else -1 for s_, i in enumerate(wl.init_index)], dtype=torch.int32,
+                       device=dev)
+    dst = torch.arange(N, 2 * N, dtype=torch.int32, device=dev)
+    cu = wl.cu_seqlens.to(dev)
+    o = torch.empty(T, H, D, dtype=torch.bfloat16, device=dev)
+    qkv = torch.empty(T, C, dtype=torch.bfloat16, device=dev)
+    qv, kv, vv = (qkv[:, i * H * D:(i + 1) * H * D].view(T, H, D) for i in range(3))
+    nws = K.kda_prefill_workspace_bytes(qv, kv, vv, g, b, o, cu, pool, src, dst, chunk=64,
+                                        segment_len=VARLEN_SEGMENT)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+
+    def whole():
+        K.kda_prefill_varlen_conv(x_d, cw_d, cpool, csrc, cdst, g, b, o, cu, pool, src, dst, qkv=qkv, act=1,
+                                  qk_l2norm=True, chunk=64, workspace=ws, segment_len=VARLEN_SEGMENT)
+
+    def prefill_only():
+        K.kda_prefill_varlen(qv, kv, vv, g, b, o, cu, pool, src, dst, chunk=64, workspace=ws,
+                             segment_len=VARLEN_SEGMENT)
+
+    # the call's first launch alone: the same conv kernel through kda_conv_short
+    # with the same normalisation, writing the same operands
+    conv_only = K.prepare_conv_short(x_d, cw_d, cu, cpool, csrc, cdst, y=qkv, act=1, norm_d=D,
+                                     norm_channels=2 * H * D)
+
+    def timed(fn):
+        for _ in range(2):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(iters):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / iters
+
+    ms = timed(whole)
+    ms_pf = timed(prefill_only)
+    conv_us = timed(conv_only) * 1e3
+    alg_conv = 2 * T * C * 2 + 2 * N * C * (W - 1) * 2 + C * W * 2
+    conv_gbs = alg_conv / conv_us / 1e3
+    tps = T / (ms * 1e-3)
+    res = {"workload": f"prefill from raw projections: the varlen workload's {T} tokens x {C} q/k/v channels, "
+                       "conv W=4 + SiLU + q/k L2 norm + chunked prefill (chunk 64), bf16",
+           "tokens": T, "ms": round(ms, 4), "tokens_per_s": round(tps, 1),
+           "prefill_launch_ms": round(ms_pf, 4), "conv_launch_us": round(conv_us, 1),
+           "roofline": prefill_roofline("prefill_kernel<128,bf16,bf16> on the formed operands (the call's "
+                                        "dominant launch)", T, ms_pf, "prefill_varlen", "prefill_kernel_d128_bf16"),
+           "conv_roofline": {"kernel": "conv_kernel<bf16,4,norm> (the call's conv + q/k norm launch)",
+                             "bound": "hbm", "achieved": round(conv_gbs, 1), "peak": HBM_PEAK_GBS,
+                             "unit": "GB/s", "frac": round(conv_gbs / HBM_PEAK_GBS, 4),
+                             "traffic": traffic_for("conv_norm_kernel_prefill_bf16", "kda_conv.hip", T),
+                             "alg_bytes_per_launch": alg_conv, "avg_launch_us": round(conv_us, 3)}}
+    if cpu_seconds > 0:
+        res["cpu_baseline"] = cpu_prefill_conv(cpu_seconds, wl, x, cw, cst)
+    return res
 
 
 def bench_prefill_long(torch, K, make_workload, dev, iters=3, cpu_segments=0):
@@ -894,6 +986,36 @@ def cpu_prefill(cpu_seconds, wl):
     return {"value": round(tok_heads / 16 / dt, 1), "unit": "tokens/s", "cores": orc.threads(),
             "kind": "oracle", "cpu": cpu_info(),
             "sample": f"{len(done)} of 16 sequences (all 16 heads each, {tok_heads // 16} tokens), "
+                      f"fp64 oracle, {dt:.1f} s"}
+
+
+def cpu_prefill_conv(cpu_seconds, wl, x, cw, cst):
+    """The oracle's prefill from raw projections on whole sequences (all 16
+    heads), shortest first, until the time budget is spent."""
+    import numpy as np
+    import oracle
+    orc = oracle.load("f64")
+    threads = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    orc.set_threads(threads)
+    N = wl.n_seq
+    cu = wl.cu_seqlens.numpy()
+    lens = np.diff(cu)
+    done, toks = 0, 0
+    t0 = time.perf_counter()
+    for s_ in sorted(range(N), key=lambda i: lens[i]):
+        i = wl.init_index[s_]
+        init = wl.init_states[i].double().numpy()[None] if i >= 0 else None
+        rows = slice(int(cu[s_]), int(cu[s_ + 1]))
+        orc.kda_prefill_conv(x[rows], cw, wl.g[rows], wl.beta[rows], np.array([0, lens[s_]], np.int32), H=16,
+                             d=128, act=1, conv_state=cst[s_:s_ + 1], qk_l2norm=1, init=init)
+        done += 1
+        toks += int(lens[s_])
+        if time.perf_counter() - t0 > cpu_seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(toks / dt, 1), "unit": "tokens/s", "cores": orc.threads(), "kind": "oracle",
+            "cpu": cpu_info(),
+            "sample": f"{done} of 16 sequences ({toks} tokens, all 16 heads: conv + norm + recurrence), "
                       f"fp64 oracle, {dt:.1f} s"}
 
 

@@ -194,6 +194,7 @@ size_t kda_args_sizeof(int which) {
     case 4: return sizeof(kda_decode_conv_args);
     case 5: return sizeof(kda_verify_conv_args);
     case 6: return sizeof(kda_plan_args);
+    case 7: return sizeof(kda_prefill_conv_args);
     default: return 0;
   }
 }
@@ -222,6 +223,15 @@ int kda_conv_short(const kda_conv_args* a, kda_stream_t stream_) {
     return fail(KDA_ERR_ALIGN, "conv: x, y, weight or conv_pool not 16-byte aligned");
   if (b.T_tot / 16 + b.n_seq + 1 > 0x7fffffffLL) return fail(KDA_ERR_SHAPE, "conv: too many tokens");
   if (b.act != 0 && b.act != 1) return fail(KDA_ERR_ARG, "conv: act = %d (0 none, 1 SiLU)", b.act);
+  if (b.norm_d != 0) {
+    if (b.norm_d != 16 && b.norm_d != 32 && b.norm_d != 64 && b.norm_d != 128)
+      return fail(KDA_ERR_UNSUPPORTED, "conv: norm_d = %d (16, 32, 64, 128)", b.norm_d);
+    if (b.W > 4) return fail(KDA_ERR_UNSUPPORTED, "conv: normalisation with W = %d (2..4)", b.W);
+    if (b.norm_channels < 0 || b.norm_channels > b.C || b.norm_channels % b.norm_d)
+      return fail(KDA_ERR_ARG, "conv: norm_channels %lld (a multiple of norm_d, <= C)", (long long)b.norm_channels);
+    if (b.C % b.norm_d) return fail(KDA_ERR_ARG, "conv: C %d not a multiple of norm_d %d", b.C, b.norm_d);
+    if (!(b.norm_eps >= 0.f)) return fail(KDA_ERR_ARG, "conv: norm_eps < 0");
+  }
   if (check_enabled()) {
     int st = check_cu(b.cu_seqlens, b.n_seq, b.T_tot, stream);
     if (st) return st;
@@ -233,6 +243,9 @@ int kda_conv_short(const kda_conv_args* a, kda_stream_t stream_) {
   p.src_slot = b.src_slot; p.dst_slot = b.dst_slot; p.adv = b.advance_len;
   p.x_stride = b.x_stride; p.y_stride = b.y_stride; p.T_tot = b.T_tot; p.n_slots = b.n_slots;
   p.n_seq = b.n_seq; p.C = b.C; p.W = b.W; p.act = b.act;
+  p.norm_d = b.norm_d;
+  p.norm_channels = b.norm_d ? b.norm_channels : 0;
+  p.norm_eps = b.norm_eps;
   return launch_conv(p, b.dtype, stream);
 }
 
@@ -532,13 +545,10 @@ int64_t kda_prefill_workspace_bytes(const kda_prefill_args* a) {
   return prefill_workspace_bytes(prefill_params(b), b.d_k);
 }
 
-int kda_prefill_varlen(const kda_prefill_args* a, kda_stream_t stream_) {
-  hipStream_t stream = static_cast<hipStream_t>(stream_);
-  kda_prefill_args b;
-  int st = prefill_validate(a, b);
-  if (st) return st;
-  if (b.n_seq == 0) return KDA_OK;
-  PrefillParams p = prefill_params(b);
+// The workspace test and the KDA_CHECK=1 validation of validated prefill
+// args; nothing is launched.
+static int prefill_precheck(const kda_prefill_args& b, const PrefillParams& p, hipStream_t stream) {
+  int st;
   const int64_t need = prefill_workspace_bytes(p, b.d_k);
   if (need > 0 && (!b.workspace || b.workspace_bytes < need))
     return fail(KDA_ERR_WORKSPACE, "workspace %lld bytes < %lld needed", (long long)b.workspace_bytes, (long long)need);
@@ -559,6 +569,77 @@ int kda_prefill_varlen(const kda_prefill_args* a, kda_stream_t stream_) {
                           b.chunk == 16 ? 16 : 32, b.T_tot, stream);
     if (st) return st;
   }
+  return KDA_OK;
+}
+
+int kda_prefill_varlen(const kda_prefill_args* a, kda_stream_t stream_) {
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  kda_prefill_args b;
+  int st = prefill_validate(a, b);
+  if (st) return st;
+  if (b.n_seq == 0) return KDA_OK;
+  PrefillParams p = prefill_params(b);
+  if ((st = prefill_precheck(b, p, stream))) return st;
+  return launch_prefill(p, b.d_k, b.in_dtype, b.out_dtype, stream);
+}
+
+int kda_prefill_varlen_conv(const kda_prefill_conv_args* a, kda_stream_t stream_) {
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  if (!a) return fail(KDA_ERR_NULL, "args is NULL");
+  if (a->struct_size != sizeof(kda_prefill_conv_args)) return fail(KDA_ERR_ARG, "struct_size mismatch");
+  kda_prefill_args pa = a->prefill;
+  if (pa.q || pa.k || pa.v || pa.q_stride || pa.k_stride || pa.v_stride)
+    return fail(KDA_ERR_ARG, "prefill_conv: prefill.q / k / v must be NULL and their strides 0 (they are formed in qkv)");
+  if (pa.d_k != pa.d_v) return fail(KDA_ERR_ARG, "prefill_conv: d_k %d != d_v %d", pa.d_k, pa.d_v);
+  const int in_dt = pa.in_dtype;
+  if (in_dt != KDA_BF16 && in_dt != KDA_F32) return fail(KDA_ERR_DTYPE, "in_dtype %d", in_dt);
+  if (pa.H <= 0) return fail(KDA_ERR_SHAPE, "H = %d", pa.H);
+  if (!supported_d(pa.d_k, pa.d_v)) return fail(KDA_ERR_UNSUPPORTED, "d = %d (16/32/64/128)", pa.d_k);
+  if (a->W < 2 || a->W > 4) return fail(KDA_ERR_UNSUPPORTED, "prefill_conv: W = %d (2..4)", a->W);
+  if (a->act != 0 && a->act != 1) return fail(KDA_ERR_ARG, "prefill_conv: act = %d (0 none, 1 SiLU)", a->act);
+  if (a->qk_l2norm != 0 && a->qk_l2norm != 1) return fail(KDA_ERR_ARG, "prefill_conv: qk_l2norm = %d", a->qk_l2norm);
+  if (!(a->norm_eps >= 0.f)) return fail(KDA_ERR_ARG, "prefill_conv: norm_eps < 0");
+  if (a->n_conv_slots < 0 || a->qkv_bytes < 0) return fail(KDA_ERR_SHAPE, "negative size");
+  if (!a->qkv) return fail(KDA_ERR_NULL, "prefill_conv: qkv is NULL");
+  const int64_t HD = static_cast<int64_t>(pa.H) * pa.d_k;
+  const int64_t C = 3 * HD;
+  if (C > 0x7fffffffLL) return fail(KDA_ERR_SHAPE, "prefill_conv: 3 H d too large");
+  const int64_t eb = dtype_bytes(in_dt);
+  char* qkv = static_cast<char*>(a->qkv);
+  pa.q = qkv;
+  pa.k = qkv + HD * eb;
+  pa.v = qkv + 2 * HD * eb;
+  pa.q_stride = pa.k_stride = pa.v_stride = C;
+  kda_prefill_args b;
+  int st = prefill_validate(&pa, b);
+  if (st) return st;
+  if (b.n_seq == 0) return KDA_OK;
+  if (!a->x || !a->conv_weight || !a->conv_pool || !a->conv_src_slot || !a->conv_dst_slot)
+    return fail(KDA_ERR_NULL, "prefill_conv: required pointer is NULL");
+  int64_t x_stride = a->x_stride == 0 ? C : a->x_stride;
+  if (x_stride < C) return fail(KDA_ERR_SHAPE, "prefill_conv: x_stride < 3 H d");
+  if (!aligned16(a->x) || !aligned16(a->qkv) || !aligned16(a->conv_weight) || !aligned16(a->conv_pool) ||
+      (x_stride * eb) % 16)
+    return fail(KDA_ERR_ALIGN, "prefill_conv: x, qkv, conv_weight or conv_pool not 16-byte aligned");
+  if (a->qkv_bytes / eb / C < b.T_tot)
+    return fail(KDA_ERR_WORKSPACE, "prefill_conv: qkv %lld bytes < %lld needed", (long long)a->qkv_bytes,
+                (long long)(b.T_tot * C * eb));
+  if (b.T_tot / 16 + b.n_seq + 1 > 0x7fffffffLL) return fail(KDA_ERR_SHAPE, "prefill_conv: too many tokens");
+  PrefillParams p = prefill_params(b);
+  if ((st = prefill_precheck(b, p, stream))) return st;
+  if (check_enabled()) {
+    st = check_slots(a->conv_src_slot, a->conv_dst_slot, b.n_seq, a->n_conv_slots, nullptr, stream);
+    if (st) return st;
+  }
+  ConvParams cp{};
+  cp.x = a->x; cp.y = a->qkv; cp.w = a->conv_weight; cp.bias = a->conv_bias; cp.cu = b.cu_seqlens;
+  cp.pool = a->conv_pool; cp.src_slot = a->conv_src_slot; cp.dst_slot = a->conv_dst_slot; cp.adv = nullptr;
+  cp.x_stride = x_stride; cp.y_stride = C; cp.T_tot = b.T_tot; cp.n_slots = a->n_conv_slots;
+  cp.n_seq = b.n_seq; cp.C = static_cast<int32_t>(C); cp.W = a->W; cp.act = a->act;
+  cp.norm_channels = a->qk_l2norm ? 2 * HD : 0;
+  cp.norm_d = a->qk_l2norm ? b.d_k : 0;
+  cp.norm_eps = a->norm_eps;
+  if ((st = launch_conv(cp, in_dt, stream))) return st;
   return launch_prefill(p, b.d_k, b.in_dtype, b.out_dtype, stream);
 }
 

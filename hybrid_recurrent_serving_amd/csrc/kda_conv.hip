@@ -21,6 +21,8 @@
 //    sequence's first W-1 tokens.  These only read x, with a sliding window
 //    of the previous W-1 rows in registers.
 
+#include <type_traits>
+
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -94,12 +96,50 @@ __device__ __forceinline__ void st_blocks(T* p, const float (&x)[NB * Vec16<T>::
 }
 
 __device__ __forceinline__ float conv_finish(float acc, int act) {
-  if (act == 1) acc = acc / (1.f + expf(-acc));
-  return acc;
+  return act == 1 ? silu_fast(acc) : acc;
 }
 
-template <typename T, int W>
+// Per-head L2 normalisation of one output row (NL > 0 only): the NL = norm_d
+// / V threads that hold one head's channels are adjacent lanes of one wave
+// (their group starts at a multiple of NL, which divides 64), so the sum of
+// squares closes over them by a butterfly.  Inside a row of 16 lanes it runs
+// on DPP moves: the two quad permutations pair lanes 1 and 2 apart, then the
+// half-row mirror joins the two (now uniform) quads of each 8 lanes and the
+// row mirror the two halves; a 32-lane group adds the other row by one
+// cross-lane read.  NL is a template argument so that the reduction has no
+// branches and the rows of a tile overlap.  Channels at or past
+// norm_channels (the v block) keep their values.
+template <int NL>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(NL == 2 || NL == 4 || NL == 8 || NL == 16 || NL == 32, "group of 2..32 lanes");
+  auto dpp = [](float v, auto ctrl) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), decltype(ctrl)::value, 0xf, 0xf, false));
+  };
+  x += dpp(x, std::integral_constant<int, 0xB1>{});                          // quad_perm [1, 0, 3, 2]
+  if constexpr (NL > 2) x += dpp(x, std::integral_constant<int, 0x4E>{});    // quad_perm [2, 3, 0, 1]
+  if constexpr (NL > 4) x += dpp(x, std::integral_constant<int, 0x141>{});   // row_half_mirror
+  if constexpr (NL > 8) x += dpp(x, std::integral_constant<int, 0x140>{});   // row_mirror
+  if constexpr (NL > 16) x += __shfl_xor(x, 16, 64);
+  return x;
+}
+
+template <int NL, int V>
+__device__ __forceinline__ void norm_row(float (&out)[V], const ConvParams& p, int64_t c0) {
+  if constexpr (NL > 0) {
+    float ss = 0.f;
+#pragma unroll
+    for (int v = 0; v < V; ++v) ss = fmaf(out[v], out[v], ss);
+    ss = group_sum<NL>(ss);
+    const float inv = 1.f / sqrtf(ss + p.norm_eps);
+    const bool qk = c0 < p.norm_channels;
+#pragma unroll
+    for (int v = 0; v < V; ++v) out[v] = qk ? out[v] * inv : out[v];
+  }
+}
+
+template <typename T, int W, int NL>
 __global__ void __launch_bounds__(CONV_THREADS) conv_kernel(const ConvParams p) {
+  constexpr bool NORM = NL > 0;
   constexpr int V = Vec16<T>::N;
   constexpr int HIST = W - 1;
   const int item = blockIdx.x;
@@ -192,6 +232,7 @@ __global__ void __launch_bounds__(CONV_THREADS) conv_kernel(const ConvParams p) 
           for (int j = 0; j < W; ++j) acc = fmaf(wt[j][i], xh[t + j][i], acc);
           out[i] = conv_finish(acc, p.act);
         }
+        norm_row<NL, V>(out, p, c0);
         Vec16<T>::st(yb + (bos + t) * p.y_stride + c0, out);
       }
     }
@@ -249,7 +290,9 @@ __global__ void __launch_bounds__(CONV_THREADS) conv_kernel(const ConvParams p) 
   }
 #pragma unroll
   for (int i = 0; i < CONV_TT; ++i) {
-    if (!tok_ok[i]) continue;
+    // the normalised form computes every row (the group reductions want all
+    // lanes, and rows without branches overlap) and stores the valid ones
+    if (!NORM && !tok_ok[i]) continue;
     float out[V];
 #pragma unroll
     for (int v = 0; v < V; ++v) out[v] = bias[v];
@@ -262,7 +305,8 @@ __global__ void __launch_bounds__(CONV_THREADS) conv_kernel(const ConvParams p) 
     }
 #pragma unroll
     for (int v = 0; v < V; ++v) out[v] = conv_finish(out[v], p.act);
-    Vec16<T>::st(yb + (t0 + i) * p.y_stride + c0, out);
+    norm_row<NL, V>(out, p, c0);
+    if (!NORM || tok_ok[i]) Vec16<T>::st(yb + (t0 + i) * p.y_stride + c0, out);
   }
 }
 
@@ -272,7 +316,26 @@ static int launch_conv_t(const ConvParams& p, hipStream_t stream) {
   const int64_t groups = (p.C + V - 1) / V;
   dim3 grid(static_cast<uint32_t>(p.n_seq + p.n_tiles),
             static_cast<uint32_t>((groups + CONV_THREADS - 1) / CONV_THREADS));
-  hipLaunchKernelGGL((conv_kernel<T, W>), grid, dim3(CONV_THREADS), 0, stream, p);
+  if (p.norm_d > 0) {
+    // the normalised form is built for the widths the fused paths take and
+    // the head sizes 16 .. 128 (groups of norm_d / V lanes)
+    if constexpr (W <= 4) {
+      switch (p.norm_d / V) {
+        case 2: if constexpr (V == 8) { hipLaunchKernelGGL((conv_kernel<T, W, 2>), grid, dim3(CONV_THREADS), 0, stream, p); break; }
+                return fail(KDA_ERR_UNSUPPORTED, "conv norm group of 2 lanes (fp32)");
+        case 4: hipLaunchKernelGGL((conv_kernel<T, W, 4>), grid, dim3(CONV_THREADS), 0, stream, p); break;
+        case 8: hipLaunchKernelGGL((conv_kernel<T, W, 8>), grid, dim3(CONV_THREADS), 0, stream, p); break;
+        case 16: hipLaunchKernelGGL((conv_kernel<T, W, 16>), grid, dim3(CONV_THREADS), 0, stream, p); break;
+        case 32: if constexpr (V == 4) { hipLaunchKernelGGL((conv_kernel<T, W, 32>), grid, dim3(CONV_THREADS), 0, stream, p); break; }
+                 return fail(KDA_ERR_UNSUPPORTED, "conv norm group of 32 lanes (bf16)");
+        default: return fail(KDA_ERR_UNSUPPORTED, "conv norm: head size %d", p.norm_d);
+      }
+    } else {
+      return fail(KDA_ERR_UNSUPPORTED, "conv with q/k normalisation: W = %d (2..4)", W);
+    }
+  } else {
+    hipLaunchKernelGGL((conv_kernel<T, W, 0>), grid, dim3(CONV_THREADS), 0, stream, p);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(KDA_ERR_HIP, "conv kernel launch: %s", hipGetErrorString(e));
   return KDA_OK;

@@ -75,6 +75,14 @@ __device__ __forceinline__ void st4_stream(float* p, const float (&x)[4]) {
   __builtin_nontemporal_store(v, reinterpret_cast<nt4*>(p));
 }
 
+// sigmoid and SiLU from the hardware base-2 exponential and reciprocal (each
+// about one unit in the last place); a large negative argument gives
+// exp2 = inf, reciprocal 0, so SiLU tends to (-)0 and sigmoid to 0.
+__device__ __forceinline__ float sigmoid_fast(float x) {
+  return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-x * 1.4426950408889634f));
+}
+__device__ __forceinline__ float silu_fast(float x) { return x * sigmoid_fast(x); }
+
 // Sum over the lanes that differ only in bits >= log2(FIRST) of the lane id.
 template <int FIRST>
 __device__ __forceinline__ float wave_sum_from(float x) {

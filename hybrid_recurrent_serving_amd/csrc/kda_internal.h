@@ -79,6 +79,11 @@ struct ConvParams {
   int64_t x_stride, y_stride, T_tot, n_slots;
   int32_t n_seq, C, W, act;
   int32_t n_tiles;                // body tiles of TT tokens
+  // per-head L2 normalisation of the outputs (the prefill's q and k): the
+  // channels below norm_channels, in groups of norm_d; norm_d = 0 = none
+  int64_t norm_channels;
+  int32_t norm_d;
+  float norm_eps;
 };
 
 int launch_conv(const ConvParams& p, int dtype, hipStream_t stream);

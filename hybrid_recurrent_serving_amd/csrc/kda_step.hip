@@ -362,12 +362,6 @@ template <> struct Vec16x<float> {
 
 // SiLU x / (1 + exp(-x)) from the hardware exp2 and reciprocal (each within
 // about one ulp)
-__device__ __forceinline__ float silu_fast(float x) {
-  return x * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-x * 1.4426950408889634f));
-}
-__device__ __forceinline__ float sigmoid_fast(float x) {
-  return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-x * 1.4426950408889634f));
-}
 
 // Gated RMS norm of one output vector of D channels held 4 per lane by
 // D / 4 consecutive lanes (sum of squares across them by butterfly

@@ -39,7 +39,7 @@ class ConvArgs(ctypes.Structure):
         ("conv_pool", c_vp), ("src_slot", c_vp), ("dst_slot", c_vp), ("advance_len", c_vp),
         ("x_stride", c_i64), ("y_stride", c_i64), ("T_tot", c_i64), ("n_slots", c_i64),
         ("n_seq", c_i32), ("C", c_i32), ("W", c_i32), ("dtype", c_i32), ("act", c_i32),
-        ("reserved", c_i32),
+        ("norm_d", c_i32), ("norm_channels", c_i64), ("norm_eps", c_f32), ("reserved", c_i32),
     ]
 
 
@@ -67,6 +67,17 @@ class PrefillArgs(ctypes.Structure):
         ("n_seq", c_i32), ("H", c_i32), ("d_k", c_i32), ("d_v", c_i32), ("chunk", c_i32),
         ("in_dtype", c_i32), ("out_dtype", c_i32), ("ckpt_interval", c_i32), ("scale", c_f32),
         ("segment_len", c_i32),
+    ]
+
+
+class PrefillConvArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", c_size),
+        ("prefill", PrefillArgs),
+        ("x", c_vp), ("conv_weight", c_vp), ("conv_bias", c_vp), ("conv_pool", c_vp),
+        ("conv_src_slot", c_vp), ("conv_dst_slot", c_vp), ("qkv", c_vp),
+        ("x_stride", c_i64), ("n_conv_slots", c_i64), ("qkv_bytes", c_i64),
+        ("W", c_i32), ("act", c_i32), ("qk_l2norm", c_i32), ("norm_eps", c_f32),
     ]
 
 
@@ -133,7 +144,7 @@ class VerifyArgs(ctypes.Structure):
 EXPORTS = ["kda_status_str", "kda_abi_version", "kda_last_error", "kda_args_sizeof",
            "kda_conv_short", "kda_ckpt_plan", "kda_ckpt_plan_device", "kda_prefill_workspace_bytes",
            "kda_prefill_varlen", "kda_decode", "kda_verify", "kda_decode_conv", "kda_verify_conv",
-           "kda_prefill_varlen_noalloc", "kda_prefill_noalloc_max_bytes"]
+           "kda_prefill_varlen_noalloc", "kda_prefill_noalloc_max_bytes", "kda_prefill_varlen_conv"]
 
 _lib = None
 
@@ -171,8 +182,9 @@ def load_library(path: Optional[Path] = None):
     lib.kda_verify.argtypes = [ctypes.POINTER(VerifyArgs), c_vp]
     lib.kda_decode_conv.argtypes = [ctypes.POINTER(DecodeConvArgs), c_vp]
     lib.kda_verify_conv.argtypes = [ctypes.POINTER(VerifyConvArgs), c_vp]
+    lib.kda_prefill_varlen_conv.argtypes = [ctypes.POINTER(PrefillConvArgs), c_vp]
     for name in ("kda_conv_short", "kda_ckpt_plan", "kda_ckpt_plan_device", "kda_prefill_varlen", "kda_decode", "kda_verify",
-                 "kda_decode_conv", "kda_verify_conv", "kda_prefill_varlen_noalloc"):
+                 "kda_decode_conv", "kda_verify_conv", "kda_prefill_varlen_noalloc", "kda_prefill_varlen_conv"):
         getattr(lib, name).restype = ctypes.c_int
     if path is None:
         _lib = lib
@@ -269,7 +281,8 @@ def kda_args_sizeof(which: int) -> int:
     return load_library().kda_args_sizeof(which)
 
 
-def _conv_args(x, weight, cu_seqlens, conv_pool, src_slot, dst_slot, y, bias, act, advance_len):
+def _conv_args(x, weight, cu_seqlens, conv_pool, src_slot, dst_slot, y, bias, act, advance_len, norm_d=0,
+               norm_channels=0, norm_eps=1e-6):
     _expect(x.dim() == 2 and y.shape == x.shape, "x and y must be [T, C]")
     T, C = x.shape
     _expect(weight.dim() == 2 and weight.shape[0] == C, "weight must be [C, W]")
@@ -293,17 +306,21 @@ def _conv_args(x, weight, cu_seqlens, conv_pool, src_slot, dst_slot, y, bias, ac
     a.T_tot, a.n_slots = x.shape[0], conv_pool.shape[0]
     a.n_seq, a.C, a.W = cu_seqlens.numel() - 1, x.shape[1], weight.shape[1]
     a.dtype, a.act = _dtype_code(x), act
+    a.norm_d, a.norm_channels, a.norm_eps = int(norm_d), int(norm_channels), float(norm_eps)
     return a
 
 
 def kda_conv_short(x, weight, cu_seqlens, conv_pool, src_slot, dst_slot, *, y=None, bias=None,
-                   act: int = 0, advance_len=None, stream=None):
+                   act: int = 0, advance_len=None, norm_d: int = 0, norm_channels: int = 0,
+                   norm_eps: float = 1e-6, stream=None):
     """Short causal conv.  x [T, C]; weight [C, W]; conv_pool [S, C, W-1].
-    Returns y (allocated by torch when not given)."""
+    With norm_d > 0, channels [0, norm_channels) are L2-normalised per token
+    in groups of norm_d.  Returns y (allocated by torch when not given)."""
     import torch
     if y is None:
         y = torch.empty_like(x)
-    a = _conv_args(x, weight, cu_seqlens, conv_pool, src_slot, dst_slot, y, bias, act, advance_len)
+    a = _conv_args(x, weight, cu_seqlens, conv_pool, src_slot, dst_slot, y, bias, act, advance_len, norm_d,
+                   norm_channels, norm_eps)
     _check(load_library().kda_conv_short(ctypes.byref(a), _stream(stream)))
     return y
 
@@ -330,9 +347,11 @@ def prepare_decode(q, k, v, g, beta, o, state_pool, src_slot, dst_slot, *, scale
 
 
 def prepare_conv_short(x, weight, cu_seqlens, conv_pool, src_slot, dst_slot, *, y, bias=None, act: int = 0,
-                       advance_len=None) -> Prepared:
+                       advance_len=None, norm_d: int = 0, norm_channels: int = 0,
+                       norm_eps: float = 1e-6) -> Prepared:
     """kda_conv_short with fixed buffers, as a Prepared call."""
-    a = _conv_args(x, weight, cu_seqlens, conv_pool, src_slot, dst_slot, y, bias, act, advance_len)
+    a = _conv_args(x, weight, cu_seqlens, conv_pool, src_slot, dst_slot, y, bias, act, advance_len, norm_d,
+                   norm_channels, norm_eps)
     return Prepared(load_library().kda_conv_short, a,
                     (x, weight, cu_seqlens, conv_pool, src_slot, dst_slot, y, bias, advance_len))
 
@@ -479,6 +498,65 @@ def kda_prefill_varlen_noalloc(q, k, v, g, beta, o, cu_seqlens, state_pool, src_
                       segment_len)
     _check(load_library().kda_prefill_varlen_noalloc(ctypes.byref(a), _stream(stream)))
     return o
+
+
+def kda_prefill_varlen_conv(x, conv_weight, conv_pool, conv_src_slot, conv_dst_slot, g, beta, o, cu_seqlens,
+                            state_pool, src_slot, dst_slot, *, qkv=None, conv_bias=None, act: int = 0,
+                            qk_l2norm: bool = True, norm_eps: float = 1e-6, chunk=64, start_pos=None,
+                            ckpt_interval=0, ckpt_cu=None, ckpt_slot=None, ckpt_pos_out=None, workspace=None,
+                            scale=1.0, segment_len=0, stream=None):
+    """Prefill from the tokens' raw projections: the short conv (+ SiLU),
+    per-head q / k normalisation and the chunked prefill (include/kda.h).
+
+    x [T, 3 H d] (q | k | v projections, packed rows); conv_weight
+    [3 H d, W]; conv_pool [n_conv_slots, 3 H d, W-1]; g [T, H, d]; beta
+    [T, H]; o [T, H, d].  ``qkv`` [T, 3 H d] (x's dtype, packed) receives the
+    formed q | k | v; allocated when None.  ``workspace`` as
+    kda_prefill_varlen.  Returns (o, qkv)."""
+    import torch
+    _expect(x.dim() == 2 and g.dim() == 3, "x [T, 3 H d], g [T, H, d]")
+    T, C = x.shape
+    H, d = g.shape[1], g.shape[2]
+    _expect(C == 3 * H * d, "x must have 3 H d channels")
+    _expect(x.stride(1) == 1, "x rows must be contiguous")
+    W = conv_weight.shape[1]
+    _expect(tuple(conv_weight.shape) == (C, W) and conv_weight.is_contiguous(), "conv_weight must be [3 H d, W]")
+    _expect(conv_pool.dim() == 3 and tuple(conv_pool.shape[1:]) == (C, W - 1) and conv_pool.is_contiguous(),
+            "conv_pool must be [n_conv_slots, 3 H d, W-1]")
+    if qkv is None:
+        qkv = torch.empty(T, C, dtype=x.dtype, device=x.device)
+    _expect(tuple(qkv.shape) == (T, C) and qkv.is_contiguous() and qkv.dtype == x.dtype,
+            "qkv must be a packed [T, 3 H d] tensor of x's dtype")
+    _device_tensors(x=x, conv_weight=conv_weight, conv_pool=conv_pool, conv_src_slot=conv_src_slot,
+                    conv_dst_slot=conv_dst_slot, conv_bias=conv_bias, qkv=qkv)
+    _same_dtype(x, conv_weight=conv_weight, conv_pool=conv_pool, g=g)
+    if conv_bias is not None:
+        _same_dtype(x, conv_bias=conv_bias)
+    HD = H * d
+    views = [qkv[:, i * HD:(i + 1) * HD].view(T, H, d) if T else qkv.new_empty(0, H, d) for i in range(3)]
+    pa = _prefill_args(views[0], views[1], views[2], g, beta, o, cu_seqlens, state_pool, src_slot, dst_slot,
+                       chunk, start_pos, ckpt_interval, ckpt_cu, ckpt_slot, ckpt_pos_out, workspace, scale,
+                       segment_len)
+    lib = load_library()
+    if workspace is None:
+        need = lib.kda_prefill_workspace_bytes(ctypes.byref(pa))
+        if need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+            pa.workspace, pa.workspace_bytes = _ptr(workspace), need
+    # q / k / v are formed by the library inside qkv
+    pa.q = pa.k = pa.v = None
+    pa.q_stride = pa.k_stride = pa.v_stride = 0
+    a = PrefillConvArgs()
+    a.struct_size = ctypes.sizeof(PrefillConvArgs)
+    a.prefill = pa
+    a.x, a.conv_weight, a.conv_bias, a.conv_pool = _ptr(x), _ptr(conv_weight), _ptr(conv_bias), _ptr(conv_pool)
+    a.conv_src_slot, a.conv_dst_slot, a.qkv = _ptr(conv_src_slot), _ptr(conv_dst_slot), _ptr(qkv)
+    a.x_stride = x.stride(0) if T else 0
+    a.n_conv_slots = conv_pool.shape[0]
+    a.qkv_bytes = qkv.numel() * qkv.element_size()
+    a.W, a.act, a.qk_l2norm, a.norm_eps = W, int(act), int(qk_l2norm), float(norm_eps)
+    _check(lib.kda_prefill_varlen_conv(ctypes.byref(a), _stream(stream)))
+    return o, qkv
 
 
 def kda_prefill_noalloc_max_bytes() -> int:

@@ -83,8 +83,8 @@ int kda_abi_version(void);
 /* One-line reason for the calling thread's most recent non-OK status. */
 const char *kda_last_error(void);
 /* sizeof() of each args struct as compiled into the library: which = 0 conv,
- * 1 prefill, 2 decode, 3 verify, 4 decode_conv, 5 verify_conv, 6 plan.  Returns 0
- * for other values. */
+ * 1 prefill, 2 decode, 3 verify, 4 decode_conv, 5 verify_conv, 6 plan,
+ * 7 prefill_conv.  Returns 0 for other values. */
 size_t kda_args_sizeof(int which);
 
 /* ------------------------------------------------------------------------
@@ -104,6 +104,14 @@ size_t kda_args_sizeof(int which);
  * advance_len[s] tokens, or after all tokens when advance_len is NULL) is
  * written to dst_slot[s] when >= 0; src == dst (in place) is allowed.
  * Outputs are produced for every token.  Sequences may be empty.
+ *
+ * Optional per-head normalisation (the q / k step of the fused order,
+ * kda_prefill_varlen_conv): with norm_d > 0 every token's channels
+ * [0, norm_channels) are taken in groups of norm_d and each group is divided
+ * by sqrt(sum of its squares + norm_eps), after the SiLU; the channels past
+ * norm_channels keep their values.  norm_d in {16, 32, 64, 128},
+ * norm_channels a multiple of norm_d and <= C, W <= 4 (else
+ * KDA_ERR_UNSUPPORTED / KDA_ERR_ARG); y is then rounded to dtype once.
  * ---------------------------------------------------------------------- */
 typedef struct kda_conv_args {
     size_t struct_size;          /* sizeof(kda_conv_args) */
@@ -125,6 +133,9 @@ typedef struct kda_conv_args {
     int32_t W;                   /* 2..8 */
     int32_t dtype;               /* x, y, weight, bias and conv_pool */
     int32_t act;                 /* 0 none, 1 SiLU */
+    int32_t norm_d;              /* 0 = no normalisation, else the group size */
+    int64_t norm_channels;       /* channels normalised (from channel 0) */
+    float norm_eps;              /* >= 0 */
     int32_t reserved;
 } kda_conv_args;
 
@@ -287,6 +298,65 @@ typedef struct kda_prefill_args {
 /* Workspace bytes kda_prefill_varlen needs for these args (host-only). */
 int64_t kda_prefill_workspace_bytes(const kda_prefill_args *args);
 int kda_prefill_varlen(const kda_prefill_args *args, kda_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * kda_prefill_varlen_conv -- the prefill from the tokens' raw projections.
+ *
+ * The prefill side of the layer's fused order (Day-0 Integration page,
+ * section "Separate Prefill/Decode Code Paths": the short causal conv over
+ * the q / k / v projections in front of the recurrence; section "Kimi Delta
+ * Attention: When Prefix Caching Meets Recurrent State" for the conv state
+ * a prefix snapshot carries).  Per sequence s of the packed batch:
+ *   y = conv(history ++ tokens) (+ SiLU when act == 1), channel c:
+ *       y[t, c] = bias[c] + sum_{j<W} w[c, j] xbar[t - (W-1) + j, c]
+ *   q, k, v = the three channel blocks of y, each [H, d]
+ *   qk_l2norm: q <- q / sqrt(|q|^2 + norm_eps) per token and head, k alike
+ *   q, k, v rounded once to in_dtype and written to `qkv`
+ *   then kda_varlen of `prefill` on those q, k, v.
+ * The conv history of s is read from conv_pool[conv_src_slot[s]] (zeros when
+ * -1) and the last W-1 raw inputs of history ++ tokens are written to
+ * conv_pool[conv_dst_slot[s]] (not when -1); src == dst is allowed.
+ *
+ * Two launches on `stream`: the conv with the normalisation (one streaming
+ * pass over x that writes qkv), then the chunked prefill reading qkv.  The
+ * prefill kernel holds its whole register file and LDS for the chunk
+ * pipeline, so the conv is not folded into its tile loads.
+ *
+ * Layout: x [T_tot, 3 H d] in_dtype (row stride x_stride; 0 = 3 H d),
+ * conv_weight [3 H d, W], conv_bias [3 H d] or NULL, conv_pool
+ * [n_conv_slots, 3 H d, W-1] in_dtype; qkv [T_tot, 3 H d] in_dtype packed,
+ * caller-owned (also an output: the q | k | v the recurrence consumed).
+ * `prefill` is a kda_prefill_args with q, k and v NULL and their strides 0
+ * (the library points them into qkv), d_k == d_v == d; every other field
+ * as kda_prefill_varlen (g, beta, o, slots, checkpoints, workspace from
+ * kda_prefill_workspace_bytes of the same args, segment_len).
+ * Errors: those of kda_prefill_varlen, raised before anything is launched;
+ * q / k / v given or d_k != d_v -> KDA_ERR_ARG; W outside 2..4 ->
+ * KDA_ERR_UNSUPPORTED; qkv smaller than T_tot * 3 H d elements ->
+ * KDA_ERR_WORKSPACE; x, qkv, conv_weight or conv_pool not 16-byte aligned,
+ * or an x stride that breaks 16-byte rows -> KDA_ERR_ALIGN; act not 0/1,
+ * qk_l2norm not 0/1 or norm_eps < 0 -> KDA_ERR_ARG.
+ * ---------------------------------------------------------------------- */
+typedef struct kda_prefill_conv_args {
+    size_t struct_size;          /* sizeof(kda_prefill_conv_args) */
+    kda_prefill_args prefill;    /* q, k, v NULL; see above */
+    const void *x;               /* [T_tot, 3 H d] raw q | k | v projections */
+    const void *conv_weight;     /* [3 H d, W] */
+    const void *conv_bias;       /* [3 H d] or NULL */
+    void *conv_pool;             /* [n_conv_slots, 3 H d, W-1] in_dtype */
+    const int32_t *conv_src_slot;/* [n_seq]; -1 = zero history */
+    const int32_t *conv_dst_slot;/* [n_seq]; -1 = not written */
+    void *qkv;                   /* [T_tot, 3 H d] in_dtype, packed */
+    int64_t x_stride;            /* elements between tokens of x (0 = 3 H d) */
+    int64_t n_conv_slots;
+    int64_t qkv_bytes;           /* size of qkv in bytes */
+    int32_t W;                   /* 2..4 */
+    int32_t act;                 /* 0 none, 1 SiLU */
+    int32_t qk_l2norm;           /* 0 / 1 */
+    float norm_eps;              /* >= 0 */
+} kda_prefill_conv_args;
+
+int kda_prefill_varlen_conv(const kda_prefill_conv_args *args, kda_stream_t stream);
 
 /* ------------------------------------------------------------------------
  * kda_prefill_varlen_noalloc -- kda_prefill_varlen for callers that cannot

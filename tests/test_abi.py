@@ -36,9 +36,9 @@ def test_every_declared_symbol_is_exported(lib):
 def test_abi_version_and_struct_sizes(lib):
     assert lib.kda_abi_version() == 2
     for which, cls in enumerate([K.ConvArgs, K.PrefillArgs, K.DecodeArgs, K.VerifyArgs, K.DecodeConvArgs,
-                                 K.VerifyConvArgs, K.PlanArgs]):
+                                 K.VerifyConvArgs, K.PlanArgs, K.PrefillConvArgs]):
         assert lib.kda_args_sizeof(which) == ctypes.sizeof(cls), cls.__name__
-    assert lib.kda_args_sizeof(7) == 0
+    assert lib.kda_args_sizeof(8) == 0
 
 
 def test_status_strings(lib):
@@ -190,6 +190,13 @@ def test_conv_validation(lib):
     assert _call(lib, "kda_conv_short", _conv_args(x_stride=65)) == 4
     assert _call(lib, "kda_conv_short", _conv_args(act=2)) == 8
     assert _call(lib, "kda_conv_short", _conv_args(n_seq=0)) == 0
+    # the optional per-head normalisation
+    assert _call(lib, "kda_conv_short", _conv_args(norm_d=48, norm_channels=48)) == 6
+    assert _call(lib, "kda_conv_short", _conv_args(norm_d=16, norm_channels=32, W=5)) == 6
+    assert _call(lib, "kda_conv_short", _conv_args(norm_d=16, norm_channels=24)) == 8
+    assert _call(lib, "kda_conv_short", _conv_args(norm_d=16, norm_channels=80)) == 8   # > C
+    assert _call(lib, "kda_conv_short", _conv_args(norm_d=128, norm_channels=0)) == 8   # C not a multiple
+    assert _call(lib, "kda_conv_short", _conv_args(norm_d=16, norm_channels=32, norm_eps=-1.0)) == 8
 
 
 def _prefill_args(**kw):
@@ -304,3 +311,53 @@ def _plan_args(**kw):
 def test_ckpt_plan_device_validation(lib, kw, status):
     st = lib.kda_ckpt_plan_device(ctypes.byref(_plan_args(**kw)), None)
     assert lib.kda_status_str(st).decode() == status, lib.kda_last_error()
+
+
+def test_prefill_conv_validation(lib):
+    """kda_prefill_varlen_conv rejects bad arguments before launching
+    anything (every case here fails on the host)."""
+    f = "kda_prefill_varlen_conv"
+    fake = 1 << 20
+
+    def args(**kw):
+        a = K.PrefillConvArgs()
+        a.struct_size = ctypes.sizeof(K.PrefillConvArgs)
+        p = a.prefill
+        p.struct_size = ctypes.sizeof(K.PrefillArgs)
+        for fld in ("g", "beta", "o", "cu_seqlens", "state_pool", "src_slot", "dst_slot"):
+            setattr(p, fld, fake)
+        p.T_tot, p.n_slots, p.n_seq, p.H, p.d_k, p.d_v, p.chunk = 64, 4, 2, 2, 64, 64, 64
+        p.in_dtype, p.out_dtype, p.scale = 0, 0, 1.0
+        for fld in ("x", "conv_weight", "conv_pool", "conv_src_slot", "conv_dst_slot", "qkv"):
+            setattr(a, fld, fake)
+        a.n_conv_slots, a.qkv_bytes, a.W, a.act, a.qk_l2norm, a.norm_eps = 4, 64 * 384 * 2, 4, 1, 1, 1e-6
+        for k, v in kw.items():
+            if k.startswith("p_"):
+                setattr(p, k[2:], v)
+            else:
+                setattr(a, k, v)
+        return a
+
+    assert lib.kda_prefill_varlen_conv(None, None) == 1
+    assert _call(lib, f, args(struct_size=8)) == 8
+    assert _call(lib, f, args(p_q=fake)) == 8                    # q is formed by the library
+    assert _call(lib, f, args(p_k_stride=384)) == 8
+    assert _call(lib, f, args(p_d_v=32)) == 8
+    assert _call(lib, f, args(p_in_dtype=7)) == 3
+    assert _call(lib, f, args(p_d_k=48, p_d_v=48)) == 6
+    assert _call(lib, f, args(W=5)) == 6
+    assert _call(lib, f, args(W=1)) == 6
+    assert _call(lib, f, args(act=2)) == 8
+    assert _call(lib, f, args(qk_l2norm=2)) == 8
+    assert _call(lib, f, args(norm_eps=-1.0)) == 8
+    assert _call(lib, f, args(qkv=None)) == 1
+    assert _call(lib, f, args(x=None)) == 1
+    assert _call(lib, f, args(conv_pool=None)) == 1
+    assert _call(lib, f, args(p_chunk=48)) == 6                  # prefill's own checks
+    assert _call(lib, f, args(p_o=None)) == 1
+    assert _call(lib, f, args(qkv_bytes=64 * 384 * 2 - 2)) == 5  # qkv too small
+    assert _call(lib, f, args(x=fake + 4)) == 4
+    assert _call(lib, f, args(x_stride=100)) == 2                # < 3 H d
+    assert _call(lib, f, args(x_stride=388)) == 4                # rows not 16-byte aligned
+    assert _call(lib, f, args(p_n_seq=0)) == 0                   # no-op
+

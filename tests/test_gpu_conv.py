@@ -111,3 +111,49 @@ def test_conv_tiny_fp32(dev, oracle64):
     torch.cuda.synchronize()
     _check_y("y", y, y_ref, torch.float32)
     assert np.array_equal(U.to_np(pool), st_ref)
+
+
+@pytest.mark.parametrize("dtype,hd", [(torch.bfloat16, 128), (torch.bfloat16, 16), (torch.float32, 128),
+                                      (torch.float32, 32)])
+def test_conv_head_norm(dev, oracle64, dtype, hd):
+    """The optional per-head normalisation: C = 3 H d channels, the first
+    2 H d (q and k blocks) normalised per token in groups of d after the
+    SiLU, the v block as convolved; packed sequences with ragged lengths
+    (0, 1, 2, 3, 40, 130), some without history.  Against the oracle's
+    operand forming (one rounding to dtype of the normalised fp64 value)."""
+    import oracle as O
+    U.say(f"conv head norm d={hd} {dtype}")
+    H = 2
+    C = 3 * H * hd
+    lens = [0, 1, 2, 3, 40, 130]
+    N = len(lens)
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32)
+    T = int(cu[-1])
+    gen = torch.Generator().manual_seed(700 + hd)
+    x = torch.randn(T, C, generator=gen).to(dtype)
+    w = (torch.rand(C, 4, generator=gen) - 0.5).to(dtype)
+    st = torch.randn(N, C, 3, generator=gen).to(dtype)
+    has = np.array([1, 0, 1, 1, 0, 1], np.int32)
+    y_ref, st_ref = oracle64.conv_short(x, w, cu, act=1, state=st, has_state=has)
+    q, k, v = O.conv_operands(y_ref, H, hd, 1, 1e-6, "bf16" if dtype == torch.bfloat16 else "f32")
+    want = np.concatenate([q.reshape(T, -1), k.reshape(T, -1), v.reshape(T, -1)], axis=1)
+    pool = torch.cat([st, torch.zeros_like(st)]).to(dev)
+    src = torch.tensor([s if has[s] else -1 for s in range(N)], dtype=torch.int32, device=dev)
+    dst = torch.arange(N, 2 * N, dtype=torch.int32, device=dev)
+    y = K.kda_conv_short(x.to(dev), w.to(dev), cu.to(dev), pool, src, dst, act=1, norm_d=hd,
+                         norm_channels=2 * H * hd)
+    torch.cuda.synchronize()
+    got = y.to("cpu", torch.float32).numpy().astype(np.float64)
+    if dtype == torch.bfloat16:
+        diff = np.abs(got - want)
+        ulp = np.ldexp(1.0, np.floor(np.log2(np.abs(want) + 1e-30)).astype(int) - 7)
+        floor = 2.0 ** -16 * np.abs(want).max()
+        assert np.all(diff <= ulp + floor), float((diff / (ulp + floor)).max())
+        assert float(np.mean(diff > 0)) < 0.02
+    else:
+        U.assert_close("y", got, want, rel=1e-5, mx=1e-5)
+    # the q and k groups have unit norm (up to eps and the rounding)
+    norms = np.sqrt((got[:, :2 * H * hd].reshape(T, 2 * H, hd) ** 2).sum(-1))
+    if T:
+        assert np.all(np.abs(norms - 1.0) < 1e-2)
+    assert np.array_equal(pool[N:].to("cpu", torch.float32).numpy(), st_ref.astype(np.float32))

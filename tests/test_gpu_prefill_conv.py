@@ -1,0 +1,209 @@
+"""GPU parity of kda_prefill_varlen_conv (the prefill from the tokens' raw
+q / k / v projections: short conv, optional SiLU, per-head q / k
+normalisation, then the chunked prefill) against the oracle's composition,
+through the C ABI."""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import gpu_util as U
+from hybrid_recurrent_serving_amd import kda as K
+from hybrid_recurrent_serving_amd.inputs import draw_conv, make_workload
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    d = U.device()
+    K.load_library()
+    return d
+
+
+def _case(lengths, H, d, W, dtype, seed):
+    """Packed sequences in the varlen workload's distribution (gates, beta,
+    initial states on even sequences), raw projections x N(0, 1), conv
+    weights U(-1/sqrt(W), 1/sqrt(W)), histories N(0, 1), bias 0.1 N(0, 1)."""
+    wl = make_workload(2, lengths=lengths, H=H, d=d, seed=seed)
+    wl.g, wl.beta = wl.g.to(dtype), wl.beta.to(dtype)
+    N, T = len(lengths), int(sum(lengths))
+    C = 3 * H * d
+    gen = torch.Generator().manual_seed(3000 + seed)
+    w, st, x = draw_conv(gen, T, C, W, N, dtype, torch.device("cpu"))
+    bias = (0.1 * torch.randn(C, generator=gen)).to(dtype)
+    init = np.zeros((N, H, d, d))
+    has = np.zeros(N, np.int32)
+    for s, i in enumerate(wl.init_index):
+        if i >= 0:
+            init[s] = wl.init_states[i].double().numpy()
+            has[s] = 1
+    return wl, x, w, st, bias, init, has
+
+
+def _run(dev, wl, x, w, st, bias, init, has, conv_has, *, act, norm, chunk=64, out_dtype=torch.bfloat16,
+         ckpt_interval=0, segment_len=0, in_place=False):
+    """State slots: sources [0, N), destinations [N, 2N) (or the sources
+    when in_place), checkpoints from 2N; conv slots likewise."""
+    N = wl.n_seq
+    H, d = wl.H, wl.dk
+    C = x.shape[1]
+    W = w.shape[1]
+    i32 = lambda v: torch.tensor(v, dtype=torch.int32, device=dev)
+    n_ck = 0
+    kw = {}
+    if ckpt_interval:
+        ck_cu, _ = K.kda_ckpt_plan(wl.cu_seqlens.numpy(), ckpt_interval, chunk)
+        n_ck = int(ck_cu[-1])
+        kw = dict(ckpt_interval=ckpt_interval, ckpt_cu=i32(list(ck_cu)),
+                  ckpt_slot=i32(list(range(2 * N, 2 * N + n_ck))),
+                  ckpt_pos_out=torch.full((max(n_ck, 1),), -1, dtype=torch.int32, device=dev))
+    pool = torch.full((2 * N + max(n_ck, 1), H, d, d), float("nan"), device=dev)
+    pool[:N] = torch.tensor(init, dtype=torch.float32, device=dev)
+    src = i32([s if has[s] else -1 for s in range(N)])
+    dst = i32(list(range(N))) if in_place else i32(list(range(N, 2 * N)))
+    cpool = torch.full((2 * N, C, W - 1), float("nan"), dtype=x.dtype, device=dev)
+    cpool[:N] = st.to(dev)
+    csrc = i32([s if conv_has[s] else -1 for s in range(N)])
+    cdst = i32(list(range(N))) if in_place else i32(list(range(N, 2 * N)))
+    o = torch.full((x.shape[0], H, d), float("nan"), dtype=out_dtype, device=dev)
+    _, qkv = K.kda_prefill_varlen_conv(x.to(dev), w.to(dev), cpool, csrc, cdst, wl.g.to(dev), wl.beta.to(dev), o,
+                                       wl.cu_seqlens.to(dev), pool, src, dst,
+                                       conv_bias=None if bias is None else bias.to(dev), act=act,
+                                       qk_l2norm=norm, chunk=chunk, segment_len=segment_len, **kw)
+    torch.cuda.synchronize()
+    out = {"o": o, "final": pool[dst.long()], "conv": cpool[cdst.long()], "qkv": qkv,
+           "ckpt": pool[2 * N:2 * N + n_ck]}
+    if ckpt_interval:
+        out["ckpt_pos"] = kw["ckpt_pos_out"][:n_ck].cpu().numpy()
+    return out
+
+
+def _reference(orc, wl, x, w, st, bias, init, has, conv_has, *, act, norm, ckpt_interval=0,
+               operand_dtype="bf16"):
+    return orc.kda_prefill_conv(x, w, wl.g, wl.beta, wl.cu_seqlens, H=wl.H, d=wl.dk,
+                                bias=None if bias is None else bias, act=act, conv_state=st,
+                                has_conv_state=conv_has, qk_l2norm=norm, operand_dtype=operand_dtype,
+                                init=init, has_init=has, ckpt_interval=ckpt_interval)
+
+
+def _check_qkv(got, ref, dtype):
+    """The formed operands: bf16 values equal the oracle's up to one unit in
+    the last place, and only where the two unrounded values straddle a
+    rounding midpoint (a small fraction); fp32 ones to a few fp32 units.
+    Where the conv's terms nearly cancel, the fp32 sum's own error (a few
+    2^-24 of the terms) can exceed a bf16 unit of the small result: hence
+    an absolute allowance of 2^-16 of the block's largest value."""
+    T = got.shape[0]
+    g_ = got.to("cpu", torch.float32).numpy().reshape(T, 3, -1)
+    r_ = np.stack([ref["q"], ref["k"], ref["v"]], axis=1).reshape(T, 3, -1)
+    diff = np.abs(g_.astype(np.float64) - r_)
+    if dtype == torch.bfloat16:
+        ulp = np.ldexp(1.0, np.floor(np.log2(np.abs(r_) + 1e-30)).astype(int) - 7)
+        floor = 2.0 ** -16 * np.abs(r_).max(axis=(0, 2), keepdims=True)
+        ratio = diff / (ulp + floor)
+        U.say(f"  qkv: largest difference {float(ratio.max()):.3f} of (one bf16 unit + floor)")
+        assert np.all(ratio <= 1 + 1e-6), "qkv: a difference above one bf16 unit"
+        frac = float(np.mean(diff > 0))
+        U.say(f"  qkv: {frac:.2e} of the operands differ")
+        assert frac < 0.02
+    else:
+        U.assert_close("qkv", g_, r_, rel=1e-5, mx=1e-5)
+
+
+def _check_conv_state(got, ref):
+    """The new history is a copy of raw inputs: bit-exact."""
+    assert np.array_equal(got.to("cpu", torch.float32).numpy(), ref.astype(np.float32))
+
+
+def test_prefill_conv_ragged_bf16(dev, oracle64):
+    """Ragged batch with sequences shorter than the conv window (1 and 2
+    tokens), mixed histories and initial states, H=2, d=128, W=4, SiLU and
+    q/k norm, bias, chunk 64, checkpoints every 64."""
+    U.say("prefill_conv ragged bf16 d128")
+    lengths = [37, 1, 2, 300, 77, 129]
+    wl, x, w, st, bias, init, has = _case(lengths, 2, 128, 4, torch.bfloat16, seed=91)
+    conv_has = np.array([1, 1, 0, 1, 0, 1], np.int32)
+    got = _run(dev, wl, x, w, st, bias, init, has, conv_has, act=1, norm=1, ckpt_interval=64)
+    ref = _reference(oracle64, wl, x, w, st, bias, init, has, conv_has, act=1, norm=1, ckpt_interval=64)
+    _check_qkv(got["qkv"], ref, torch.bfloat16)
+    U.assert_close("o", U.to_np(got["o"]), ref["o"])
+    U.assert_close("states", np.concatenate([U.to_np(got["final"]), U.to_np(got["ckpt"])]),
+                   np.concatenate([ref["final"], ref["ckpt"]]))
+    assert list(got["ckpt_pos"]) == list(ref["ckpt_pos"])
+    _check_conv_state(got["conv"], ref["conv_state"])
+
+
+@pytest.mark.parametrize("d,W,act,norm", [(16, 2, 0, 1), (32, 3, 1, 1), (64, 4, 1, 0)])
+def test_prefill_conv_fp32(dev, oracle64, d, W, act, norm):
+    """fp32 inputs and outputs: small heads, every conv width, with and
+    without the activation and the normalisation."""
+    U.say(f"prefill_conv fp32 d={d} W={W} act={act} norm={norm}")
+    lengths = [5, 40, 1, 70]
+    wl, x, w, st, bias, init, has = _case(lengths, 3, d, W, torch.float32, seed=92 + d)
+    if not norm:
+        x, st, bias = (t * 0.15 for t in (x, st, bias))
+    conv_has = np.array([1, 0, 1, 1], np.int32)
+    got = _run(dev, wl, x, w, st, bias, init, has, conv_has, act=act, norm=norm, chunk=32,
+               out_dtype=torch.float32)
+    ref = _reference(oracle64, wl, x, w, st, bias, init, has, conv_has, act=act, norm=norm, operand_dtype="f32")
+    _check_qkv(got["qkv"], ref, torch.float32)
+    U.assert_close("o", U.to_np(got["o"]), ref["o"])
+    U.assert_close("final", U.to_np(got["final"]), ref["final"])
+    _check_conv_state(got["conv"], ref["conv_state"])
+
+
+def test_prefill_conv_in_place_segment_scan(dev, oracle64):
+    """Conv and state slots updated in place, no bias, and a sequence split
+    into 256-token segments (the segment scan reads the formed operands)."""
+    U.say("prefill_conv in place, segment scan")
+    lengths = [700, 90, 300]
+    wl, x, w, st, _, init, has = _case(lengths, 2, 64, 4, torch.bfloat16, seed=95)
+    conv_has = np.array([1, 1, 0], np.int32)
+    got = _run(dev, wl, x, w, st, None, init, has, conv_has, act=1, norm=1, segment_len=256, in_place=True)
+    ref = _reference(oracle64, wl, x, w, st, None, init, has, conv_has, act=1, norm=1)
+    _check_qkv(got["qkv"], ref, torch.bfloat16)
+    U.assert_close("o", U.to_np(got["o"]), ref["o"])
+    U.assert_close("final", U.to_np(got["final"]), ref["final"])
+    _check_conv_state(got["conv"], ref["conv_state"])
+
+
+def test_prefill_conv_varlen_full_size(dev, oracle64):
+    """The varlen workload at full size (16 sequences, lengths U{512..16384},
+    H=16, d=128, bf16, chunk 64, 4,096-token segments as the benchmark runs
+    it), all conv histories carried.  Every conv history is compared bit for
+    bit; outputs and final states of three sequences (the first, the longest
+    and the last, re-packed as a batch of their own for the oracle) over all
+    heads."""
+    U.say("prefill_conv varlen full size")
+    wl = make_workload(2, with_conv=True)
+    N = wl.n_seq
+    init = np.zeros((N, wl.H, wl.dk, wl.dv))
+    has = np.zeros(N, np.int32)
+    for s, i in enumerate(wl.init_index):
+        if i >= 0:
+            init[s] = wl.init_states[i].double().numpy()
+            has[s] = 1
+    conv_has = np.ones(N, np.int32)
+    x, w, st = wl.conv_x, wl.conv_w, wl.conv_state
+    got = _run(dev, wl, x, w, st, None, init, has, conv_has, act=1, norm=1, segment_len=4096)
+    # the new histories: the last 3 raw inputs of every sequence (each has >= 512 tokens)
+    cu = wl.cu_seqlens.numpy()
+    want = np.stack([x[cu[s + 1] - 3:cu[s + 1]].float().numpy().T for s in range(N)])
+    assert np.array_equal(got["conv"].to("cpu", torch.float32).numpy(), want)
+    lens = np.diff(cu)
+    pick = sorted({0, int(np.argmax(lens)), N - 1})
+    U.say(f"  oracle on sequences {pick} ({int(lens[pick].sum())} tokens)")
+    rows = np.concatenate([np.arange(cu[s], cu[s + 1]) for s in pick])
+    sub_cu = np.concatenate([[0], np.cumsum(lens[pick])]).astype(np.int32)
+    rt = torch.as_tensor(rows)
+    ref = oracle64.kda_prefill_conv(x[rt], w, wl.g[rt], wl.beta[rt], sub_cu, H=wl.H, d=wl.dk, act=1,
+                                    conv_state=st[pick], has_conv_state=conv_has[pick], qk_l2norm=1,
+                                    init=init[pick], has_init=has[pick])
+    o = got["o"][torch.as_tensor(rows, device=got["o"].device)]
+    U.assert_close("o (3 sequences)", U.to_np(o), ref["o"])
+    U.assert_close("final (3 sequences)", U.to_np(got["final"][pick]), ref["final"])
+    qkv = got["qkv"][torch.as_tensor(rows, device=got["qkv"].device)]
+    _check_qkv(qkv, ref, torch.bfloat16)
