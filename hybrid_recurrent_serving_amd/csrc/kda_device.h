@@ -83,11 +83,34 @@ __device__ __forceinline__ float sigmoid_fast(float x) {
 }
 __device__ __forceinline__ float silu_fast(float x) { return x * sigmoid_fast(x); }
 
-// Sum over the lanes that differ only in bits >= log2(FIRST) of the lane id.
+// Sum over the lanes that differ only in bits >= log2(FIRST) of the lane id,
+// without the LDS crossbar: inside a row of 16 lanes by DPP moves (quad
+// permutations for lane bits 0 and 1, row rotations by 4 and 8 for bits 2
+// and 3: after x += ror4(x) and x += ror8(x) every lane holds the sum of the
+// four lanes i, i +- 4, i +- 8 of its row that agree in bits 0 and 1), then
+// across rows by the gfx950 permlane swaps (rows 2r and 2r+1, then the two
+// halves of the wave; each swap of x with itself hands every lane the value
+// of its partner, and the sum is symmetric).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
 template <int FIRST>
 __device__ __forceinline__ float wave_sum_from(float x) {
-#pragma unroll
-  for (int m = FIRST; m < 64; m <<= 1) x += __shfl_xor(x, m, 64);
+  static_assert(FIRST == 1 || FIRST == 2 || FIRST == 4 || FIRST == 8 || FIRST == 16 || FIRST == 32 ||
+                FIRST == 64, "a power of two up to 64");
+  if constexpr (FIRST <= 1) x += dpp_mov<0xB1>(x);   // quad_perm [1, 0, 3, 2]
+  if constexpr (FIRST <= 2) x += dpp_mov<0x4E>(x);   // quad_perm [2, 3, 0, 1]
+  if constexpr (FIRST <= 4) x += dpp_mov<0x124>(x);  // row_ror:4
+  if constexpr (FIRST <= 8) x += dpp_mov<0x128>(x);  // row_ror:8
+  if constexpr (FIRST <= 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  if constexpr (FIRST <= 32) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
   return x;
 }
 

@@ -360,8 +360,6 @@ template <> struct Vec16x<float> {
   __device__ static __forceinline__ void st(float* p, const float (&x)[4]) { io<float>::st4(p, x); }
 };
 
-// SiLU x / (1 + exp(-x)) from the hardware exp2 and reciprocal (each within
-// about one ulp)
 
 // Gated RMS norm of one output vector of D channels held 4 per lane by
 // D / 4 consecutive lanes (sum of squares across them by butterfly
