@@ -102,26 +102,9 @@ __device__ __forceinline__ float conv_finish(float acc, int act) {
 // Per-head L2 normalisation of one output row (NL > 0 only): the NL = norm_d
 // / V threads that hold one head's channels are adjacent lanes of one wave
 // (their group starts at a multiple of NL, which divides 64), so the sum of
-// squares closes over them by a butterfly.  Inside a row of 16 lanes it runs
-// on DPP moves: the two quad permutations pair lanes 1 and 2 apart, then the
-// half-row mirror joins the two (now uniform) quads of each 8 lanes and the
-// row mirror the two halves; a 32-lane group adds the other row by one
-// cross-lane read.  NL is a template argument so that the reduction has no
-// branches and the rows of a tile overlap.  Channels at or past
-// norm_channels (the v block) keep their values.
-template <int NL>
-__device__ __forceinline__ float group_sum(float x) {
-  static_assert(NL == 2 || NL == 4 || NL == 8 || NL == 16 || NL == 32, "group of 2..32 lanes");
-  auto dpp = [](float v, auto ctrl) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), decltype(ctrl)::value, 0xf, 0xf, false));
-  };
-  x += dpp(x, std::integral_constant<int, 0xB1>{});                          // quad_perm [1, 0, 3, 2]
-  if constexpr (NL > 2) x += dpp(x, std::integral_constant<int, 0x4E>{});    // quad_perm [2, 3, 0, 1]
-  if constexpr (NL > 4) x += dpp(x, std::integral_constant<int, 0x141>{});   // row_half_mirror
-  if constexpr (NL > 8) x += dpp(x, std::integral_constant<int, 0x140>{});   // row_mirror
-  if constexpr (NL > 16) x += __shfl_xor(x, 16, 64);
-  return x;
-}
+// squares closes over them by group_sum.  NL is a template argument so that
+// the reduction has no branches and the rows of a tile overlap.  Channels at
+// or past norm_channels (the v block) keep their values.
 
 template <int NL, int V>
 __device__ __forceinline__ void norm_row(float (&out)[V], const ConvParams& p, int64_t c0) {

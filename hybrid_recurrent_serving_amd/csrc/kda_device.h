@@ -114,4 +114,24 @@ __device__ __forceinline__ float wave_sum_from(float x) {
   return x;
 }
 
+// Sum of x over aligned groups of NL adjacent lanes (NL = 2 .. 32, a power of
+// two; every lane of a group active).  Inside a row of 16 lanes on DPP moves:
+// the two quad permutations pair lanes 1 and 2 apart, then the half-row
+// mirror joins the two (now uniform) quads of each 8 lanes and the row mirror
+// the two halves; a 32-lane group adds the neighbouring row by the permlane
+// swap of rows 2r and 2r + 1.
+template <int NL>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(NL == 2 || NL == 4 || NL == 8 || NL == 16 || NL == 32, "group of 2..32 lanes");
+  x += dpp_mov<0xB1>(x);                          // quad_perm [1, 0, 3, 2]
+  if constexpr (NL > 2) x += dpp_mov<0x4E>(x);    // quad_perm [2, 3, 0, 1]
+  if constexpr (NL > 4) x += dpp_mov<0x141>(x);   // row_half_mirror
+  if constexpr (NL > 8) x += dpp_mov<0x140>(x);   // row_mirror
+  if constexpr (NL > 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  return x;
+}
+
 }  // namespace kda

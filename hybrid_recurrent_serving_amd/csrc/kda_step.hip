@@ -24,6 +24,8 @@
 // describes the fixed-size matrix state; the update rule is the gated delta
 // rule with per-key-channel decay).
 
+#include <type_traits>
+
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -922,9 +924,9 @@ static int launch_decode128_conv(const DecodeConvParams& p, hipStream_t stream) 
 // ---------------------------------------------------------------------------
 // Speculative verify with the short convolution fused in.  As the staged
 // verify of step_kernel, with q, k, v of the T_spec tokens formed by the
-// short convolution of the head's q, k, v channels (+ SiLU) and the q / k
-// norms of token j formed in the token loop from LDS (every wave, no extra
-// barrier).  The conv history is committed with the state: the W-1 raw
+// short convolution of the head's q, k, v channels (+ SiLU) and q / k
+// normalised per token in the same pass (the conv items of one block are
+// adjacent lanes).  The conv history is committed with the state: the W-1 raw
 // inputs ending at token L-1.
 //
 // Every conv input of the workgroup (history, taps, bias, the token rows of
@@ -942,19 +944,22 @@ __host__ __device__ constexpr int vconv_units(int n_tok) {
   constexpr int UPB = D * static_cast<int>(sizeof(Tin)) / 16;
   return 3 * (W - 1) * UPB + 3 * W * UPB + 3 * UPB + n_tok * 4 * UPB;
 }
-// staged units per thread, and the staging area in units: every thread
-// stores all of its units (those past the end into the area's tail), so no
-// load sits behind a condition the compiler could sink it into
-template <int D, typename Tin, int W>
+// staged units per thread for windows of up to TB tokens, and the staging
+// area in units: every thread stores all of its units (those past the end
+// into the area's tail), so no load sits behind a condition the compiler
+// could sink it into.  The area is sized by the window bucket (8 or 16
+// tokens), not the longest window: at 8 tokens it keeps the workgroup's LDS
+// small enough for four workgroups per CU.
+template <int D, typename Tin, int W, int TB>
 __host__ __device__ constexpr int vconv_per_thread() {
-  return (vconv_units<D, Tin, W>(STEP_TMAX) + 64 * StepLayout<D>::WPH - 1) / (64 * StepLayout<D>::WPH);
+  return (vconv_units<D, Tin, W>(TB) + 64 * StepLayout<D>::WPH - 1) / (64 * StepLayout<D>::WPH);
 }
-template <int D, typename Tin, int W>
+template <int D, typename Tin, int W, int TB>
 __host__ __device__ constexpr int vconv_stage_units() {
-  return vconv_per_thread<D, Tin, W>() * 64 * StepLayout<D>::WPH;
+  return vconv_per_thread<D, Tin, W, TB>() * 64 * StepLayout<D>::WPH;
 }
 
-template <int D, typename Tin, typename Tout, int W>
+template <int D, typename Tin, typename Tout, int W, int TB>
 __global__ void __launch_bounds__(64 * StepLayout<D>::WPH)
 verify_conv_kernel(const DecodeConvParams p) {
   using L = StepLayout<D>;
@@ -966,13 +971,13 @@ verify_conv_kernel(const DecodeConvParams p) {
   constexpr int U_HIST = 3 * HW * UPB;
   constexpr int U_TAPS = 3 * W * UPB;
   constexpr int U_FIX = U_HIST + U_TAPS + 3 * UPB;
-  constexpr int NU = vconv_per_thread<D, Tin, W>();   // staged units per thread
+  constexpr int NU = vconv_per_thread<D, Tin, W, TB>();   // staged units per thread
   static_assert(NCI <= NTH, "one conv item per thread");
   extern __shared__ __align__(16) float s_dyn[];
   const int T = p.T_spec;
   const int TD = T * D;
   uint4* const stg = reinterpret_cast<uint4*>(s_dyn);              // staged units
-  float* const fl = s_dyn + 4 * vconv_stage_units<D, Tin, W>();
+  float* const fl = s_dyn + 4 * vconv_stage_units<D, Tin, W, TB>();
   float* const s_a = fl;               // exp(g) [T][D]
   float* const s_k = fl + TD;          // k [T][D]
   float* const s_q = fl + 2 * TD;      // q [T][D]
@@ -1103,14 +1108,23 @@ verify_conv_kernel(const DecodeConvParams p) {
 #pragma unroll
     for (int k = 0; k < W; ++k) xbar(j + k, blk, cc, xbf[k]);
     float* yb = blk == 0 ? s_q : (blk == 1 ? s_k : s_v);
+    float yv[V];
 #pragma unroll
     for (int i = 0; i < V; ++i) {
       float acc = bs ? io<Tin>::ld(st_bias + blk * D + cc + i) : 0.f;
 #pragma unroll
       for (int k = 0; k < W; ++k) acc = fmaf(tapf[(i * W + k) / V][(i * W + k) % V], xbf[k][i], acc);
-      if (p.act == 1) acc = silu_fast(acc);
-      yb[j * D + cc + i] = acc;
+      yv[i] = p.act == 1 ? silu_fast(acc) : acc;
     }
+    // q / k normalisation of token j: the UPB items of a block are adjacent
+    // lanes (a block starts at a multiple of UPB, so does every item group)
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < V; ++i) ss = fmaf(yv[i], yv[i], ss);
+    ss = group_sum<UPB>(ss);
+    const float inv = (p.qk_l2norm && blk < 2) ? 1.f / sqrtf(ss + p.eps) : 1.f;
+#pragma unroll
+    for (int i = 0; i < V; ++i) yb[j * D + cc + i] = yv[i] * inv;
   }
   if (valid && cdst >= 0 && cdst < p.n_cslots && tid < NCI) {
     const int blk = tid / UPB, cc = (tid % UPB) * V;
@@ -1143,17 +1157,6 @@ verify_conv_kernel(const DecodeConvParams p) {
     for (int i = 0; i < L::RPL; ++i) st4_rsrc(rd, vd, i * D * 4, S[i]);
   }
   for (int j = 0; j < n_tok; ++j) {
-    float inv_q = 1.f, inv_k = 1.f;
-    if (p.qk_l2norm) {
-      float sq = 0.f, sk = 0.f;
-#pragma unroll
-      for (int c = lane; c < D; c += 64) {
-        sq = fmaf(s_q[j * D + c], s_q[j * D + c], sq);
-        sk = fmaf(s_k[j * D + c], s_k[j * D + c], sk);
-      }
-      inv_q = 1.f / sqrtf(wave_sum_from<1>(sq) + p.eps);
-      inv_k = 1.f / sqrtf(wave_sum_from<1>(sk) + p.eps);
-    }
     float kr[L::RPL], qr[L::RPL], ar[L::RPL], vc[4];
 #pragma unroll
     for (int i = 0; i < L::RPL; i += 4) {
@@ -1176,13 +1179,11 @@ verify_conv_kernel(const DecodeConvParams p) {
         w[c] = fmaf(S[i][c], kr[i], w[c]);
       }
     }
-    // the norms act on the reduced values: w = inv_k S^T k, S += k (inv_k u)^T,
-    // o = inv_q S^T q
     float uk[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      w[c] = wave_sum_from<L::LPR>(w[c]) * inv_k;
-      uk[c] = beta * (vc[c] - w[c]) * inv_k;
+      w[c] = wave_sum_from<L::LPR>(w[c]);
+      uk[c] = beta * (vc[c] - w[c]);
     }
     float o[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -1195,7 +1196,7 @@ verify_conv_kernel(const DecodeConvParams p) {
     }
     if (p.o) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) o[c] = wave_sum_from<L::LPR>(o[c]) * (inv_q * p.scale);
+      for (int c = 0; c < 4; ++c) o[c] = wave_sum_from<L::LPR>(o[c]) * p.scale;
       if (rg == 0) *reinterpret_cast<float4*>(&s_o[j * D + col]) = make_float4(o[0], o[1], o[2], o[3]);
     }
     if (do_store && j + 1 == Lc) {
@@ -1228,15 +1229,20 @@ static int launch_verify_conv_t(const DecodeConvParams& p, hipStream_t stream) {
   dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(p.n_seq) * p.H));
   dim3 block(64 * L::WPH);
   const size_t fl = (4 * static_cast<size_t>(p.T_spec) * D + 64 * L::WPH) * sizeof(float);
-  auto lds = [&](int W) -> size_t {
-    const int u = W == 2 ? vconv_stage_units<D, Tin, 2>()
-                         : (W == 3 ? vconv_stage_units<D, Tin, 3>() : vconv_stage_units<D, Tin, 4>());
-    return 16 * static_cast<size_t>(u) + fl;
+  // the window bucket: every kernel instance stages at most TB tokens
+  auto go = [&](auto w_t, auto tb_t) {
+    constexpr int W = decltype(w_t)::value, TB = decltype(tb_t)::value;
+    const size_t lds = 16 * static_cast<size_t>(vconv_stage_units<D, Tin, W, TB>()) + fl;
+    hipLaunchKernelGGL((verify_conv_kernel<D, Tin, Tout, W, TB>), grid, block, lds, stream, p);
+  };
+  auto go_w = [&](auto w_t) {
+    if (p.T_spec <= 8) go(w_t, std::integral_constant<int, 8>{});
+    else go(w_t, std::integral_constant<int, STEP_TMAX>{});
   };
   switch (p.W) {
-    case 2: hipLaunchKernelGGL((verify_conv_kernel<D, Tin, Tout, 2>), grid, block, lds(2), stream, p); break;
-    case 3: hipLaunchKernelGGL((verify_conv_kernel<D, Tin, Tout, 3>), grid, block, lds(3), stream, p); break;
-    case 4: hipLaunchKernelGGL((verify_conv_kernel<D, Tin, Tout, 4>), grid, block, lds(4), stream, p); break;
+    case 2: go_w(std::integral_constant<int, 2>{}); break;
+    case 3: go_w(std::integral_constant<int, 3>{}); break;
+    case 4: go_w(std::integral_constant<int, 4>{}); break;
     default: return fail(KDA_ERR_UNSUPPORTED, "verify_conv: W = %d (2..4)", p.W);
   }
   hipError_t e = hipGetLastError();
