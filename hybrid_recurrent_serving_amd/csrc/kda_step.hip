@@ -983,6 +983,8 @@ verify_conv_kernel(const DecodeConvParams p) {
   float* const s_q = fl + 2 * TD;      // q [T][D]
   float* const s_v = fl + 3 * TD;      // v [T][D]
   float* const s_b = fl + 4 * TD;      // beta [T] (one slot per thread: every thread stores one)
+  // the conv history element-major, [W-1][3][D] (16-byte rows like the tokens)
+  Tin* const s_h = reinterpret_cast<Tin*>(fl + 4 * TD + NTH);
   float* const s_o = s_dyn;            // o [T][D], over the staged units (dead once the conv has run)
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1067,10 +1069,23 @@ verify_conv_kernel(const DecodeConvParams p) {
     }
   }
 
-  // 3. units and beta to LDS
+  // 3. units and beta to LDS; the history units also scattered element-major
+  //    (zeros without a history: those units hold taps)
 #pragma unroll
-  for (int k = 0; k < NU; ++k)
+  for (int k = 0; k < NU; ++k) {
     stg[k * NTH + tid] = raw[k];
+    const int u = k * NTH + tid;
+    if (u < U_HIST) {
+      const int blk = u / (HW * UPB), r = u % (HW * UPB);
+      const Tin* el = reinterpret_cast<const Tin*>(&raw[k]);
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        const int f = r * V + e;             // element ch * HW + q of the block
+        const int ch = f / HW, q = f % HW;
+        s_h[(q * 3 + blk) * D + ch] = hist_ok ? el[e] : Tin(0);
+      }
+    }
+  }
   s_b[tid] = io<Tin>::ld(&braw);
   __syncthreads();
 
@@ -1091,12 +1106,8 @@ verify_conv_kernel(const DecodeConvParams p) {
   auto xbar = [&](const int idx, const int blk, const int cc, float (&x)[V]) __attribute__((always_inline)) {
     if (idx >= HW) {
       Vec16x<Tin>::ld(st_x + (static_cast<int64_t>(idx - HW) * 3 + blk) * D + cc, x);
-    } else if (hist_ok) {
-#pragma unroll
-      for (int i = 0; i < V; ++i) x[i] = io<Tin>::ld(st + (blk * D + cc + i) * HW + idx);
     } else {
-#pragma unroll
-      for (int i = 0; i < V; ++i) x[i] = 0.f;
+      Vec16x<Tin>::ld(s_h + (idx * 3 + blk) * D + cc, x);
     }
   };
   for (int it = tid; it < n_tok * NCI; it += NTH) {
@@ -1124,7 +1135,9 @@ verify_conv_kernel(const DecodeConvParams p) {
     ss = group_sum<UPB>(ss);
     const float inv = (p.qk_l2norm && blk < 2) ? 1.f / sqrtf(ss + p.eps) : 1.f;
 #pragma unroll
-    for (int i = 0; i < V; ++i) yb[j * D + cc + i] = yv[i] * inv;
+    for (int i = 0; i < V; i += 4)
+      *reinterpret_cast<float4*>(&yb[j * D + cc + i]) =
+          make_float4(yv[i] * inv, yv[i + 1] * inv, yv[i + 2] * inv, yv[i + 3] * inv);
   }
   if (valid && cdst >= 0 && cdst < p.n_cslots && tid < NCI) {
     const int blk = tid / UPB, cc = (tid % UPB) * V;
@@ -1228,7 +1241,8 @@ static int launch_verify_conv_t(const DecodeConvParams& p, hipStream_t stream) {
   using L = StepLayout<D>;
   dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(p.n_seq) * p.H));
   dim3 block(64 * L::WPH);
-  const size_t fl = (4 * static_cast<size_t>(p.T_spec) * D + 64 * L::WPH) * sizeof(float);
+  const size_t fl = (4 * static_cast<size_t>(p.T_spec) * D + 64 * L::WPH) * sizeof(float) +
+                    (static_cast<size_t>(p.W - 1) * 3 * D * sizeof(Tin) + 15) / 16 * 16;
   // the window bucket: every kernel instance stages at most TB tokens
   auto go = [&](auto w_t, auto tb_t) {
     constexpr int W = decltype(w_t)::value, TB = decltype(tb_t)::value;
