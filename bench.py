@@ -73,8 +73,12 @@ def parse():
 
 
 def kernel_source_hash(name: str) -> str:
-    src = ROOT / "hybrid_recurrent_serving_amd" / "csrc" / name
-    return hashlib.sha256(src.read_bytes()).hexdigest()[:16]
+    """The kernel's source file together with the device headers it includes."""
+    csrc = ROOT / "hybrid_recurrent_serving_amd" / "csrc"
+    h = hashlib.sha256()
+    for f in (name, "kda_device.h", "kda_internal.h"):
+        h.update((csrc / f).read_bytes())
+    return h.hexdigest()[:16]
 
 
 def traffic_for(kernel_key: str, src_name: str, per_launch_units: float):
@@ -147,13 +151,19 @@ def pmc_pass(torch, K, make_workload, long=False):
     torch.cuda.empty_cache()
     bench_prefill_varlen(torch, K, make_workload, dev, iters=PMC_PREFILL_CALLS - 2)   # + 2 warm-up calls
     torch.cuda.synchronize()
-    torch.cuda.empty_cache()
-    bench_prefill_conv(torch, K, make_workload(2), dev, iters=1)   # 3 conv + 6 prefill launches
-    torch.cuda.synchronize()
     if long:
         torch.cuda.empty_cache()
         bench_prefill_long(torch, K, make_workload, dev, iters=PMC_LONG_CALLS - 1)   # + 1 warm-up call
         torch.cuda.synchronize()
+    # the conv at prefill scale (3 + 1 launches) and the prefill from raw
+    # projections (3 calls, 3 prefills alone, 3 conv + norm launches alone),
+    # after every prefill call the ingest counts by position
+    torch.cuda.empty_cache()
+    wl2 = make_workload(2)
+    bench_conv_prefill(torch, K, wl2, dev, iters=1)
+    torch.cuda.empty_cache()
+    bench_prefill_conv(torch, K, wl2, dev, iters=1)
+    torch.cuda.synchronize()
 
 
 def varlen_tokens():
@@ -184,11 +194,21 @@ def ingest_pmc(fetch_csv, write_csv):
         raise SystemExit("calibration copy not found in the counter files")
     f_scale = COPY_BYTES / (sum(cf) / len(cf))
     w_scale = COPY_BYTES / (sum(cw) / len(cw))
+    def named(part):
+        return lambda r: part in r["Kernel_Name"].replace(" ", "")
+
     for key, pred, src, units in (
             ("decode_step_kernel_d128_bf16", lambda r: is_decode128(r["Kernel_Name"], 0), "kda_step.hip",
              128 * 16),
             ("decode_conv_kernel_d128_bf16", lambda r: is_decode128(r["Kernel_Name"], 4),
-             "kda_step.hip", 128 * 16)):
+             "kda_step.hip", 128 * 16),
+            ("verify_step_kernel_d128_bf16", named("step_kernel<128,unsignedshort,unsignedshort,true>"),
+             "kda_step.hip", 128 * 16),
+            ("verify_conv_kernel_d128_bf16", named("verify_conv_kernel<128,unsignedshort,unsignedshort,4,8>"),
+             "kda_step.hip", 128 * 16),
+            ("conv_kernel_prefill_bf16", named("conv_kernel<unsignedshort,4,0>"), "kda_conv.hip", varlen_tokens()),
+            ("conv_norm_kernel_prefill_bf16", named("conv_kernel<unsignedshort,4,16>"), "kda_conv.hip",
+             varlen_tokens())):
         f = sel("FETCH_SIZE", pred)
         w = sel("WRITE_SIZE", pred)
         if not f or not w:
@@ -260,7 +280,7 @@ def ingest_mfma(paths):
         for key, pred in (("decode_conv_kernel_d128_bf16", lambda n: is_decode128(n, 4)),
                           ("decode_step_kernel_d128_bf16", lambda n: is_decode128(n, 0)),
                           ("verify_kernel_d128_bf16", lambda n: n.startswith("void kda::step_kernel<128, unsigned short, unsigned short, true>")),
-                          ("verify_conv_kernel_d128_bf16", lambda n: n.startswith("void kda::verify_conv_kernel<128, unsigned short, unsigned short, 4>"))):
+                          ("verify_conv_kernel_d128_bf16", lambda n: n.startswith("void kda::verify_conv_kernel<128, unsigned short, unsigned short, 4, 8>"))):
             ds = [d for d in order if pred(d["name"])]
             if not ds or key in out:
                 continue
@@ -633,11 +653,18 @@ def bench_verify_secondary(torch, K, make_workload, dev, n=200, warm=10, cpu_sec
     torch.cuda.synchronize()
     us2 = a_.elapsed_time(b2) / n * 1e3
     io2 = N * Ts * (C * 2 + H * (D * 2 + 2 + D * 2 + D * 2)) + N * C * (W - 1) * 2 * 2 + C * W * 2 + D * 2
+    alg2 = state_bytes + io2
     res["fused_conv"] = {"call": "kda_verify_conv (conv + SiLU + q/k norm + verify + gated output norm, "
                                  "state and conv history committed at L)", "us": round(us2, 2),
                          "state_GB_s": round(state_bytes / us2 / 1e3, 1),
-                         "alg_GB_s": round((state_bytes + io2) / us2 / 1e3, 1),
-                         "hbm_frac": round((state_bytes + io2) / us2 / 1e3 / HBM_PEAK_GBS, 4)}
+                         "alg_GB_s": round(alg2 / us2 / 1e3, 1),
+                         "hbm_frac": round(alg2 / us2 / 1e3 / HBM_PEAK_GBS, 4),
+                         "roofline": {"kernel": "verify_conv_kernel<128,bf16,bf16,W=4,window 8> (kda_verify_conv, "
+                                                "one launch per call)", "bound": "hbm",
+                                      "achieved": round(alg2 / us2 / 1e3, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                      "frac": round(alg2 / us2 / 1e3 / HBM_PEAK_GBS, 4),
+                                      "traffic": traffic_for("verify_conv_kernel_d128_bf16", "kda_step.hip", N * H),
+                                      "alg_bytes_per_launch": alg2, "avg_launch_us": round(us2, 3)}}
     return res
 
 

@@ -83,3 +83,32 @@ def test_ingest_pmc_calibrates_and_splits_calls(tmp_path, tokens):
         assert e["units_per_launch"] == units
         assert e["fetch_bytes"] == round(2 * 10.0 * 1024 * 2)   # two dispatches per call, scaled x 2
         assert e["write_bytes"] == round(2 * 4.0 * 1024)
+
+
+def test_ingest_pmc_single_kernels(tmp_path, tokens):
+    """The verify, fused verify and prefill-scale conv kernels: their
+    dispatches averaged, each counter scaled by the calibration copy."""
+    names = {"verify_step_kernel_d128_bf16": "void kda::step_kernel<128, unsigned short, unsigned short, true>(kda::StepParams)",
+             "verify_conv_kernel_d128_bf16": "void kda::verify_conv_kernel<128, unsigned short, unsigned short, 4, 8>(kda::DecodeConvParams)",
+             "conv_kernel_prefill_bf16": "void kda::conv_kernel<unsigned short, 4, 0>(kda::ConvParams)",
+             "conv_norm_kernel_prefill_bf16": "void kda::conv_kernel<unsigned short, 4, 16>(kda::ConvParams)"}
+
+    def rows_for(counter, copy_val):
+        rows, did = [], 0
+        for name, val in [(COPY, copy_val)] + [(n, 8.0 + i) for i, n in enumerate(names.values()) for _ in range(2)]:
+            did += 1
+            rows.append({"Dispatch_Id": did, "Kernel_Name": name, "Counter_Name": counter, "Counter_Value": val})
+        return rows
+
+    kib = bench.COPY_BYTES / 1024
+    fp, wp = tmp_path / "f.csv", tmp_path / "w.csv"
+    _write(fp, rows_for("FETCH_SIZE", kib / 2))
+    _write(wp, rows_for("WRITE_SIZE", kib))
+    out = bench.ingest_pmc(str(fp), str(wp))
+    for i, key in enumerate(names):
+        e = out[key]
+        assert e["dispatches"] == 2
+        assert e["fetch_bytes"] == round((8.0 + i) * 1024 * 2)
+        assert e["write_bytes"] == round((8.0 + i) * 1024)
+    assert out["verify_step_kernel_d128_bf16"]["units_per_launch"] == 128 * 16
+    assert out["conv_norm_kernel_prefill_bf16"]["units_per_launch"] == tokens
