@@ -125,7 +125,17 @@ __global__ void __launch_bounds__(CONV_THREADS) conv_kernel(const ConvParams p) 
   constexpr bool NORM = NL > 0;
   constexpr int V = Vec16<T>::N;
   constexpr int HIST = W - 1;
-  const int item = blockIdx.x;
+  // Workgroups go to the 8 XCDs round robin (x fastest); item indices are
+  // handed out so that each XCD takes one contiguous run of them: the tile
+  // after a tile then runs on the same XCD, and the W-1 rows it reads ahead
+  // of its own are still in that XCD's L2.  A bijection of [0, gridDim.x).
+  int item;
+  {
+    const int nb = static_cast<int>(gridDim.x);
+    const int x8 = static_cast<int>(blockIdx.x) % 8, s8 = static_cast<int>(blockIdx.x) / 8;
+    const int q = nb / 8, r = nb % 8;
+    item = x8 * q + (x8 < r ? x8 : r) + s8;
+  }
   const int64_t c0 = (static_cast<int64_t>(blockIdx.y) * CONV_THREADS + threadIdx.x) * V;
   // threads past the last channel stay for the workgroup barrier of body items
   const bool active = c0 < p.C;
