@@ -220,8 +220,15 @@ class Oracle:
         history of each sequence is the last W-1 raw inputs of history ++
         tokens.
 
-        Returns the dict of :meth:`kda_varlen` plus conv_state [N, 3 H d, W-1]
-        and the operands q, k, v [T, H, d] (float32)."""
+        With ckpt_interval > 0, every checkpoint of the recurrence (the
+        positions of :meth:`ckpt_enumerate`) also gets the conv history a
+        resumed run needs: the last W-1 raw inputs of history ++ tokens before
+        the checkpoint's position, the new-state rule of :meth:`conv_short`
+        after that many tokens.
+
+        Returns the dict of :meth:`kda_varlen` plus conv_state [N, 3 H d, W-1],
+        conv_ckpt [n_ckpt, 3 H d, W-1] and the operands q, k, v [T, H, d]
+        (float32)."""
         xa = np.asarray(_as_f32(x), np.float32)
         T, C = xa.shape
         if C != 3 * H * d:
@@ -231,7 +238,25 @@ class Oracle:
         q, k, v = conv_operands(y, H, d, qk_l2norm, norm_eps, operand_dtype)
         res = self.kda_varlen(q, k, v, g, beta, cu_seqlens, init=init, has_init=has_init,
                               start_pos=start_pos, scale=scale, ckpt_interval=ckpt_interval)
+        cu = _as_i32(cu_seqlens)
+        W = np.asarray(_as_f32(w)).shape[1]
+        sp = np.zeros(cu.size - 1, np.int64) if start_pos is None else np.asarray(_as_i32(start_pos), np.int64)
+        ck_cu, ck_pos = res["ckpt_cu"], res["ckpt_pos"]
+        cst = None if conv_state is None else np.asarray(_as_f32(conv_state), np.float32)
+        hs = None if has_conv_state is None else np.asarray(_as_i32(has_conv_state))
+        conv_ckpt = np.zeros((int(ck_cu[-1]), C, W - 1), self.real)
+        for s in range(cu.size - 1):
+            for j in range(int(ck_cu[s]), int(ck_cu[s + 1])):
+                rel = int(ck_pos[j] - sp[s])   # tokens of the sequence before the checkpoint
+                one_hist = None
+                if cst is not None and (hs is None or hs[s]):
+                    one_hist = cst[s:s + 1]
+                _, st = self.conv_short(xa[cu[s]:cu[s + 1]], w, np.array([0, cu[s + 1] - cu[s]], np.int32),
+                                        bias=bias, act=act, state=one_hist,
+                                        advance_len=np.array([rel], np.int32))
+                conv_ckpt[j] = st[0]
         res["conv_state"] = ns
+        res["conv_ckpt"] = conv_ckpt
         res["q"], res["k"], res["v"] = q, k, v
         return res
 

@@ -513,6 +513,24 @@ def pin_prefill_conv(orc):
     assert np.array_equal(np.concatenate([one["o"], two["o"]]), full["o"])
     assert np.array_equal(two["final"], full["final"])
     assert np.array_equal(two["conv_state"], full["conv_state"])
+    # the same split through an interval checkpoint of the continuous run:
+    # its recurrent state and conv history resume the tail bit for bit
+    ck = orc.kda_prefill_conv(x[cu[2]:cu[3]], w, g[cu[2]:cu[3]], beta[cu[2]:cu[3]],
+                              np.array([0, cu[3] - cu[2]], np.int32), H=H, d=d, bias=bias, act=1, qk_l2norm=1,
+                              ckpt_interval=4)
+    assert list(ck["ckpt_pos"]) == [4, 8]
+    assert np.array_equal(ck["o"], full["o"]) and np.array_equal(ck["ckpt"][0], one["final"][0])
+    assert np.array_equal(ck["conv_ckpt"][0], one["conv_state"][0])
+    tail = orc.kda_prefill_conv(x[p:cu[3]], w, g[p:cu[3]], beta[p:cu[3]], np.array([0, cu[3] - p], np.int32),
+                                H=H, d=d, bias=bias, act=1, conv_state=ck["conv_ckpt"][0].astype(np.float32)[None],
+                                qk_l2norm=1, init=ck["ckpt"][0][None], start_pos=np.array([4], np.int32))
+    assert np.array_equal(tail["o"], full["o"][4:]) and np.array_equal(tail["final"], full["final"])
+    # a checkpoint inside the first W-1 tokens takes part of its history from
+    # the carried one: the raw inputs before position 2 of sequence 0
+    c2 = orc.kda_prefill_conv(x[:cu[1]], w, g[:cu[1]], beta[:cu[1]], np.array([0, cu[1]], np.int32), H=H, d=d,
+                              act=1, conv_state=cst[:1], qk_l2norm=1, ckpt_interval=2)
+    want = np.concatenate([cst[0], x[:2].T], axis=1)[:, -(W - 1):]
+    assert list(c2["ckpt_pos"])[:1] == [2] and np.array_equal(c2["conv_ckpt"][0], want)
     # normalisation: positive scalings of the q and k projections (linear
     # conv, no activation, no bias, eps = 0) leave everything unchanged
     b0 = orc.kda_prefill_conv(x, w, g, beta, cu, H=H, d=d, conv_state=cst, has_conv_state=has_c,
