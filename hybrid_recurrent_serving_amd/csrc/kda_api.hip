@@ -625,11 +625,33 @@ int kda_prefill_varlen_conv(const kda_prefill_conv_args* a, kda_stream_t stream_
     return fail(KDA_ERR_WORKSPACE, "prefill_conv: qkv %lld bytes < %lld needed", (long long)a->qkv_bytes,
                 (long long)(b.T_tot * C * eb));
   if (b.T_tot / 16 + b.n_seq + 1 > 0x7fffffffLL) return fail(KDA_ERR_SHAPE, "prefill_conv: too many tokens");
+  const bool conv_ckpt = a->conv_ckpt_slot != nullptr && b.n_ckpt > 0;
+  if (a->conv_ckpt_slot && b.ckpt_interval <= 0)
+    return fail(KDA_ERR_ARG, "prefill_conv: conv_ckpt_slot given without checkpoints (ckpt_interval 0)");
+  if (b.n_ckpt > 0x7fffffffLL) return fail(KDA_ERR_SHAPE, "prefill_conv: too many checkpoints");
   PrefillParams p = prefill_params(b);
   if ((st = prefill_precheck(b, p, stream))) return st;
   if (check_enabled()) {
-    st = check_slots(a->conv_src_slot, a->conv_dst_slot, b.n_seq, a->n_conv_slots, nullptr, stream);
+    std::vector<int32_t> cck;
+    if (conv_ckpt) {
+      if (!copy_to_host(cck, a->conv_ckpt_slot, (size_t)b.n_ckpt, stream))
+        return fail(KDA_ERR_HIP, "KDA_CHECK: copy failed");
+      for (int32_t c : cck)
+        if (c < -1 || c >= a->n_conv_slots) return fail(KDA_ERR_ARG, "conv_ckpt_slot %d out of range", c);
+    }
+    st = check_slots(a->conv_src_slot, a->conv_dst_slot, b.n_seq, a->n_conv_slots, conv_ckpt ? &cck : nullptr,
+                     stream);
     if (st) return st;
+  }
+  if (conv_ckpt) {
+    // before the conv launch: it reads the source histories, which that
+    // launch may advance in place
+    ConvCkptParams kp{};
+    kp.x = a->x; kp.pool = a->conv_pool; kp.cu = b.cu_seqlens; kp.start_pos = b.start_pos;
+    kp.src_slot = a->conv_src_slot; kp.ckpt_cu = b.ckpt_cu; kp.ckpt_slot = a->conv_ckpt_slot;
+    kp.x_stride = x_stride; kp.T_tot = b.T_tot; kp.n_slots = a->n_conv_slots; kp.n_ckpt = b.n_ckpt;
+    kp.n_seq = b.n_seq; kp.C = static_cast<int32_t>(C); kp.W = a->W; kp.interval = b.ckpt_interval;
+    if ((st = launch_conv_ckpt(kp, in_dt, stream))) return st;
   }
   ConvParams cp{};
   cp.x = a->x; cp.y = a->qkv; cp.w = a->conv_weight; cp.bias = a->conv_bias; cp.cu = b.cu_seqlens;

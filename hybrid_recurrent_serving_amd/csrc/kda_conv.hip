@@ -348,6 +348,90 @@ static int launch_conv_w(const ConvParams& p, hipStream_t stream) {
   }
 }
 
+// One workgroup per (checkpoint, 256 channel vectors); each thread copies the
+// W-1 raw inputs before the checkpoint of its V channels: from the carried
+// history where the checkpoint lies within the sequence's first W-1 tokens,
+// else from x.  Reads only the source slots and x, so it runs before the
+// conv launch, which may update the history in place.
+template <typename T, int W>
+__global__ void __launch_bounds__(CONV_THREADS) conv_ckpt_kernel(const ConvCkptParams p) {
+  constexpr int V = Vec16<T>::N;
+  constexpr int HIST = W - 1;
+  const int64_t j = blockIdx.x;
+  const int64_t c0 = (static_cast<int64_t>(blockIdx.y) * CONV_THREADS + threadIdx.x) * V;
+  if (c0 >= p.C || j >= p.n_ckpt || j >= p.ckpt_cu[p.n_seq]) return;
+  int a = 0, b = p.n_seq;                 // ckpt_cu[a] <= j < ckpt_cu[b]
+  while (b - a > 1) {
+    const int mid = (a + b) >> 1;
+    if (p.ckpt_cu[mid] <= j) a = mid; else b = mid;
+  }
+  const int s = a;
+  const int slot = p.ckpt_slot[j];
+  if (slot < 0 || slot >= p.n_slots) return;
+  int64_t bos = p.cu[s], eos = p.cu[s + 1];
+  bos = bos < 0 ? 0 : (bos > p.T_tot ? p.T_tot : bos);
+  eos = eos < bos ? bos : (eos > p.T_tot ? p.T_tot : eos);
+  int64_t start = p.start_pos ? static_cast<int64_t>(p.start_pos[s]) : 0;
+  if (start < 0) start = 0;
+  const int64_t pos = (start / p.interval + 1 + (j - p.ckpt_cu[s])) * p.interval;
+  const int64_t rel = pos - start;        // tokens of the sequence before the checkpoint
+  if (rel <= 0 || rel >= eos - bos) return;
+  const T* xb = static_cast<const T*>(p.x);
+  const int src = p.src_slot[s];
+  const bool has_src = src >= 0 && src < p.n_slots;
+  float hist[HIST * V];                   // [i * HIST + q]: channel c0 + i, history entry q
+  if (has_src) {
+    ld_blocks<T, HIST>(static_cast<const T*>(p.pool) + (static_cast<int64_t>(src) * p.C + c0) * HIST, hist);
+  } else {
+#pragma unroll
+    for (int e = 0; e < HIST * V; ++e) hist[e] = 0.f;
+  }
+  float out[HIST * V];
+#pragma unroll
+  for (int q = 0; q < HIST; ++q) {
+    const int64_t idx = rel + q;          // index into history ++ tokens
+    float xv[V];
+    if (idx >= HIST) {
+      Vec16<T>::ld(xb + (bos + idx - HIST) * p.x_stride + c0, xv);
+    } else {
+#pragma unroll
+      for (int i = 0; i < V; ++i) {
+        float v = hist[i * HIST];
+#pragma unroll
+        for (int r = 1; r < HIST; ++r) v = idx == r ? hist[i * HIST + r] : v;
+        xv[i] = v;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < V; ++i) out[i * HIST + q] = xv[i];
+  }
+  st_blocks<T, HIST>(static_cast<T*>(p.pool) + (static_cast<int64_t>(slot) * p.C + c0) * HIST, out);
+}
+
+int launch_conv_ckpt(const ConvCkptParams& p, int dtype, hipStream_t stream) {
+  if (p.n_ckpt <= 0) return KDA_OK;
+  const int V = dtype == KDA_BF16 ? 8 : 4;
+  const int64_t groups = (p.C + V - 1) / V;
+  const dim3 grid(static_cast<uint32_t>(p.n_ckpt), static_cast<uint32_t>((groups + CONV_THREADS - 1) / CONV_THREADS));
+  auto go = [&](auto t_tag, auto w_t) {
+    using T = decltype(t_tag);
+    hipLaunchKernelGGL((conv_ckpt_kernel<T, decltype(w_t)::value>), grid, dim3(CONV_THREADS), 0, stream, p);
+  };
+  auto by_w = [&](auto t_tag) -> int {
+    switch (p.W) {
+      case 2: go(t_tag, std::integral_constant<int, 2>{}); return KDA_OK;
+      case 3: go(t_tag, std::integral_constant<int, 3>{}); return KDA_OK;
+      case 4: go(t_tag, std::integral_constant<int, 4>{}); return KDA_OK;
+      default: return fail(KDA_ERR_UNSUPPORTED, "conv checkpoints: W = %d (2..4)", p.W);
+    }
+  };
+  const int st = dtype == KDA_BF16 ? by_w(bf16_t{}) : by_w(float{});
+  if (st) return st;
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, "conv checkpoint kernel launch: %s", hipGetErrorString(e));
+  return KDA_OK;
+}
+
 int launch_conv(const ConvParams& p0, int dtype, hipStream_t stream) {
   ConvParams p = p0;
   p.n_tiles = static_cast<int32_t>((p.T_tot + CONV_TT - 1) / CONV_TT);

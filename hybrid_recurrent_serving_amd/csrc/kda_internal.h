@@ -88,6 +88,19 @@ struct ConvParams {
 
 int launch_conv(const ConvParams& p, int dtype, hipStream_t stream);
 
+// Conv history at the interval checkpoints of a prefill: checkpoint j of
+// sequence s (ckpt_cu[s] <= j < ckpt_cu[s + 1]) at absolute position
+// (start / I + 1 + j - ckpt_cu[s]) * I gets the W-1 raw inputs of
+// history ++ tokens before it, in conv_pool[ckpt_slot[j]].
+struct ConvCkptParams {
+  const void* x;
+  void* pool;
+  const int32_t *cu, *start_pos, *src_slot, *ckpt_cu, *ckpt_slot;
+  int64_t x_stride, T_tot, n_slots, n_ckpt;
+  int32_t n_seq, C, W, interval;
+};
+int launch_conv_ckpt(const ConvCkptParams& p, int dtype, hipStream_t stream);
+
 // ---------------------------------------------------------------- prefill
 struct PrefillParams {
   const void *q, *k, *v, *g, *beta;

@@ -75,7 +75,7 @@ class PrefillConvArgs(ctypes.Structure):
         ("struct_size", c_size),
         ("prefill", PrefillArgs),
         ("x", c_vp), ("conv_weight", c_vp), ("conv_bias", c_vp), ("conv_pool", c_vp),
-        ("conv_src_slot", c_vp), ("conv_dst_slot", c_vp), ("qkv", c_vp),
+        ("conv_src_slot", c_vp), ("conv_dst_slot", c_vp), ("conv_ckpt_slot", c_vp), ("qkv", c_vp),
         ("x_stride", c_i64), ("n_conv_slots", c_i64), ("qkv_bytes", c_i64),
         ("W", c_i32), ("act", c_i32), ("qk_l2norm", c_i32), ("norm_eps", c_f32),
     ]
@@ -504,9 +504,11 @@ def kda_prefill_varlen_conv(x, conv_weight, conv_pool, conv_src_slot, conv_dst_s
                             state_pool, src_slot, dst_slot, *, qkv=None, conv_bias=None, act: int = 0,
                             qk_l2norm: bool = True, norm_eps: float = 1e-6, chunk=64, start_pos=None,
                             ckpt_interval=0, ckpt_cu=None, ckpt_slot=None, ckpt_pos_out=None, workspace=None,
-                            scale=1.0, segment_len=0, stream=None):
+                            scale=1.0, segment_len=0, conv_ckpt_slot=None, stream=None):
     """Prefill from the tokens' raw projections: the short conv (+ SiLU),
     per-head q / k normalisation and the chunked prefill (include/kda.h).
+    ``conv_ckpt_slot`` [n_ckpt]: conv pool slots that receive the conv
+    history at each interval checkpoint.
 
     x [T, 3 H d] (q | k | v projections, packed rows); conv_weight
     [3 H d, W]; conv_pool [n_conv_slots, 3 H d, W-1]; g [T, H, d]; beta
@@ -528,7 +530,9 @@ def kda_prefill_varlen_conv(x, conv_weight, conv_pool, conv_src_slot, conv_dst_s
     _expect(tuple(qkv.shape) == (T, C) and qkv.is_contiguous() and qkv.dtype == x.dtype,
             "qkv must be a packed [T, 3 H d] tensor of x's dtype")
     _device_tensors(x=x, conv_weight=conv_weight, conv_pool=conv_pool, conv_src_slot=conv_src_slot,
-                    conv_dst_slot=conv_dst_slot, conv_bias=conv_bias, qkv=qkv)
+                    conv_dst_slot=conv_dst_slot, conv_bias=conv_bias, qkv=qkv, conv_ckpt_slot=conv_ckpt_slot)
+    _expect(conv_ckpt_slot is None or ckpt_slot is None or conv_ckpt_slot.numel() >= ckpt_slot.numel(),
+            "conv_ckpt_slot shorter than ckpt_slot")
     _same_dtype(x, conv_weight=conv_weight, conv_pool=conv_pool, g=g)
     if conv_bias is not None:
         _same_dtype(x, conv_bias=conv_bias)
@@ -551,6 +555,7 @@ def kda_prefill_varlen_conv(x, conv_weight, conv_pool, conv_src_slot, conv_dst_s
     a.prefill = pa
     a.x, a.conv_weight, a.conv_bias, a.conv_pool = _ptr(x), _ptr(conv_weight), _ptr(conv_bias), _ptr(conv_pool)
     a.conv_src_slot, a.conv_dst_slot, a.qkv = _ptr(conv_src_slot), _ptr(conv_dst_slot), _ptr(qkv)
+    a.conv_ckpt_slot = _ptr(conv_ckpt_slot)
     a.x_stride = x.stride(0) if T else 0
     a.n_conv_slots = conv_pool.shape[0]
     a.qkv_bytes = qkv.numel() * qkv.element_size()

@@ -316,6 +316,13 @@ int kda_prefill_varlen(const kda_prefill_args *args, kda_stream_t stream);
  * The conv history of s is read from conv_pool[conv_src_slot[s]] (zeros when
  * -1) and the last W-1 raw inputs of history ++ tokens are written to
  * conv_pool[conv_dst_slot[s]] (not when -1); src == dst is allowed.
+ * With conv_ckpt_slot, every interval checkpoint j of the prefill (the
+ * positions and table of kda_ckpt_plan) also gets the conv history a run
+ * resumed there needs -- the W-1 raw inputs of history ++ tokens before the
+ * checkpoint's position -- in conv_pool[conv_ckpt_slot[j]] (not when -1 or
+ * out of range): with the recurrent checkpoint it makes the snapshot a
+ * prefix hit resumes from.  Checkpoint conv slots must differ from every
+ * conv source and destination slot of the call.
  *
  * Two launches on `stream`: the conv with the normalisation (one streaming
  * pass over x that writes qkv), then the chunked prefill reading qkv.  The
@@ -331,7 +338,8 @@ int kda_prefill_varlen(const kda_prefill_args *args, kda_stream_t stream);
  * as kda_prefill_varlen (g, beta, o, slots, checkpoints, workspace from
  * kda_prefill_workspace_bytes of the same args, segment_len).
  * Errors: those of kda_prefill_varlen, raised before anything is launched;
- * q / k / v given or d_k != d_v -> KDA_ERR_ARG; W outside 2..4 ->
+ * q / k / v given or d_k != d_v -> KDA_ERR_ARG; conv_ckpt_slot without
+ * checkpoints (ckpt_interval 0) -> KDA_ERR_ARG; W outside 2..4 ->
  * KDA_ERR_UNSUPPORTED; qkv smaller than T_tot * 3 H d elements ->
  * KDA_ERR_WORKSPACE; x, qkv, conv_weight or conv_pool not 16-byte aligned,
  * or an x stride that breaks 16-byte rows -> KDA_ERR_ALIGN; act not 0/1,
@@ -346,6 +354,7 @@ typedef struct kda_prefill_conv_args {
     void *conv_pool;             /* [n_conv_slots, 3 H d, W-1] in_dtype */
     const int32_t *conv_src_slot;/* [n_seq]; -1 = zero history */
     const int32_t *conv_dst_slot;/* [n_seq]; -1 = not written */
+    const int32_t *conv_ckpt_slot; /* [n_ckpt] conv slot of each checkpoint, or NULL */
     void *qkv;                   /* [T_tot, 3 H d] in_dtype, packed */
     int64_t x_stride;            /* elements between tokens of x (0 = 3 H d) */
     int64_t n_conv_slots;

@@ -360,4 +360,5 @@ def test_prefill_conv_validation(lib):
     assert _call(lib, f, args(x_stride=100)) == 2                # < 3 H d
     assert _call(lib, f, args(x_stride=388)) == 4                # rows not 16-byte aligned
     assert _call(lib, f, args(p_n_seq=0)) == 0                   # no-op
+    assert _call(lib, f, args(conv_ckpt_slot=fake)) == 8         # conv checkpoints without checkpoints
 

@@ -44,9 +44,10 @@ def _case(lengths, H, d, W, dtype, seed):
 
 
 def _run(dev, wl, x, w, st, bias, init, has, conv_has, *, act, norm, chunk=64, out_dtype=torch.bfloat16,
-         ckpt_interval=0, segment_len=0, in_place=False):
+         ckpt_interval=0, segment_len=0, in_place=False, start_pos=None, conv_ckpt=False):
     """State slots: sources [0, N), destinations [N, 2N) (or the sources
-    when in_place), checkpoints from 2N; conv slots likewise."""
+    when in_place), checkpoints from 2N; conv slots likewise (conv
+    checkpoints from 2N when conv_ckpt)."""
     N = wl.n_seq
     H, d = wl.H, wl.dk
     C = x.shape[1]
@@ -54,17 +55,22 @@ def _run(dev, wl, x, w, st, bias, init, has, conv_has, *, act, norm, chunk=64, o
     i32 = lambda v: torch.tensor(v, dtype=torch.int32, device=dev)
     n_ck = 0
     kw = {}
+    if start_pos is not None:
+        kw["start_pos"] = i32(list(start_pos))
     if ckpt_interval:
-        ck_cu, _ = K.kda_ckpt_plan(wl.cu_seqlens.numpy(), ckpt_interval, chunk)
+        ck_cu, _ = K.kda_ckpt_plan(wl.cu_seqlens.numpy(), ckpt_interval, chunk,
+                                   start_pos=None if start_pos is None else np.asarray(start_pos, np.int32))
         n_ck = int(ck_cu[-1])
-        kw = dict(ckpt_interval=ckpt_interval, ckpt_cu=i32(list(ck_cu)),
+        kw.update(ckpt_interval=ckpt_interval, ckpt_cu=i32(list(ck_cu)),
                   ckpt_slot=i32(list(range(2 * N, 2 * N + n_ck))),
                   ckpt_pos_out=torch.full((max(n_ck, 1),), -1, dtype=torch.int32, device=dev))
+        if conv_ckpt:
+            kw["conv_ckpt_slot"] = i32(list(range(2 * N, 2 * N + n_ck)))
     pool = torch.full((2 * N + max(n_ck, 1), H, d, d), float("nan"), device=dev)
     pool[:N] = torch.tensor(init, dtype=torch.float32, device=dev)
     src = i32([s if has[s] else -1 for s in range(N)])
     dst = i32(list(range(N))) if in_place else i32(list(range(N, 2 * N)))
-    cpool = torch.full((2 * N, C, W - 1), float("nan"), dtype=x.dtype, device=dev)
+    cpool = torch.full((2 * N + max(n_ck, 1), C, W - 1), float("nan"), dtype=x.dtype, device=dev)
     cpool[:N] = st.to(dev)
     csrc = i32([s if conv_has[s] else -1 for s in range(N)])
     cdst = i32(list(range(N))) if in_place else i32(list(range(N, 2 * N)))
@@ -75,18 +81,19 @@ def _run(dev, wl, x, w, st, bias, init, has, conv_has, *, act, norm, chunk=64, o
                                        qk_l2norm=norm, chunk=chunk, segment_len=segment_len, **kw)
     torch.cuda.synchronize()
     out = {"o": o, "final": pool[dst.long()], "conv": cpool[cdst.long()], "qkv": qkv,
-           "ckpt": pool[2 * N:2 * N + n_ck]}
+           "ckpt": pool[2 * N:2 * N + n_ck], "conv_ckpt": cpool[2 * N:2 * N + n_ck]}
     if ckpt_interval:
         out["ckpt_pos"] = kw["ckpt_pos_out"][:n_ck].cpu().numpy()
     return out
 
 
 def _reference(orc, wl, x, w, st, bias, init, has, conv_has, *, act, norm, ckpt_interval=0,
-               operand_dtype="bf16"):
+               operand_dtype="bf16", start_pos=None):
     return orc.kda_prefill_conv(x, w, wl.g, wl.beta, wl.cu_seqlens, H=wl.H, d=wl.dk,
                                 bias=None if bias is None else bias, act=act, conv_state=st,
                                 has_conv_state=conv_has, qk_l2norm=norm, operand_dtype=operand_dtype,
-                                init=init, has_init=has, ckpt_interval=ckpt_interval)
+                                init=init, has_init=has, ckpt_interval=ckpt_interval,
+                                start_pos=None if start_pos is None else np.asarray(start_pos, np.int32))
 
 
 def _check_qkv(got, ref, dtype):
@@ -126,7 +133,7 @@ def test_prefill_conv_ragged_bf16(dev, oracle64):
     lengths = [37, 1, 2, 300, 77, 129]
     wl, x, w, st, bias, init, has = _case(lengths, 2, 128, 4, torch.bfloat16, seed=91)
     conv_has = np.array([1, 1, 0, 1, 0, 1], np.int32)
-    got = _run(dev, wl, x, w, st, bias, init, has, conv_has, act=1, norm=1, ckpt_interval=64)
+    got = _run(dev, wl, x, w, st, bias, init, has, conv_has, act=1, norm=1, ckpt_interval=64, conv_ckpt=True)
     ref = _reference(oracle64, wl, x, w, st, bias, init, has, conv_has, act=1, norm=1, ckpt_interval=64)
     _check_qkv(got["qkv"], ref, torch.bfloat16)
     U.assert_close("o", U.to_np(got["o"]), ref["o"])
@@ -134,6 +141,29 @@ def test_prefill_conv_ragged_bf16(dev, oracle64):
                    np.concatenate([ref["final"], ref["ckpt"]]))
     assert list(got["ckpt_pos"]) == list(ref["ckpt_pos"])
     _check_conv_state(got["conv"], ref["conv_state"])
+    _check_conv_state(got["conv_ckpt"], ref["conv_ckpt"])
+
+
+def test_prefill_conv_start_positions_and_checkpoints(dev, oracle64):
+    """Sequences that start mid-stream (absolute start 64, 0, 128: a resumed
+    prefix), checkpoints every 32 tokens at absolute positions, and the conv
+    history at every checkpoint (checkpoints sit at least one chunk after a
+    start, so their W-1 inputs are all tokens of the call)."""
+    U.say("prefill_conv start positions, conv checkpoints")
+    lengths = [300, 33, 130]
+    start = [64, 0, 128]
+    wl, x, w, st, bias, init, has = _case(lengths, 2, 64, 4, torch.bfloat16, seed=97)
+    conv_has = np.array([1, 0, 1], np.int32)
+    got = _run(dev, wl, x, w, st, bias, init, has, conv_has, act=1, norm=1, chunk=32, ckpt_interval=32,
+               start_pos=start, conv_ckpt=True)
+    ref = _reference(oracle64, wl, x, w, st, bias, init, has, conv_has, act=1, norm=1, ckpt_interval=32,
+                     start_pos=start)
+    assert list(got["ckpt_pos"]) == list(ref["ckpt_pos"])
+    U.assert_close("o", U.to_np(got["o"]), ref["o"])
+    U.assert_close("states", np.concatenate([U.to_np(got["final"]), U.to_np(got["ckpt"])]),
+                   np.concatenate([ref["final"], ref["ckpt"]]))
+    _check_conv_state(got["conv"], ref["conv_state"])
+    _check_conv_state(got["conv_ckpt"], ref["conv_ckpt"])
 
 
 @pytest.mark.parametrize("d,W,act,norm", [(16, 2, 0, 1), (32, 3, 1, 1), (64, 4, 1, 0)])
