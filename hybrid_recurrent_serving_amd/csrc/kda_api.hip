@@ -508,6 +508,17 @@ static int prefill_validate(const kda_prefill_args* a, kda_prefill_args& b) {
   if (a->n_seq < 0 || a->T_tot < 0 || a->n_slots < 0 || a->n_ckpt < 0 || a->workspace_bytes < 0)
     return fail(KDA_ERR_SHAPE, "negative size");
   b = *a;
+  if (b.T_tot == 0) {
+    // no tokens: the per-token tensors are never touched (an empty tensor
+    // may come as NULL), only the states are copied and written
+    void* f = b.state_pool;
+    if (!b.q) b.q = f;
+    if (!b.k) b.k = f;
+    if (!b.v) b.v = f;
+    if (!b.g) b.g = f;
+    if (!b.beta) b.beta = f;
+    if (!b.o) b.o = f;
+  }
   if (b.chunk != 16 && b.chunk != 32 && b.chunk != 64) return fail(KDA_ERR_UNSUPPORTED, "chunk %d (16, 32, 64)", b.chunk);
   if (b.ckpt_interval < 0) return fail(KDA_ERR_SHAPE, "ckpt_interval < 0");
   if (b.ckpt_interval > 0 && b.ckpt_interval % b.chunk != 0)
@@ -600,22 +611,27 @@ int kda_prefill_varlen_conv(const kda_prefill_conv_args* a, kda_stream_t stream_
   if (a->qk_l2norm != 0 && a->qk_l2norm != 1) return fail(KDA_ERR_ARG, "prefill_conv: qk_l2norm = %d", a->qk_l2norm);
   if (!(a->norm_eps >= 0.f)) return fail(KDA_ERR_ARG, "prefill_conv: norm_eps < 0");
   if (a->n_conv_slots < 0 || a->qkv_bytes < 0) return fail(KDA_ERR_SHAPE, "negative size");
-  if (!a->qkv) return fail(KDA_ERR_NULL, "prefill_conv: qkv is NULL");
+  if (!a->qkv && pa.T_tot > 0) return fail(KDA_ERR_NULL, "prefill_conv: qkv is NULL");
   const int64_t HD = static_cast<int64_t>(pa.H) * pa.d_k;
   const int64_t C = 3 * HD;
   if (C > 0x7fffffffLL) return fail(KDA_ERR_SHAPE, "prefill_conv: 3 H d too large");
   const int64_t eb = dtype_bytes(in_dt);
   char* qkv = static_cast<char*>(a->qkv);
-  pa.q = qkv;
-  pa.k = qkv + HD * eb;
-  pa.v = qkv + 2 * HD * eb;
+  if (qkv) {   // (NULL only without tokens)
+    pa.q = qkv;
+    pa.k = qkv + HD * eb;
+    pa.v = qkv + 2 * HD * eb;
+  }
   pa.q_stride = pa.k_stride = pa.v_stride = C;
   kda_prefill_args b;
   int st = prefill_validate(&pa, b);
   if (st) return st;
   if (b.n_seq == 0) return KDA_OK;
-  if (!a->x || !a->conv_weight || !a->conv_pool || !a->conv_src_slot || !a->conv_dst_slot)
+  if ((!a->x && b.T_tot > 0) || !a->conv_weight || !a->conv_pool || !a->conv_src_slot || !a->conv_dst_slot)
     return fail(KDA_ERR_NULL, "prefill_conv: required pointer is NULL");
+  // without tokens x and qkv are never touched (the conv only copies histories)
+  const void* xp = a->x ? a->x : a->conv_pool;
+  void* yp = a->qkv ? a->qkv : a->conv_pool;
   int64_t x_stride = a->x_stride == 0 ? C : a->x_stride;
   if (x_stride < C) return fail(KDA_ERR_SHAPE, "prefill_conv: x_stride < 3 H d");
   if (!aligned16(a->x) || !aligned16(a->qkv) || !aligned16(a->conv_weight) || !aligned16(a->conv_pool) ||
@@ -647,14 +663,14 @@ int kda_prefill_varlen_conv(const kda_prefill_conv_args* a, kda_stream_t stream_
     // before the conv launch: it reads the source histories, which that
     // launch may advance in place
     ConvCkptParams kp{};
-    kp.x = a->x; kp.pool = a->conv_pool; kp.cu = b.cu_seqlens; kp.start_pos = b.start_pos;
+    kp.x = xp; kp.pool = a->conv_pool; kp.cu = b.cu_seqlens; kp.start_pos = b.start_pos;
     kp.src_slot = a->conv_src_slot; kp.ckpt_cu = b.ckpt_cu; kp.ckpt_slot = a->conv_ckpt_slot;
     kp.x_stride = x_stride; kp.T_tot = b.T_tot; kp.n_slots = a->n_conv_slots; kp.n_ckpt = b.n_ckpt;
     kp.n_seq = b.n_seq; kp.C = static_cast<int32_t>(C); kp.W = a->W; kp.interval = b.ckpt_interval;
     if ((st = launch_conv_ckpt(kp, in_dt, stream))) return st;
   }
   ConvParams cp{};
-  cp.x = a->x; cp.y = a->qkv; cp.w = a->conv_weight; cp.bias = a->conv_bias; cp.cu = b.cu_seqlens;
+  cp.x = xp; cp.y = yp; cp.w = a->conv_weight; cp.bias = a->conv_bias; cp.cu = b.cu_seqlens;
   cp.pool = a->conv_pool; cp.src_slot = a->conv_src_slot; cp.dst_slot = a->conv_dst_slot; cp.adv = nullptr;
   cp.x_stride = x_stride; cp.y_stride = C; cp.T_tot = b.T_tot; cp.n_slots = a->n_conv_slots;
   cp.n_seq = b.n_seq; cp.C = static_cast<int32_t>(C); cp.W = a->W; cp.act = a->act;

@@ -254,6 +254,10 @@ int kda_ckpt_plan_device(const kda_plan_args *args, kda_stream_t stream);
  * sequences (the final state is written only after every segment has read
  * its starting state).
  *
+ * With T_tot == 0 the per-token pointers (q, k, v, g, beta, o) may be NULL:
+ * every sequence is empty, and only the final states (the source states)
+ * are written.
+ *
  * Decay range (precondition).  The chunked form scales the rows of a tile
  * (32 tokens at absolute multiples of 32; 16 when chunk == 16) by
  * exp(+-(G_r - G_15)), G being the running sum of g over the tile's rows.
@@ -337,6 +341,9 @@ int kda_prefill_varlen(const kda_prefill_args *args, kda_stream_t stream);
  * (the library points them into qkv), d_k == d_v == d; every other field
  * as kda_prefill_varlen (g, beta, o, slots, checkpoints, workspace from
  * kda_prefill_workspace_bytes of the same args, segment_len).
+ * With T_tot == 0, x and qkv may be NULL (and the per-token pointers of
+ * `prefill`, as in kda_prefill_varlen): nothing is read from them; the conv
+ * histories and the final states are still copied to their destinations.
  * Errors: those of kda_prefill_varlen, raised before anything is launched;
  * q / k / v given or d_k != d_v -> KDA_ERR_ARG; conv_ckpt_slot without
  * checkpoints (ckpt_interval 0) -> KDA_ERR_ARG; W outside 2..4 ->

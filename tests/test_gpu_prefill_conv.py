@@ -237,3 +237,42 @@ def test_prefill_conv_varlen_full_size(dev, oracle64):
     U.assert_close("final (3 sequences)", U.to_np(got["final"][pick]), ref["final"])
     qkv = got["qkv"][torch.as_tensor(rows, device=got["qkv"].device)]
     _check_qkv(qkv, ref, torch.bfloat16)
+
+
+def test_prefill_conv_empty_sequences(dev, oracle64):
+    """Empty sequences among non-empty ones (their conv history passes
+    through unchanged, their state is the source state), and a batch whose
+    sequences are all empty (T_tot = 0: nothing but the history copies and
+    the final states)."""
+    U.say("prefill_conv empty sequences")
+    lengths = [0, 5, 0, 40]
+    wl, x, w, st, bias, init, has = _case(lengths, 2, 32, 3, torch.bfloat16, seed=99)
+    conv_has = np.array([1, 1, 0, 1], np.int32)
+    got = _run(dev, wl, x, w, st, bias, init, has, conv_has, act=1, norm=1, chunk=16)
+    ref = _reference(oracle64, wl, x, w, st, bias, init, has, conv_has, act=1, norm=1)
+    U.assert_close("o", U.to_np(got["o"]), ref["o"])
+    U.assert_close("final", U.to_np(got["final"]), ref["final"])
+    _check_conv_state(got["conv"], ref["conv_state"])
+    # all empty
+    N, H, d, W = 3, 2, 32, 3
+    C = 3 * H * d
+    i32 = lambda v: torch.tensor(v, dtype=torch.int32, device=dev)
+    gen = torch.Generator().manual_seed(990)
+    stc = torch.randn(N, C, W - 1, generator=gen).to(torch.bfloat16)
+    cw = (torch.rand(C, W, generator=gen) - 0.5).to(torch.bfloat16)
+    s0 = torch.randn(N, H, d, d, generator=gen) * 0.1
+    cpool = torch.cat([stc, torch.full_like(stc, float("nan"))]).to(dev)
+    pool = torch.cat([s0, torch.full_like(s0, float("nan"))]).to(dev)
+    e = torch.empty(0, C, dtype=torch.bfloat16, device=dev)
+    g0 = torch.empty(0, H, d, dtype=torch.bfloat16, device=dev)
+    b0 = torch.empty(0, H, dtype=torch.bfloat16, device=dev)
+    o0 = torch.empty(0, H, d, dtype=torch.bfloat16, device=dev)
+    K.kda_prefill_varlen_conv(e, cw.to(dev), cpool, i32([0, -1, 2]), i32([3, 4, 5]), g0, b0, o0, i32([0, 0, 0, 0]),
+                              pool, i32([0, 1, -1]), i32([3, 4, 5]), act=1, qk_l2norm=True, chunk=16)
+    torch.cuda.synchronize()
+    got_c = cpool[3:].cpu()
+    assert torch.equal(got_c[0], stc[0]) and torch.equal(got_c[2], stc[2])
+    assert torch.equal(got_c[1], torch.zeros_like(stc[1]))          # no history: zeros
+    got_s = pool[3:].cpu()
+    assert torch.equal(got_s[0], s0[0]) and torch.equal(got_s[1], s0[1])
+    assert torch.equal(got_s[2], torch.zeros_like(s0[2]))           # no source: zero state
