@@ -49,6 +49,42 @@ def test_decode_tiny_stepped_64(dev, oracle64):
     U.assert_close("state", U.to_np(pool[0]), ref["final"][0], rel=1e-5, mx=1e-5)
 
 
+def test_verify_tiny_windows_of_8(dev, oracle64):
+    """Tiny workload (T=64, H=2, d=16, fp32) verified as 8 consecutive
+    8-token windows, each starting from the state the window before
+    committed (all 8 accepted): every output and the final state equal the
+    oracle's token loop over the 64 tokens.  Then one window with L = 5 from
+    the state after 16 tokens commits the oracle's state after 21."""
+    U.say("verify tiny, 8-token windows")
+    wl = make_workload(0)
+    H, d = wl.H, wl.dk
+    ref = oracle64.kda_varlen(wl.q, wl.k, wl.v, wl.g, wl.beta, wl.cu_seqlens)
+    q, k, v, g, b = (t.to(dev) for t in (wl.q, wl.k, wl.v, wl.g, wl.beta))
+    pool = torch.zeros(2, H, d, d, device=dev)
+    i32 = lambda x: torch.tensor(x, dtype=torch.int32, device=dev)
+    o = torch.empty(8, 8, H, d, device=dev)
+    clen = torch.full((8,), -7, dtype=torch.int32, device=dev)
+    win = lambda t, j: t[8 * j:8 * j + 8].unsqueeze(0).contiguous()
+    for j in range(8):
+        K.kda_verify(win(q, j), win(k, j), win(v, j), win(g, j), win(b, j), pool, i32([j % 2]),
+                     i32([(j + 1) % 2]), o=o[j:j + 1], accepted_len=i32([8]), committed_len_out=clen[j:j + 1])
+    torch.cuda.synchronize()
+    assert clen.cpu().tolist() == [8] * 8
+    U.assert_close("o", U.to_np(o.reshape(64, H, d)), ref["o"], rel=1e-5, mx=1e-5)
+    U.assert_close("state", U.to_np(pool[0]), ref["final"][0], rel=1e-5, mx=1e-5)
+    # the state after 16 tokens, then a window of 8 with 5 accepted
+    cu16 = torch.tensor([0, 16], dtype=torch.int32)
+    s16 = oracle64.kda_varlen(wl.q[:16], wl.k[:16], wl.v[:16], wl.g[:16], wl.beta[:16], cu16)["final"]
+    cu21 = torch.tensor([0, 21], dtype=torch.int32)
+    s21 = oracle64.kda_varlen(wl.q[:21], wl.k[:21], wl.v[:21], wl.g[:21], wl.beta[:21], cu21)["final"]
+    pool2 = torch.zeros(2, H, d, d, device=dev)
+    pool2[0] = torch.tensor(s16[0], dtype=torch.float32, device=dev)
+    K.kda_verify(win(q, 2), win(k, 2), win(v, 2), win(g, 2), win(b, 2), pool2, i32([0]), i32([1]),
+                 accepted_len=i32([5]))
+    torch.cuda.synchronize()
+    U.assert_close("state after 21", U.to_np(pool2[1]), s21[0], rel=1e-5, mx=1e-5)
+
+
 def test_decode_batched_128(dev, oracle64):
     """Batched decode: 128 sequences x 1 token, H=16, d=128, bf16 inputs,
     random fp32 states updated in place."""
