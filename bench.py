@@ -76,7 +76,7 @@ def kernel_source_hash(name: str) -> str:
     """The kernel's source file together with the device headers it includes."""
     csrc = ROOT / "hybrid_recurrent_serving_amd" / "csrc"
     h = hashlib.sha256()
-    for f in (name, "kda_device.h", "kda_internal.h"):
+    for f in (name, "kda_device.h", "kda_internal.h", "kda_mfma.h"):
         h.update((csrc / f).read_bytes())
     return h.hexdigest()[:16]
 

@@ -134,4 +134,32 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+// State slices through a buffer resource: one whose size is 0 makes every
+// load return 0, so a slice with no source needs no branch and its loads are
+// issued on every path (which keeps the compiler's load-counter waits exact).
+constexpr int kBufWord3 = 0x00020000;   // raw 32-bit buffer (gfx9 descriptor word 3)
+constexpr int kBufNonTemporal = 2;
+
+// A buffer resource from values that are the same on every lane, held in
+// scalar registers (the compiler cannot always prove that by itself).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* base, int bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
+  void* ua = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(ua, 0, __builtin_amdgcn_readfirstlane(bytes), kBufWord3);
+}
+
+// 16 bytes of a state slice through a buffer resource (non-temporal; dropped
+// when the resource has size 0).  The whole offset goes in the vector
+// offset and the scalar offset is the constant 0: with a scalar register
+// there, the compiler inserts no wait before a vector write to the store's
+// data registers, and measured stores then took some lanes' first dword
+// from the next value written to that register.
+__device__ __forceinline__ void st4_rsrc(__amdgpu_buffer_rsrc_t r, int voff, int off, const float (&x)[4]) {
+  typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+  const u32x4 v = {__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3])};
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, voff + off, 0, kBufNonTemporal);
+}
+
 }  // namespace kda

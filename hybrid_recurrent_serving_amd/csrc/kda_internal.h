@@ -29,6 +29,8 @@ struct StepParams {
 };
 
 int launch_step(const StepParams& p, int D, int in_dtype, int out_dtype, hipStream_t stream);
+// verify at d = 128 with bf16 inputs and 2..16 tokens on matrix cores
+int launch_verify_mfma(const StepParams& p, int out_dtype, hipStream_t stream);
 
 // decode step with the short convolution fused in
 struct DecodeConvParams {
