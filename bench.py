@@ -202,8 +202,8 @@ def ingest_pmc(fetch_csv, write_csv):
              128 * 16),
             ("decode_conv_kernel_d128_bf16", lambda r: is_decode128(r["Kernel_Name"], 4),
              "kda_step.hip", 128 * 16),
-            ("verify_step_kernel_d128_bf16", named("step_kernel<128,unsignedshort,unsignedshort,true>"),
-             "kda_step.hip", 128 * 16),
+            ("verify_kernel_d128_bf16", named("vf::verify_kernel<unsignedshort>"),
+             "kda_verify.hip", 128 * 16),
             ("verify_conv_kernel_d128_bf16", named("verify_conv_kernel<128,unsignedshort,unsignedshort,4,8>"),
              "kda_step.hip", 128 * 16),
             ("conv_kernel_prefill_bf16", named("conv_kernel<unsignedshort,4,0>"), "kda_conv.hip", varlen_tokens()),
@@ -277,10 +277,14 @@ def ingest_mfma(paths):
                 "note": f"torch.mm of two {GEMM_N} x {GEMM_N} bf16 matrices (library GEMM)"}
         # the decode and verify kernels: MfmaUtil / VALUBusy averaged over
         # their dispatches, weighted by active cycles
-        for key, pred in (("decode_conv_kernel_d128_bf16", lambda n: is_decode128(n, 4)),
-                          ("decode_step_kernel_d128_bf16", lambda n: is_decode128(n, 0)),
-                          ("verify_kernel_d128_bf16", lambda n: n.startswith("void kda::step_kernel<128, unsigned short, unsigned short, true>")),
-                          ("verify_conv_kernel_d128_bf16", lambda n: n.startswith("void kda::verify_conv_kernel<128, unsigned short, unsigned short, 4, 8>"))):
+        for key, pred, src in (
+                ("decode_conv_kernel_d128_bf16", lambda n: is_decode128(n, 4), "kda_step.hip"),
+                ("decode_step_kernel_d128_bf16", lambda n: is_decode128(n, 0), "kda_step.hip"),
+                ("verify_kernel_d128_bf16", lambda n: n.startswith("void kda::vf::verify_kernel<unsigned short>"),
+                 "kda_verify.hip"),
+                ("verify_conv_kernel_d128_bf16",
+                 lambda n: n.startswith("void kda::verify_conv_kernel<128, unsigned short, unsigned short, 4, 8>"),
+                 "kda_step.hip")):
             ds = [d for d in order if pred(d["name"])]
             if not ds or key in out:
                 continue
@@ -288,7 +292,7 @@ def ingest_mfma(paths):
             out[key] = {"dispatches": len(ds),
                         "mfma_util": round(sum(d["MfmaUtil"] * d["GRBM_GUI_ACTIVE"] for d in ds) / w / 100, 4),
                         "valu_busy": round(sum(d["VALUBusy"] * d["GRBM_GUI_ACTIVE"] for d in ds) / w / 100, 4),
-                        "source_sha256_16": kernel_source_hash("kda_step.hip")}
+                        "source_sha256_16": kernel_source_hash(src)}
         # calls: each prefill call starts with its segment plan launch
         calls, cur = [], None
         for d in order:
@@ -621,10 +625,10 @@ def bench_verify_secondary(torch, K, make_workload, dev, n=200, warm=10, cpu_sec
            "state_GB_s": round(state_bytes / us / 1e3, 1),
            "alg_GB_s": round(alg / us / 1e3, 1),
            "hbm_frac": round(alg / us / 1e3 / HBM_PEAK_GBS, 4),
-           "roofline": {"kernel": "step_kernel<128,bf16,bf16,staged> (kda_verify, one launch per call)",
+           "roofline": {"kernel": "verify_kernel<bf16> (kda_verify on bf16 matrix cores, one launch per call)",
                         "bound": "hbm", "achieved": round(alg / us / 1e3, 1), "peak": HBM_PEAK_GBS,
                         "unit": "GB/s", "frac": round(alg / us / 1e3 / HBM_PEAK_GBS, 4),
-                        "traffic": traffic_for("verify_step_kernel_d128_bf16", "kda_step.hip", N * H),
+                        "traffic": traffic_for("verify_kernel_d128_bf16", "kda_verify.hip", N * H),
                         "alg_bytes_per_launch": alg, "avg_launch_us": round(us, 3)}}
     if cpu_seconds > 0:
         res["cpu_baseline"] = cpu_verify(wl, state_bytes, cpu_seconds)

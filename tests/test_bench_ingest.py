@@ -11,7 +11,7 @@ import bench
 PLAN = "kda::pf::segment_plan_kernel(kda::PrefillParams, int*, int*)"
 PF = "void kda::pf::prefill_kernel<128, unsigned short, unsigned short>(kda::PrefillParams, int, int)"
 COMB = "kda::pf::segment_combine_kernel(kda::PrefillParams, int)"
-VER = "void kda::step_kernel<128, unsigned short, unsigned short, true>(kda::StepParams)"
+VER = "void kda::vf::verify_kernel<unsigned short>(kda::StepParams)"
 COPY = "__amd_rocclr_copyBuffer"
 
 
@@ -88,7 +88,7 @@ def test_ingest_pmc_calibrates_and_splits_calls(tmp_path, tokens):
 def test_ingest_pmc_single_kernels(tmp_path, tokens):
     """The verify, fused verify and prefill-scale conv kernels: their
     dispatches averaged, each counter scaled by the calibration copy."""
-    names = {"verify_step_kernel_d128_bf16": "void kda::step_kernel<128, unsigned short, unsigned short, true>(kda::StepParams)",
+    names = {"verify_kernel_d128_bf16": "void kda::vf::verify_kernel<unsigned short>(kda::StepParams)",
              "verify_conv_kernel_d128_bf16": "void kda::verify_conv_kernel<128, unsigned short, unsigned short, 4, 8>(kda::DecodeConvParams)",
              "conv_kernel_prefill_bf16": "void kda::conv_kernel<unsigned short, 4, 0>(kda::ConvParams)",
              "conv_norm_kernel_prefill_bf16": "void kda::conv_kernel<unsigned short, 4, 16>(kda::ConvParams)"}
@@ -110,5 +110,5 @@ def test_ingest_pmc_single_kernels(tmp_path, tokens):
         assert e["dispatches"] == 2
         assert e["fetch_bytes"] == round((8.0 + i) * 1024 * 2)
         assert e["write_bytes"] == round((8.0 + i) * 1024)
-    assert out["verify_step_kernel_d128_bf16"]["units_per_launch"] == 128 * 16
+    assert out["verify_kernel_d128_bf16"]["units_per_launch"] == 128 * 16
     assert out["conv_norm_kernel_prefill_bf16"]["units_per_launch"] == tokens
