@@ -162,4 +162,20 @@ __device__ __forceinline__ void st4_rsrc(__amdgpu_buffer_rsrc_t r, int voff, int
   __builtin_amdgcn_raw_buffer_store_b128(v, r, voff + off, 0, kBufNonTemporal);
 }
 
+// Gated RMS norm of one output vector of D channels held 4 per lane by
+// D / 4 consecutive lanes (sum of squares across them by butterfly
+// shuffles): o <- o / sqrt(mean o^2 + eps) * weight * sigmoid(gate).
+template <int D, typename Tin>
+__device__ __forceinline__ void gate_norm4(float (&o)[4], const Tin* gate, const Tin* weight, float eps) {
+  float ss = o[0] * o[0] + o[1] * o[1] + o[2] * o[2] + o[3] * o[3];
+#pragma unroll
+  for (int m = 1; m < D / 4; m <<= 1) ss += __shfl_xor(ss, m, 64);
+  const float inv = 1.f / sqrtf(ss * (1.f / D) + eps);
+  float z[4], w[4];
+  io<Tin>::ld4(gate, z);
+  io<Tin>::ld4(weight, w);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) o[c] = o[c] * inv * w[c] * sigmoid_fast(z[c]);
+}
+
 }  // namespace kda

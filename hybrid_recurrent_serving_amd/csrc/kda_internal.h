@@ -57,6 +57,8 @@ struct DecodeConvParams {
 
 int launch_decode_conv(const DecodeConvParams& p, int D, int in_dtype, int out_dtype, hipStream_t stream);
 int launch_verify_conv(const DecodeConvParams& p, int D, int in_dtype, int out_dtype, hipStream_t stream);
+// verify_conv at d = 128 with bf16 inputs and 2..16 tokens on matrix cores
+int launch_verify_conv_mfma(const DecodeConvParams& p, int out_dtype, hipStream_t stream);
 
 // ---------------------------------------------------------------- plan
 // device-side checkpoint plan (kda_ckpt_plan_device)

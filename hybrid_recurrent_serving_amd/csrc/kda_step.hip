@@ -337,22 +337,6 @@ template <> struct Vec16x<float> {
 };
 
 
-// Gated RMS norm of one output vector of D channels held 4 per lane by
-// D / 4 consecutive lanes (sum of squares across them by butterfly
-// shuffles): o <- o / sqrt(mean o^2 + eps) * weight * sigmoid(gate).
-template <int D, typename Tin>
-__device__ __forceinline__ void gate_norm4(float (&o)[4], const Tin* gate, const Tin* weight, float eps) {
-  float ss = o[0] * o[0] + o[1] * o[1] + o[2] * o[2] + o[3] * o[3];
-#pragma unroll
-  for (int m = 1; m < D / 4; m <<= 1) ss += __shfl_xor(ss, m, 64);
-  const float inv = 1.f / sqrtf(ss * (1.f / D) + eps);
-  float z[4], w[4];
-  io<Tin>::ld4(gate, z);
-  io<Tin>::ld4(weight, w);
-#pragma unroll
-  for (int c = 0; c < 4; ++c) o[c] = o[c] * inv * w[c] * sigmoid_fast(z[c]);
-}
-
 template <int D, typename Tin, typename Tout, int W>
 __global__ void __launch_bounds__(64 * StepLayout<D>::WPH)
 decode_conv_kernel(const DecodeConvParams p) {
@@ -1212,6 +1196,9 @@ verify_conv_kernel(const DecodeConvParams p) {
 
 template <int D, typename Tin, typename Tout>
 static int launch_verify_conv_t(const DecodeConvParams& p, hipStream_t stream) {
+  if constexpr (D == 128 && std::is_same<Tin, bf16_t>::value) {
+    if (p.T_spec >= 2) return launch_verify_conv_mfma(p, std::is_same<Tout, float>::value ? KDA_F32 : KDA_BF16, stream);
+  }
   using L = StepLayout<D>;
   dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(p.n_seq) * p.H));
   dim3 block(64 * L::WPH);
