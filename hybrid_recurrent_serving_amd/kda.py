@@ -691,15 +691,9 @@ def prepare_decode_conv(x, conv_weight, conv_pool, conv_src_slot, conv_dst_slot,
                      src_slot, dst_slot, conv_bias, out_gate, out_norm_weight))
 
 
-def kda_verify_conv(x, conv_weight, conv_pool, conv_src_slot, conv_dst_slot, g, beta, state_pool, src_slot,
-                    dst_slot, *, o=None, accepted_len=None, committed_len_out=None, conv_bias=None,
-                    act: int = 0, qk_l2norm: bool = True, norm_eps: float = 1e-6, scale=1.0, out_gate=None,
-                    out_norm_weight=None, out_norm_eps: float = 1e-6, stream=None):
-    """Speculative verify with the short convolution fused in.  x [N, T_spec,
-    3 H d] (q | k | v projections of the tokens); g [N, T_spec, H, d]; beta
-    [N, T_spec, H]; o [N, T_spec, H, d] or None; conv and state pools as
-    kda_decode_conv; out_gate [N, T_spec, H, d] and out_norm_weight [d]
-    (optional gated RMS norm of every output)."""
+def _verify_conv_args(x, conv_weight, conv_pool, conv_src_slot, conv_dst_slot, g, beta, state_pool, src_slot,
+                      dst_slot, o, accepted_len, committed_len_out, conv_bias, act, qk_l2norm, norm_eps, scale,
+                      out_gate, out_norm_weight, out_norm_eps):
     import torch
     _expect(x.dim() == 3 and g.dim() == 4 and beta.dim() == 3,
             "x [N, T_spec, 3 H d], g [N, T_spec, H, d], beta [N, T_spec, H]")
@@ -749,13 +743,39 @@ def kda_verify_conv(x, conv_weight, conv_pool, conv_src_slot, conv_dst_slot, g, 
     if out_gate is not None:
         _expect(out_gate.stride(0) == Ts * out_gate.stride(1), "out_gate: sequence stride must be T_spec tokens")
     _out_gate_fields(a, out_gate, out_norm_weight, out_norm_eps, (N, Ts), H, d, x)
+    return a
+
+
+def kda_verify_conv(x, conv_weight, conv_pool, conv_src_slot, conv_dst_slot, g, beta, state_pool, src_slot,
+                    dst_slot, *, o=None, accepted_len=None, committed_len_out=None, conv_bias=None,
+                    act: int = 0, qk_l2norm: bool = True, norm_eps: float = 1e-6, scale=1.0, out_gate=None,
+                    out_norm_weight=None, out_norm_eps: float = 1e-6, stream=None):
+    """Speculative verify with the short convolution fused in.  x [N, T_spec,
+    3 H d] (q | k | v projections of the tokens); g [N, T_spec, H, d]; beta
+    [N, T_spec, H]; o [N, T_spec, H, d] or None; conv and state pools as
+    kda_decode_conv; out_gate [N, T_spec, H, d] and out_norm_weight [d]
+    (optional gated RMS norm of every output)."""
+    a = _verify_conv_args(x, conv_weight, conv_pool, conv_src_slot, conv_dst_slot, g, beta, state_pool, src_slot,
+                          dst_slot, o, accepted_len, committed_len_out, conv_bias, act, qk_l2norm, norm_eps, scale,
+                          out_gate, out_norm_weight, out_norm_eps)
     _check(load_library().kda_verify_conv(ctypes.byref(a), _stream(stream)))
     return o
 
 
-def kda_verify(q, k, v, g, beta, state_pool, src_slot, dst_slot, *, o=None, accepted_len=None,
-               committed_len_out=None, scale=1.0, stream=None):
-    """Speculative verify.  q, k, v, g [N, T_spec, H, d]; beta [N, T_spec, H]."""
+def prepare_verify_conv(x, conv_weight, conv_pool, conv_src_slot, conv_dst_slot, g, beta, state_pool, src_slot,
+                        dst_slot, *, o=None, accepted_len=None, committed_len_out=None, conv_bias=None,
+                        act: int = 0, qk_l2norm: bool = True, norm_eps: float = 1e-6, scale=1.0, out_gate=None,
+                        out_norm_weight=None, out_norm_eps: float = 1e-6) -> Prepared:
+    """kda_verify_conv with fixed buffers, as a Prepared call."""
+    a = _verify_conv_args(x, conv_weight, conv_pool, conv_src_slot, conv_dst_slot, g, beta, state_pool, src_slot,
+                          dst_slot, o, accepted_len, committed_len_out, conv_bias, act, qk_l2norm, norm_eps, scale,
+                          out_gate, out_norm_weight, out_norm_eps)
+    return Prepared(load_library().kda_verify_conv, a,
+                    (x, conv_weight, conv_pool, conv_src_slot, conv_dst_slot, g, beta, state_pool, src_slot,
+                     dst_slot, o, accepted_len, committed_len_out, conv_bias, out_gate, out_norm_weight))
+
+
+def _verify_args(q, k, v, g, beta, state_pool, src_slot, dst_slot, o, accepted_len, committed_len_out, scale):
     import torch
     _expect(q.dim() == 4 and v.dim() == 4 and beta.dim() == 3,
             "q/k/v/g [N, T_spec, H, d], beta [N, T_spec, H]")
@@ -790,5 +810,20 @@ def kda_verify(q, k, v, g, beta, state_pool, src_slot, dst_slot, *, o=None, acce
     a.in_dtype = _dtype_code(q)
     a.out_dtype = _dtype_code(o) if o is not None else KDA_F32
     a.scale = scale
+    return a
+
+
+def kda_verify(q, k, v, g, beta, state_pool, src_slot, dst_slot, *, o=None, accepted_len=None,
+               committed_len_out=None, scale=1.0, stream=None):
+    """Speculative verify.  q, k, v, g [N, T_spec, H, d]; beta [N, T_spec, H]."""
+    a = _verify_args(q, k, v, g, beta, state_pool, src_slot, dst_slot, o, accepted_len, committed_len_out, scale)
     _check(load_library().kda_verify(ctypes.byref(a), _stream(stream)))
     return o
+
+
+def prepare_verify(q, k, v, g, beta, state_pool, src_slot, dst_slot, *, o=None, accepted_len=None,
+                   committed_len_out=None, scale=1.0) -> Prepared:
+    """kda_verify with fixed buffers, as a Prepared call."""
+    a = _verify_args(q, k, v, g, beta, state_pool, src_slot, dst_slot, o, accepted_len, committed_len_out, scale)
+    return Prepared(load_library().kda_verify, a,
+                    (q, k, v, g, beta, state_pool, src_slot, dst_slot, o, accepted_len, committed_len_out))

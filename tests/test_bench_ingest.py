@@ -89,7 +89,7 @@ def test_ingest_pmc_single_kernels(tmp_path, tokens):
     """The verify, fused verify and prefill-scale conv kernels: their
     dispatches averaged, each counter scaled by the calibration copy."""
     names = {"verify_kernel_d128_bf16": "void kda::vf::verify_kernel<unsigned short>(kda::StepParams)",
-             "verify_conv_kernel_d128_bf16": "void kda::verify_conv_kernel<128, unsigned short, unsigned short, 4, 8>(kda::DecodeConvParams)",
+             "verify_conv_kernel_d128_bf16": "void kda::vf::verify_conv_kernel<unsigned short, 4, 8>(kda::DecodeConvParams)",
              "conv_kernel_prefill_bf16": "void kda::conv_kernel<unsigned short, 4, 0>(kda::ConvParams)",
              "conv_norm_kernel_prefill_bf16": "void kda::conv_kernel<unsigned short, 4, 16>(kda::ConvParams)"}
 
