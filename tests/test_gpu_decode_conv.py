@@ -315,6 +315,37 @@ def test_verify_conv_16_tokens_bias_absent_sources(dev, oracle64):
     assert torch.equal(st_src.cpu(), init) and torch.equal(cs_src.cpu(), cst)
 
 
+@pytest.mark.parametrize("W,Ts", [(2, 5), (3, 12)])
+def test_verify_conv_matrix_core_widths_fp32_outputs(dev, oracle64, W, Ts):
+    """The matrix-core fused verify (d = 128, bf16 inputs) at conv widths 2
+    and 3, both window buckets (5 and 12 tokens), with a conv bias, without
+    SiLU and without the q/k norm, fp32 outputs: outputs and committed states
+    at fp32-grade tolerance, the conv history bit for bit."""
+    U.say(f"verify_conv bf16 d128 W={W} T={Ts} fp32 out")
+    N, H, d = 6, 2, 128
+    x, w, cst, g, b, init = _verify_case(N, Ts, H, d, W, torch.bfloat16, seed=80 + W)
+    bias = (torch.rand(3 * H * d, generator=torch.Generator().manual_seed(81 + W)) - 0.5).to(torch.bfloat16)
+    L = [Ts, 0, 1, Ts // 2, Ts + 1, 3]
+    conv_src = [0, -1, 2, 3, 4, 5]
+    o, st, cs, clen, _, _ = _run_verify(dev, x, w, cst, g, b, init, L, out_dtype=torch.float32,
+                                        conv_src=conv_src, act=0, norm=0, bias=bias)
+    ref, _ = _verify_reference(oracle64, x, w, cst, g, b, init, L, conv_src, act=0, norm=0, bias=bias)
+    ok = np.array([0 <= v <= Ts for v in L])
+    assert clen.cpu().tolist() == [v if 0 <= v <= Ts else -1 for v in L]
+    # without the q / k norm the outputs and states are far from unit scale
+    # (|k|^2 ~ 40, so beta k k^T amplifies what it multiplies): the pair
+    # products are good to ~1e-5 of their operands, so the relative bounds
+    # are 2e-5 and the max-abs bounds scale with the reference's largest
+    # magnitude
+    o_pk = float(np.abs(ref["o"]).max())
+    s_pk = float(np.abs(ref["committed"][ok]).max())
+    U.say(f"  largest |o| {o_pk:.3e}, largest |committed| {s_pk:.3e}")
+    U.assert_close("o", U.to_np(o), ref["o"], rel=2e-5, mx=5e-5 * max(1.0, o_pk))
+    U.assert_close("committed", U.to_np(st)[ok], ref["committed"][ok], rel=2e-5, mx=5e-5 * max(1.0, s_pk))
+    assert torch.isnan(st[4]).all() and torch.isnan(cs[4]).all()
+    assert np.array_equal(cs.to("cpu", torch.float32).numpy()[ok], ref["conv_state"][ok].astype(np.float32))
+
+
 def test_verify_conv_fp32_d128_16_tokens(dev, oracle64):
     """fp32 inputs and outputs at d = 128 with 16 tokens: the largest LDS
     footprint of the fused verify (staged units and token arrays)."""

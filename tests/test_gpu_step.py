@@ -380,6 +380,39 @@ def test_verify_d128_decay_spikes(dev, oracle64):
     U.assert_close("committed", U.to_np(pool[N:]), ref["committed"], rel=1e-5, mx=1e-4)
 
 
+@pytest.mark.parametrize("T_spec", [2, 9, 16])
+def test_verify_d128_matrix_core_fp32_outputs(dev, oracle64, T_spec):
+    """d = 128, bf16 inputs (the matrix-core verify, one chunk of T_spec rows
+    with reference row (T_spec - 1) / 2), fp32 outputs: outputs and committed
+    states against the oracle at fp32-grade tolerance for every accepted
+    length 0..T_spec and a rejected one, and a commit-only call that commits
+    the same states bit for bit."""
+    U.say(f"verify d128 bf16 in / fp32 out T_spec={T_spec}")
+    N, H, d = T_spec + 2, 2, 128
+    wl = make_workload(4, n_seq=N, H=H, d=d, T=T_spec, seed=70 + T_spec)
+    L = torch.arange(N, dtype=torch.int32) % (T_spec + 1)
+    L[N - 1] = -2   # rejected
+    ref = oracle64.kda_verify(wl.q, wl.k, wl.v, wl.g, wl.beta, wl.init_states, L)
+    q, k, v, g, b = (t.to(dev) for t in (wl.q, wl.k, wl.v, wl.g, wl.beta))
+    pool = torch.cat([wl.init_states, torch.full_like(wl.init_states, 3.0)]).to(dev)
+    src = torch.arange(N, dtype=torch.int32, device=dev)
+    dst = src + N
+    o = torch.empty(N, T_spec, H, d, device=dev)
+    clen = torch.full((N,), -7, dtype=torch.int32, device=dev)
+    K.kda_verify(q, k, v, g, b, pool, src, dst, o=o, accepted_len=L.to(dev), committed_len_out=clen)
+    torch.cuda.synchronize()
+    expect = L.clone()
+    expect[N - 1] = -1
+    assert torch.equal(clen.cpu(), expect)
+    U.assert_close("o", U.to_np(o), ref["o"], rel=2e-5, mx=1e-4)
+    U.assert_close("committed", U.to_np(pool[N:2 * N - 1]), ref["committed"][:N - 1], rel=1e-5, mx=1e-4)
+    assert torch.all(pool[2 * N - 1] == 3.0), "rejected sequence wrote its destination"
+    pool2 = torch.cat([wl.init_states, torch.full_like(wl.init_states, 3.0)]).to(dev)
+    K.kda_verify(q, k, v, g, b, pool2, src, dst, accepted_len=L.to(dev))   # commit only
+    torch.cuda.synchronize()
+    assert torch.equal(pool2, pool)
+
+
 def test_decode_d128_item_count_not_multiple_of_8(dev, oracle64):
     """d = 128 decode with 5 sequences x 3 heads = 15 (sequence, head) items:
     the blocks past the last whole group of 8 items take the plain block
