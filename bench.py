@@ -149,26 +149,41 @@ def pmc_pass(torch, K, make_workload, long=False):
     del pool
     bench_verify_secondary(torch, K, make_workload, dev, n=2, warm=2)   # 4 verify + 4 fused verify calls
     torch.cuda.empty_cache()
-    bench_prefill_varlen(torch, K, make_workload, dev, iters=PMC_PREFILL_CALLS - 2)   # + 2 warm-up calls
+    bench_prefill_varlen(torch, K, make_workload, dev, iters=1, warm=PMC_PREFILL_CALLS - 1)
     torch.cuda.synchronize()
     if long:
         torch.cuda.empty_cache()
-        bench_prefill_long(torch, K, make_workload, dev, iters=PMC_LONG_CALLS - 1)   # + 1 warm-up call
+        bench_prefill_long(torch, K, make_workload, dev, iters=1, warm=PMC_LONG_CALLS - 1)
         torch.cuda.synchronize()
     # the conv at prefill scale (3 + 1 launches) and the prefill from raw
     # projections (3 calls, 3 prefills alone, 3 conv + norm launches alone),
     # after every prefill call the ingest counts by position
     torch.cuda.empty_cache()
     wl2 = make_workload(2)
-    bench_conv_prefill(torch, K, wl2, dev, iters=1)
+    bench_conv_prefill(torch, K, wl2, dev, iters=1, warm=3)
     torch.cuda.empty_cache()
-    bench_prefill_conv(torch, K, wl2, dev, iters=1)
+    bench_prefill_conv(torch, K, wl2, dev, iters=1, warm=2)
     torch.cuda.synchronize()
 
 
 def varlen_tokens():
     from hybrid_recurrent_serving_amd.inputs import make_workload
     return int(make_workload(2).cu_seqlens[-1])
+
+
+def check_prefill_calls(first_grids):
+    """The counter pass's varlen prefill calls and its 1M-token calls launch
+    pass A on different grids: first_grids holds the grid of each call's
+    first prefill-kernel dispatch, in call order (None where the CSV has no
+    grid column).  Calls whose grids do not fall into the expected groups
+    mean the pass's call counts are out of step with PMC_PREFILL_CALLS and
+    PMC_LONG_CALLS: the ingestion stops rather than mix the workloads."""
+    v = first_grids[:PMC_PREFILL_CALLS]
+    lg = first_grids[PMC_PREFILL_CALLS:PMC_PREFILL_CALLS + PMC_LONG_CALLS]
+    if None in v + lg:
+        return
+    if len(set(v)) > 1 or (lg and (len(set(lg)) > 1 or lg[0] == v[0])):
+        raise SystemExit(f"prefill calls out of step with the counter pass: pass-A grids {first_grids[:8]}")
 
 
 def ingest_pmc(fetch_csv, write_csv):
@@ -223,12 +238,16 @@ def ingest_pmc(fetch_csv, write_csv):
     # call: every prefill-kernel dispatch of the call, averaged over calls.
     per_call = {}
     for name in ("FETCH_SIZE", "WRITE_SIZE"):
-        calls = []
+        calls, grids = [], []
         for r in sorted(rows[name], key=lambda r: int(r["Dispatch_Id"])):
             if "segment_plan_kernel" in r["Kernel_Name"]:
                 calls.append(0.0)
+                grids.append(False)
             elif calls and "prefill_kernel<128" in r["Kernel_Name"]:
                 calls[-1] += float(r["Counter_Value"]) * 1024
+                if grids[-1] is False:
+                    grids[-1] = r.get("Grid_Size")
+        check_prefill_calls(grids)
         per_call[name] = calls
     for key, c0, nc, units in (("prefill_kernel_d128_bf16", 0, PMC_PREFILL_CALLS, varlen_tokens()),
                                ("prefill_long_kernel_d128_bf16", PMC_PREFILL_CALLS, PMC_LONG_CALLS, 1 << 20)):
@@ -262,7 +281,7 @@ def ingest_mfma(paths):
     for path in paths:
         disp = {}
         for r in csv.DictReader(open(path)):
-            d = disp.setdefault(int(r["Dispatch_Id"]), {"name": r["Kernel_Name"]})
+            d = disp.setdefault(int(r["Dispatch_Id"]), {"name": r["Kernel_Name"], "grid": r.get("Grid_Size")})
             d[r["Counter_Name"]] = float(r["Counter_Value"])
         order = [disp[i] for i in sorted(disp)]
         need = ("MfmaUtil", "VALUBusy", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "GRBM_GUI_ACTIVE")
@@ -301,6 +320,8 @@ def ingest_mfma(paths):
                 calls.append(cur)
             elif cur is not None and ("prefill_kernel<" in d["name"] or "segment_combine_kernel" in d["name"]):
                 cur.append(d)
+        check_prefill_calls([next((d.get("grid") for d in c if "prefill_kernel<" in d["name"]), None)
+                             for c in calls])
         groups = [("prefill_varlen", calls[:PMC_PREFILL_CALLS], varlen_tokens())]
         if len(calls) >= PMC_PREFILL_CALLS + PMC_LONG_CALLS:
             groups.append(("prefill_long_1m", calls[PMC_PREFILL_CALLS:PMC_PREFILL_CALLS + PMC_LONG_CALLS],
@@ -349,10 +370,10 @@ def mfma_counters(key: str, tokens: int, ms: float):
 
 
 def is_decode128(kernel_name: str, W: int) -> bool:
-    """The d = 128 decode kernel: plain (W = 0, two workgroups of 64 columns
-    per head) or with the W-tap conv fused in (one workgroup per head)."""
-    cols = 64 if W == 0 else 128
-    return "decode128_kernel<" in kernel_name and kernel_name.replace(" ", "").endswith(f",{W},{cols}>(kda::Dec128Args)")
+    """The d = 128 decode kernel with bf16 inputs and outputs (one workgroup
+    of four waves per head): plain (W = 0) or with the W-tap conv fused in."""
+    return kernel_name.replace(" ", "").endswith(
+        f"decode128_kernel<unsignedshort,unsignedshort,{W}>(kda::Dec128Args)")
 
 
 def cpu_info():
@@ -462,7 +483,7 @@ def bench_decode(args, torch, K, make_workload):
     value = state_bytes / (ms_step * 1e-3) / 1e9
     achieved = alg_bytes / (k_ms * 1e-3) / 1e9
     traffic = traffic_for("decode_conv_kernel_d128_bf16", "kda_step.hip", N * H)
-    roof = {"kernel": "decode128_kernel<bf16,bf16,W=4,128 columns> (kda_decode_conv)", "bound": "hbm",
+    roof = {"kernel": "decode128_kernel<bf16,bf16,W=4> (kda_decode_conv)", "bound": "hbm",
             "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
             "alg_bytes_per_launch": alg_bytes, "avg_launch_us": round(k_ms * 1e3, 3)}
@@ -686,7 +707,7 @@ PREFILL_WARMUP = 10
 VARLEN_SEGMENT = 4096
 
 
-def bench_prefill_varlen(torch, K, make_workload, dev, iters=20, wl=None, cpu_seconds=0.0):
+def bench_prefill_varlen(torch, K, make_workload, dev, iters=20, wl=None, cpu_seconds=0.0, warm=PREFILL_WARMUP):
     """16 packed sequences, lengths U{512..16384}, H=16, d=128, chunk 64,
     even sequences from random initial states, final states to fresh slots."""
     if wl is None:
@@ -711,7 +732,7 @@ def bench_prefill_varlen(torch, K, make_workload, dev, iters=20, wl=None, cpu_se
         K.kda_prefill_varlen(q, k, v, g, b, o, cu, pool, src, dst, chunk=64, workspace=ws,
                              segment_len=VARLEN_SEGMENT)
 
-    for _ in range(PREFILL_WARMUP):
+    for _ in range(warm):
         run()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
     torch.cuda.synchronize()
@@ -749,7 +770,7 @@ def prefill_roofline(kernel, T, ms, counters_key, traffic_key):
                      "counters": mfma_counters(counters_key, T, ms)}}
 
 
-def bench_conv_prefill(torch, K, wl, dev, iters=20):
+def bench_conv_prefill(torch, K, wl, dev, iters=20, warm=PREFILL_WARMUP):
     """kda_conv_short at prefill scale: the varlen workload's 16 sequences
     (140,625 tokens) over the 3 H d = 6,144 q/k/v channels, W = 4 with SiLU,
     bf16, carried conv history read from and written to per-sequence slots.
@@ -767,7 +788,7 @@ def bench_conv_prefill(torch, K, wl, dev, iters=20):
     cu = wl.cu_seqlens.to(dev)
     y = torch.empty_like(x)
     call = K.prepare_conv_short(x, cw, cu, cpool, src, dst, y=y, act=1)
-    for _ in range(PREFILL_WARMUP):
+    for _ in range(warm):
         call()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -788,7 +809,7 @@ def bench_conv_prefill(torch, K, wl, dev, iters=20):
                          "alg_bytes_per_launch": alg, "avg_launch_us": round(us, 3)}}
 
 
-def bench_prefill_conv(torch, K, wl, dev, iters=10, cpu_seconds=0.0):
+def bench_prefill_conv(torch, K, wl, dev, iters=10, cpu_seconds=0.0, warm=PREFILL_WARMUP):
     """kda_prefill_varlen_conv on the varlen workload: the 16 sequences'
     raw q / k / v projections (6,144 channels, bf16) through the conv
     (W = 4, carried history, SiLU), the per-head q / k normalisation and the
@@ -839,7 +860,7 @@ def bench_prefill_conv(torch, K, wl, dev, iters=10, cpu_seconds=0.0):
                                      norm_channels=2 * H * D)
 
     def timed(fn):
-        for _ in range(PREFILL_WARMUP):
+        for _ in range(warm):
             fn()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
@@ -872,7 +893,7 @@ def bench_prefill_conv(torch, K, wl, dev, iters=10, cpu_seconds=0.0):
     return res
 
 
-def bench_prefill_long(torch, K, make_workload, dev, iters=3, cpu_segments=0):
+def bench_prefill_long(torch, K, make_workload, dev, iters=3, cpu_segments=0, warm=3):
     """B=1, T=1,048,576, H=16, d=128, chunk 64, checkpoints every 32,768 (31
     interior + final), run as 32 segments by the segment scan.  Inputs are
     drawn on the GPU (17 GB bf16).  With cpu_segments > 0 the oracle is timed
@@ -896,7 +917,7 @@ def bench_prefill_long(torch, K, make_workload, dev, iters=3, cpu_segments=0):
     def run():
         K.kda_prefill_varlen(wl.q, wl.k, wl.v, wl.g, wl.beta, o, cu, pool, src, dst, workspace=ws, **kw)
 
-    for _ in range(3):
+    for _ in range(warm):
         run()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

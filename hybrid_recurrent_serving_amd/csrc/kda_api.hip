@@ -388,8 +388,10 @@ int kda_decode_conv(const kda_decode_conv_args* a, kda_stream_t stream_) {
   if (b.x_stride == 0) b.x_stride = C;
   if (b.x_stride < C) return fail(KDA_ERR_SHAPE, "decode_conv: x_stride < 3 H d");
   if (!aligned16(b.x) || !aligned16(b.conv_weight) || !aligned16(b.conv_pool) || !aligned16(b.g) ||
-      !aligned16(b.o) || !aligned16(b.state_pool) || (b.x_stride * eb) % 16)
-    return fail(KDA_ERR_ALIGN, "decode_conv: x, conv_weight, conv_pool, g, o or state_pool not 16-byte aligned");
+      !aligned16(b.o) || !aligned16(b.state_pool) || (b.conv_bias && !aligned16(b.conv_bias)) ||
+      (b.x_stride * eb) % 16)
+    return fail(KDA_ERR_ALIGN,
+                "decode_conv: x, conv_weight, conv_bias, conv_pool, g, o or state_pool not 16-byte aligned");
   int st;
   if ((st = fix_stride(b.g_stride, (int64_t)b.H * b.d, in_dt, "g"))) return st;
   if ((st = fix_stride(b.o_stride, (int64_t)b.H * b.d, out_dt, "o"))) return st;
@@ -443,8 +445,10 @@ int kda_verify_conv(const kda_verify_conv_args* a, kda_stream_t stream_) {
   if (b.x_stride == 0) b.x_stride = C;
   if (b.x_stride < C) return fail(KDA_ERR_SHAPE, "verify_conv: x_stride < 3 H d");
   if (!aligned16(b.x) || !aligned16(b.conv_weight) || !aligned16(b.conv_pool) || !aligned16(b.g) ||
-      (b.o && !aligned16(b.o)) || !aligned16(b.state_pool) || (b.x_stride * eb) % 16)
-    return fail(KDA_ERR_ALIGN, "verify_conv: x, conv_weight, conv_pool, g, o or state_pool not 16-byte aligned");
+      (b.o && !aligned16(b.o)) || !aligned16(b.state_pool) || (b.conv_bias && !aligned16(b.conv_bias)) ||
+      (b.x_stride * eb) % 16)
+    return fail(KDA_ERR_ALIGN,
+                "verify_conv: x, conv_weight, conv_bias, conv_pool, g, o or state_pool not 16-byte aligned");
   int st;
   if ((st = fix_stride(b.g_stride, (int64_t)b.H * b.d, in_dt, "g"))) return st;
   if ((st = fix_stride(b.o_stride, (int64_t)b.H * b.d, out_dt, "o"))) return st;

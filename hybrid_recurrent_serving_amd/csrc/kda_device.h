@@ -150,6 +150,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* base,
   return __builtin_amdgcn_make_buffer_rsrc(ua, 0, __builtin_amdgcn_readfirstlane(bytes), kBufWord3);
 }
 
+// 16 bytes of a state slice through a buffer resource (non-temporal; 0 when
+// the resource has size 0), whole offset in the vector offset
+__device__ __forceinline__ void ld4_rsrc(__amdgpu_buffer_rsrc_t r, int voff, float (&x)[4]) {
+  typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, kBufNonTemporal);
+  x[0] = __uint_as_float(v[0]); x[1] = __uint_as_float(v[1]);
+  x[2] = __uint_as_float(v[2]); x[3] = __uint_as_float(v[3]);
+}
+
 // 16 bytes of a state slice through a buffer resource (non-temporal; dropped
 // when the resource has size 0).  The whole offset goes in the vector
 // offset and the scalar offset is the constant 0: with a scalar register

@@ -557,18 +557,36 @@ int launch_decode_conv(const DecodeConvParams& p, int D, int in_dtype, int out_d
 
 // ---------------------------------------------------------------------------
 // The decode step at d = 128, plain (W = 0) or with the short convolution
-// fused in (W >= 2), laid out for streaming: a lane holds 4 rows x 4 columns
-// of the state (four 16-byte vectors).  A plain copy of the same bytes runs
-// markedly faster with a few 16-byte accesses per lane than with sixteen,
-// so the rows of a head are split across waves instead of the columns:
-// wave w of a workgroup owns rows [16 w, 16 w + 16) of the workgroup's CPW
-// columns, 16 lanes cover 64 columns (256 contiguous bytes of a row), and
-// the reductions over rows (S^T k, S^T q) finish across waves through LDS,
-// in a fixed wave order.  CPW = 64 splits a head over two workgroups, whose
-// blocks are numbered so that both land on the same XCD (block b runs on
-// XCD b mod 8); the fused conv keeps the whole head in one workgroup
-// (CPW = 128), so that each history vector is read and rewritten by one
-// thread even when the conv state is updated in place.
+// fused in (W >= 2), laid out for streaming: one workgroup of four waves per
+// (sequence, head), wave w owning the 64 x 64 block of rows
+// [64 (w >> 1), + 64) and columns [64 (w & 1), + 64).  Lane l holds columns
+// 64 (w & 1) + 4 (l & 15) .. + 3 of the sixteen rows 64 (w >> 1) + (l >> 4) + 4 j:
+// each of its sixteen 16-byte accesses covers, across the wave, 256
+// contiguous bytes of four consecutive rows.  A copy-only probe of the
+// decode's 268 MB of state (read, a reduction over the rows, write back in
+// place) took 44.8 us in this layout against 48.4-49.0 us with four rows
+// per lane in 8- or 16-wave workgroups: a wave keeps 16 KiB of state in
+// flight rather than 4 KiB.
+//
+// Every token-level load (q, k, v, g or the conv inputs, beta, the output
+// gate and norm weight) is issued before the state loads, as raw bits, and
+// the state loads go through a buffer resource that has size 0 when the
+// source slot is absent (every load returns 0): the loads are then issued on
+// every path, and since the load counter is in order, the token work waits
+// for its own loads only while the state is in flight, and the first pass
+// takes the state rows as they arrive.
+//
+// Pass 1 forms Diag(alpha) S and, over the lane's rows, the partial S^T k
+// and (Diag(alpha) S)^T q, reduced across the four lane groups of the wave by
+// the permlane swaps and then over the two row halves through LDS, in a
+// fixed order.  The read-out of the updated state follows without a second
+// pass over it: S'^T q = (Diag(alpha) S)^T q + u (k . q).  Pass 2 is the
+// rank-1 correction S' = Diag(alpha) S + k u^T alone, each row stored as soon
+// as it is formed; with the read-out out of the way the stores leave during
+// the pass rather than after it, which measured 0.7-1.7 us faster per step.
+// The per-row values (alpha = exp g, k, q) sit in LDS in lane-group order,
+// row r at (r & 3) * 32 + (r >> 2), so that a lane reads its sixteen rows as
+// four 16-byte vectors.
 struct Dec128Args {
   const void *q, *k, *v;                // plain inputs [n_seq, H, 128] (W = 0)
   const void *x, *w, *bias;             // conv inputs (W >= 2)
@@ -591,261 +609,287 @@ struct Dec128Args {
 
 namespace d128 {
 constexpr int D = 128;
-constexpr int RPL = 4;                  // rows per lane
-template <int CPW> struct Shape {
-  static constexpr int PARTS = D / CPW; // workgroups per (sequence, head)
-  static constexpr int LPR = CPW / 4;   // lanes per row
-  static constexpr int RG = 64 / LPR;   // row groups per wave
-  static constexpr int RPW = RG * RPL;  // rows per wave
-  static constexpr int NW = D / RPW;    // waves per workgroup
+constexpr int NW = 4;                   // waves per workgroup: (row half, column half)
+constexpr int NT = 64 * NW;
+constexpr int RPL = 16;                 // rows per lane
+// LDS position of row r in lane-group order
+__device__ __forceinline__ int grp_pos(int r) { return (r & 3) * (D / 4) + (r >> 2); }
+
+// four consecutive elements as raw bits (8 bytes of bf16, 16 of fp32),
+// converted where they are first used
+template <typename T> struct raw4;
+template <> struct raw4<bf16_t> {
+  typedef uint2 type;
+  __device__ static __forceinline__ type ld(const bf16_t* p) { return *reinterpret_cast<const uint2*>(p); }
+  __device__ static __forceinline__ void cvt(const type r, float (&x)[4]) {
+    x[0] = __uint_as_float(r.x << 16);
+    x[1] = __uint_as_float(r.x & 0xffff0000u);
+    x[2] = __uint_as_float(r.y << 16);
+    x[3] = __uint_as_float(r.y & 0xffff0000u);
+  }
+  __device__ static __forceinline__ type zero() { return make_uint2(0u, 0u); }
+};
+template <> struct raw4<float> {
+  typedef float4 type;
+  __device__ static __forceinline__ type ld(const float* p) { return *reinterpret_cast<const float4*>(p); }
+  __device__ static __forceinline__ void cvt(const type r, float (&x)[4]) {
+    x[0] = r.x; x[1] = r.y; x[2] = r.z; x[3] = r.w;
+  }
+  __device__ static __forceinline__ type zero() { return make_float4(0.f, 0.f, 0.f, 0.f); }
 };
 }  // namespace d128
 
-template <typename Tin, typename Tout, int W, int CPW>
-__global__ void __launch_bounds__(64 * d128::Shape<CPW>::NW) decode128_kernel(const Dec128Args p) {
+template <typename Tin, typename Tout, int W>
+__global__ void __launch_bounds__(d128::NT) __attribute__((amdgpu_waves_per_eu(4)))
+decode128_kernel(const Dec128Args p) {
   using namespace d128;
-  using SH = Shape<CPW>;
+  using R4 = raw4<Tin>;
   constexpr bool CONV = W >= 2;
-  static_assert(!CONV || SH::PARTS == 1, "the fused conv keeps a head in one workgroup");
-  constexpr int NW = SH::NW, LPR = SH::LPR, RPW = SH::RPW, PARTS = SH::PARTS;
-  constexpr int V = Vec16x<Tin>::N;     // channels per conv item
-  constexpr int NCI = 3 * D / V;        // conv items of one head
   constexpr int HW = CONV ? W - 1 : 1;  // history length
-  static_assert(!CONV || NCI <= 64 * NW, "one conv item per thread");
-  __shared__ __align__(16) float s_y[CONV ? 3 * D : 4];   // q | k | v of the head (fp32)
-  __shared__ __align__(16) float s_w[NW][CPW], s_o[NW][CPW];
+  constexpr int NTAP = CONV ? W : 1;
+  __shared__ __align__(16) float s_q[D], s_k[D], s_a[D], s_v[D];   // q, k, alpha in lane-group order; v
+  __shared__ __align__(16) float s_w[NW][64], s_o[NW][64];          // per-wave partial S^T k, S^T q
   __shared__ __align__(16) float s_gz[CONV ? D : 4], s_gw[CONV ? D : 4];   // output gate and norm weight
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  int64_t item;
-  int part;
-  {
-    const int64_t b = blockIdx.x;
-    const int64_t n_items = static_cast<int64_t>(p.n_seq) * p.H;
-    const int64_t full = (n_items / 8) * 8 * PARTS;
-    if (PARTS > 1 && b < full) {
-      item = (b / (8 * PARTS)) * 8 + b % 8;
-      part = static_cast<int>((b / 8) % PARTS);
-    } else {
-      item = b / PARTS;
-      part = static_cast<int>(b % PARTS);
-    }
-  }
-  const int s = static_cast<int>(item / p.H);
-  const int h = static_cast<int>(item % p.H);
-  const int cg = lane % LPR;
-  const int rg = lane / LPR;
-  const int lc = 4 * cg;                // column inside the workgroup's block
-  const int col = CPW * part + lc;
-  const int row0 = RPW * wave + RPL * rg;
+  const int t = static_cast<int>(threadIdx.x);
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  const int rh = wave >> 1;             // row half
+  const int cb = wave & 1;              // column half
+  const int grp = lane >> 4;
+  const int lc = 4 * (lane & 15);
+  const int col = 64 * cb + lc;
+  const int s = static_cast<int>(blockIdx.x / p.H);
+  const int h = static_cast<int>(blockIdx.x % p.H);
   const int src = p.src_slot[s];
   const int dst = p.dst_slot[s];
   const bool has_src = src >= 0 && src < p.n_slots;
   const bool has_dst = dst >= 0 && dst < p.n_slots;
 
-  // The convolution (conv waves only, before their own state loads: their
-  // conv data and their state slice are never live together, which keeps
-  // the register count of the 16-wave workgroup low).  Item t < NCI owns V
-  // channels of the head's q, k or v block.
-  if constexpr (CONV) {
-    if (wave < (NCI + 63) / 64) {
-      const int t = static_cast<int>(threadIdx.x);
-      const int64_t C = 3LL * p.H * D;
-      const int csrc = p.csrc[s];
-      const int cdst = p.cdst[s];
-      if (t < NCI) {
-        const int blk = t / (D / V);    // 0 q, 1 k, 2 v
-        const int cc = (t % (D / V)) * V;
-        const int64_t ch = static_cast<int64_t>(blk) * p.H * D + static_cast<int64_t>(h) * D + cc;
-        const bool has_hist = csrc >= 0 && csrc < p.n_cslots;
-        // taps: the V * W values of channels ch .. ch + V - 1 are contiguous
-        // (W 16-byte vectors), tapf[b][e] = weight[(b V + e) / W, (b V + e) % W];
-        // history likewise (W - 1 vectors); the token (one vector)
-        float tapf[W][V], histf[HW][V], xt[V];
-        const Tin* wp = static_cast<const Tin*>(p.w) + ch * W;
+  // Token-level inputs.  Thread t handles the 4 channels c4 .. c4 + 3 of
+  // role t >> 5: 0 q, 1 k, 2 v (the conv of those channels when W >= 2),
+  // 3 g, 4 the output gate, 5 the output norm weight (gated output only).
+  const int role = t >> 5;
+  const int c4 = 4 * (t & 31);
+  typename R4::type xr = R4::zero();
+  typename R4::type tr[NTAP], hr[HW];
+  typename R4::type br = R4::zero();    // bias
+  const int64_t C = 3LL * p.H * D;
+  const int64_t ch = static_cast<int64_t>(role) * p.H * D + static_cast<int64_t>(h) * D + c4;
+  bool has_hist = false;
+  if (role < 3) {
+    if constexpr (CONV) {
+      // taps of channels ch .. ch + 3 (4 W contiguous values), the token, the history (4 (W - 1) values)
+      const Tin* wp = static_cast<const Tin*>(p.w) + ch * W;
 #pragma unroll
-        for (int b = 0; b < W; ++b) Vec16x<Tin>::ld(wp + b * V, tapf[b]);
-        Vec16x<Tin>::ld(static_cast<const Tin*>(p.x) + static_cast<int64_t>(s) * p.x_stride + ch, xt);
-        if (has_hist) {
-          const Tin* hp = static_cast<const Tin*>(p.cpool) + (static_cast<int64_t>(csrc) * C + ch) * HW;
+      for (int b = 0; b < W; ++b) tr[b] = R4::ld(wp + 4 * b);
+      xr = R4::ld(static_cast<const Tin*>(p.x) + static_cast<int64_t>(s) * p.x_stride + ch);
+      const int cs = p.csrc[s];
+      has_hist = cs >= 0 && cs < p.n_cslots;
+      const Tin* hp = static_cast<const Tin*>(p.cpool) + (static_cast<int64_t>(has_hist ? cs : 0) * C + ch) * HW;
 #pragma unroll
-          for (int b = 0; b < HW; ++b) Vec16x<Tin>::ld(hp + b * V, histf[b]);
-        }
-        float wt[V][W], hist[V][HW];
-#pragma unroll
-        for (int b = 0; b < W; ++b)
-#pragma unroll
-          for (int e = 0; e < V; ++e) wt[(b * V + e) / W][(b * V + e) % W] = tapf[b][e];
-#pragma unroll
-        for (int b = 0; b < HW; ++b)
-#pragma unroll
-          for (int e = 0; e < V; ++e) hist[(b * V + e) / HW][(b * V + e) % HW] = has_hist ? histf[b][e] : 0.f;
-#pragma unroll
-        for (int i = 0; i < V; ++i) {
-          // tap W-1 multiplies the token, tap j < W-1 the history value j
-          float acc = p.bias ? io<Tin>::ld(static_cast<const Tin*>(p.bias) + ch + i) : 0.f;
-#pragma unroll
-          for (int j = 0; j < HW; ++j) acc = fmaf(wt[i][j], hist[i][j], acc);
-          acc = fmaf(wt[i][HW], xt[i], acc);
-          if (p.act == 1) acc = silu_fast(acc);
-          s_y[blk * D + cc + i] = acc;
-        }
-        // advanced history: hist[1 .. W-2] ++ token (read and rewritten by this thread only)
-        if (cdst >= 0 && cdst < p.n_cslots) {
-          float nh[V * HW];
-#pragma unroll
-          for (int i = 0; i < V; ++i)
-#pragma unroll
-            for (int j = 0; j < HW; ++j) nh[i * HW + j] = j + 1 < HW ? hist[i][j + 1] : xt[i];
-          Tin* np_ = static_cast<Tin*>(p.cpool) + (static_cast<int64_t>(cdst) * C + ch) * HW;
-#pragma unroll
-          for (int b = 0; b < HW; ++b) {
-            float f[V];
-#pragma unroll
-            for (int e = 0; e < V; ++e) f[e] = nh[b * V + e];
-            Vec16x<Tin>::st(np_ + b * V, f);
-          }
-        }
-      }
+      for (int b = 0; b < HW; ++b) hr[b] = has_hist ? R4::ld(hp + 4 * b) : R4::zero();
+      if (p.bias) br = R4::ld(static_cast<const Tin*>(p.bias) + ch);
+    } else {
+      const Tin* base = role == 0 ? static_cast<const Tin*>(p.q) + static_cast<int64_t>(s) * p.q_stride
+                      : role == 1 ? static_cast<const Tin*>(p.k) + static_cast<int64_t>(s) * p.k_stride
+                                  : static_cast<const Tin*>(p.v) + static_cast<int64_t>(s) * p.v_stride;
+      xr = R4::ld(base + static_cast<int64_t>(h) * D + c4);
     }
+  } else if (role == 3) {
+    xr = R4::ld(static_cast<const Tin*>(p.g) + static_cast<int64_t>(s) * p.g_stride + static_cast<int64_t>(h) * D + c4);
+  } else if (CONV && p.ogate && role < 6) {
+    xr = R4::ld(role == 4 ? static_cast<const Tin*>(p.ogate) + static_cast<int64_t>(s) * p.ogate_stride +
+                                static_cast<int64_t>(h) * D + c4
+                          : static_cast<const Tin*>(p.onorm_w) + c4);
   }
-
-  float S[RPL][4];
-  if (has_src) {
-    const float* sp = p.pool + ((static_cast<int64_t>(src) * p.H + h) * D + row0) * D + col;
-#pragma unroll
-    for (int i = 0; i < RPL; ++i) ld4_stream(sp + static_cast<int64_t>(i) * D, S[i]);
-  } else {
-#pragma unroll
-    for (int i = 0; i < RPL; ++i) S[i][0] = S[i][1] = S[i][2] = S[i][3] = 0.f;
-  }
-  float ar[RPL], kr[RPL], qr[RPL], vc[4];
-  ld_vec<Tin, RPL>(static_cast<const Tin*>(p.g) + static_cast<int64_t>(s) * p.g_stride + static_cast<int64_t>(h) * D + row0,
-                   ar);
   const float beta = io<Tin>::ld(static_cast<const Tin*>(p.beta) + static_cast<int64_t>(s) * p.beta_stride + h);
-  // The output gate and norm weight (gated output only), put in LDS with the
-  // conv results by the first wave that runs no conv, after its own state
-  // loads: their registers are then never live across the conv, whose
-  // register peak sets the kernel's occupancy.
-  constexpr int GATE_WAVE = (NCI + 63) / 64;
-  static_assert(!CONV || GATE_WAVE < NW, "a wave without conv items");
-  const int gt = static_cast<int>(threadIdx.x) - 64 * GATE_WAVE;
-  const bool gate_lane = CONV && p.ogate && gt >= 0 && gt < D / 4;
-  float gz[4] = {0.f, 0.f, 0.f, 0.f}, gw[4] = {0.f, 0.f, 0.f, 0.f};
-  if (gate_lane) {
-    io<Tin>::ld4(static_cast<const Tin*>(p.ogate) + static_cast<int64_t>(s) * p.ogate_stride +
-                     static_cast<int64_t>(h) * D + 4 * gt, gz);
-    io<Tin>::ld4(static_cast<const Tin*>(p.onorm_w) + 4 * gt, gw);
-  }
-  if constexpr (!CONV) {
-    ld_vec<Tin, RPL>(static_cast<const Tin*>(p.k) + static_cast<int64_t>(s) * p.k_stride + static_cast<int64_t>(h) * D + row0,
-                     kr);
-    ld_vec<Tin, RPL>(static_cast<const Tin*>(p.q) + static_cast<int64_t>(s) * p.q_stride + static_cast<int64_t>(h) * D + row0,
-                     qr);
-    io<Tin>::ld4(static_cast<const Tin*>(p.v) + static_cast<int64_t>(s) * p.v_stride + static_cast<int64_t>(h) * D + col, vc);
-  } else {
-    if (gate_lane) {
-      *reinterpret_cast<float4*>(&s_gz[4 * gt]) = make_float4(gz[0], gz[1], gz[2], gz[3]);
-      *reinterpret_cast<float4*>(&s_gw[4 * gt]) = make_float4(gw[0], gw[1], gw[2], gw[3]);
-    }
-    __syncthreads();
-    float inv_q = 1.f, inv_k = 1.f;
-    if (p.qk_l2norm) {
-      float sq = 0.f, sk = 0.f;
-#pragma unroll
-      for (int c = lane; c < D; c += 64) {
-        sq = fmaf(s_y[c], s_y[c], sq);
-        sk = fmaf(s_y[D + c], s_y[D + c], sk);
-      }
-      sq = wave_sum_from<1>(sq);
-      sk = wave_sum_from<1>(sk);
-      inv_q = 1.f / sqrtf(sq + p.eps);
-      inv_k = 1.f / sqrtf(sk + p.eps);
-    }
-#pragma unroll
-    for (int i = 0; i < RPL; ++i) {
-      qr[i] = s_y[row0 + i] * inv_q;
-      kr[i] = s_y[D + row0 + i] * inv_k;
-    }
-#pragma unroll
-    for (int c = 0; c < 4; ++c) vc[c] = s_y[2 * D + col + c];
-  }
-#pragma unroll
-  for (int i = 0; i < RPL; ++i) ar[i] = expf(ar[i]);
 
-  // Diag(alpha) S and the partial S^T k of the lane's rows, summed over the
-  // wave's rows, then over the waves (in order)
+  // the state block, in flight while the token work runs (an absent source
+  // reads through a resource of size 0)
+  float S[RPL][4];
+  const int voff = ((64 * rh + grp) * D + col) * 4;
+  {
+    const __amdgpu_buffer_rsrc_t rs = uniform_rsrc(
+        p.pool + (static_cast<int64_t>(has_src ? src : 0) * p.H + h) * D * D, has_src ? D * D * 4 : 0);
+#pragma unroll
+    for (int j = 0; j < RPL; ++j) ld4_rsrc(rs, voff + 16 * j * D, S[j]);
+  }
+
+  // token work into LDS
+  if (role < 3) {
+    float y[4];
+    if constexpr (CONV) {
+      float tv[W * 4], hv[HW * 4], xv[4];
+#pragma unroll
+      for (int b = 0; b < W; ++b) {
+        float f[4];
+        R4::cvt(tr[b], f);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) tv[4 * b + e] = f[e];
+      }
+#pragma unroll
+      for (int b = 0; b < HW; ++b) {
+        float f[4];
+        R4::cvt(hr[b], f);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) hv[4 * b + e] = f[e];
+      }
+      R4::cvt(xr, xv);
+      float bv[4];
+      R4::cvt(br, bv);
+      // channel i: tap W-1 multiplies the token, tap j < W-1 the history value j
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float acc = bv[i];
+#pragma unroll
+        for (int j = 0; j < HW; ++j) acc = fmaf(tv[i * W + j], hv[i * HW + j], acc);
+        acc = fmaf(tv[i * W + HW], xv[i], acc);
+        y[i] = p.act == 1 ? silu_fast(acc) : acc;
+      }
+      // advanced history: values 1 .. W-2 then the token (read and rewritten by this thread only)
+      const int cd = p.cdst[s];
+      if (cd >= 0 && cd < p.n_cslots) {
+        Tin* np_ = static_cast<Tin*>(p.cpool) + (static_cast<int64_t>(cd) * C + ch) * HW;
+#pragma unroll
+        for (int b = 0; b < HW; ++b) {
+          float f[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i = (4 * b + e) / HW, j = (4 * b + e) % HW;
+            f[e] = j + 1 < HW ? hv[i * HW + j + 1] : xv[i];
+          }
+          io<Tin>::st4(np_ + 4 * b, f);
+        }
+      }
+    } else {
+      R4::cvt(xr, y);
+    }
+    if (role == 2) {
+      *reinterpret_cast<float4*>(&s_v[c4]) = make_float4(y[0], y[1], y[2], y[3]);
+    } else {
+      float* dq = role == 0 ? s_q : s_k;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dq[grp_pos(c4 + i)] = y[i];
+    }
+  } else if (role == 3) {
+    float gv[4];
+    R4::cvt(xr, gv);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s_a[grp_pos(c4 + i)] = expf(gv[i]);
+  } else if (CONV && p.ogate && role < 6) {
+    float f[4];
+    R4::cvt(xr, f);
+    *reinterpret_cast<float4*>(role == 4 ? &s_gz[c4] : &s_gw[c4]) = make_float4(f[0], f[1], f[2], f[3]);
+  }
+  __syncthreads();
+
+  float inv_q = 1.f, inv_k = 1.f;
+  if (CONV && p.qk_l2norm) {
+    float sq = s_q[lane] * s_q[lane];
+    sq = fmaf(s_q[lane + 64], s_q[lane + 64], sq);
+    float sk = s_k[lane] * s_k[lane];
+    sk = fmaf(s_k[lane + 64], s_k[lane + 64], sk);
+    sq = wave_sum_from<1>(sq);
+    sk = wave_sum_from<1>(sk);
+    inv_q = 1.f / sqrtf(sq + p.eps);
+    inv_k = 1.f / sqrtf(sk + p.eps);
+  }
+  const int rp = grp * (D / 4) + 16 * rh;   // LDS position of the lane's first row
+
+  // As the rows arrive: Diag(alpha) S, the partial S^T k and the partial
+  // read-out (Diag(alpha) S)^T q over the lane's rows, then over the wave's
+  // (the read-out of the updated state follows from the latter as
+  // S'^T q = (Diag(alpha) S)^T q + u (k . q)), then the two row halves
   float w[4] = {0.f, 0.f, 0.f, 0.f};
+  float oq[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int i = 0; i < RPL; ++i)
+  for (int jj = 0; jj < RPL / 4; ++jj) {
+    const float4 a4 = *reinterpret_cast<const float4*>(&s_a[rp + 4 * jj]);
+    const float4 k4 = *reinterpret_cast<const float4*>(&s_k[rp + 4 * jj]);
+    const float4 q4 = *reinterpret_cast<const float4*>(&s_q[rp + 4 * jj]);
+    const float av[4] = {a4.x, a4.y, a4.z, a4.w};
+    const float kv[4] = {k4.x * inv_k, k4.y * inv_k, k4.z * inv_k, k4.w * inv_k};
+    const float qv[4] = {q4.x * inv_q, q4.y * inv_q, q4.z * inv_q, q4.w * inv_q};
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      S[i][c] *= ar[i];
-      w[c] = fmaf(S[i][c], kr[i], w[c]);
-    }
+    for (int e = 0; e < 4; ++e)
 #pragma unroll
-  for (int c = 0; c < 4; ++c) w[c] = wave_sum_from<LPR>(w[c]);
-  if (rg == 0) *reinterpret_cast<float4*>(&s_w[wave][lc]) = make_float4(w[0], w[1], w[2], w[3]);
-  __syncthreads();
-  float u[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int ww = 0; ww < NW; ++ww) {
-    const float4 a = *reinterpret_cast<const float4*>(&s_w[ww][lc]);
-    u[0] += a.x;
-    u[1] += a.y;
-    u[2] += a.z;
-    u[3] += a.w;
+      for (int c = 0; c < 4; ++c) {
+        S[4 * jj + e][c] *= av[e];
+        w[c] = fmaf(S[4 * jj + e][c], kv[e], w[c]);
+        oq[c] = fmaf(S[4 * jj + e][c], qv[e], oq[c]);
+      }
   }
 #pragma unroll
-  for (int c = 0; c < 4; ++c) u[c] = beta * (vc[c] - u[c]);
-  // rank-1 correction, state out, partial read-out S^T q
-  float o[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int i = 0; i < RPL; ++i)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      S[i][c] = fmaf(kr[i], u[c], S[i][c]);
-      o[c] = fmaf(S[i][c], qr[i], o[c]);
-    }
+  for (int c = 0; c < 4; ++c) {
+    w[c] = wave_sum_from<16>(w[c]);
+    oq[c] = wave_sum_from<16>(oq[c]);
+  }
+  if (grp == 0) {
+    *reinterpret_cast<float4*>(&s_w[wave][lc]) = make_float4(w[0], w[1], w[2], w[3]);
+    *reinterpret_cast<float4*>(&s_o[wave][lc]) = make_float4(oq[0], oq[1], oq[2], oq[3]);
+  }
+  __syncthreads();
+  // u = beta (v - S^T k) of columns c0 .. c0 + 3, both row halves in order
+  auto delta = [&](int c0, float (&u)[4]) {
+    const int half = c0 >> 6, cc = c0 & 63;
+    const float4 a = *reinterpret_cast<const float4*>(&s_w[half][cc]);
+    const float4 b = *reinterpret_cast<const float4*>(&s_w[2 + half][cc]);
+    const float4 v4 = *reinterpret_cast<const float4*>(&s_v[c0]);
+    u[0] = beta * (v4.x - (a.x + b.x));
+    u[1] = beta * (v4.y - (a.y + b.y));
+    u[2] = beta * (v4.z - (a.z + b.z));
+    u[3] = beta * (v4.w - (a.w + b.w));
+  };
   if (has_dst) {
-    float* dp = p.pool + ((static_cast<int64_t>(dst) * p.H + h) * D + row0) * D + col;
+    // rank-1 correction and the state out (the outputs do not read it)
+    float u[4];
+    delta(col, u);
+    float* dp = p.pool + ((static_cast<int64_t>(dst) * p.H + h) * D + 64 * rh + grp) * D + col;
 #pragma unroll
-    for (int i = 0; i < RPL; ++i) st4_stream(dp + static_cast<int64_t>(i) * D, S[i]);
+    for (int jj = 0; jj < RPL / 4; ++jj) {
+      const float4 k4 = *reinterpret_cast<const float4*>(&s_k[rp + 4 * jj]);
+      const float kv[4] = {k4.x * inv_k, k4.y * inv_k, k4.z * inv_k, k4.w * inv_k};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) S[4 * jj + e][c] = fmaf(kv[e], u[c], S[4 * jj + e][c]);
+        st4_stream(dp + static_cast<int64_t>(4 * (4 * jj + e)) * D, S[4 * jj + e]);
+      }
+    }
   }
+  if (wave == 0) {
+    // k . q over the head (every lane of the wave), then the outputs of
+    // columns 4 t .. 4 t + 3 on lanes t < D / 4
+    float kq = s_k[lane] * s_q[lane];
+    kq = fmaf(s_k[lane + 64], s_q[lane + 64], kq);
+    kq = wave_sum_from<1>(kq) * (inv_k * inv_q);
+    if (t < D / 4) {
+      float u[4];
+      delta(4 * t, u);
+      const int half = t >> 4, cc = 4 * (t & 15);
+      const float4 a = *reinterpret_cast<const float4*>(&s_o[half][cc]);
+      const float4 b = *reinterpret_cast<const float4*>(&s_o[2 + half][cc]);
+      float ov[4] = {fmaf(u[0], kq, a.x + b.x) * p.scale, fmaf(u[1], kq, a.y + b.y) * p.scale,
+                     fmaf(u[2], kq, a.z + b.z) * p.scale, fmaf(u[3], kq, a.w + b.w) * p.scale};
+      if (CONV && p.ogate) {
+        // gated RMS norm: the D outputs are held 4 per lane by lanes 0 .. D/4 - 1
+        float ss = ov[0] * ov[0] + ov[1] * ov[1] + ov[2] * ov[2] + ov[3] * ov[3];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) o[c] = wave_sum_from<LPR>(o[c]);
-  if (rg == 0) *reinterpret_cast<float4*>(&s_o[wave][lc]) = make_float4(o[0], o[1], o[2], o[3]);
-  __syncthreads();
-  if (wave == 0 && rg == 0) {
-    float ov[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int m = 1; m < D / 4; m <<= 1) ss += __shfl_xor(ss, m, 64);
+        const float inv = 1.f / sqrtf(ss * (1.f / D) + p.onorm_eps);
 #pragma unroll
-    for (int ww = 0; ww < NW; ++ww) {
-      const float4 a = *reinterpret_cast<const float4*>(&s_o[ww][lc]);
-      ov[0] += a.x;
-      ov[1] += a.y;
-      ov[2] += a.z;
-      ov[3] += a.w;
+        for (int c = 0; c < 4; ++c) ov[c] = ov[c] * inv * s_gw[4 * t + c] * sigmoid_fast(s_gz[4 * t + c]);
+      }
+      io<Tout>::st4(static_cast<Tout*>(p.o) + static_cast<int64_t>(s) * p.o_stride + static_cast<int64_t>(h) * D + 4 * t,
+                    ov);
     }
-#pragma unroll
-    for (int c = 0; c < 4; ++c) ov[c] *= p.scale;
-    if (CONV && p.ogate) {
-      // gated RMS norm: the D outputs are held 4 per lane by lanes 0 .. D/4 - 1
-      float ss = ov[0] * ov[0] + ov[1] * ov[1] + ov[2] * ov[2] + ov[3] * ov[3];
-#pragma unroll
-      for (int m = 1; m < LPR; m <<= 1) ss += __shfl_xor(ss, m, 64);
-      const float inv = 1.f / sqrtf(ss * (1.f / D) + p.onorm_eps);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) ov[c] = ov[c] * inv * s_gw[lc + c] * sigmoid_fast(s_gz[lc + c]);
-    }
-    io<Tout>::st4(static_cast<Tout*>(p.o) + static_cast<int64_t>(s) * p.o_stride + static_cast<int64_t>(h) * D + col, ov);
   }
 }
 
-template <typename Tin, typename Tout, int W, int CPW>
+template <typename Tin, typename Tout, int W>
 static int launch_decode128(const Dec128Args& a, hipStream_t stream) {
-  using SH = d128::Shape<CPW>;
-  const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(a.n_seq) * a.H * SH::PARTS));
-  hipLaunchKernelGGL((decode128_kernel<Tin, Tout, W, CPW>), grid, dim3(64 * SH::NW), 0, stream, a);
+  const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(a.n_seq) * a.H));
+  hipLaunchKernelGGL((decode128_kernel<Tin, Tout, W>), grid, dim3(d128::NT), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(KDA_ERR_HIP, "decode kernel launch: %s", hipGetErrorString(e));
   return KDA_OK;
@@ -859,7 +903,7 @@ static int launch_decode128_plain(const StepParams& p, hipStream_t stream) {
   a.q_stride = p.q_stride; a.k_stride = p.k_stride; a.v_stride = p.v_stride; a.g_stride = p.g_stride;
   a.beta_stride = p.beta_stride; a.o_stride = p.o_stride; a.n_slots = p.n_slots;
   a.n_seq = p.n_seq; a.H = p.H; a.scale = p.scale;
-  return launch_decode128<Tin, Tout, 0, 64>(a, stream);
+  return launch_decode128<Tin, Tout, 0>(a, stream);
 }
 
 template <typename Tin, typename Tout>
@@ -872,9 +916,9 @@ static int launch_decode128_conv(const DecodeConvParams& p, hipStream_t stream) 
   a.n_seq = p.n_seq; a.H = p.H; a.scale = p.scale;
   a.ogate = p.ogate; a.onorm_w = p.onorm_w; a.ogate_stride = p.ogate_stride; a.onorm_eps = p.onorm_eps;
   switch (p.W) {
-    case 2: return launch_decode128<Tin, Tout, 2, 128>(a, stream);
-    case 3: return launch_decode128<Tin, Tout, 3, 128>(a, stream);
-    case 4: return launch_decode128<Tin, Tout, 4, 128>(a, stream);
+    case 2: return launch_decode128<Tin, Tout, 2>(a, stream);
+    case 3: return launch_decode128<Tin, Tout, 3>(a, stream);
+    case 4: return launch_decode128<Tin, Tout, 4>(a, stream);
     default: return fail(KDA_ERR_UNSUPPORTED, "decode_conv: W = %d (2..4)", p.W);
   }
 }

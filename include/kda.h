@@ -464,11 +464,11 @@ int kda_decode(const kda_decode_args *args, kda_stream_t stream);
  *                packed), or NULL (o as computed); out_norm_weight [d]
  *                in_dtype, shared by the heads, required with out_gate
  * Errors: W outside 2..4 -> KDA_ERR_UNSUPPORTED; d not 16/32/64/128 ->
- * KDA_ERR_UNSUPPORTED; x, conv_weight, conv_pool, g, o, state_pool,
- * out_gate or out_norm_weight not 16-byte aligned, or an x or out_gate
- * stride that breaks 16-byte rows -> KDA_ERR_ALIGN; act not 0/1, qk_l2norm
- * not 0/1, norm_eps or out_norm_eps < 0 -> KDA_ERR_ARG; out_gate without
- * out_norm_weight -> KDA_ERR_NULL.
+ * KDA_ERR_UNSUPPORTED; x, conv_weight, conv_bias (when given), conv_pool,
+ * g, o, state_pool, out_gate or out_norm_weight not 16-byte aligned, or an
+ * x or out_gate stride that breaks 16-byte rows -> KDA_ERR_ALIGN; act not
+ * 0/1, qk_l2norm not 0/1, norm_eps or out_norm_eps < 0 -> KDA_ERR_ARG;
+ * out_gate without out_norm_weight -> KDA_ERR_NULL.
  * ---------------------------------------------------------------------- */
 typedef struct kda_decode_conv_args {
     size_t struct_size;          /* sizeof(kda_decode_conv_args) */

@@ -23,19 +23,27 @@ def tokens(monkeypatch):
 
 def _write(path, rows):
     with open(path, "w", newline="") as f:
-        w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Grid_Size", "Counter_Name",
+                                          "Counter_Value"])
         w.writeheader()
         w.writerows(rows)
+
+
+def _grid(call):
+    """pass-A grid of a prefill call of the counter pass: the varlen calls
+    first, then the 1M-token calls (another grid)"""
+    return 1000 if call < bench.PMC_PREFILL_CALLS else 500
 
 
 def test_ingest_mfma_groups_and_weights(tmp_path, tokens):
     rows, did = [], [0]
 
-    def add(name, util, valu, mops, grbm):
+    def add(name, util, valu, mops, grbm, grid=64):
         did[0] += 1
         for c, v in (("MfmaUtil", util), ("VALUBusy", valu), ("SQ_INSTS_VALU_MFMA_MOPS_BF16", mops),
                      ("GRBM_GUI_ACTIVE", grbm)):
-            rows.append({"Dispatch_Id": did[0], "Kernel_Name": name, "Counter_Name": c, "Counter_Value": v})
+            rows.append({"Dispatch_Id": did[0], "Kernel_Name": name, "Grid_Size": grid, "Counter_Name": c,
+                         "Counter_Value": v})
 
     add(COPY, 0, 1, 0, 100)
     add("Cijk_gemm", 70, 20, 2 * bench.GEMM_N ** 3 / 512, 1000)
@@ -43,9 +51,9 @@ def test_ingest_mfma_groups_and_weights(tmp_path, tokens):
     add(VER, 0, 40, 0, 100)
     for call in range(bench.PMC_PREFILL_CALLS + bench.PMC_LONG_CALLS):
         add(PLAN, 0, 5, 0, 10)
-        add(PF, 20, 40, 1000 * (call + 1), 300)   # pass A
+        add(PF, 20, 40, 1000 * (call + 1), 300, _grid(call))   # pass A
         add(COMB, 0, 2, 0, 10)
-        add(PF, 10, 30, 100, 100)                 # fix-up
+        add(PF, 10, 30, 100, 100, _grid(call) // 2)            # fix-up
     path = tmp_path / "mfma.csv"
     _write(path, rows)
     out = bench.ingest_mfma([str(path)])
@@ -65,10 +73,12 @@ def test_ingest_mfma_groups_and_weights(tmp_path, tokens):
 def test_ingest_pmc_calibrates_and_splits_calls(tmp_path, tokens):
     def rows_for(counter, copy_val, pf_val):
         rows, did = [], 0
-        for name, val in [(COPY, copy_val)] + [(x, y) for _ in range(bench.PMC_PREFILL_CALLS + bench.PMC_LONG_CALLS)
-                                               for x, y in ((PLAN, 1.0), (PF, pf_val), (COMB, 1.0), (PF, pf_val))]:
+        for name, val, grid in [(COPY, copy_val, 1)] + [
+                (x, y, z) for c in range(bench.PMC_PREFILL_CALLS + bench.PMC_LONG_CALLS)
+                for x, y, z in ((PLAN, 1.0, 1), (PF, pf_val, _grid(c)), (COMB, 1.0, 1), (PF, pf_val, _grid(c)))]:
             did += 1
-            rows.append({"Dispatch_Id": did, "Kernel_Name": name, "Counter_Name": counter, "Counter_Value": val})
+            rows.append({"Dispatch_Id": did, "Kernel_Name": name, "Grid_Size": grid, "Counter_Name": counter,
+                         "Counter_Value": val})
         return rows
 
     kib = bench.COPY_BYTES / 1024
@@ -112,3 +122,29 @@ def test_ingest_pmc_single_kernels(tmp_path, tokens):
         assert e["write_bytes"] == round((8.0 + i) * 1024)
     assert out["verify_kernel_d128_bf16"]["units_per_launch"] == 128 * 16
     assert out["conv_norm_kernel_prefill_bf16"]["units_per_launch"] == tokens
+
+
+def test_decode_kernel_names():
+    """The decode rows of the counter ingestion pick the bf16 d = 128 decode
+    kernel by its template arguments: the plain step (W = 0) and the fused
+    conv step (W = 4), not the fp32 instances or the other widths."""
+    plain = "void kda::decode128_kernel<unsigned short, unsigned short, 0>(kda::Dec128Args)"
+    fused = "void kda::decode128_kernel<unsigned short, unsigned short, 4>(kda::Dec128Args)"
+    assert bench.is_decode128(plain, 0) and not bench.is_decode128(plain, 4)
+    assert bench.is_decode128(fused, 4) and not bench.is_decode128(fused, 0)
+    assert not bench.is_decode128("void kda::decode128_kernel<unsigned short, float, 4>(kda::Dec128Args)", 4)
+    assert not bench.is_decode128("void kda::decode128_kernel<unsigned short, unsigned short, 3>(kda::Dec128Args)", 4)
+
+
+def test_prefill_call_layout_checked():
+    """A counter pass whose call counts drift from the ingestion's (more
+    warm-up calls than PMC_PREFILL_CALLS / PMC_LONG_CALLS allow for) would put
+    varlen calls where the 1M-token calls are expected: the pass-A grids
+    expose it and the ingestion stops."""
+    n, m = bench.PMC_PREFILL_CALLS, bench.PMC_LONG_CALLS
+    bench.check_prefill_calls([1000] * n + [500] * m + [1000] * 3)   # as expected
+    bench.check_prefill_calls([None] * (n + m))                       # no grid column: nothing to check
+    with pytest.raises(SystemExit):
+        bench.check_prefill_calls([1000] * (n + m + 4))               # long calls late
+    with pytest.raises(SystemExit):
+        bench.check_prefill_calls([1000] * (n - 1) + [500] * (m + 1))  # long calls early
