@@ -129,8 +129,8 @@ def test_decode_conv_widths_in_place(dev, oracle64, W):
 
 @pytest.mark.parametrize("d", [16, 32, 128])
 def test_decode_conv_fp32_small(dev, oracle64, d):
-    """fp32 inputs and outputs (small head sizes, and d = 128 with its
-    16-wave layout and fp32 conv items on two waves): the only roundings
+    """fp32 inputs and outputs (small head sizes, and d = 128 with one
+    4-wave workgroup per head and 16-byte conv units): the only roundings
     left are the fp32 accumulation orders."""
     U.say(f"decode_conv fp32 d={d}")
     N, H, W = 9, 3, 4
@@ -142,6 +142,53 @@ def test_decode_conv_fp32_small(dev, oracle64, d):
     U.assert_close("o", U.to_np(o), ref["o"], rel=1e-5, mx=1e-5)
     U.assert_close("state", U.to_np(st), ref["state"], rel=1e-5, mx=1e-5)
     _check_conv_state(cs, x, hist)
+
+
+@pytest.mark.parametrize("W", [2, 3])
+def test_decode_conv_d128_widths_absent_slots(dev, oracle64, W):
+    """d = 128, bf16 inputs, fp32 outputs, conv widths 2 and 3 with a bias
+    (W = 3 also with the gated output norm): absent state sources start from
+    zero, absent state destinations store nothing (the slot keeps its
+    sentinel), absent conv histories read zeros, results copied on write."""
+    U.say(f"decode_conv d128 W={W} absent slots")
+    N, H, d = 12, 4, 128
+    x, w, bias, cst, g, b, init = _case(N, H, d, W, torch.bfloat16, seed=70 + W)
+    C = 3 * H * d
+    ssrc = [s if s % 3 != 1 else -1 for s in range(N)]
+    sdst = [N + s if s % 4 != 2 else -1 for s in range(N)]
+    csrc = [s if s % 2 == 0 else -1 for s in range(N)]
+    gate = gw = None
+    if W == 3:
+        gate, gw = _gate(torch.Generator().manual_seed(470), (N, H, d), torch.bfloat16, d)
+    cpool = torch.zeros(2 * N, C, W - 1, dtype=torch.bfloat16, device=dev)
+    cpool[:N] = cst.to(dev)
+    pool = torch.zeros(2 * N, H, d, d, device=dev)
+    pool[:N] = init.to(dev)
+    pool[N:] = 7.0
+    before = pool.clone()
+
+    def i32(v):
+        return torch.tensor(v, dtype=torch.int32, device=dev)
+
+    o = torch.empty(N, H, d, device=dev)
+    K.kda_decode_conv(x.to(dev), w.to(dev), cpool, i32(csrc), i32([N + s for s in range(N)]), g.to(dev),
+                      b.to(dev), o, pool, i32(ssrc), i32(sdst), conv_bias=bias.to(dev), act=1, qk_l2norm=1,
+                      out_gate=None if gate is None else gate.to(dev),
+                      out_norm_weight=None if gw is None else gw.to(dev))
+    torch.cuda.synchronize()
+    init0 = init.clone()
+    for s in range(N):
+        if ssrc[s] < 0:
+            init0[s] = 0.0
+    ref, hist = _reference(oracle64, x, w, bias, cst, g, b, init0, csrc, act=1, norm=1, gate=gate, gw=gw)
+    U.assert_close("o", U.to_np(o), ref["o"], rel=1e-5, mx=1e-4)
+    stored = [s for s in range(N) if sdst[s] >= 0]
+    U.assert_close("state", U.to_np(pool[[N + s for s in stored]]), ref["state"][stored], rel=1e-5, mx=1e-4)
+    for s in range(N):
+        if sdst[s] < 0:
+            assert torch.equal(pool[N + s], before[N + s]), "absent destination written"
+    assert torch.equal(pool[:N], before[:N]), "source states modified"
+    _check_conv_state(cpool[N:], x, hist)
 
 
 def test_decode_conv_gated_norm_128(dev, oracle64):

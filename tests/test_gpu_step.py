@@ -184,6 +184,26 @@ def test_decode_strided_inputs(dev, oracle64):
     U.assert_close("state", U.to_np(pool), ref["final"], rel=1e-5, mx=1e-4)
 
 
+def test_decode_d128_strided_inputs(dev, oracle64):
+    """d = 128: q, k, v as views into one fused projection buffer (token
+    stride 3 H d), the per-row values staged from strided rows."""
+    U.say("decode d128 strided")
+    wl = make_workload(1, n_seq=9, H=4, d=128)
+    init, has = _oracle_states(wl)
+    ref = oracle64.kda_varlen(wl.q, wl.k, wl.v, wl.g, wl.beta, wl.cu_seqlens, init=init,
+                              has_init=has)
+    fused = torch.cat([wl.q, wl.k, wl.v], dim=1).to(dev)  # [N, 3H, d]
+    q, k, v = fused[:, 0:4], fused[:, 4:8], fused[:, 8:12]
+    g, b = wl.g.to(dev), wl.beta.to(dev)
+    pool = wl.init_states.to(dev).clone()
+    slots = torch.arange(9, dtype=torch.int32, device=dev)
+    o = torch.empty(9, 4, 128, dtype=torch.bfloat16, device=dev)
+    K.kda_decode(q, k, v, g, b, o, pool, slots, slots)
+    torch.cuda.synchronize()
+    U.assert_close("o", U.to_np(o), ref["o"])
+    U.assert_close("state", U.to_np(pool), ref["final"], rel=1e-5, mx=1e-4)
+
+
 # ------------------------------------------------------------------ verify
 def test_verify_fused_128x8(dev, oracle64):
     """Speculative verify: 128 sequences x 8 tokens, outputs at all positions,
@@ -414,10 +434,9 @@ def test_verify_d128_matrix_core_fp32_outputs(dev, oracle64, T_spec):
 
 
 def test_decode_d128_item_count_not_multiple_of_8(dev, oracle64):
-    """d = 128 decode with 5 sequences x 3 heads = 15 (sequence, head) items:
-    the blocks past the last whole group of 8 items take the plain block
-    order (the two halves of a head are otherwise placed on one XCD).  fp32
-    in and out against the oracle, in place and copy-on-write."""
+    """d = 128 decode with 5 sequences x 3 heads = 15 (sequence, head) items,
+    a grid that is no multiple of the 8 XCDs; fp32 in and out against the
+    oracle, in place and copy-on-write."""
     U.say("decode d128, 15 items")
     wl = make_workload(1, n_seq=5, H=3, d=128)
     init, has = _oracle_states(wl)
