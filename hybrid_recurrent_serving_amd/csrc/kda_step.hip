@@ -777,8 +777,13 @@ decode128_kernel(const Dec128Args p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) s_a[grp_pos(c4 + i)] = expf(gv[i]);
   } else if (CONV && p.ogate && role < 6) {
+    // the output gate as sigmoid(z), the norm weight as it is
     float f[4];
     R4::cvt(xr, f);
+    if (role == 4) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) f[i] = sigmoid_fast(f[i]);
+    }
     *reinterpret_cast<float4*>(role == 4 ? &s_gz[c4] : &s_gw[c4]) = make_float4(f[0], f[1], f[2], f[3]);
   }
   __syncthreads();
@@ -874,11 +879,10 @@ decode128_kernel(const Dec128Args p) {
       if (CONV && p.ogate) {
         // gated RMS norm: the D outputs are held 4 per lane by lanes 0 .. D/4 - 1
         float ss = ov[0] * ov[0] + ov[1] * ov[1] + ov[2] * ov[2] + ov[3] * ov[3];
-#pragma unroll
-        for (int m = 1; m < D / 4; m <<= 1) ss += __shfl_xor(ss, m, 64);
+        ss = group_sum<D / 4>(ss);
         const float inv = 1.f / sqrtf(ss * (1.f / D) + p.onorm_eps);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) ov[c] = ov[c] * inv * s_gw[4 * t + c] * sigmoid_fast(s_gz[4 * t + c]);
+        for (int c = 0; c < 4; ++c) ov[c] = ov[c] * inv * s_gw[4 * t + c] * s_gz[4 * t + c];
       }
       io<Tout>::st4(static_cast<Tout*>(p.o) + static_cast<int64_t>(s) * p.o_stride + static_cast<int64_t>(h) * D + 4 * t,
                     ov);
