@@ -596,6 +596,26 @@ verify_conv_kernel(const DecodeConvParams p) {
   }
   bf16_t braw = 0;
   if (tid < T) braw = static_cast<const bf16_t*>(p.beta)[(static_cast<int64_t>(s) * T + tid) * p.beta_stride + h];
+  // the output gate and norm weight of this thread's output units (4
+  // channels of one token each) as raw bits, also requested before the
+  // state: read at the end they would wait for the state stores as well (the
+  // vector memory counter takes loads and stores in issue order).  Padded
+  // tokens and an ungated call read valid addresses whose values are unused.
+  constexpr int OU = TB * D / 4 / NT;   // output units per thread
+  uint2 graw[OU], wraw[OU];
+  {
+    const bool gated = with_o && p.ogate;
+#pragma unroll
+    for (int k = 0; k < OU; ++k) {
+      const int e = 4 * (k * NT + tid);
+      const int j = e / D < T ? e / D : T - 1, c = e % D;
+      const bf16_t* gp = gated ? static_cast<const bf16_t*>(p.ogate) + (static_cast<int64_t>(s) * T + j) * p.ogate_stride + hd + c
+                               : static_cast<const bf16_t*>(p.x);
+      const bf16_t* wp = gated ? static_cast<const bf16_t*>(p.onorm_w) + c : static_cast<const bf16_t*>(p.x);
+      graw[k] = *reinterpret_cast<const uint2*>(gp);
+      wraw[k] = *reinterpret_cast<const uint2*>(wp);
+    }
+  }
   f32x4 S[2][D / 16];
   load_state(S, p.pool, src, p.n_slots, p.H, h, ln);
 
@@ -760,14 +780,27 @@ verify_conv_kernel(const DecodeConvParams p) {
     // a token's D outputs by D / 4 consecutive lanes (the gated norm sums
     // across exactly those; every round covers whole tokens)
     Tout* ob = static_cast<Tout*>(p.o);
-    for (int e = 4 * tid; e < T * D; e += 4 * NT) {
-      const int j = e / D, c = e % D;
-      const float4 o4 = *reinterpret_cast<const float4*>(&sm.x.o[j][c]);
-      float ov[4] = {o4.x, o4.y, o4.z, o4.w};
-      if (p.ogate)
-        gate_norm4<D, bf16_t>(ov, static_cast<const bf16_t*>(p.ogate) + (static_cast<int64_t>(s) * T + j) * p.ogate_stride + hd + c,
-                              static_cast<const bf16_t*>(p.onorm_w) + c, p.onorm_eps);
-      io<Tout>::st4(ob + (static_cast<int64_t>(s) * T + j) * p.o_stride + hd + c, ov);
+#pragma unroll
+    for (int k = 0; k < OU; ++k) {
+      const int e = 4 * (k * NT + tid);
+      if (e < T * D) {
+        const int j = e / D, c = e % D;
+        const float4 o4 = *reinterpret_cast<const float4*>(&sm.x.o[j][c]);
+        float ov[4] = {o4.x, o4.y, o4.z, o4.w};
+        if (p.ogate) {
+          // gated RMS norm over the token's D outputs, held 4 per lane by
+          // an aligned group of D / 4 lanes (every lane of it active)
+          float ss = ov[0] * ov[0] + ov[1] * ov[1] + ov[2] * ov[2] + ov[3] * ov[3];
+          ss = group_sum<D / 4>(ss);
+          const float inv = 1.f / sqrtf(ss * (1.f / D) + p.onorm_eps);
+          float z[4], w[4];
+          unpack4(graw[k], z);
+          unpack4(wraw[k], w);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) ov[i] = ov[i] * inv * w[i] * sigmoid_fast(z[i]);
+        }
+        io<Tout>::st4(ob + (static_cast<int64_t>(s) * T + j) * p.o_stride + hd + c, ov);
+      }
     }
   }
 }
