@@ -98,6 +98,8 @@ def test_decode_conv_validation(lib):
     assert _call(lib, f, _decode_conv_args(x_stride=769)) == 4       # rows not 16-byte aligned
     assert b"aligned" in lib.kda_last_error()
     fake = 1 << 20
+    assert _call(lib, f, _decode_conv_args(conv_bias=fake + 8)) == 4  # bias read in 8- / 16-byte units
+    assert b"conv_bias" in lib.kda_last_error()
     assert _call(lib, f, _decode_conv_args(out_gate=fake)) == 1      # gate without norm weight
     assert _call(lib, f, _decode_conv_args(out_gate=fake, out_norm_weight=fake, out_norm_eps=-1.0)) == 8
     assert _call(lib, f, _decode_conv_args(out_gate=fake + 8, out_norm_weight=fake)) == 4
@@ -131,6 +133,7 @@ def test_verify_conv_validation(lib):
     assert _call(lib, f, args(W=5)) == 6
     assert _call(lib, f, args(act=3)) == 8
     assert _call(lib, f, args(x_stride=769)) == 4
+    assert _call(lib, f, args(conv_bias=fake + 2)) == 4
     assert _call(lib, f, args(out_gate=fake)) == 1
     assert _call(lib, f, args(out_gate=fake, out_norm_weight=fake + 4)) == 4
 
