@@ -31,6 +31,13 @@ namespace kda {
 constexpr int CONV_TT = 16;      // tokens per body item
 constexpr int CONV_THREADS = 256;
 
+// Outputs and new histories are written once and not read again by this
+// kernel: non-temporal stores (the conv at prefill scale ran 4% faster with
+// them: 631 us against 659 us for 140,625 tokens x 6,144 channels).  The
+// loads keep the default policy: a tile's W-1 rows before its own are the
+// previous tile's last rows, found in L2 (non-temporal loads: 666 us).
+typedef __attribute__((ext_vector_type(4))) uint32_t nt4u;
+
 template <typename T> struct Vec16;
 template <> struct Vec16<bf16_t> {
   static constexpr int N = 8;
@@ -57,7 +64,8 @@ template <> struct Vec16<bf16_t> {
     for (int i = 0; i < 4; ++i)
       w[i] = static_cast<uint32_t>(f32_to_bf16(x[2 * i])) |
              (static_cast<uint32_t>(f32_to_bf16(x[2 * i + 1])) << 16);
-    *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+    const nt4u v = {w[0], w[1], w[2], w[3]};
+    __builtin_nontemporal_store(v, reinterpret_cast<nt4u*>(p));
   }
 };
 template <> struct Vec16<float> {
@@ -67,7 +75,7 @@ template <> struct Vec16<float> {
     x[2] = __uint_as_float(t.z); x[3] = __uint_as_float(t.w);
   }
   __device__ static __forceinline__ void ld(const float* p, float (&x)[4]) { io<float>::ld4(p, x); }
-  __device__ static __forceinline__ void st(float* p, const float (&x)[4]) { io<float>::st4(p, x); }
+  __device__ static __forceinline__ void st(float* p, const float (&x)[4]) { st4_stream(p, x); }
 };
 
 // NB consecutive 16-byte vectors starting at p (16-byte aligned) <-> floats
