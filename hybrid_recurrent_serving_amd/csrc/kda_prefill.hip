@@ -665,15 +665,22 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
       if constexpr (MORE) {
         if (wave < 3) {
           auto a_prod = [&](const int I, const int J, f32x4& acc) __attribute__((always_inline)) {
+            // the three terms of the pair product in accumulators of their own:
+            // dependent chains of D / 32 matrix operations instead of 3 D / 32
+            f32x4 acc1 = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < D / 32; ++ks) {
               const bf16x8 a = frag_lds(&sm.lk[lp][16 * I + l16][32 * ks + kq]);
               const bf16x8 bb = frag_lds(&sm.rk_hi[lp][16 * J + l16][32 * ks + kq]);
               acc = mfma(a, bb, acc);
               if constexpr (HP) {
-                acc = mfma(a, frag_lds(&sm.rk_lo[lp][16 * J + l16][32 * ks + kq]), acc);
-                acc = mfma(frag_lds(&sm.lk_lo[lp][16 * I + l16][32 * ks + kq]), bb, acc);
+                acc1 = mfma(a, frag_lds(&sm.rk_lo[lp][16 * J + l16][32 * ks + kq]), acc1);
+                acc2 = mfma(frag_lds(&sm.lk_lo[lp][16 * I + l16][32 * ks + kq]), bb, acc2);
               }
+            }
+            if constexpr (HP) {
+#pragma unroll
+              for (int i = 0; i < 4; ++i) acc[i] += acc1[i] + acc2[i];
             }
           };
           const int I = wave == 0 ? 0 : 1;
@@ -837,15 +844,18 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
         // P tile per wave: 0 -> (0,0), 1 -> (1,0), 2 -> (1,1); lower incl. diagonal
         const int I = wave == 0 ? 0 : 1;
         const int J = wave == 2 ? 1 : 0;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        // the pair product's three terms in accumulators of their own
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc1 = acc, acc2 = acc;
 #pragma unroll
         for (int ks = 0; ks < D / 32; ++ks) {
           const bf16x8 ah = frag_lds(&sm.lq_hi[lp][16 * I + l16][32 * ks + kq]);
           const bf16x8 bh = frag_lds(&sm.rk_hi[lp][16 * J + l16][32 * ks + kq]);
           acc = mfma(ah, bh, acc);
-          acc = mfma(ah, frag_lds(&sm.rk_lo[lp][16 * J + l16][32 * ks + kq]), acc);
-          acc = mfma(frag_lds(&sm.lq_lo[lp][16 * I + l16][32 * ks + kq]), bh, acc);
+          acc1 = mfma(ah, frag_lds(&sm.rk_lo[lp][16 * J + l16][32 * ks + kq]), acc1);
+          acc2 = mfma(frag_lds(&sm.lq_lo[lp][16 * I + l16][32 * ks + kq]), bh, acc2);
         }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] += acc1[i] + acc2[i];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = 16 * I + 4 * g4 + i;
