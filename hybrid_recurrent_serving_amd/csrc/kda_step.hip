@@ -685,7 +685,9 @@ decode128_kernel(const Dec128Args p) {
       xr = R4::ld(static_cast<const Tin*>(p.x) + static_cast<int64_t>(s) * p.x_stride + ch);
       const int cs = p.csrc[s];
       has_hist = cs >= 0 && cs < p.n_cslots;
-      const Tin* hp = static_cast<const Tin*>(p.cpool) + (static_cast<int64_t>(has_hist ? cs : 0) * C + ch) * HW;
+      // without a history slot the address is this thread's taps (valid for
+      // any slot count, 0 included) and the values read are replaced by zeros
+      const Tin* hp = has_hist ? static_cast<const Tin*>(p.cpool) + (static_cast<int64_t>(cs) * C + ch) * HW : wp;
 #pragma unroll
       for (int b = 0; b < HW; ++b) hr[b] = has_hist ? R4::ld(hp + 4 * b) : R4::zero();
       if (p.bias) br = R4::ld(static_cast<const Tin*>(p.bias) + ch);
