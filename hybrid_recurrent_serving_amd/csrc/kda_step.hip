@@ -581,9 +581,12 @@ int launch_decode_conv(const DecodeConvParams& p, int D, int in_dtype, int out_d
 // the permlane swaps and then over the two row halves through LDS, in a
 // fixed order.  The read-out of the updated state follows without a second
 // pass over it: S'^T q = (Diag(alpha) S)^T q + u (k . q).  Pass 2 is the
-// rank-1 correction S' = Diag(alpha) S + k u^T alone, each row stored as soon
-// as it is formed; with the read-out out of the way the stores leave during
-// the pass rather than after it, which measured 0.7-1.7 us faster per step.
+// rank-1 correction S' = Diag(alpha) S + k u^T alone, each row stored (plain
+// non-temporal global stores) as soon as it is formed.  With the read-out
+// after the update, the compiler issued the sixteen stores after both passes
+// of FMAs (and buffer stores measured slower still): 48.9-49.1 us per fused
+// step and 48.9-49.0 us per plain step, against 47.8-47.9 and 46.4-46.5 us
+// for this form.
 // The per-row values (alpha = exp g, k, q) sit in LDS in lane-group order,
 // row r at (r & 3) * 32 + (r >> 2), so that a lane reads its sixteen rows as
 // four 16-byte vectors.
@@ -648,7 +651,7 @@ decode128_kernel(const Dec128Args p) {
   constexpr int HW = CONV ? W - 1 : 1;  // history length
   constexpr int NTAP = CONV ? W : 1;
   __shared__ __align__(16) float s_q[D], s_k[D], s_a[D], s_v[D];   // q, k, alpha in lane-group order; v
-  __shared__ __align__(16) float s_w[NW][64], s_o[NW][64];          // per-wave partial S^T k, S^T q
+  __shared__ __align__(16) float s_w[NW][64], s_o[NW][64];          // per-wave S^T k, (Diag(alpha) S)^T q
   __shared__ __align__(16) float s_gz[CONV ? D : 4], s_gw[CONV ? D : 4];   // output gate and norm weight
   const int t = static_cast<int>(threadIdx.x);
   const int lane = t & 63;
