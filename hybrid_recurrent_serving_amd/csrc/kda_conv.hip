@@ -33,9 +33,11 @@ constexpr int CONV_THREADS = 256;
 
 // Outputs and new histories are written once and not read again by this
 // kernel: non-temporal stores (the conv at prefill scale ran 4% faster with
-// them: 631 us against 659 us for 140,625 tokens x 6,144 channels).  The
-// loads keep the default policy: a tile's W-1 rows before its own are the
-// previous tile's last rows, found in L2 (non-temporal loads: 666 us).
+// them: 631 us against 659 us for 140,625 tokens x 6,144 channels).  Of a
+// body tile's rows, the W-1 before its own are the previous tile's last rows
+// (found in L2) and its own last W-1 rows are the next tile's first: those
+// keep the default policy, the rows in between are read non-temporally
+// (625 us against 633 us; every row non-temporal: 666 us).
 typedef __attribute__((ext_vector_type(4))) uint32_t nt4u;
 
 template <typename T> struct Vec16;
@@ -287,7 +289,14 @@ __global__ void __launch_bounds__(CONV_THREADS) conv_kernel(const ConvParams p) 
   for (int j = 0; j < HIST + CONV_TT; ++j) {
     const int64_t row = t0 - HIST + j;
     raw[j] = make_uint4(0, 0, 0, 0);
-    if (row >= 0 && row < t1) raw[j] = *reinterpret_cast<const uint4*>(xb + row * p.x_stride + c0);
+    if (row >= 0 && row < t1) {
+      if (j >= HIST && j < CONV_TT) {
+        const nt4u v = __builtin_nontemporal_load(reinterpret_cast<const nt4u*>(xb + row * p.x_stride + c0));
+        raw[j] = make_uint4(v[0], v[1], v[2], v[3]);
+      } else {
+        raw[j] = *reinterpret_cast<const uint4*>(xb + row * p.x_stride + c0);
+      }
+    }
   }
 #pragma unroll
   for (int i = 0; i < CONV_TT; ++i) {
