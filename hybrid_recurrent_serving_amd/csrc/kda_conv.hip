@@ -283,7 +283,12 @@ __global__ void __launch_bounds__(CONV_THREADS) conv_kernel(const ConvParams p) 
     tok_ok[threadIdx.x] = (t < t1 && t >= bos && t < eos && t - bos >= HIST) ? 1 : 0;
   }
   __syncthreads();
-  if (!active) return;
+  // a tile whose tokens all belong to head items (one-token sequences, as in
+  // a decode batch) has nothing to form: no loads
+  int any_ok = 0;
+#pragma unroll
+  for (int i = 0; i < CONV_TT; ++i) any_ok |= tok_ok[i];
+  if (!active || !any_ok) return;
   uint4 raw[HIST + CONV_TT];
 #pragma unroll
   for (int j = 0; j < HIST + CONV_TT; ++j) {
