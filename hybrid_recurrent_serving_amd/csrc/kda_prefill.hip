@@ -151,7 +151,7 @@ struct Smem {
   alignas(16) float eg_c[2][D];           // exp(G_last - G_m) of the chunk before times exp(G_m)
   uint32_t eg_split[2][GATE_WAVES];       // that product is below the normal fp32 range somewhere
   alignas(16) float G[TILE][D];           // cumulative gates (log2 units) of the next chunk
-  float beta[2][TILE];                    // by chunk parity
+  alignas(16) float beta[2][TILE];        // by chunk parity
   bf16_t Tb[TILE][PT];                    // T = (I + A)^{-1} diag(beta) [r][s], block (1,0) zero
   bf16_t Tb_lo[F32IN ? TILE : 1][PT];
   alignas(16) bf16_t Mb[16][PT];          // -M = -L_1^{-1} A10: hi in columns 0..15, lo in 16..31
@@ -198,6 +198,10 @@ __device__ __forceinline__ void to_f32(const uint2* w, float (&x)[8]) {
 // ---------------------------------------------------------------------------
 template <int D, typename TIN, typename TOUT>
 __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, const int d, const int CH) {
+  // Waves w and w + 4 share a SIMD and run the same instruction stream, so
+  // their matrix and vector work would line up in time.  Waves 0-3 issue
+  // first (higher wave priority); waves 4-7 fill their stalls.
+  if (__builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6) < 4) __builtin_amdgcn_s_setprio(1);
   using SM = Smem<D, TIN, TOUT>;
   __shared__ SM sm;
   constexpr bool HP = SM::F32IN;        // all products as pairs
@@ -657,8 +661,9 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
     };
     // The blocks of A = strict-lower(diag(beta) left_k right_k^T) of chunk
     // b (operands complete since the previous step), one per wave on waves
-    // 0-2 -- the chain waves whose own work ends first -- written transposed
-    // to the At tiles for the solve waves of phase II:
+    // 0-2, after their chain's products (issued before them, the A products
+    // held up the chain: 1.566 against 1.522 ms per varlen call), written
+    // transposed to the At tiles for the solve waves of phase II:
     // At[t][c][r] = beta_r <left_k[16 I + r], right_k[16 J + c]>, t = 0: A00,
     // 1: A11, 2: A10.
     auto a_products = [&]() __attribute__((always_inline)) {
@@ -688,10 +693,15 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
           const int tt = wave == 0 ? 0 : (wave == 1 ? 2 : 1);
           f32x4 acc = {0.f, 0.f, 0.f, 0.f};
           a_prod(I, J, acc);
+          // beta of the lane's four rows in one read (read under the mask,
+          // element by element, each read was waited for on its own)
+          const float4 b4 = *reinterpret_cast<const float4*>(&sm.beta[lp][16 * I + 4 * g4]);
+          const float bv[4] = {b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int r = 4 * g4 + i;
-            sm.At[tt][l16][r] = (I > J || r > l16) ? acc[i] * sm.beta[lp][16 * I + r] : 0.f;
+            const float a = acc[i] * bv[i];
+            sm.At[tt][l16][r] = (I > J || r > l16) ? a : 0.f;
           }
         }
       }
@@ -712,7 +722,6 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) wf[ks][mt] = frag_lds(&sm.u.w.Wn[16 * mt + l16][32 * ks + kq]);
       __builtin_amdgcn_sched_barrier(0);
-      a_products();
       bf16x8 sh[NQ / 2], sl[NQ / 2], uh, ul;
 #pragma unroll
       for (int ks = 0; ks < NQ / 2; ++ks) frag_pair(S[2 * ks], S[2 * ks + 1], sh[ks], sl[ks]);
@@ -823,6 +832,7 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
 #pragma unroll
         for (int q = 0; q < NQ; ++q) scale_tile(q);
       }
+      a_products();
       if (ck >= 0) {
         const int slot = p.ckpt_slot[ck];
         if (slot >= 0 && slot < p.n_slots && ncol < d)
