@@ -32,9 +32,9 @@
 // leaves the wave.  The chunk-local operands (gates, gated q / k, A, T, P,
 // W, U) depend only on the chunk's own inputs, so the loop is a software
 // pipeline: while the chain of chunk n runs, the operands of chunk n + 1 are
-// built in the same three barrier-separated phases (the chain in the first,
-// the products and the triangular solve in the second, W / U and the gated
-// operands in the third).  Operands read by a chain while the next chunk's
+// built in the same three barrier-separated phases (the chain and the blocks
+// of A in the first, P and the triangular solve in the second, W / U and the
+// gated operands in the third).  Operands read by a chain while the next chunk's
 // are formed are double-buffered in LDS; raw rows are prefetched into
 // registers one or two chunks ahead.
 //
@@ -619,7 +619,8 @@ __global__ void __launch_bounds__(NT, 1) prefill_kernel(const PrefillParams p, c
   // nothing from the state.  Three phases separated by workgroup barriers:
   //   I    chain of n: state update, outputs  | v of b, g / beta of b + CH to LDS;
   //                                           | their requests for b + CH, b + 2 CH
-  //   II   outputs of n stored                | P and T of b (A inside the solve waves);
+  //   II   outputs of n stored                | P and T of b (T from the A blocks formed
+  //                                           | by waves 0-2 at the end of phase I);
   //                                           | gates of b + CH
   //   III                                     | W = T left_k, U = T V of b;
   //                                           | gated operands of b + CH
