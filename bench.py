@@ -710,8 +710,11 @@ PREFILL_WARMUP = 10
 
 # Segment length of the varlen prefill: sequences of >= 2 segments run as
 # parallel segments (a caller-chosen launch parameter; same function of the
-# inputs up to rounding), which shortens the longest sequence's chain.
-VARLEN_SEGMENT = 4096
+# inputs up to rounding), which shortens the longest sequence's chain.  On
+# this workload (same-process sweep, 4 x 20 calls): 2,048 -> 1.57 ms, 2,560
+# -> 1.58, 3,072 -> 1.455, 3,584 -> 1.64, 4,096 -> 1.50, 5,120 -> 1.52,
+# 6,144 -> 1.71, 8,192 -> 1.59; the segments' packing onto the CUs decides.
+VARLEN_SEGMENT = 3072
 
 
 def bench_prefill_varlen(torch, K, make_workload, dev, iters=20, wl=None, cpu_seconds=0.0, warm=PREFILL_WARMUP):
@@ -820,7 +823,7 @@ def bench_prefill_conv(torch, K, wl, dev, iters=10, cpu_seconds=0.0, warm=PREFIL
     """kda_prefill_varlen_conv on the varlen workload: the 16 sequences'
     raw q / k / v projections (6,144 channels, bf16) through the conv
     (W = 4, carried history, SiLU), the per-head q / k normalisation and the
-    chunked prefill (chunk 64, 4,096-token segments), gates, beta and initial
+    chunked prefill (chunk 64, 3,072-token segments), gates, beta and initial
     states as the varlen row.  Two launches per call (conv + norm, then the
     prefill); each is also timed alone on the same data (the conv through
     kda_conv_short with the same normalisation, the prefill through

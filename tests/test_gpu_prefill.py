@@ -216,13 +216,13 @@ def varlen16(oracle64):
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("segment_len", [0, 4096])
+@pytest.mark.parametrize("segment_len", [0, 3072, 4096])
 def test_prefill_varlen_16_sequences_full(dev, varlen16, segment_len):
     """16 packed sequences, lengths U{512..16384}, H=16, d=128, chunk 64, bf16;
     even sequences from random initial states.  Every output of every
     (sequence, head) and all 16 final states against the oracle.  Unsplit
-    (the default segment length exceeds every sequence) and with the
-    4,096-token segments the benchmark runs."""
+    (the default segment length exceeds every sequence), with the
+    3,072-token segments the benchmark runs, and with 4,096-token ones."""
     U.say(f"prefill 16-sequence varlen (full oracle), segment_len={segment_len}")
     wl, ref = varlen16
     r = run_prefill(dev, wl, chunk=64, segment_len=segment_len)

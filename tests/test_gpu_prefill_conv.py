@@ -202,7 +202,7 @@ def test_prefill_conv_in_place_segment_scan(dev, oracle64):
 
 def test_prefill_conv_varlen_full_size(dev, oracle64):
     """The varlen workload at full size (16 sequences, lengths U{512..16384},
-    H=16, d=128, bf16, chunk 64, 4,096-token segments as the benchmark runs
+    H=16, d=128, bf16, chunk 64, 3,072-token segments as the benchmark runs
     it), all conv histories carried.  Every conv history is compared bit for
     bit; outputs and final states of three sequences (the first, the longest
     and the last, re-packed as a batch of their own for the oracle) over all
@@ -218,7 +218,7 @@ def test_prefill_conv_varlen_full_size(dev, oracle64):
             has[s] = 1
     conv_has = np.ones(N, np.int32)
     x, w, st = wl.conv_x, wl.conv_w, wl.conv_state
-    got = _run(dev, wl, x, w, st, None, init, has, conv_has, act=1, norm=1, segment_len=4096)
+    got = _run(dev, wl, x, w, st, None, init, has, conv_has, act=1, norm=1, segment_len=3072)
     # the new histories: the last 3 raw inputs of every sequence (each has >= 512 tokens)
     cu = wl.cu_seqlens.numpy()
     want = np.stack([x[cu[s + 1] - 3:cu[s + 1]].float().numpy().T for s in range(N)])
